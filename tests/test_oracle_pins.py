@@ -1,0 +1,492 @@
+"""Pins of the CPU oracle against facts fixed by mathematics, not by the oracle.
+
+Each test names the property it checks.  The pages print no worked example of
+the forward pass, so the pins are closed forms, invariants, special cases that
+reduce to something simpler, brute force on tiny inputs, and the exact
+equivalence of cached decode with a layer-major full-sequence forward.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as O
+import persistent_megakernel_02_amd.inputs as I
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def f32_to_bits(x):
+    return np.asarray(x, np.float32).view(np.uint32)
+
+
+def bits_to_f32(b):
+    return (np.asarray(b, np.uint32) << 16).view(np.float32)
+
+
+def ulp_diff(a, b):
+    a = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    b = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    return np.abs(a - b)
+
+
+# ---------------------------------------------------------------------------------------------
+# bf16 rounding
+# ---------------------------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def bf16_checker(tmp_path_factory):
+    out = tmp_path_factory.mktemp("pins") / "libbf16ref.so"
+    subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-o", str(out), os.path.join(HERE, "pins", "bf16_ref.c"),
+                           "-lm", "-lpthread"])
+    lib = ctypes.CDLL(str(out))
+    lib.check_range.restype = ctypes.c_uint64
+    lib.check_range.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,
+                                ctypes.POINTER(ctypes.c_uint32)]
+    return lib
+
+
+def test_bf16_rounding_exhaustive(bf16_checker):
+    """All 2^32 fp32 patterns: nearest bf16, ties to even, overflow to inf, NaN kept."""
+    fn = ctypes.cast(O.lib().orc_bf16_bits, ctypes.c_void_p).value
+    first = ctypes.c_uint32(0)
+    nthreads = max(1, min(8, os.cpu_count() or 1))
+    bad = bf16_checker.check_range(fn, 0, 1 << 32, nthreads, ctypes.byref(first))
+    assert bad == 0, f"{bad} mismatches, first pattern {first.value:#010x}"
+
+
+def test_bf16_rounding_examples():
+    assert O.bf16_bits(1.0) == 0x3F80
+    assert O.bf16_bits(float(np.float32(1.0 + 2**-8))) == 0x3F80      # tie -> even (down)
+    assert O.bf16_bits(float(np.float32(1.0 + 3 * 2**-8))) == 0x3F82  # tie -> even (up)
+    assert O.bf16_bits(float("inf")) == 0x7F80
+    assert O.bf16_bits(-0.0) == 0x8000
+
+
+# ---------------------------------------------------------------------------------------------
+# dot products
+# ---------------------------------------------------------------------------------------------
+def test_dot_small_integers_exact():
+    rng = np.random.default_rng(1)
+    for n in (1, 7, 256, 2048, 8192):
+        wi = rng.integers(-8, 9, n)
+        xi = rng.integers(-8, 9, n)
+        w_bits = (wi.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)  # small ints are exact in bf16
+        assert np.array_equal(bits_to_f32(w_bits), wi.astype(np.float32))
+        assert O.dot(w_bits, xi.astype(np.float32)) == float(int((wi * xi).sum()))
+
+
+def test_dot_random_vs_long_double():
+    rng = np.random.default_rng(2)
+    for n in (3, 100, 4096):
+        w_bits = I.normal_bf16(I.key(5, 99, n), (n,), 0.0, 0.02)
+        x = bits_to_f32(I.normal_bf16(I.key(6, 99, n), (n,), 0.0, 1.0))
+        ref = np.sum(bits_to_f32(w_bits).astype(np.longdouble) * x.astype(np.longdouble))
+        assert ulp_diff(O.dot(w_bits, x), np.float32(ref)) <= 1
+
+
+def test_dot_index_order_matters_only_in_double():
+    # a sum whose fp32 left-to-right value differs from the exact one: the oracle must give the exact one
+    w_bits = np.array([0x3F80, 0x3F80, 0x3F80], np.uint16)  # ones
+    x = np.array([2.0**24, 1.0, 1.0], np.float32)
+    assert O.dot(w_bits, x) == 2.0**24 + 2.0
+
+
+# ---------------------------------------------------------------------------------------------
+# RMSNorm
+# ---------------------------------------------------------------------------------------------
+def test_rmsnorm_constant_vector_closed_form():
+    d = 2048
+    g_bits = I.normal_bf16(I.key(0, 77), (d,), 1.0, 0.5)
+    g = bits_to_f32(g_bits)
+    for c in (2.0, -0.25, 8.0):  # mean(h^2) = c^2, eps = 0 -> scale 1/|c| exactly
+        x = O.rmsnorm(np.full(d, c, np.float32), g_bits, 0.0)
+        assert np.array_equal(x, g * np.float32(np.sign(c)))
+    # with eps: x_i = bf16(c / sqrt(c^2 + eps) * g_i); c = 0.003 makes eps matter (scale ~0.69)
+    for c, eps in ((0.5, 1e-5), (0.003, 1e-5)):
+        x = O.rmsnorm(np.full(d, c, np.float32), g_bits, eps)
+        scale = np.longdouble(np.float32(c)) / np.sqrt(np.longdouble(np.float32(c)) ** 2 + np.longdouble(eps))
+        want = (scale * g.astype(np.longdouble)).astype(np.float32)
+        want_bf = np.array([O.bf16_bits(float(v)) for v in want], np.uint32)
+        assert (f32_to_bits(x) >> 16 == want_bf).mean() > 0.995
+        assert np.abs(x.astype(np.float64) / (scale * g) - 1).max() <= 2.0**-8
+
+
+def test_rmsnorm_random_vs_long_double():
+    d = 4096
+    h = bits_to_f32(I.normal_bf16(I.key(3, 1), (d,), 0.0, 3.0)) * np.float32(1.37)
+    g_bits = I.normal_bf16(I.key(3, 2), (d,), 1.0, 0.02)
+    x = O.rmsnorm(h, g_bits, 1e-5)
+    hl = h.astype(np.longdouble)
+    r = 1 / np.sqrt(np.mean(hl * hl) + np.longdouble(1e-5))
+    exact = (hl * r * bits_to_f32(g_bits).astype(np.longdouble))
+    # the result is the bf16 rounding of the exact value, except within fp32 noise of a rounding boundary
+    rel = np.abs((x.astype(np.longdouble) - exact) / exact)
+    assert rel.max() <= 2.0**-8 * (1 + 1e-6)
+    want_bits = np.array([O.bf16_bits(float(v)) for v in exact.astype(np.float32)], np.uint32)
+    assert (f32_to_bits(x) >> 16 == want_bits).mean() > 0.999
+
+
+def test_rmsnorm_scale_invariance():
+    d = 512
+    h = bits_to_f32(I.normal_bf16(I.key(4, 1), (d,), 0.0, 1.0))
+    g_bits = I.normal_bf16(I.key(4, 2), (d,), 1.0, 0.1)
+    assert np.array_equal(O.rmsnorm(h, g_bits, 0.0), O.rmsnorm(h * np.float32(4.0), g_bits, 0.0))
+
+
+# ---------------------------------------------------------------------------------------------
+# RoPE
+# ---------------------------------------------------------------------------------------------
+def test_rope_position_zero_is_identity():
+    v = bits_to_f32(I.normal_bf16(I.key(8, 1), (128,), 0.0, 1.0))
+    assert np.array_equal(O.rope(v, 0, 500000.0), v)
+
+
+def test_rope_preserves_pair_norms():
+    hd = 64
+    v = bits_to_f32(I.normal_bf16(I.key(8, 2), (hd,), 0.0, 1.0))
+    for p in (1, 17, 159, 8191):
+        r = O.rope(v, p, 10000.0).astype(np.float64)
+        n0 = v[: hd // 2].astype(np.float64) ** 2 + v[hd // 2:].astype(np.float64) ** 2
+        n1 = r[: hd // 2] ** 2 + r[hd // 2:] ** 2
+        assert np.allclose(n1, n0, rtol=1e-6, atol=1e-12)
+
+
+def test_rope_pair_zero_turns_by_position_radians():
+    hd = 64
+    for p in (1, 5, 100, 8000):
+        e0 = np.zeros(hd, np.float32)
+        e0[0] = 1.0
+        r = O.rope(e0, p, 10000.0)
+        assert ulp_diff(r[0], np.float32(np.cos(np.float64(p)))) <= 1
+        assert ulp_diff(r[hd // 2], np.float32(np.sin(np.float64(p)))) <= 1
+
+
+def test_rope_relative_position_invariance():
+    hd = 64
+    q = bits_to_f32(I.normal_bf16(I.key(9, 1), (hd,), 0.0, 1.0))
+    k = bits_to_f32(I.normal_bf16(I.key(9, 2), (hd,), 0.0, 1.0))
+    base = float(np.dot(O.rope(q, 10, 10000.0).astype(np.float64), O.rope(k, 3, 10000.0).astype(np.float64)))
+    for s in (1, 50, 100):
+        sh = float(np.dot(O.rope(q, 10 + s, 10000.0).astype(np.float64),
+                          O.rope(k, 3 + s, 10000.0).astype(np.float64)))
+        assert abs(sh - base) <= 1e-5 * max(1.0, abs(base))
+
+
+def test_rope_uses_rotate_half_pairs_and_frequencies():
+    hd, theta, p = 8, 10000.0, 3
+    for i in range(hd // 2):
+        e = np.zeros(hd, np.float32)
+        e[i] = 1.0
+        r = O.rope(e, p, theta)
+        ang = p * theta ** (-2.0 * i / hd)
+        assert ulp_diff(r[i], np.float32(np.cos(ang))) <= 1
+        assert ulp_diff(r[i + hd // 2], np.float32(np.sin(ang))) <= 1
+        others = np.delete(r, [i, i + hd // 2])
+        assert not others.any()
+
+
+# ---------------------------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------------------------
+def _attend_long_double(q, K, V):
+    qd = q.astype(np.longdouble)
+    Kd = bits_to_f32(K).astype(np.longdouble)
+    Vd = bits_to_f32(V).astype(np.longdouble)
+    s = (Kd @ qd) / np.sqrt(np.longdouble(q.size))
+    s = s.astype(np.float32).astype(np.longdouble)  # scores are fp32 in the contract
+    e = np.exp(s - s.max())
+    p = e / e.sum()
+    return (p @ Vd)
+
+
+def test_attention_brute_force_small():
+    for n in (1, 2, 5, 16):
+        hd = 64
+        q = bits_to_f32(I.normal_bf16(I.key(10, n, 0), (hd,), 0.0, 1.0))
+        K = I.normal_bf16(I.key(10, n, 1), (n, hd), 0.0, 1.0)
+        V = I.normal_bf16(I.key(10, n, 2), (n, hd), 0.0, 1.0)
+        o = O.attend(q, K, V)
+        ref = _attend_long_double(q, K, V)
+        assert np.max(np.abs(o.astype(np.longdouble) - ref)) <= 4 * np.finfo(np.float32).eps * max(1, np.abs(ref).max())
+
+
+def test_attention_single_position_returns_value_row():
+    hd = 64
+    q = bits_to_f32(I.normal_bf16(I.key(11, 1), (hd,), 0.0, 1.0))
+    K = I.normal_bf16(I.key(11, 2), (1, hd), 0.0, 1.0)
+    V = I.normal_bf16(I.key(11, 3), (1, hd), 0.0, 1.0)
+    assert np.array_equal(O.attend(q, K, V), bits_to_f32(V[0]))
+
+
+def test_attention_zero_query_is_mean_of_values():
+    n, hd = 9, 64
+    K = I.normal_bf16(I.key(12, 2), (n, hd), 0.0, 1.0)
+    V = I.normal_bf16(I.key(12, 3), (n, hd), 0.0, 1.0)
+    o = O.attend(np.zeros(hd, np.float32), K, V)
+    want = bits_to_f32(V).astype(np.longdouble).mean(axis=0).astype(np.float32)
+    assert ulp_diff(o, want).max() <= 1
+
+
+def test_attention_dominant_score_selects_row():
+    n, hd = 12, 64
+    K = np.zeros((n, hd), np.uint16)
+    K[7, :] = 0x4100  # 8.0
+    q = np.full(hd, 8.0, np.float32)  # score of row 7 = 64*64/8 = 512, others 0
+    V = I.normal_bf16(I.key(13, 3), (n, hd), 0.0, 1.0)
+    o = O.attend(q, K, V)
+    assert np.array_equal(o, bits_to_f32(V[7]))
+
+
+def test_attention_weights_sum_to_one_via_constant_values():
+    n, hd = 33, 64
+    q = bits_to_f32(I.normal_bf16(I.key(14, 1), (hd,), 0.0, 1.0))
+    K = I.normal_bf16(I.key(14, 2), (n, hd), 0.0, 1.0)
+    V = np.full((n, hd), 0x3FC0, np.uint16)  # 1.5 everywhere
+    assert np.allclose(O.attend(q, K, V), 1.5, rtol=0, atol=4e-7)
+
+
+# ---------------------------------------------------------------------------------------------
+# SwiGLU, argmax, routing
+# ---------------------------------------------------------------------------------------------
+def test_swiglu_special_values():
+    assert O.swiglu(0.0, 5.0) == 0.0
+    assert O.swiglu(40.0, 1.5) == 60.0          # silu(z) -> z for large z
+    assert O.swiglu(-40.0, 1.0) > -1e-15         # silu(z) -> 0 from below
+    z, u = 1.25, -0.75
+    ref = np.longdouble(z) / (1 + np.exp(-np.longdouble(z))) * np.longdouble(u)
+    assert O.swiglu(z, u) == float(bits_to_f32(O.bf16_bits(float(np.float32(ref)))))
+
+
+def test_argmax_ties_take_lowest_index():
+    v = np.array([0.5, 2.0, -1.0, 2.0, 2.0], np.float32)
+    assert O.argmax(v) == 1
+    v = np.zeros(100, np.float32)
+    assert O.argmax(v) == 0
+    v[[40, 41, 99]] = 1.0
+    assert O.argmax(v) == 40
+    v[3] = np.nan
+    assert O.argmax(v) == -1
+
+
+def test_route_ties_and_probabilities():
+    z = np.zeros(8, np.float32)
+    z[[2, 5, 6]] = 1.0
+    sel, prob = O.route(z, 2)
+    assert list(sel) == [2, 5]  # three-way tie -> lower indices
+    assert abs(float(prob.astype(np.float64).sum()) - 1.0) < 1e-6
+    e = np.exp(np.array(z, np.float64) - 1.0)
+    assert np.allclose(prob, e / e.sum(), rtol=1e-7)
+    sel, _ = O.route(np.arange(8, dtype=np.float32)[::-1].copy(), 3)
+    assert list(sel) == [0, 1, 2]
+
+
+# ---------------------------------------------------------------------------------------------
+# whole-model pins (tiny shapes)
+# ---------------------------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def tiny_weights():
+    return I.make_weights(I.TINY, seed=0)
+
+
+def _greedy_run(cfg, w, prompt, steps):
+    orc = O.Oracle(cfg, w, prompt.shape[0], prompt.shape[1] + steps + 1)
+    nxt, logits = orc.prefill(prompt)
+    toks, rows = [nxt.copy()], [logits.copy()]
+    for _ in range(steps):
+        nxt, logits = orc.step(nxt)
+        toks.append(nxt.copy())
+        rows.append(logits.copy())
+    return np.stack(toks, 1), np.stack(rows, 1), orc
+
+
+def test_cached_decode_equals_full_recompute(tiny_weights):
+    """KV-cached step-by-step decode and a layer-major forward without cache agree bitwise."""
+    prompt = I.make_prompt(I.TINY, 1, 8, seed=0)
+    toks, logits, _ = _greedy_run(I.TINY, tiny_weights, prompt, 16)
+    seq = np.concatenate([prompt[0], toks[0, :-1]])  # the 24 inputs fed at positions 0..23
+    orc = O.Oracle(I.TINY, tiny_weights, 1, 32)
+    full = orc.sequence(seq)
+    # decode logits at positions 7..23 are the prefill tail and the 16 decode steps
+    assert np.array_equal(full[7:], logits[0])
+
+
+def test_batch_independence(tiny_weights):
+    prompt = I.make_prompt(I.TINY, 3, 8, seed=1)
+    toks, logits, _ = _greedy_run(I.TINY, tiny_weights, prompt, 4)
+    for b in range(3):
+        t1, l1, _ = _greedy_run(I.TINY, tiny_weights, prompt[b:b + 1], 4)
+        assert np.array_equal(t1[0], toks[b]) and np.array_equal(l1[0], logits[b])
+
+
+def test_zero_output_projections_reduce_to_embedding_head(tiny_weights):
+    """With W_o = W_down = 0 every layer is the identity on the residual stream, so
+    logits = W_head . bf16(RMSNorm(E[tok]) g_final) at any position."""
+    cfg = I.TINY
+    w = I.make_weights(cfg, seed=3)
+    for L in w.layers:
+        L["wo"] = np.zeros_like(L["wo"])
+        L["w_down"] = np.zeros_like(L["w_down"])
+    orc = O.Oracle(cfg, w, 1, 16)
+    toks = [5, 4095, 17, 5]
+    outs = [orc.step([t])[1][0] for t in toks]
+    head = bits_to_f32(w.head).astype(np.float64)
+    for t, got in zip(toks, outs):
+        h = bits_to_f32(w.embed[t])
+        x = O.rmsnorm(h, w.final_norm, cfg.rms_eps)
+        want = (head @ x.astype(np.float64)).astype(np.float32)
+        assert ulp_diff(got, want).max() <= 1
+    assert np.array_equal(outs[0], outs[3])  # same token, different position
+
+
+def test_untied_head_is_used():
+    cfg = I.replace(I.TINY, tied=False)
+    w = I.make_weights(cfg, seed=0)
+    assert w.lm_head is not None
+    orc_u = O.Oracle(cfg, w, 1, 4)
+    w_t = I.make_weights(I.TINY, seed=0)
+    orc_t = O.Oracle(I.TINY, w_t, 1, 4)
+    lu = orc_u.step([11])[1]
+    lt = orc_t.step([11])[1]
+    assert not np.array_equal(lu, lt)
+
+
+def test_dense_ffn_closed_form():
+    """One-hot rows pick single normed features: with gate row e_0, up row e_1 and
+    W_down = e_0 column the FFN adds bf16(silu(x0) * x1) to h_0 only."""
+    cfg = I.replace(I.TINY, hidden=8, ffn=4, n_layers=1, vocab=16)
+    d, F = 8, 4
+    one = 0x3F80
+    Wg = np.zeros((F, d), np.uint16); Wg[0, 0] = one
+    Wu = np.zeros((F, d), np.uint16); Wu[0, 1] = one
+    Wd = np.zeros((d, F), np.uint16); Wd[0, 0] = one
+    g = np.full(d, one, np.uint16)
+    L = {"attn_norm": g, "wq": np.zeros((cfg.n_q_heads * 64, d), np.uint16), "wk": np.zeros((128, d), np.uint16),
+         "wv": np.zeros((128, d), np.uint16), "wo": np.zeros((d, cfg.n_q_heads * 64), np.uint16), "mlp_norm": g,
+         "w_gate": Wg, "w_up": Wu, "w_down": Wd}
+    w = I.Weights(cfg, np.zeros((16, d), np.uint16), None, g, [L])
+    orc = O.Oracle(cfg, w, 1, 4)
+    h = np.array([[3.0, -1.0, 0.5, 2.0, 0.0, 1.0, -2.0, 0.25]], np.float32)
+    out = orc.ffn(0, h)
+    x = O.rmsnorm(h[0], g, cfg.rms_eps)
+    x0, x1 = np.longdouble(x[0]), np.longdouble(x[1])
+    a = O.bf16_bits(float(np.float32(x0 / (1 + np.exp(-x0)) * x1)))
+    want = h.copy()
+    want[0, 0] = np.float32(np.float32(h[0, 0]) + bits_to_f32(a))
+    assert np.array_equal(out, want)
+
+
+# ---------------------------------------------------------------------------------------------
+# MoE pins
+# ---------------------------------------------------------------------------------------------
+def _tiny_moe(top_k, seed=0):
+    cfg = I.replace(I.TINY, name="tiny-moe", n_layers=1, ffn=0, n_experts=8, top_k=top_k, n_shared=1,
+                    expert_ffn=128, tied=False)
+    return cfg, I.make_weights(cfg, seed=seed)
+
+
+def _expert(orc_cfg_w, x, gate, up, down):
+    """One SwiGLU expert from the pinned primitives: fp32(W_d . bf16(silu(W_g x) * (W_u x)))."""
+    Fe = gate.shape[0]
+    a = np.array([O.swiglu(O.dot(gate[f], x), O.dot(up[f], x)) for f in range(Fe)], np.float32)
+    return np.array([O.dot(down[i], a) for i in range(down.shape[0])], np.float32)
+
+
+def test_moe_all_experts_is_dense_weighted_mixture():
+    cfg, w = _tiny_moe(top_k=8)
+    L = w.layers[0]
+    orc = O.Oracle(cfg, w, 1, 4)
+    h = bits_to_f32(I.normal_bf16(I.key(21, 1), (1, cfg.hidden), 0.0, 1.0))
+    out = orc.ffn(0, h)
+    x = O.rmsnorm(h[0], L["mlp_norm"], cfg.rms_eps)
+    zeta = np.array([O.dot(L["router"][e], x) for e in range(8)], np.float32)
+    e = np.exp(zeta.astype(np.float64) - zeta.max())
+    p = (e / e.sum()).astype(np.float32)
+    acc = _expert(None, x, L["s_gate"], L["s_up"], L["s_down"]).astype(np.float64)
+    for k in range(8):
+        acc += np.float64(p[k]) * _expert(None, x, L["e_gate"][k], L["e_up"][k], L["e_down"][k]).astype(np.float64)
+    want = (h[0].astype(np.float64) + acc.astype(np.float32).astype(np.float64)).astype(np.float32)
+    assert ulp_diff(out[0], want).max() <= 1
+
+
+def test_moe_overwhelming_router_logit_selects_one_expert():
+    cfg, w = _tiny_moe(top_k=2)
+    L = w.layers[0]
+    h = bits_to_f32(I.normal_bf16(I.key(22, 1), (1, cfg.hidden), 0.0, 1.0))
+    x = O.rmsnorm(h[0], L["mlp_norm"], cfg.rms_eps)
+    # router row 5 = 8 sign(x): logit 8 sum|x| dominates; row 2 = 7.9375 sign(x) comes
+    # second with a small but nonzero probability; every other expert underflows to 0
+    r = np.zeros_like(L["router"])
+    r[5] = np.where(x >= 0, 0x4100, 0xC100).astype(np.uint16)
+    r[2] = np.where(x >= 0, 0x40FE, 0xC0FE).astype(np.uint16)
+    L["router"] = r
+    orc = O.Oracle(cfg, w, 1, 4)
+    out = orc.ffn(0, h)
+    sel, prob = O.route(np.array([O.dot(r[e], x) for e in range(8)], np.float32), 2)
+    assert list(sel) == [2, 5] and prob[5] > 0.999 and 0.0 < prob[2] < 1e-3
+    assert not np.delete(prob, [2, 5]).any()
+    y = _expert(None, x, L["s_gate"], L["s_up"], L["s_down"]).astype(np.float64)
+    y += np.float64(prob[2]) * _expert(None, x, L["e_gate"][2], L["e_up"][2], L["e_down"][2]).astype(np.float64)
+    y += np.float64(prob[5]) * _expert(None, x, L["e_gate"][5], L["e_up"][5], L["e_down"][5]).astype(np.float64)
+    want = (h[0].astype(np.float64) + y.astype(np.float32).astype(np.float64)).astype(np.float32)
+    assert ulp_diff(out[0], want).max() <= 1
+
+
+def test_gqa_grouping_with_uniform_attention():
+    """q = 0 makes attention uniform, so q-head h returns the mean of its KV group's
+    values; with W_o = identity and W_down = 0 the logits expose which KV head each
+    q-head read: head h must read KV head h // (Hq / Hkv)."""
+    cfg = I.replace(I.TINY, n_layers=1)
+    assert cfg.hidden == cfg.n_q_heads * cfg.head_dim
+    w = I.make_weights(cfg, seed=4)
+    L = w.layers[0]
+    L["wq"] = np.zeros_like(L["wq"])
+    L["wo"] = np.where(np.eye(cfg.hidden, dtype=bool), 0x3F80, 0).astype(np.uint16)
+    L["w_down"] = np.zeros_like(L["w_down"])
+    orc = O.Oracle(cfg, w, 1, 8)
+    toks = [9, 300, 4000]
+    for t in toks:
+        _, logits = orc.step([t])
+    n, hd, grp = len(toks), cfg.head_dim, cfg.n_q_heads // cfg.n_kv_heads
+    V = bits_to_f32(orc.v_cache[0, 0, :, :n, :]).astype(np.float64)  # [Hkv, n, hd]
+    o = np.concatenate([V[h // grp].mean(axis=0) for h in range(cfg.n_q_heads)]).astype(np.float32)
+    o = bits_to_f32(np.array([O.bf16_bits(float(v)) for v in o], np.uint32))
+    h = (bits_to_f32(w.embed[toks[-1]]) + o).astype(np.float32)
+    x = O.rmsnorm(h, w.final_norm, cfg.rms_eps)
+    want = (bits_to_f32(w.head).astype(np.float64) @ x.astype(np.float64)).astype(np.float32)
+    assert ulp_diff(logits[0], want).max() <= 1
+
+
+def test_one_layer_attention_composition():
+    """One layer with W_o = identity and W_down = 0: the logits are
+    W_head . RMSNorm(E[tok] + bf16(o)), where o_h = attend(bf16(RoPE(W_q,h x, p)),
+    K, V) over the cache, and the cache holds bf16(RoPE(W_k x)) and bf16(W_v x) of
+    every earlier position.  Rebuilt here from the pinned primitives."""
+    cfg = I.replace(I.TINY, n_layers=1)
+    w = I.make_weights(cfg, seed=6, weight_std=0.06)
+    L = w.layers[0]
+    L["wo"] = np.where(np.eye(cfg.hidden, dtype=bool), 0x3F80, 0).astype(np.uint16)
+    L["w_down"] = np.zeros_like(L["w_down"])
+    hd, Hq, Hkv = cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads
+    orc = O.Oracle(cfg, w, 1, 8)
+    toks = [77, 1234, 4095, 5]
+    for p, t in enumerate(toks):
+        _, logits = orc.step([t])
+        x = O.rmsnorm(bits_to_f32(w.embed[t]), L["attn_norm"], cfg.rms_eps)
+        for g in range(Hkv):
+            k = np.array([O.dot(L["wk"][g * hd + i], x) for i in range(hd)], np.float32)
+            v = np.array([O.dot(L["wv"][g * hd + i], x) for i in range(hd)], np.float32)
+            kr = O.rope(k, p, cfg.rope_theta)
+            assert np.array_equal(orc.k_cache[0, 0, g, p], np.array([O.bf16_bits(float(a)) for a in kr], np.uint16))
+            assert np.array_equal(orc.v_cache[0, 0, g, p], np.array([O.bf16_bits(float(a)) for a in v], np.uint16))
+        o = []
+        for h in range(Hq):
+            q = np.array([O.dot(L["wq"][h * hd + i], x) for i in range(hd)], np.float32)
+            q = O.bf16_round(O.rope(q, p, cfg.rope_theta))
+            g = h // (Hq // Hkv)
+            o.append(O.bf16_round(O.attend(q, orc.k_cache[0, 0, g, :p + 1], orc.v_cache[0, 0, g, :p + 1])))
+        hh = (bits_to_f32(w.embed[t]) + np.concatenate(o)).astype(np.float32)
+        xf = O.rmsnorm(hh, w.final_norm, cfg.rms_eps)
+        want = (bits_to_f32(w.head).astype(np.float64) @ xf.astype(np.float64)).astype(np.float32)
+        assert ulp_diff(logits[0], want).max() <= 1
