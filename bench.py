@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Decode benchmark: µs/token of the persistent megakernel at batch 1 on the
+Llama-3.2-1B shape (32 prompt tokens, then greedy decode), as a fraction of the
+MI355X HBM roofline, next to the one-kernel-per-op hipGraph path, the measured
+streaming-read ceiling, and the CPU oracle timed on the host.
+
+One "step" is one decode step (one token per sequence): a single persistent
+launch.  Weights are random (seeded, bf16 N(0, 0.02)), inputs already resident
+in HBM when timing starts.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps 128] [--warmup 32]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def step_bytes(cfg, batch: int, positions) -> int:
+    """Algorithmic HBM bytes of one decode step: every weight byte once, the
+    token's embedding row, the K/V of the cached positions read once per
+    (sequence, KV head), the new K/V written, the fp32 logits written."""
+    kv_pos = cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim * 2
+    b = cfg.weight_bytes() + batch * cfg.hidden * 2
+    b += sum(int(p) for p in positions) * kv_pos  # cached positions 0..p-1 read
+    b += batch * kv_pos                            # position p written
+    b += batch * cfg.vocab * 4
+    return b
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--prompt", type=int, default=32)
+    ap.add_argument("--horizon", type=int, default=128, help="decode steps before the context is reset to the prompt")
+    ap.add_argument("--no-graph", action="store_true", help="skip the one-kernel-per-op comparison")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-steps", type=int, default=24)
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this decode path runs on one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding is a design note, not built)"}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    import persistent_megakernel_02_amd.inputs as I
+    import persistent_megakernel_02_amd.mk as mk
+
+    cfg = I.LLAMA_1B
+    B, P, H = 1, args.prompt, args.horizon
+    max_seq = P + H + 1
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    w = I.make_weights(cfg, seed=args.seed)
+    prompt = I.make_prompt(cfg, B, P, seed=args.seed)
+    log(f"weights generated in {time.time() - t0:.1f}s")
+    dw = mk.upload_weights(w, dev)
+    torch.cuda.synchronize()
+    prompt_dev = torch.from_numpy(prompt).to(dev)
+
+    def run_path(mode: int, label: str):
+        dec = mk.Decoder(cfg, w, max_batch=B, max_seq=max_seq, mode=mode, device="cuda:0", device_weights=dw)
+        st = dec.stream
+        tok = torch.zeros(B, dtype=torch.int32, device=dev)
+        logits = torch.empty((B, cfg.vocab), dtype=torch.float32, device=dev)
+
+        def start_horizon():
+            dec.set_context_len([0] * B)
+            dec.prefill(prompt_dev, logits, tok)
+
+        # warmup
+        start_horizon()
+        done = 0
+        for _ in range(args.warmup):
+            if done == H:
+                start_horizon()
+                done = 0
+            dec.decode_step(tok, tok, logits)
+            done += 1
+        torch.cuda.synchronize()
+        # timed: horizons of <= H steps from the prompt; events on the launch stream
+        total_ms, left, positions, per_h = 0.0, args.steps, [], []
+        while left > 0:
+            n = min(left, H)
+            start_horizon()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for i in range(n):
+                dec.decode_step(tok, tok, logits)
+            e1.record(st)
+            e1.synchronize()
+            ms = e0.elapsed_time(e1)
+            total_ms += ms
+            per_h.append(ms * 1000.0 / n)
+            positions.extend(range(P, P + n))
+            left -= n
+        kps = dec.kernels_per_step()
+        dec.close()
+        us = total_ms * 1000.0 / args.steps
+        log(f"{label}: {us:.1f} us/token over {args.steps} steps ({kps} kernels/step)")
+        return us, positions, kps, per_h
+
+    us_mk, positions, kps_mk, per_h = run_path(mk.MK_MODE_MEGAKERNEL, "megakernel")
+    bytes_step = [step_bytes(cfg, B, [p]) for p in positions]
+    mean_bytes = float(np.mean(bytes_step))
+    gbs = mean_bytes / (us_mk * 1e-6) / 1e9
+
+    us_graph = kps_graph = None
+    if not args.no_graph:
+        us_graph, _, kps_graph, _ = run_path(mk.MK_MODE_GRAPH, "hipGraph one-kernel-per-op")
+
+    # streaming-read ceiling on a buffer the size of the step
+    buf = torch.empty(int(mean_bytes) // 16 * 16, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        mk.bench_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    reps = 10
+    for _ in range(reps):
+        mk.bench_stream_read(buf, sink)
+    e1.record()
+    e1.synchronize()
+    ceil_gbs = buf.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    log(f"streaming-read ceiling: {ceil_gbs:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle as O
+
+        orc = O.Oracle(cfg, w, B, max_seq)
+        t1 = time.time()
+        nxt, _ = orc.prefill(prompt[:, :4])
+        orc.pos[:] = P
+        t2 = time.time()
+        for _ in range(args.cpu_steps):
+            nxt, _ = orc.step(nxt)
+        t3 = time.time()
+        cpu_us = (t3 - t2) * 1e6 / args.cpu_steps
+        cpu = {"value": round(cpu_us, 1), "unit": "us/token", "cores": O.threads(), "kind": "oracle",
+               "sample": f"{args.cpu_steps} batch-1 decode steps of the same 1B-shape model at positions "
+                         f"{P}..{P + args.cpu_steps - 1} (fp64-accumulated C oracle, OpenMP over rows)"}
+        log(f"cpu oracle: {cpu_us / 1000:.1f} ms/token on {O.threads()} threads")
+
+    out = {
+        "metric": "decode us/token at batch 1 (Llama-3.2-1B shape) + % of peak HBM BW",
+        "value": round(us_mk, 2),
+        "unit": "us/token",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_mk / 1000.0, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama-3.2-1b-shape decode, batch 1, 32 prompt tokens then greedy steps, "
+                               "random bf16 weights N(0,0.02)", "batch": B, "prompt": P, "horizon": H,
+                   "layers": cfg.n_layers, "hidden": cfg.hidden, "vocab": cfg.vocab},
+        "tokens_per_s": round(1e6 / us_mk, 1),
+        "pct_peak_hbm": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "pct_stream_ceiling": round(100.0 * gbs / ceil_gbs, 2),
+        "stream_read_ceiling_gbs": round(ceil_gbs, 1),
+        "kernels_per_step": kps_mk,
+        "us_per_token_per_horizon": [round(x, 2) for x in per_h],
+        "graph_path": None if us_graph is None else {"us_per_token": round(us_graph, 2),
+                                                     "kernels_per_step": kps_graph,
+                                                     "pct_peak_hbm": round(100.0 * mean_bytes / (us_graph * 1e-6)
+                                                                           / 1e9 / HBM_PEAK_GBS, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(mean_bytes)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,32 @@
+/*
+ * mk_bench.h - measurement helpers shipped with the decode library.
+ *
+ * The decode step is bounded by HBM bandwidth, so its report needs the device's
+ * practical streaming-read ceiling next to the nominal peak, and the HBM byte
+ * counters of the profiler need a calibration against a transfer of known size.
+ * (The page "斯坦福团队新作让Llama1B实现毫秒级推理获Karpathy盛赞", section
+ * "Megakernel：从零设计的深度融合方案", reports the megakernel as a fraction of
+ * memory bandwidth; these kernels give the MI355X denominators.)
+ */
+#ifndef MK_BENCH_H
+#define MK_BENCH_H
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Read `bytes` (multiple of 16, 16-byte aligned) from device memory d_src with
+ * 16-byte vector loads over the whole device; d_sink is a device word the kernel
+ * may write.  Enqueued on `stream` (hipStream_t).  Returns 0, 1 on bad arguments,
+ * 4 on a launch error. */
+int mk_bench_stream_read(const void* d_src, size_t bytes, void* d_sink, void* stream);
+
+/* Copy `bytes` (multiple of 16, both pointers 16-byte aligned) device to device
+ * with 16-byte loads and stores.  Same return codes. */
+int mk_bench_copy(void* d_dst, const void* d_src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,500 @@
+// The persistent decode megakernel: one launch runs a whole decode step.
+//
+// Design (page "斯坦福团队新作让Llama1B实现毫秒级推理获Karpathy盛赞", section
+// "Megakernel：从零设计的深度融合方案", re-made for CDNA4):
+//  - one workgroup per compute unit walks that CU's instruction queue, built on
+//    the host before launch (the per-SM plan);
+//  - shared memory cut into pages lets the next instructions' weights load while
+//    the current one computes: here one LOADER wave streams the CU's weight and
+//    KV bytes HBM -> LDS with 16-byte-per-lane direct-to-LDS loads
+//    (global_load_lds_dwordx4) into a 128 KB ring, ahead of the four COMPUTE
+//    waves, and keeps streaming while they wait on dependencies;
+//  - dependencies are global-memory counters: the last wave of a CU to finish an
+//    instruction releases its results and increments the instruction's counter;
+//    a dependant spins (one relaxed agent-scope load per poll, s_sleep between
+//    polls) until counter >= epoch * producers, then acquires.  Counters are
+//    monotonic across steps, so nothing is reset between launches;
+//  - every spin is bounded by a watchdog (s_memrealtime, 100 MHz): on expiry the
+//    CU records an error and all waves leave, so a launch always terminates.
+//
+// The loader's vector-memory instructions are only these LDS loads, so its
+// vmcnt counter counts exactly the chunks in flight; it publishes progress in
+// LDS after `s_waitcnt vmcnt(N)`.  Compute waves publish, per wave, the first
+// ring chunk they still need; the loader reuses ring space below the minimum.
+#include <hip/hip_runtime.h>
+
+#include "mk_device.h"
+
+namespace mk {
+
+struct Ctl {
+    uint32_t landed;                     // chunks of the stream resident in the ring
+    uint32_t consumed[kComputeWaves];    // first chunk each compute wave still needs
+    uint32_t done;                       // instruction completions (monotonic, per wave)
+    uint32_t bar;                        // compute-wave barrier arrivals (monotonic)
+    uint32_t abort;                      // set when a wave gives up (error)
+    int32_t ctx[kMaxBatch];              // context lengths at launch
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+
+__device__ __forceinline__ uint32_t lds_ld(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_st(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+__device__ __forceinline__ uint32_t align_chunk(uint32_t b) { return (b + kChunk - 1u) & ~(kChunk - 1u); }
+
+// Bytes of the CU stream that instruction `in` consumes.
+template <int HD>
+__device__ __forceinline__ uint32_t instr_bytes(const Params& P, const Instr& in, const int32_t* ctx) {
+    switch (in.op) {
+        case OP_QKV:
+        case OP_HEAD: return align_chunk(in.count * (uint32_t)P.d * 2u);
+        case OP_O: return align_chunk(in.count * (uint32_t)(P.Hq * HD) * 2u);
+        case OP_GATEUP: return align_chunk(2u * in.count * (uint32_t)P.d * 2u);
+        case OP_DOWN: return align_chunk(in.count * (uint32_t)P.F * 2u);
+        case OP_ATTN: {
+            const int per_b = P.Hkv * P.nsplit;
+            const int b = (int)in.begin / per_b, s = (int)in.begin % P.nsplit;
+            const SplitRange R = split_range<HD>(ctx[b], s, P.nsplit);
+            return (uint32_t)R.ngroups * 2u * kChunk;
+        }
+        default: return 0;
+    }
+}
+
+// Global source address of this lane's 16 bytes of chunk c of instruction `in`.
+template <int HD>
+__device__ __forceinline__ const char* chunk_src(const Params& P, const Instr& in, const DevLayer& Lw, uint32_t c,
+                                                 const int32_t* ctx) {
+    const uint32_t off = c * kChunk + (uint32_t)lane_id() * 16u;
+    switch (in.op) {
+        case OP_QKV: {
+            const uint32_t rb = (uint32_t)P.d * 2u;
+            uint32_t r = off / rb, col = off - r * rb;
+            if (r >= in.count) { r = 0; col = 0; }
+            const uint32_t row = in.begin + r, nq = (uint32_t)(P.Hq * HD), nk = (uint32_t)(P.Hkv * HD);
+            const uint16_t* base = row < nq ? Lw.wq + (size_t)row * P.d
+                                 : row < nq + nk ? Lw.wk + (size_t)(row - nq) * P.d
+                                                 : Lw.wv + (size_t)(row - nq - nk) * P.d;
+            return (const char*)base + col;
+        }
+        case OP_O: {
+            const uint32_t K = (uint32_t)(P.Hq * HD), rb = K * 2u;
+            uint32_t r = off / rb, col = off - r * rb;
+            if (r >= in.count) { r = 0; col = 0; }
+            return (const char*)(Lw.wo + (size_t)(in.begin + r) * K) + col;
+        }
+        case OP_GATEUP: {
+            const uint32_t rb = (uint32_t)P.d * 2u;
+            uint32_t j = off / rb, col = off - j * rb;
+            if (j >= 2u * in.count) { j = 0; col = 0; }
+            const uint16_t* W = (j & 1u) ? Lw.w_up : Lw.w_gate;
+            return (const char*)(W + (size_t)(in.begin + (j >> 1)) * P.d) + col;
+        }
+        case OP_DOWN: {
+            const uint32_t rb = (uint32_t)P.F * 2u;
+            uint32_t r = off / rb, col = off - r * rb;
+            if (r >= in.count) { r = 0; col = 0; }
+            return (const char*)(Lw.w_down + (size_t)(in.begin + r) * P.F) + col;
+        }
+        case OP_HEAD: {
+            const uint32_t rb = (uint32_t)P.d * 2u;
+            uint32_t r = off / rb, col = off - r * rb;
+            if (r >= in.count) { r = 0; col = 0; }
+            return (const char*)(P.head + (size_t)(in.begin + r) * P.d) + col;
+        }
+        case OP_ATTN: {
+            constexpr uint32_t rbkv = HD * 2u;
+            const int per_b = P.Hkv * P.nsplit;
+            const int b = (int)in.begin / per_b, g = ((int)in.begin % per_b) / P.nsplit, s = (int)in.begin % P.nsplit;
+            const SplitRange R = split_range<HD>(ctx[b], s, P.nsplit);
+            const uint32_t t = off >> 11, w = off & 2047u, inner = w & 1023u;
+            int pos = R.s0 + (int)(t * AttnGeom<HD>::PPW + inner / rbkv);
+            uint32_t col = inner % rbkv;
+            if (pos >= R.s0 + R.ncached) { pos = R.s0; col = 0; }
+            const uint16_t* cache = (w >= 1024u) ? P.vcache : P.kcache;
+            return (const char*)(cache + ((((size_t)in.layer * P.kv_b + b) * P.Hkv + g) * P.S + pos) * HD) + col;
+        }
+        default: return (const char*)P.embed;
+    }
+}
+
+__device__ __forceinline__ uint32_t min_consumed(const Ctl* ctl) {
+    uint32_t m = lds_ld(&ctl->consumed[0]);
+#pragma unroll
+    for (int w = 1; w < kComputeWaves; ++w) m = min(m, lds_ld(&ctl->consumed[w]));
+    return m;
+}
+
+// One 1 KB chunk HBM -> LDS: each lane moves 16 bytes from `src` to
+// lds_addr + 16 * lane.  Written as one asm block (M0 is set and consumed inside
+// it, the instruction has no destination register) so the compiler neither
+// counts it nor guards later LDS accesses with vmcnt waits: this wave's vmcnt is
+// managed explicitly by the loader.
+__device__ __forceinline__ void dma_chunk(const char* src, uint32_t lds_addr) {
+    asm volatile(
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src)
+        : "memory");
+}
+
+template <int HD>
+__device__ void loader_wave(const Params& P, Ctl* ctl, char* ring, uint32_t q0, uint32_t q1, const int32_t* ctx) {
+    const uint32_t ring_base = (uint32_t)(size_t)(lds_ptr_t)ring;
+    uint32_t issued = 0, landed = 0;
+    bool stop = false;
+    for (uint32_t i = q0; i < q1 && !stop; ++i) {
+        const Instr in = ld_const(P.instrs + i);
+        const uint32_t nch = instr_bytes<HD>(P, in, ctx) / kChunk;
+        if (nch == 0) continue;
+        const DevLayer Lw = ld_const(P.layers + (in.layer < P.L ? in.layer : 0));
+        for (uint32_t c = 0; c < nch; ++c) {
+            while (issued - min_consumed(ctl) >= kRingChunks) {
+                wait_vmcnt<0>();
+                landed = issued;
+                lds_st(&ctl->landed, landed);
+                if (lds_ld(&ctl->abort)) {
+                    stop = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (stop) break;
+            const char* src = chunk_src<HD>(P, in, Lw, c, ctx);
+            dma_chunk(src, ring_base + (issued % kRingChunks) * kChunk);
+            ++issued;
+            if (issued - landed > (uint32_t)kLoaderLag) {
+                wait_vmcnt<kLoaderLag>();
+                landed = issued - kLoaderLag;
+                lds_st(&ctl->landed, landed);
+            }
+        }
+    }
+    wait_vmcnt<0>();
+    lds_st(&ctl->landed, issued);
+}
+
+// ------------------------------------------------------------------------------------------------
+// compute waves
+// ------------------------------------------------------------------------------------------------
+__device__ __noinline__ void raise_error_impl(DevState* state, HostErr* herr, uint32_t* abort_flag, uint32_t code,
+                                             uint32_t a, uint32_t b) {
+    __hip_atomic_store(abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if ((threadIdx.x & 63) == 0) {
+        uint32_t expected = 0;
+        if (__hip_atomic_compare_exchange_strong(&state->error, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)) {
+            state->err_info[0] = a;
+            state->err_info[1] = b;
+            state->err_info[2] = blockIdx.x;
+            if (herr) {
+                __hip_atomic_store(&herr->info[0], a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                __hip_atomic_store(&herr->info[1], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                __hip_atomic_store(&herr->info[2], blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                __hip_atomic_store(&herr->code, code, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+        }
+    }
+}
+__device__ __forceinline__ void raise_error(const Params& P, Ctl* ctl, uint32_t code, uint32_t a, uint32_t b) {
+    raise_error_impl(P.state, P.host_err, &ctl->abort, code, a, b);
+}
+
+// Spin until *ctr >= target (wrapping compare), then acquire at agent scope.
+__device__ __forceinline__ bool wait_counter(const Params& P, Ctl* ctl, uint32_t* ctr, uint32_t target) {
+    uint32_t v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int32_t)(v - target) < 0) {
+        const uint64_t t0 = now_ticks();
+        uint32_t polls = 0;
+        for (;;) {
+            __builtin_amdgcn_s_sleep(1);
+            v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((int32_t)(v - target) >= 0) break;
+            if (lds_ld(&ctl->abort)) return false;
+            if ((++polls & 63u) == 0) {
+                if (__hip_atomic_load(&P.state->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+                    lds_st(&ctl->abort, 1u);
+                    return false;
+                }
+                if (now_ticks() - t0 > P.spin_ticks) {
+                    raise_error(P, ctl, DERR_TIMEOUT, target, v);
+                    return false;
+                }
+            }
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return true;
+}
+
+// Wait until the loader has `need` chunks resident.
+__device__ __forceinline__ bool wait_landed(const Params& P, Ctl* ctl, uint32_t need) {
+    if (lds_ld(&ctl->landed) >= need) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        return true;
+    }
+    const uint64_t t0 = now_ticks();
+    uint32_t polls = 0;
+    while (lds_ld(&ctl->landed) < need) {
+        if (lds_ld(&ctl->abort)) return false;
+        if ((++polls & 255u) == 0 && now_ticks() - t0 > P.spin_ticks) {
+            raise_error(P, ctl, DERR_TIMEOUT, 0xFFFFFFFFu, need);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(0);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    return true;
+}
+
+__device__ __forceinline__ void set_consumed(Ctl* ctl, int wave, uint32_t chunk) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    lds_st(&ctl->consumed[wave], chunk);
+}
+
+// Barrier of the compute waves only (the loader wave never joins s_barrier).
+struct CwBarrier {
+    Ctl* ctl;
+    const Params* P;
+    uint32_t* gen;
+    __device__ void operator()() const {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (lane_id() == 0) __hip_atomic_fetch_add(&ctl->bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const uint32_t target = (++*gen) * (uint32_t)kComputeWaves;
+        const uint64_t t0 = now_ticks();
+        uint32_t polls = 0;
+        while (lds_ld(&ctl->bar) < target) {
+            if (lds_ld(&ctl->abort)) break;
+            if ((++polls & 255u) == 0 && now_ticks() - t0 > P->spin_ticks) {
+                raise_error(*P, ctl, DERR_TIMEOUT, 0xFFFFFFFEu, target);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+};
+
+template <int B, int HD>
+__device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, uint16_t* xlds,
+                             float* attn_lds, int wave, uint32_t q0, uint32_t q1, const int32_t* ctx) {
+    const int lane = lane_id();
+    uint32_t S = 0, k = 0, bar_gen = 0;
+    float best_v[B];
+    int32_t best_i[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        best_v[b] = -INFINITY;
+        best_i[b] = 0x7FFFFFFF;
+    }
+    bool nan_seen = false;
+    for (uint32_t qi = q0; qi < q1; ++qi, ++k) {
+        const Instr in = ld_const(P.instrs + qi);
+        const uint32_t bytes = instr_bytes<HD>(P, in, ctx);
+        if (in.wait_ctr != kNoCounter) {
+            if (!wait_counter(P, ctl, P.counters + (size_t)in.wait_ctr * kCtrStride, A.epoch * in.wait_n)) return;
+        }
+        const int layer = in.layer;
+        const DevLayer Lw = ld_const(P.layers + (layer < P.L ? layer : 0));
+        bool ok = true;
+        switch (in.op) {
+            case OP_QKV:
+            case OP_GATEUP:
+            case OP_HEAD: {
+                const uint16_t* gain = in.op == OP_QKV ? Lw.attn_norm : in.op == OP_GATEUP ? Lw.mlp_norm : P.final_norm;
+                const bool from_embed = (in.op == OP_QKV && layer == 0);
+                rmsnorm_rows<B>(P.h, from_embed ? P.embed : nullptr, A.tok_in, A.tok_stride, P.V, gain, P.d, P.eps, xlds);
+                const uint32_t rb = (uint32_t)P.d * 2u;
+                const int np = P.d >> 3;
+                const RingRows rows{ring, S, rb};
+                const XLds x{xlds, (uint32_t)P.d};
+                if (in.op == OP_GATEUP) {
+                    for (uint32_t i = wave; i < in.count && ok; i += kComputeWaves) {
+                        const uint32_t off = S + 2u * i * rb;
+                        set_consumed(ctl, wave, off / kChunk);
+                        ok = wait_landed(P, ctl, (off + 2u * rb + kChunk - 1u) / kChunk);
+                        if (!ok) break;
+                        float zg[B], zu[B];
+                        row_dot<B>(rows, 2u * i, np, x, zg);
+                        row_dot<B>(rows, 2u * i + 1u, np, x, zu);
+                        const uint32_t f = in.begin + i;
+                        if (lane < B) {
+                            const float a = silu_mul(pick<B>(zg, lane), pick<B>(zu, lane));
+                            P.act[(size_t)lane * P.F + f] = (uint16_t)f_to_bf(a);
+                        }
+                    }
+                } else {
+                    for (uint32_t r = wave; r < in.count && ok; r += kComputeWaves) {
+                        const uint32_t off = S + r * rb;
+                        set_consumed(ctl, wave, off / kChunk);
+                        ok = wait_landed(P, ctl, (off + rb + kChunk - 1u) / kChunk);
+                        if (!ok) break;
+                        float acc[B];
+                        row_dot<B>(rows, r, np, x, acc);
+                        const uint32_t row = in.begin + r;
+                        if (in.op == OP_QKV) {
+                            if (lane < B) P.qkv[(size_t)lane * P.qkv_rows + row] = pick<B>(acc, lane);
+                        } else {
+#pragma unroll
+                            for (int b = 0; b < B; ++b) {
+                                if (acc[b] != acc[b]) nan_seen = true;
+                                if (head_better(acc[b], (int32_t)row, best_v[b], best_i[b])) {
+                                    best_v[b] = acc[b];
+                                    best_i[b] = (int32_t)row;
+                                }
+                            }
+                            if (lane < B) A.logits[(size_t)lane * P.V + row] = pick<B>(acc, lane);
+                        }
+                    }
+                }
+                break;
+            }
+            case OP_O:
+            case OP_DOWN: {
+                const uint32_t K = in.op == OP_O ? (uint32_t)(P.Hq * HD) : (uint32_t)P.F;
+                const uint32_t rb = K * 2u;
+                const int np = (int)(K >> 3);
+                const RingRows rows{ring, S, rb};
+                const XGlobal x{in.op == OP_O ? P.attn : P.act, K};
+                for (uint32_t r = wave; r < in.count && ok; r += kComputeWaves) {
+                    const uint32_t off = S + r * rb;
+                    set_consumed(ctl, wave, off / kChunk);
+                    ok = wait_landed(P, ctl, (off + rb + kChunk - 1u) / kChunk);
+                    if (!ok) break;
+                    float acc[B];
+                    row_dot<B>(rows, r, np, x, acc);
+                    const uint32_t row = in.begin + r;
+                    if (lane < B) {
+                        float* hp = P.h + (size_t)lane * P.d + row;
+                        const float resid = (in.op == OP_O && layer == 0)
+                                                ? bf_to_f(P.embed[token_row(A.tok_in, lane, A.tok_stride, P.V) * P.d + row])
+                                                : *hp;
+                        *hp = resid + pick<B>(acc, lane);
+                    }
+                }
+                break;
+            }
+            case OP_ATTN: {
+                const int per_b = P.Hkv * P.nsplit;
+                const int b = (int)in.begin / per_b, g = ((int)in.begin % per_b) / P.nsplit,
+                          s = (int)in.begin % P.nsplit;
+                const int p = ctx[b];
+                const RingKV kv{ring, S};
+                auto need = [&](int t) {
+                    const uint32_t off = S + (uint32_t)t * 2048u;
+                    set_consumed(ctl, wave, off / kChunk);
+                    if (!wait_landed(P, ctl, (off + 2048u) / kChunk)) ok = false;
+                };
+                const CwBarrier barrier{ctl, &P, &bar_gen};
+                bool merged = false;
+                attn_item<HD>(P, layer, b, g, s, p, kv, need, barrier, attn_lds, wave, kComputeWaves, P.attn_ticket,
+                              merged);
+                break;
+            }
+            default: break;
+        }
+        if (!ok || lds_ld(&ctl->abort)) return;
+        S += bytes;
+        set_consumed(ctl, wave, S / kChunk);
+        if (in.op == OP_HEAD && lane < B) {
+            HeadPart hp;
+            hp.v = pick<B>(best_v, lane);
+            int32_t bi = best_i[0];
+#pragma unroll
+            for (int b = 1; b < B; ++b)
+                if (lane == b) bi = best_i[b];
+            hp.i = bi;
+            P.head_part[((size_t)blockIdx.x * kComputeWaves + wave) * B + lane] = hp;
+        }
+        // the last wave of this CU to finish the instruction publishes it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        uint32_t old = 0;
+        if (lane == 0) old = __hip_atomic_fetch_add(&ctl->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+        old = __shfl(old, 0, 64);
+        if (old == (k + 1u) * (uint32_t)kComputeWaves - 1u && in.sig_ctr != kNoCounter) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            uint32_t prev = 0;
+            if (lane == 0)
+                prev = __hip_atomic_fetch_add(P.counters + (size_t)in.sig_ctr * kCtrStride, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+            prev = __shfl(prev, 0, 64);
+            if (in.op == OP_HEAD && prev + 1u == A.epoch * P.n_head_instr) {
+                // last CU: greedy choice over every partial, then advance the contexts
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                uint32_t nanf = 0;
+                reduce_head_parts(P.head_part, P.n_cu * kComputeWaves, B, A.tok_out, &nanf);
+                nanf = __shfl(nanf, 0, 64) | (uint32_t)__any(nanf != 0);
+                if (lane < B) P.state->ctx_len[lane] = ctx[lane] + 1;
+                if (nanf) raise_error(P, ctl, DERR_NAN, 0, 0);
+            }
+        }
+        if (in.op == OP_HEAD && nan_seen) raise_error(P, ctl, DERR_NAN, 1, blockIdx.x);
+    }
+}
+
+template <int B, int HD>
+__global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs A) {
+    __shared__ __attribute__((aligned(1024))) char ring[kRingBytes];
+    constexpr uint32_t kAttnBytes = kComputeWaves * kMaxGroup * (HD + 2) * 4;
+    __shared__ __attribute__((aligned(16))) char scratch[kXBytes > kAttnBytes ? kXBytes : kAttnBytes];
+    __shared__ Ctl ctl;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (threadIdx.x == 0) {
+        ctl.landed = 0;
+        for (int w = 0; w < kComputeWaves; ++w) ctl.consumed[w] = 0;
+        ctl.done = 0;
+        ctl.bar = 0;
+        ctl.abort = 0;
+    }
+    if (threadIdx.x < kMaxBatch) ctl.ctx[threadIdx.x] = (int)threadIdx.x < B ? P.state->ctx_len[threadIdx.x] : 0;
+    __syncthreads();
+    const uint32_t q0 = ld_const(P.queue_off + blockIdx.x), q1 = ld_const(P.queue_off + blockIdx.x + 1);
+    const int32_t* ctx = ctl.ctx;
+    if (wave == kComputeWaves) {
+        loader_wave<HD>(P, &ctl, ring, q0, q1, ctx);
+    } else {
+        compute_wave<B, HD>(P, A, &ctl, ring, (uint16_t*)scratch, (float*)scratch, wave, q0, q1, ctx);
+        if (lds_ld(&ctl.abort)) lds_st(&ctl.abort, 1u);
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// host-side launch
+// ------------------------------------------------------------------------------------------------
+template <int B, int HD>
+static hipError_t launch_t(const Params& P, const StepArgs& A, hipStream_t stream) {
+    void* args[] = {(void*)&P, (void*)&A};
+    return hipLaunchCooperativeKernel((const void*)mk_megakernel<B, HD>, dim3(P.n_cu), dim3(kThreads), args, 0,
+                                      stream);
+}
+
+hipError_t launch_megakernel(const Params& P, const StepArgs& A, hipStream_t stream) {
+    if (P.hd == 64) {
+        if (P.B == 1) return launch_t<1, 64>(P, A, stream);
+        if (P.B == 2) return launch_t<2, 64>(P, A, stream);
+    } else if (P.hd == 128) {
+        if (P.B == 1) return launch_t<1, 128>(P, A, stream);
+        if (P.B == 2) return launch_t<2, 128>(P, A, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+bool megakernel_supports(int B, int hd) { return (B == 1 || B == 2) && (hd == 64 || hd == 128); }
+
+}  // namespace mk

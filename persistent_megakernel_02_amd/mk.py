@@ -1,0 +1,276 @@
+"""Python binding of the C ABI in ``include/mk.h`` (argument marshalling only).
+
+Every function keeps the C name.  PyTorch provides device memory and streams:
+the weights, workspace, KV cache, token and logit buffers are torch tensors on
+the GPU whose pointers are handed to the library; every step of the decode path
+runs in the HIP kernels of ``libmk.so``.  There is no fallback: if the library
+is missing the import raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmk.so")
+
+MK_OK, MK_E_INVALID, MK_E_UNSUPPORTED, MK_E_CAPACITY, MK_E_HIP, MK_E_DEVICE_TIMEOUT, MK_E_STATE, MK_E_DEVICE_NAN = range(8)
+MK_MODE_MEGAKERNEL, MK_MODE_GRAPH = 0, 1
+
+EXPORTS = ["mk_query_sizes", "mk_create", "mk_kv_layout", "mk_prefill", "mk_set_context_len", "mk_decode_step",
+           "mk_get_context_len", "mk_reset", "mk_debug_inject", "mk_status_string", "mk_last_error",
+           "mk_plan_inspect", "mk_kernels_per_step", "mk_destroy", "mk_bench_stream_read", "mk_bench_copy"]
+
+
+class mk_model_config(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("tied_embeddings", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+                ("rope_theta", ctypes.c_double), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("n_shared_experts", ctypes.c_int32), ("expert_ffn", ctypes.c_int32)]
+
+
+class mk_layer_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up",
+                                               "w_down", "router", "e_gate", "e_up", "e_down", "s_gate", "s_up",
+                                               "s_down")]
+
+
+class mk_weights(ctypes.Structure):
+    _fields_ = [("tok_embedding", ctypes.c_void_p), ("lm_head", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(mk_layer_weights))]
+
+
+class mk_runtime_config(ctypes.Structure):
+    _fields_ = [("max_batch", ctypes.c_int32), ("max_seq", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("num_cus", ctypes.c_int32), ("gemv_kind", ctypes.c_int32), ("spin_timeout_ms", ctypes.c_uint32),
+                ("trace", ctypes.c_int32), ("attn_splits", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmk.so (built in-tree by ``__graft_entry__.build()``); raises if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.mk_query_sizes.argtypes = [ctypes.POINTER(mk_model_config), ctypes.POINTER(mk_runtime_config),
+                                     ctypes.POINTER(sz), ctypes.POINTER(sz)]
+        L.mk_create.argtypes = [ctypes.POINTER(mk_model_config), ctypes.POINTER(mk_weights),
+                                ctypes.POINTER(mk_runtime_config), vp, sz, vp, sz, vp, ctypes.POINTER(vp)]
+        L.mk_kv_layout.argtypes = [vp, ctypes.POINTER(ctypes.c_int64)]
+        L.mk_prefill.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+        L.mk_set_context_len.argtypes = [vp, ctypes.POINTER(i32), i32]
+        L.mk_get_context_len.argtypes = [vp, ctypes.POINTER(i32), i32]
+        L.mk_decode_step.argtypes = [vp, vp, i32, vp, vp, vp]
+        L.mk_reset.argtypes = [vp, vp]
+        L.mk_debug_inject.argtypes = [vp, i32, i32]
+        L.mk_status_string.argtypes = [ctypes.c_int]
+        L.mk_status_string.restype = ctypes.c_char_p
+        L.mk_last_error.argtypes = [vp]
+        L.mk_last_error.restype = ctypes.c_char_p
+        L.mk_plan_inspect.argtypes = [ctypes.POINTER(mk_model_config), ctypes.POINTER(mk_runtime_config), i32,
+                                      ctypes.POINTER(ctypes.c_int64), i32]
+        L.mk_kernels_per_step.argtypes = [vp]
+        L.mk_kernels_per_step.restype = i32
+        L.mk_destroy.argtypes = [vp]
+        L.mk_bench_stream_read.argtypes = [vp, sz, vp, vp]
+        L.mk_bench_copy.argtypes = [vp, vp, sz, vp]
+        for n in ("mk_query_sizes", "mk_create", "mk_kv_layout", "mk_prefill", "mk_set_context_len",
+                  "mk_get_context_len", "mk_decode_step", "mk_reset", "mk_debug_inject", "mk_plan_inspect",
+                  "mk_destroy", "mk_bench_stream_read", "mk_bench_copy"):
+            getattr(L, n).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+class MKError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        msg = lib().mk_status_string(status).decode()
+        super().__init__(f"{where}: {msg} ({status}){': ' + detail if detail else ''}")
+
+
+def model_config(cfg) -> mk_model_config:
+    """Marshal a ModelConfig-like object (see persistent_megakernel_02_amd.inputs)."""
+    c = mk_model_config()
+    c.n_layers, c.hidden, c.n_q_heads, c.n_kv_heads = cfg.n_layers, cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads
+    c.head_dim, c.ffn, c.vocab = cfg.head_dim, cfg.ffn, cfg.vocab
+    c.tied_embeddings = 1 if cfg.tied else 0
+    c.rms_eps = cfg.rms_eps
+    c.rope_theta = cfg.rope_theta
+    c.n_experts, c.top_k, c.n_shared_experts, c.expert_ffn = cfg.n_experts, cfg.top_k, cfg.n_shared, cfg.expert_ffn
+    return c
+
+
+def runtime_config(max_batch: int, max_seq: int, mode: int = MK_MODE_MEGAKERNEL, num_cus: int = 0,
+                   spin_timeout_ms: int = 0, attn_splits: int = 0) -> mk_runtime_config:
+    r = mk_runtime_config()
+    r.max_batch, r.max_seq, r.mode, r.num_cus = max_batch, max_seq, mode, num_cus
+    r.gemv_kind, r.spin_timeout_ms, r.trace, r.attn_splits = 0, spin_timeout_ms, 0, attn_splits
+    return r
+
+
+def mk_query_sizes(cfg: mk_model_config, rt: mk_runtime_config):
+    ws, kv = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = lib().mk_query_sizes(ctypes.byref(cfg), ctypes.byref(rt), ctypes.byref(ws), ctypes.byref(kv))
+    return st, ws.value, kv.value
+
+
+def mk_plan_inspect(cfg: mk_model_config, rt: mk_runtime_config, num_cus: int):
+    out = (ctypes.c_int64 * 8)()
+    st = lib().mk_plan_inspect(ctypes.byref(cfg), ctypes.byref(rt), num_cus, out, 8)
+    keys = ["cus", "instructions", "counters", "max_per_cu", "weight_bytes", "verify", "attn_splits", "phases"]
+    return st, dict(zip(keys, list(out)))
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+class Decoder:
+    """Owns the torch device buffers for one handle: weights, workspace, KV cache.
+
+    ``weights`` is an inputs.Weights (numpy bf16 bit patterns); they are copied to
+    the GPU once.  Tokens and logits stay on the GPU between steps.
+    """
+
+    def __init__(self, cfg, weights, max_batch: int, max_seq: int, mode: int = MK_MODE_MEGAKERNEL,
+                 device: str = "cuda:0", num_cus: int = 0, spin_timeout_ms: int = 0, attn_splits: int = 0,
+                 device_weights: Optional[Dict[str, object]] = None):
+        import torch
+
+        self.torch = torch
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.B = max_batch
+        self.max_seq = max_seq
+        self._c = model_config(cfg)
+        self._rt = runtime_config(max_batch, max_seq, mode, num_cus, spin_timeout_ms, attn_splits)
+        st, ws, kv = mk_query_sizes(self._c, self._rt)
+        if st != MK_OK:
+            raise MKError(st, "mk_query_sizes")
+        self._keep: List[object] = []
+        dw = device_weights if device_weights is not None else upload_weights(weights, self.device)
+        self.dw = dw
+        L = self.cfg.n_layers
+        layers = (mk_layer_weights * L)()
+        for l in range(L):
+            for n in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down"):
+                setattr(layers[l], n, dw["layers"][l][n].data_ptr())
+        self._layers = layers
+        w = mk_weights()
+        w.tok_embedding = dw["embed"].data_ptr()
+        w.lm_head = dw["lm_head"].data_ptr() if dw.get("lm_head") is not None else None
+        w.final_norm = dw["final_norm"].data_ptr()
+        w.layers = layers
+        self._w = w
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
+        self.kv = torch.empty(kv, dtype=torch.uint8, device=self.device)
+        self.stream = torch.cuda.current_stream(self.device)
+        h = ctypes.c_void_p()
+        st = lib().mk_create(ctypes.byref(self._c), ctypes.byref(w), ctypes.byref(self._rt), self.workspace.data_ptr(),
+                             ws, self.kv.data_ptr(), kv, self.stream.cuda_stream, ctypes.byref(h))
+        if st != MK_OK:
+            raise MKError(st, "mk_create")
+        self.h = h
+        self.tok = torch.zeros(max_batch, dtype=torch.int32, device=self.device)
+        self.logits = torch.empty((max_batch, cfg.vocab), dtype=torch.float32, device=self.device)
+
+    # -- ABI wrappers --------------------------------------------------------------------------
+    def _check(self, st: int, where: str):
+        if st != MK_OK:
+            raise MKError(st, where, lib().mk_last_error(self.h).decode())
+
+    def kv_layout(self):
+        s = (ctypes.c_int64 * 5)()
+        self._check(lib().mk_kv_layout(self.h, s), "mk_kv_layout")
+        return list(s)
+
+    def kv_views(self):
+        """(K, V) uint16 views [L][B][Hkv][S][hd] of the cache."""
+        t = self.torch
+        c = self.cfg
+        shape = (c.n_layers, self.B, c.n_kv_heads, self.max_seq, c.head_dim)
+        n = int(np.prod(shape))
+        flat = self.kv.view(t.int16)
+        return flat[:n].view(shape), flat[n:2 * n].view(shape)
+
+    def prefill(self, prompt_dev, logits_out=None, next_out=None):
+        """prompt_dev int32 [B, P] on the device -> (next tokens [B], logits [B, V]) device tensors."""
+        t = self.torch
+        B, P = prompt_dev.shape
+        logits_out = self.logits if logits_out is None else logits_out
+        next_out = self.tok if next_out is None else next_out
+        self._check(lib().mk_prefill(self.h, prompt_dev.data_ptr(), B, P, logits_out.data_ptr(), next_out.data_ptr(),
+                                     self.stream.cuda_stream), "mk_prefill")
+        return next_out, logits_out
+
+    def decode_step(self, tok_in, tok_out=None, logits_out=None):
+        tok_out = self.tok if tok_out is None else tok_out
+        logits_out = self.logits if logits_out is None else logits_out
+        self._check(lib().mk_decode_step(self.h, tok_in.data_ptr(), self.B, tok_out.data_ptr(), logits_out.data_ptr(),
+                                         self.stream.cuda_stream), "mk_decode_step")
+        return tok_out, logits_out
+
+    def set_context_len(self, lens: Sequence[int]):
+        arr = (ctypes.c_int32 * self.B)(*[int(x) for x in lens])
+        self._check(lib().mk_set_context_len(self.h, arr, self.B), "mk_set_context_len")
+
+    def context_len(self):
+        arr = (ctypes.c_int32 * self.B)()
+        self._check(lib().mk_get_context_len(self.h, arr, self.B), "mk_get_context_len")
+        return list(arr)
+
+    def reset(self):
+        self._check(lib().mk_reset(self.h, self.stream.cuda_stream), "mk_reset")
+
+    def debug_inject(self, fault: int, arg: int = 0):
+        self._check(lib().mk_debug_inject(self.h, fault, arg), "mk_debug_inject")
+
+    def kernels_per_step(self) -> int:
+        return int(lib().mk_kernels_per_step(self.h))
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().mk_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def upload_weights(weights, device) -> Dict[str, object]:
+    """Copy numpy bf16 bit patterns to device int16 tensors (same bytes)."""
+    import torch
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device, non_blocking=False)
+
+    out: Dict[str, object] = {"embed": dev(weights.embed), "final_norm": dev(weights.final_norm),
+                              "lm_head": dev(weights.lm_head) if weights.lm_head is not None else None, "layers": []}
+    for L in weights.layers:
+        out["layers"].append({k: dev(v) for k, v in L.items() if isinstance(v, np.ndarray)})
+    return out
+
+
+def bench_stream_read(src, sink, stream=None) -> int:
+    return lib().mk_bench_stream_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(),
+                                      _stream_ptr(stream))
+
+
+def bench_copy(dst, src, stream=None) -> int:
+    return lib().mk_bench_copy(dst.data_ptr(), src.data_ptr(), src.numel() * src.element_size(), _stream_ptr(stream))

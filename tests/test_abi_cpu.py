@@ -1,0 +1,116 @@
+"""Host-only checks of the C ABI: the library loads, exports every function the
+headers declare, validates shapes, and builds schedules that verify."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import persistent_megakernel_02_amd.inputs as I
+import persistent_megakernel_02_amd.mk as mk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in ("mk.h", "mk_bench.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[\w\s\*]+?\b(mk_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_function():
+    lib = mk.lib()
+    decl = declared_functions()
+    assert len(decl) >= 15
+    missing = [n for n in sorted(decl) if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(mk.EXPORTS) == decl
+
+
+def test_status_strings():
+    for s in range(8):
+        assert mk.lib().mk_status_string(s)
+    assert b"unknown" in mk.lib().mk_status_string(99)
+
+
+def rt(b=1, s=161, mode=mk.MK_MODE_MEGAKERNEL, cus=256, splits=0):
+    return mk.runtime_config(b, s, mode, cus, 0, splits)
+
+
+def test_query_sizes_kv_bytes_match_layout():
+    c = mk.model_config(I.LLAMA_1B)
+    st, ws, kv = mk.mk_query_sizes(c, rt(1, 160))
+    assert st == mk.MK_OK
+    assert kv == 2 * 16 * 1 * 8 * 160 * 64 * 2
+    assert 0 < ws < 64 << 20
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 96, mk.MK_E_UNSUPPORTED),
+    ("n_kv_heads", 5, mk.MK_E_UNSUPPORTED),
+    ("hidden", 300, mk.MK_E_UNSUPPORTED),
+    ("n_layers", 0, mk.MK_E_INVALID),
+    ("n_experts", 64, mk.MK_E_UNSUPPORTED),
+])
+def test_query_sizes_rejects_bad_shapes(field, value, status):
+    c = mk.model_config(I.LLAMA_1B)
+    setattr(c, field, value)
+    st, _, _ = mk.mk_query_sizes(c, rt())
+    assert st == status
+
+
+def test_runtime_validation():
+    c = mk.model_config(I.TINY)
+    assert mk.mk_query_sizes(c, rt(b=0))[0] == mk.MK_E_UNSUPPORTED
+    assert mk.mk_query_sizes(c, rt(b=9))[0] == mk.MK_E_UNSUPPORTED
+    assert mk.mk_query_sizes(c, rt(s=0))[0] == mk.MK_E_INVALID
+    bad = rt()
+    bad.mode = 7
+    assert mk.mk_query_sizes(c, bad)[0] == mk.MK_E_INVALID
+    bad = rt()
+    bad.trace = 1
+    assert mk.mk_query_sizes(c, bad)[0] == mk.MK_E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("cfg", [I.TINY, I.LLAMA_1B, I.LLAMA_8B], ids=lambda c: c.name)
+@pytest.mark.parametrize("cus", [256, 304, 80, 7, 1])
+@pytest.mark.parametrize("batch", [1, 2])
+def test_schedule_verifies(cfg, cus, batch):
+    st, info = mk.mk_plan_inspect(mk.model_config(cfg), rt(batch, 200), cus)
+    assert st == mk.MK_OK
+    assert info["verify"] == 0
+    assert info["phases"] == 5 * cfg.n_layers + 1
+    assert info["counters"] == 5 * cfg.n_layers + 2
+    assert info["weight_bytes"] == cfg.weight_bytes()
+    items = batch * cfg.n_kv_heads * info["attn_splits"]
+    assert info["instructions"] <= cfg.n_layers * (4 * cus + items) + cus
+
+
+def test_schedule_one_tile_per_cu_per_matrix():
+    st, info = mk.mk_plan_inspect(mk.model_config(I.LLAMA_1B), rt(1, 161), 256)
+    assert st == mk.MK_OK
+    # 16 layers x (QKV, O, gate/up, down) one tile on each CU, attention items, LM head
+    items = 8 * info["attn_splits"]
+    assert info["instructions"] == 16 * (4 * 256 + items) + 256
+    assert info["max_per_cu"] == 16 * 5 + 1
+
+
+def test_schedule_balances_bytes():
+    """Rows per CU differ by at most one in every matrix: no tail wave of
+    stragglers (512 blocks on 148 SMs leave 80 SMs idle in the last wave)."""
+    import math
+    blocks, sms = 512, 148
+    waves = math.ceil(blocks / sms)
+    assert waves == 4 and blocks - (waves - 1) * sms == 68 and sms - 68 == 80
+    for R in (3072, 2048, 8192, 128256):
+        per = [(R * (c + 1)) // 256 - (R * c) // 256 for c in range(256)]
+        assert max(per) - min(per) <= 1 and sum(per) == R
+
+
+def test_plan_inspect_rejects_bad_cu_count():
+    assert mk.mk_plan_inspect(mk.model_config(I.TINY), rt(), 0)[0] == mk.MK_E_INVALID
+    assert mk.mk_plan_inspect(mk.model_config(I.TINY), rt(), 5000)[0] == mk.MK_E_INVALID
