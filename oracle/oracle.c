@@ -29,23 +29,22 @@ uint16_t orc_bf16_bits(float x) {
     return (uint16_t)(u >> 16);
 }
 
-static inline float round_bf(float x) { return bf_to_f(orc_bf16_bits(x)); }
-
 int32_t orc_threads(void) { return (int32_t)omp_get_max_threads(); }
 
-/* dot(w, x) = sum_i w_i x_i, accumulated in double in index order, rounded once to fp32. */
+/* dot(w, x) = sum_i w_i x_i (bf16 weights, fp32 activations), accumulated in
+ * double in index order (every product is exact in double), rounded once to fp32. */
 float orc_dot(const uint16_t* w, const float* x, int32_t n) {
     double s = 0.0;
     for (int32_t i = 0; i < n; ++i) s += (double)bf_to_f(w[i]) * (double)x[i];
     return (float)s;
 }
 
-/* RMSNorm: x_i = bf16(fp32(h_i * g_i / sqrt(mean(h^2) + eps))), statistics in double. */
+/* RMSNorm: x_i = fp32(h_i * g_i / sqrt(mean(h^2) + eps)), statistics in double. */
 void orc_rmsnorm(const float* h, const uint16_t* g, int32_t d, double eps, float* x) {
     double ss = 0.0;
     for (int32_t i = 0; i < d; ++i) ss += (double)h[i] * (double)h[i];
     double r = 1.0 / sqrt(ss / (double)d + eps);
-    for (int32_t i = 0; i < d; ++i) x[i] = round_bf((float)((double)h[i] * r * (double)bf_to_f(g[i])));
+    for (int32_t i = 0; i < d; ++i) x[i] = (float)((double)h[i] * r * (double)bf_to_f(g[i]));
 }
 
 /* Rotary embedding, rotate-half pairing: for i < hd/2 the pair (v_i, v_{i+hd/2})
@@ -91,11 +90,11 @@ void orc_attend(const float* q, const uint16_t* K, const uint16_t* V, int64_t st
     free(e);
 }
 
-/* SwiGLU product: bf16(fp32(silu(z) * u)), silu(z) = z / (1 + e^-z) in double. */
+/* SwiGLU product: fp32(silu(z) * u), silu(z) = z / (1 + e^-z) in double. */
 float orc_swiglu(float z, float u) {
     double zz = z;
     double silu = zz / (1.0 + exp(-zz));
-    return round_bf((float)(silu * (double)u));
+    return (float)(silu * (double)u);
 }
 
 /* Greedy choice: the lowest index attaining the maximum; -1 if any entry is NaN. */
@@ -263,9 +262,7 @@ int orc_step(const orc_cfg* c, const orc_weights* w, orc_cache* kv, int32_t B, c
         gemv(lw->wv, Hkv * hd, d, x, d, B, v, Hkv * hd);
         for (int32_t b = 0; b < B; ++b) {
             for (int32_t hh = 0; hh < Hq; ++hh) {
-                float* qh = q + ((int64_t)b * Hq + hh) * hd;
-                orc_rope(qh, hd, pos[b], c->rope_theta);
-                for (int32_t i = 0; i < hd; ++i) qh[i] = round_bf(qh[i]);
+                orc_rope(q + ((int64_t)b * Hq + hh) * hd, hd, pos[b], c->rope_theta);
             }
             for (int32_t g = 0; g < Hkv; ++g) {
                 float* kg = k + ((int64_t)b * Hkv + g) * hd;
@@ -283,9 +280,8 @@ int orc_step(const orc_cfg* c, const orc_weights* w, orc_cache* kv, int32_t B, c
             for (int32_t hh = 0; hh < Hq; ++hh) {
                 int32_t g = hh / group;
                 int64_t base = (((int64_t)l * kv->batch + b) * Hkv + g) * S * hd;
-                float* oh = o + ((int64_t)b * Hq + hh) * hd;
-                orc_attend(q + ((int64_t)b * Hq + hh) * hd, kv->k + base, kv->v + base, hd, pos[b] + 1, hd, oh);
-                for (int32_t i = 0; i < hd; ++i) oh[i] = round_bf(oh[i]);
+                orc_attend(q + ((int64_t)b * Hq + hh) * hd, kv->k + base, kv->v + base, hd, pos[b] + 1, hd,
+                           o + ((int64_t)b * Hq + hh) * hd);
             }
         gemv(lw->wo, d, Hq * hd, o, Hq * hd, B, ao, d);
         for (int64_t i = 0; i < (int64_t)B * d; ++i) h[i] = (float)((double)h[i] + (double)ao[i]);
@@ -322,9 +318,7 @@ int orc_sequence(const orc_cfg* c, const orc_weights* w, const int32_t* tokens, 
         gemv(lw->wv, kvw, d, x, d, n, v, kvw);
         for (int32_t t = 0; t < n; ++t) {
             for (int32_t hh = 0; hh < Hq; ++hh) {
-                float* qh = q + ((int64_t)t * Hq + hh) * hd;
-                orc_rope(qh, hd, t, c->rope_theta);
-                for (int32_t i = 0; i < hd; ++i) qh[i] = round_bf(qh[i]);
+                orc_rope(q + ((int64_t)t * Hq + hh) * hd, hd, t, c->rope_theta);
             }
             for (int32_t g = 0; g < Hkv; ++g) orc_rope(k + (int64_t)t * kvw + (int64_t)g * hd, hd, t, c->rope_theta);
             for (int32_t i = 0; i < kvw; ++i) {
@@ -337,10 +331,8 @@ int orc_sequence(const orc_cfg* c, const orc_weights* w, const int32_t* tokens, 
         for (int32_t t = 0; t < n; ++t)
             for (int32_t hh = 0; hh < Hq; ++hh) {
                 int32_t g = hh / group;
-                float* oh = o + ((int64_t)t * Hq + hh) * hd;
                 orc_attend(q + ((int64_t)t * Hq + hh) * hd, Kl + (int64_t)g * hd, Vl + (int64_t)g * hd, kvw, t + 1, hd,
-                           oh);
-                for (int32_t i = 0; i < hd; ++i) oh[i] = round_bf(oh[i]);
+                           o + ((int64_t)t * Hq + hh) * hd);
             }
         gemv(lw->wo, d, Hq * hd, o, Hq * hd, n, ao, d);
         for (int64_t i = 0; i < (int64_t)n * d; ++i) h[i] = (float)((double)h[i] + (double)ao[i]);

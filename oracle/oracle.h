@@ -13,10 +13,11 @@
  * RoFormer), grouped-query attention (Ainslie et al. 2023), SwiGLU (Shazeer
  * 2020), top-k softmax routing for the MoE variant (Shazeer et al. 2017).
  *
- * Precision contract: every dot product accumulates in double in index order and
- * is rounded once to fp32; bf16 rounding (nearest even) happens at exactly these
- * points: normed activations, q after RoPE, the K/V cache, the attention output,
- * the SwiGLU product, the final normed activation.  Logits are fp32.
+ * Precision contract: weights and the KV cache are bf16 (round to nearest even
+ * when K and V are stored); every activation is fp32; every dot product
+ * accumulates in double in index order and is rounded once to fp32; norm
+ * statistics, RoPE rotations, softmax and SiLU are evaluated in double and
+ * rounded to fp32.  Logits are fp32.
  */
 #ifndef MK_ORACLE_H
 #define MK_ORACLE_H
