@@ -44,7 +44,7 @@ struct PairRows {  // stream row 2i = gate row, 2i + 1 = up row of f = begin + i
 
 template <int B>
 __global__ void __launch_bounds__(kConvThreads) k_qkv(Params P, StepArgs A, int layer) {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[kXBytes / 2];
+    __shared__ __attribute__((aligned(16))) float xs[kXBytes / 4];
     const int wave = threadIdx.x >> 6, lane = lane_id();
     const DevLayer Lw = P.layers[layer];
     rmsnorm_rows<B>(P.h, layer == 0 ? P.embed : nullptr, A.tok_in, A.tok_stride, P.V, Lw.attn_norm, P.d, P.eps, xs);
@@ -61,7 +61,7 @@ __global__ void __launch_bounds__(kConvThreads) k_qkv(Params P, StepArgs A, int 
 
 template <int B>
 __global__ void __launch_bounds__(kConvThreads) k_gateup(Params P, StepArgs A, int layer) {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[kXBytes / 2];
+    __shared__ __attribute__((aligned(16))) float xs[kXBytes / 4];
     const int wave = threadIdx.x >> 6, lane = lane_id();
     const DevLayer Lw = P.layers[layer];
     rmsnorm_rows<B>(P.h, nullptr, A.tok_in, A.tok_stride, P.V, Lw.mlp_norm, P.d, P.eps, xs);
@@ -75,7 +75,7 @@ __global__ void __launch_bounds__(kConvThreads) k_gateup(Params P, StepArgs A, i
         row_dot<B>(rows, 2u * i + 1u, P.d >> 3, x, zu);
         if (lane < B) {
             const float a = silu_mul(pick<B>(zg, lane), pick<B>(zu, lane));
-            P.act[(size_t)lane * P.F + begin + i] = (uint16_t)f_to_bf(a);
+            P.act[(size_t)lane * P.F + begin + i] = a;
         }
     }
 }
@@ -125,7 +125,7 @@ __global__ void __launch_bounds__(kConvThreads) k_attn(Params P, StepArgs A, int
 // and advances the context lengths.
 template <int B>
 __global__ void __launch_bounds__(kConvThreads) k_head(Params P, StepArgs A, uint32_t* ticket) {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[kXBytes / 2];
+    __shared__ __attribute__((aligned(16))) float xs[kXBytes / 4];
     const int wave = threadIdx.x >> 6, lane = lane_id();
     rmsnorm_rows<B>(P.h, nullptr, A.tok_in, A.tok_stride, P.V, P.final_norm, P.d, P.eps, xs);
     const uint32_t begin = blockIdx.x * kRowsPerBlock;

@@ -75,7 +75,7 @@ mk_status validate(const mk_model_config* c, const mk_runtime_config* rt, std::s
     if (rt->max_batch < 1 || rt->max_batch > kMaxBatch) return fail(MK_E_UNSUPPORTED, "max_batch must be 1..8");
     if (!megakernel_supports(rt->max_batch, c->head_dim))
         return fail(MK_E_UNSUPPORTED, "this build runs batch 1 and 2");
-    if ((size_t)rt->max_batch * c->hidden * 2 > kXBytes) return fail(MK_E_UNSUPPORTED, "batch x hidden too large");
+    if ((size_t)rt->max_batch * c->hidden * 4 > kXBytes) return fail(MK_E_UNSUPPORTED, "batch x hidden too large");
     if (rt->max_seq < 1 || rt->max_seq > (1 << 20)) return fail(MK_E_INVALID, "max_seq out of range");
     if (rt->mode != MK_MODE_MEGAKERNEL && rt->mode != MK_MODE_GRAPH) return fail(MK_E_INVALID, "unknown mode");
     if (rt->num_cus < 0 || rt->num_cus > kMaxCus) return fail(MK_E_INVALID, "num_cus out of range");
@@ -245,8 +245,8 @@ Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, i
     lo.rope = take((size_t)rt->max_seq * (hd / 2) * 8);
     lo.h = take(B * d * 4);
     lo.qkv = take(B * qkv_rows * 4);
-    lo.attn = take(B * c->n_q_heads * hd * 2);
-    lo.act = take(B * c->ffn * 2);
+    lo.attn = take(B * c->n_q_heads * hd * 4);
+    lo.act = take(B * c->ffn * 4);
     lo.attn_part = take(B * c->n_kv_heads * nsplit * G * (hd + 2) * 4);
     const size_t conv_blocks = ((size_t)c->vocab + 15) / 16;
     lo.head_slots = std::max((size_t)n_cu, conv_blocks) * kComputeWaves;
@@ -450,8 +450,8 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
     P.rope = (const float2*)(ws + lo.rope);
     P.h = (float*)(ws + lo.h);
     P.qkv = (float*)(ws + lo.qkv);
-    P.attn = (uint16_t*)(ws + lo.attn);
-    P.act = (uint16_t*)(ws + lo.act);
+    P.attn = (float*)(ws + lo.attn);
+    P.act = (float*)(ws + lo.act);
     P.attn_part = (float*)(ws + lo.attn_part);
     P.attn_ticket = (uint32_t*)(ws + lo.tickets);
     P.head_part = (HeadPart*)(ws + lo.head_part);

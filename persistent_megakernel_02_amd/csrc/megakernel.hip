@@ -292,7 +292,7 @@ struct CwBarrier {
 };
 
 template <int B, int HD>
-__device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, uint16_t* xlds,
+__device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xlds,
                              float* attn_lds, int wave, uint32_t q0, uint32_t q1, const int32_t* ctx) {
     const int lane = lane_id();
     uint32_t S = 0, k = 0, bar_gen = 0;
@@ -336,7 +336,7 @@ __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const
                         const uint32_t f = in.begin + i;
                         if (lane < B) {
                             const float a = silu_mul(pick<B>(zg, lane), pick<B>(zu, lane));
-                            P.act[(size_t)lane * P.F + f] = (uint16_t)f_to_bf(a);
+                            P.act[(size_t)lane * P.F + f] = a;
                         }
                     }
                 } else {
@@ -469,7 +469,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
     if (wave == kComputeWaves) {
         loader_wave<HD>(P, &ctl, ring, q0, q1, ctx);
     } else {
-        compute_wave<B, HD>(P, A, &ctl, ring, (uint16_t*)scratch, (float*)scratch, wave, q0, q1, ctx);
+        compute_wave<B, HD>(P, A, &ctl, ring, (float*)scratch, (float*)scratch, wave, q0, q1, ctx);
         if (lds_ld(&ctl.abort)) lds_st(&ctl.abort, 1u);
     }
 }

@@ -8,9 +8,9 @@
 // QKV projection and RoPE; attention; the MLP).  The textbook definitions they
 // follow: RMSNorm (Zhang and Sennrich 2019), rotary embedding with rotate-half
 // pairs (Su et al.), grouped-query attention (Ainslie et al. 2023), SwiGLU
-// (Shazeer 2020).  Rounding points: normed activations, q after RoPE, the K/V
-// cache, the attention output and the SwiGLU product are bf16; every product of
-// a matrix and a vector accumulates in fp32; the residual stream is fp32.
+// (Shazeer 2020).  Precision: weights and the K/V cache are bf16; every
+// activation (normed x, q, attention output, SwiGLU product, residual) is fp32;
+// every product of a matrix and a vector accumulates in fp32.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -52,12 +52,17 @@ __device__ __forceinline__ uint32_t f_to_bf(float f) {
 __device__ __forceinline__ float round_bf(float f) { return __uint_as_float(f_to_bf(f) << 16); }
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f_to_bf(lo) | (f_to_bf(hi) << 16); }
 
-// acc + sum of the 8 bf16 products of w and x, in a fixed order (4 packed dots).
-__device__ __forceinline__ float dot8(uint4 w, uint4 x, float acc) {
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, x.x), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, x.y), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), __builtin_bit_cast(bf16x2_t, x.z), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, x.w), acc, false);
+// acc + sum over the 8 bf16 weights of w times the 8 fp32 activations (xa, xb),
+// one fused multiply-add each, in a fixed order.
+__device__ __forceinline__ float dot8(uint4 w, float4 xa, float4 xb, float acc) {
+    acc = fmaf(bf_lo(w.x), xa.x, acc);
+    acc = fmaf(bf_hi(w.x), xa.y, acc);
+    acc = fmaf(bf_lo(w.y), xa.z, acc);
+    acc = fmaf(bf_hi(w.y), xa.w, acc);
+    acc = fmaf(bf_lo(w.z), xb.x, acc);
+    acc = fmaf(bf_hi(w.z), xb.y, acc);
+    acc = fmaf(bf_lo(w.w), xb.z, acc);
+    acc = fmaf(bf_hi(w.w), xb.w, acc);
     return acc;
 }
 
@@ -87,7 +92,7 @@ __device__ __forceinline__ size_t token_row(const int32_t* tok, int b, int strid
 }
 
 // ---------------------------------------------------------------------------------------------
-// RMSNorm of B residual rows into bf16 activations (x_i = bf16(h_i * g_i / rms(h))).
+// RMSNorm of B residual rows into fp32 activations (x_i = h_i * g_i / rms(h)).
 // Lane l handles 8-element pieces p = l + 64 j: it writes exactly the pieces it
 // later reads in row_dot, so no other lane or wave depends on its stores.
 // `src_bf16` != nullptr selects embedding rows (layer 0) instead of `h`.
@@ -95,7 +100,7 @@ __device__ __forceinline__ size_t token_row(const int32_t* tok, int b, int strid
 template <int B>
 __device__ void rmsnorm_rows(const float* __restrict__ h, const uint16_t* __restrict__ emb,
                              const int32_t* __restrict__ tok, int32_t tok_stride, int V, const uint16_t* __restrict__ g,
-                             int d, float eps, uint16_t* __restrict__ xout) {
+                             int d, float eps, float* __restrict__ xout) {
     const int lane = lane_id();
     const int np = d >> 3;
 #pragma unroll
@@ -131,12 +136,10 @@ __device__ void rmsnorm_rows(const float* __restrict__ h, const uint16_t* __rest
             uint4 gv = *(const uint4*)(g + 8 * p);
             float gg[8] = {bf_lo(gv.x), bf_hi(gv.x), bf_lo(gv.y), bf_hi(gv.y),
                            bf_lo(gv.z), bf_hi(gv.z), bf_lo(gv.w), bf_hi(gv.w)};
-            uint4 o;
-            o.x = pack_bf2(v[0] * r * gg[0], v[1] * r * gg[1]);
-            o.y = pack_bf2(v[2] * r * gg[2], v[3] * r * gg[3]);
-            o.z = pack_bf2(v[4] * r * gg[4], v[5] * r * gg[5]);
-            o.w = pack_bf2(v[6] * r * gg[6], v[7] * r * gg[7]);
-            *(uint4*)(xout + (size_t)b * d + 8 * p) = o;
+            float4 o0 = make_float4(v[0] * r * gg[0], v[1] * r * gg[1], v[2] * r * gg[2], v[3] * r * gg[3]);
+            float4 o1 = make_float4(v[4] * r * gg[4], v[5] * r * gg[5], v[6] * r * gg[6], v[7] * r * gg[7]);
+            *(float4*)(xout + (size_t)b * d + 8 * p) = o0;
+            *(float4*)(xout + (size_t)b * d + 8 * p + 4) = o1;
         }
     }
 }
@@ -152,17 +155,23 @@ struct RingRows {  // rows laid back to back in the LDS ring from stream offset 
     }
 };
 
-// Activation sources: piece p of batch row b.
+// Activation sources (fp32): the 8 values of piece p of batch row b.
 struct XLds {
-    const uint16_t* x;
+    const float* x;
     uint32_t k;
-    __device__ __forceinline__ uint4 piece(int b, uint32_t p) const { return *(const uint4*)(x + (size_t)b * k + 8 * p); }
+    __device__ __forceinline__ void piece(int b, uint32_t p, float4& a, float4& c) const {
+        const float* q = x + (size_t)b * k + 8 * p;
+        a = *(const float4*)q;
+        c = *(const float4*)(q + 4);
+    }
 };
 struct XGlobal {
-    const uint16_t* x;
+    const float* x;
     uint32_t stride;
-    __device__ __forceinline__ uint4 piece(int b, uint32_t p) const {
-        return *(const uint4*)(x + (size_t)b * stride + 8 * p);
+    __device__ __forceinline__ void piece(int b, uint32_t p, float4& a, float4& c) const {
+        const float* q = x + (size_t)b * stride + 8 * p;
+        a = *(const float4*)q;
+        c = *(const float4*)(q + 4);
     }
 };
 
@@ -175,21 +184,24 @@ __device__ __forceinline__ void row_dot(const Rows& rows, uint32_t r, int np, co
     for (int b = 0; b < B; ++b) acc[b] = 0.f;
     int p = lane;
     for (; p + 192 < np; p += 256) {
-        uint4 w0 = rows.piece(r, p), w1 = rows.piece(r, p + 64), w2 = rows.piece(r, p + 128),
-              w3 = rows.piece(r, p + 192);
+        uint4 w[4] = {rows.piece(r, p), rows.piece(r, p + 64), rows.piece(r, p + 128), rows.piece(r, p + 192)};
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            uint4 x0 = x.piece(b, p), x1 = x.piece(b, p + 64), x2 = x.piece(b, p + 128), x3 = x.piece(b, p + 192);
-            acc[b] = dot8(w0, x0, acc[b]);
-            acc[b] = dot8(w1, x1, acc[b]);
-            acc[b] = dot8(w2, x2, acc[b]);
-            acc[b] = dot8(w3, x3, acc[b]);
+            float4 xa[4], xb[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x.piece(b, p + 64 * u, xa[u], xb[u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[b] = dot8(w[u], xa[u], xb[u], acc[b]);
         }
     }
     for (; p < np; p += 64) {
-        uint4 w0 = rows.piece(r, p);
+        const uint4 w0 = rows.piece(r, p);
 #pragma unroll
-        for (int b = 0; b < B; ++b) acc[b] = dot8(w0, x.piece(b, p), acc[b]);
+        for (int b = 0; b < B; ++b) {
+            float4 xa, xb;
+            x.piece(b, p, xa, xb);
+            acc[b] = dot8(w0, xa, xb, acc[b]);
+        }
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = wave_sum(acc[b]);
@@ -205,6 +217,20 @@ __device__ __forceinline__ float pick(const float (&a)[B], int i) {
 }
 
 __device__ __forceinline__ float silu_mul(float z, float u) { return z / (1.0f + expf(-z)) * u; }
+
+// q . k over 8 dims: fp32 query, bf16 key.
+__device__ __forceinline__ float qk8(const float* q, uint4 k) {
+    float a = 0.f;
+    a = fmaf(q[0], bf_lo(k.x), a);
+    a = fmaf(q[1], bf_hi(k.x), a);
+    a = fmaf(q[2], bf_lo(k.y), a);
+    a = fmaf(q[3], bf_hi(k.y), a);
+    a = fmaf(q[4], bf_lo(k.z), a);
+    a = fmaf(q[5], bf_hi(k.z), a);
+    a = fmaf(q[6], bf_lo(k.w), a);
+    a = fmaf(q[7], bf_hi(k.w), a);
+    return a;
+}
 
 // Running greedy choice: larger value wins, ties to the lower index.
 __device__ __forceinline__ bool head_better(float v, int32_t i, float bv, int32_t bi) {
@@ -320,15 +346,11 @@ __device__ void attn_item(const Params& P, int layer, int b, int g, int s, int p
     const float2* rope_row = P.rope + (size_t)p * (HD / 2);
     const float* qkv_b = P.qkv + (size_t)b * P.qkv_rows;
 
-    // q heads of the group: RoPE, bf16, packed for the dot
-    uint4 q[kMaxGroup];
+    // q heads of the group after RoPE (fp32)
+    float q[kMaxGroup][8];
 #pragma unroll
     for (int j = 0; j < kMaxGroup; ++j) {
-        if (j < G) {
-            float o[8];
-            rope8<HD>(qkv_b + (size_t)(g * G + j) * HD, rope_row, dl, o);
-            q[j] = make_uint4(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]), pack_bf2(o[4], o[5]), pack_bf2(o[6], o[7]));
-        }
+        if (j < G) rope8<HD>(qkv_b + (size_t)(g * G + j) * HD, rope_row, dl, q[j]);
     }
     float m[kMaxGroup], l[kMaxGroup], acc[kMaxGroup][8];
 #pragma unroll
@@ -344,7 +366,7 @@ __device__ void attn_item(const Params& P, int layer, int b, int g, int s, int p
 #pragma unroll
         for (int j = 0; j < kMaxGroup; ++j) {
             if (j < G) {
-                float sc = dot8(q[j], kp, 0.f);
+                float sc = qk8(q[j], kp);
                 sc = group_sum(sc, Geo::LPP) * scale;
                 if (valid) {
                     const float mn = fmaxf(m[j], sc);
@@ -434,16 +456,16 @@ __device__ void attn_item(const Params& P, int layer, int b, int g, int s, int p
             }
         }
     }
-    uint16_t* out_b = P.attn + (size_t)b * P.Hq * HD;
+    float* out_b = P.attn + (size_t)b * P.Hq * HD;
     if (P.nsplit == 1) {
         if (ps == 0) {
 #pragma unroll
             for (int j = 0; j < kMaxGroup; ++j) {
                 if (j < G) {
                     const float inv = 1.0f / l[j];
-                    uint4 o = make_uint4(pack_bf2(acc[j][0] * inv, acc[j][1] * inv), pack_bf2(acc[j][2] * inv, acc[j][3] * inv),
-                                         pack_bf2(acc[j][4] * inv, acc[j][5] * inv), pack_bf2(acc[j][6] * inv, acc[j][7] * inv));
-                    *(uint4*)(out_b + (size_t)(g * G + j) * HD + dl) = o;
+                    float* o = out_b + (size_t)(g * G + j) * HD + dl;
+                    *(float4*)o = make_float4(acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv);
+                    *(float4*)(o + 4) = make_float4(acc[j][4] * inv, acc[j][5] * inv, acc[j][6] * inv, acc[j][7] * inv);
                 }
             }
         }
@@ -490,9 +512,9 @@ __device__ void attn_item(const Params& P, int layer, int b, int g, int s, int p
                     lse_merge(mm, ll, aa, src[0], src[1], a2);
                 }
                 const float inv = 1.0f / ll;
-                uint4 o = make_uint4(pack_bf2(aa[0] * inv, aa[1] * inv), pack_bf2(aa[2] * inv, aa[3] * inv),
-                                     pack_bf2(aa[4] * inv, aa[5] * inv), pack_bf2(aa[6] * inv, aa[7] * inv));
-                *(uint4*)(out_b + (size_t)(g * G + j) * HD + dl) = o;
+                float* o = out_b + (size_t)(g * G + j) * HD + dl;
+                *(float4*)o = make_float4(aa[0] * inv, aa[1] * inv, aa[2] * inv, aa[3] * inv);
+                *(float4*)(o + 4) = make_float4(aa[4] * inv, aa[5] * inv, aa[6] * inv, aa[7] * inv);
             }
         }
     }

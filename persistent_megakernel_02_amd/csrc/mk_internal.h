@@ -17,7 +17,7 @@ constexpr uint32_t kChunk = 1024;                       // one loader issue: 64 
 constexpr uint32_t kRingBytes = 128 * 1024;             // LDS pages of the weight stream
 constexpr uint32_t kRingChunks = kRingBytes / kChunk;
 constexpr int kLoaderLag = 48;                          // loader chunks in flight (vmcnt <= 63)
-constexpr uint32_t kXBytes = 16 * 1024;                 // LDS for the normed activations
+constexpr uint32_t kXBytes = 16 * 1024;                 // LDS for the normed activations (fp32)
 constexpr int kMaxBatch = 8;
 constexpr int kMaxGroup = 4;                            // q heads per KV head
 constexpr uint32_t kCtrStride = 32;                     // uint32 per counter (128 B apart)
@@ -84,8 +84,8 @@ struct Params {
     // activations
     float* h;            // [B][d] residual stream
     float* qkv;          // [B][qkv_rows] raw projections
-    uint16_t* attn;      // [B][Hq*hd] bf16 attention output
-    uint16_t* act;       // [B][F] bf16 SwiGLU output
+    float* attn;         // [B][Hq*hd] attention output
+    float* act;          // [B][F] SwiGLU output
     float* attn_part;    // [B][Hkv][nsplit][G][hd + 2] split partials (m, l, o)
     uint32_t* attn_ticket;  // [L][B][Hkv] * kCtrStride, reset by the merger
     HeadPart* head_part; // [n_cu * kComputeWaves][B]

@@ -178,3 +178,18 @@ def test_llama1b_b1_full_horizon(llama1b):
     worst, near = compare(rt_, rl, gt, gl, "1B b1 megakernel")
     assert near <= 2
     d.close()
+
+
+def test_llama1b_b1_graph_matches_megakernel_bitwise(llama1b):
+    """The one-kernel-per-op path on the headline shape gives the megakernel's
+    logits and tokens bit for bit (same tile functions, same order)."""
+    w, prompt = llama1b
+    toks = I.make_prompt(I.LLAMA_1B, 1, 24, seed=5)
+    outs = []
+    for mode in (0, 1):
+        print(f"case 1B b1 mode={mode} bitwise", flush=True)
+        d = _decoder(I.LLAMA_1B, w, 1, 64, mode)
+        outs.append(gpu_run(d, prompt, [toks[:, t] for t in range(24)], 24))
+        d.close()
+    for x, y in zip(outs[0][1], outs[1][1]):
+        assert np.array_equal(x, y)
