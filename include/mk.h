@@ -98,7 +98,7 @@ typedef struct {
     int32_t num_cus;          /* 0 = every compute unit of the device */
     int32_t gemv_kind;        /* 0 auto, 1 VALU dot (the only kind in this version) */
     uint32_t spin_timeout_ms; /* watchdog of every device spin-wait; 0 = 2000 ms */
-    int32_t trace;            /* reserved, must be 0 */
+    int32_t trace;            /* 1: record a per-instruction timeline (mk_read_trace) */
     int32_t attn_splits;      /* KV splits per (sequence, KV head); 0 = automatic */
 } mk_runtime_config;
 
@@ -162,6 +162,14 @@ const char* mk_last_error(const mk_handle* h);
  * (0 = ok), [6] attention splits, [7] phases. */
 mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* rt, int32_t num_cus, int64_t* out,
                           int32_t cap);
+
+/* Copy the device timeline of the last megakernel step (needs trace = 1).
+ * Per compute unit `records_per_cu` records of 8 uint32: {op | layer << 16,
+ * dependency-wait start, wait end, compute end, signal end, loader issue end,
+ * 0, 0}, times = low 32 bits of the 100 MHz s_memrealtime clock, in queue
+ * order.  With h_buf == NULL only *written (the byte size) is set.  Synchronises
+ * the handle's creation stream. */
+mk_status mk_read_trace(mk_handle* h, void* h_buf, size_t bytes, size_t* written, int32_t* records_per_cu);
 
 /* Number of kernel launches one decode step makes in the handle's mode. */
 int32_t mk_kernels_per_step(const mk_handle* h);

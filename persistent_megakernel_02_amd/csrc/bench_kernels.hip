@@ -59,3 +59,60 @@ int mk_bench_copy(void* d_dst, const void* d_src, size_t bytes, void* stream) {
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------------------------------------
+// Cost of one all-to-all dependency (every workgroup publishes a slot, bumps a
+// counter, waits for all of them, reads every slot back), the synchronisation
+// pattern of the decode step.  mode 0: release / acquire fences at agent scope
+// around plain loads and stores.  mode 1: every shared datum moved with
+// agent-scope relaxed atomics, ordered by vmcnt waits, no cache maintenance.
+// out[0] = ticks (100 MHz) of `rounds` rounds on workgroup 0, out[1] = data
+// mismatches seen by any workgroup.
+// ------------------------------------------------------------------------------------------------
+namespace {
+template <int MODE>
+__global__ void __launch_bounds__(64) k_sync(uint32_t* ctr, uint32_t* data, int rounds, uint64_t* out) {
+    const int n = gridDim.x, wg = blockIdx.x, lane = threadIdx.x;
+    uint32_t errors = 0;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (int r = 1; r <= rounds; ++r) {
+        const uint32_t v = (uint32_t)r * 4096u + (uint32_t)wg;
+        if (MODE == 0) {
+            data[wg * 64 + lane] = v;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        } else {
+            __hip_atomic_store(&data[wg * 64 + lane], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
+        }
+        if (lane == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t target = (uint32_t)r * (uint32_t)n;
+        uint64_t guard = 0;
+        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++guard > 20000000ull) break;  // bounded: never spins forever
+        }
+        if (MODE == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        for (int k = lane; k < n; k += 64) {
+            const uint32_t want = (uint32_t)r * 4096u + (uint32_t)k;
+            const uint32_t got = MODE == 0 ? data[k * 64 + (k & 63)]
+                                           : __hip_atomic_load(&data[k * 64 + (k & 63)], __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_AGENT);
+            errors += (got != want);
+        }
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    for (int m = 32; m >= 1; m >>= 1) errors += __shfl_xor(errors, m, 64);
+    if (lane == 0) {
+        if (wg == 0) out[0] = t1 - t0;
+        if (errors) atomicAdd((unsigned long long*)&out[1], (unsigned long long)errors);
+    }
+}
+}  // namespace
+
+extern "C" int mk_bench_sync(int mode, int n_wg, int rounds, void* d_ctr, void* d_data, void* d_out, void* stream) {
+    if (n_wg < 1 || n_wg > 1024 || rounds < 1 || rounds > 100000 || !d_ctr || !d_data || !d_out) return 1;
+    void* args[] = {&d_ctr, &d_data, &rounds, &d_out};
+    hipError_t e = hipLaunchCooperativeKernel(mode == 0 ? (const void*)k_sync<0> : (const void*)k_sync<1>,
+                                              dim3(n_wg), dim3(64), args, 0, (hipStream_t)stream);
+    return e == hipSuccess ? 0 : 4;
+}

@@ -80,7 +80,7 @@ mk_status validate(const mk_model_config* c, const mk_runtime_config* rt, std::s
     if (rt->mode != MK_MODE_MEGAKERNEL && rt->mode != MK_MODE_GRAPH) return fail(MK_E_INVALID, "unknown mode");
     if (rt->num_cus < 0 || rt->num_cus > kMaxCus) return fail(MK_E_INVALID, "num_cus out of range");
     if (rt->gemv_kind < 0 || rt->gemv_kind > 1) return fail(MK_E_UNSUPPORTED, "gemv_kind must be 0 or 1");
-    if (rt->trace != 0) return fail(MK_E_UNSUPPORTED, "tracing is not built");
+    if (rt->trace != 0 && rt->trace != 1) return fail(MK_E_INVALID, "trace must be 0 or 1");
     if (rt->attn_splits < 0 || rt->attn_splits > 256) return fail(MK_E_INVALID, "attn_splits out of range");
     return MK_OK;
 }
@@ -218,7 +218,7 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
 
 struct Layout {
     size_t state, counters, tickets, instrs, qoff, layers, rope, h, qkv, attn, act, attn_part, head_part, logits_scr,
-        tok_scr, total;
+        tok_scr, trace, trace_bytes, total;
     size_t head_slots;
 };
 
@@ -253,6 +253,12 @@ Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, i
     lo.head_part = take(lo.head_slots * B * sizeof(HeadPart));
     lo.logits_scr = take(B * c->vocab * 4);
     lo.tok_scr = take(B * 4);
+    // trace: one record per instruction slot; a CU holds at most 5 per layer + the head,
+    // plus the attention items beyond one per CU
+    const size_t items = B * c->n_kv_heads * nsplit;
+    const size_t per_cu = (size_t)c->n_layers * (4 + (items + n_cu - 1) / n_cu) + 1;
+    lo.trace_bytes = rt->trace ? (size_t)n_cu * per_cu * kTraceWords * 4 : 0;
+    lo.trace = take(lo.trace_bytes);
     lo.total = off;
     return lo;
 }
@@ -462,6 +468,14 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
     P.queue_off = (const uint32_t*)(ws + lo.qoff);
     P.head_ctr = h->plan.head_ctr;
     P.n_head_instr = h->plan.n_head;
+    if (rt->trace) {
+        P.trace = (uint32_t*)(ws + lo.trace);
+        P.trace_stride = (uint32_t)(lo.trace_bytes / ((size_t)n_cu * kTraceWords * 4));
+        if (h->plan.max_per_cu > P.trace_stride) {
+            delete h;
+            return MK_E_INVALID;
+        }
+    }
     const uint32_t tmo = rt->spin_timeout_ms ? rt->spin_timeout_ms : 2000u;
     P.spin_ticks = (uint64_t)tmo * 100000ull;
 
@@ -679,6 +693,22 @@ mk_status mk_debug_inject(mk_handle* h, int32_t fault, int32_t arg) {
     if (fault != 0 && fault != 1) return MK_E_INVALID;
     if (fault == 1 && h->rt.mode != MK_MODE_MEGAKERNEL) return MK_E_UNSUPPORTED;
     h->inject = fault;
+    return MK_OK;
+}
+
+mk_status mk_read_trace(mk_handle* h, void* h_buf, size_t bytes, size_t* written, int32_t* records_per_cu) {
+    if (!h || !written || !records_per_cu) return MK_E_INVALID;
+    *written = 0;
+    *records_per_cu = (int32_t)h->P.trace_stride;
+    if (!h->rt.trace) return MK_E_UNSUPPORTED;
+    if (!h_buf) {
+        *written = h->lo.trace_bytes;
+        return MK_OK;
+    }
+    const size_t n = std::min(bytes, h->lo.trace_bytes);
+    HIPCHK(h, hipStreamSynchronize(h->stream));
+    HIPCHK(h, hipMemcpy(h_buf, h->ws + h->lo.trace, n, hipMemcpyDeviceToHost));
+    *written = n;
     return MK_OK;
 }
 

@@ -162,6 +162,8 @@ __device__ void loader_wave(const Params& P, Ctl* ctl, char* ring, uint32_t q0, 
     for (uint32_t i = q0; i < q1 && !stop; ++i) {
         const Instr in = ld_const(P.instrs + i);
         const uint32_t nch = instr_bytes<HD>(P, in, ctx) / kChunk;
+        if (P.trace && i > q0 && lane_id() == 0)
+            P.trace[((size_t)blockIdx.x * P.trace_stride + (i - 1 - q0)) * kTraceWords + 5] = (uint32_t)now_ticks();
         if (nch == 0) continue;
         const DevLayer Lw = ld_const(P.layers + (in.layer < P.L ? in.layer : 0));
         for (uint32_t c = 0; c < nch; ++c) {
@@ -188,6 +190,8 @@ __device__ void loader_wave(const Params& P, Ctl* ctl, char* ring, uint32_t q0, 
     }
     wait_vmcnt<0>();
     lds_st(&ctl->landed, issued);
+    if (P.trace && q1 > q0 && lane_id() == 0)
+        P.trace[((size_t)blockIdx.x * P.trace_stride + (q1 - 1 - q0)) * kTraceWords + 5] = (uint32_t)now_ticks();
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -307,9 +311,15 @@ __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const
     for (uint32_t qi = q0; qi < q1; ++qi, ++k) {
         const Instr in = ld_const(P.instrs + qi);
         const uint32_t bytes = instr_bytes<HD>(P, in, ctx);
+        uint32_t* tr = (P.trace && wave == 0) ? P.trace + ((size_t)blockIdx.x * P.trace_stride + k) * kTraceWords : nullptr;
+        if (tr && lane == 0) {
+            tr[0] = (uint32_t)in.op | ((uint32_t)in.layer << 16);
+            tr[1] = (uint32_t)now_ticks();
+        }
         if (in.wait_ctr != kNoCounter) {
             if (!wait_counter(P, ctl, P.counters + (size_t)in.wait_ctr * kCtrStride, A.epoch * in.wait_n)) return;
         }
+        if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
         const int layer = in.layer;
         const DevLayer Lw = ld_const(P.layers + (layer < P.L ? layer : 0));
         bool ok = true;
@@ -410,6 +420,7 @@ __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const
             default: break;
         }
         if (!ok || lds_ld(&ctl->abort)) return;
+        if (tr && lane == 0) tr[3] = (uint32_t)now_ticks();
         S += bytes;
         set_consumed(ctl, wave, S / kChunk);
         if (in.op == OP_HEAD && lane < B) {
@@ -445,6 +456,7 @@ __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const
             }
         }
         if (in.op == OP_HEAD && nan_seen) raise_error(P, ctl, DERR_NAN, 1, blockIdx.x);
+        if (tr && lane == 0) tr[4] = (uint32_t)now_ticks();
     }
 }
 

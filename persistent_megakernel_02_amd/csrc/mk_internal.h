@@ -97,7 +97,14 @@ struct Params {
     const uint32_t* queue_off;  // [n_cu + 1]
     uint32_t head_ctr, n_head_instr;
     uint64_t spin_ticks;        // watchdog in s_memrealtime ticks (100 MHz)
+    uint32_t* trace;            // nullptr, or [n_cu][trace_stride][kTraceWords] records
+    uint32_t trace_stride;      // records per CU
+    uint32_t pad_tr;
 };
+
+// Trace record of one instruction on one CU (s_memrealtime ticks, low 32 bits):
+// {op | layer << 16, wait start, wait end, compute end, signal end, loader issue end}
+constexpr int kTraceWords = 8;
 
 // Per-launch arguments.
 struct StepArgs {

@@ -22,7 +22,8 @@ MK_MODE_MEGAKERNEL, MK_MODE_GRAPH = 0, 1
 
 EXPORTS = ["mk_query_sizes", "mk_create", "mk_kv_layout", "mk_prefill", "mk_set_context_len", "mk_decode_step",
            "mk_get_context_len", "mk_reset", "mk_debug_inject", "mk_status_string", "mk_last_error",
-           "mk_plan_inspect", "mk_kernels_per_step", "mk_destroy", "mk_bench_stream_read", "mk_bench_copy"]
+           "mk_plan_inspect", "mk_kernels_per_step", "mk_destroy", "mk_bench_stream_read", "mk_bench_copy",
+           "mk_bench_sync", "mk_read_trace"]
 
 
 class mk_model_config(ctypes.Structure):
@@ -83,9 +84,11 @@ def lib():
         L.mk_destroy.argtypes = [vp]
         L.mk_bench_stream_read.argtypes = [vp, sz, vp, vp]
         L.mk_bench_copy.argtypes = [vp, vp, sz, vp]
+        L.mk_bench_sync.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
+        L.mk_read_trace.argtypes = [vp, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(i32)]
         for n in ("mk_query_sizes", "mk_create", "mk_kv_layout", "mk_prefill", "mk_set_context_len",
                   "mk_get_context_len", "mk_decode_step", "mk_reset", "mk_debug_inject", "mk_plan_inspect",
-                  "mk_destroy", "mk_bench_stream_read", "mk_bench_copy"):
+                  "mk_destroy", "mk_bench_stream_read", "mk_bench_copy", "mk_bench_sync", "mk_read_trace"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -111,10 +114,10 @@ def model_config(cfg) -> mk_model_config:
 
 
 def runtime_config(max_batch: int, max_seq: int, mode: int = MK_MODE_MEGAKERNEL, num_cus: int = 0,
-                   spin_timeout_ms: int = 0, attn_splits: int = 0) -> mk_runtime_config:
+                   spin_timeout_ms: int = 0, attn_splits: int = 0, trace: int = 0) -> mk_runtime_config:
     r = mk_runtime_config()
     r.max_batch, r.max_seq, r.mode, r.num_cus = max_batch, max_seq, mode, num_cus
-    r.gemv_kind, r.spin_timeout_ms, r.trace, r.attn_splits = 0, spin_timeout_ms, 0, attn_splits
+    r.gemv_kind, r.spin_timeout_ms, r.trace, r.attn_splits = 0, spin_timeout_ms, trace, attn_splits
     return r
 
 
@@ -147,7 +150,7 @@ class Decoder:
 
     def __init__(self, cfg, weights, max_batch: int, max_seq: int, mode: int = MK_MODE_MEGAKERNEL,
                  device: str = "cuda:0", num_cus: int = 0, spin_timeout_ms: int = 0, attn_splits: int = 0,
-                 device_weights: Optional[Dict[str, object]] = None):
+                 device_weights: Optional[Dict[str, object]] = None, trace: int = 0):
         import torch
 
         self.torch = torch
@@ -156,7 +159,7 @@ class Decoder:
         self.B = max_batch
         self.max_seq = max_seq
         self._c = model_config(cfg)
-        self._rt = runtime_config(max_batch, max_seq, mode, num_cus, spin_timeout_ms, attn_splits)
+        self._rt = runtime_config(max_batch, max_seq, mode, num_cus, spin_timeout_ms, attn_splits, trace)
         st, ws, kv = mk_query_sizes(self._c, self._rt)
         if st != MK_OK:
             raise MKError(st, "mk_query_sizes")
@@ -237,6 +240,15 @@ class Decoder:
 
     def debug_inject(self, fault: int, arg: int = 0):
         self._check(lib().mk_debug_inject(self.h, fault, arg), "mk_debug_inject")
+
+    def read_trace(self):
+        """Timeline of the last megakernel step: uint32 [n_cu, records, 8] (see mk.h)."""
+        n, per = ctypes.c_size_t(0), ctypes.c_int32(0)
+        self._check(lib().mk_read_trace(self.h, None, 0, ctypes.byref(n), ctypes.byref(per)), "mk_read_trace")
+        buf = np.zeros(n.value // 4, np.uint32)
+        self._check(lib().mk_read_trace(self.h, buf.ctypes.data, n.value, ctypes.byref(n), ctypes.byref(per)),
+                    "mk_read_trace")
+        return buf.reshape(-1, per.value, 8)
 
     def kernels_per_step(self) -> int:
         return int(lib().mk_kernels_per_step(self.h))

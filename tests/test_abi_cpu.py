@@ -72,8 +72,12 @@ def test_runtime_validation():
     bad.mode = 7
     assert mk.mk_query_sizes(c, bad)[0] == mk.MK_E_INVALID
     bad = rt()
-    bad.trace = 1
-    assert mk.mk_query_sizes(c, bad)[0] == mk.MK_E_UNSUPPORTED
+    bad.trace = 2
+    assert mk.mk_query_sizes(c, bad)[0] == mk.MK_E_INVALID
+    ok = rt()
+    ok.trace = 1
+    st, ws_tr, _ = mk.mk_query_sizes(c, ok)
+    assert st == mk.MK_OK and ws_tr > mk.mk_query_sizes(c, rt())[1]
 
 
 @pytest.mark.parametrize("cfg", [I.TINY, I.LLAMA_1B, I.LLAMA_8B], ids=lambda c: c.name)
@@ -81,6 +85,9 @@ def test_runtime_validation():
 @pytest.mark.parametrize("batch", [1, 2])
 def test_schedule_verifies(cfg, cus, batch):
     st, info = mk.mk_plan_inspect(mk.model_config(cfg), rt(batch, 200), cus)
+    if batch * cfg.hidden * 4 > 16384:  # fp32 normed activations must fit the 16 KB LDS slot
+        assert st == mk.MK_E_UNSUPPORTED
+        return
     assert st == mk.MK_OK
     assert info["verify"] == 0
     assert info["phases"] == 5 * cfg.n_layers + 1
