@@ -27,12 +27,15 @@ int mk_bench_stream_read(const void* d_src, size_t bytes, void* d_sink, void* st
 int mk_bench_copy(void* d_dst, const void* d_src, size_t bytes, void* stream);
 
 /* Cost of the all-to-all dependency pattern: n_wg workgroups (one wave each,
- * co-resident, cooperative launch) run `rounds` rounds of publish -> counter
- * increment -> wait for all -> read every slot.  mode 0 orders with agent-scope
- * release/acquire fences, mode 1 with agent-scope relaxed atomics and vmcnt
- * waits.  d_ctr: one zeroed uint32; d_data: n_wg * 64 uint32; d_out: two zeroed
- * uint64 = {ticks of 100 MHz for all rounds on workgroup 0, data mismatches}.
- * Each wait is bounded, so the kernel ends even if a workgroup is missing. */
+ * co-resident, cooperative launch) run `rounds` rounds of publish -> signal ->
+ * wait for all -> read every slot (slots double-buffered by round parity).
+ * mode 0: one atomic counter + agent-scope release/acquire fences; mode 1: one
+ * counter + agent-scope relaxed atomics for data, vmcnt waits; mode 2: one
+ * completion flag per workgroup + fences; mode 3: flags + relaxed atomics.
+ * d_ctr: 64 + n_wg zeroed uint32 (counter line, then flags); d_data: 2 * n_wg
+ * * 64 uint32; d_out: two zeroed uint64 = {ticks of 100 MHz for all rounds on
+ * workgroup 0, data mismatches}.  Each wait is bounded, so the kernel ends even
+ * if a workgroup is missing.  Returns 0, 1 on bad arguments, 4 on launch error. */
 int mk_bench_sync(int mode, int n_wg, int rounds, void* d_ctr, void* d_data, void* d_out, void* stream);
 
 #ifdef __cplusplus

@@ -61,42 +61,64 @@ int mk_bench_copy(void* d_dst, const void* d_src, size_t bytes, void* stream) {
 }  // extern "C"
 
 // ------------------------------------------------------------------------------------------------
-// Cost of one all-to-all dependency (every workgroup publishes a slot, bumps a
-// counter, waits for all of them, reads every slot back), the synchronisation
-// pattern of the decode step.  mode 0: release / acquire fences at agent scope
-// around plain loads and stores.  mode 1: every shared datum moved with
-// agent-scope relaxed atomics, ordered by vmcnt waits, no cache maintenance.
+// Cost of one all-to-all dependency (every workgroup publishes a slot, signals,
+// waits for all, reads every slot back), the synchronisation pattern of the
+// decode step.  Slots are double-buffered by round parity, so a fast workgroup
+// writing round r + 1 never overwrites what a slow one still reads of round r.
+//   mode 0: one counter (atomic add), release / acquire fences, plain data
+//   mode 1: one counter, data and ordering through agent-scope relaxed atomics
+//   mode 2: one completion flag per workgroup (plain store of the round), fences
+//   mode 3: per-workgroup flags, agent-scope relaxed atomics for the data
 // out[0] = ticks (100 MHz) of `rounds` rounds on workgroup 0, out[1] = data
 // mismatches seen by any workgroup.
 // ------------------------------------------------------------------------------------------------
 namespace {
 template <int MODE>
 __global__ void __launch_bounds__(64) k_sync(uint32_t* ctr, uint32_t* data, int rounds, uint64_t* out) {
+    constexpr bool kFence = (MODE == 0 || MODE == 2);
+    constexpr bool kFlags = (MODE >= 2);
     const int n = gridDim.x, wg = blockIdx.x, lane = threadIdx.x;
+    uint32_t* flags = ctr + 64;  // per-workgroup flags follow the counter line
     uint32_t errors = 0;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     for (int r = 1; r <= rounds; ++r) {
+        uint32_t* buf = data + (size_t)(r & 1) * n * 64;
         const uint32_t v = (uint32_t)r * 4096u + (uint32_t)wg;
-        if (MODE == 0) {
-            data[wg * 64 + lane] = v;
+        if (kFence) {
+            buf[wg * 64 + lane] = v;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         } else {
-            __hip_atomic_store(&data[wg * 64 + lane], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&buf[wg * 64 + lane], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
         }
-        if (lane == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t target = (uint32_t)r * (uint32_t)n;
+        if (lane == 0) {
+            if (kFlags)
+                __hip_atomic_store(&flags[wg], (uint32_t)r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         uint64_t guard = 0;
-        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        for (;;) {
+            bool ok;
+            if (kFlags) {
+                ok = true;
+                for (int k = lane; k < n; k += 64)
+                    ok &= (int32_t)(__hip_atomic_load(&flags[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                                    (uint32_t)r) >= 0;
+                ok = __all(ok);
+            } else {
+                ok = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)r * (uint32_t)n;
+            }
+            if (ok) break;
             __builtin_amdgcn_s_sleep(1);
             if (++guard > 20000000ull) break;  // bounded: never spins forever
         }
-        if (MODE == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (kFence) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         for (int k = lane; k < n; k += 64) {
             const uint32_t want = (uint32_t)r * 4096u + (uint32_t)k;
-            const uint32_t got = MODE == 0 ? data[k * 64 + (k & 63)]
-                                           : __hip_atomic_load(&data[k * 64 + (k & 63)], __ATOMIC_RELAXED,
-                                                               __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t got = kFence ? buf[k * 64 + (k & 63)]
+                                        : __hip_atomic_load(&buf[k * 64 + (k & 63)], __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
             errors += (got != want);
         }
     }
@@ -110,9 +132,12 @@ __global__ void __launch_bounds__(64) k_sync(uint32_t* ctr, uint32_t* data, int 
 }  // namespace
 
 extern "C" int mk_bench_sync(int mode, int n_wg, int rounds, void* d_ctr, void* d_data, void* d_out, void* stream) {
-    if (n_wg < 1 || n_wg > 1024 || rounds < 1 || rounds > 100000 || !d_ctr || !d_data || !d_out) return 1;
+    if (n_wg < 1 || n_wg > 1024 || rounds < 1 || rounds > 100000 || !d_ctr || !d_data || !d_out || mode < 0 ||
+        mode > 3)
+        return 1;
+    const void* fns[4] = {(const void*)k_sync<0>, (const void*)k_sync<1>, (const void*)k_sync<2>,
+                          (const void*)k_sync<3>};
     void* args[] = {&d_ctr, &d_data, &rounds, &d_out};
-    hipError_t e = hipLaunchCooperativeKernel(mode == 0 ? (const void*)k_sync<0> : (const void*)k_sync<1>,
-                                              dim3(n_wg), dim3(64), args, 0, (hipStream_t)stream);
+    hipError_t e = hipLaunchCooperativeKernel(fns[mode], dim3(n_wg), dim3(64), args, 0, (hipStream_t)stream);
     return e == hipSuccess ? 0 : 4;
 }

@@ -42,6 +42,7 @@ struct Plan {
     std::vector<Instr> instrs;
     std::vector<uint32_t> qoff;  // [n_cu + 1]
     uint32_t n_ctr = 0, head_ctr = 0, conv_ticket_ctr = 0, n_head = 0;
+    uint32_t n_phase = 0, flag_stride = 64;
     int n_cu = 0, nsplit = 1;
     int phases = 0;
     size_t max_per_cu = 0;
@@ -119,9 +120,11 @@ Plan build_plan(const mk_model_config* c, const mk_runtime_config* rt, int n_cu)
             uint32_t b, cnt;
             tile(R, n_cu, cu, &b, &cnt);
             if (!cnt) continue;
-            q[cu].push_back(mk_instr(op, layer, b, cnt, prev_ctr, prev_n, ctr));
-            ++n;
+            Instr in = mk_instr(op, layer, b, cnt, prev_ctr, prev_n, ctr);
+            in.slot = n++;
+            q[cu].push_back(in);
         }
+        pl.flag_stride = std::max(pl.flag_stride, (n + 63u) & ~63u);
         prev_ctr = ctr;
         prev_n = n;
         ++pl.phases;
@@ -131,8 +134,12 @@ Plan build_plan(const mk_model_config* c, const mk_runtime_config* rt, int n_cu)
         gemv_phase(OP_QKV, l, qkv_rows, base + 0);
         // attention items: (b, g, s) spread one per CU round-robin
         const uint32_t items = (uint32_t)(B * c->n_kv_heads * pl.nsplit);
-        for (uint32_t it = 0; it < items; ++it)
-            q[it % n_cu].push_back(mk_instr(OP_ATTN, l, it, 1, prev_ctr, prev_n, (uint16_t)(base + 1)));
+        for (uint32_t it = 0; it < items; ++it) {
+            Instr in = mk_instr(OP_ATTN, l, it, 1, prev_ctr, prev_n, (uint16_t)(base + 1));
+            in.slot = it;
+            q[it % n_cu].push_back(in);
+        }
+        pl.flag_stride = std::max(pl.flag_stride, (items + 63u) & ~63u);
         prev_ctr = (uint16_t)(base + 1);
         prev_n = items;
         ++pl.phases;
@@ -145,6 +152,7 @@ Plan build_plan(const mk_model_config* c, const mk_runtime_config* rt, int n_cu)
     pl.n_head = prev_n;
     pl.conv_ticket_ctr = pl.head_ctr + 1;
     pl.n_ctr = pl.head_ctr + 2;
+    pl.n_phase = pl.head_ctr + 1;
     pl.qoff.resize(n_cu + 1);
     pl.qoff[0] = 0;
     for (int cu = 0; cu < n_cu; ++cu) {
@@ -213,11 +221,17 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
             if (in.wait_ctr != kNoCounter && in.wait_n != emitted[in.wait_ctr]) return 10;
         }
     if (pl.n_head != emitted[L * kPhasesPerLayer]) return 11;
+    std::vector<std::vector<uint8_t>> slot_seen(nphase);
+    for (int ph = 0; ph < nphase; ++ph) slot_seen[ph].assign(emitted[ph], 0);
+    for (const Instr& in : pl.instrs) {
+        if (in.slot >= emitted[in.sig_ctr] || in.slot >= pl.flag_stride) return 12;
+        if (slot_seen[in.sig_ctr][in.slot]++) return 13;  // two producers share a flag
+    }
     return 0;
 }
 
 struct Layout {
-    size_t state, counters, tickets, instrs, qoff, layers, rope, h, qkv, attn, act, attn_part, head_part, logits_scr,
+    size_t state, counters, flags, flags_bytes, tickets, instrs, qoff, layers, rope, h, qkv, attn, act, attn_part, head_part, logits_scr,
         tok_scr, trace, trace_bytes, total;
     size_t head_slots;
 };
@@ -225,7 +239,7 @@ struct Layout {
 inline size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
 Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, int nsplit, size_t n_instr,
-              uint32_t n_ctr) {
+              uint32_t n_ctr, uint32_t flag_stride) {
     Layout lo{};
     const size_t B = (size_t)rt->max_batch, d = c->hidden, hd = c->head_dim;
     const size_t qkv_rows = (size_t)(c->n_q_heads + 2 * c->n_kv_heads) * hd;
@@ -238,6 +252,8 @@ Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, i
     };
     lo.state = take(sizeof(DevState));
     lo.counters = take((size_t)n_ctr * kCtrStride * 4);
+    lo.flags_bytes = (size_t)n_ctr * flag_stride * 4;
+    lo.flags = take(lo.flags_bytes);
     lo.tickets = take((size_t)c->n_layers * B * c->n_kv_heads * kCtrStride * 4);
     lo.instrs = take(n_instr * sizeof(Instr));
     lo.qoff = take((size_t)(n_cu + 1) * 4);
@@ -347,7 +363,9 @@ mk_status mk_query_sizes(const mk_model_config* cfg, const mk_runtime_config* rt
     for (int cus = 1; cus <= n_cu; cus *= 2) nsplit = std::max(nsplit, auto_splits(cfg, rt, cus));
     nsplit = std::max(nsplit, auto_splits(cfg, rt, n_cu));
     const uint32_t n_ctr = (uint32_t)(cfg->n_layers * kPhasesPerLayer + 2);
-    Layout lo = layout(cfg, rt, n_cu, nsplit, max_instrs(cfg, rt, n_cu, nsplit), n_ctr);
+    const uint32_t items = (uint32_t)(rt->max_batch * cfg->n_kv_heads * nsplit);
+    const uint32_t fstride = (std::max((uint32_t)n_cu, items) + 63u) & ~63u;
+    Layout lo = layout(cfg, rt, n_cu, nsplit, max_instrs(cfg, rt, n_cu, nsplit), n_ctr, fstride);
     *workspace_bytes = lo.total;
     *kv_bytes = 2ull * cfg->n_layers * rt->max_batch * cfg->n_kv_heads * (size_t)rt->max_seq * cfg->head_dim * 2;
     return MK_OK;
@@ -404,7 +422,7 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
         delete h;
         return MK_E_INVALID;
     }
-    h->lo = layout(cfg, rt, n_cu, h->plan.nsplit, h->plan.instrs.size(), h->plan.n_ctr);
+    h->lo = layout(cfg, rt, n_cu, h->plan.nsplit, h->plan.instrs.size(), h->plan.n_ctr, h->plan.flag_stride);
     if (workspace_bytes < h->lo.total || workspace_bytes < need_ws || kv_bytes < need_kv) {
         delete h;
         return MK_E_INVALID;
@@ -462,6 +480,8 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
     P.attn_ticket = (uint32_t*)(ws + lo.tickets);
     P.head_part = (HeadPart*)(ws + lo.head_part);
     P.counters = (uint32_t*)(ws + lo.counters);
+    P.flags = (uint32_t*)(ws + lo.flags);
+    P.flag_stride = h->plan.flag_stride;
     P.state = (DevState*)(ws + lo.state);
     P.host_err = h->host_err_dev;
     P.instrs = (const Instr*)(ws + lo.instrs);
@@ -675,6 +695,7 @@ mk_status mk_reset(mk_handle* h, void* stream) {
     HIPCHK(h, hipMemcpy(&ds, h->ws + h->lo.state, sizeof(ds), hipMemcpyDeviceToHost));
     for (int b = 0; b < h->rt.max_batch; ++b) h->ctx[b] = ds.ctx_len[b];
     HIPCHK(h, hipMemsetAsync(h->ws + h->lo.counters, 0, (size_t)h->plan.n_ctr * kCtrStride * 4, st));
+    HIPCHK(h, hipMemsetAsync(h->ws + h->lo.flags, 0, h->lo.flags_bytes, st));
     HIPCHK(h, hipMemsetAsync(h->ws + h->lo.tickets, 0,
                              (size_t)h->cfg.n_layers * h->rt.max_batch * h->cfg.n_kv_heads * kCtrStride * 4, st));
     HIPCHK(h, hipMemsetAsync(h->ws + h->lo.state + offsetof(DevState, error), 0, 16, st));

@@ -154,11 +154,103 @@ __device__ __forceinline__ void dma_chunk(const char* src, uint32_t lds_addr) {
         : "memory");
 }
 
+// Row model of an instruction's stream: row j of `rb` bytes starts at
+// row_ptr(j); rb is a multiple of the chunk size on every fast path, so a chunk
+// never straddles two rows and its lane address is row base + 1 KB * k + 16 * lane.
+// ATTN rows are the 1 KB K and V blocks of consecutive position groups.
+template <int HD>
+struct RowSrc {
+    uint16_t op;
+    uint32_t rb, nrows, begin;
+    const char *w0, *w1, *w2;  // tensors (QKV: q, k, v; GATEUP: gate, up; ATTN: K, V rows of (layer, b, g))
+    uint32_t nq, nk;           // QKV row split
+    int s0, ncached;           // ATTN positions
+    __device__ __forceinline__ const char* row_ptr(uint32_t j) const {
+        switch (op) {
+            case OP_QKV: {
+                const uint32_t row = begin + j;
+                return row < nq ? w0 + (size_t)row * rb
+                     : row < nq + nk ? w1 + (size_t)(row - nq) * rb : w2 + (size_t)(row - nq - nk) * rb;
+            }
+            case OP_GATEUP: return ((j & 1u) ? w1 : w0) + (size_t)(begin + (j >> 1)) * rb;
+            case OP_ATTN: return ((j & 1u) ? w1 : w0) + (size_t)(j >> 1) * kChunk;
+            default: return w0 + (size_t)(begin + j) * rb;
+        }
+    }
+};
+
+template <int HD>
+__device__ __forceinline__ bool setup_rows(const Params& P, const Instr& in, const DevLayer& Lw, const int32_t* ctx,
+                                           RowSrc<HD>& R) {
+    R.op = in.op;
+    R.begin = in.begin;
+    R.nq = (uint32_t)(P.Hq * HD);
+    R.nk = (uint32_t)(P.Hkv * HD);
+    R.s0 = 0;
+    R.ncached = 0;
+    switch (in.op) {
+        case OP_QKV:
+            R.rb = (uint32_t)P.d * 2u; R.nrows = in.count;
+            R.w0 = (const char*)Lw.wq; R.w1 = (const char*)Lw.wk; R.w2 = (const char*)Lw.wv;
+            break;
+        case OP_O:
+            R.rb = (uint32_t)(P.Hq * HD) * 2u; R.nrows = in.count; R.w0 = (const char*)Lw.wo;
+            break;
+        case OP_GATEUP:
+            R.rb = (uint32_t)P.d * 2u; R.nrows = 2u * in.count;
+            R.w0 = (const char*)Lw.w_gate; R.w1 = (const char*)Lw.w_up;
+            break;
+        case OP_DOWN:
+            R.rb = (uint32_t)P.F * 2u; R.nrows = in.count; R.w0 = (const char*)Lw.w_down;
+            break;
+        case OP_HEAD:
+            R.rb = (uint32_t)P.d * 2u; R.nrows = in.count; R.w0 = (const char*)P.head;
+            break;
+        case OP_ATTN: {
+            const int per_b = P.Hkv * P.nsplit;
+            const int b = (int)in.begin / per_b, g = ((int)in.begin % per_b) / P.nsplit, s = (int)in.begin % P.nsplit;
+            const SplitRange Rg = split_range<HD>(ctx[b], s, P.nsplit);
+            const size_t base = ((((size_t)in.layer * P.kv_b + b) * P.Hkv + g) * P.S + Rg.s0) * HD;
+            R.w0 = (const char*)(P.kcache + base);
+            R.w1 = (const char*)(P.vcache + base);
+            R.rb = kChunk;
+            R.nrows = 2u * (uint32_t)Rg.ngroups;
+            R.s0 = Rg.s0;
+            R.ncached = Rg.ncached;
+            return true;
+        }
+        default: return false;
+    }
+    return (R.rb & (kChunk - 1u)) == 0;  // fast path needs whole chunks per row
+}
+
 template <int HD>
 __device__ void loader_wave(const Params& P, Ctl* ctl, char* ring, uint32_t q0, uint32_t q1, const int32_t* ctx) {
     const uint32_t ring_base = (uint32_t)(size_t)(lds_ptr_t)ring;
-    uint32_t issued = 0, landed = 0;
+    const uint32_t lane16 = (uint32_t)lane_id() * 16u;
+    uint32_t issued = 0, landed = 0, limit = kRingChunks;
     bool stop = false;
+    // Wait until chunk `issued` may be written into the ring; refreshes `limit`.
+    auto make_room = [&]() -> bool {
+        for (;;) {
+            limit = min_consumed(ctl) + kRingChunks;
+            if (issued < limit) return true;
+            wait_vmcnt<0>();
+            landed = issued;
+            lds_st(&ctl->landed, landed);
+            if (lds_ld(&ctl->abort)) return false;
+            __builtin_amdgcn_s_sleep(1);
+        }
+    };
+    auto issue = [&](const char* src) {
+        dma_chunk(src, ring_base + (issued % kRingChunks) * kChunk);
+        ++issued;
+        if (issued - landed > (uint32_t)kLoaderLag) {
+            wait_vmcnt<kLoaderLag>();
+            landed = issued - kLoaderLag;
+            lds_st(&ctl->landed, landed);
+        }
+    };
     for (uint32_t i = q0; i < q1 && !stop; ++i) {
         const Instr in = ld_const(P.instrs + i);
         const uint32_t nch = instr_bytes<HD>(P, in, ctx) / kChunk;
@@ -166,25 +258,30 @@ __device__ void loader_wave(const Params& P, Ctl* ctl, char* ring, uint32_t q0, 
             P.trace[((size_t)blockIdx.x * P.trace_stride + (i - 1 - q0)) * kTraceWords + 5] = (uint32_t)now_ticks();
         if (nch == 0) continue;
         const DevLayer Lw = ld_const(P.layers + (in.layer < P.L ? in.layer : 0));
-        for (uint32_t c = 0; c < nch; ++c) {
-            while (issued - min_consumed(ctl) >= kRingChunks) {
-                wait_vmcnt<0>();
-                landed = issued;
-                lds_st(&ctl->landed, landed);
-                if (lds_ld(&ctl->abort)) {
-                    stop = true;
-                    break;
+        RowSrc<HD> R;
+        if (setup_rows<HD>(P, in, Lw, ctx, R)) {
+            const uint32_t cpr = R.rb / kChunk;
+            if (in.op == OP_ATTN) {
+                constexpr int LPP = AttnGeom<HD>::LPP, PPW = AttnGeom<HD>::PPW;
+                const int lane_pos = lane_id() / LPP;
+                for (uint32_t j = 0; j < R.nrows && !stop; ++j) {
+                    if (issued >= limit && !make_room()) { stop = true; break; }
+                    const bool valid = (int)((j >> 1) * PPW) + lane_pos < R.ncached;
+                    issue(valid ? R.row_ptr(j) + lane16 : R.w0);
                 }
-                __builtin_amdgcn_s_sleep(1);
+            } else {
+                for (uint32_t j = 0; j < R.nrows && !stop; ++j) {
+                    const char* row = R.row_ptr(j) + lane16;
+                    for (uint32_t k = 0; k < cpr; ++k) {
+                        if (issued >= limit && !make_room()) { stop = true; break; }
+                        issue(row + k * kChunk);
+                    }
+                }
             }
-            if (stop) break;
-            const char* src = chunk_src<HD>(P, in, Lw, c, ctx);
-            dma_chunk(src, ring_base + (issued % kRingChunks) * kChunk);
-            ++issued;
-            if (issued - landed > (uint32_t)kLoaderLag) {
-                wait_vmcnt<kLoaderLag>();
-                landed = issued - kLoaderLag;
-                lds_st(&ctl->landed, landed);
+        } else {
+            for (uint32_t c = 0; c < nch; ++c) {
+                if (issued >= limit && !make_room()) { stop = true; break; }
+                issue(chunk_src<HD>(P, in, Lw, c, ctx));
             }
         }
     }
@@ -220,16 +317,25 @@ __device__ __forceinline__ void raise_error(const Params& P, Ctl* ctl, uint32_t 
     raise_error_impl(P.state, P.host_err, &ctl->abort, code, a, b);
 }
 
-// Spin until *ctr >= target (wrapping compare), then acquire at agent scope.
-__device__ __forceinline__ bool wait_counter(const Params& P, Ctl* ctl, uint32_t* ctr, uint32_t target) {
-    uint32_t v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((int32_t)(v - target) < 0) {
+// Spin until the first n completion flags of a phase all hold `epoch` (wrapping
+// compare), then acquire at agent scope.  Lane l polls flags l, l + 64, ...
+__device__ __forceinline__ bool wait_flags(const Params& P, Ctl* ctl, const uint32_t* flags, uint32_t n,
+                                           uint32_t epoch) {
+    const uint32_t lane = (uint32_t)lane_id();
+    auto ready = [&]() {
+        bool ok = true;
+        for (uint32_t s = lane; s < n; s += 64u) {
+            const uint32_t f = __hip_atomic_load(flags + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ok &= (int32_t)(f - epoch) >= 0;
+        }
+        return __all(ok);
+    };
+    if (!ready()) {
         const uint64_t t0 = now_ticks();
         uint32_t polls = 0;
         for (;;) {
             __builtin_amdgcn_s_sleep(1);
-            v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if ((int32_t)(v - target) >= 0) break;
+            if (ready()) break;
             if (lds_ld(&ctl->abort)) return false;
             if ((++polls & 63u) == 0) {
                 if (__hip_atomic_load(&P.state->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
@@ -237,7 +343,7 @@ __device__ __forceinline__ bool wait_counter(const Params& P, Ctl* ctl, uint32_t
                     return false;
                 }
                 if (now_ticks() - t0 > P.spin_ticks) {
-                    raise_error(P, ctl, DERR_TIMEOUT, target, v);
+                    raise_error(P, ctl, DERR_TIMEOUT, epoch, n);
                     return false;
                 }
             }
@@ -317,7 +423,7 @@ __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const
             tr[1] = (uint32_t)now_ticks();
         }
         if (in.wait_ctr != kNoCounter) {
-            if (!wait_counter(P, ctl, P.counters + (size_t)in.wait_ctr * kCtrStride, A.epoch * in.wait_n)) return;
+            if (!wait_flags(P, ctl, P.flags + (size_t)in.wait_ctr * P.flag_stride, in.wait_n, A.epoch)) return;
         }
         if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
         const int layer = in.layer;
@@ -440,9 +546,12 @@ __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const
         old = __shfl(old, 0, 64);
         if (old == (k + 1u) * (uint32_t)kComputeWaves - 1u && in.sig_ctr != kNoCounter) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            uint32_t prev = 0;
             if (lane == 0)
-                prev = __hip_atomic_fetch_add(P.counters + (size_t)in.sig_ctr * kCtrStride, 1u, __ATOMIC_RELAXED,
+                __hip_atomic_store(P.flags + (size_t)in.sig_ctr * P.flag_stride + in.slot, A.epoch, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t prev = 0;
+            if (in.op == OP_HEAD && lane == 0)
+                prev = __hip_atomic_fetch_add(P.counters + (size_t)P.head_ctr * kCtrStride, 1u, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
             prev = __shfl(prev, 0, 64);
             if (in.op == OP_HEAD && prev + 1u == A.epoch * P.n_head_instr) {

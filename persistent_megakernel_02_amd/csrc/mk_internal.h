@@ -36,12 +36,16 @@ constexpr uint16_t kNoCounter = 0xFFFF;
 
 // One queue entry (32 bytes).  For GEMV ops `begin/count` are rows (GATEUP:
 // f-index pairs); for ATTN `begin` is the item id b*Hkv*nsplit + g*nsplit + s.
+// Dependencies: every instruction of phase c owns one completion flag
+// flags[c][slot]; a dependant waits until the wait_n flags of phase wait_ctr
+// all hold the current epoch.
 struct Instr {
     uint16_t op, layer;
     uint32_t begin, count;
     uint16_t wait_ctr, sig_ctr;
-    uint32_t wait_n;   // producers of wait_ctr per step: wait until ctr >= epoch * wait_n
-    uint32_t aux[3];
+    uint32_t wait_n;   // producers of phase wait_ctr
+    uint32_t slot;     // this instruction's flag in phase sig_ctr
+    uint32_t aux[2];
 };
 static_assert(sizeof(Instr) == 32, "instruction record is 32 bytes");
 
@@ -89,7 +93,10 @@ struct Params {
     float* attn_part;    // [B][Hkv][nsplit][G][hd + 2] split partials (m, l, o)
     uint32_t* attn_ticket;  // [L][B][Hkv] * kCtrStride, reset by the merger
     HeadPart* head_part; // [n_cu * kComputeWaves][B]
-    uint32_t* counters;  // [n_ctr] * kCtrStride
+    uint32_t* counters;  // [n_ctr] * kCtrStride (LM-head ticket, one-kernel-per-op ticket)
+    uint32_t* flags;     // [n_phase][flag_stride] completion epochs
+    uint32_t flag_stride;
+    uint32_t pad_fl;
     DevState* state;
     HostErr* host_err;   // pinned, host-mapped
     // schedule
