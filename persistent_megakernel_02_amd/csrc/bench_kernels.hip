@@ -141,3 +141,47 @@ extern "C" int mk_bench_sync(int mode, int n_wg, int rounds, void* d_ctr, void* 
     hipError_t e = hipLaunchCooperativeKernel(fns[mode], dim3(n_wg), dim3(64), args, 0, (hipStream_t)stream);
     return e == hipSuccess ? 0 : 4;
 }
+
+// ------------------------------------------------------------------------------------------------
+// HBM -> LDS streaming rate of the direct-to-LDS load the decode loader uses:
+// every workgroup (one per CU) runs WAVES waves; each wave streams its share of
+// `src` 1 KB at a time into a private 32 KB LDS ring with LAG loads in flight.
+// out[0] = ticks of workgroup 0.
+// ------------------------------------------------------------------------------------------------
+namespace {
+template <int LAG, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES) k_lds_stream(const char* src, size_t bytes, uint64_t* out) {
+    __shared__ __attribute__((aligned(1024))) char ring[WAVES * 32 * 1024];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const size_t chunks = bytes / 1024;
+    const size_t per = chunks / ((size_t)gridDim.x * WAVES);
+    const size_t first = ((size_t)blockIdx.x * WAVES + wave) * per;
+    const uint32_t base = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)ring + wave * 32768u;
+    const char* p = src + first * 1024 + (threadIdx.x & 63) * 16;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (size_t c = 0; c < per; ++c) {
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :
+                     : "{m0}"(__builtin_amdgcn_readfirstlane(base + (uint32_t)(c & 31) * 1024u)), "v"(p + c * 1024)
+                     : "memory");
+        __builtin_amdgcn_s_waitcnt((LAG & 15) | ((LAG >> 4) << 14) | (7 << 4) | (15 << 8));
+    }
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
+    __syncthreads();
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    if (blockIdx.x == 0 && threadIdx.x == 0) out[0] = t1 - t0;
+}
+}  // namespace
+
+extern "C" int mk_bench_lds_stream(int lag, int waves, const void* d_src, size_t bytes, int n_wg, void* d_out,
+                                   void* stream) {
+    if (!d_src || !d_out || n_wg < 1 || bytes < (size_t)n_wg * waves * 1024) return 1;
+    const void* f = nullptr;
+#define MK_LS(L, W) if (lag == L && waves == W) f = (const void*)k_lds_stream<L, W>;
+    MK_LS(4, 1) MK_LS(12, 1) MK_LS(24, 1) MK_LS(48, 1) MK_LS(60, 1)
+    MK_LS(12, 2) MK_LS(24, 2) MK_LS(48, 2) MK_LS(12, 4) MK_LS(24, 4)
+#undef MK_LS
+    if (!f) return 1;
+    void* args[] = {&d_src, &bytes, &d_out};
+    return hipLaunchKernel(f, dim3(n_wg), dim3(64 * waves), args, 0, (hipStream_t)stream) == hipSuccess ? 0 : 4;
+}
