@@ -231,15 +231,18 @@ __device__ void loader_wave(const Params& P, Ctl* ctl, char* ring, uint32_t q0, 
     uint32_t issued = 0, landed = 0, limit = kRingChunks;
     bool stop = false;
     // Wait until chunk `issued` may be written into the ring; refreshes `limit`.
+    uint32_t stall = 0;
     auto make_room = [&]() -> bool {
         for (;;) {
             limit = min_consumed(ctl) + kRingChunks;
             if (issued < limit) return true;
+            const uint32_t ts = P.trace ? (uint32_t)now_ticks() : 0u;
             wait_vmcnt<0>();
             landed = issued;
             lds_st(&ctl->landed, landed);
             if (lds_ld(&ctl->abort)) return false;
             __builtin_amdgcn_s_sleep(1);
+            if (P.trace) stall += (uint32_t)now_ticks() - ts;
         }
     };
     auto issue = [&](const char* src) {
@@ -254,8 +257,12 @@ __device__ void loader_wave(const Params& P, Ctl* ctl, char* ring, uint32_t q0, 
     for (uint32_t i = q0; i < q1 && !stop; ++i) {
         const Instr in = ld_const(P.instrs + i);
         const uint32_t nch = instr_bytes<HD>(P, in, ctx) / kChunk;
-        if (P.trace && i > q0 && lane_id() == 0)
-            P.trace[((size_t)blockIdx.x * P.trace_stride + (i - 1 - q0)) * kTraceWords + 5] = (uint32_t)now_ticks();
+        if (P.trace && lane_id() == 0) {
+            uint32_t* rec = P.trace + ((size_t)blockIdx.x * P.trace_stride + (i - q0)) * kTraceWords;
+            if (i > q0) rec[5 - kTraceWords] = (uint32_t)now_ticks();
+            if (i > q0) rec[7 - kTraceWords] = stall;
+        }
+        stall = 0;
         if (nch == 0) continue;
         const DevLayer Lw = ld_const(P.layers + (in.layer < P.L ? in.layer : 0));
         RowSrc<HD> R;
@@ -287,8 +294,10 @@ __device__ void loader_wave(const Params& P, Ctl* ctl, char* ring, uint32_t q0, 
     }
     wait_vmcnt<0>();
     lds_st(&ctl->landed, issued);
-    if (P.trace && q1 > q0 && lane_id() == 0)
+    if (P.trace && q1 > q0 && lane_id() == 0) {
         P.trace[((size_t)blockIdx.x * P.trace_stride + (q1 - 1 - q0)) * kTraceWords + 5] = (uint32_t)now_ticks();
+        P.trace[((size_t)blockIdx.x * P.trace_stride + (q1 - 1 - q0)) * kTraceWords + 7] = stall;
+    }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -354,12 +363,19 @@ __device__ __forceinline__ bool wait_flags(const Params& P, Ctl* ctl, const uint
 }
 
 // Wait until the loader has `need` chunks resident.
-__device__ __forceinline__ bool wait_landed(const Params& P, Ctl* ctl, uint32_t need) {
+__device__ __forceinline__ bool wait_landed(const Params& P, Ctl* ctl, uint32_t need, uint32_t* waited = nullptr) {
     if (lds_ld(&ctl->landed) >= need) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         return true;
     }
     const uint64_t t0 = now_ticks();
+    struct Acc {
+        uint32_t* w;
+        uint64_t t0;
+        __device__ ~Acc() {
+            if (w) *w += (uint32_t)(now_ticks() - t0);
+        }
+    } acc{waited, t0};
     uint32_t polls = 0;
     while (lds_ld(&ctl->landed) < need) {
         if (lds_ld(&ctl->abort)) return false;
@@ -426,6 +442,8 @@ __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const
             if (!wait_flags(P, ctl, P.flags + (size_t)in.wait_ctr * P.flag_stride, in.wait_n, A.epoch)) return;
         }
         if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
+        uint32_t land_wait = 0;
+        uint32_t* lw = tr ? &land_wait : nullptr;
         const int layer = in.layer;
         const DevLayer Lw = ld_const(P.layers + (layer < P.L ? layer : 0));
         bool ok = true;
@@ -444,7 +462,7 @@ __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const
                     for (uint32_t i = wave; i < in.count && ok; i += kComputeWaves) {
                         const uint32_t off = S + 2u * i * rb;
                         set_consumed(ctl, wave, off / kChunk);
-                        ok = wait_landed(P, ctl, (off + 2u * rb + kChunk - 1u) / kChunk);
+                        ok = wait_landed(P, ctl, (off + 2u * rb + kChunk - 1u) / kChunk, lw);
                         if (!ok) break;
                         float zg[B], zu[B];
                         row_dot<B>(rows, 2u * i, np, x, zg);
@@ -459,7 +477,7 @@ __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const
                     for (uint32_t r = wave; r < in.count && ok; r += kComputeWaves) {
                         const uint32_t off = S + r * rb;
                         set_consumed(ctl, wave, off / kChunk);
-                        ok = wait_landed(P, ctl, (off + rb + kChunk - 1u) / kChunk);
+                        ok = wait_landed(P, ctl, (off + rb + kChunk - 1u) / kChunk, lw);
                         if (!ok) break;
                         float acc[B];
                         row_dot<B>(rows, r, np, x, acc);
@@ -491,7 +509,7 @@ __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const
                 for (uint32_t r = wave; r < in.count && ok; r += kComputeWaves) {
                     const uint32_t off = S + r * rb;
                     set_consumed(ctl, wave, off / kChunk);
-                    ok = wait_landed(P, ctl, (off + rb + kChunk - 1u) / kChunk);
+                    ok = wait_landed(P, ctl, (off + rb + kChunk - 1u) / kChunk, lw);
                     if (!ok) break;
                     float acc[B];
                     row_dot<B>(rows, r, np, x, acc);
@@ -515,7 +533,7 @@ __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const
                 auto need = [&](int t) {
                     const uint32_t off = S + (uint32_t)t * 2048u;
                     set_consumed(ctl, wave, off / kChunk);
-                    if (!wait_landed(P, ctl, (off + 2048u) / kChunk)) ok = false;
+                    if (!wait_landed(P, ctl, (off + 2048u) / kChunk, lw)) ok = false;
                 };
                 const CwBarrier barrier{ctl, &P, &bar_gen};
                 bool merged = false;
@@ -526,7 +544,10 @@ __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const
             default: break;
         }
         if (!ok || lds_ld(&ctl->abort)) return;
-        if (tr && lane == 0) tr[3] = (uint32_t)now_ticks();
+        if (tr && lane == 0) {
+            tr[3] = (uint32_t)now_ticks();
+            tr[6] = land_wait;
+        }
         S += bytes;
         set_consumed(ctl, wave, S / kChunk);
         if (in.op == OP_HEAD && lane < B) {
