@@ -42,66 +42,75 @@ struct PairRows {  // stream row 2i = gate row, 2i + 1 = up row of f = begin + i
     }
 };
 
+// Rows [0, count) of a block in batches of R rows per wave (the same tile
+// function as the megakernel, so every row's value is bitwise identical).
+template <int B, int R, class Rows, class X, class Epi>
+__device__ __forceinline__ void conv_rows(const Rows& rows, uint32_t count, int np, const X& x, Epi&& epi) {
+    const int wave = threadIdx.x >> 6;
+    for (uint32_t r0 = (uint32_t)wave * R; r0 < count; r0 += (uint32_t)R * kConvWaves) {
+        const uint32_t nr = min((uint32_t)R, count - r0);
+        float res[R][B];
+        rows_dot<B, R>(rows, r0, (int)nr, np, x, res);
+        epi(r0, nr, res);
+    }
+}
+
 template <int B>
 __global__ void __launch_bounds__(kConvThreads) k_qkv(Params P, StepArgs A, int layer) {
     __shared__ __attribute__((aligned(16))) float xs[kXBytes / 4];
-    const int wave = threadIdx.x >> 6, lane = lane_id();
+    const int lane = lane_id();
     const DevLayer Lw = P.layers[layer];
     rmsnorm_rows<B>(P.h, layer == 0 ? P.embed : nullptr, A.tok_in, A.tok_stride, P.V, Lw.attn_norm, P.d, P.eps, xs);
     const uint32_t begin = blockIdx.x * kRowsPerBlock;
     const uint32_t count = min((uint32_t)kRowsPerBlock, (uint32_t)P.qkv_rows - begin);
     const QkvRows rows{Lw.wq, Lw.wk, Lw.wv, (uint32_t)P.d, (uint32_t)(P.Hq * P.hd), (uint32_t)(P.Hkv * P.hd), begin};
     const XLds x{xs, (uint32_t)P.d};
-    for (uint32_t r = wave; r < count; r += kConvWaves) {
-        float acc[B];
-        row_dot<B>(rows, r, P.d >> 3, x, acc);
-        if (lane < B) P.qkv[(size_t)lane * P.qkv_rows + begin + r] = pick<B>(acc, lane);
-    }
+    conv_rows<B, 4>(rows, count, P.d >> 3, x, [&](uint32_t r0, uint32_t nr, auto& res) {
+        for (uint32_t i = 0; i < nr; ++i)
+            if (lane < B) P.qkv[(size_t)lane * P.qkv_rows + begin + r0 + i] = pick<B>(res[i], lane);
+    });
 }
 
 template <int B>
 __global__ void __launch_bounds__(kConvThreads) k_gateup(Params P, StepArgs A, int layer) {
     __shared__ __attribute__((aligned(16))) float xs[kXBytes / 4];
-    const int wave = threadIdx.x >> 6, lane = lane_id();
+    const int lane = lane_id();
     const DevLayer Lw = P.layers[layer];
     rmsnorm_rows<B>(P.h, nullptr, A.tok_in, A.tok_stride, P.V, Lw.mlp_norm, P.d, P.eps, xs);
     const uint32_t begin = blockIdx.x * kRowsPerBlock;
     const uint32_t count = min((uint32_t)kRowsPerBlock, (uint32_t)P.F - begin);
     const PairRows rows{Lw.w_gate, Lw.w_up, (uint32_t)P.d, begin};
     const XLds x{xs, (uint32_t)P.d};
-    for (uint32_t i = wave; i < count; i += kConvWaves) {
-        float zg[B], zu[B];
-        row_dot<B>(rows, 2u * i, P.d >> 3, x, zg);
-        row_dot<B>(rows, 2u * i + 1u, P.d >> 3, x, zu);
-        if (lane < B) {
-            const float a = silu_mul(pick<B>(zg, lane), pick<B>(zu, lane));
-            P.act[(size_t)lane * P.F + begin + i] = a;
-        }
-    }
+    conv_rows<B, 4>(rows, 2u * count, P.d >> 3, x, [&](uint32_t r0, uint32_t nr, auto& res) {
+        for (uint32_t i = 0; i + 1 < nr; i += 2)
+            if (lane < B)
+                P.act[(size_t)lane * P.F + begin + (r0 + i) / 2u] = silu_mul(pick<B>(res[i], lane), pick<B>(res[i + 1], lane));
+    });
 }
 
 // O projection (is_down = 0) or down projection (is_down = 1) with residual add.
 template <int B>
 __global__ void __launch_bounds__(kConvThreads) k_proj_resid(Params P, StepArgs A, int layer, int is_down) {
-    const int wave = threadIdx.x >> 6, lane = lane_id();
+    const int lane = lane_id();
     const DevLayer Lw = P.layers[layer];
     const uint32_t K = is_down ? (uint32_t)P.F : (uint32_t)(P.Hq * P.hd);
     const uint32_t begin = blockIdx.x * kRowsPerBlock;
     const uint32_t count = min((uint32_t)kRowsPerBlock, (uint32_t)P.d - begin);
     const PlainRows rows{is_down ? Lw.w_down : Lw.wo, K, begin};
     const XGlobal x{is_down ? P.act : P.attn, K};
-    for (uint32_t r = wave; r < count; r += kConvWaves) {
-        float acc[B];
-        row_dot<B>(rows, r, (int)(K >> 3), x, acc);
-        const uint32_t row = begin + r;
-        if (lane < B) {
-            float* hp = P.h + (size_t)lane * P.d + row;
-            const float resid = (!is_down && layer == 0)
-                                    ? bf_to_f(P.embed[token_row(A.tok_in, lane, A.tok_stride, P.V) * P.d + row])
-                                    : *hp;
-            *hp = resid + pick<B>(acc, lane);
+    auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
+        for (uint32_t i = 0; i < nr; ++i) {
+            const uint32_t row = begin + r0 + i;
+            if (lane < B) {
+                float* hp = P.h + (size_t)lane * P.d + row;
+                const float resid = (!is_down && layer == 0)
+                                        ? bf_to_f(P.embed[token_row(A.tok_in, lane, A.tok_stride, P.V) * P.d + row])
+                                        : *hp;
+                *hp = resid + pick<B>(res[i], lane);
+            }
         }
-    }
+    };
+    conv_rows<B, 4>(rows, count, (int)(K >> 3), x, epi);
 }
 
 template <int HD>
@@ -139,19 +148,19 @@ __global__ void __launch_bounds__(kConvThreads) k_head(Params P, StepArgs A, uin
         best_v[b] = -INFINITY;
         best_i[b] = 0x7FFFFFFF;
     }
-    for (uint32_t r = wave; r < count; r += kConvWaves) {
-        float acc[B];
-        row_dot<B>(rows, r, P.d >> 3, x, acc);
-        const int32_t row = (int32_t)(begin + r);
+    conv_rows<B, 4>(rows, count, P.d >> 3, x, [&](uint32_t r0, uint32_t nr, auto& res) {
+        for (uint32_t i = 0; i < nr; ++i) {
+            const int32_t row = (int32_t)(begin + r0 + i);
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-            if (head_better(acc[b], row, best_v[b], best_i[b])) {
-                best_v[b] = acc[b];
-                best_i[b] = row;
+            for (int b = 0; b < B; ++b) {
+                if (head_better(res[i][b], row, best_v[b], best_i[b])) {
+                    best_v[b] = res[i][b];
+                    best_i[b] = row;
+                }
             }
+            if (lane < B) A.logits[(size_t)lane * P.V + row] = pick<B>(res[i], lane);
         }
-        if (lane < B) A.logits[(size_t)lane * P.V + row] = pick<B>(acc, lane);
-    }
+    });
     if (lane < B) {
         HeadPart hp;
         hp.v = pick<B>(best_v, lane);

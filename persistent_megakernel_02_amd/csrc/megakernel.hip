@@ -158,6 +158,24 @@ __device__ __forceinline__ void dma_chunk(const char* src, uint32_t lds_addr) {
 // row_ptr(j); rb is a multiple of the chunk size on every fast path, so a chunk
 // never straddles two rows and its lane address is row base + 1 KB * k + 16 * lane.
 // ATTN rows are the 1 KB K and V blocks of consecutive position groups.
+// Same transfer with a wave-uniform base in SGPRs and a per-lane 32-bit offset:
+// the per-chunk address arithmetic runs on the scalar unit.
+__device__ __forceinline__ void dma_chunk_s(const char* base, uint32_t voff, uint32_t lds_addr) {
+    asm volatile(
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1 offset:0"
+        :
+        : "v"(voff), "s"(base), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+        : "memory");
+}
+
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
 template <int HD>
 struct RowSrc {
     uint16_t op;
@@ -245,6 +263,15 @@ __device__ void loader_wave(const Params& P, Ctl* ctl, char* ring, uint32_t q0, 
             if (P.trace) stall += (uint32_t)now_ticks() - ts;
         }
     };
+    auto issue_s = [&](const char* base, uint32_t voff) {
+        dma_chunk_s(base, voff, ring_base + (issued % kRingChunks) * kChunk);
+        ++issued;
+        if (issued - landed > (uint32_t)kLoaderLag) {
+            wait_vmcnt<kLoaderLag>();
+            landed = issued - kLoaderLag;
+            lds_st(&ctl->landed, landed);
+        }
+    };
     auto issue = [&](const char* src) {
         dma_chunk(src, ring_base + (issued % kRingChunks) * kChunk);
         ++issued;
@@ -274,14 +301,14 @@ __device__ void loader_wave(const Params& P, Ctl* ctl, char* ring, uint32_t q0, 
                 for (uint32_t j = 0; j < R.nrows && !stop; ++j) {
                     if (issued >= limit && !make_room()) { stop = true; break; }
                     const bool valid = (int)((j >> 1) * PPW) + lane_pos < R.ncached;
-                    issue(valid ? R.row_ptr(j) + lane16 : R.w0);
+                    issue_s(uniform_ptr(R.row_ptr(j)), valid ? lane16 : 0u);
                 }
             } else {
                 for (uint32_t j = 0; j < R.nrows && !stop; ++j) {
-                    const char* row = R.row_ptr(j) + lane16;
+                    const char* row = uniform_ptr(R.row_ptr(j));
                     for (uint32_t k = 0; k < cpr; ++k) {
                         if (issued >= limit && !make_room()) { stop = true; break; }
-                        issue(row + k * kChunk);
+                        issue_s(row + k * kChunk, lane16);
                     }
                 }
             }
@@ -417,6 +444,26 @@ struct CwBarrier {
     }
 };
 
+// Stream rows [0, nrows) of the current instruction from the ring in batches of
+// R consecutive rows; batch t goes to compute wave t mod kComputeWaves, so the
+// four waves work on neighbouring rows and the ring span stays small.
+template <int B, int R, class X, class Epi>
+__device__ __forceinline__ bool gemv_stream(const Params& P, Ctl* ctl, const char* ring, uint32_t S, uint32_t rb,
+                                            uint32_t nrows, const X& x, int wave, uint32_t* lw, Epi& epi) {
+    const int np = (int)(rb >> 4);
+    const RingRows rows{ring, S, rb};
+    for (uint32_t r0 = (uint32_t)wave * R; r0 < nrows; r0 += (uint32_t)R * kComputeWaves) {
+        const uint32_t nr = min((uint32_t)R, nrows - r0);
+        const uint32_t off = S + r0 * rb;
+        set_consumed(ctl, wave, off / kChunk);
+        if (!wait_landed(P, ctl, (off + nr * rb + kChunk - 1u) / kChunk, lw)) return false;
+        float res[R][B];
+        rows_dot<B, R>(rows, r0, (int)nr, np, x, res);
+        epi(r0, nr, res);
+    }
+    return true;
+}
+
 template <int B, int HD>
 __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xlds,
                              float* attn_lds, int wave, uint32_t q0, uint32_t q1, const int32_t* ctx) {
@@ -455,73 +502,58 @@ __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const
                 const bool from_embed = (in.op == OP_QKV && layer == 0);
                 rmsnorm_rows<B>(P.h, from_embed ? P.embed : nullptr, A.tok_in, A.tok_stride, P.V, gain, P.d, P.eps, xlds);
                 const uint32_t rb = (uint32_t)P.d * 2u;
-                const int np = P.d >> 3;
-                const RingRows rows{ring, S, rb};
                 const XLds x{xlds, (uint32_t)P.d};
-                if (in.op == OP_GATEUP) {
-                    for (uint32_t i = wave; i < in.count && ok; i += kComputeWaves) {
-                        const uint32_t off = S + 2u * i * rb;
-                        set_consumed(ctl, wave, off / kChunk);
-                        ok = wait_landed(P, ctl, (off + 2u * rb + kChunk - 1u) / kChunk, lw);
-                        if (!ok) break;
-                        float zg[B], zu[B];
-                        row_dot<B>(rows, 2u * i, np, x, zg);
-                        row_dot<B>(rows, 2u * i + 1u, np, x, zu);
-                        const uint32_t f = in.begin + i;
-                        if (lane < B) {
-                            const float a = silu_mul(pick<B>(zg, lane), pick<B>(zu, lane));
-                            P.act[(size_t)lane * P.F + f] = a;
+                const uint32_t nrows = in.op == OP_GATEUP ? 2u * in.count : in.count;
+                auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
+                    if (in.op == OP_GATEUP) {
+                        for (uint32_t i = 0; i + 1 < nr; i += 2) {
+                            const uint32_t f = in.begin + (r0 + i) / 2u;
+                            if (lane < B) P.act[(size_t)lane * P.F + f] = silu_mul(pick<B>(res[i], lane), pick<B>(res[i + 1], lane));
                         }
-                    }
-                } else {
-                    for (uint32_t r = wave; r < in.count && ok; r += kComputeWaves) {
-                        const uint32_t off = S + r * rb;
-                        set_consumed(ctl, wave, off / kChunk);
-                        ok = wait_landed(P, ctl, (off + rb + kChunk - 1u) / kChunk, lw);
-                        if (!ok) break;
-                        float acc[B];
-                        row_dot<B>(rows, r, np, x, acc);
-                        const uint32_t row = in.begin + r;
-                        if (in.op == OP_QKV) {
-                            if (lane < B) P.qkv[(size_t)lane * P.qkv_rows + row] = pick<B>(acc, lane);
-                        } else {
+                    } else if (in.op == OP_QKV) {
+                        for (uint32_t i = 0; i < nr; ++i)
+                            if (lane < B) P.qkv[(size_t)lane * P.qkv_rows + in.begin + r0 + i] = pick<B>(res[i], lane);
+                    } else {
+                        for (uint32_t i = 0; i < nr; ++i) {
+                            const int32_t row = (int32_t)(in.begin + r0 + i);
 #pragma unroll
                             for (int b = 0; b < B; ++b) {
-                                if (acc[b] != acc[b]) nan_seen = true;
-                                if (head_better(acc[b], (int32_t)row, best_v[b], best_i[b])) {
-                                    best_v[b] = acc[b];
-                                    best_i[b] = (int32_t)row;
+                                const float v = res[i][b];
+                                if (v != v) nan_seen = true;
+                                if (head_better(v, row, best_v[b], best_i[b])) {
+                                    best_v[b] = v;
+                                    best_i[b] = row;
                                 }
                             }
-                            if (lane < B) A.logits[(size_t)lane * P.V + row] = pick<B>(acc, lane);
+                            if (lane < B) A.logits[(size_t)lane * P.V + row] = pick<B>(res[i], lane);
                         }
                     }
-                }
+                };
+                if (rows_per_batch(rb) == 4) ok = gemv_stream<B, 4>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
+                else ok = gemv_stream<B, 2>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
                 break;
             }
             case OP_O:
             case OP_DOWN: {
                 const uint32_t K = in.op == OP_O ? (uint32_t)(P.Hq * HD) : (uint32_t)P.F;
                 const uint32_t rb = K * 2u;
-                const int np = (int)(K >> 3);
-                const RingRows rows{ring, S, rb};
                 const XGlobal x{in.op == OP_O ? P.attn : P.act, K};
-                for (uint32_t r = wave; r < in.count && ok; r += kComputeWaves) {
-                    const uint32_t off = S + r * rb;
-                    set_consumed(ctl, wave, off / kChunk);
-                    ok = wait_landed(P, ctl, (off + rb + kChunk - 1u) / kChunk, lw);
-                    if (!ok) break;
-                    float acc[B];
-                    row_dot<B>(rows, r, np, x, acc);
-                    const uint32_t row = in.begin + r;
-                    if (lane < B) {
-                        float* hp = P.h + (size_t)lane * P.d + row;
-                        const float resid = (in.op == OP_O && layer == 0)
-                                                ? bf_to_f(P.embed[token_row(A.tok_in, lane, A.tok_stride, P.V) * P.d + row])
-                                                : *hp;
-                        *hp = resid + pick<B>(acc, lane);
+                auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
+                    for (uint32_t i = 0; i < nr; ++i) {
+                        const uint32_t row = in.begin + r0 + i;
+                        if (lane < B) {
+                            float* hp = P.h + (size_t)lane * P.d + row;
+                            const float resid = (in.op == OP_O && layer == 0)
+                                                    ? bf_to_f(P.embed[token_row(A.tok_in, lane, A.tok_stride, P.V) * P.d + row])
+                                                    : *hp;
+                            *hp = resid + pick<B>(res[i], lane);
+                        }
                     }
-                }
+                };
+                const int R = rows_per_batch(rb);
+                if (R == 4) ok = gemv_stream<B, 4>(P, ctl, ring, S, rb, in.count, x, wave, lw, epi);
+                else if (R == 2) ok = gemv_stream<B, 2>(P, ctl, ring, S, rb, in.count, x, wave, lw, epi);
+                else ok = gemv_stream<B, 1>(P, ctl, ring, S, rb, in.count, x, wave, lw, epi);
                 break;
             }
             case OP_ATTN: {

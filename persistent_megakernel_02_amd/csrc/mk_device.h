@@ -78,6 +78,19 @@ __device__ __forceinline__ float wave_max(float v) {
     for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
     return v;
 }
+// Total over the 64 lanes with DPP, in a fixed tree: quad butterflies, half-row
+// and row mirrors (16-lane sums), then row broadcasts accumulate rows 0..3 into
+// lane 63.  The value of lane 63 is returned to every lane (scalar).
+__device__ __forceinline__ float wave_total(float v) {
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x140, 0xF, 0xF, false);  // row_mirror
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64).
 __device__ __forceinline__ float group_sum(float v, int width) {
     for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m, 64);
@@ -103,43 +116,49 @@ __device__ void rmsnorm_rows(const float* __restrict__ h, const uint16_t* __rest
                              int d, float eps, float* __restrict__ xout) {
     const int lane = lane_id();
     const int np = d >> 3;
+    constexpr int kMaxPieces = 8;  // d <= 4096: at most 8 pieces per lane
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         const float* hb = h + (size_t)b * d;
         const uint16_t* eb = emb ? emb + token_row(tok, b, tok_stride, V) * d : nullptr;
+        float v[kMaxPieces][8];
         float ss = 0.f;
-        for (int p = lane; p < np; p += 64) {
-            float v[8];
-            if (eb) {
-                uint4 u = *(const uint4*)(eb + 8 * p);
-                v[0] = bf_lo(u.x); v[1] = bf_hi(u.x); v[2] = bf_lo(u.y); v[3] = bf_hi(u.y);
-                v[4] = bf_lo(u.z); v[5] = bf_hi(u.z); v[6] = bf_lo(u.w); v[7] = bf_hi(u.w);
-            } else {
-                float4 a = *(const float4*)(hb + 8 * p), c = *(const float4*)(hb + 8 * p + 4);
-                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
-            }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
-        }
-        ss = wave_sum(ss);
-        const float r = 1.0f / sqrtf(ss / (float)d + eps);
-        for (int p = lane; p < np; p += 64) {
-            float v[8];
-            if (eb) {
-                uint4 u = *(const uint4*)(eb + 8 * p);
-                v[0] = bf_lo(u.x); v[1] = bf_hi(u.x); v[2] = bf_lo(u.y); v[3] = bf_hi(u.y);
-                v[4] = bf_lo(u.z); v[5] = bf_hi(u.z); v[6] = bf_lo(u.w); v[7] = bf_hi(u.w);
-            } else {
-                float4 a = *(const float4*)(hb + 8 * p), c = *(const float4*)(hb + 8 * p + 4);
-                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+        for (int j = 0; j < kMaxPieces; ++j) {
+            const int p = lane + 64 * j;
+            if (p < np) {
+                if (eb) {
+                    uint4 u = *(const uint4*)(eb + 8 * p);
+                    v[j][0] = bf_lo(u.x); v[j][1] = bf_hi(u.x); v[j][2] = bf_lo(u.y); v[j][3] = bf_hi(u.y);
+                    v[j][4] = bf_lo(u.z); v[j][5] = bf_hi(u.z); v[j][6] = bf_lo(u.w); v[j][7] = bf_hi(u.w);
+                } else {
+                    float4 a = *(const float4*)(hb + 8 * p), c = *(const float4*)(hb + 8 * p + 4);
+                    v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
+                    v[j][4] = c.x; v[j][5] = c.y; v[j][6] = c.z; v[j][7] = c.w;
+                }
             }
-            uint4 gv = *(const uint4*)(g + 8 * p);
-            float gg[8] = {bf_lo(gv.x), bf_hi(gv.x), bf_lo(gv.y), bf_hi(gv.y),
-                           bf_lo(gv.z), bf_hi(gv.z), bf_lo(gv.w), bf_hi(gv.w)};
-            float4 o0 = make_float4(v[0] * r * gg[0], v[1] * r * gg[1], v[2] * r * gg[2], v[3] * r * gg[3]);
-            float4 o1 = make_float4(v[4] * r * gg[4], v[5] * r * gg[5], v[6] * r * gg[6], v[7] * r * gg[7]);
-            *(float4*)(xout + (size_t)b * d + 8 * p) = o0;
-            *(float4*)(xout + (size_t)b * d + 8 * p + 4) = o1;
+        }
+#pragma unroll
+        for (int j = 0; j < kMaxPieces; ++j)
+            if (lane + 64 * j < np)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss = fmaf(v[j][e], v[j][e], ss);
+        ss = wave_total(ss);
+        const float r = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+        for (int j = 0; j < kMaxPieces; ++j) {
+            const int p = lane + 64 * j;
+            if (p < np) {
+                uint4 gv = *(const uint4*)(g + 8 * p);
+                float gg[8] = {bf_lo(gv.x), bf_hi(gv.x), bf_lo(gv.y), bf_hi(gv.y),
+                               bf_lo(gv.z), bf_hi(gv.z), bf_lo(gv.w), bf_hi(gv.w)};
+                float4 o0 = make_float4(v[j][0] * r * gg[0], v[j][1] * r * gg[1], v[j][2] * r * gg[2],
+                                        v[j][3] * r * gg[3]);
+                float4 o1 = make_float4(v[j][4] * r * gg[4], v[j][5] * r * gg[5], v[j][6] * r * gg[6],
+                                        v[j][7] * r * gg[7]);
+                *(float4*)(xout + (size_t)b * d + 8 * p) = o0;
+                *(float4*)(xout + (size_t)b * d + 8 * p + 4) = o1;
+            }
         }
     }
 }
@@ -175,37 +194,44 @@ struct XGlobal {
     }
 };
 
-// acc[b] = dot(row r, x_b) over np pieces; every lane returns the full sums.
-// Per lane the pieces accumulate in ascending order, then a butterfly reduces.
-template <int B, class Rows, class X>
-__device__ __forceinline__ void row_dot(const Rows& rows, uint32_t r, int np, const X& x, float (&acc)[B]) {
+// out[i][b] = dot(row r0 + i, x_b) for i < nr (nr <= R rows processed together:
+// the activation pieces are read once for all of them).  Per row, lane l
+// accumulates pieces p = l, l + 64, ... in ascending order, then wave_total
+// reduces in its fixed tree; the value of a row never depends on R, nr or on
+// which other rows share the batch.
+template <int B, int R, class Rows, class X>
+__device__ __forceinline__ void rows_dot(const Rows& rows, uint32_t r0, int nr, int np, const X& x,
+                                         float (&out)[R][B]) {
     const int lane = lane_id();
+    float acc[R][B];
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = 0.f;
-    int p = lane;
-    for (; p + 192 < np; p += 256) {
-        uint4 w[4] = {rows.piece(r, p), rows.piece(r, p + 64), rows.piece(r, p + 128), rows.piece(r, p + 192)};
+    for (int i = 0; i < R; ++i)
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-            float4 xa[4], xb[4];
+        for (int b = 0; b < B; ++b) acc[i][b] = 0.f;
+#pragma unroll 2
+    for (int p = lane; p < np; p += 64) {
+        float4 xa[B], xb[B];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) x.piece(b, p + 64 * u, xa[u], xb[u]);
+        for (int b = 0; b < B; ++b) x.piece(b, (uint32_t)p, xa[b], xb[b]);
+        uint4 w[R];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) acc[b] = dot8(w[u], xa[u], xb[u], acc[b]);
-        }
-    }
-    for (; p < np; p += 64) {
-        const uint4 w0 = rows.piece(r, p);
+        for (int i = 0; i < R; ++i)
+            if (i < nr) w[i] = rows.piece(r0 + i, (uint32_t)p);
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-            float4 xa, xb;
-            x.piece(b, p, xa, xb);
-            acc[b] = dot8(w0, xa, xb, acc[b]);
-        }
+        for (int i = 0; i < R; ++i)
+            if (i < nr)
+#pragma unroll
+                for (int b = 0; b < B; ++b) acc[i][b] = dot8(w[i], xa[b], xb[b], acc[i][b]);
     }
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = wave_sum(acc[b]);
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int b = 0; b < B; ++b) out[i][b] = (i < nr) ? wave_total(acc[i][b]) : 0.f;
 }
+
+// Rows processed together for a row of `rb` bytes: the batch of the four
+// compute waves stays within 64 KB of the ring.
+__host__ __device__ constexpr int rows_per_batch(uint32_t rb) { return rb <= 4096u ? 4 : rb <= 8192u ? 2 : 1; }
 
 template <int B>
 __device__ __forceinline__ float pick(const float (&a)[B], int i) {
