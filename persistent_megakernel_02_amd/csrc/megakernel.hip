@@ -154,15 +154,15 @@ __device__ __forceinline__ void dma_chunk(const char* src, uint32_t lds_addr) {
         : "memory");
 }
 
-// Row model of an instruction's stream: row j of `rb` bytes starts at
-// row_ptr(j); rb is a multiple of the chunk size on every fast path, so a chunk
-// never straddles two rows and its lane address is row base + 1 KB * k + 16 * lane.
-// ATTN rows are the 1 KB K and V blocks of consecutive position groups.
-// Same transfer with a wave-uniform base in SGPRs and a per-lane 32-bit offset:
-// the per-chunk address arithmetic runs on the scalar unit.
+// Same transfer with a wave-uniform base in SGPRs and a per-lane 32-bit offset.
+// The base usually comes out of v_readfirstlane, a VALU write of an SGPR, and a
+// VMEM instruction that reads such an SGPR as its address needs five wait
+// states after the write (CDNA3/CDNA4 ISA, manually inserted wait states).  The
+// compiler does not look inside asm for hazards, so the block supplies them
+// itself; the same s_nop also covers the one wait state after the M0 write.
 __device__ __forceinline__ void dma_chunk_s(const char* base, uint32_t voff, uint32_t lds_addr) {
     asm volatile(
-        "s_nop 0\n\t"
+        "s_nop 4\n\t"
         "global_load_lds_dwordx4 %0, %1 offset:0"
         :
         : "v"(voff), "s"(base), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
@@ -176,70 +176,83 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
     return (const char*)(((uint64_t)hi << 32) | lo);
 }
 
-template <int HD>
-struct RowSrc {
-    uint16_t op;
-    uint32_t rb, nrows, begin;
-    const char *w0, *w1, *w2;  // tensors (QKV: q, k, v; GATEUP: gate, up; ATTN: K, V rows of (layer, b, g))
-    uint32_t nq, nk;           // QKV row split
-    int s0, ncached;           // ATTN positions
-    __device__ __forceinline__ const char* row_ptr(uint32_t j) const {
-        switch (op) {
-            case OP_QKV: {
-                const uint32_t row = begin + j;
-                return row < nq ? w0 + (size_t)row * rb
-                     : row < nq + nk ? w1 + (size_t)(row - nq) * rb : w2 + (size_t)(row - nq - nk) * rb;
-            }
-            case OP_GATEUP: return ((j & 1u) ? w1 : w0) + (size_t)(begin + (j >> 1)) * rb;
-            case OP_ATTN: return ((j & 1u) ? w1 : w0) + (size_t)(j >> 1) * kChunk;
-            default: return w0 + (size_t)(begin + j) * rb;
-        }
-    }
+// Byte model of an instruction's stream on the fast path.  Consecutive rows of a
+// row-major matrix are consecutive bytes, so every stream is one of:
+//  - up to three contiguous byte ranges read in order (QKV: the q, k and v rows
+//    of the tile; O, DOWN, HEAD: one range);
+//  - two matrices interleaved row by row (GATEUP: gate row r then up row r),
+//    `per` chunks of each in turn;
+//  - the K and V blocks of consecutive position groups interleaved (ATTN), one
+//    chunk each, lanes past the cached positions re-reading the block start.
+// Only pointers and chunk counts, all wave-uniform, so the loop runs on SGPRs.
+struct Stream {
+    const char* p[3];
+    uint32_t n[3];    // chunks per range (ranges), or pairs (interleaved)
+    uint32_t per;     // interleaved: chunks of each matrix per turn; 0 = ranges
+    int ncached;      // ATTN: valid positions of the split
+    bool attn;
 };
 
 template <int HD>
-__device__ __forceinline__ bool setup_rows(const Params& P, const Instr& in, const DevLayer& Lw, const int32_t* ctx,
-                                           RowSrc<HD>& R) {
-    R.op = in.op;
-    R.begin = in.begin;
-    R.nq = (uint32_t)(P.Hq * HD);
-    R.nk = (uint32_t)(P.Hkv * HD);
-    R.s0 = 0;
-    R.ncached = 0;
+__device__ __forceinline__ bool setup_stream(const Params& P, const Instr& in, const DevLayer& Lw, const int32_t* ctx,
+                                             Stream& S) {
+    S.per = 0;
+    S.attn = false;
+    S.ncached = 0;
+    S.n[1] = S.n[2] = 0;
+    S.p[1] = S.p[2] = nullptr;
+    uint32_t rb = 0;
     switch (in.op) {
-        case OP_QKV:
-            R.rb = (uint32_t)P.d * 2u; R.nrows = in.count;
-            R.w0 = (const char*)Lw.wq; R.w1 = (const char*)Lw.wk; R.w2 = (const char*)Lw.wv;
+        case OP_QKV: {
+            rb = (uint32_t)P.d * 2u;
+            const uint32_t nq = (uint32_t)(P.Hq * HD), nk = (uint32_t)(P.Hkv * HD);
+            const uint32_t r0 = in.begin, r1 = in.begin + in.count;
+            const uint32_t q0 = min(r0, nq), q1 = min(r1, nq);
+            const uint32_t k0 = min(max(r0, nq), nq + nk) - nq, k1 = min(max(r1, nq), nq + nk) - nq;
+            const uint32_t v0 = max(r0, nq + nk) - nq - nk, v1 = max(r1, nq + nk) - nq - nk;
+            S.p[0] = (const char*)Lw.wq + (size_t)q0 * rb; S.n[0] = q1 - q0;
+            S.p[1] = (const char*)Lw.wk + (size_t)k0 * rb; S.n[1] = k1 - k0;
+            S.p[2] = (const char*)Lw.wv + (size_t)v0 * rb; S.n[2] = v1 - v0;
             break;
+        }
         case OP_O:
-            R.rb = (uint32_t)(P.Hq * HD) * 2u; R.nrows = in.count; R.w0 = (const char*)Lw.wo;
-            break;
-        case OP_GATEUP:
-            R.rb = (uint32_t)P.d * 2u; R.nrows = 2u * in.count;
-            R.w0 = (const char*)Lw.w_gate; R.w1 = (const char*)Lw.w_up;
+            rb = (uint32_t)(P.Hq * HD) * 2u;
+            S.p[0] = (const char*)Lw.wo + (size_t)in.begin * rb; S.n[0] = in.count;
             break;
         case OP_DOWN:
-            R.rb = (uint32_t)P.F * 2u; R.nrows = in.count; R.w0 = (const char*)Lw.w_down;
+            rb = (uint32_t)P.F * 2u;
+            S.p[0] = (const char*)Lw.w_down + (size_t)in.begin * rb; S.n[0] = in.count;
             break;
         case OP_HEAD:
-            R.rb = (uint32_t)P.d * 2u; R.nrows = in.count; R.w0 = (const char*)P.head;
+            rb = (uint32_t)P.d * 2u;
+            S.p[0] = (const char*)P.head + (size_t)in.begin * rb; S.n[0] = in.count;
             break;
+        case OP_GATEUP:
+            rb = (uint32_t)P.d * 2u;
+            S.p[0] = (const char*)Lw.w_gate + (size_t)in.begin * rb;
+            S.p[1] = (const char*)Lw.w_up + (size_t)in.begin * rb;
+            S.n[0] = in.count;
+            S.per = rb / kChunk;
+            return (rb & (kChunk - 1u)) == 0;
         case OP_ATTN: {
             const int per_b = P.Hkv * P.nsplit;
             const int b = (int)in.begin / per_b, g = ((int)in.begin % per_b) / P.nsplit, s = (int)in.begin % P.nsplit;
             const SplitRange Rg = split_range<HD>(ctx[b], s, P.nsplit);
             const size_t base = ((((size_t)in.layer * P.kv_b + b) * P.Hkv + g) * P.S + Rg.s0) * HD;
-            R.w0 = (const char*)(P.kcache + base);
-            R.w1 = (const char*)(P.vcache + base);
-            R.rb = kChunk;
-            R.nrows = 2u * (uint32_t)Rg.ngroups;
-            R.s0 = Rg.s0;
-            R.ncached = Rg.ncached;
+            S.p[0] = (const char*)(P.kcache + base);
+            S.p[1] = (const char*)(P.vcache + base);
+            S.n[0] = (uint32_t)Rg.ngroups;
+            S.per = 1;
+            S.ncached = Rg.ncached;
+            S.attn = true;
             return true;
         }
         default: return false;
     }
-    return (R.rb & (kChunk - 1u)) == 0;  // fast path needs whole chunks per row
+    if (rb & (kChunk - 1u)) return false;  // fast path needs whole chunks per row
+    const uint32_t cpr = rb / kChunk;
+    S.n[0] *= cpr; S.n[1] *= cpr; S.n[2] *= cpr;
+    return true;
 }
 
 template <int HD>
@@ -292,23 +305,33 @@ __device__ void loader_wave(const Params& P, Ctl* ctl, char* ring, uint32_t q0, 
         stall = 0;
         if (nch == 0) continue;
         const DevLayer Lw = ld_const(P.layers + (in.layer < P.L ? in.layer : 0));
-        RowSrc<HD> R;
-        if (setup_rows<HD>(P, in, Lw, ctx, R)) {
-            const uint32_t cpr = R.rb / kChunk;
-            if (in.op == OP_ATTN) {
-                constexpr int LPP = AttnGeom<HD>::LPP, PPW = AttnGeom<HD>::PPW;
-                const int lane_pos = lane_id() / LPP;
-                for (uint32_t j = 0; j < R.nrows && !stop; ++j) {
-                    if (issued >= limit && !make_room()) { stop = true; break; }
-                    const bool valid = (int)((j >> 1) * PPW) + lane_pos < R.ncached;
-                    issue_s(uniform_ptr(R.row_ptr(j)), valid ? lane16 : 0u);
+        Stream S;
+        if (setup_stream<HD>(P, in, Lw, ctx, S)) {
+            if (S.per == 0) {
+#pragma unroll
+                for (int r = 0; r < 3; ++r) {
+                    const char* base = uniform_ptr(S.p[r]);
+                    for (uint32_t c = 0; c < S.n[r] && !stop; ++c) {
+                        if (issued >= limit && !make_room()) { stop = true; break; }
+                        issue_s(base, c * kChunk + lane16);
+                    }
                 }
             } else {
-                for (uint32_t j = 0; j < R.nrows && !stop; ++j) {
-                    const char* row = uniform_ptr(R.row_ptr(j));
-                    for (uint32_t k = 0; k < cpr; ++k) {
+                const char* ba = uniform_ptr(S.p[0]);
+                const char* bb = uniform_ptr(S.p[1]);
+                // ATTN: lanes whose position lies past the cached ones re-read the block start
+                const int lane_pos = lane_id() / AttnGeom<HD>::LPP;
+                const uint32_t rbytes = S.per * kChunk;
+                for (uint32_t r = 0; r < S.n[0] && !stop; ++r) {
+                    const bool valid = !S.attn || (int)(r * AttnGeom<HD>::PPW) + lane_pos < S.ncached;
+                    const uint32_t lane_off = valid ? lane16 : 0u;
+                    for (uint32_t k = 0; k < S.per && !stop; ++k) {
                         if (issued >= limit && !make_room()) { stop = true; break; }
-                        issue_s(row + k * kChunk, lane16);
+                        issue_s(ba, r * rbytes + k * kChunk + lane_off);
+                    }
+                    for (uint32_t k = 0; k < S.per && !stop; ++k) {
+                        if (issued >= limit && !make_room()) { stop = true; break; }
+                        issue_s(bb, r * rbytes + k * kChunk + lane_off);
                     }
                 }
             }
@@ -389,31 +412,28 @@ __device__ __forceinline__ bool wait_flags(const Params& P, Ctl* ctl, const uint
     return true;
 }
 
-// Wait until the loader has `need` chunks resident.
-__device__ __forceinline__ bool wait_landed(const Params& P, Ctl* ctl, uint32_t need, uint32_t* waited = nullptr) {
+// Wait until the loader has `need` chunks resident; adds the ticks spent waiting
+// to `waited` (read only by the trace).
+__device__ __forceinline__ bool wait_landed(const Params& P, Ctl* ctl, uint32_t need, uint32_t& waited) {
     if (lds_ld(&ctl->landed) >= need) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         return true;
     }
     const uint64_t t0 = now_ticks();
-    struct Acc {
-        uint32_t* w;
-        uint64_t t0;
-        __device__ ~Acc() {
-            if (w) *w += (uint32_t)(now_ticks() - t0);
-        }
-    } acc{waited, t0};
     uint32_t polls = 0;
+    bool ok = true;
     while (lds_ld(&ctl->landed) < need) {
-        if (lds_ld(&ctl->abort)) return false;
+        if (lds_ld(&ctl->abort)) { ok = false; break; }
         if ((++polls & 255u) == 0 && now_ticks() - t0 > P.spin_ticks) {
             raise_error(P, ctl, DERR_TIMEOUT, 0xFFFFFFFFu, need);
-            return false;
+            ok = false;
+            break;
         }
         __builtin_amdgcn_s_sleep(0);
     }
+    waited += (uint32_t)(now_ticks() - t0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    return true;
+    return ok;
 }
 
 __device__ __forceinline__ void set_consumed(Ctl* ctl, int wave, uint32_t chunk) {
@@ -449,7 +469,7 @@ struct CwBarrier {
 // four waves work on neighbouring rows and the ring span stays small.
 template <int B, int R, class X, class Epi>
 __device__ __forceinline__ bool gemv_stream(const Params& P, Ctl* ctl, const char* ring, uint32_t S, uint32_t rb,
-                                            uint32_t nrows, const X& x, int wave, uint32_t* lw, Epi& epi) {
+                                            uint32_t nrows, const X& x, int wave, uint32_t& lw, Epi& epi) {
     const int np = (int)(rb >> 4);
     const RingRows rows{ring, S, rb};
     for (uint32_t r0 = (uint32_t)wave * R; r0 < nrows; r0 += (uint32_t)R * kComputeWaves) {
@@ -490,7 +510,6 @@ __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const
         }
         if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
         uint32_t land_wait = 0;
-        uint32_t* lw = tr ? &land_wait : nullptr;
         const int layer = in.layer;
         const DevLayer Lw = ld_const(P.layers + (layer < P.L ? layer : 0));
         bool ok = true;
@@ -529,8 +548,8 @@ __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const
                         }
                     }
                 };
-                if (rows_per_batch(rb) == 4) ok = gemv_stream<B, 4>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
-                else ok = gemv_stream<B, 2>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
+                if (rows_per_batch(rb) == 4) ok = gemv_stream<B, 4>(P, ctl, ring, S, rb, nrows, x, wave, land_wait, epi);
+                else ok = gemv_stream<B, 2>(P, ctl, ring, S, rb, nrows, x, wave, land_wait, epi);
                 break;
             }
             case OP_O:
@@ -551,9 +570,9 @@ __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const
                     }
                 };
                 const int R = rows_per_batch(rb);
-                if (R == 4) ok = gemv_stream<B, 4>(P, ctl, ring, S, rb, in.count, x, wave, lw, epi);
-                else if (R == 2) ok = gemv_stream<B, 2>(P, ctl, ring, S, rb, in.count, x, wave, lw, epi);
-                else ok = gemv_stream<B, 1>(P, ctl, ring, S, rb, in.count, x, wave, lw, epi);
+                if (R == 4) ok = gemv_stream<B, 4>(P, ctl, ring, S, rb, in.count, x, wave, land_wait, epi);
+                else if (R == 2) ok = gemv_stream<B, 2>(P, ctl, ring, S, rb, in.count, x, wave, land_wait, epi);
+                else ok = gemv_stream<B, 1>(P, ctl, ring, S, rb, in.count, x, wave, land_wait, epi);
                 break;
             }
             case OP_ATTN: {
@@ -565,7 +584,7 @@ __device__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const
                 auto need = [&](int t) {
                     const uint32_t off = S + (uint32_t)t * 2048u;
                     set_consumed(ctl, wave, off / kChunk);
-                    if (!wait_landed(P, ctl, (off + 2048u) / kChunk, lw)) ok = false;
+                    if (!wait_landed(P, ctl, (off + 2048u) / kChunk, land_wait)) ok = false;
                 };
                 const CwBarrier barrier{ctl, &P, &bar_gen};
                 bool merged = false;
