@@ -13,8 +13,9 @@
  *        into one kernel; a per-SM plan of composite instructions whose
  *        dependencies are arranged before launch; an on-GPU interpreter with a
  *        uniform load/compute/store template; shared memory cut into pages so the
- *        next stage's weights load early; global-memory counters incremented when
- *        an instruction finishes and watched by dependants instead of a barrier.
+ *        next stage's weights load early; completion signals in global memory,
+ *        watched by dependants instead of a grid barrier (here carried by each
+ *        activation word as a tag naming its step and phase).
  *  [ROOT] same page, section "传统推理方式效率低下的根源剖析": the one-kernel-per-op
  *        design and its launch gaps (1.3-2.1 us even with graphs), the
  *        conventional path this library also provides (MK_MODE_GRAPH).
@@ -105,7 +106,7 @@ typedef struct {
 typedef struct mk_handle mk_handle;
 
 /* Bytes of caller-provided device memory that mk_create needs for this model and
- * runtime: the workspace (schedule, counters, activations, RoPE table) and the
+ * runtime: the workspace (schedule, tickets, tagged activations, RoPE table) and the
  * KV cache [2][n_layers][max_batch][n_kv_heads][max_seq][head_dim] bf16.
  * Host only; MK_E_UNSUPPORTED for shapes this build does not run. */
 mk_status mk_query_sizes(const mk_model_config* cfg, const mk_runtime_config* rt, size_t* workspace_bytes,
@@ -144,12 +145,16 @@ mk_status mk_decode_step(mk_handle* h, const int32_t* d_tokens_in, int32_t B, in
 /* Host mirror of the context lengths (what the enqueued steps will have reached). */
 mk_status mk_get_context_len(const mk_handle* h, int32_t* h_lens, int32_t B);
 
-/* Clear counters, the epoch and a latched device error (enqueued on `stream`). */
+/* Clear the merge tickets and a latched device error (enqueued on `stream`); the
+ * host mirror of the context lengths is re-read from the device.  The step
+ * counter behind the value tags keeps counting, so values an aborted step left
+ * behind never satisfy a later step. */
 mk_status mk_reset(mk_handle* h, void* stream);
 
-/* Test hook: fault 1 = the next step's spin-waits get a 1 ms watchdog and one
- * counter target is made unreachable, so every workgroup times out and exits;
- * fault 0 clears it. */
+/* Test hook: fault 1 = the next step runs with a 1 ms watchdog and its layer-0
+ * attention waits for a value tag that no instruction writes, so every
+ * workgroup times out or sees the error and exits (the step reports
+ * MK_E_DEVICE_TIMEOUT); fault 0 clears a pending fault.  Both modes. */
 mk_status mk_debug_inject(mk_handle* h, int32_t fault, int32_t arg);
 
 /* Human-readable status / last host-side error of a handle. */
@@ -157,18 +162,19 @@ const char* mk_status_string(mk_status s);
 const char* mk_last_error(const mk_handle* h);
 
 /* Host-side description of the schedule (for tests and reports).  Fills up to
- * `cap` int64 values: [0] compute units, [1] instructions, [2] counters,
- * [3] max instructions on one CU, [4] weight bytes per step, [5] verifier result
- * (0 = ok), [6] attention splits, [7] phases. */
+ * `cap` int64 values: [0] compute units, [1] instructions, [2] LDS ring chunks
+ * (1 KB each), [3] max instructions on one CU, [4] weight bytes per step,
+ * [5] verifier result (0 = ok), [6] attention splits, [7] phases, [8] LDS bytes of
+ * staged activations, [9] LM-head instructions. */
 mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* rt, int32_t num_cus, int64_t* out,
                           int32_t cap);
 
 /* Copy the device timeline of the last megakernel step (needs trace = 1).
  * Per compute unit `records_per_cu` records of 8 uint32: {op | layer << 16,
- * dependency-wait start, wait end, compute end, signal end, loader issue end,
- * 0, 0}, times = low 32 bits of the 100 MHz s_memrealtime clock, in queue
- * order.  With h_buf == NULL only *written (the byte size) is set.  Synchronises
- * the handle's creation stream. */
+ * start, inputs staged, compute end, end, loader issue end, ticks waiting for
+ * the loader, ticks the loader waited for ring space}, times = low 32 bits of
+ * the 100 MHz s_memrealtime clock, in queue order.  With h_buf == NULL only
+ * *written (the byte size) is set.  Synchronises the handle's creation stream. */
 mk_status mk_read_trace(mk_handle* h, void* h_buf, size_t bytes, size_t* written, int32_t* records_per_cu);
 
 /* Number of kernel launches one decode step makes in the handle's mode. */

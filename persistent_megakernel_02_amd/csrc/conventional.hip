@@ -2,9 +2,10 @@
 // head, replayed from a hipGraph.  This is the design the megakernel replaces
 // (page "斯坦福团队新作让Llama1B实现毫秒级推理获Karpathy盛赞", section
 // "传统推理方式效率低下的根源剖析": many small kernels in sequence, each launch leaving
-// a gap in which no weight is loaded).  Every kernel calls the same tile
-// functions as the megakernel with the same four-wave lane mapping, so the two
-// paths give bitwise-identical logits and tokens.
+// a gap in which no weight is loaded).  Every kernel stages its inputs and calls
+// the same tile functions as the megakernel with the same four-wave lane mapping,
+// so the two paths give bitwise-identical logits and tokens.  Kernel order makes
+// every tag match on the first poll.
 #include <hip/hip_runtime.h>
 
 #include "mk_device.h"
@@ -13,109 +14,207 @@ namespace mk {
 
 constexpr int kConvWaves = kComputeWaves;  // same wave count per item as the megakernel
 constexpr int kConvThreads = 64 * kConvWaves;
-constexpr int kRowsPerBlock = 16;
+constexpr uint32_t kRowsPerBlock = 16;
 
-struct QkvRows {
-    const uint16_t *wq, *wk, *wv;
-    uint32_t d, nq, nk, begin;
-    __device__ __forceinline__ uint4 piece(uint32_t r, uint32_t p) const {
-        const uint32_t row = begin + r;
-        const uint16_t* base = row < nq ? wq + (size_t)row * d
-                             : row < nq + nk ? wk + (size_t)(row - nq) * d
-                                             : wv + (size_t)(row - nq - nk) * d;
-        return *(const uint4*)(base + 8 * p);
-    }
-};
-struct PlainRows {
-    const uint16_t* w;
-    uint32_t k, begin;
-    __device__ __forceinline__ uint4 piece(uint32_t r, uint32_t p) const {
-        return *(const uint4*)(w + (size_t)(begin + r) * k + 8 * p);
-    }
-};
-struct PairRows {  // stream row 2i = gate row, 2i + 1 = up row of f = begin + i
-    const uint16_t *wg, *wu;
-    uint32_t d, begin;
-    __device__ __forceinline__ uint4 piece(uint32_t r, uint32_t p) const {
-        const uint16_t* w = (r & 1u) ? wu : wg;
-        return *(const uint4*)(w + (size_t)(begin + (r >> 1)) * d + 8 * p);
+struct BlockBarrier {
+    __device__ __forceinline__ bool operator()() {
+        __syncthreads();
+        return true;
     }
 };
 
-// Rows [0, count) of a block in batches of R rows per wave (the same tile
-// function as the megakernel, so every row's value is bitwise identical).
-template <int B, int R, class Rows, class X, class Epi>
-__device__ __forceinline__ void conv_rows(const Rows& rows, uint32_t count, int np, const X& x, Epi&& epi) {
+// R rows of a batch read straight from global memory.
+template <int R>
+struct GlobalBatch {
+    const uint16_t* row[R];
+    __device__ __forceinline__ uint4 piece(uint32_t i, uint32_t p) const {
+        return *(const uint4*)(row[i] + 8 * p);
+    }
+};
+
+// Row j of an instruction's row sequence (QKV: [Wq; Wk; Wv] rows from `begin`;
+// GATEUP: gate row, up row of f = begin + j / 2; others: rows from `begin`).
+template <int OP>
+__device__ __forceinline__ const uint16_t* seq_row(const Params& P, const DevLayer& Lw, uint32_t begin, uint32_t j) {
+    if (OP == OP_QKV) {
+        const uint32_t row = begin + j, nq = (uint32_t)(P.Hq * P.hd), nk = (uint32_t)(P.Hkv * P.hd);
+        return row < nq ? Lw.wq + (size_t)row * P.d
+             : row < nq + nk ? Lw.wk + (size_t)(row - nq) * P.d
+                             : Lw.wv + (size_t)(row - nq - nk) * P.d;
+    } else if (OP == OP_GATEUP) {
+        return ((j & 1u) ? Lw.w_up : Lw.w_gate) + (size_t)(begin + (j >> 1)) * P.d;
+    } else if (OP == OP_HEAD) {
+        return P.head + (size_t)(begin + j) * P.d;
+    } else if (OP == OP_O) {
+        return Lw.wo + (size_t)(begin + j) * (P.Hq * P.hd);
+    } else {
+        return Lw.w_down + (size_t)(begin + j) * P.F;
+    }
+}
+
+// Rows [0, nrows) of the block in batches of R rows per wave (rows of a short
+// last batch repeat its first row; their results are not used).
+template <int B, int R, int OP, class X, class Epi>
+__device__ __forceinline__ void conv_rows(const Params& P, const DevLayer& Lw, uint32_t begin, uint32_t nrows,
+                                          uint32_t rb, const X& x, Epi& epi) {
     const int wave = threadIdx.x >> 6;
-    for (uint32_t r0 = (uint32_t)wave * R; r0 < count; r0 += (uint32_t)R * kConvWaves) {
-        const uint32_t nr = min((uint32_t)R, count - r0);
+    for (uint32_t r0 = (uint32_t)wave * R; r0 < nrows; r0 += (uint32_t)R * kConvWaves) {
+        const uint32_t nr = min((uint32_t)R, nrows - r0);
+        GlobalBatch<R> rows;
+#pragma unroll
+        for (int i = 0; i < R; ++i) rows.row[i] = seq_row<OP>(P, Lw, begin, r0 + ((uint32_t)i < nr ? (uint32_t)i : 0u));
         float res[R][B];
-        rows_dot<B, R>(rows, r0, (int)nr, np, x, res);
+        rows_dot<B, R>(rows, (int)(rb >> 4), x, res);
         epi(r0, nr, res);
     }
 }
 
-template <int B>
-__global__ void __launch_bounds__(kConvThreads) k_qkv(Params P, StepArgs A, int layer) {
-    __shared__ __attribute__((aligned(16))) float xs[kXBytes / 4];
-    const int lane = lane_id();
-    const DevLayer Lw = P.layers[layer];
-    rmsnorm_rows<B>(P.h, layer == 0 ? P.embed : nullptr, A.tok_in, A.tok_stride, P.V, Lw.attn_norm, P.d, P.eps, xs);
-    const uint32_t begin = blockIdx.x * kRowsPerBlock;
-    const uint32_t count = min((uint32_t)kRowsPerBlock, (uint32_t)P.qkv_rows - begin);
-    const QkvRows rows{Lw.wq, Lw.wk, Lw.wv, (uint32_t)P.d, (uint32_t)(P.Hq * P.hd), (uint32_t)(P.Hkv * P.hd), begin};
-    const XLds x{xs, (uint32_t)P.d};
-    conv_rows<B, 4>(rows, count, P.d >> 3, x, [&](uint32_t r0, uint32_t nr, auto& res) {
-        for (uint32_t i = 0; i < nr; ++i)
-            if (lane < B) P.qkv[(size_t)lane * P.qkv_rows + begin + r0 + i] = pick<B>(res[i], lane);
-    });
+template <int B, int OP, class X, class Epi>
+__device__ __forceinline__ void conv_rows_auto(const Params& P, const DevLayer& Lw, uint32_t begin, uint32_t nrows,
+                                               uint32_t rb, const X& x, Epi& epi) {
+    const int R = rows_per_batch(rb);
+    if (R >= 4) conv_rows<B, 4, OP>(P, Lw, begin, nrows, rb, x, epi);
+    else if (R == 2 || OP == OP_GATEUP) conv_rows<B, 2, OP>(P, Lw, begin, nrows, rb, x, epi);
+    else conv_rows<B, 1, OP>(P, Lw, begin, nrows, rb, x, epi);
 }
 
-template <int B>
-__global__ void __launch_bounds__(kConvThreads) k_gateup(Params P, StepArgs A, int layer) {
-    __shared__ __attribute__((aligned(16))) float xs[kXBytes / 4];
-    const int lane = lane_id();
-    const DevLayer Lw = P.layers[layer];
-    rmsnorm_rows<B>(P.h, nullptr, A.tok_in, A.tok_stride, P.V, Lw.mlp_norm, P.d, P.eps, xs);
+// RMSNorm + rows: QKV, GATEUP (row pairs) and the LM head.
+template <int B, int OP>
+__global__ void __launch_bounds__(kConvThreads) k_norm_gemv(Params P, StepArgs A, int layer) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    __shared__ float ssp[kMaxBatch][kConvWaves];
+    float* xs = (float*)lds;
+    const int wave = threadIdx.x >> 6, lane = lane_id();
+    Spin spin(&P, nullptr);
+    const DevLayer Lw = P.layers[layer < P.L ? layer : 0];
+    const uint16_t* gain = OP == OP_QKV ? Lw.attn_norm : OP == OP_GATEUP ? Lw.mlp_norm : P.final_norm;
+    const uint32_t tag_in = OP == OP_QKV      ? phase_tag(A.tag0, layer - 1, 4)
+                            : OP == OP_GATEUP ? phase_tag(A.tag0, layer, 2)
+                                              : phase_tag(A.tag0, P.L - 1, 4);
+    const uint32_t d = (uint32_t)P.d;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float ss = 0.f;
+        if (OP == OP_QKV && layer == 0) {
+            stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * d, d, xs + b * d, gain, wave, kConvWaves,
+                       ss);
+        } else if (!stage_tagged<true>(P.h + (size_t)b * d, d, tag_in, xs + b * d, gain, wave, kConvWaves, spin, ss)) {
+            return;
+        }
+        ss = wave_total(ss);
+        if (lane == 0) ssp[b][wave] = ss;
+    }
+    __syncthreads();
+    float r[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) r[b] = rms_scale(ssp[b], kConvWaves, P.d, P.eps);
+    const uint32_t total = OP == OP_QKV ? (uint32_t)P.qkv_rows : OP == OP_GATEUP ? (uint32_t)P.F : (uint32_t)P.V;
     const uint32_t begin = blockIdx.x * kRowsPerBlock;
-    const uint32_t count = min((uint32_t)kRowsPerBlock, (uint32_t)P.F - begin);
-    const PairRows rows{Lw.w_gate, Lw.w_up, (uint32_t)P.d, begin};
-    const XLds x{xs, (uint32_t)P.d};
-    conv_rows<B, 4>(rows, 2u * count, P.d >> 3, x, [&](uint32_t r0, uint32_t nr, auto& res) {
-        for (uint32_t i = 0; i + 1 < nr; i += 2)
-            if (lane < B)
-                P.act[(size_t)lane * P.F + begin + (r0 + i) / 2u] = silu_mul(pick<B>(res[i], lane), pick<B>(res[i + 1], lane));
-    });
+    const uint32_t count = min(kRowsPerBlock, total - begin);
+    const uint32_t nrows = OP == OP_GATEUP ? 2u * count : count;
+    const XLds x{xs, d};
+    if (OP == OP_QKV) {
+        const uint32_t tag_out = phase_tag(A.tag0, layer, 0);
+        auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
+            for (uint32_t i = 0; i < nr; ++i)
+                if (lane < B)
+                    st_tagged(P.qkv + (size_t)lane * P.qkv_rows + begin + r0 + i,
+                              pick<B>(res[i], lane) * pick<B>(r, lane), tag_out);
+        };
+        conv_rows_auto<B, OP>(P, Lw, begin, nrows, d * 2u, x, epi);
+    } else if (OP == OP_GATEUP) {
+        const uint32_t tag_out = phase_tag(A.tag0, layer, 3);
+        auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
+            for (uint32_t i = 0; i + 1 < nr; i += 2) {
+                const uint32_t f = begin + (r0 + i) / 2u;
+                if (lane < B) {
+                    const float rr = pick<B>(r, lane);
+                    st_tagged(P.act + (size_t)lane * P.F + f,
+                              silu_mul(pick<B>(res[i], lane) * rr, pick<B>(res[i + 1], lane) * rr), tag_out);
+                }
+            }
+        };
+        conv_rows_auto<B, OP>(P, Lw, begin, nrows, d * 2u, x, epi);
+    } else {
+        float best_v[B];
+        int32_t best_i[B];
+        bool nan_seen = false;
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            best_v[b] = -INFINITY;
+            best_i[b] = 0x7FFFFFFF;
+        }
+        auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
+            for (uint32_t i = 0; i < nr; ++i) {
+                const int32_t row = (int32_t)(begin + r0 + i);
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const float v = res[i][b] * r[b];
+                    if (v != v) nan_seen = true;
+                    if (head_better(v, row, best_v[b], best_i[b])) {
+                        best_v[b] = v;
+                        best_i[b] = row;
+                    }
+                }
+                if (lane < B) A.logits[(size_t)lane * P.V + row] = pick<B>(res[i], lane) * pick<B>(r, lane);
+            }
+        };
+        conv_rows_auto<B, OP>(P, Lw, begin, nrows, d * 2u, x, epi);
+        if (nan_seen) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) best_v[b] = __int_as_float(0x7FC00000);
+        }
+        head_publish<B>(P, A, blockIdx.x * kConvWaves + (uint32_t)wave, best_v, best_i, spin);
+    }
 }
 
 // O projection (is_down = 0) or down projection (is_down = 1) with residual add.
 template <int B>
-__global__ void __launch_bounds__(kConvThreads) k_proj_resid(Params P, StepArgs A, int layer, int is_down) {
-    const int lane = lane_id();
+__global__ void __launch_bounds__(kConvThreads) k_proj(Params P, StepArgs A, int layer, int is_down) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    float* xs = (float*)lds;
+    const int wave = threadIdx.x >> 6, lane = lane_id();
+    Spin spin(&P, nullptr);
     const DevLayer Lw = P.layers[layer];
     const uint32_t K = is_down ? (uint32_t)P.F : (uint32_t)(P.Hq * P.hd);
+    const uint32_t tag_x = is_down ? phase_tag(A.tag0, layer, 3) : phase_tag(A.tag0, layer, 1);
+    const uint32_t tag_res = is_down ? phase_tag(A.tag0, layer, 2) : phase_tag(A.tag0, layer - 1, 4);
+    const uint32_t tag_out = is_down ? phase_tag(A.tag0, layer, 4) : phase_tag(A.tag0, layer, 2);
     const uint32_t begin = blockIdx.x * kRowsPerBlock;
-    const uint32_t count = min((uint32_t)kRowsPerBlock, (uint32_t)P.d - begin);
-    const PlainRows rows{is_down ? Lw.w_down : Lw.wo, K, begin};
-    const XGlobal x{is_down ? P.act : P.attn, K};
+    const uint32_t count = min(kRowsPerBlock, (uint32_t)P.d - begin);
+    float* hres = xs + B * K;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float ss = 0.f;
+        if (!stage_tagged<false>((is_down ? P.act : P.attn) + (size_t)b * K, K, tag_x, xs + b * K, nullptr, wave,
+                                 kConvWaves, spin, ss))
+            return;
+        if (!is_down && layer == 0) {
+            stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * P.d + begin, count, hres + b * count,
+                       nullptr, wave, kConvWaves, ss);
+        } else if (!stage_tagged<false>(P.h + (size_t)b * P.d + begin, count, tag_res, hres + b * count, nullptr,
+                                        wave, kConvWaves, spin, ss)) {
+            return;
+        }
+    }
+    __syncthreads();
+    const XLds x{xs, K};
     auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
         for (uint32_t i = 0; i < nr; ++i) {
             const uint32_t row = begin + r0 + i;
-            if (lane < B) {
-                float* hp = P.h + (size_t)lane * P.d + row;
-                const float resid = (!is_down && layer == 0)
-                                        ? bf_to_f(P.embed[token_row(A.tok_in, lane, A.tok_stride, P.V) * P.d + row])
-                                        : *hp;
-                *hp = resid + pick<B>(res[i], lane);
-            }
+            if (lane < B)
+                st_tagged(P.h + (size_t)lane * P.d + row, hres[lane * count + r0 + i] + pick<B>(res[i], lane),
+                          tag_out);
         }
     };
-    conv_rows<B, 4>(rows, count, (int)(K >> 3), x, epi);
+    if (is_down) conv_rows_auto<B, OP_DOWN>(P, Lw, begin, count, K * 2u, x, epi);
+    else conv_rows_auto<B, OP_O>(P, Lw, begin, count, K * 2u, x, epi);
 }
 
 template <int HD>
 __global__ void __launch_bounds__(kConvThreads) k_attn(Params P, StepArgs A, int layer) {
-    __shared__ __attribute__((aligned(16))) float part[kConvWaves * kMaxGroup * (HD + 2)];
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    float* xs = (float*)lds;
     const int wave = threadIdx.x >> 6;
     const int item = blockIdx.x;
     const int per_b = P.Hkv * P.nsplit;
@@ -124,72 +223,10 @@ __global__ void __launch_bounds__(kConvThreads) k_attn(Params P, StepArgs A, int
     const SplitRange R = split_range<HD>(p, s, P.nsplit);
     const size_t base = (((size_t)layer * P.kv_b + b) * P.Hkv + g) * (size_t)P.S * HD;
     const GlobalKV<HD> kv{P.kcache + base, P.vcache + base, R.s0, max(0, R.s0 + R.ncached - 1)};
-    auto need = [](int) {};
-    auto barrier = []() { __syncthreads(); };
-    bool merged = false;
-    attn_item<HD>(P, layer, b, g, s, p, kv, need, barrier, part, wave, kConvWaves, P.attn_ticket, merged);
-}
-
-// LM head rows with per-wave argmax partials; the last block chooses the tokens
-// and advances the context lengths.
-template <int B>
-__global__ void __launch_bounds__(kConvThreads) k_head(Params P, StepArgs A, uint32_t* ticket) {
-    __shared__ __attribute__((aligned(16))) float xs[kXBytes / 4];
-    const int wave = threadIdx.x >> 6, lane = lane_id();
-    rmsnorm_rows<B>(P.h, nullptr, A.tok_in, A.tok_stride, P.V, P.final_norm, P.d, P.eps, xs);
-    const uint32_t begin = blockIdx.x * kRowsPerBlock;
-    const uint32_t count = min((uint32_t)kRowsPerBlock, (uint32_t)P.V - begin);
-    const PlainRows rows{P.head, (uint32_t)P.d, begin};
-    const XLds x{xs, (uint32_t)P.d};
-    float best_v[B];
-    int32_t best_i[B];
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-        best_v[b] = -INFINITY;
-        best_i[b] = 0x7FFFFFFF;
-    }
-    conv_rows<B, 4>(rows, count, P.d >> 3, x, [&](uint32_t r0, uint32_t nr, auto& res) {
-        for (uint32_t i = 0; i < nr; ++i) {
-            const int32_t row = (int32_t)(begin + r0 + i);
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                if (head_better(res[i][b], row, best_v[b], best_i[b])) {
-                    best_v[b] = res[i][b];
-                    best_i[b] = row;
-                }
-            }
-            if (lane < B) A.logits[(size_t)lane * P.V + row] = pick<B>(res[i], lane);
-        }
-    });
-    if (lane < B) {
-        HeadPart hp;
-        hp.v = pick<B>(best_v, lane);
-        int32_t bi = best_i[0];
-#pragma unroll
-        for (int b = 1; b < B; ++b)
-            if (lane == b) bi = best_i[b];
-        hp.i = bi;
-        P.head_part[((size_t)blockIdx.x * kConvWaves + wave) * B + lane] = hp;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    if (wave != 0) return;
-    uint32_t old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __shfl(old, 0, 64);
-    if (old != gridDim.x - 1u) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    uint32_t nanf = 0;
-    reduce_head_parts(P.head_part, (int)gridDim.x * kConvWaves, B, A.tok_out, &nanf);
-    if (lane < B) P.state->ctx_len[lane] = P.state->ctx_len[lane] + 1;
-    if (lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__any(nanf != 0) && lane == 0) {
-        uint32_t expected = 0;
-        if (__hip_atomic_compare_exchange_strong(&P.state->error, &expected, (uint32_t)DERR_NAN, __ATOMIC_RELAXED,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &&
-            P.host_err)
-            __hip_atomic_store(&P.host_err->code, (uint32_t)DERR_NAN, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-    }
+    auto need = [](int) { return true; };
+    BlockBarrier barrier;
+    Spin spin(&P, nullptr);
+    attn_item<HD>(P, A.tag0, layer, b, g, s, p, kv, need, barrier, xs, wave, kConvWaves, spin);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -197,33 +234,56 @@ __global__ void __launch_bounds__(kConvThreads) k_head(Params P, StepArgs A, uin
 // ------------------------------------------------------------------------------------------------
 int conventional_kernels_per_step(const Params& P) { return P.L * kPhasesPerLayer + 1; }
 
-int conventional_head_blocks(const Params& P) { return (P.V + kRowsPerBlock - 1) / kRowsPerBlock; }
+int conventional_head_blocks(const Params& P) { return (int)((P.V + kRowsPerBlock - 1) / kRowsPerBlock); }
 
 template <int B, int HD>
-static hipError_t launch_step_t(const Params& P, const StepArgs& A, uint32_t* head_ticket, hipStream_t st) {
+static hipError_t prepare_t(size_t lds) {
+    const void* fns[] = {(const void*)k_norm_gemv<B, OP_QKV>, (const void*)k_norm_gemv<B, OP_GATEUP>,
+                         (const void*)k_norm_gemv<B, OP_HEAD>, (const void*)k_proj<B>, (const void*)k_attn<HD>};
+    for (const void* f : fns) {
+        const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int B, int HD>
+static hipError_t launch_step_t(const Params& P, const StepArgs& A, hipStream_t st) {
     const dim3 blk(kConvThreads);
-    const int qkv_blocks = (P.qkv_rows + kRowsPerBlock - 1) / kRowsPerBlock;
-    const int d_blocks = (P.d + kRowsPerBlock - 1) / kRowsPerBlock;
-    const int f_blocks = (P.F + kRowsPerBlock - 1) / kRowsPerBlock;
+    const size_t lds = P.x_bytes;
+    const int qkv_blocks = (int)((P.qkv_rows + kRowsPerBlock - 1) / kRowsPerBlock);
+    const int d_blocks = (int)((P.d + kRowsPerBlock - 1) / kRowsPerBlock);
+    const int f_blocks = (int)((P.F + kRowsPerBlock - 1) / kRowsPerBlock);
     const int items = P.B * P.Hkv * P.nsplit;
     for (int l = 0; l < P.L; ++l) {
-        hipLaunchKernelGGL(k_qkv<B>, dim3(qkv_blocks), blk, 0, st, P, A, l);
-        hipLaunchKernelGGL(k_attn<HD>, dim3(items), blk, 0, st, P, A, l);
-        hipLaunchKernelGGL(k_proj_resid<B>, dim3(d_blocks), blk, 0, st, P, A, l, 0);
-        hipLaunchKernelGGL(k_gateup<B>, dim3(f_blocks), blk, 0, st, P, A, l);
-        hipLaunchKernelGGL(k_proj_resid<B>, dim3(d_blocks), blk, 0, st, P, A, l, 1);
+        hipLaunchKernelGGL((k_norm_gemv<B, OP_QKV>), dim3(qkv_blocks), blk, lds, st, P, A, l);
+        hipLaunchKernelGGL(k_attn<HD>, dim3(items), blk, lds, st, P, A, l);
+        hipLaunchKernelGGL(k_proj<B>, dim3(d_blocks), blk, lds, st, P, A, l, 0);
+        hipLaunchKernelGGL((k_norm_gemv<B, OP_GATEUP>), dim3(f_blocks), blk, lds, st, P, A, l);
+        hipLaunchKernelGGL(k_proj<B>, dim3(d_blocks), blk, lds, st, P, A, l, 1);
     }
-    hipLaunchKernelGGL(k_head<B>, dim3(conventional_head_blocks(P)), blk, 0, st, P, A, head_ticket);
+    hipLaunchKernelGGL((k_norm_gemv<B, OP_HEAD>), dim3(conventional_head_blocks(P)), blk, lds, st, P, A, P.L);
     return hipGetLastError();
 }
 
-hipError_t launch_conventional(const Params& P, const StepArgs& A, uint32_t* head_ticket, hipStream_t stream) {
+hipError_t prepare_conventional(const Params& P) {
     if (P.hd == 64) {
-        if (P.B == 1) return launch_step_t<1, 64>(P, A, head_ticket, stream);
-        if (P.B == 2) return launch_step_t<2, 64>(P, A, head_ticket, stream);
+        if (P.B == 1) return prepare_t<1, 64>(P.x_bytes);
+        if (P.B == 2) return prepare_t<2, 64>(P.x_bytes);
     } else if (P.hd == 128) {
-        if (P.B == 1) return launch_step_t<1, 128>(P, A, head_ticket, stream);
-        if (P.B == 2) return launch_step_t<2, 128>(P, A, head_ticket, stream);
+        if (P.B == 1) return prepare_t<1, 128>(P.x_bytes);
+        if (P.B == 2) return prepare_t<2, 128>(P.x_bytes);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_conventional(const Params& P, const StepArgs& A, hipStream_t stream) {
+    if (P.hd == 64) {
+        if (P.B == 1) return launch_step_t<1, 64>(P, A, stream);
+        if (P.B == 2) return launch_step_t<2, 64>(P, A, stream);
+    } else if (P.hd == 128) {
+        if (P.B == 1) return launch_step_t<1, 128>(P, A, stream);
+        if (P.B == 2) return launch_step_t<2, 128>(P, A, stream);
     }
     return hipErrorInvalidValue;
 }

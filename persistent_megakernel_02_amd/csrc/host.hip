@@ -27,7 +27,9 @@
 namespace mk {
 hipError_t launch_megakernel(const Params& P, const StepArgs& A, hipStream_t stream);
 bool megakernel_supports(int B, int hd);
-hipError_t launch_conventional(const Params& P, const StepArgs& A, uint32_t* head_ticket, hipStream_t stream);
+size_t megakernel_lds_bytes(const Params& P);
+hipError_t launch_conventional(const Params& P, const StepArgs& A, hipStream_t stream);
+hipError_t prepare_conventional(const Params& P);
 int conventional_kernels_per_step(const Params& P);
 int conventional_head_blocks(const Params& P);
 }  // namespace mk
@@ -37,23 +39,53 @@ using namespace mk;
 namespace {
 
 constexpr int kMaxCus = 1024;
+constexpr int kMaxSplits = 64;
 
 struct Plan {
     std::vector<Instr> instrs;
     std::vector<uint32_t> qoff;  // [n_cu + 1]
-    uint32_t n_ctr = 0, head_ctr = 0, conv_ticket_ctr = 0, n_head = 0;
-    uint32_t n_phase = 0, flag_stride = 64;
+    uint32_t n_head = 0;         // LM-head instructions
     int n_cu = 0, nsplit = 1;
     int phases = 0;
     size_t max_per_cu = 0;
 };
 
+// LDS floats of activations one instruction stages (x rows, residual rows of
+// O / DOWN, or an attention item's area).
+size_t x_floats(const mk_model_config* c, const mk_runtime_config* rt, int nsplit) {
+    const size_t B = (size_t)rt->max_batch, hd = (size_t)c->head_dim, G = (size_t)(c->n_q_heads / c->n_kv_heads);
+    size_t n = B * (size_t)c->hidden;
+    n = std::max(n, B * ((size_t)c->n_q_heads * hd + kMaxResidRows));
+    n = std::max(n, B * ((size_t)c->ffn + kMaxResidRows));
+    const size_t attn = (G + 2) * hd + (size_t)kComputeWaves * kMaxGroup * (hd + 2) + (size_t)nsplit * G * (hd + 2) + 4;
+    return std::max(n, attn);
+}
+
+size_t x_bytes_for(const mk_model_config* c, const mk_runtime_config* rt, int nsplit) {
+    return (x_floats(c, rt, nsplit) * 4 + 15) & ~(size_t)15;
+}
+
+uint32_t ring_chunks_for(size_t x_bytes) {
+    const size_t avail = kLdsBytes - kStaticLds;
+    return x_bytes >= avail ? 0u : (uint32_t)((avail - x_bytes) / kChunk);
+}
+
+// Most KV splits whose merge area still leaves the minimum weight ring (0: none).
+int max_splits_lds(const mk_model_config* c, const mk_runtime_config* rt) {
+    int best = 0;
+    for (int n = 1; n <= kMaxSplits; ++n)
+        if (ring_chunks_for(x_bytes_for(c, rt, n)) >= kMinRingChunks) best = n;
+    return best;
+}
+
+// KV splits per (sequence, KV head): about 512 positions per split, at most one
+// item per compute unit.  Short contexts get one split and no merge.
 int auto_splits(const mk_model_config* c, const mk_runtime_config* rt, int n_cu) {
     if (rt->attn_splits > 0) return rt->attn_splits;
     const int pairs = std::max(1, rt->max_batch * c->n_kv_heads);
-    int by_cu = std::max(1, n_cu / pairs);
-    int by_len = std::max(1, (rt->max_seq + 63) / 64);
-    return std::max(1, std::min(std::min(by_cu, by_len), 64));
+    const int by_cu = std::max(1, n_cu / pairs);
+    const int by_len = std::max(1, (rt->max_seq + 511) / 512);
+    return std::max(1, std::min(std::min(by_cu, by_len), std::min(kMaxSplits, max_splits_lds(c, rt))));
 }
 
 mk_status validate(const mk_model_config* c, const mk_runtime_config* rt, std::string* why) {
@@ -76,13 +108,16 @@ mk_status validate(const mk_model_config* c, const mk_runtime_config* rt, std::s
     if (rt->max_batch < 1 || rt->max_batch > kMaxBatch) return fail(MK_E_UNSUPPORTED, "max_batch must be 1..8");
     if (!megakernel_supports(rt->max_batch, c->head_dim))
         return fail(MK_E_UNSUPPORTED, "this build runs batch 1 and 2");
-    if ((size_t)rt->max_batch * c->hidden * 4 > kXBytes) return fail(MK_E_UNSUPPORTED, "batch x hidden too large");
     if (rt->max_seq < 1 || rt->max_seq > (1 << 20)) return fail(MK_E_INVALID, "max_seq out of range");
     if (rt->mode != MK_MODE_MEGAKERNEL && rt->mode != MK_MODE_GRAPH) return fail(MK_E_INVALID, "unknown mode");
     if (rt->num_cus < 0 || rt->num_cus > kMaxCus) return fail(MK_E_INVALID, "num_cus out of range");
     if (rt->gemv_kind < 0 || rt->gemv_kind > 1) return fail(MK_E_UNSUPPORTED, "gemv_kind must be 0 or 1");
     if (rt->trace != 0 && rt->trace != 1) return fail(MK_E_INVALID, "trace must be 0 or 1");
-    if (rt->attn_splits < 0 || rt->attn_splits > 256) return fail(MK_E_INVALID, "attn_splits out of range");
+    if (rt->attn_splits < 0 || rt->attn_splits > kMaxSplits) return fail(MK_E_INVALID, "attn_splits out of range");
+    // the activations one instruction stages must leave room for the weight ring
+    const int lds_splits = max_splits_lds(c, rt);
+    if (lds_splits == 0) return fail(MK_E_UNSUPPORTED, "activations of one instruction exceed the LDS budget");
+    if (rt->attn_splits > lds_splits) return fail(MK_E_UNSUPPORTED, "attention split merge exceeds the LDS budget");
     return MK_OK;
 }
 
@@ -93,6 +128,9 @@ inline void tile(uint32_t R, int n, int c, uint32_t* b, uint32_t* cnt) {
     *cnt = (uint32_t)(hi - lo);
 }
 
+// Every weight matrix is split by rows into one contiguous tile per compute unit;
+// O and DOWN tiles are cut into instructions of at most kMaxResidRows rows (their
+// residual rows are staged in LDS).  Attention items go round-robin, one per CU.
 Plan build_plan(const mk_model_config* c, const mk_runtime_config* rt, int n_cu) {
     Plan pl;
     pl.n_cu = n_cu;
@@ -100,59 +138,38 @@ Plan build_plan(const mk_model_config* c, const mk_runtime_config* rt, int n_cu)
     const int L = c->n_layers, B = rt->max_batch;
     const uint32_t qkv_rows = (uint32_t)((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim);
     std::vector<std::vector<Instr>> q(n_cu);
-    auto mk_instr = [](uint16_t op, int layer, uint32_t begin, uint32_t count, uint16_t wc, uint32_t wn, uint16_t sc) {
+    auto mk_instr = [](uint16_t op, int layer, uint32_t begin, uint32_t count) {
         Instr in;
         std::memset(&in, 0, sizeof(in));
         in.op = op;
         in.layer = (uint16_t)layer;
         in.begin = begin;
         in.count = count;
-        in.wait_ctr = wc;
-        in.wait_n = wn;
-        in.sig_ctr = sc;
         return in;
     };
-    uint16_t prev_ctr = kNoCounter;
-    uint32_t prev_n = 0;
-    auto gemv_phase = [&](uint16_t op, int layer, uint32_t R, uint16_t ctr) {
-        uint32_t n = 0;
+    auto gemv_phase = [&](uint16_t op, int layer, uint32_t R, uint32_t max_rows) {
         for (int cu = 0; cu < n_cu; ++cu) {
             uint32_t b, cnt;
             tile(R, n_cu, cu, &b, &cnt);
-            if (!cnt) continue;
-            Instr in = mk_instr(op, layer, b, cnt, prev_ctr, prev_n, ctr);
-            in.slot = n++;
-            q[cu].push_back(in);
+            for (uint32_t o = 0; o < cnt; o += max_rows) {
+                Instr in = mk_instr(op, layer, b + o, std::min(max_rows, cnt - o));
+                if (op == OP_HEAD) in.slot = pl.n_head++;
+                q[cu].push_back(in);
+            }
         }
-        pl.flag_stride = std::max(pl.flag_stride, (n + 63u) & ~63u);
-        prev_ctr = ctr;
-        prev_n = n;
         ++pl.phases;
     };
+    const uint32_t all = 0xFFFFFFFFu;
     for (int l = 0; l < L; ++l) {
-        const uint16_t base = (uint16_t)(l * kPhasesPerLayer);
-        gemv_phase(OP_QKV, l, qkv_rows, base + 0);
-        // attention items: (b, g, s) spread one per CU round-robin
+        gemv_phase(OP_QKV, l, qkv_rows, all);
         const uint32_t items = (uint32_t)(B * c->n_kv_heads * pl.nsplit);
-        for (uint32_t it = 0; it < items; ++it) {
-            Instr in = mk_instr(OP_ATTN, l, it, 1, prev_ctr, prev_n, (uint16_t)(base + 1));
-            in.slot = it;
-            q[it % n_cu].push_back(in);
-        }
-        pl.flag_stride = std::max(pl.flag_stride, (items + 63u) & ~63u);
-        prev_ctr = (uint16_t)(base + 1);
-        prev_n = items;
+        for (uint32_t it = 0; it < items; ++it) q[it % n_cu].push_back(mk_instr(OP_ATTN, l, it, 1));
         ++pl.phases;
-        gemv_phase(OP_O, l, (uint32_t)c->hidden, base + 2);
-        gemv_phase(OP_GATEUP, l, (uint32_t)c->ffn, base + 3);
-        gemv_phase(OP_DOWN, l, (uint32_t)c->hidden, base + 4);
+        gemv_phase(OP_O, l, (uint32_t)c->hidden, kMaxResidRows);
+        gemv_phase(OP_GATEUP, l, (uint32_t)c->ffn, all);
+        gemv_phase(OP_DOWN, l, (uint32_t)c->hidden, kMaxResidRows);
     }
-    pl.head_ctr = (uint32_t)(L * kPhasesPerLayer);
-    gemv_phase(OP_HEAD, L, (uint32_t)c->vocab, (uint16_t)pl.head_ctr);
-    pl.n_head = prev_n;
-    pl.conv_ticket_ctr = pl.head_ctr + 1;
-    pl.n_ctr = pl.head_ctr + 2;
-    pl.n_phase = pl.head_ctr + 1;
+    gemv_phase(OP_HEAD, L, (uint32_t)c->vocab, all);
     pl.qoff.resize(n_cu + 1);
     pl.qoff[0] = 0;
     for (int cu = 0; cu < n_cu; ++cu) {
@@ -163,14 +180,14 @@ Plan build_plan(const mk_model_config* c, const mk_runtime_config* rt, int n_cu)
     return pl;
 }
 
-// Every row / item exactly once; each queue in strictly increasing phase order;
-// every wait names the phase right before its own and the number of
-// instructions that phase emitted.  Returns 0 or an error code.
+// Every row / item exactly once; each queue in non-decreasing phase order (an
+// instruction only waits on values of earlier phases, so no queue can wait on
+// itself or on a later queue position); O and DOWN instructions within the
+// residual staging limit; LM-head slots 0..n_head-1 each once.  0 or an error code.
 int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Plan& pl) {
     const int L = c->n_layers, B = rt->max_batch;
     const uint32_t qkv_rows = (uint32_t)((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim);
     const int nphase = L * kPhasesPerLayer + 1;
-    std::vector<uint32_t> emitted(nphase, 0);
     std::vector<std::vector<uint8_t>> seen(nphase);
     auto phase_of = [&](const Instr& in) -> int {
         if (in.op == OP_HEAD) return L * kPhasesPerLayer;
@@ -188,6 +205,8 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
         }
     };
     for (int ph = 0; ph < nphase; ++ph) seen[ph].assign(extent(ph), 0);
+    std::vector<uint8_t> slot_seen(pl.n_head, 0);
+    if (pl.qoff.size() != (size_t)pl.n_cu + 1 || pl.qoff[pl.n_cu] != pl.instrs.size()) return 1;
     for (int cu = 0; cu < pl.n_cu; ++cu) {
         int last = -1;
         for (uint32_t i = pl.qoff[cu]; i < pl.qoff[cu + 1]; ++i) {
@@ -197,53 +216,50 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
             const int ph = phase_of(in);
             if (ph < last) return 3;  // queue not in phase order
             last = ph;
-            if (in.sig_ctr != ph) return 4;
             const uint32_t ext = extent(ph);
-            if (in.count == 0 || in.begin + in.count > ext) return 5;
+            if (in.count == 0 || in.begin + in.count > ext || in.begin + in.count < in.begin) return 5;
+            if ((in.op == OP_O || in.op == OP_DOWN) && in.count > kMaxResidRows) return 4;
             for (uint32_t r = in.begin; r < in.begin + in.count; ++r) {
                 if (seen[ph][r]) return 6;  // covered twice
                 seen[ph][r] = 1;
             }
-            ++emitted[ph];
-            if (ph == 0) {
-                if (in.wait_ctr != kNoCounter) return 7;
-            } else if (in.wait_ctr != ph - 1) {
-                return 8;
+            if (in.op == OP_HEAD) {
+                if (in.slot >= pl.n_head) return 7;
+                if (slot_seen[in.slot]++) return 8;
             }
         }
     }
     for (int ph = 0; ph < nphase; ++ph)
-        for (uint8_t s : seen[ph])
-            if (!s) return 9;  // row never covered
-    for (int cu = 0; cu < pl.n_cu; ++cu)
-        for (uint32_t i = pl.qoff[cu]; i < pl.qoff[cu + 1]; ++i) {
-            const Instr& in = pl.instrs[i];
-            if (in.wait_ctr != kNoCounter && in.wait_n != emitted[in.wait_ctr]) return 10;
-        }
-    if (pl.n_head != emitted[L * kPhasesPerLayer]) return 11;
-    std::vector<std::vector<uint8_t>> slot_seen(nphase);
-    for (int ph = 0; ph < nphase; ++ph) slot_seen[ph].assign(emitted[ph], 0);
-    for (const Instr& in : pl.instrs) {
-        if (in.slot >= emitted[in.sig_ctr] || in.slot >= pl.flag_stride) return 12;
-        if (slot_seen[in.sig_ctr][in.slot]++) return 13;  // two producers share a flag
-    }
+        for (uint8_t v : seen[ph])
+            if (!v) return 9;  // row never covered
     return 0;
 }
 
 struct Layout {
-    size_t state, counters, flags, flags_bytes, tickets, instrs, qoff, layers, rope, h, qkv, attn, act, attn_part, head_part, logits_scr,
-        tok_scr, trace, trace_bytes, total;
-    size_t head_slots;
+    size_t state, tickets, instrs, qoff, layers, rope, h, qkv, attn, act, attn_part, head_part, logits_scr, tok_scr,
+        trace, trace_bytes, total;
+    size_t head_slots;  // argmax partial slots (per sequence)
 };
 
 inline size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, int nsplit, size_t n_instr,
-              uint32_t n_ctr, uint32_t flag_stride) {
+// Instruction counts of a plan on n compute units (total and the longest queue).
+void plan_counts(const mk_model_config* c, const mk_runtime_config* rt, int n, int nsplit, size_t* total,
+                 size_t* per_cu) {
+    const size_t items = (size_t)rt->max_batch * c->n_kv_heads * nsplit;
+    const size_t d_rows = ((size_t)c->hidden + n - 1) / n;
+    const size_t od = (d_rows + kMaxResidRows - 1) / kMaxResidRows;  // O / DOWN instructions per CU
+    *per_cu = (size_t)c->n_layers * (2 + 2 * od + (items + n - 1) / n) + 1;
+    *total = (size_t)c->n_layers * (2 * (size_t)n + items + 2 * od * (size_t)n) + (size_t)n;
+}
+
+Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, int nsplit) {
     Layout lo{};
     const size_t B = (size_t)rt->max_batch, d = c->hidden, hd = c->head_dim;
     const size_t qkv_rows = (size_t)(c->n_q_heads + 2 * c->n_kv_heads) * hd;
     const size_t G = (size_t)(c->n_q_heads / c->n_kv_heads);
+    size_t n_instr = 0, per_cu = 0;
+    plan_counts(c, rt, n_cu, nsplit, &n_instr, &per_cu);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
@@ -251,38 +267,25 @@ Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, i
         return o;
     };
     lo.state = take(sizeof(DevState));
-    lo.counters = take((size_t)n_ctr * kCtrStride * 4);
-    lo.flags_bytes = (size_t)n_ctr * flag_stride * 4;
-    lo.flags = take(lo.flags_bytes);
-    lo.tickets = take((size_t)c->n_layers * B * c->n_kv_heads * kCtrStride * 4);
+    lo.tickets = take(((size_t)c->n_layers * B * c->n_kv_heads + 1) * kCtrStride * 4);
     lo.instrs = take(n_instr * sizeof(Instr));
     lo.qoff = take((size_t)(n_cu + 1) * 4);
     lo.layers = take((size_t)c->n_layers * sizeof(DevLayer));
     lo.rope = take((size_t)rt->max_seq * (hd / 2) * 8);
-    lo.h = take(B * d * 4);
-    lo.qkv = take(B * qkv_rows * 4);
-    lo.attn = take(B * c->n_q_heads * hd * 4);
-    lo.act = take(B * c->ffn * 4);
-    lo.attn_part = take(B * c->n_kv_heads * nsplit * G * (hd + 2) * 4);
+    lo.h = take(B * d * 8);
+    lo.qkv = take(B * qkv_rows * 8);
+    lo.attn = take(B * c->n_q_heads * hd * 8);
+    lo.act = take(B * c->ffn * 8);
+    lo.attn_part = take(B * c->n_kv_heads * nsplit * G * (hd + 2) * 8);
     const size_t conv_blocks = ((size_t)c->vocab + 15) / 16;
     lo.head_slots = std::max((size_t)n_cu, conv_blocks) * kComputeWaves;
-    lo.head_part = take(lo.head_slots * B * sizeof(HeadPart));
+    lo.head_part = take(lo.head_slots * B * 2 * 8);
     lo.logits_scr = take(B * c->vocab * 4);
     lo.tok_scr = take(B * 4);
-    // trace: one record per instruction slot; a CU holds at most 5 per layer + the head,
-    // plus the attention items beyond one per CU
-    const size_t items = B * c->n_kv_heads * nsplit;
-    const size_t per_cu = (size_t)c->n_layers * (4 + (items + n_cu - 1) / n_cu) + 1;
     lo.trace_bytes = rt->trace ? (size_t)n_cu * per_cu * kTraceWords * 4 : 0;
     lo.trace = take(lo.trace_bytes);
     lo.total = off;
     return lo;
-}
-
-// Upper bound on the instruction count for any n_cu <= cus.
-size_t max_instrs(const mk_model_config* c, const mk_runtime_config* rt, int cus, int nsplit) {
-    const size_t items = (size_t)rt->max_batch * c->n_kv_heads * nsplit;
-    return (size_t)c->n_layers * (4 * (size_t)cus + items) + cus;
 }
 
 int device_cus() {
@@ -358,15 +361,12 @@ mk_status mk_query_sizes(const mk_model_config* cfg, const mk_runtime_config* rt
     if (!workspace_bytes || !kv_bytes) return MK_E_INVALID;
     mk_status s = validate(cfg, rt, nullptr);
     if (s != MK_OK) return s;
-    const int n_cu = rt->num_cus > 0 ? rt->num_cus : kMaxCus;
-    int nsplit = 1;
-    for (int cus = 1; cus <= n_cu; cus *= 2) nsplit = std::max(nsplit, auto_splits(cfg, rt, cus));
-    nsplit = std::max(nsplit, auto_splits(cfg, rt, n_cu));
-    const uint32_t n_ctr = (uint32_t)(cfg->n_layers * kPhasesPerLayer + 2);
-    const uint32_t items = (uint32_t)(rt->max_batch * cfg->n_kv_heads * nsplit);
-    const uint32_t fstride = (std::max((uint32_t)n_cu, items) + 63u) & ~63u;
-    Layout lo = layout(cfg, rt, n_cu, nsplit, max_instrs(cfg, rt, n_cu, nsplit), n_ctr, fstride);
-    *workspace_bytes = lo.total;
+    // the compute-unit count may be resolved only at mk_create: size for every count up to the bound
+    const int n_max = rt->num_cus > 0 ? rt->num_cus : kMaxCus;
+    size_t ws = 0;
+    for (int n = rt->num_cus > 0 ? n_max : 1; n <= n_max; ++n)
+        ws = std::max(ws, layout(cfg, rt, n, auto_splits(cfg, rt, n)).total);
+    *workspace_bytes = ws;
     *kv_bytes = 2ull * cfg->n_layers * rt->max_batch * cfg->n_kv_heads * (size_t)rt->max_seq * cfg->head_dim * 2;
     return MK_OK;
 }
@@ -382,10 +382,11 @@ mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* r
     const int64_t d = cfg->hidden, hd = cfg->head_dim;
     const int64_t per_layer = (cfg->n_q_heads + 2 * cfg->n_kv_heads) * hd * d + d * cfg->n_q_heads * hd +
                               3 * (int64_t)cfg->ffn * d + 2 * d;
-    int64_t vals[8] = {num_cus, (int64_t)pl.instrs.size(), pl.n_ctr, (int64_t)pl.max_per_cu,
-                       2 * (cfg->n_layers * per_layer + (int64_t)cfg->vocab * d + d), verify_plan(cfg, rt, pl),
-                       pl.nsplit, pl.phases};
-    for (int i = 0; i < cap && i < 8; ++i) out[i] = vals[i];
+    const size_t xb = x_bytes_for(cfg, rt, pl.nsplit);
+    int64_t vals[10] = {num_cus, (int64_t)pl.instrs.size(), (int64_t)ring_chunks_for(xb), (int64_t)pl.max_per_cu,
+                        2 * (cfg->n_layers * per_layer + (int64_t)cfg->vocab * d + d), verify_plan(cfg, rt, pl),
+                        pl.nsplit, pl.phases, (int64_t)xb, (int64_t)pl.n_head};
+    for (int i = 0; i < cap && i < 10; ++i) out[i] = vals[i];
     return MK_OK;
 }
 
@@ -422,7 +423,7 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
         delete h;
         return MK_E_INVALID;
     }
-    h->lo = layout(cfg, rt, n_cu, h->plan.nsplit, h->plan.instrs.size(), h->plan.n_ctr, h->plan.flag_stride);
+    h->lo = layout(cfg, rt, n_cu, h->plan.nsplit);
     if (workspace_bytes < h->lo.total || workspace_bytes < need_ws || kv_bytes < need_kv) {
         delete h;
         return MK_E_INVALID;
@@ -472,28 +473,41 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
     P.kcache = (uint16_t*)d_kv;
     P.vcache = (uint16_t*)d_kv + kv_half;
     P.rope = (const float2*)(ws + lo.rope);
-    P.h = (float*)(ws + lo.h);
-    P.qkv = (float*)(ws + lo.qkv);
-    P.attn = (float*)(ws + lo.attn);
-    P.act = (float*)(ws + lo.act);
-    P.attn_part = (float*)(ws + lo.attn_part);
+    P.h = (uint64_t*)(ws + lo.h);
+    P.qkv = (uint64_t*)(ws + lo.qkv);
+    P.attn = (uint64_t*)(ws + lo.attn);
+    P.act = (uint64_t*)(ws + lo.act);
+    P.attn_part = (uint64_t*)(ws + lo.attn_part);
+    P.head_part = (uint64_t*)(ws + lo.head_part);
     P.attn_ticket = (uint32_t*)(ws + lo.tickets);
-    P.head_part = (HeadPart*)(ws + lo.head_part);
-    P.counters = (uint32_t*)(ws + lo.counters);
-    P.flags = (uint32_t*)(ws + lo.flags);
-    P.flag_stride = h->plan.flag_stride;
+    P.head_ticket = P.attn_ticket + (size_t)cfg->n_layers * rt->max_batch * cfg->n_kv_heads * kCtrStride;
     P.state = (DevState*)(ws + lo.state);
     P.host_err = h->host_err_dev;
     P.instrs = (const Instr*)(ws + lo.instrs);
     P.queue_off = (const uint32_t*)(ws + lo.qoff);
-    P.head_ctr = h->plan.head_ctr;
-    P.n_head_instr = h->plan.n_head;
+    P.x_bytes = (uint32_t)x_bytes_for(cfg, rt, h->plan.nsplit);
+    P.ring_chunks = ring_chunks_for(P.x_bytes);
+    P.n_head_slots = rt->mode == MK_MODE_MEGAKERNEL ? h->plan.n_head * (uint32_t)kComputeWaves
+                                                    : (uint32_t)conventional_head_blocks(P) * (uint32_t)kComputeWaves;
+    auto give_up = [&](mk_status st) {
+        if (h->host_err) (void)hipHostFree(h->host_err);
+        delete h;
+        return st;
+    };
+    if (P.ring_chunks < kMinRingChunks || P.n_head_slots > lo.head_slots ||
+        h->plan.instrs.size() * sizeof(Instr) > lo.qoff - lo.instrs)
+        return give_up(MK_E_UNSUPPORTED);
     if (rt->trace) {
         P.trace = (uint32_t*)(ws + lo.trace);
         P.trace_stride = (uint32_t)(lo.trace_bytes / ((size_t)n_cu * kTraceWords * 4));
-        if (h->plan.max_per_cu > P.trace_stride) {
-            delete h;
-            return MK_E_INVALID;
+        if (h->plan.max_per_cu > P.trace_stride) return give_up(MK_E_INVALID);
+    }
+    if (rt->mode == MK_MODE_GRAPH) {
+        // kernel attributes are set before any capture
+        const hipError_t pe = prepare_conventional(P);
+        if (pe != hipSuccess) {
+            hip_fail(h, pe, "prepare_conventional");
+            return give_up(MK_E_HIP);
         }
     }
     const uint32_t tmo = rt->spin_timeout_ms ? rt->spin_timeout_ms : 2000u;
@@ -517,7 +531,6 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
             rope[((size_t)p * half + i) * 2 + 0] = (float)std::cos(a);
             rope[((size_t)p * half + i) * 2 + 1] = (float)std::sin(a);
         }
-    std::vector<HeadPart> hp(lo.head_slots * rt->max_batch, HeadPart{-INFINITY, 0x7FFFFFFF});
     hipError_t e = hipSuccess;
     auto cp = [&](size_t off, const void* src, size_t bytes) {
         if (e == hipSuccess && bytes) e = hipMemcpyAsync(ws + off, src, bytes, hipMemcpyHostToDevice, h->stream);
@@ -527,7 +540,6 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
     cp(lo.qoff, h->plan.qoff.data(), h->plan.qoff.size() * 4);
     cp(lo.layers, dl.data(), dl.size() * sizeof(DevLayer));
     cp(lo.rope, rope.data(), rope.size() * 4);
-    cp(lo.head_part, hp.data(), hp.size() * sizeof(HeadPart));
     if (e == hipSuccess) e = hipMemsetAsync(d_kv, 0, need_kv, h->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
     if (e != hipSuccess) {
@@ -578,31 +590,25 @@ static mk_status run_step(mk_handle* h, const int32_t* tok_in, int32_t stride, i
     A.tok_stride = stride;
     A.tok_out = tok_out;
     A.logits = logits;
-    A.epoch = ++h->epoch;
+    A.tag0 = (++h->epoch) * tags_per_step(h->cfg.n_layers);
     Params P = h->P;
     if (h->inject == 1) {
-        P.spin_ticks = 100000ull;  // 1 ms
-        // the first QKV instruction of layer 0 waits for nothing; make the ATTN phase
-        // of layer 0 wait for twice as many producers as exist
-        std::vector<Instr> bad = h->plan.instrs;
-        for (Instr& in : bad)
-            if (in.op == OP_ATTN && in.layer == 0) in.wait_n *= 2;
-        HIPCHK(h, hipMemcpyAsync(h->ws + h->lo.instrs, bad.data(), bad.size() * sizeof(Instr), hipMemcpyHostToDevice,
-                                 st));
-        HIPCHK(h, hipStreamSynchronize(st));
-        h->inject = 2;  // restore after this step
+        // one step whose layer-0 attention waits for a tag no producer writes, with a
+        // 1 ms watchdog: every workgroup times out or sees the error and leaves
+        P.spin_ticks = 100000ull;
+        P.inject = 1;
+        h->inject = 0;
     }
     if (h->rt.mode == MK_MODE_MEGAKERNEL) {
         HIPCHK(h, launch_megakernel(P, A, st));
+    } else if (stride != 1 || P.inject) {
+        // prompt positions (strided tokens) and the fault test run uncaptured
+        HIPCHK(h, launch_conventional(P, A, st));
     } else {
-        // replay a graph captured for these pointers (re-captured when they change)
-        if (!h->gexec || h->g_in != tok_in || h->g_out != tok_out || h->g_logits != logits || stride != 1) {
-            if (stride != 1) {
-                HIPCHK(h, launch_conventional(P, A, (uint32_t*)(h->ws + h->lo.counters) +
-                                                        (size_t)h->plan.conv_ticket_ctr * kCtrStride,
-                                              st));
-                goto done;
-            }
+        // replay a graph captured for these pointers (re-captured when they change); the
+        // captured tag base stays fixed, which is enough because kernel order alone
+        // orders the one-kernel-per-op path
+        if (!h->gexec || h->g_in != tok_in || h->g_out != tok_out || h->g_logits != logits) {
             if (h->gexec) {
                 (void)hipGraphExecDestroy(h->gexec);
                 h->gexec = nullptr;
@@ -614,10 +620,7 @@ static mk_status run_step(mk_handle* h, const int32_t* tok_in, int32_t stride, i
             hipStream_t cap;
             HIPCHK(h, hipStreamCreateWithFlags(&cap, hipStreamNonBlocking));
             hipError_t e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
-            if (e == hipSuccess)
-                e = launch_conventional(P, A, (uint32_t*)(h->ws + h->lo.counters) + (size_t)h->plan.conv_ticket_ctr *
-                                                                                          kCtrStride,
-                                        cap);
+            if (e == hipSuccess) e = launch_conventional(P, A, cap);
             hipGraph_t g = nullptr;
             hipError_t e2 = hipStreamEndCapture(cap, &g);
             (void)hipStreamDestroy(cap);
@@ -631,15 +634,7 @@ static mk_status run_step(mk_handle* h, const int32_t* tok_in, int32_t stride, i
         }
         HIPCHK(h, hipGraphLaunch(h->gexec, st));
     }
-done:
     for (int b = 0; b < h->rt.max_batch; ++b) h->ctx[b] += 1;
-    if (h->inject == 2) {
-        HIPCHK(h, hipStreamSynchronize(st));
-        HIPCHK(h, hipMemcpyAsync(h->ws + h->lo.instrs, h->plan.instrs.data(), h->plan.instrs.size() * sizeof(Instr),
-                                 hipMemcpyHostToDevice, st));
-        HIPCHK(h, hipStreamSynchronize(st));
-        h->inject = 0;
-    }
     return MK_OK;
 }
 
@@ -694,14 +689,13 @@ mk_status mk_reset(mk_handle* h, void* stream) {
     DevState ds;
     HIPCHK(h, hipMemcpy(&ds, h->ws + h->lo.state, sizeof(ds), hipMemcpyDeviceToHost));
     for (int b = 0; b < h->rt.max_batch; ++b) h->ctx[b] = ds.ctx_len[b];
-    HIPCHK(h, hipMemsetAsync(h->ws + h->lo.counters, 0, (size_t)h->plan.n_ctr * kCtrStride * 4, st));
-    HIPCHK(h, hipMemsetAsync(h->ws + h->lo.flags, 0, h->lo.flags_bytes, st));
+    // tickets back to zero; the step counter (tag base) keeps counting, so values
+    // left by an aborted step never match a later step's tags
     HIPCHK(h, hipMemsetAsync(h->ws + h->lo.tickets, 0,
-                             (size_t)h->cfg.n_layers * h->rt.max_batch * h->cfg.n_kv_heads * kCtrStride * 4, st));
+                             ((size_t)h->cfg.n_layers * h->rt.max_batch * h->cfg.n_kv_heads + 1) * kCtrStride * 4, st));
     HIPCHK(h, hipMemsetAsync(h->ws + h->lo.state + offsetof(DevState, error), 0, 16, st));
     HIPCHK(h, hipStreamSynchronize(st));
     if (h->host_err) std::memset(h->host_err, 0, sizeof(HostErr));
-    h->epoch = 0;
     h->latched = false;
     h->latched_status = MK_OK;
     h->last_error.clear();
@@ -712,7 +706,6 @@ mk_status mk_debug_inject(mk_handle* h, int32_t fault, int32_t arg) {
     (void)arg;
     if (!h) return MK_E_INVALID;
     if (fault != 0 && fault != 1) return MK_E_INVALID;
-    if (fault == 1 && h->rt.mode != MK_MODE_MEGAKERNEL) return MK_E_UNSUPPORTED;
     h->inject = fault;
     return MK_OK;
 }

@@ -19,8 +19,6 @@
 
 namespace mk {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 // Load through the constant address space: uniform, read-only data (schedule,
@@ -39,6 +37,8 @@ __device__ __forceinline__ T ld_const(const T* p) {
     return out;
 }
 
+__device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 __device__ __forceinline__ float bf_to_f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
@@ -49,7 +49,6 @@ __device__ __forceinline__ uint32_t f_to_bf(float f) {
     if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
-__device__ __forceinline__ float round_bf(float f) { return __uint_as_float(f_to_bf(f) << 16); }
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f_to_bf(lo) | (f_to_bf(hi) << 16); }
 
 // acc + sum over the 8 bf16 weights of w times the 8 fp32 activations (xa, xb),
@@ -66,18 +65,6 @@ __device__ __forceinline__ float dot8(uint4 w, float4 xa, float4 xb, float acc) 
     return acc;
 }
 
-// Butterfly sum over the 64 lanes.  Partner lanes add the same two partial sums
-// (addition commutes), so every lane ends with the bitwise-identical total.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
-}
 // Total over the 64 lanes with DPP, in a fixed tree: quad butterflies, half-row
 // and row mirrors (16-lane sums), then row broadcasts accumulate rows 0..3 into
 // lane 63.  The value of lane 63 is returned to every lane (scalar).
@@ -105,76 +92,155 @@ __device__ __forceinline__ size_t token_row(const int32_t* tok, int b, int strid
 }
 
 // ---------------------------------------------------------------------------------------------
-// RMSNorm of B residual rows into fp32 activations (x_i = h_i * g_i / rms(h)).
-// Lane l handles 8-element pieces p = l + 64 j: it writes exactly the pieces it
-// later reads in row_dot, so no other lane or wave depends on its stores.
-// `src_bf16` != nullptr selects embedding rows (layer 0) instead of `h`.
+// Tagged activation words {fp32 value (low half), tag (high half)}.  Stores and
+// loads are single 8-byte accesses at agent scope: the store writes through to
+// the device coherence point and the load reads it there, so a word whose tag
+// matches carries the matching value.
 // ---------------------------------------------------------------------------------------------
-template <int B>
-__device__ void rmsnorm_rows(const float* __restrict__ h, const uint16_t* __restrict__ emb,
-                             const int32_t* __restrict__ tok, int32_t tok_stride, int V, const uint16_t* __restrict__ g,
-                             int d, float eps, float* __restrict__ xout) {
-    const int lane = lane_id();
-    const int np = d >> 3;
-    constexpr int kMaxPieces = 8;  // d <= 4096: at most 8 pieces per lane
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-        const float* hb = h + (size_t)b * d;
-        const uint16_t* eb = emb ? emb + token_row(tok, b, tok_stride, V) * d : nullptr;
-        float v[kMaxPieces][8];
-        float ss = 0.f;
-#pragma unroll
-        for (int j = 0; j < kMaxPieces; ++j) {
-            const int p = lane + 64 * j;
-            if (p < np) {
-                if (eb) {
-                    uint4 u = *(const uint4*)(eb + 8 * p);
-                    v[j][0] = bf_lo(u.x); v[j][1] = bf_hi(u.x); v[j][2] = bf_lo(u.y); v[j][3] = bf_hi(u.y);
-                    v[j][4] = bf_lo(u.z); v[j][5] = bf_hi(u.z); v[j][6] = bf_lo(u.w); v[j][7] = bf_hi(u.w);
-                } else {
-                    float4 a = *(const float4*)(hb + 8 * p), c = *(const float4*)(hb + 8 * p + 4);
-                    v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
-                    v[j][4] = c.x; v[j][5] = c.y; v[j][6] = c.z; v[j][7] = c.w;
-                }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kMaxPieces; ++j)
-            if (lane + 64 * j < np)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ss = fmaf(v[j][e], v[j][e], ss);
-        ss = wave_total(ss);
-        const float r = 1.0f / sqrtf(ss / (float)d + eps);
-#pragma unroll
-        for (int j = 0; j < kMaxPieces; ++j) {
-            const int p = lane + 64 * j;
-            if (p < np) {
-                uint4 gv = *(const uint4*)(g + 8 * p);
-                float gg[8] = {bf_lo(gv.x), bf_hi(gv.x), bf_lo(gv.y), bf_hi(gv.y),
-                               bf_lo(gv.z), bf_hi(gv.z), bf_lo(gv.w), bf_hi(gv.w)};
-                float4 o0 = make_float4(v[j][0] * r * gg[0], v[j][1] * r * gg[1], v[j][2] * r * gg[2],
-                                        v[j][3] * r * gg[3]);
-                float4 o1 = make_float4(v[j][4] * r * gg[4], v[j][5] * r * gg[5], v[j][6] * r * gg[6],
-                                        v[j][7] * r * gg[7]);
-                *(float4*)(xout + (size_t)b * d + 8 * p) = o0;
-                *(float4*)(xout + (size_t)b * d + 8 * p + 4) = o1;
+__device__ __forceinline__ void st_tagged(uint64_t* p, float v, uint32_t tag) {
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tagged(const uint64_t* p) {
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float tv_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
+__device__ __forceinline__ uint32_t tv_tag(uint64_t w) { return (uint32_t)(w >> 32); }
+
+// Device error: the first code wins the state word and is mirrored to the
+// pinned host word; the workgroup's abort flag (LDS) stops its other waves.
+__device__ __noinline__ void raise_error_impl(DevState* state, HostErr* herr, uint32_t* abort_flag, uint32_t code,
+                                             uint32_t a, uint32_t b) {
+    if (abort_flag) __hip_atomic_store(abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if ((threadIdx.x & 63) == 0) {
+        uint32_t expected = 0;
+        if (__hip_atomic_compare_exchange_strong(&state->error, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)) {
+            state->err_info[0] = a;
+            state->err_info[1] = b;
+            state->err_info[2] = blockIdx.x;
+            if (herr) {
+                __hip_atomic_store(&herr->info[0], a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                __hip_atomic_store(&herr->info[1], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                __hip_atomic_store(&herr->info[2], blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                __hip_atomic_store(&herr->code, code, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
             }
         }
     }
 }
 
-// ---------------------------------------------------------------------------------------------
-// Row sources: piece p (16 bytes = 8 bf16) of row r of the current instruction.
-// ---------------------------------------------------------------------------------------------
-struct RingRows {  // rows laid back to back in the LDS ring from stream offset `base`
-    const char* ring;
-    uint32_t base, rb;
-    __device__ __forceinline__ uint4 piece(uint32_t r, uint32_t p) const {
-        return *(const uint4*)(ring + ((base + r * rb + p * 16u) & (kRingBytes - 1u)));
+// Bounded spin of one wave: again() sleeps briefly and answers whether to keep
+// polling.  It gives up when the workgroup aborted, when another workgroup
+// latched a device error, or (raising DERR_TIMEOUT) when the watchdog expires.
+struct Spin {
+    const Params* P;
+    uint32_t* abort_flag;  // LDS flag of the workgroup, or nullptr
+    uint64_t t0;
+    uint32_t polls;
+    __device__ Spin(const Params* p, uint32_t* ab) : P(p), abort_flag(ab), t0(0), polls(0) {}
+    __device__ __forceinline__ bool aborted() const {
+        return abort_flag && __hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+    }
+    __device__ __forceinline__ void start() { polls = 0; }  // begin a new wait
+    __device__ __forceinline__ bool again(uint32_t a, uint32_t b) {
+        if (polls == 0) t0 = now_ticks();
+        ++polls;
+        __builtin_amdgcn_s_sleep(1);
+        if (aborted()) return false;
+        if ((polls & 63u) == 0) {
+            if (__hip_atomic_load(&P->state->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+                if (abort_flag) __hip_atomic_store(abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                return false;
+            }
+            if (now_ticks() - t0 > P->spin_ticks) {
+                raise_error_impl(P->state, P->host_err, abort_flag, DERR_TIMEOUT, a, b);
+                return false;
+            }
+        }
+        return true;
     }
 };
 
-// Activation sources (fp32): the 8 values of piece p of batch row b.
+// ---------------------------------------------------------------------------------------------
+// Staging: wave w of nw moves elements e = 64 (w + nw i) + lane of a vector into
+// LDS, kStageWords words per lane in flight, polling until every tag matches.
+// ---------------------------------------------------------------------------------------------
+// dst[e] = value of src[e] (optionally times the bf16 gain g[e]); ss gets the
+// lane's sum of squares of the raw values in ascending i (RMSNorm statistics).
+template <bool GAIN>
+__device__ __forceinline__ bool stage_tagged(const uint64_t* __restrict__ src, uint32_t n, uint32_t tag,
+                                             float* __restrict__ dst, const uint16_t* __restrict__ g, int w, int nw,
+                                             Spin& spin, float& ss) {
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint32_t step = 64u * (uint32_t)nw;
+    // `base` is wave-uniform so every lane takes part in the polls
+    for (uint32_t base = 64u * (uint32_t)w; base < n; base += step * kStageWords) {
+        uint64_t v[kStageWords];
+#pragma unroll
+        for (int i = 0; i < kStageWords; ++i) {
+            const uint32_t e = base + lane + step * i;
+            v[i] = e < n ? ld_tagged(src + e) : ((uint64_t)tag << 32);
+        }
+        spin.start();
+        for (;;) {
+            bool ok = true;
+#pragma unroll
+            for (int i = 0; i < kStageWords; ++i) ok &= tv_tag(v[i]) == tag;
+            if (__all(ok)) break;
+            if (!spin.again(tag, base)) return false;
+#pragma unroll
+            for (int i = 0; i < kStageWords; ++i) {
+                const uint32_t e = base + lane + step * i;
+                if (tv_tag(v[i]) != tag) v[i] = ld_tagged(src + e);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kStageWords; ++i) {
+            const uint32_t e = base + lane + step * i;
+            if (e < n) {
+                const float x = tv_val(v[i]);
+                ss = fmaf(x, x, ss);
+                dst[e] = GAIN ? x * bf_to_f(g[e]) : x;
+            }
+        }
+    }
+    return true;
+}
+
+// Same from a bf16 row that needs no wait (the token embedding of layer 0);
+// g == nullptr copies without a gain.
+__device__ __forceinline__ void stage_bf16(const uint16_t* __restrict__ src, uint32_t n, float* __restrict__ dst,
+                                           const uint16_t* __restrict__ g, int w, int nw, float& ss) {
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint32_t step = 64u * (uint32_t)nw;
+    for (uint32_t e = 64u * (uint32_t)w + lane; e < n; e += step) {
+        const float x = bf_to_f(src[e]);
+        ss = fmaf(x, x, ss);
+        dst[e] = g ? x * bf_to_f(g[e]) : x;
+    }
+}
+
+// RMSNorm statistics: wave w stored its total wave_total(ss) in part[w]; every
+// wave forms r = 1 / sqrt(mean + eps) from the four partials in order 0..3.
+__device__ __forceinline__ float rms_scale(const float* part, int nw, int d, float eps) {
+    float s = part[0];
+    for (int w = 1; w < nw; ++w) s += part[w];
+    return 1.0f / sqrtf(s / (float)d + eps);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Row sources: piece p (16 bytes = 8 bf16) of row i of the current batch.
+// ---------------------------------------------------------------------------------------------
+struct RingBatch {  // rows back to back in the LDS ring starting at byte `base`
+    const char* ring;
+    uint32_t base, rb, ring_bytes;
+    __device__ __forceinline__ uint4 piece(uint32_t i, uint32_t p) const {
+        uint32_t a = base + i * rb + p * 16u;
+        a = a >= ring_bytes ? a - ring_bytes : a;
+        return *(const uint4*)(ring + a);
+    }
+};
+
+// Activation source (fp32 in LDS): the 8 values of piece p of batch row b.
 struct XLds {
     const float* x;
     uint32_t k;
@@ -184,24 +250,12 @@ struct XLds {
         c = *(const float4*)(q + 4);
     }
 };
-struct XGlobal {
-    const float* x;
-    uint32_t stride;
-    __device__ __forceinline__ void piece(int b, uint32_t p, float4& a, float4& c) const {
-        const float* q = x + (size_t)b * stride + 8 * p;
-        a = *(const float4*)q;
-        c = *(const float4*)(q + 4);
-    }
-};
 
-// out[i][b] = dot(row r0 + i, x_b) for i < nr (nr <= R rows processed together:
-// the activation pieces are read once for all of them).  Per row, lane l
-// accumulates pieces p = l, l + 64, ... in ascending order, then wave_total
-// reduces in its fixed tree; the value of a row never depends on R, nr or on
-// which other rows share the batch.
+// out[i][b] = dot(row i, x_b) for the R rows of a batch.  Lane l accumulates
+// pieces p = l, l + 64, ... in ascending order, then wave_total reduces in its
+// fixed tree; a row's value never depends on R or on the other rows.
 template <int B, int R, class Rows, class X>
-__device__ __forceinline__ void rows_dot(const Rows& rows, uint32_t r0, int nr, int np, const X& x,
-                                         float (&out)[R][B]) {
+__device__ __forceinline__ void rows_dot(const Rows& rows, int np, const X& x, float (&out)[R][B]) {
     const int lane = lane_id();
     float acc[R][B];
 #pragma unroll
@@ -210,28 +264,25 @@ __device__ __forceinline__ void rows_dot(const Rows& rows, uint32_t r0, int nr, 
         for (int b = 0; b < B; ++b) acc[i][b] = 0.f;
 #pragma unroll 2
     for (int p = lane; p < np; p += 64) {
+        uint4 w[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) w[i] = rows.piece((uint32_t)i, (uint32_t)p);
         float4 xa[B], xb[B];
 #pragma unroll
         for (int b = 0; b < B; ++b) x.piece(b, (uint32_t)p, xa[b], xb[b]);
-        uint4 w[R];
 #pragma unroll
         for (int i = 0; i < R; ++i)
-            if (i < nr) w[i] = rows.piece(r0 + i, (uint32_t)p);
 #pragma unroll
-        for (int i = 0; i < R; ++i)
-            if (i < nr)
-#pragma unroll
-                for (int b = 0; b < B; ++b) acc[i][b] = dot8(w[i], xa[b], xb[b], acc[i][b]);
+            for (int b = 0; b < B; ++b) acc[i][b] = dot8(w[i], xa[b], xb[b], acc[i][b]);
     }
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
-        for (int b = 0; b < B; ++b) out[i][b] = (i < nr) ? wave_total(acc[i][b]) : 0.f;
+        for (int b = 0; b < B; ++b) out[i][b] = wave_total(acc[i][b]);
 }
 
-// Rows processed together for a row of `rb` bytes: the batch of the four
-// compute waves stays within 64 KB of the ring.
-__host__ __device__ constexpr int rows_per_batch(uint32_t rb) { return rb <= 4096u ? 4 : rb <= 8192u ? 2 : 1; }
+// Rows of one compute wave's batch for a row of `rb` bytes: about 8 KB per wave.
+__host__ __device__ constexpr int rows_per_batch(uint32_t rb) { return rb <= 2048u ? 4 : rb <= 4096u ? 2 : 1; }
 
 template <int B>
 __device__ __forceinline__ float pick(const float (&a)[B], int i) {
@@ -258,7 +309,7 @@ __device__ __forceinline__ float qk8(const float* q, uint4 k) {
     return a;
 }
 
-// Running greedy choice: larger value wins, ties to the lower index.
+// Greedy order: larger logit first, ties to the lower token id (first maximum).
 __device__ __forceinline__ bool head_better(float v, int32_t i, float bv, int32_t bi) {
     return v > bv || (v == bv && i < bi);
 }
@@ -270,24 +321,25 @@ __device__ __forceinline__ bool head_better(float v, int32_t i, float bv, int32_
 // the last split to finish).
 //
 // KV sources give the 16-byte piece (8 dims) of K or V at group t for this lane.
-// Group t holds kPPW consecutive positions; lane -> (position ps = lane / LPP,
+// Group t holds PPW consecutive positions; lane -> (position ps = lane / LPP,
 // dims dl = 8 * (lane % LPP)).
 // ---------------------------------------------------------------------------------------------
 template <int HD>
 struct AttnGeom {
-    static constexpr int LPP = HD / 8;     // lanes per position
-    static constexpr int PPW = 64 / LPP;   // positions per 1 KB group
+    static constexpr int LPP = HD / 8;    // lanes per position
+    static constexpr int PPW = 64 / LPP;  // positions per 1 KB group
 };
 
 struct RingKV {
     const char* ring;
-    uint32_t base;  // stream offset of the item: group t = [K 1 KB][V 1 KB]
-    __device__ __forceinline__ uint4 k(int t) const {
-        return *(const uint4*)(ring + ((base + (uint32_t)t * 2048u + lane_id() * 16u) & (kRingBytes - 1u)));
+    uint32_t base, ring_bytes;  // ring byte of the item's first group: group t = [K 1 KB][V 1 KB]
+    __device__ __forceinline__ uint4 at(uint32_t off) const {
+        uint32_t a = base + off + lane_id() * 16u;
+        a = a >= ring_bytes ? a - ring_bytes : a;
+        return *(const uint4*)(ring + a);
     }
-    __device__ __forceinline__ uint4 v(int t) const {
-        return *(const uint4*)(ring + ((base + (uint32_t)t * 2048u + 1024u + lane_id() * 16u) & (kRingBytes - 1u)));
-    }
+    __device__ __forceinline__ uint4 k(int t) const { return at((uint32_t)t * 2048u); }
+    __device__ __forceinline__ uint4 v(int t) const { return at((uint32_t)t * 2048u + 1024u); }
 };
 
 template <int HD>
@@ -334,11 +386,10 @@ __device__ __forceinline__ void lse_merge(float& m, float& l, float* acc, float 
     m = mm;
 }
 
-// RoPE of the 8 dims [dl, dl+8) of one head whose raw fp32 values start at `raw`;
-// rotate-half pairs (i, i + HD/2) turn by the angle of table row `rope_row`.
+// RoPE of the 8 dims [dl, dl+8) of one head whose raw fp32 values start at `raw`
+// (LDS); rotate-half pairs (i, i + HD/2) turn by the angle of table row `rope_row`.
 template <int HD>
-__device__ __forceinline__ void rope8(const float* __restrict__ raw, const float2* __restrict__ rope_row, int dl,
-                                      float* out) {
+__device__ __forceinline__ void rope8(const float* raw, const float2* __restrict__ rope_row, int dl, float* out) {
     constexpr int half = HD / 2;
     const bool lo = dl < half;
 #pragma unroll
@@ -350,18 +401,21 @@ __device__ __forceinline__ void rope8(const float* __restrict__ raw, const float
     }
 }
 
-struct AttnScratch {  // LDS scratch of one item: per wave and head (m, l, acc[HD])
-    float* part;      // [kComputeWaves][kMaxGroup][HD + 2]
-};
+// LDS floats one attention item needs: staged q/k/v, per-wave partials, and the
+// partials of every split when this item merges them.
+template <int HD>
+__host__ __device__ constexpr uint32_t attn_lds_floats(int G, int nsplit) {
+    return (uint32_t)((G + 2) * HD + kComputeWaves * kMaxGroup * (HD + 2) + nsplit * G * (HD + 2) + 4);
+}
 
-// Runs one attention item with the calling wave (`wave` of `nwaves` waves of the
-// workgroup).  `need(t)` is called before group t is read (ring: wait for the
-// loader), `barrier()` synchronises the waves of the item.  Returns true when
-// this workgroup merged the final output (or no merge was needed).
+// Runs one attention item with the calling wave (`wave` of `nw` waves of the
+// workgroup, which all call it).  `need(t)` is called before group t is read
+// (ring: wait for the loader), `barrier()` synchronises the waves of the item.
+// Writes the attention output (tagged) or, when split, the item's partial; the
+// last split to arrive merges all partials in split order.  False on abort.
 template <int HD, class KV, class Need, class Barrier>
-__device__ void attn_item(const Params& P, int layer, int b, int g, int s, int p, const KV& kv, Need need,
-                          Barrier barrier, float* lds_part, int wave, int nwaves, uint32_t* tickets,
-                          bool& merged_here) {
+__device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int layer, int b, int g, int s, int p, const KV& kv,
+                          Need& need, Barrier& barrier, float* xs, int wave, int nw, Spin& spin) {
     using Geo = AttnGeom<HD>;
     const int lane = lane_id();
     const int ps = lane / Geo::LPP;
@@ -370,14 +424,33 @@ __device__ void attn_item(const Params& P, int layer, int b, int g, int s, int p
     const SplitRange R = split_range<HD>(p, s, P.nsplit);
     const float scale = P.attn_scale;
     const float2* rope_row = P.rope + (size_t)p * (HD / 2);
-    const float* qkv_b = P.qkv + (size_t)b * P.qkv_rows;
+    const uint32_t tag_in = phase_tag(tag0, layer, 0) ^ ((P.inject && layer == 0) ? 0x80000000u : 0u);
+    const uint32_t tag_out = phase_tag(tag0, layer, 1);
+    const uint32_t stride = HD + 2;
 
-    // q heads of the group after RoPE (fp32)
+    // stage this group's raw q (G heads), k and v rows of the QKV output
+    float* q_raw = xs;
+    float* k_raw = xs + G * HD;
+    float* v_raw = k_raw + HD;
+    float* wpart = v_raw + HD;                          // [nw][kMaxGroup][HD + 2]
+    float* spart = wpart + kComputeWaves * kMaxGroup * stride;  // [nsplit][G][HD + 2]
+    uint32_t* flag = (uint32_t*)(spart + P.nsplit * G * stride);
+    {
+        const uint64_t* row = P.qkv + (size_t)b * P.qkv_rows;
+        float ss = 0.f;
+        bool ok = stage_tagged<false>(row + (size_t)g * G * HD, (uint32_t)(G * HD), tag_in, q_raw, nullptr, wave, nw,
+                                      spin, ss);
+        ok = ok && stage_tagged<false>(row + (size_t)(P.Hq + g) * HD, HD, tag_in, k_raw, nullptr, wave, nw, spin, ss);
+        ok = ok && stage_tagged<false>(row + (size_t)(P.Hq + P.Hkv + g) * HD, HD, tag_in, v_raw, nullptr, wave, nw,
+                                       spin, ss);
+        if (!ok) return false;
+    }
+    if (!barrier()) return false;
+
     float q[kMaxGroup][8];
 #pragma unroll
-    for (int j = 0; j < kMaxGroup; ++j) {
-        if (j < G) rope8<HD>(qkv_b + (size_t)(g * G + j) * HD, rope_row, dl, q[j]);
-    }
+    for (int j = 0; j < kMaxGroup; ++j)
+        if (j < G) rope8<HD>(q_raw + j * HD, rope_row, dl, q[j]);
     float m[kMaxGroup], l[kMaxGroup], acc[kMaxGroup][8];
 #pragma unroll
     for (int j = 0; j < kMaxGroup; ++j) {
@@ -406,22 +479,20 @@ __device__ void attn_item(const Params& P, int layer, int b, int g, int s, int p
             }
         }
     };
-    for (int t = wave; t < R.ngroups; t += nwaves) {
-        need(t);
+    for (int t = wave; t < R.ngroups; t += nw) {
+        if (!need(t)) return false;
         const uint4 kp = kv.k(t), vp = kv.v(t);
         consume(kp, vp, R.s0 + t * Geo::PPW + ps < R.s0 + R.ncached);
     }
     // the new position: rotated k and bf16 k/v from this step's projections
     if (R.has_new && wave == 0) {
-        const float* kraw = qkv_b + (size_t)P.Hq * HD + (size_t)g * HD;
-        const float* vraw = qkv_b + (size_t)(P.Hq + P.Hkv) * HD + (size_t)g * HD;
         float kr[8];
-        rope8<HD>(kraw, rope_row, dl, kr);
+        rope8<HD>(k_raw, rope_row, dl, kr);
         const uint4 kp = make_uint4(pack_bf2(kr[0], kr[1]), pack_bf2(kr[2], kr[3]), pack_bf2(kr[4], kr[5]),
                                     pack_bf2(kr[6], kr[7]));
-        const uint4 vp = make_uint4(pack_bf2(vraw[dl], vraw[dl + 1]), pack_bf2(vraw[dl + 2], vraw[dl + 3]),
-                                    pack_bf2(vraw[dl + 4], vraw[dl + 5]), pack_bf2(vraw[dl + 6], vraw[dl + 7]));
-        if (ps == 0) {  // KV append at position p
+        const uint4 vp = make_uint4(pack_bf2(v_raw[dl], v_raw[dl + 1]), pack_bf2(v_raw[dl + 2], v_raw[dl + 3]),
+                                    pack_bf2(v_raw[dl + 4], v_raw[dl + 5]), pack_bf2(v_raw[dl + 6], v_raw[dl + 7]));
+        if (ps == 0) {  // KV append at position p (read by later steps)
             const size_t row = ((((size_t)layer * P.kv_b + b) * P.Hkv + g) * P.S + p) * HD + dl;
             *(uint4*)(P.kcache + row) = kp;
             *(uint4*)(P.vcache + row) = vp;
@@ -442,12 +513,11 @@ __device__ void attn_item(const Params& P, int layer, int b, int g, int s, int p
         }
     }
     // merge the waves in order through LDS
-    const int stride = HD + 2;
     if (ps == 0) {
 #pragma unroll
         for (int j = 0; j < kMaxGroup; ++j) {
             if (j < G) {
-                float* dst = lds_part + ((size_t)wave * kMaxGroup + j) * stride;
+                float* dst = wpart + ((size_t)wave * kMaxGroup + j) * stride;
                 if (dl == 0) {
                     dst[0] = m[j];
                     dst[1] = l[j];
@@ -457,19 +527,17 @@ __device__ void attn_item(const Params& P, int layer, int b, int g, int s, int p
             }
         }
     }
-    barrier();
-    merged_here = false;
-    if (wave != 0) return;
-    if (ps == 0) {
+    if (!barrier()) return false;
+    if (wave == 0 && ps == 0) {
 #pragma unroll
         for (int j = 0; j < kMaxGroup; ++j) {
             if (j < G) {
-                const float* src = lds_part + (size_t)j * stride;
+                const float* src = wpart + (size_t)j * stride;
                 float mm = src[0], ll = src[1], aa[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) aa[e] = src[2 + dl + e];
-                for (int w = 1; w < nwaves; ++w) {
-                    const float* sw = lds_part + ((size_t)w * kMaxGroup + j) * stride;
+                for (int w = 1; w < nw; ++w) {
+                    const float* sw = wpart + ((size_t)w * kMaxGroup + j) * stride;
                     float a2[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) a2[e] = sw[2 + dl + e];
@@ -482,100 +550,160 @@ __device__ void attn_item(const Params& P, int layer, int b, int g, int s, int p
             }
         }
     }
-    float* out_b = P.attn + (size_t)b * P.Hq * HD;
+    uint64_t* out_b = P.attn + (size_t)b * P.Hq * HD;
     if (P.nsplit == 1) {
-        if (ps == 0) {
+        if (wave == 0 && ps == 0) {
 #pragma unroll
             for (int j = 0; j < kMaxGroup; ++j) {
                 if (j < G) {
                     const float inv = 1.0f / l[j];
-                    float* o = out_b + (size_t)(g * G + j) * HD + dl;
-                    *(float4*)o = make_float4(acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv);
-                    *(float4*)(o + 4) = make_float4(acc[j][4] * inv, acc[j][5] * inv, acc[j][6] * inv, acc[j][7] * inv);
+                    uint64_t* o = out_b + (size_t)(g * G + j) * HD + dl;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) st_tagged(o + e, acc[j][e] * inv, tag_out);
                 }
             }
         }
-        merged_here = true;
-        return;
+        return true;
     }
-    // split: publish the partial, the last split to arrive merges all of them in order
+    // split: publish the partial; the last split to arrive merges all of them
     const size_t pstride = (size_t)G * stride;
-    float* part = P.attn_part + (((size_t)b * P.Hkv + g) * P.nsplit) * pstride;
-    if (ps == 0) {
+    uint64_t* part = P.attn_part + (((size_t)b * P.Hkv + g) * P.nsplit) * pstride;
+    uint32_t* tk = P.attn_ticket + (((size_t)layer * P.B + b) * P.Hkv + g) * kCtrStride;
+    if (wave == 0) {
+        if (ps == 0) {
 #pragma unroll
-        for (int j = 0; j < kMaxGroup; ++j) {
-            if (j < G) {
-                float* dst = part + (size_t)s * pstride + (size_t)j * stride;
-                if (dl == 0) {
-                    dst[0] = m[j];
-                    dst[1] = l[j];
+            for (int j = 0; j < kMaxGroup; ++j) {
+                if (j < G) {
+                    uint64_t* dst = part + (size_t)s * pstride + (size_t)j * stride;
+                    if (dl == 0) {
+                        st_tagged(dst, m[j], tag_out);
+                        st_tagged(dst + 1, l[j], tag_out);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) st_tagged(dst + 2 + dl + e, acc[j][e], tag_out);
                 }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dst[2 + dl + e] = acc[j][e];
             }
         }
+        uint32_t old = 0;
+        if (lane == 0) old = __hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = __shfl(old, 0, 64);
+        if (lane == 0) *flag = (old == (uint32_t)P.nsplit - 1u) ? 1u : 0u;
     }
-    uint32_t* tk = tickets + (((size_t)layer * P.B + b) * P.Hkv + g) * kCtrStride;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    uint32_t old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __shfl(old, 0, 64);
-    if (old != (uint32_t)P.nsplit - 1u) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (ps == 0) {
+    if (!barrier()) return false;
+    if (*flag == 0u) return true;
+    // last arrival: every wave stages the partials, wave 0 merges them in split order
+    {
+        float ss = 0.f;
+        if (!stage_tagged<false>(part, (uint32_t)(P.nsplit * pstride), tag_out, spart, nullptr, wave, nw, spin, ss))
+            return false;
+    }
+    if (!barrier()) return false;
+    if (wave == 0) {
+        if (ps == 0) {
 #pragma unroll
-        for (int j = 0; j < kMaxGroup; ++j) {
-            if (j < G) {
-                const float* s0p = part + (size_t)j * stride;
-                float mm = s0p[0], ll = s0p[1], aa[8];
+            for (int j = 0; j < kMaxGroup; ++j) {
+                if (j < G) {
+                    const float* s0p = spart + (size_t)j * stride;
+                    float mm = s0p[0], ll = s0p[1], aa[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) aa[e] = s0p[2 + dl + e];
-                for (int sp = 1; sp < P.nsplit; ++sp) {
-                    const float* src = part + (size_t)sp * pstride + (size_t)j * stride;
-                    float a2[8];
+                    for (int e = 0; e < 8; ++e) aa[e] = s0p[2 + dl + e];
+                    for (int sp = 1; sp < P.nsplit; ++sp) {
+                        const float* src = spart + (size_t)sp * pstride + (size_t)j * stride;
+                        float a2[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) a2[e] = src[2 + dl + e];
-                    lse_merge(mm, ll, aa, src[0], src[1], a2);
+                        for (int e = 0; e < 8; ++e) a2[e] = src[2 + dl + e];
+                        lse_merge(mm, ll, aa, src[0], src[1], a2);
+                    }
+                    const float inv = 1.0f / ll;
+                    uint64_t* o = out_b + (size_t)(g * G + j) * HD + dl;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) st_tagged(o + e, aa[e] * inv, tag_out);
                 }
-                const float inv = 1.0f / ll;
-                float* o = out_b + (size_t)(g * G + j) * HD + dl;
-                *(float4*)o = make_float4(aa[0] * inv, aa[1] * inv, aa[2] * inv, aa[3] * inv);
-                *(float4*)(o + 4) = make_float4(aa[4] * inv, aa[5] * inv, aa[6] * inv, aa[7] * inv);
             }
         }
+        if (lane == 0) __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (lane == 0) __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    merged_here = true;
+    return true;
 }
 
 // ---------------------------------------------------------------------------------------------
-// Greedy argmax over the per-wave partials (value, index) of every sequence.
+// LM head: every compute wave publishes its argmax partial (value, index) tagged;
+// the last wave to arrive on the ticket reduces all partials, writes the greedy
+// tokens and advances the context lengths.  A NaN logit travels as a NaN partial.
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ void reduce_head_parts(const HeadPart* parts, int nparts, int B, int32_t* tok_out,
-                                                  uint32_t* nan_flag) {
+template <int B>
+__device__ __forceinline__ bool head_publish(const Params& P, const StepArgs& A, uint32_t slot, const float (&bv)[B],
+                                             const int32_t (&bi)[B], Spin& spin) {
     const int lane = lane_id();
+    const uint32_t tag = phase_tag(A.tag0, P.L, 0);
+    if (lane < B) {
+        uint64_t* dst = P.head_part + ((size_t)slot * P.B + lane) * 2;
+        int32_t i = bi[0];
+#pragma unroll
+        for (int b = 1; b < B; ++b)
+            if (lane == b) i = bi[b];
+        st_tagged(dst, pick<B>(bv, lane), tag);
+        st_tagged(dst + 1, __int_as_float(i), tag);
+    }
+    uint32_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(P.head_ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0, 64);
+    if (old != P.n_head_slots - 1u) return true;
+    // last wave of the step
+    bool nan_seen = false;
     for (int b = 0; b < B; ++b) {
-        float bv = -INFINITY;
-        int32_t bi = 0x7FFFFFFF;
-        for (int k = lane; k < nparts; k += 64) {
-            HeadPart hp = parts[(size_t)k * B + b];
-            if (hp.v != hp.v) *nan_flag = 1;
-            if (head_better(hp.v, hp.i, bv, bi)) {
-                bv = hp.v;
-                bi = hp.i;
+        float best = -INFINITY;
+        int32_t besti = 0x7FFFFFFF;
+        for (uint32_t k0 = 0; k0 < P.n_head_slots; k0 += 64u * kStageWords / 2) {
+            uint64_t w[kStageWords];
+#pragma unroll
+            for (int i = 0; i < kStageWords; ++i) {
+                const uint32_t k = k0 + (uint32_t)lane + 64u * (uint32_t)(i / 2);
+                w[i] = k < P.n_head_slots ? ld_tagged(P.head_part + ((size_t)k * P.B + b) * 2 + (i & 1))
+                                          : ((uint64_t)tag << 32);
+            }
+            spin.start();
+            for (;;) {
+                bool ok = true;
+#pragma unroll
+                for (int i = 0; i < kStageWords; ++i) ok &= tv_tag(w[i]) == tag;
+                if (__all(ok)) break;
+                if (!spin.again(tag, k0)) return false;
+#pragma unroll
+                for (int i = 0; i < kStageWords; ++i) {
+                    const uint32_t k = k0 + (uint32_t)lane + 64u * (uint32_t)(i / 2);
+                    if (tv_tag(w[i]) != tag) w[i] = ld_tagged(P.head_part + ((size_t)k * P.B + b) * 2 + (i & 1));
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kStageWords; i += 2) {
+                const uint32_t k = k0 + (uint32_t)lane + 64u * (uint32_t)(i / 2);
+                if (k < P.n_head_slots) {
+                    const float v = tv_val(w[i]);
+                    const int32_t idx = __float_as_int(tv_val(w[i + 1]));
+                    if (v != v) nan_seen = true;
+                    if (head_better(v, idx, best, besti)) {
+                        best = v;
+                        besti = idx;
+                    }
+                }
             }
         }
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            const float ov = __shfl_xor(bv, m, 64);
-            const int32_t oi = __shfl_xor(bi, m, 64);
-            if (head_better(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
+        for (int msk = 32; msk >= 1; msk >>= 1) {
+            const float ov = __shfl_xor(best, msk, 64);
+            const int32_t oi = __shfl_xor(besti, msk, 64);
+            if (head_better(ov, oi, best, besti)) {
+                best = ov;
+                besti = oi;
             }
         }
-        if (lane == 0) tok_out[b] = bi;
+        if (lane == 0) A.tok_out[b] = besti;
     }
+    if (lane < B) P.state->ctx_len[lane] = P.state->ctx_len[lane] + 1;
+    if (lane == 0) __hip_atomic_store(P.head_ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__any(nan_seen)) raise_error_impl(P.state, P.host_err, spin.abort_flag, DERR_NAN, 0, 0);
+    return true;
 }
 
 }  // namespace mk

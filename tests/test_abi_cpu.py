@@ -80,21 +80,33 @@ def test_runtime_validation():
     assert st == mk.MK_OK and ws_tr > mk.mk_query_sizes(c, rt())[1]
 
 
+LDS_BYTES, LDS_STATIC, CHUNK, MIN_RING = 160 * 1024, 1024, 1024, 64
+
+
+def staged_bytes(cfg, batch):
+    """fp32 activations one GEMV instruction stages in LDS: x rows of the widest
+    input (d, Hq*hd or ffn) plus up to 64 residual rows for O / DOWN."""
+    return 4 * batch * max(cfg.hidden, cfg.n_q_heads * cfg.head_dim + 64, cfg.ffn + 64)
+
+
 @pytest.mark.parametrize("cfg", [I.TINY, I.LLAMA_1B, I.LLAMA_8B], ids=lambda c: c.name)
 @pytest.mark.parametrize("cus", [256, 304, 80, 7, 1])
 @pytest.mark.parametrize("batch", [1, 2])
 def test_schedule_verifies(cfg, cus, batch):
     st, info = mk.mk_plan_inspect(mk.model_config(cfg), rt(batch, 200), cus)
-    if batch * cfg.hidden * 4 > 16384:  # fp32 normed activations must fit the 16 KB LDS slot
+    if LDS_BYTES - LDS_STATIC - staged_bytes(cfg, batch) < MIN_RING * CHUNK:  # no room left for the weight ring
         assert st == mk.MK_E_UNSUPPORTED
         return
     assert st == mk.MK_OK
     assert info["verify"] == 0
     assert info["phases"] == 5 * cfg.n_layers + 1
-    assert info["counters"] == 5 * cfg.n_layers + 2
     assert info["weight_bytes"] == cfg.weight_bytes()
+    assert info["x_bytes"] >= staged_bytes(cfg, batch)
+    assert info["ring_chunks"] == (LDS_BYTES - LDS_STATIC - info["x_bytes"]) // CHUNK >= MIN_RING
     items = batch * cfg.n_kv_heads * info["attn_splits"]
-    assert info["instructions"] <= cfg.n_layers * (4 * cus + items) + cus
+    od = -(-(-(-cfg.hidden // cus)) // 64)  # O / DOWN instructions per CU (<= 64 rows each)
+    assert info["instructions"] <= cfg.n_layers * (2 * cus + items + 2 * od * cus) + cus
+    assert info["head_instructions"] == min(cus, cfg.vocab)
 
 
 def test_schedule_one_tile_per_cu_per_matrix():
