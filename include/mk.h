@@ -170,11 +170,13 @@ mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* r
                           int32_t cap);
 
 /* Copy the device timeline of the last megakernel step (needs trace = 1).
- * Per compute unit `records_per_cu` records of 8 uint32: {op | layer << 16,
+ * Per compute unit `records_per_cu` records of 12 uint32: {op | layer << 16,
  * start, inputs staged, compute end, end, loader issue end, ticks waiting for
- * the loader, ticks the loader waited for ring space}, times = low 32 bits of
- * the 100 MHz s_memrealtime clock, in queue order.  With h_buf == NULL only
- * *written (the byte size) is set.  Synchronises the handle's creation stream. */
+ * the loaders, ticks the loaders waited for ring space, staging start (after
+ * the wave barrier), then for attention: inputs staged, KV groups consumed,
+ * output written (0 elsewhere)}, times = low 32 bits of the 100 MHz
+ * s_memrealtime clock, in queue order.  With h_buf == NULL only *written (the
+ * byte size) is set.  Synchronises the handle's creation stream. */
 mk_status mk_read_trace(mk_handle* h, void* h_buf, size_t bytes, size_t* written, int32_t* records_per_cu);
 
 /* Number of kernel launches one decode step makes in the handle's mode. */

@@ -40,10 +40,16 @@ int mk_bench_sync(int mode, int n_wg, int rounds, void* d_ctr, void* d_data, voi
 
 /* HBM -> LDS streaming rate of the direct-to-LDS 16-byte-per-lane load:
  * n_wg workgroups of `waves` waves; each wave streams its share of d_src 1 KB
- * per load with `lag` loads in flight (lag in {4,12,24,48,60} for 1 wave,
- * {12,24,48} for 2, {12,24} for 4).  d_out: one uint64 = ticks (100 MHz) of
- * workgroup 0.  Returns 0, 1 on unsupported arguments, 4 on launch error. */
-int mk_bench_lds_stream(int lag, int waves, const void* d_src, size_t bytes, int n_wg, void* d_out, void* stream);
+ * per load with `lag` loads in flight (lag in {4,12,24,32,40,48,60} for 1 wave,
+ * {12,24,48} for 2, {12,24} for 4).  gran == 0: each wave reads one contiguous
+ * share; gran > 0: blocks of `gran` KB dealt round-robin over the waves (the
+ * share must be a whole number of blocks).  probe > 0: every probe-th load is
+ * followed by an LDS read the wave waits for (lgkmcnt(0)), to show whether the
+ * direct-to-LDS loads in flight hold that counter too.  d_out: two uint64, [0] =
+ * ticks (100 MHz) of workgroup 0.  Returns 0, 1 on unsupported arguments, 4 on
+ * launch error. */
+int mk_bench_lds_stream(int lag, int waves, int gran, int probe, const void* d_src, size_t bytes, int n_wg,
+                        void* d_out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -150,21 +150,31 @@ extern "C" int mk_bench_sync(int mode, int n_wg, int rounds, void* d_ctr, void* 
 // ------------------------------------------------------------------------------------------------
 namespace {
 template <int LAG, int WAVES>
-__global__ void __launch_bounds__(64 * WAVES) k_lds_stream(const char* src, size_t bytes, uint64_t* out) {
+__global__ void __launch_bounds__(64 * WAVES) k_lds_stream(const char* src, size_t bytes, uint32_t gran,
+                                                           uint32_t probe, uint64_t* out) {
     __shared__ __attribute__((aligned(1024))) char ring[WAVES * 32 * 1024];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const size_t chunks = bytes / 1024;
-    const size_t per = chunks / ((size_t)gridDim.x * WAVES);
-    const size_t first = ((size_t)blockIdx.x * WAVES + wave) * per;
+    const size_t streams = (size_t)gridDim.x * WAVES, s = (size_t)blockIdx.x * WAVES + wave;
+    const size_t per = bytes / 1024 / streams;
     const uint32_t base = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)ring + wave * 32768u;
-    const char* p = src + first * 1024 + (threadIdx.x & 63) * 16;
+    const char* lane_src = src + (threadIdx.x & 63) * 16;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     for (size_t c = 0; c < per; ++c) {
+        // stream s owns chunks [s * per, (s + 1) * per) (gran == 0), or blocks of
+        // `gran` chunks dealt round-robin over the streams
+        const size_t chunk = gran == 0 ? s * per + c : ((c / gran) * streams + s) * gran + c % gran;
         asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                      :
-                     : "{m0}"(__builtin_amdgcn_readfirstlane(base + (uint32_t)(c & 31) * 1024u)), "v"(p + c * 1024)
+                     : "{m0}"(__builtin_amdgcn_readfirstlane(base + (uint32_t)(c & 31) * 1024u)),
+                       "v"(lane_src + chunk * 1024)
                      : "memory");
         __builtin_amdgcn_s_waitcnt((LAG & 15) | ((LAG >> 4) << 14) | (7 << 4) | (15 << 8));
+        if (probe && (c % probe) == 0) {
+            // one LDS read whose value is needed at once: s_waitcnt lgkmcnt(0)
+            const uint32_t v = __hip_atomic_load((const uint32_t*)(ring + 32768 * WAVES - 64), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (v == 0xDEADBEEFu) out[1] = v;
+        }
     }
     __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
     __syncthreads();
@@ -173,15 +183,18 @@ __global__ void __launch_bounds__(64 * WAVES) k_lds_stream(const char* src, size
 }
 }  // namespace
 
-extern "C" int mk_bench_lds_stream(int lag, int waves, const void* d_src, size_t bytes, int n_wg, void* d_out,
-                                   void* stream) {
-    if (!d_src || !d_out || n_wg < 1 || bytes < (size_t)n_wg * waves * 1024) return 1;
+extern "C" int mk_bench_lds_stream(int lag, int waves, int gran, int probe, const void* d_src, size_t bytes,
+                                   int n_wg, void* d_out, void* stream) {
+    if (!d_src || !d_out || n_wg < 1 || gran < 0 || probe < 0 || bytes < (size_t)n_wg * waves * 1024) return 1;
+    const size_t per = bytes / 1024 / ((size_t)n_wg * waves);
+    if (gran > 0 && per % (size_t)gran) return 1;  // whole blocks per stream keep every chunk in range
     const void* f = nullptr;
 #define MK_LS(L, W) if (lag == L && waves == W) f = (const void*)k_lds_stream<L, W>;
-    MK_LS(4, 1) MK_LS(12, 1) MK_LS(24, 1) MK_LS(48, 1) MK_LS(60, 1)
+    MK_LS(4, 1) MK_LS(12, 1) MK_LS(24, 1) MK_LS(32, 1) MK_LS(40, 1) MK_LS(48, 1) MK_LS(60, 1)
     MK_LS(12, 2) MK_LS(24, 2) MK_LS(48, 2) MK_LS(12, 4) MK_LS(24, 4)
 #undef MK_LS
     if (!f) return 1;
-    void* args[] = {&d_src, &bytes, &d_out};
+    uint32_t g = (uint32_t)gran, pr = (uint32_t)probe;
+    void* args[] = {&d_src, &bytes, &g, &pr, &d_out};
     return hipLaunchKernel(f, dim3(n_wg), dim3(64 * waves), args, 0, (hipStream_t)stream) == hipSuccess ? 0 : 4;
 }

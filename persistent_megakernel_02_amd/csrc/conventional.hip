@@ -226,7 +226,8 @@ __global__ void __launch_bounds__(kConvThreads) k_attn(Params P, StepArgs A, int
     auto need = [](int) { return true; };
     BlockBarrier barrier;
     Spin spin(&P, nullptr);
-    attn_item<HD>(P, A.tag0, layer, b, g, s, p, kv, need, barrier, xs, wave, kConvWaves, spin);
+    auto mark = [](int) {};
+    attn_item<HD>(P, A.tag0, layer, b, g, s, p, kv, need, barrier, xs, wave, kConvWaves, spin, mark);
 }
 
 // ------------------------------------------------------------------------------------------------

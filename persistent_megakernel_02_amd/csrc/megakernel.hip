@@ -5,21 +5,26 @@
 //  - one workgroup per compute unit walks that CU's instruction queue, built on
 //    the host before launch (the per-SM plan);
 //  - shared memory cut into pages lets the next instructions' weights load while
-//    the current one computes: one LOADER wave streams the CU's weight and KV
-//    bytes HBM -> LDS with 16-byte-per-lane direct-to-LDS loads
+//    the current one computes: LOADER waves stream the CU's weight and KV bytes
+//    HBM -> LDS with 16-byte-per-lane direct-to-LDS loads
 //    (global_load_lds_dwordx4) into a ring of 1 KB chunks that fills every byte
-//    of LDS the activations do not need, ahead of the four COMPUTE waves, and it
-//    keeps streaming while they wait on other compute units;
+//    of LDS the activations do not need, ahead of the four COMPUTE waves, and
+//    keep streaming while those wait on other compute units.  One wave's
+//    direct-to-LDS issue rate tops out near 16 GB/s, below a compute unit's
+//    share of HBM bandwidth, so the stream is dealt to kLoaderWaves waves:
+//    chunk c of the CU stream belongs to loader c mod kLoaderWaves;
 //  - dependencies travel with the data: every cross-CU activation is a tagged
 //    word (see mk_internal.h) and an instruction first stages its inputs into
 //    LDS, polling until every tag names the current step and phase;
 //  - every spin is bounded by a watchdog (s_memrealtime, 100 MHz): on expiry the
 //    CU records an error and all waves leave, so a launch always terminates.
 //
-// The loader's vector-memory instructions are only these LDS loads, so its
-// vmcnt counter counts exactly the chunks in flight; it publishes progress in
-// LDS after `s_waitcnt vmcnt(N)`.  Compute waves publish, per wave, the first
-// stream chunk they still need; the loader reuses ring space below the minimum.
+// A loader's vector-memory instructions are only these LDS loads, so its vmcnt
+// counter counts exactly its chunks in flight; after `s_waitcnt vmcnt(N)` it
+// publishes, in LDS, the first of its own chunks not yet resident (its j-th chunk
+// is stream chunk j * kLoaderWaves + k), and the stream prefix resident in the
+// ring is the minimum over the loaders.  Compute waves publish, per wave, the
+// first stream chunk they still need; loaders reuse ring space below the minimum.
 #include <hip/hip_runtime.h>
 
 #include "mk_device.h"
@@ -27,7 +32,7 @@
 namespace mk {
 
 struct Ctl {
-    uint32_t landed;                     // chunks of the stream resident in the ring
+    uint32_t landed[kLoaderWaves];       // loader k: first stream chunk of its own not yet resident
     uint32_t consumed[kComputeWaves];    // first chunk each compute wave still needs
     uint32_t bar;                        // compute-wave barrier arrivals (monotonic)
     uint32_t abort;                      // set when a wave gives up (error)
@@ -53,6 +58,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ uint32_t align_chunk(uint32_t b) { return (b + kChunk - 1u) & ~(kChunk - 1u); }
 
+// Context length of sequence b (LDS copy made at launch), wave-uniform so the
+// stream arithmetic that depends on it stays on the scalar unit.
+__device__ __forceinline__ int ctx_of(const int32_t* ctx, int b) { return __builtin_amdgcn_readfirstlane(ctx[b]); }
+
 // Bytes of the CU stream that instruction `in` consumes (whole chunks).
 template <int HD>
 __device__ __forceinline__ uint32_t instr_bytes(const Params& P, const Instr& in, const int32_t* ctx) {
@@ -65,7 +74,7 @@ __device__ __forceinline__ uint32_t instr_bytes(const Params& P, const Instr& in
         case OP_ATTN: {
             const int per_b = P.Hkv * P.nsplit;
             const int b = (int)in.begin / per_b, s = (int)in.begin % P.nsplit;
-            const SplitRange R = split_range<HD>(ctx[b], s, P.nsplit);
+            const SplitRange R = split_range<HD>(ctx_of(ctx, b), s, P.nsplit);
             return (uint32_t)R.ngroups * 2u * kChunk;
         }
         default: return 0;
@@ -179,120 +188,147 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 //  - up to three contiguous byte ranges read in order (QKV: the q, k and v rows
 //    of the tile; O, DOWN, HEAD: one range);
 //  - two matrices interleaved row by row (GATEUP: gate row r then up row r),
-//    `per` chunks of each in turn;
+//    2^per_shift chunks of each in turn;
 //  - the K and V blocks of consecutive position groups interleaved (ATTN), one
 //    chunk each, lanes past the cached positions re-reading the block start.
-// Only pointers and chunk counts, all wave-uniform, so the loop runs on SGPRs.
+// Only pointers and chunk counts, all wave-uniform: the address of any chunk is
+// a few scalar operations, so a loader can take every kLoaderWaves-th chunk.
 struct Stream {
-    const char* p[3];
-    uint32_t n[3];  // chunks per range (ranges), or pairs (interleaved)
-    uint32_t per;   // interleaved: chunks of each matrix per turn; 0 = ranges
-    int ncached;    // ATTN: valid positions of the split
-    bool attn;
+    const char *p0, *p1, *p2;
+    uint32_t end0, end1;  // ranges: chunk ends of the first two ranges
+    uint32_t per_shift;   // interleaved: log2(chunks of each matrix per turn)
+    int ncached;          // ATTN: valid positions of the split
+    bool inter, attn;
 };
 
 template <int HD>
 __device__ __forceinline__ bool setup_stream(const Params& P, const Instr& in, const DevLayer& Lw, const int32_t* ctx,
                                              Stream& S) {
-    S.per = 0;
+    S.inter = false;
     S.attn = false;
     S.ncached = 0;
-    S.n[1] = S.n[2] = 0;
-    S.p[1] = S.p[2] = nullptr;
+    S.per_shift = 0;
+    S.p1 = S.p2 = nullptr;
+    S.end0 = S.end1 = 0xFFFFFFFFu;
     uint32_t rb = 0;
     switch (in.op) {
         case OP_QKV: {
             rb = (uint32_t)P.d * 2u;
+            if (rb & (kChunk - 1u)) return false;
+            const uint32_t cpr = rb / kChunk;
             const uint32_t nq = (uint32_t)(P.Hq * HD), nk = (uint32_t)(P.Hkv * HD);
             const uint32_t r0 = in.begin, r1 = in.begin + in.count;
             const uint32_t q0 = min(r0, nq), q1 = min(r1, nq);
             const uint32_t k0 = min(max(r0, nq), nq + nk) - nq, k1 = min(max(r1, nq), nq + nk) - nq;
-            const uint32_t v0 = max(r0, nq + nk) - nq - nk, v1 = max(r1, nq + nk) - nq - nk;
-            S.p[0] = (const char*)Lw.wq + (size_t)q0 * rb;
-            S.n[0] = q1 - q0;
-            S.p[1] = (const char*)Lw.wk + (size_t)k0 * rb;
-            S.n[1] = k1 - k0;
-            S.p[2] = (const char*)Lw.wv + (size_t)v0 * rb;
-            S.n[2] = v1 - v0;
-            break;
+            const uint32_t v0 = max(r0, nq + nk) - nq - nk;
+            S.p0 = (const char*)Lw.wq + (size_t)q0 * rb;
+            S.p1 = (const char*)Lw.wk + (size_t)k0 * rb;
+            S.p2 = (const char*)Lw.wv + (size_t)v0 * rb;
+            S.end0 = (q1 - q0) * cpr;
+            S.end1 = S.end0 + (k1 - k0) * cpr;
+            return true;
         }
-        case OP_O:
-            rb = (uint32_t)(P.Hq * HD) * 2u;
-            S.p[0] = (const char*)Lw.wo + (size_t)in.begin * rb;
-            S.n[0] = in.count;
-            break;
-        case OP_DOWN:
-            rb = (uint32_t)P.F * 2u;
-            S.p[0] = (const char*)Lw.w_down + (size_t)in.begin * rb;
-            S.n[0] = in.count;
-            break;
-        case OP_HEAD:
+        case OP_O: rb = (uint32_t)(P.Hq * HD) * 2u; S.p0 = (const char*)Lw.wo + (size_t)in.begin * rb; break;
+        case OP_DOWN: rb = (uint32_t)P.F * 2u; S.p0 = (const char*)Lw.w_down + (size_t)in.begin * rb; break;
+        case OP_HEAD: rb = (uint32_t)P.d * 2u; S.p0 = (const char*)P.head + (size_t)in.begin * rb; break;
+        case OP_GATEUP: {
             rb = (uint32_t)P.d * 2u;
-            S.p[0] = (const char*)P.head + (size_t)in.begin * rb;
-            S.n[0] = in.count;
-            break;
-        case OP_GATEUP:
-            rb = (uint32_t)P.d * 2u;
-            S.p[0] = (const char*)Lw.w_gate + (size_t)in.begin * rb;
-            S.p[1] = (const char*)Lw.w_up + (size_t)in.begin * rb;
-            S.n[0] = in.count;
-            S.per = rb / kChunk;
-            return (rb & (kChunk - 1u)) == 0;
+            const uint32_t cpr = rb / kChunk;
+            if ((rb & (kChunk - 1u)) || (cpr & (cpr - 1u))) return false;  // whole, power-of-two chunks per row
+            S.p0 = (const char*)Lw.w_gate + (size_t)in.begin * rb;
+            S.p1 = (const char*)Lw.w_up + (size_t)in.begin * rb;
+            S.per_shift = (uint32_t)__builtin_ctz(cpr);
+            S.inter = true;
+            return true;
+        }
         case OP_ATTN: {
             const int per_b = P.Hkv * P.nsplit;
             const int b = (int)in.begin / per_b, g = ((int)in.begin % per_b) / P.nsplit, s = (int)in.begin % P.nsplit;
-            const SplitRange Rg = split_range<HD>(ctx[b], s, P.nsplit);
+            const SplitRange Rg = split_range<HD>(ctx_of(ctx, b), s, P.nsplit);
             const size_t base = ((((size_t)in.layer * P.kv_b + b) * P.Hkv + g) * P.S + Rg.s0) * HD;
-            S.p[0] = (const char*)(P.kcache + base);
-            S.p[1] = (const char*)(P.vcache + base);
-            S.n[0] = (uint32_t)Rg.ngroups;
-            S.per = 1;
+            S.p0 = (const char*)(P.kcache + base);
+            S.p1 = (const char*)(P.vcache + base);
             S.ncached = Rg.ncached;
+            S.inter = true;
             S.attn = true;
             return true;
         }
         default: return false;
     }
-    if (rb & (kChunk - 1u)) return false;  // fast path needs whole chunks per row
-    const uint32_t cpr = rb / kChunk;
-    S.n[0] *= cpr;
-    S.n[1] *= cpr;
-    S.n[2] *= cpr;
-    return true;
+    return (rb & (kChunk - 1u)) == 0;  // fast path needs whole chunks per row
+}
+
+// Wave-uniform base and per-lane offset of chunk c (instruction-relative) of a
+// fast-path stream.
+template <int HD>
+__device__ __forceinline__ const char* stream_chunk(const Stream& S, uint32_t c, uint32_t& voff) {
+    const uint32_t lane16 = (uint32_t)lane_id() * 16u;
+    if (!S.inter) {
+        if (c < S.end0) {
+            voff = c * kChunk + lane16;
+            return S.p0;
+        }
+        if (c < S.end1) {
+            voff = (c - S.end0) * kChunk + lane16;
+            return S.p1;
+        }
+        voff = (c - S.end1) * kChunk + lane16;
+        return S.p2;
+    }
+    const uint32_t pair = c >> (S.per_shift + 1u);
+    const uint32_t within = c & ((2u << S.per_shift) - 1u);
+    const uint32_t off = ((pair << S.per_shift) + (within & ((1u << S.per_shift) - 1u))) * kChunk;
+    bool valid = true;
+    if (S.attn) valid = (int)(pair * AttnGeom<HD>::PPW) + lane_id() / AttnGeom<HD>::LPP < S.ncached;
+    voff = off + (valid ? lane16 : 0u);
+    return (within >> S.per_shift) ? S.p1 : S.p0;
 }
 
 // ------------------------------------------------------------------------------------------------
-// loader wave
+// loader waves
 // ------------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t landed_prefix(const Ctl* ctl) {
+    uint32_t m = lds_ld(&ctl->landed[0]);
+#pragma unroll
+    for (int k = 1; k < kLoaderWaves; ++k) m = min(m, lds_ld(&ctl->landed[k]));
+    return m;
+}
+
 template <int HD>
-__device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* ring, uint32_t q0, uint32_t q1, const int32_t* ctx) {
-    const uint32_t ring_base = (uint32_t)(size_t)(lds_ptr_t)ring;
+__device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* ring, int k, uint32_t q0, uint32_t q1,
+                                            const int32_t* ctx) {
     const uint32_t N = P.ring_chunks;
-    const uint32_t lane16 = (uint32_t)lane_id() * 16u;
-    uint32_t issued = 0, landed = 0, limit = N, slot = 0;
+    const uint32_t NL = (uint32_t)kLoaderWaves;
+    const uint32_t ring_base = (uint32_t)(size_t)(lds_ptr_t)ring;
+    const uint32_t ring_end = ring_base + N * kChunk;
+    uint32_t issued = 0, landed = 0;  // this loader's own chunks
+    uint32_t limit = N;               // stream chunks below it may be written
+    uint32_t cb = 0;                  // stream index of the current instruction's first chunk
+    uint32_t c = (uint32_t)k;         // stream index of this loader's next chunk (c = k mod NL)
+    uint32_t slot = ring_base + ((uint32_t)k % N) * kChunk;  // LDS address of ring slot c mod N
     bool stop = false;
     uint32_t stall = 0;
     auto publish = [&](uint32_t n) {
         landed = n;
-        lds_st(&ctl->landed, n);
+        lds_st(&ctl->landed[k], n * NL + (uint32_t)k);
     };
-    // Ring full: retire the chunks in flight in steps (so compute waves can free
-    // space without the pipe draining), then sleep until space appears.
+    // Ring full: retire this loader's chunks in flight in steps (so compute waves
+    // can free space without the pipe draining), then sleep until space appears.
     auto make_room = [&]() -> bool {
         const uint32_t ts = P.trace ? (uint32_t)now_ticks() : 0u;
         uint64_t t0 = 0;
         uint32_t polls = 0;
         bool ok = true;
         for (;;) {
-            limit = min_consumed(ctl) + N;
-            if (issued < limit) break;
+            limit = __builtin_amdgcn_readfirstlane(min_consumed(ctl)) + N;
+            if (c < limit) break;
             const uint32_t fly = issued - landed;
-            if (fly > 24u) {
-                wait_vmcnt<24>();
-                publish(issued - 24u);
-            } else if (fly > 8u) {
-                wait_vmcnt<8>();
-                publish(issued - 8u);
+            if (fly > 12u) {
+                wait_vmcnt<12>();
+                publish(issued - 12u);
+            } else if (fly > 4u) {
+                wait_vmcnt<4>();
+                publish(issued - 4u);
             } else if (fly > 0u) {
                 wait_vmcnt<0>();
                 publish(issued);
@@ -313,8 +349,11 @@ __device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* rin
         if (P.trace) stall += (uint32_t)now_ticks() - ts;
         return ok;
     };
+    // after each issue: next own chunk and slot, and keep at most kLoaderLag in flight
     auto advance = [&]() {
-        slot = (slot + 1u == N) ? 0u : slot + 1u;
+        c += NL;
+        slot += NL * kChunk;
+        if (slot >= ring_end) slot -= N * kChunk;
         ++issued;
         if (issued - landed > (uint32_t)kLoaderLag) {
             wait_vmcnt<kLoaderLag>();
@@ -324,70 +363,44 @@ __device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* rin
     for (uint32_t i = q0; i < q1 && !stop; ++i) {
         const Instr in = ld_const(P.instrs + i);
         const uint32_t nch = instr_bytes<HD>(P, in, ctx) / kChunk;
-        if (P.trace && lane_id() == 0 && i > q0) {
+        if (k == 0 && P.trace && lane_id() == 0 && i > q0) {
             uint32_t* rec = P.trace + ((size_t)blockIdx.x * P.trace_stride + (i - 1 - q0)) * kTraceWords;
             rec[5] = (uint32_t)now_ticks();
             rec[7] = stall;
         }
         stall = 0;
-        if (nch == 0) continue;
-        const DevLayer Lw = ld_const(P.layers + (in.layer < P.L ? in.layer : 0));
-        Stream S;
-        if (setup_stream<HD>(P, in, Lw, ctx, S)) {
-            if (S.per == 0) {
-#pragma unroll
-                for (int r = 0; r < 3; ++r) {
-                    const char* base = uniform_ptr(S.p[r]);
-                    for (uint32_t c = 0; c < S.n[r] && !stop; ++c) {
-                        if (issued >= limit && !make_room()) {
-                            stop = true;
-                            break;
-                        }
-                        dma_chunk_s(base, c * kChunk + lane16, ring_base + slot * kChunk);
-                        advance();
+        const uint32_t ce = cb + nch;
+        if (c < ce) {
+            const DevLayer Lw = ld_const(P.layers + (in.layer < P.L ? in.layer : 0));
+            Stream S;
+            if (setup_stream<HD>(P, in, Lw, ctx, S)) {
+                for (; c < ce; ) {
+                    if (c >= limit && !make_room()) {
+                        stop = true;
+                        break;
                     }
+                    uint32_t voff;
+                    const char* base = uniform_ptr(stream_chunk<HD>(S, c - cb, voff));
+                    dma_chunk_s(base, voff, slot);
+                    advance();
                 }
             } else {
-                const char* ba = uniform_ptr(S.p[0]);
-                const char* bb = uniform_ptr(S.p[1]);
-                const int lane_pos = lane_id() / AttnGeom<HD>::LPP;
-                const uint32_t rbytes = S.per * kChunk;
-                for (uint32_t r = 0; r < S.n[0] && !stop; ++r) {
-                    // ATTN: lanes whose position lies past the cached ones re-read the block start
-                    const bool valid = !S.attn || (int)(r * AttnGeom<HD>::PPW) + lane_pos < S.ncached;
-                    const uint32_t lane_off = valid ? lane16 : 0u;
-                    for (uint32_t k = 0; k < S.per && !stop; ++k) {
-                        if (issued >= limit && !make_room()) {
-                            stop = true;
-                            break;
-                        }
-                        dma_chunk_s(ba, r * rbytes + k * kChunk + lane_off, ring_base + slot * kChunk);
-                        advance();
+                for (; c < ce; ) {
+                    if (c >= limit && !make_room()) {
+                        stop = true;
+                        break;
                     }
-                    for (uint32_t k = 0; k < S.per && !stop; ++k) {
-                        if (issued >= limit && !make_room()) {
-                            stop = true;
-                            break;
-                        }
-                        dma_chunk_s(bb, r * rbytes + k * kChunk + lane_off, ring_base + slot * kChunk);
-                        advance();
-                    }
+                    dma_chunk(chunk_src<HD>(P, in, Lw, c - cb, ctx), slot);
+                    advance();
                 }
-            }
-        } else {
-            for (uint32_t c = 0; c < nch; ++c) {
-                if (issued >= limit && !make_room()) {
-                    stop = true;
-                    break;
-                }
-                dma_chunk(chunk_src<HD>(P, in, Lw, c, ctx), ring_base + slot * kChunk);
-                advance();
             }
         }
+        cb = ce;
     }
     wait_vmcnt<0>();
-    publish(issued);
-    if (P.trace && q1 > q0 && lane_id() == 0) {
+    landed = issued;
+    lds_st(&ctl->landed[k], 0xFFFFFFFFu);  // every chunk of this loader is resident
+    if (k == 0 && P.trace && q1 > q0 && lane_id() == 0) {
         P.trace[((size_t)blockIdx.x * P.trace_stride + (q1 - 1 - q0)) * kTraceWords + 5] = (uint32_t)now_ticks();
         P.trace[((size_t)blockIdx.x * P.trace_stride + (q1 - 1 - q0)) * kTraceWords + 7] = stall;
     }
@@ -399,14 +412,14 @@ __device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* rin
 // Wait until the loader has `need` chunks resident; adds the ticks spent waiting
 // to `waited` (read only by the trace).
 __device__ __forceinline__ bool wait_landed(const Params& P, Ctl* ctl, uint32_t need, uint32_t& waited) {
-    if (lds_ld(&ctl->landed) >= need) {
+    if (landed_prefix(ctl) >= need) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         return true;
     }
     const uint64_t t0 = now_ticks();
     uint32_t polls = 0;
     bool ok = true;
-    while (lds_ld(&ctl->landed) < need) {
+    while (landed_prefix(ctl) < need) {
         if (lds_ld(&ctl->abort)) {
             ok = false;
             break;
@@ -508,6 +521,7 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
         }
         // every wave has finished reading the previous instruction's staged inputs
         if (!barrier()) return;
+        if (tr && lane == 0) tr[8] = (uint32_t)now_ticks();
         uint32_t land_wait = 0;
         const int layer = in.layer;
         const DevLayer Lw = ld_const(P.layers + (layer < P.L ? layer : 0));
@@ -647,8 +661,11 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                     return wait_landed(P, ctl, (off + 2048u) / kChunk, land_wait);
                 };
                 if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
-                ok = attn_item<HD>(P, A.tag0, layer, b, g, s, ctx[b], kv, need, barrier, xs, wave, kComputeWaves,
-                                   spin);
+                auto mark = [&](int m) {
+                    if (tr && lane == 0) tr[9 + m] = (uint32_t)now_ticks();
+                };
+                ok = attn_item<HD>(P, A.tag0, layer, b, g, s, ctx_of(ctx, b), kv, need, barrier, xs, wave, kComputeWaves,
+                                   spin, mark);
                 break;
             }
             default: break;
@@ -672,7 +689,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
     float* xs = (float*)(lds + (size_t)P.ring_chunks * kChunk);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (threadIdx.x == 0) {
-        ctl.landed = 0;
+        for (int k = 0; k < kLoaderWaves; ++k) ctl.landed[k] = (uint32_t)k;
         for (int w = 0; w < kComputeWaves; ++w) ctl.consumed[w] = 0;
         ctl.bar = 0;
         ctl.abort = 0;
@@ -680,8 +697,8 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
     if (threadIdx.x < kMaxBatch) ctl.ctx[threadIdx.x] = (int)threadIdx.x < B ? P.state->ctx_len[threadIdx.x] : 0;
     __syncthreads();
     const uint32_t q0 = ld_const(P.queue_off + blockIdx.x), q1 = ld_const(P.queue_off + blockIdx.x + 1);
-    if (wave == kComputeWaves) {
-        loader_wave<HD>(P, &ctl, ring, q0, q1, ctl.ctx);
+    if (wave >= kComputeWaves) {
+        loader_wave<HD>(P, &ctl, ring, wave - kComputeWaves, q0, q1, ctl.ctx);
     } else {
         compute_wave<B, HD>(P, A, &ctl, ring, xs, wave, q0, q1, ctl.ctx);
     }

@@ -413,9 +413,9 @@ __host__ __device__ constexpr uint32_t attn_lds_floats(int G, int nsplit) {
 // (ring: wait for the loader), `barrier()` synchronises the waves of the item.
 // Writes the attention output (tagged) or, when split, the item's partial; the
 // last split to arrive merges all partials in split order.  False on abort.
-template <int HD, class KV, class Need, class Barrier>
+template <int HD, class KV, class Need, class Barrier, class Mark>
 __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int layer, int b, int g, int s, int p, const KV& kv,
-                          Need& need, Barrier& barrier, float* xs, int wave, int nw, Spin& spin) {
+                          Need& need, Barrier& barrier, float* xs, int wave, int nw, Spin& spin, Mark& mark) {
     using Geo = AttnGeom<HD>;
     const int lane = lane_id();
     const int ps = lane / Geo::LPP;
@@ -446,6 +446,7 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
         if (!ok) return false;
     }
     if (!barrier()) return false;
+    mark(0);
 
     float q[kMaxGroup][8];
 #pragma unroll
@@ -499,6 +500,7 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
         }
         consume(kp, vp, ps == 0);
     }
+    mark(1);
     // merge the position groups of the wave (lanes with equal dims)
 #pragma unroll
     for (int j = 0; j < kMaxGroup; ++j) {
@@ -563,6 +565,7 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
                 }
             }
         }
+        mark(2);
         return true;
     }
     // split: publish the partial; the last split to arrive merges all of them
@@ -623,6 +626,7 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
         }
         if (lane == 0) __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    mark(2);
     return true;
 }
 

@@ -17,12 +17,13 @@
 namespace mk {
 
 constexpr int kComputeWaves = 4;                    // waves that run instructions
-constexpr int kThreads = 64 * (kComputeWaves + 1);  // + one loader wave
+constexpr int kLoaderWaves = 4;                     // waves that stream weights HBM -> LDS
+constexpr int kThreads = 64 * (kComputeWaves + kLoaderWaves);
 constexpr uint32_t kChunk = 1024;                   // one loader issue: 64 lanes x 16 B
 constexpr uint32_t kLdsBytes = 160 * 1024;          // LDS of one gfx950 compute unit
 constexpr uint32_t kStaticLds = 1024;               // reserved for the control block
 constexpr uint32_t kMinRingChunks = 64;
-constexpr int kLoaderLag = 40;                      // loader chunks in flight (vmcnt <= 63)
+constexpr int kLoaderLag = 8;                       // chunks in flight per loader wave (vmcnt <= 63)
 constexpr int kMaxBatch = 8;
 constexpr int kMaxGroup = 4;                        // q heads per KV head
 constexpr uint32_t kMaxResidRows = 64;              // O / DOWN rows per instruction
@@ -117,8 +118,10 @@ struct Params {
 
 // Trace record of one instruction on one CU (s_memrealtime ticks, low 32 bits):
 // {op | layer << 16, start, inputs staged, compute end, end, loader issue end,
-//  ticks waiting for landed chunks, ticks the loader waited for ring space}
-constexpr int kTraceWords = 8;
+//  ticks waiting for landed chunks, ticks the loaders waited for ring space,
+//  staging start (after the wave barrier), then op-specific marks: attention
+//  inputs staged, its KV groups consumed, its merged output written; 0 = unused}
+constexpr int kTraceWords = 12;
 
 // Per-launch arguments.
 struct StepArgs {

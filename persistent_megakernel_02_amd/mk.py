@@ -16,6 +16,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmk.so")
+TRACE_WORDS = 12  # uint32 per trace record (include/mk.h, mk_read_trace)
 
 MK_OK, MK_E_INVALID, MK_E_UNSUPPORTED, MK_E_CAPACITY, MK_E_HIP, MK_E_DEVICE_TIMEOUT, MK_E_STATE, MK_E_DEVICE_NAN = range(8)
 MK_MODE_MEGAKERNEL, MK_MODE_GRAPH = 0, 1
@@ -86,7 +87,7 @@ def lib():
         L.mk_bench_copy.argtypes = [vp, vp, sz, vp]
         L.mk_bench_sync.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
         L.mk_read_trace.argtypes = [vp, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(i32)]
-        L.mk_bench_lds_stream.argtypes = [ctypes.c_int, ctypes.c_int, vp, sz, ctypes.c_int, vp, vp]
+        L.mk_bench_lds_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, sz, ctypes.c_int, vp, vp]
         for n in ("mk_query_sizes", "mk_create", "mk_kv_layout", "mk_prefill", "mk_set_context_len",
                   "mk_get_context_len", "mk_decode_step", "mk_reset", "mk_debug_inject", "mk_plan_inspect",
                   "mk_destroy", "mk_bench_stream_read", "mk_bench_copy", "mk_bench_sync", "mk_read_trace", "mk_bench_lds_stream"):
@@ -250,7 +251,7 @@ class Decoder:
         buf = np.zeros(n.value // 4, np.uint32)
         self._check(lib().mk_read_trace(self.h, buf.ctypes.data, n.value, ctypes.byref(n), ctypes.byref(per)),
                     "mk_read_trace")
-        return buf.reshape(-1, per.value, 8)
+        return buf.reshape(-1, per.value, TRACE_WORDS)
 
     def kernels_per_step(self) -> int:
         return int(lib().mk_kernels_per_step(self.h))
