@@ -222,12 +222,14 @@ __global__ void __launch_bounds__(kConvThreads) k_attn(Params P, StepArgs A, int
     const int p = P.state->ctx_len[b];
     const SplitRange R = split_range<HD>(p, s, P.nsplit);
     const size_t base = (((size_t)layer * P.kv_b + b) * P.Hkv + g) * (size_t)P.S * HD;
-    const GlobalKV<HD> kv{P.kcache + base, P.vcache + base, R.s0, max(0, R.s0 + R.ncached - 1)};
+    const GlobalKV<HD> kv{P.kcache + base, P.vcache + base, R.s0, max(0, R.s0 + R.ncached - 1),
+                          P.rope + (size_t)p * (HD / 2)};
     auto need = [](int) { return true; };
+    auto release = [](int) {};
     BlockBarrier barrier;
     Spin spin(&P, nullptr);
     auto mark = [](int) {};
-    attn_item<HD>(P, A.tag0, layer, b, g, s, p, kv, need, barrier, xs, wave, kConvWaves, spin, mark);
+    attn_item<HD>(P, A.tag0, layer, b, g, s, p, kv, need, release, barrier, xs, wave, kConvWaves, spin, mark);
 }
 
 // ------------------------------------------------------------------------------------------------

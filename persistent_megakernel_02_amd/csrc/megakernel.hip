@@ -75,7 +75,7 @@ __device__ __forceinline__ uint32_t instr_bytes(const Params& P, const Instr& in
             const int per_b = P.Hkv * P.nsplit;
             const int b = (int)in.begin / per_b, s = (int)in.begin % P.nsplit;
             const SplitRange R = split_range<HD>(ctx_of(ctx, b), s, P.nsplit);
-            return (uint32_t)R.ngroups * 2u * kChunk;
+            return (1u + (uint32_t)R.ngroups * 2u) * kChunk;  // RoPE row of position p, then the K/V groups
         }
         default: return 0;
     }
@@ -128,8 +128,14 @@ __device__ __forceinline__ const char* chunk_src(const Params& P, const Instr& i
             constexpr uint32_t rbkv = HD * 2u;
             const int per_b = P.Hkv * P.nsplit;
             const int b = (int)in.begin / per_b, g = ((int)in.begin % per_b) / P.nsplit, s = (int)in.begin % P.nsplit;
-            const SplitRange R = split_range<HD>(ctx[b], s, P.nsplit);
-            const uint32_t t = off >> 11, w = off & 2047u, inner = w & 1023u;
+            const int p = ctx_of(ctx, b);
+            if (c == 0) {  // (cos, sin) row of position p: HD / 2 float2, lanes past it re-read its start
+                const uint32_t lo = (uint32_t)lane_id() * 16u;
+                return (const char*)(P.rope + (size_t)p * (HD / 2)) + (lo < HD * 4u ? lo : 0u);
+            }
+            const SplitRange R = split_range<HD>(p, s, P.nsplit);
+            const uint32_t o = off - kChunk;
+            const uint32_t t = o >> 11, w = o & 2047u, inner = w & 1023u;
             int pos = R.s0 + (int)(t * AttnGeom<HD>::PPW + inner / rbkv);
             uint32_t col = inner % rbkv;
             if (pos >= R.s0 + R.ncached) { pos = R.s0; col = 0; }
@@ -195,6 +201,7 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 // a few scalar operations, so a loader can take every kLoaderWaves-th chunk.
 struct Stream {
     const char *p0, *p1, *p2;
+    const char* head;     // ATTN: the (cos, sin) row streamed as chunk 0 ahead of the groups
     uint32_t end0, end1;  // ranges: chunk ends of the first two ranges
     uint32_t per_shift;   // interleaved: log2(chunks of each matrix per turn)
     int ncached;          // ATTN: valid positions of the split
@@ -208,7 +215,7 @@ __device__ __forceinline__ bool setup_stream(const Params& P, const Instr& in, c
     S.attn = false;
     S.ncached = 0;
     S.per_shift = 0;
-    S.p1 = S.p2 = nullptr;
+    S.p1 = S.p2 = S.head = nullptr;
     S.end0 = S.end1 = 0xFFFFFFFFu;
     uint32_t rb = 0;
     switch (in.op) {
@@ -244,10 +251,12 @@ __device__ __forceinline__ bool setup_stream(const Params& P, const Instr& in, c
         case OP_ATTN: {
             const int per_b = P.Hkv * P.nsplit;
             const int b = (int)in.begin / per_b, g = ((int)in.begin % per_b) / P.nsplit, s = (int)in.begin % P.nsplit;
-            const SplitRange Rg = split_range<HD>(ctx_of(ctx, b), s, P.nsplit);
+            const int p = ctx_of(ctx, b);
+            const SplitRange Rg = split_range<HD>(p, s, P.nsplit);
             const size_t base = ((((size_t)in.layer * P.kv_b + b) * P.Hkv + g) * P.S + Rg.s0) * HD;
             S.p0 = (const char*)(P.kcache + base);
             S.p1 = (const char*)(P.vcache + base);
+            S.head = (const char*)(P.rope + (size_t)p * (HD / 2));
             S.ncached = Rg.ncached;
             S.inter = true;
             S.attn = true;
@@ -274,6 +283,13 @@ __device__ __forceinline__ const char* stream_chunk(const Stream& S, uint32_t c,
         }
         voff = (c - S.end1) * kChunk + lane16;
         return S.p2;
+    }
+    if (S.attn) {
+        if (c == 0) {  // the (cos, sin) row: HD * 4 bytes, lanes past it re-read its start
+            voff = lane16 < (uint32_t)HD * 4u ? lane16 : 0u;
+            return S.head;
+        }
+        c -= 1u;
     }
     const uint32_t pair = c >> (S.per_shift + 1u);
     const uint32_t within = c & ((2u << S.per_shift) - 1u);
@@ -654,18 +670,20 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                 const int per_b = P.Hkv * P.nsplit;
                 const int b = (int)in.begin / per_b, g = ((int)in.begin % per_b) / P.nsplit,
                           s = (int)in.begin % P.nsplit;
-                const RingKV kv{ring, ring_addr(S, P.ring_chunks), P.ring_chunks * kChunk};
-                auto need = [&](int t) -> bool {
-                    const uint32_t off = S + (uint32_t)t * 2048u;
-                    set_consumed(ctl, wave, off / kChunk);
-                    return wait_landed(P, ctl, (off + 2048u) / kChunk, land_wait);
+                // stream: [RoPE row 1 KB][group 0: K 1 KB, V 1 KB][group 1] ...
+                const RingKV kv{ring, S + kChunk, P.ring_chunks};
+                auto need = [&](int t) -> bool {  // group t resident (K and V chunks); t = -1: the RoPE row
+                    return wait_landed(P, ctl, (S + kChunk + (uint32_t)(t + 1) * 2048u) / kChunk, land_wait);
+                };
+                auto release = [&](int t) {  // groups before t no longer needed by this wave
+                    set_consumed(ctl, wave, (S + kChunk + (uint32_t)t * 2048u) / kChunk);
                 };
                 if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
                 auto mark = [&](int m) {
                     if (tr && lane == 0) tr[9 + m] = (uint32_t)now_ticks();
                 };
-                ok = attn_item<HD>(P, A.tag0, layer, b, g, s, ctx_of(ctx, b), kv, need, barrier, xs, wave, kComputeWaves,
-                                   spin, mark);
+                ok = attn_item<HD>(P, A.tag0, layer, b, g, s, ctx_of(ctx, b), kv, need, release, barrier, xs, wave,
+                                   kComputeWaves, spin, mark);
                 break;
             }
             default: break;

@@ -330,16 +330,37 @@ struct AttnGeom {
     static constexpr int PPW = 64 / LPP;  // positions per 1 KB group
 };
 
+// K/V groups of an attention item in the LDS ring: block(t0) gives the groups
+// from t0 on (at most kAttnBlockGroups of them, so one wrap at most).
 struct RingKV {
     const char* ring;
-    uint32_t base, ring_bytes;  // ring byte of the item's first group: group t = [K 1 KB][V 1 KB]
-    __device__ __forceinline__ uint4 at(uint32_t off) const {
-        uint32_t a = base + off + lane_id() * 16u;
-        a = a >= ring_bytes ? a - ring_bytes : a;
-        return *(const uint4*)(ring + a);
+    uint32_t S, nchunks;  // stream byte of the item's first group (group t = [K 1 KB][V 1 KB]), ring size
+    struct Block {
+        const char* ring;
+        uint32_t base, ring_bytes;  // ring byte of group t0
+        __device__ __forceinline__ uint4 at(uint32_t off) const {
+            uint32_t a = base + off + lane_id() * 16u;
+            a = a >= ring_bytes ? a - ring_bytes : a;
+            return *(const uint4*)(ring + a);
+        }
+        __device__ __forceinline__ uint4 k(int t) const { return at((uint32_t)t * 2048u); }
+        __device__ __forceinline__ uint4 v(int t) const { return at((uint32_t)t * 2048u + 1024u); }
+    };
+    __device__ __forceinline__ Block block(int t0) const {
+        const uint32_t x = S + (uint32_t)t0 * 2048u;
+        return Block{ring, ((x >> 10) % nchunks) * 1024u + (x & 1023u), nchunks * 1024u};
     }
-    __device__ __forceinline__ uint4 k(int t) const { return at((uint32_t)t * 2048u); }
-    __device__ __forceinline__ uint4 v(int t) const { return at((uint32_t)t * 2048u + 1024u); }
+    // (cos, sin) entries i0 .. i0 + 7 of the position's RoPE row, the chunk before group 0
+    __device__ __forceinline__ void rope(int i0, float2 (&cs)[8]) const {
+        const uint32_t x = S - 1024u;
+        const float4* q = (const float4*)(ring + ((x >> 10) % nchunks) * 1024u + (uint32_t)i0 * 8u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float4 v = q[e];
+            cs[2 * e] = make_float2(v.x, v.y);
+            cs[2 * e + 1] = make_float2(v.z, v.w);
+        }
+    }
 };
 
 template <int HD>
@@ -352,8 +373,18 @@ struct GlobalKV {
         if (j < 0) j = 0;
         return (size_t)j * HD + 8 * (lane_id() % AttnGeom<HD>::LPP);
     }
-    __device__ __forceinline__ uint4 k(int t) const { return *(const uint4*)(kb + off(t)); }
-    __device__ __forceinline__ uint4 v(int t) const { return *(const uint4*)(vb + off(t)); }
+    const float2* rope_row;   // (cos, sin) row of the position
+    __device__ __forceinline__ void rope(int i0, float2 (&cs)[8]) const {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs[e] = rope_row[i0 + e];
+    }
+    struct Block {
+        const GlobalKV* kv;
+        int t0;
+        __device__ __forceinline__ uint4 k(int t) const { return *(const uint4*)(kv->kb + kv->off(t0 + t)); }
+        __device__ __forceinline__ uint4 v(int t) const { return *(const uint4*)(kv->vb + kv->off(t0 + t)); }
+    };
+    __device__ __forceinline__ Block block(int t0) const { return Block{this, t0}; }
 };
 
 // Split geometry of item s for a context of n = p + 1 positions.
@@ -387,53 +418,91 @@ __device__ __forceinline__ void lse_merge(float& m, float& l, float* acc, float 
 }
 
 // RoPE of the 8 dims [dl, dl+8) of one head whose raw fp32 values start at `raw`
-// (LDS); rotate-half pairs (i, i + HD/2) turn by the angle of table row `rope_row`.
+// (LDS): rotate-half pairs (i, i + HD/2) turn by the angles whose (cos, sin) the
+// lane holds in cs (entries dl mod HD/2 .. + 7 of the position's table row).
 template <int HD>
-__device__ __forceinline__ void rope8(const float* raw, const float2* __restrict__ rope_row, int dl, float* out) {
+__device__ __forceinline__ void rope8(const float* raw, const float2 (&cs)[8], int dl, float* out) {
     constexpr int half = HD / 2;
     const bool lo = dl < half;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int i = dl + e, ii = lo ? i : i - half;
         const float a = raw[ii], b = raw[ii + half];
-        const float2 cs = rope_row[ii];
-        out[e] = lo ? fmaf(a, cs.x, -(b * cs.y)) : fmaf(a, cs.y, b * cs.x);
+        out[e] = lo ? fmaf(a, cs[e].x, -(b * cs[e].y)) : fmaf(a, cs[e].y, b * cs[e].x);
     }
 }
 
-// LDS floats one attention item needs: staged q/k/v, per-wave partials, and the
+// Sum over the groups of `LPP` consecutive lanes (8 or 16) with DPP: quad
+// butterflies, then the half-row mirror (and the row mirror for 16); partners
+// add the same two values, so every lane of a group ends with identical bits.
+template <int LPP>
+__device__ __forceinline__ float group_sum_dpp(float v) {
+    static_assert(LPP == 8 || LPP == 16, "8 or 16 lanes per position");
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    if (LPP == 16) v += __builtin_amdgcn_update_dpp(0.0f, v, 0x140, 0xF, 0xF, false);  // row_mirror
+    return v;
+}
+
+// Maximum over the 64 lanes (DPP tree as wave_total), returned to every lane.
+__device__ __forceinline__ float wave_maxf(float v) {
+    v = fmaxf(v, __builtin_amdgcn_update_dpp(-INFINITY, v, 0xB1, 0xF, 0xF, false));
+    v = fmaxf(v, __builtin_amdgcn_update_dpp(-INFINITY, v, 0x4E, 0xF, 0xF, false));
+    v = fmaxf(v, __builtin_amdgcn_update_dpp(-INFINITY, v, 0x141, 0xF, 0xF, false));
+    v = fmaxf(v, __builtin_amdgcn_update_dpp(-INFINITY, v, 0x140, 0xF, 0xF, false));
+    v = fmaxf(v, __builtin_amdgcn_update_dpp(-INFINITY, v, 0x142, 0xA, 0xF, false));
+    v = fmaxf(v, __builtin_amdgcn_update_dpp(-INFINITY, v, 0x143, 0xC, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// LDS floats one attention item needs: staged q/k/v, per-head scores of one
+// block of position groups (plus the group of the new position), and the
 // partials of every split when this item merges them.
 template <int HD>
 __host__ __device__ constexpr uint32_t attn_lds_floats(int G, int nsplit) {
-    return (uint32_t)((G + 2) * HD + kComputeWaves * kMaxGroup * (HD + 2) + nsplit * G * (HD + 2) + 4);
+    return (uint32_t)((G + 2) * HD + kComputeWaves * (kAttnBlockGroups + 1) * (64 / (HD / 8)) +
+                      nsplit * G * (HD + 2) + 4);
 }
 
-// Runs one attention item with the calling wave (`wave` of `nw` waves of the
-// workgroup, which all call it).  `need(t)` is called before group t is read
-// (ring: wait for the loader), `barrier()` synchronises the waves of the item.
-// Writes the attention output (tagged) or, when split, the item's partial; the
-// last split to arrive merges all partials in split order.  False on abort.
-template <int HD, class KV, class Need, class Barrier, class Mark>
-__device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int layer, int b, int g, int s, int p, const KV& kv,
-                          Need& need, Barrier& barrier, float* xs, int wave, int nw, Spin& spin, Mark& mark) {
+// Runs one attention item (sequence b, KV head g, split s) with `nw` waves of the
+// workgroup, which all call it.  Wave j handles q head j of the group end to end:
+// it scores every position of the split block by block (block = kAttnBlockGroups
+// groups of PPW positions; lanes = (position slot, 8 dims), the per-position dot
+// summed over the slot's lanes with DPP), exponentiates against the running
+// maximum (two-pass softmax inside a block, rescaled across blocks), and
+// accumulates the probability-weighted V per (slot, dims), summed over the slots
+// at the end.  `need(t)` waits for ring group t; `release(t)` frees ring groups
+// before t; `barrier()` synchronises the waves.  The new position (its K rotated
+// and rounded to bf16, appended to the cache) joins as one extra group.  Writes
+// the attention output (tagged) or, when split, the item's (max, sum, output)
+// partial; the last split to arrive merges all partials in split order.
+template <int HD, class KV, class Need, class Release, class Barrier, class Mark>
+__device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int layer, int b, int g, int s, int p,
+                                          const KV& kv, Need& need, Release& release, Barrier& barrier, float* xs,
+                                          int wave, int nw, Spin& spin, Mark& mark) {
     using Geo = AttnGeom<HD>;
+    constexpr int LPP = Geo::LPP, PPW = Geo::PPW;
     const int lane = lane_id();
-    const int ps = lane / Geo::LPP;
-    const int dl = 8 * (lane % Geo::LPP);
+    const int ps = lane / LPP;
+    const int dl = 8 * (lane % LPP);
     const int G = P.G;
     const SplitRange R = split_range<HD>(p, s, P.nsplit);
     const float scale = P.attn_scale;
-    const float2* rope_row = P.rope + (size_t)p * (HD / 2);
     const uint32_t tag_in = phase_tag(tag0, layer, 0) ^ ((P.inject && layer == 0) ? 0x80000000u : 0u);
     const uint32_t tag_out = phase_tag(tag0, layer, 1);
     const uint32_t stride = HD + 2;
+    constexpr int kSlots = (kAttnBlockGroups + 1) * PPW;
 
-    // stage this group's raw q (G heads), k and v rows of the QKV output
+    // the (cos, sin) row of position p (for the ring: the item's first chunk)
+    if (!need(-1)) return false;
+    float2 cs[8];
+    kv.rope(dl < HD / 2 ? dl : dl - HD / 2, cs);
     float* q_raw = xs;
     float* k_raw = xs + G * HD;
     float* v_raw = k_raw + HD;
-    float* wpart = v_raw + HD;                          // [nw][kMaxGroup][HD + 2]
-    float* spart = wpart + kComputeWaves * kMaxGroup * stride;  // [nsplit][G][HD + 2]
+    float* sc = v_raw + HD + wave * kSlots;                // this wave's scores / weights
+    float* spart = v_raw + HD + kComputeWaves * kSlots;    // [nsplit][G][HD + 2]
     uint32_t* flag = (uint32_t*)(spart + P.nsplit * G * stride);
     {
         const uint64_t* row = P.qkv + (size_t)b * P.qkv_rows;
@@ -448,122 +517,111 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
     if (!barrier()) return false;
     mark(0);
 
-    float q[kMaxGroup][8];
-#pragma unroll
-    for (int j = 0; j < kMaxGroup; ++j)
-        if (j < G) rope8<HD>(q_raw + j * HD, rope_row, dl, q[j]);
-    float m[kMaxGroup], l[kMaxGroup], acc[kMaxGroup][8];
-#pragma unroll
-    for (int j = 0; j < kMaxGroup; ++j) {
-        m[j] = -INFINITY;
-        l[j] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+    // Rotations on every path (waves without a q head rotate a neighbour's values,
+    // unused): the (cos, sin) loads are consumed here, before any store, so no
+    // load stays pending past this instruction.
+    const int j = wave;  // q head of this wave
+    float q[8];
+    rope8<HD>(q_raw + j * HD, cs, dl, q);
+    // the new position: K rotated, K and V rounded to bf16 as the cache holds them
+    float kr[8];
+    rope8<HD>(k_raw, cs, dl, kr);
+    const uint4 kn = make_uint4(pack_bf2(kr[0], kr[1]), pack_bf2(kr[2], kr[3]), pack_bf2(kr[4], kr[5]),
+                                pack_bf2(kr[6], kr[7]));
+    const uint4 vn = make_uint4(pack_bf2(v_raw[dl], v_raw[dl + 1]), pack_bf2(v_raw[dl + 2], v_raw[dl + 3]),
+                                pack_bf2(v_raw[dl + 4], v_raw[dl + 5]), pack_bf2(v_raw[dl + 6], v_raw[dl + 7]));
+    if (R.has_new && wave == 0 && ps == 0) {  // KV append at position p (read by later steps)
+        const size_t row = ((((size_t)layer * P.kv_b + b) * P.Hkv + g) * P.S + p) * HD + dl;
+        *(uint4*)(P.kcache + row) = kn;
+        *(uint4*)(P.vcache + row) = vn;
     }
-    auto consume = [&](uint4 kp, uint4 vp, bool valid) {
-        const float vv[8] = {bf_lo(vp.x), bf_hi(vp.x), bf_lo(vp.y), bf_hi(vp.y),
-                             bf_lo(vp.z), bf_hi(vp.z), bf_lo(vp.w), bf_hi(vp.w)};
+    const int ngr = R.ngroups + (R.has_new ? 1 : 0);  // ring groups, then the new position's group
+    float m_run = -INFINITY, l_run = 0.f, acc[8];
 #pragma unroll
-        for (int j = 0; j < kMaxGroup; ++j) {
-            if (j < G) {
-                float sc = qk8(q[j], kp);
-                sc = group_sum(sc, Geo::LPP) * scale;
-                if (valid) {
-                    const float mn = fmaxf(m[j], sc);
-                    const float c = (m[j] == -INFINITY) ? 0.f : expf(m[j] - mn);
-                    const float e = expf(sc - mn);
-                    l[j] = l[j] * c + e;
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    if (j < G) {
+        for (int t0 = 0; t0 < ngr; t0 += kAttnBlockGroups) {
+            const int t1 = min(ngr, t0 + kAttnBlockGroups);
+            const auto blk = kv.block(t0);
+            // every ring group of the block resident (one wait per block)
+            if (t0 < R.ngroups && !need(min(t1, R.ngroups) - 1)) return false;
+            // scores of the block, four groups per step so their LDS reads overlap
+            float mx = -INFINITY;
+            for (int t = t0; t < t1; t += 4) {
+                uint4 kp[4];
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) acc[j][k] = fmaf(e, vv[k], acc[j][k] * c);
-                    m[j] = mn;
+                for (int u = 0; u < 4; ++u) {
+                    const int tt = t + u;
+                    kp[u] = (tt < R.ngroups && tt < t1) ? blk.k(tt - t0) : kn;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int tt = t + u;
+                    if (tt < t1) {
+                        float v = group_sum_dpp<LPP>(qk8(q, kp[u])) * scale;
+                        const bool valid = tt == R.ngroups ? ps == 0 : tt * PPW + ps < R.ncached;
+                        v = valid ? v : -INFINITY;
+                        if (dl == 0) sc[(tt - t0) * PPW + ps] = v;
+                        mx = fmaxf(mx, v);
+                    }
                 }
             }
+            mx = wave_maxf(mx);
+            const float m_new = fmaxf(m_run, mx);
+            // weights against the running maximum, and their sum
+            float l_blk = 0.f;
+            for (int i = lane; i < (t1 - t0) * PPW; i += 64) {
+                const float v = sc[i];
+                const float e = v == -INFINITY ? 0.f : expf(v - m_new);
+                sc[i] = e;
+                l_blk += e;
+            }
+            l_blk = wave_total(l_blk);
+            // rescale what earlier blocks accumulated, then add this block's weighted V
+            const float c = m_run == -INFINITY ? 0.f : expf(m_run - m_new);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] *= c;
+            l_run = l_run * c + l_blk;
+            m_run = m_new;
+            for (int t = t0; t < t1; t += 4) {
+                uint4 vp[4];
+                float w[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int tt = t + u;
+                    vp[u] = (tt < R.ngroups && tt < t1) ? blk.v(tt - t0) : vn;
+                    w[u] = tt < t1 ? sc[(tt - t0) * PPW + ps] : 0.f;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    acc[0] = fmaf(w[u], bf_lo(vp[u].x), acc[0]);
+                    acc[1] = fmaf(w[u], bf_hi(vp[u].x), acc[1]);
+                    acc[2] = fmaf(w[u], bf_lo(vp[u].y), acc[2]);
+                    acc[3] = fmaf(w[u], bf_hi(vp[u].y), acc[3]);
+                    acc[4] = fmaf(w[u], bf_lo(vp[u].z), acc[4]);
+                    acc[5] = fmaf(w[u], bf_hi(vp[u].z), acc[5]);
+                    acc[6] = fmaf(w[u], bf_lo(vp[u].w), acc[6]);
+                    acc[7] = fmaf(w[u], bf_hi(vp[u].w), acc[7]);
+                }
+            }
+            release(min(t1, R.ngroups));
         }
-    };
-    for (int t = wave; t < R.ngroups; t += nw) {
-        if (!need(t)) return false;
-        const uint4 kp = kv.k(t), vp = kv.v(t);
-        consume(kp, vp, R.s0 + t * Geo::PPW + ps < R.s0 + R.ncached);
-    }
-    // the new position: rotated k and bf16 k/v from this step's projections
-    if (R.has_new && wave == 0) {
-        float kr[8];
-        rope8<HD>(k_raw, rope_row, dl, kr);
-        const uint4 kp = make_uint4(pack_bf2(kr[0], kr[1]), pack_bf2(kr[2], kr[3]), pack_bf2(kr[4], kr[5]),
-                                    pack_bf2(kr[6], kr[7]));
-        const uint4 vp = make_uint4(pack_bf2(v_raw[dl], v_raw[dl + 1]), pack_bf2(v_raw[dl + 2], v_raw[dl + 3]),
-                                    pack_bf2(v_raw[dl + 4], v_raw[dl + 5]), pack_bf2(v_raw[dl + 6], v_raw[dl + 7]));
-        if (ps == 0) {  // KV append at position p (read by later steps)
-            const size_t row = ((((size_t)layer * P.kv_b + b) * P.Hkv + g) * P.S + p) * HD + dl;
-            *(uint4*)(P.kcache + row) = kp;
-            *(uint4*)(P.vcache + row) = vp;
-        }
-        consume(kp, vp, ps == 0);
+        // sum the position slots (lanes with equal dims)
+#pragma unroll
+        for (int msk = LPP; msk < 64; msk <<= 1)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], msk, 64);
+    } else {
+        release(R.ngroups);
     }
     mark(1);
-    // merge the position groups of the wave (lanes with equal dims)
-#pragma unroll
-    for (int j = 0; j < kMaxGroup; ++j) {
-        if (j < G) {
-            for (int msk = Geo::LPP; msk < 64; msk <<= 1) {
-                float acc2[8];
-                const float m2 = __shfl_xor(m[j], msk, 64), l2 = __shfl_xor(l[j], msk, 64);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc2[e] = __shfl_xor(acc[j][e], msk, 64);
-                lse_merge(m[j], l[j], acc[j], m2, l2, acc2);
-            }
-        }
-    }
-    // merge the waves in order through LDS
-    if (ps == 0) {
-#pragma unroll
-        for (int j = 0; j < kMaxGroup; ++j) {
-            if (j < G) {
-                float* dst = wpart + ((size_t)wave * kMaxGroup + j) * stride;
-                if (dl == 0) {
-                    dst[0] = m[j];
-                    dst[1] = l[j];
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dst[2 + dl + e] = acc[j][e];
-            }
-        }
-    }
-    if (!barrier()) return false;
-    if (wave == 0 && ps == 0) {
-#pragma unroll
-        for (int j = 0; j < kMaxGroup; ++j) {
-            if (j < G) {
-                const float* src = wpart + (size_t)j * stride;
-                float mm = src[0], ll = src[1], aa[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) aa[e] = src[2 + dl + e];
-                for (int w = 1; w < nw; ++w) {
-                    const float* sw = wpart + ((size_t)w * kMaxGroup + j) * stride;
-                    float a2[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) a2[e] = sw[2 + dl + e];
-                    lse_merge(mm, ll, aa, sw[0], sw[1], a2);
-                }
-                m[j] = mm;
-                l[j] = ll;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[j][e] = aa[e];
-            }
-        }
-    }
     uint64_t* out_b = P.attn + (size_t)b * P.Hq * HD;
     if (P.nsplit == 1) {
-        if (wave == 0 && ps == 0) {
+        if (j < G && ps == 0) {
+            const float inv = 1.0f / l_run;
+            uint64_t* o = out_b + (size_t)(g * G + j) * HD + dl;
 #pragma unroll
-            for (int j = 0; j < kMaxGroup; ++j) {
-                if (j < G) {
-                    const float inv = 1.0f / l[j];
-                    uint64_t* o = out_b + (size_t)(g * G + j) * HD + dl;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) st_tagged(o + e, acc[j][e] * inv, tag_out);
-                }
-            }
+            for (int e = 0; e < 8; ++e) st_tagged(o + e, acc[e] * inv, tag_out);
         }
         mark(2);
         return true;
@@ -572,60 +630,52 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
     const size_t pstride = (size_t)G * stride;
     uint64_t* part = P.attn_part + (((size_t)b * P.Hkv + g) * P.nsplit) * pstride;
     uint32_t* tk = P.attn_ticket + (((size_t)layer * P.B + b) * P.Hkv + g) * kCtrStride;
-    if (wave == 0) {
-        if (ps == 0) {
-#pragma unroll
-            for (int j = 0; j < kMaxGroup; ++j) {
-                if (j < G) {
-                    uint64_t* dst = part + (size_t)s * pstride + (size_t)j * stride;
-                    if (dl == 0) {
-                        st_tagged(dst, m[j], tag_out);
-                        st_tagged(dst + 1, l[j], tag_out);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) st_tagged(dst + 2 + dl + e, acc[j][e], tag_out);
-                }
-            }
+    if (j < G && ps == 0) {
+        uint64_t* dst = part + (size_t)s * pstride + (size_t)j * stride;
+        if (dl == 0) {
+            st_tagged(dst, m_run, tag_out);
+            st_tagged(dst + 1, l_run, tag_out);
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st_tagged(dst + 2 + dl + e, acc[e], tag_out);
+    }
+    if (!barrier()) return false;  // every head's partial is issued
+    if (wave == 0) {
         uint32_t old = 0;
         if (lane == 0) old = __hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         old = __shfl(old, 0, 64);
         if (lane == 0) *flag = (old == (uint32_t)P.nsplit - 1u) ? 1u : 0u;
     }
     if (!barrier()) return false;
-    if (*flag == 0u) return true;
-    // last arrival: every wave stages the partials, wave 0 merges them in split order
+    if (*flag == 0u) {
+        mark(2);
+        return true;
+    }
+    // last arrival: every wave stages the partials, wave j merges head j in split order
     {
         float ss = 0.f;
         if (!stage_tagged<false>(part, (uint32_t)(P.nsplit * pstride), tag_out, spart, nullptr, wave, nw, spin, ss))
             return false;
     }
     if (!barrier()) return false;
-    if (wave == 0) {
-        if (ps == 0) {
+    if (j < G && ps == 0) {
+        const float* s0p = spart + (size_t)j * stride;
+        float mm = s0p[0], ll = s0p[1], aa[8];
 #pragma unroll
-            for (int j = 0; j < kMaxGroup; ++j) {
-                if (j < G) {
-                    const float* s0p = spart + (size_t)j * stride;
-                    float mm = s0p[0], ll = s0p[1], aa[8];
+        for (int e = 0; e < 8; ++e) aa[e] = s0p[2 + dl + e];
+        for (int sp = 1; sp < P.nsplit; ++sp) {
+            const float* src = spart + (size_t)sp * pstride + (size_t)j * stride;
+            float a2[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) aa[e] = s0p[2 + dl + e];
-                    for (int sp = 1; sp < P.nsplit; ++sp) {
-                        const float* src = spart + (size_t)sp * pstride + (size_t)j * stride;
-                        float a2[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) a2[e] = src[2 + dl + e];
-                        lse_merge(mm, ll, aa, src[0], src[1], a2);
-                    }
-                    const float inv = 1.0f / ll;
-                    uint64_t* o = out_b + (size_t)(g * G + j) * HD + dl;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) st_tagged(o + e, aa[e] * inv, tag_out);
-                }
-            }
+            for (int e = 0; e < 8; ++e) a2[e] = src[2 + dl + e];
+            lse_merge(mm, ll, aa, src[0], src[1], a2);
         }
-        if (lane == 0) __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float inv = 1.0f / ll;
+        uint64_t* o = out_b + (size_t)(g * G + j) * HD + dl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st_tagged(o + e, aa[e] * inv, tag_out);
     }
+    if (wave == 0 && lane == 0) __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     mark(2);
     return true;
 }

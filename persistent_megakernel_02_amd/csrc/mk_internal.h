@@ -29,6 +29,7 @@ constexpr int kMaxGroup = 4;                        // q heads per KV head
 constexpr uint32_t kMaxResidRows = 64;              // O / DOWN rows per instruction
 constexpr uint32_t kCtrStride = 32;                 // uint32 per counter (128 B apart)
 constexpr int kStageWords = 16;                     // tagged words per lane in flight when staging
+constexpr int kAttnBlockGroups = 32;                // KV position groups (2 KB each) one attention pass holds
 
 enum Op : uint16_t {
     OP_QKV = 1,     // RMSNorm + rows of [Wq; Wk; Wv] -> raw q/k/v (fp32)
