@@ -23,6 +23,73 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 
+# Kernel sources whose hash keys the committed counter summary: the summary's
+# traffic figure is reported only while these files are unchanged.
+KERNEL_SOURCES = ["persistent_megakernel_02_amd/csrc/megakernel.hip",
+                  "persistent_megakernel_02_amd/csrc/mk_device.h",
+                  "persistent_megakernel_02_amd/csrc/mk_internal.h",
+                  "persistent_megakernel_02_amd/csrc/host.hip"]
+COUNTER_SUMMARY = "profiles/mk_megakernel_llama1b_b1_hbm_counters.md"
+
+
+def kernel_sources_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per megakernel launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by the factor the same
+    counter reads for a copy kernel of known size), or None when the summary is
+    missing or was taken from different kernel sources."""
+    path = os.path.join(ROOT, COUNTER_SUMMARY)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_sources_sha256") != kernel_sources_hash():
+        return None, "kernel changed since the counters were taken"
+    return int(fields["traffic_bytes_per_launch"]), COUNTER_SUMMARY
+
+
+def profile_run(args) -> int:
+    """Workload for the counter runs: a few megakernel decode steps on the 1B
+    shape at batch 1, then a 256 MiB device copy whose counter readings give the
+    scale factors of FETCH_SIZE and WRITE_SIZE."""
+    import torch
+
+    import persistent_megakernel_02_amd.inputs as I
+    import persistent_megakernel_02_amd.mk as mk
+
+    cfg = I.LLAMA_1B
+    dev = torch.device("cuda:0")
+    w = I.make_weights(cfg, seed=args.seed)
+    prompt = torch.from_numpy(I.make_prompt(cfg, 1, args.prompt, seed=args.seed)).to(dev)
+    dec = mk.Decoder(cfg, w, max_batch=1, max_seq=args.prompt + args.horizon + 1, device="cuda:0")
+    tok, logits = dec.prefill(prompt)
+    for _ in range(args.steps):
+        dec.decode_step(tok, tok, logits)
+    torch.cuda.synchronize()
+    dec.close()
+    nb = 256 << 20
+    a = torch.empty(nb, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        mk.bench_copy(b, a)
+    torch.cuda.synchronize()
+    log(f"profile run: prefill {args.prompt} + {args.steps} decode steps, 2 copies of {nb} B")
+    return 0
+
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
@@ -51,6 +118,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-steps", type=int, default=24)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--profile-run", action="store_true",
+                    help="untimed workload for rocprofv3 counter runs (no JSON line)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -58,6 +127,9 @@ def main() -> int:
         print(json.dumps({"error": "this decode path runs on one GPU; --gpus must be 1 "
                                    "(multi-GPU sharding is a design note, not built)"}))
         return 2
+
+    if args.profile_run:
+        return profile_run(args)
 
     import numpy as np
     import torch
@@ -115,20 +187,37 @@ def main() -> int:
             per_h.append(ms * 1000.0 / n)
             positions.extend(range(P, P + n))
             left -= n
+        # separate pass with an event after every step, for the percentiles
+        per_step = []
+        left = args.steps
+        while left > 0:
+            n = min(left, H)
+            start_horizon()
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+            ev[0].record(st)
+            for i in range(n):
+                dec.decode_step(tok, tok, logits)
+                ev[i + 1].record(st)
+            ev[-1].synchronize()
+            per_step.extend(ev[i].elapsed_time(ev[i + 1]) * 1000.0 for i in range(n))
+            left -= n
         kps = dec.kernels_per_step()
         dec.close()
         us = total_ms * 1000.0 / args.steps
-        log(f"{label}: {us:.1f} us/token over {args.steps} steps ({kps} kernels/step)")
-        return us, positions, kps, per_h
+        pct = (float(np.percentile(per_step, 50)), float(np.percentile(per_step, 95)))
+        log(f"{label}: {us:.1f} us/token over {args.steps} steps ({kps} kernels/step), "
+            f"p50 {pct[0]:.1f} p95 {pct[1]:.1f}")
+        return us, positions, kps, per_h, pct
 
-    us_mk, positions, kps_mk, per_h = run_path(mk.MK_MODE_MEGAKERNEL, "megakernel")
+    us_mk, positions, kps_mk, per_h, pct_mk = run_path(mk.MK_MODE_MEGAKERNEL, "megakernel")
     bytes_step = [step_bytes(cfg, B, [p]) for p in positions]
     mean_bytes = float(np.mean(bytes_step))
     gbs = mean_bytes / (us_mk * 1e-6) / 1e9
 
-    us_graph = kps_graph = None
+    us_graph = kps_graph = pct_graph = None
     if not args.no_graph:
-        us_graph, _, kps_graph, _ = run_path(mk.MK_MODE_GRAPH, "hipGraph one-kernel-per-op")
+        us_graph, _, kps_graph, _, pct_graph = run_path(mk.MK_MODE_GRAPH, "hipGraph one-kernel-per-op")
 
     # streaming-read ceiling on a buffer the size of the step
     buf = torch.empty(int(mean_bytes) // 16 * 16, dtype=torch.uint8, device=dev)
@@ -165,6 +254,7 @@ def main() -> int:
                          f"{P}..{P + args.cpu_steps - 1} (fp64-accumulated C oracle, OpenMP over rows)"}
         log(f"cpu oracle: {cpu_us / 1000:.1f} ms/token on {O.threads()} threads")
 
+    traffic, traffic_src = counter_traffic()
     out = {
         "metric": "decode us/token at batch 1 (Llama-3.2-1B shape) + % of peak HBM BW",
         "value": round(us_mk, 2),
@@ -182,18 +272,22 @@ def main() -> int:
                                "random bf16 weights N(0,0.02)", "batch": B, "prompt": P, "horizon": H,
                    "layers": cfg.n_layers, "hidden": cfg.hidden, "vocab": cfg.vocab},
         "tokens_per_s": round(1e6 / us_mk, 1),
+        "us_per_token_p50": round(pct_mk[0], 2),
+        "us_per_token_p95": round(pct_mk[1], 2),
         "pct_peak_hbm": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "pct_stream_ceiling": round(100.0 * gbs / ceil_gbs, 2),
         "stream_read_ceiling_gbs": round(ceil_gbs, 1),
         "kernels_per_step": kps_mk,
         "us_per_token_per_horizon": [round(x, 2) for x in per_h],
         "graph_path": None if us_graph is None else {"us_per_token": round(us_graph, 2),
+                                                     "p50": round(pct_graph[0], 2),
+                                                     "p95": round(pct_graph[1], 2),
                                                      "kernels_per_step": kps_graph,
                                                      "pct_peak_hbm": round(100.0 * mean_bytes / (us_graph * 1e-6)
                                                                            / 1e9 / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": int(mean_bytes)},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": int(mean_bytes), "traffic_source": traffic_src},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
