@@ -295,4 +295,8 @@ def main() -> int:
 
 
 if __name__ == "__main__":
-    sys.exit(main())
+    # Return normally on success: a profiler that writes its results from exit
+    # handlers has lost them when the interpreter left through SystemExit.
+    rc = main()
+    if rc:
+        sys.exit(rc)

@@ -96,7 +96,10 @@ typedef struct {
     int32_t max_batch;        /* 1..8 sequences per step */
     int32_t max_seq;          /* KV capacity per sequence */
     mk_mode mode;
-    int32_t num_cus;          /* 0 = every compute unit of the device */
+    int32_t num_cus;          /* 0 = every compute unit of the device; the persistent
+                                 mode needs num_cus <= the device's compute units (one
+                                 resident workgroup each), else mk_create answers
+                                 MK_E_UNSUPPORTED */
     int32_t gemv_kind;        /* 0 auto, 1 VALU dot (the only kind in this version) */
     uint32_t spin_timeout_ms; /* watchdog of every device spin-wait; 0 = 2000 ms */
     int32_t trace;            /* 1: record a per-instruction timeline (mk_read_trace) */

@@ -31,12 +31,23 @@ int mk_bench_copy(void* d_dst, const void* d_src, size_t bytes, void* stream);
  * wait for all -> read every slot (slots double-buffered by round parity).
  * mode 0: one atomic counter + agent-scope release/acquire fences; mode 1: one
  * counter + agent-scope relaxed atomics for data, vmcnt waits; mode 2: one
- * completion flag per workgroup + fences; mode 3: flags + relaxed atomics.
+ * completion flag per workgroup + fences; mode 3: flags + relaxed atomics;
+ * mode 4: no counter or flag, every slot an 8-byte {value, round} word that
+ * readers re-poll until the round matches (the decode step's protocol).
  * d_ctr: 64 + n_wg zeroed uint32 (counter line, then flags); d_data: 2 * n_wg
- * * 64 uint32; d_out: two zeroed uint64 = {ticks of 100 MHz for all rounds on
+ * * 64 uint32 (modes 0-3) or 2 * n_wg * 64 zeroed uint64 (mode 4); d_out: two zeroed uint64 = {ticks of 100 MHz for all rounds on
  * workgroup 0, data mismatches}.  Each wait is bounded, so the kernel ends even
  * if a workgroup is missing.  Returns 0, 1 on bad arguments, 4 on launch error. */
 int mk_bench_sync(int mode, int n_wg, int rounds, void* d_ctr, void* d_data, void* d_out, void* stream);
+
+/* One-way latency of a value passed between two workgroups: workgroups 0 and
+ * `peer` (1..255) bounce an 8-byte word `rounds` times (flavor 0: agent-scope
+ * relaxed atomics; flavor 1: system scope).  Workgroups are dealt round-robin
+ * over the XCDs, so `peer` selects a same-XCD or a cross-XCD pair.  d_words: 64
+ * zeroed uint64; d_out: four zeroed uint64 = {ticks (100 MHz) of all rounds,
+ * waits that hit their bound, XCC id of workgroup 0, XCC id of the peer}.  Each
+ * wait is bounded.  Returns 0, 1 on bad arguments, 4 on launch error. */
+int mk_bench_pingpong(int flavor, int peer, int rounds, void* d_words, void* d_out, void* stream);
 
 /* HBM -> LDS streaming rate of the direct-to-LDS 16-byte-per-lane load:
  * n_wg workgroups of `waves` waves; each wave streams its share of d_src 1 KB

@@ -69,12 +69,59 @@ int mk_bench_copy(void* d_dst, const void* d_src, size_t bytes, void* stream) {
 //   mode 1: one counter, data and ordering through agent-scope relaxed atomics
 //   mode 2: one completion flag per workgroup (plain store of the round), fences
 //   mode 3: per-workgroup flags, agent-scope relaxed atomics for the data
+//   mode 4: no counter or flag: every slot is an 8-byte {value, round} word
+//           stored with one agent-scope atomic, and readers re-poll the words
+//           whose round does not match yet (the decode step's protocol)
 // out[0] = ticks (100 MHz) of `rounds` rounds on workgroup 0, out[1] = data
 // mismatches seen by any workgroup.
 // ------------------------------------------------------------------------------------------------
 namespace {
+// mode 4: slots are 8-byte words, data holds 2 * n * 64 of them
+__device__ void sync_tagged(uint64_t* data, int rounds, uint64_t* out) {
+    const int n = gridDim.x, wg = blockIdx.x, lane = threadIdx.x;
+    uint32_t errors = 0;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    bool lost = false;
+    for (int r = 1; r <= rounds && !lost; ++r) {
+        uint64_t* buf = data + (size_t)(r & 1) * n * 64;
+        const uint64_t v = ((uint64_t)(uint32_t)r << 32) | ((uint32_t)r * 4096u + (uint32_t)wg);
+        __hip_atomic_store(&buf[wg * 64 + lane], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // every lane reads slot word (k & 63) of workgroups k = lane, lane + 64, ...
+        for (int k0 = 0; k0 < n && !lost; k0 += 64) {
+            const int k = k0 + lane;
+            uint32_t guard = 0;
+            bool ok = k >= n;
+            while (!__all(ok)) {
+                if (!ok) {
+                    const uint64_t w = __hip_atomic_load(&buf[k * 64 + (k & 63)], __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+                    if ((uint32_t)(w >> 32) == (uint32_t)r) {
+                        ok = true;
+                        errors += ((uint32_t)w != (uint32_t)r * 4096u + (uint32_t)k);
+                    }
+                }
+                if (++guard > 4000000u) {  // bounded: a missing workgroup ends the run
+                    lost = true;
+                    errors += 1u << 20;
+                    break;
+                }
+            }
+        }
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    for (int m = 32; m >= 1; m >>= 1) errors += __shfl_xor(errors, m, 64);
+    if (lane == 0) {
+        if (wg == 0) out[0] = t1 - t0;
+        if (errors) atomicAdd((unsigned long long*)&out[1], (unsigned long long)errors);
+    }
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(64) k_sync(uint32_t* ctr, uint32_t* data, int rounds, uint64_t* out) {
+    if constexpr (MODE == 4) {
+        sync_tagged((uint64_t*)data, rounds, out);
+        return;
+    }
     constexpr bool kFence = (MODE == 0 || MODE == 2);
     constexpr bool kFlags = (MODE >= 2);
     const int n = gridDim.x, wg = blockIdx.x, lane = threadIdx.x;
@@ -133,12 +180,71 @@ __global__ void __launch_bounds__(64) k_sync(uint32_t* ctr, uint32_t* data, int 
 
 extern "C" int mk_bench_sync(int mode, int n_wg, int rounds, void* d_ctr, void* d_data, void* d_out, void* stream) {
     if (n_wg < 1 || n_wg > 1024 || rounds < 1 || rounds > 100000 || !d_ctr || !d_data || !d_out || mode < 0 ||
-        mode > 3)
+        mode > 4)
         return 1;
-    const void* fns[4] = {(const void*)k_sync<0>, (const void*)k_sync<1>, (const void*)k_sync<2>,
-                          (const void*)k_sync<3>};
+    const void* fns[5] = {(const void*)k_sync<0>, (const void*)k_sync<1>, (const void*)k_sync<2>,
+                          (const void*)k_sync<3>, (const void*)k_sync<4>};
     void* args[] = {&d_ctr, &d_data, &rounds, &d_out};
     hipError_t e = hipLaunchCooperativeKernel(fns[mode], dim3(n_wg), dim3(64), args, 0, (hipStream_t)stream);
+    return e == hipSuccess ? 0 : 4;
+}
+
+// ------------------------------------------------------------------------------------------------
+// One-way latency of a value passed between two workgroups: workgroup 0 and
+// workgroup `peer` bounce an 8-byte {round, round} word back and forth `rounds`
+// times; the other workgroups of the grid leave at once.  Workgroups are placed
+// round-robin over the XCDs, so the peer index picks same-XCD or cross-XCD pairs
+// (out[2], out[3] report the XCC of each side).
+//   flavor 0: agent-scope relaxed atomic load and store
+//   flavor 1: system-scope relaxed atomic load and store
+// out[0] = ticks of workgroup 0 for all rounds, out[1] = waits that hit the bound.
+// ------------------------------------------------------------------------------------------------
+namespace {
+__device__ __forceinline__ uint32_t xcc_id() {
+    // HW_REG_XCC_ID (hardware register 20), bits [3:0]
+    return __builtin_amdgcn_s_getreg((15 << 11) | (0 << 6) | 20) & 15u;
+}
+
+template <int FLAVOR>
+__global__ void __launch_bounds__(64) k_pingpong(uint64_t* words, int peer, int rounds, uint64_t* out) {
+    const int wg = blockIdx.x;
+    if ((wg != 0 && wg != peer) || threadIdx.x != 0) return;
+    constexpr int scope = FLAVOR == 0 ? __HIP_MEMORY_SCOPE_AGENT : __HIP_MEMORY_SCOPE_SYSTEM;
+    uint64_t* mine = words + (wg == 0 ? 0 : 32);   // 256 bytes apart
+    uint64_t* theirs = words + (wg == 0 ? 32 : 0);
+    uint64_t misses = 0;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (int r = 1; r <= rounds; ++r) {
+        const uint64_t want = ((uint64_t)(uint32_t)r << 32) | (uint32_t)r;
+        if (wg == 0) __hip_atomic_store(mine, want, __ATOMIC_RELAXED, scope);
+        uint32_t guard = 0;
+        while ((int32_t)((uint32_t)(__hip_atomic_load(theirs, __ATOMIC_RELAXED, scope) >> 32) - (uint32_t)r) < 0) {
+            if (++guard > 4000000u) {
+                ++misses;
+                break;
+            }
+        }
+        if (misses) break;  // the other side is missing: stop
+        if (wg != 0) __hip_atomic_store(mine, want, __ATOMIC_RELAXED, scope);
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    if (wg == 0) {
+        out[0] = t1 - t0;
+        out[1] += misses;
+        out[2] = xcc_id();
+    } else {
+        out[3] = xcc_id();
+        if (misses) atomicAdd((unsigned long long*)&out[1], (unsigned long long)misses);
+    }
+}
+}  // namespace
+
+extern "C" int mk_bench_pingpong(int flavor, int peer, int rounds, void* d_words, void* d_out, void* stream) {
+    if (peer < 1 || peer > 255 || rounds < 1 || rounds > 100000 || !d_words || !d_out || flavor < 0 || flavor > 1)
+        return 1;
+    const void* f = flavor == 0 ? (const void*)k_pingpong<0> : (const void*)k_pingpong<1>;
+    void* args[] = {&d_words, &peer, &rounds, &d_out};
+    hipError_t e = hipLaunchCooperativeKernel(f, dim3(peer + 1), dim3(64), args, 0, (hipStream_t)stream);
     return e == hipSuccess ? 0 : 4;
 }
 

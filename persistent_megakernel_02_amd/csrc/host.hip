@@ -414,7 +414,9 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
     h->rt = *rt;
     h->stream = (hipStream_t)stream;
     const int n_cu = resolve_cus(rt);
-    if (n_cu <= 0 || n_cu > kMaxCus || (uint32_t)cfg->vocab < (uint32_t)n_cu) {
+    if (n_cu <= 0 || n_cu > kMaxCus || (uint32_t)cfg->vocab < (uint32_t)n_cu ||
+        (rt->mode == MK_MODE_MEGAKERNEL && n_cu > device_cus())) {
+        // the persistent kernel needs every workgroup resident: one per compute unit
         delete h;
         return MK_E_UNSUPPORTED;
     }

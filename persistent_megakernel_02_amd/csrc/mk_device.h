@@ -253,7 +253,9 @@ struct XLds {
 
 // out[i][b] = dot(row i, x_b) for the R rows of a batch.  Lane l accumulates
 // pieces p = l, l + 64, ... in ascending order, then wave_total reduces in its
-// fixed tree; a row's value never depends on R or on the other rows.
+// fixed tree; a row's value never depends on R or on the other rows.  (Issuing
+// four pieces' loads ahead of their use measured slower in the persistent
+// kernel: the extra registers cost more than the latency they hide.)
 template <int B, int R, class Rows, class X>
 __device__ __forceinline__ void rows_dot(const Rows& rows, int np, const X& x, float (&out)[R][B]) {
     const int lane = lane_id();
