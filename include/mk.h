@@ -177,7 +177,7 @@ mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* r
  * start, inputs staged, compute end, end, loader issue end, ticks waiting for
  * the loaders, ticks the loaders waited for ring space, staging start (after
  * the wave barrier), then for attention: inputs staged, KV groups consumed,
- * output written (0 elsewhere)}, times = low 32 bits of the 100 MHz
+ * output written; for the other ops: compute end of waves 1, 2, 3}, times = low 32 bits of the 100 MHz
  * s_memrealtime clock, in queue order.  With h_buf == NULL only *written (the
  * byte size) is set.  Synchronises the handle's creation stream. */
 mk_status mk_read_trace(mk_handle* h, void* h_buf, size_t bytes, size_t* written, int32_t* records_per_cu);

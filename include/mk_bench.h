@@ -49,6 +49,21 @@ int mk_bench_sync(int mode, int n_wg, int rounds, void* d_ctr, void* d_data, voi
  * wait is bounded.  Returns 0, 1 on bad arguments, 4 on launch error. */
 int mk_bench_pingpong(int flavor, int peer, int rounds, void* d_words, void* d_out, void* stream);
 
+/* One dependency edge of the decode step at its real size: n_wg (1..256)
+ * workgroups of four compute and four streaming waves, co-resident (cooperative
+ * launch).  Per round each workgroup publishes `words` (1..64) 8-byte {value,
+ * round} words; its compute waves gather all n_wg * words into LDS, re-polling
+ * stale words, then meet at a barrier.  stream != 0: the streaming waves read
+ * d_src (src_bytes >= n_wg * 4 KB) into LDS with direct-to-LDS loads, eight
+ * 1 KB loads in flight per wave, for as long as the rounds run (stream == 2:
+ * the loads carry the non-temporal hint).  d_data: 2 *
+ * n_wg * words zeroed uint64; d_out: three zeroed uint64 = {ticks (100 MHz) of
+ * workgroup 0's rounds, mismatches (lost waits count 2^20), KB streamed by
+ * workgroup 0's first streaming wave}.  Waits are bounded.  Returns 0, 1 on bad
+ * arguments, 4 on launch error. */
+int mk_bench_edge(int n_wg, int words, int rounds, int stream, const void* d_src, size_t src_bytes, void* d_data,
+                  void* d_out, void* hstream);
+
 /* HBM -> LDS streaming rate of the direct-to-LDS 16-byte-per-lane load:
  * n_wg workgroups of `waves` waves; each wave streams its share of d_src 1 KB
  * per load with `lag` loads in flight (lag in {4,12,24,32,40,48,60} for 1 wave,

@@ -249,6 +249,141 @@ extern "C" int mk_bench_pingpong(int flavor, int peer, int rounds, void* d_words
 }
 
 // ------------------------------------------------------------------------------------------------
+// One dependency edge of the decode step at its real size, with or without the
+// weight stream running beside it.  Each workgroup has four compute waves and
+// four streaming waves.  Per round every workgroup publishes `w` 8-byte
+// {value, round} words (agent-scope atomic stores), then its compute waves
+// gather all n * w words into LDS, re-polling the words whose round does not
+// match yet, and meet at a barrier of the four compute waves.  With `stream`
+// set, the streaming waves meanwhile read `src` into LDS with direct-to-LDS
+// loads (eight 1 KB loads in flight per wave) until the compute waves finish;
+// stream == 2 marks those loads non-temporal.
+// Words are double-buffered by round parity.  out[0] = ticks of workgroup 0's
+// rounds, out[1] = mismatches or lost waits, out[2] = KB streamed by workgroup 0.
+// ------------------------------------------------------------------------------------------------
+namespace {
+constexpr int kEdgeMaxWords = 64;
+
+__global__ void __launch_bounds__(512) k_edge(uint64_t* data, int w, int rounds, int stream, const char* src,
+                                              size_t src_kb, uint64_t* out) {
+    __shared__ float stage[4096];
+    __shared__ __attribute__((aligned(1024))) char ring[4 * 8 * 1024];
+    __shared__ uint32_t ctl[4];  // barrier arrivals, done flag
+    const int n = gridDim.x, wg = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (tid < 4) ctl[tid] = 0;
+    __syncthreads();
+    if (wave >= 4) {
+        // streaming wave: stream its share of src round and round until done
+        const int sw = wave - 4;
+        const uint32_t base = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)ring + sw * 8192u;
+        const size_t streams = (size_t)n * 4, sid = (size_t)wg * 4 + sw;
+        const size_t per = src_kb / streams;
+        uint64_t kb = 0;
+        if (stream && per > 0) {
+            for (uint32_t guard = 0; guard < (1u << 24); ++guard) {
+                if (__hip_atomic_load(&ctl[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) break;
+                const size_t c = sid * per + (guard % per);
+                if (stream == 2)
+                    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                                 :
+                                 : "{m0}"(__builtin_amdgcn_readfirstlane(base + (guard & 7u) * 1024u)),
+                                   "v"(src + c * 1024 + lane * 16)
+                                 : "memory");
+                else
+                    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                                 :
+                                 : "{m0}"(__builtin_amdgcn_readfirstlane(base + (guard & 7u) * 1024u)),
+                                   "v"(src + c * 1024 + lane * 16)
+                                 : "memory");
+                __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8));
+                ++kb;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
+        if (wg == 0 && sw == 0 && lane == 0) out[2] = kb;
+        return;
+    }
+    const int total = n * w;
+    uint32_t errors = 0;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    bool lost = false;
+    for (int r = 1; r <= rounds && !lost; ++r) {
+        uint64_t* buf = data + (size_t)(r & 1) * total;
+        if (wave == 0 && lane < w) {
+            const uint32_t val = (uint32_t)r * 131071u + (uint32_t)(wg * w + lane);
+            __hip_atomic_store(&buf[wg * w + lane], ((uint64_t)(uint32_t)r << 32) | val, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // gather: lane of wave `wave` takes words e = 64 * wave + lane + 256 * i
+        for (int e0 = 64 * wave; e0 < total && !lost; e0 += 256 * 16) {
+            uint64_t v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int e = e0 + lane + 256 * i;
+                v[i] = e < total ? __hip_atomic_load(&buf[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                 : ((uint64_t)(uint32_t)r << 32);
+            }
+            for (uint32_t guard = 0;; ++guard) {
+                bool ok = true;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) ok &= (uint32_t)(v[i] >> 32) == (uint32_t)r;
+                if (__all(ok)) break;
+                if (guard > 4000000u) {
+                    lost = true;
+                    errors += 1u << 20;
+                    break;
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int e = e0 + lane + 256 * i;
+                    if ((uint32_t)(v[i] >> 32) != (uint32_t)r)
+                        v[i] = __hip_atomic_load(&buf[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int e = e0 + lane + 256 * i;
+                if (e < total) {
+                    errors += (uint32_t)v[i] != (uint32_t)r * 131071u + (uint32_t)e;
+                    if (e < 4096) stage[e] = __uint_as_float((uint32_t)v[i]);
+                }
+            }
+        }
+        // barrier of the four compute waves
+        if (lane == 0) __hip_atomic_fetch_add(&ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        for (uint32_t guard = 0; __hip_atomic_load(&ctl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) <
+                                 (uint32_t)(4 * r);
+             ++guard) {
+            if (guard > 4000000u) {
+                lost = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(0);
+        }
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    if (lane == 0) __hip_atomic_store(&ctl[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int m = 32; m >= 1; m >>= 1) errors += __shfl_xor(errors, m, 64);
+    if (lane == 0) {
+        if (wg == 0 && wave == 0) out[0] = t1 - t0;
+        if (errors) atomicAdd((unsigned long long*)&out[1], (unsigned long long)errors);
+    }
+}
+}  // namespace
+
+extern "C" int mk_bench_edge(int n_wg, int words, int rounds, int stream, const void* d_src, size_t src_bytes,
+                             void* d_data, void* d_out, void* hstream) {
+    if (n_wg < 1 || n_wg > 256 || words < 1 || words > kEdgeMaxWords || rounds < 1 || rounds > 100000 || !d_data ||
+        !d_out || (stream && (!d_src || src_bytes < (size_t)n_wg * 4 * 1024)))
+        return 1;
+    size_t kb = stream ? src_bytes / 1024 : 0;
+    void* args[] = {&d_data, &words, &rounds, &stream, (void*)&d_src, &kb, &d_out};
+    hipError_t e = hipLaunchCooperativeKernel((const void*)k_edge, dim3(n_wg), dim3(512), args, 0,
+                                              (hipStream_t)hstream);
+    return e == hipSuccess ? 0 : 4;
+}
+
+// ------------------------------------------------------------------------------------------------
 // HBM -> LDS streaming rate of the direct-to-LDS load the decode loader uses:
 // every workgroup (one per CU) runs WAVES waves; each wave streams its share of
 // `src` 1 KB at a time into a private 32 KB LDS ring with LAG loads in flight.

@@ -120,8 +120,9 @@ struct Params {
 // Trace record of one instruction on one CU (s_memrealtime ticks, low 32 bits):
 // {op | layer << 16, start, inputs staged, compute end, end, loader issue end,
 //  ticks waiting for landed chunks, ticks the loaders waited for ring space,
-//  staging start (after the wave barrier), then op-specific marks: attention
-//  inputs staged, its KV groups consumed, its merged output written; 0 = unused}
+//  staging start (after the wave barrier), then three op-specific words: for
+//  attention the marks inputs staged, KV groups consumed, merged output
+//  written; for the other ops the compute ends of waves 1, 2, 3; 0 = unused}
 constexpr int kTraceWords = 12;
 
 // Per-launch arguments.

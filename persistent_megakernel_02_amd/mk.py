@@ -24,7 +24,7 @@ MK_MODE_MEGAKERNEL, MK_MODE_GRAPH = 0, 1
 EXPORTS = ["mk_query_sizes", "mk_create", "mk_kv_layout", "mk_prefill", "mk_set_context_len", "mk_decode_step",
            "mk_get_context_len", "mk_reset", "mk_debug_inject", "mk_status_string", "mk_last_error",
            "mk_plan_inspect", "mk_kernels_per_step", "mk_destroy", "mk_bench_stream_read", "mk_bench_copy",
-           "mk_bench_sync", "mk_read_trace", "mk_bench_lds_stream", "mk_bench_pingpong"]
+           "mk_bench_sync", "mk_read_trace", "mk_bench_lds_stream", "mk_bench_pingpong", "mk_bench_edge"]
 
 
 class mk_model_config(ctypes.Structure):
@@ -87,11 +87,12 @@ def lib():
         L.mk_bench_copy.argtypes = [vp, vp, sz, vp]
         L.mk_bench_sync.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
         L.mk_bench_pingpong.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+        L.mk_bench_edge.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, sz, vp, vp, vp]
         L.mk_read_trace.argtypes = [vp, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(i32)]
         L.mk_bench_lds_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, sz, ctypes.c_int, vp, vp]
         for n in ("mk_query_sizes", "mk_create", "mk_kv_layout", "mk_prefill", "mk_set_context_len",
                   "mk_get_context_len", "mk_decode_step", "mk_reset", "mk_debug_inject", "mk_plan_inspect",
-                  "mk_destroy", "mk_bench_stream_read", "mk_bench_copy", "mk_bench_sync", "mk_read_trace", "mk_bench_lds_stream", "mk_bench_pingpong"):
+                  "mk_destroy", "mk_bench_stream_read", "mk_bench_copy", "mk_bench_sync", "mk_read_trace", "mk_bench_lds_stream", "mk_bench_pingpong", "mk_bench_edge"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
