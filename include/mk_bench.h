@@ -64,6 +64,17 @@ int mk_bench_pingpong(int flavor, int peer, int rounds, void* d_words, void* d_o
 int mk_bench_edge(int n_wg, int words, int rounds, int stream, const void* d_src, size_t src_bytes, void* d_data,
                   void* d_out, void* hstream);
 
+/* How much a weight stream slows LDS-bound compute on the same compute unit:
+ * n_wg (1..256) co-resident workgroups of four compute and four streaming waves.
+ * The compute waves run `iters` steps of four 16-byte LDS reads and 16 FMAs;
+ * meanwhile the streaming waves read d_src (src_bytes >= n_wg * 4 KB) with mode
+ * 0: nothing; 1: direct-to-LDS loads, eight 1 KB loads in flight per wave; 2:
+ * plain 16-byte loads into registers.  d_out: four zeroed uint64 = {ticks (100
+ * MHz) of workgroup 0's compute wave 0, KB streamed by its first streaming wave,
+ * unused, unused}.  Returns 0, 1 on bad arguments, 4 on launch error. */
+int mk_bench_lds_contention(int mode, int iters, int n_wg, const void* d_src, size_t src_bytes, void* d_out,
+                            void* stream);
+
 /* HBM -> LDS streaming rate of the direct-to-LDS 16-byte-per-lane load:
  * n_wg workgroups of `waves` waves; each wave streams its share of d_src 1 KB
  * per load with `lag` loads in flight (lag in {4,12,24,32,40,48,60} for 1 wave,

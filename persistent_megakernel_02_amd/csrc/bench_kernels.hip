@@ -384,6 +384,89 @@ extern "C" int mk_bench_edge(int n_wg, int words, int rounds, int stream, const 
 }
 
 // ------------------------------------------------------------------------------------------------
+// How much a weight stream slows LDS-bound compute on the same compute unit.
+// Four compute waves run `iters` steps of (four 16-byte LDS reads, 32 FMAs
+// that use them); four streaming waves meanwhile read `src` with mode 0: nothing;
+// mode 1: direct-to-LDS loads (eight 1 KB loads in flight per wave); mode 2: the
+// same bytes into registers with plain 16-byte loads.  out[0] = ticks (100 MHz)
+// of wave 0 of workgroup 0 for its steps, out[1] = KB streamed by workgroup 0's
+// first streaming wave, out[2] = a checksum that keeps the arithmetic alive.
+// ------------------------------------------------------------------------------------------------
+namespace {
+__global__ void __launch_bounds__(512) k_lds_contention(int mode, int iters, const char* src, size_t src_kb,
+                                                        uint64_t* out) {
+    __shared__ __attribute__((aligned(1024))) char ring[4 * 8 * 1024];
+    __shared__ __attribute__((aligned(16))) float tile[4][2048];
+    __shared__ uint32_t done;
+    const int n = gridDim.x, wg = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    for (int i = tid; i < 4 * 2048; i += 512) (&tile[0][0])[i] = (float)(i & 255) * 1e-3f;
+    if (tid == 0) done = 0;
+    __syncthreads();
+    if (wave >= 4) {
+        const int sw = wave - 4;
+        const uint32_t base = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)ring + sw * 8192u;
+        const size_t streams = (size_t)n * 4, sid = (size_t)wg * 4 + sw;
+        const size_t per = src_kb / streams;
+        uint64_t kb = 0;
+        uint32_t acc = 0;
+        if (mode != 0 && per > 0) {
+            for (uint32_t guard = 0; guard < (1u << 24); ++guard) {
+                if (__hip_atomic_load(&done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) break;
+                const size_t c = sid * per + (guard % per);
+                if (mode == 1) {
+                    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                                 :
+                                 : "{m0}"(__builtin_amdgcn_readfirstlane(base + (guard & 7u) * 1024u)),
+                                   "v"(src + c * 1024 + lane * 16)
+                                 : "memory");
+                    __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8));
+                } else {
+                    const uint4 v = *(const uint4*)(src + c * 1024 + lane * 16);
+                    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+                }
+                ++kb;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
+        if (wg == 0 && sw == 0 && lane == 0) out[1] = kb;
+        if (acc == 0x9E3779B9u) out[3] = acc;
+        return;
+    }
+    const float* t = tile[wave];
+    float a0 = 0.f, a1 = 0.f;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+        const int o = ((it * 16 + lane) * 8) & 2047;
+        const float4 x0 = *(const float4*)(t + o);
+        const float4 x1 = *(const float4*)(t + ((o + 512) & 2047));
+        const float4 x2 = *(const float4*)(t + ((o + 1024) & 2047));
+        const float4 x3 = *(const float4*)(t + ((o + 1536) & 2047));
+        a0 = fmaf(x0.x, x1.x, a0); a1 = fmaf(x0.y, x1.y, a1); a0 = fmaf(x0.z, x1.z, a0); a1 = fmaf(x0.w, x1.w, a1);
+        a0 = fmaf(x2.x, x3.x, a0); a1 = fmaf(x2.y, x3.y, a1); a0 = fmaf(x2.z, x3.z, a0); a1 = fmaf(x2.w, x3.w, a1);
+        a0 = fmaf(x0.x, x3.x, a0); a1 = fmaf(x0.y, x3.y, a1); a0 = fmaf(x0.z, x3.z, a0); a1 = fmaf(x0.w, x3.w, a1);
+        a0 = fmaf(x2.x, x1.x, a0); a1 = fmaf(x2.y, x1.y, a1); a0 = fmaf(x2.z, x1.z, a0); a1 = fmaf(x2.w, x1.w, a1);
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    if (lane == 0 && wave == 0) __hip_atomic_store(&done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (wg == 0 && wave == 0 && lane == 0) out[0] = t1 - t0;
+    if (a0 + a1 == 123456.f) out[2] = 1;
+}
+}  // namespace
+
+extern "C" int mk_bench_lds_contention(int mode, int iters, int n_wg, const void* d_src, size_t src_bytes,
+                                       void* d_out, void* stream) {
+    if (mode < 0 || mode > 2 || iters < 1 || n_wg < 1 || n_wg > 256 || !d_out ||
+        (mode && (!d_src || src_bytes < (size_t)n_wg * 4 * 1024)))
+        return 1;
+    int m = mode, it = iters;
+    size_t kb = mode ? src_bytes / 1024 : 0;
+    void* args[] = {&m, &it, (void*)&d_src, &kb, &d_out};
+    hipError_t e = hipLaunchCooperativeKernel((const void*)k_lds_contention, dim3(n_wg), dim3(512), args, 0,
+                                              (hipStream_t)stream);
+    return e == hipSuccess ? 0 : 4;
+}
+
+// ------------------------------------------------------------------------------------------------
 // HBM -> LDS streaming rate of the direct-to-LDS load the decode loader uses:
 // every workgroup (one per CU) runs WAVES waves; each wave streams its share of
 // `src` 1 KB at a time into a private 32 KB LDS ring with LAG loads in flight.

@@ -92,17 +92,22 @@ __global__ void __launch_bounds__(kConvThreads) k_norm_gemv(Params P, StepArgs A
                             : OP == OP_GATEUP ? phase_tag(A.tag0, layer, 2)
                                               : phase_tag(A.tag0, P.L - 1, 4);
     const uint32_t d = (uint32_t)P.d;
+    float ss[B];
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-        float ss = 0.f;
-        if (OP == OP_QKV && layer == 0) {
+    for (int b = 0; b < B; ++b) ss[b] = 0.f;
+    if (OP == OP_QKV && layer == 0) {
+#pragma unroll
+        for (int b = 0; b < B; ++b)
             stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * d, d, xs + b * d, gain, wave, kConvWaves,
-                       ss);
-        } else if (!stage_tagged<true>(P.h + (size_t)b * d, d, tag_in, xs + b * d, gain, wave, kConvWaves, spin, ss)) {
-            return;
-        }
-        ss = wave_total(ss);
-        if (lane == 0) ssp[b][wave] = ss;
+                       ss[b]);
+    } else {
+        const StageSeg sg[1] = {{P.h, xs, gain, d, (uint32_t)B, d, d, tag_in}};
+        if (!stage_segs<kStagePassWords, B, 1>(sg, wave, kConvWaves, spin, ss)) return;
+    }
+    wave_total_n<B>(ss);
+    if (lane == 0) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) ssp[b][wave] = ss[b];
     }
     __syncthreads();
     float r[B];
@@ -183,19 +188,18 @@ __global__ void __launch_bounds__(kConvThreads) k_proj(Params P, StepArgs A, int
     const uint32_t begin = blockIdx.x * kRowsPerBlock;
     const uint32_t count = min(kRowsPerBlock, (uint32_t)P.d - begin);
     float* hres = xs + B * K;
+    float ss[1] = {0.f};
+    const StageSeg sx = {is_down ? P.act : P.attn, xs, nullptr, K, (uint32_t)B, K, K, tag_x};
+    if (!is_down && layer == 0) {
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-        float ss = 0.f;
-        if (!stage_tagged<false>((is_down ? P.act : P.attn) + (size_t)b * K, K, tag_x, xs + b * K, nullptr, wave,
-                                 kConvWaves, spin, ss))
-            return;
-        if (!is_down && layer == 0) {
+        for (int b = 0; b < B; ++b)
             stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * P.d + begin, count, hres + b * count,
-                       nullptr, wave, kConvWaves, ss);
-        } else if (!stage_tagged<false>(P.h + (size_t)b * P.d + begin, count, tag_res, hres + b * count, nullptr,
-                                        wave, kConvWaves, spin, ss)) {
-            return;
-        }
+                       nullptr, wave, kConvWaves, ss[0]);
+        const StageSeg sg[1] = {sx};
+        if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kConvWaves, spin, ss)) return;
+    } else {
+        const StageSeg sg[2] = {sx, {P.h + begin, hres, nullptr, count, (uint32_t)B, (uint32_t)P.d, count, tag_res}};
+        if (!stage_segs<kStagePassWordsWide, 1, 2>(sg, wave, kConvWaves, spin, ss)) return;
     }
     __syncthreads();
     const XLds x{xs, K};

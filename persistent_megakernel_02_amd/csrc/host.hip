@@ -57,9 +57,7 @@ size_t x_floats(const mk_model_config* c, const mk_runtime_config* rt, int nspli
     size_t n = B * (size_t)c->hidden;
     n = std::max(n, B * ((size_t)c->n_q_heads * hd + kMaxResidRows));
     n = std::max(n, B * ((size_t)c->ffn + kMaxResidRows));
-    const size_t slots = (size_t)(kAttnBlockGroups + 1) * (64 / (hd / 8));  // scores of one block of groups
-    const size_t attn = (G + 2) * hd + (size_t)kComputeWaves * slots + (size_t)nsplit * G * (hd + 2) + 4;
-    return std::max(n, attn);
+    return std::max(n, attn_lds_floats((int)G, (int)hd, nsplit));
 }
 
 size_t x_bytes_for(const mk_model_config* c, const mk_runtime_config* rt, int nsplit) {

@@ -556,18 +556,22 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                                         : in.op == OP_GATEUP ? phase_tag(A.tag0, layer, 2)
                                                              : phase_tag(A.tag0, P.L - 1, 4);
                 const uint32_t d = (uint32_t)P.d;
+                float ss[B];
 #pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    float ss = 0.f;
-                    if (in.op == OP_QKV && layer == 0) {
+                for (int b = 0; b < B; ++b) ss[b] = 0.f;
+                if (in.op == OP_QKV && layer == 0) {
+#pragma unroll
+                    for (int b = 0; b < B; ++b)
                         stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * d, d, xs + b * d, gain, wave,
-                                   kComputeWaves, ss);
-                    } else if (!stage_tagged<true>(P.h + (size_t)b * d, d, tag_in, xs + b * d, gain, wave,
-                                                   kComputeWaves, spin, ss)) {
-                        return;
-                    }
-                    ss = wave_total(ss);
-                    if (lane == 0) ctl->ss[b][wave] = ss;
+                                   kComputeWaves, ss[b]);
+                } else {
+                    const StageSeg sg[1] = {{P.h, xs, gain, d, (uint32_t)B, d, d, tag_in}};
+                    if (!stage_segs<kStagePassWords, B, 1>(sg, wave, kComputeWaves, spin, ss)) return;
+                }
+                wave_total_n<B>(ss);
+                if (lane == 0) {
+#pragma unroll
+                    for (int b = 0; b < B; ++b) ctl->ss[b][wave] = ss[b];
                 }
                 if (!barrier()) return;
                 float r[B];
@@ -643,19 +647,20 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                 const uint32_t tag_res = is_o ? phase_tag(A.tag0, layer - 1, 4) : phase_tag(A.tag0, layer, 2);
                 const uint32_t tag_out = is_o ? phase_tag(A.tag0, layer, 2) : phase_tag(A.tag0, layer, 4);
                 float* hres = xs + B * K;  // [B][count] residual rows before this op
+                float ss[1] = {0.f};
+                const StageSeg sx = {is_o ? P.attn : P.act, xs, nullptr, K, (uint32_t)B, K, K, tag_x};
+                if (is_o && layer == 0) {
+                    // the residual is the token embedding: no wait
 #pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    float ss = 0.f;
-                    if (!stage_tagged<false>((is_o ? P.attn : P.act) + (size_t)b * K, K, tag_x, xs + b * K, nullptr,
-                                             wave, kComputeWaves, spin, ss))
-                        return;
-                    if (is_o && layer == 0) {
+                    for (int b = 0; b < B; ++b)
                         stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * P.d + in.begin, in.count,
-                                   hres + b * in.count, nullptr, wave, kComputeWaves, ss);
-                    } else if (!stage_tagged<false>(P.h + (size_t)b * P.d + in.begin, in.count, tag_res,
-                                                    hres + b * in.count, nullptr, wave, kComputeWaves, spin, ss)) {
-                        return;
-                    }
+                                   hres + b * in.count, nullptr, wave, kComputeWaves, ss[0]);
+                    const StageSeg sg[1] = {sx};
+                    if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kComputeWaves, spin, ss)) return;
+                } else {
+                    const StageSeg sg[2] = {sx, {P.h + in.begin, hres, nullptr, in.count, (uint32_t)B, (uint32_t)P.d,
+                                                 in.count, tag_res}};
+                    if (!stage_segs<kStagePassWordsWide, 1, 2>(sg, wave, kComputeWaves, spin, ss)) return;
                 }
                 if (!barrier()) return;
                 if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
@@ -676,7 +681,7 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                 const int b = (int)in.begin / per_b, g = ((int)in.begin % per_b) / P.nsplit,
                           s = (int)in.begin % P.nsplit;
                 // stream: [RoPE row 1 KB][group 0: K 1 KB, V 1 KB][group 1] ...
-                const RingKV kv{ring, S + kChunk, P.ring_chunks};
+                const RingKV<HD> kv{ring, S + kChunk, P.ring_chunks};
                 auto need = [&](int t) -> bool {  // group t resident (K and V chunks); t = -1: the RoPE row
                     return wait_landed(P, ctl, (S + kChunk + (uint32_t)(t + 1) * 2048u) / kChunk, land_wait);
                 };

@@ -78,6 +78,28 @@ __device__ __forceinline__ float wave_total(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// wave_total of N values at once: the same tree, one DPP step applied to every
+// value before the next step, so consecutive DPP reads never depend on each
+// other (no wait states between them).  Each result is bit-identical to
+// wave_total of that value alone.
+template <int N>
+__device__ __forceinline__ void wave_total_n(float (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += __builtin_amdgcn_update_dpp(0.0f, v[i], 0xB1, 0xF, 0xF, false);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += __builtin_amdgcn_update_dpp(0.0f, v[i], 0x4E, 0xF, 0xF, false);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += __builtin_amdgcn_update_dpp(0.0f, v[i], 0x141, 0xF, 0xF, false);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += __builtin_amdgcn_update_dpp(0.0f, v[i], 0x140, 0xF, 0xF, false);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += __builtin_amdgcn_update_dpp(0.0f, v[i], 0x142, 0xA, 0xF, false);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += __builtin_amdgcn_update_dpp(0.0f, v[i], 0x143, 0xC, 0xF, false);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 63));
+}
+
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64).
 __device__ __forceinline__ float group_sum(float v, int width) {
     for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m, 64);
@@ -161,47 +183,166 @@ struct Spin {
 };
 
 // ---------------------------------------------------------------------------------------------
-// Staging: wave w of nw moves elements e = 64 (w + nw i) + lane of a vector into
-// LDS, kStageWords words per lane in flight, polling until every tag matches.
+// Staging of tagged activations into LDS.  A segment is `rows` rows of n tagged
+// words (row r at src + r * src_stride) that land as fp32 at dst + r * dst_stride,
+// optionally times a bf16 gain g[i] (the RMSNorm weight).  The segments of one
+// instruction are numbered as one sequence; wave w of nw takes elements
+// e = 64 (w + nw k) + lane, K words per lane per pass.  Every load of a pass
+// is issued at once (the gains with the words), and the next pass is issued
+// before the current one is checked, so a staging costs about one memory round
+// trip however many segments and passes it has.  Words whose tag does not match
+// yet are re-read until it does (bounded by the watchdog).
 // ---------------------------------------------------------------------------------------------
-// dst[e] = value of src[e] (optionally times the bf16 gain g[e]); ss gets the
-// lane's sum of squares of the raw values in ascending i (RMSNorm statistics).
-template <bool GAIN>
-__device__ __forceinline__ bool stage_tagged(const uint64_t* __restrict__ src, uint32_t n, uint32_t tag,
-                                             float* __restrict__ dst, const uint16_t* __restrict__ g, int w, int nw,
-                                             Spin& spin, float& ss) {
+struct StageSeg {
+    const uint64_t* src;
+    float* dst;
+    const uint16_t* g;  // gain, or nullptr
+    uint32_t n, rows, src_stride, dst_stride;
+    uint32_t tag;       // tag the words must carry
+};
+
+// Element e of the concatenated segments resolved to its row's source, target,
+// gain and tag.  The segment fields are wave-uniform; only the choice between
+// them is per lane, made by selects (no indexing of the segment array by a
+// per-lane value, which would move it to scratch memory).
+struct StageLoc {
+    const uint64_t* src;  // the tagged word
+    float* dst;           // where its value lands
+    const uint16_t* g;    // its gain, or nullptr
+    uint32_t tag;
+    uint32_t row;
+};
+
+template <class T>
+__device__ __forceinline__ T* uniform_p(T* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (T*)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ uint32_t uniform_u(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <int NS>
+struct StageMap {
+    // the segment fields as wave-uniform register values (read once)
+    const uint64_t* src[NS];
+    float* dst[NS];
+    const uint16_t* g[NS];
+    uint32_t n[NS], rows[NS], ss[NS], ds[NS], tag[NS], end[NS];
+    uint32_t total;
+    __device__ __forceinline__ explicit StageMap(const StageSeg (&s)[NS]) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            src[i] = uniform_p(s[i].src);
+            dst[i] = uniform_p(s[i].dst);
+            g[i] = uniform_p(s[i].g);
+            n[i] = uniform_u(s[i].n);
+            ss[i] = uniform_u(s[i].src_stride);
+            ds[i] = uniform_u(s[i].dst_stride);
+            tag[i] = uniform_u(s[i].tag);
+            rows[i] = uniform_u(s[i].rows);
+            t += n[i] * rows[i];
+            end[i] = t;
+        }
+        total = t;
+    }
+    __device__ __forceinline__ StageLoc locate(uint32_t e) const {
+        const uint64_t* sp = src[0];
+        float* dp = dst[0];
+        const uint16_t* gp = g[0];
+        uint32_t nn = n[0], nr = rows[0], s1 = ss[0], d1 = ds[0], tg = tag[0], e0 = 0;
+#pragma unroll
+        for (int k = 1; k < NS; ++k) {
+            const bool in = e >= end[k - 1];
+            sp = in ? src[k] : sp;
+            dp = in ? dst[k] : dp;
+            gp = in ? g[k] : gp;
+            nn = in ? n[k] : nn;
+            nr = in ? rows[k] : nr;
+            s1 = in ? ss[k] : s1;
+            d1 = in ? ds[k] : d1;
+            tg = in ? tag[k] : tg;
+            e0 = in ? end[k - 1] : e0;
+        }
+        // row of element x of the segment by comparisons (at most kMaxBatch rows):
+        // no integer division per element
+        const uint32_t x = e - e0;
+        uint32_t r = 0;
+#pragma unroll
+        for (int k = 1; k < kMaxBatch; ++k) r += ((uint32_t)k < nr && x >= (uint32_t)k * nn) ? 1u : 0u;
+        const uint32_t i = x - r * nn;
+        return StageLoc{sp + (size_t)r * s1 + i, dp + (size_t)r * d1 + i, gp ? gp + i : nullptr, tg, r};
+    }
+};
+
+// ss[r] gets the lane's sum of squares of the raw values of row r of the gained
+// segments, in ascending element order (RMSNorm statistics).
+template <int K, int R, int NS>
+__device__ __forceinline__ bool stage_segs(const StageSeg (&sg)[NS], int w, int nw, Spin& spin, float (&ss)[R]) {
+    const StageMap<NS> map(sg);
     const uint32_t lane = (uint32_t)lane_id();
     const uint32_t step = 64u * (uint32_t)nw;
-    // `base` is wave-uniform so every lane takes part in the polls
-    for (uint32_t base = 64u * (uint32_t)w; base < n; base += step * kStageWords) {
-        uint64_t v[kStageWords];
+    const uint32_t per_pass = step * (uint32_t)K;
+    const uint32_t total = map.total;
+    // loads of the pass starting at p0 (elements past the end re-read element 0)
+    auto issue = [&](uint32_t p0, uint64_t (&v)[K], uint32_t (&gv)[K]) {
 #pragma unroll
-        for (int i = 0; i < kStageWords; ++i) {
-            const uint32_t e = base + lane + step * i;
-            v[i] = e < n ? ld_tagged(src + e) : ((uint64_t)tag << 32);
+        for (int k = 0; k < K; ++k) {
+            const uint32_t e = p0 + 64u * (uint32_t)w + lane + step * (uint32_t)k;
+            const StageLoc L = map.locate(e < total ? e : 0u);
+            v[k] = ld_tagged(L.src);
+            gv[k] = *(L.g ? L.g : (const uint16_t*)L.src);
         }
+    };
+    // wait for, check and store the pass starting at p0
+    auto finish = [&](uint32_t p0, uint64_t (&v)[K], const uint32_t (&gv)[K]) -> bool {
         spin.start();
         for (;;) {
             bool ok = true;
 #pragma unroll
-            for (int i = 0; i < kStageWords; ++i) ok &= tv_tag(v[i]) == tag;
+            for (int k = 0; k < K; ++k) {
+                const uint32_t e = p0 + 64u * (uint32_t)w + lane + step * (uint32_t)k;
+                ok &= e >= total || tv_tag(v[k]) == map.locate(e).tag;
+            }
             if (__all(ok)) break;
-            if (!spin.again(tag, base)) return false;
+            if (!spin.again(map.tag[0], p0)) return false;
 #pragma unroll
-            for (int i = 0; i < kStageWords; ++i) {
-                const uint32_t e = base + lane + step * i;
-                if (tv_tag(v[i]) != tag) v[i] = ld_tagged(src + e);
+            for (int k = 0; k < K; ++k) {
+                const uint32_t e = p0 + 64u * (uint32_t)w + lane + step * (uint32_t)k;
+                if (e < total) {
+                    const StageLoc L = map.locate(e);
+                    if (tv_tag(v[k]) != L.tag) v[k] = ld_tagged(L.src);
+                }
             }
         }
 #pragma unroll
-        for (int i = 0; i < kStageWords; ++i) {
-            const uint32_t e = base + lane + step * i;
-            if (e < n) {
-                const float x = tv_val(v[i]);
-                ss = fmaf(x, x, ss);
-                dst[e] = GAIN ? x * bf_to_f(g[e]) : x;
+        for (int k = 0; k < K; ++k) {
+            const uint32_t e = p0 + 64u * (uint32_t)w + lane + step * (uint32_t)k;
+            if (e < total) {
+                const StageLoc L = map.locate(e);
+                const float x = tv_val(v[k]);
+                if (L.g) {
+#pragma unroll
+                    for (int rr = 0; rr < R; ++rr)
+                        if (rr == (int)L.row) ss[rr] = fmaf(x, x, ss[rr]);
+                    *L.dst = x * bf_to_f((uint16_t)gv[k]);
+                } else {
+                    *L.dst = x;
+                }
             }
         }
+        return true;
+    };
+    uint64_t va[K], vb[K];
+    uint32_t ga[K], gb[K];
+    issue(0u, va, ga);
+    for (uint32_t p0 = 0;; p0 += 2u * per_pass) {
+        issue(p0 + per_pass, vb, gb);
+        if (!finish(p0, va, ga)) return false;
+        if (p0 + per_pass >= total) break;
+        issue(p0 + 2u * per_pass, va, ga);
+        if (!finish(p0 + per_pass, vb, gb)) return false;
+        if (p0 + 2u * per_pass >= total) break;
     }
     return true;
 }
@@ -277,10 +418,16 @@ __device__ __forceinline__ void rows_dot(const Rows& rows, int np, const X& x, f
 #pragma unroll
             for (int b = 0; b < B; ++b) acc[i][b] = dot8(w[i], xa[b], xb[b], acc[i][b]);
     }
+    float t[R * B];
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
-        for (int b = 0; b < B; ++b) out[i][b] = wave_total(acc[i][b]);
+        for (int b = 0; b < B; ++b) t[i * B + b] = acc[i][b];
+    wave_total_n<R * B>(t);
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int b = 0; b < B; ++b) out[i][b] = t[i * B + b];
 }
 
 // Rows of one compute wave's batch for a row of `rb` bytes: about 8 KB per wave.
@@ -318,50 +465,75 @@ __device__ __forceinline__ bool head_better(float v, int32_t i, float bv, int32_
 
 // ---------------------------------------------------------------------------------------------
 // Attention of one (sequence b, KV head g, split s) over the positions of that split.
-// Online softmax per lane, then merges across position groups (butterfly), across
-// waves (through LDS, fixed order) and, when split, across splits (fixed order, by
-// the last split to finish).
 //
-// KV sources give the 16-byte piece (8 dims) of K or V at group t for this lane.
-// Group t holds PPW consecutive positions; lane -> (position ps = lane / LPP,
-// dims dl = 8 * (lane % LPP)).
+// The G query heads of a KV head read the same keys and values, so each of the
+// four compute waves takes a quarter of the positions (every fourth group of
+// PPW positions) and scores all G heads on them; each wave keeps its own online
+// softmax (running maximum, sum, weighted V) per head, and the four wave
+// partials are merged at the end in wave order, as split partials are merged in
+// split order.
+//
+// Score pass: lane -> (position slot ps = lane / LPP, dims dl .. dl + 7 with
+// dl = 8 * (lane % LPP)); the per-position dot is summed over the slot's lanes
+// with DPP.  Value pass: lane -> dims lane * DPL .. + DPL - 1, one position at a
+// time, so no reduction across lanes is needed.
 // ---------------------------------------------------------------------------------------------
 template <int HD>
 struct AttnGeom {
-    static constexpr int LPP = HD / 8;    // lanes per position
+    static constexpr int LPP = HD / 8;    // lanes per position (score pass)
     static constexpr int PPW = 64 / LPP;  // positions per 1 KB group
+    static constexpr int DPL = HD / 64;   // dims per lane (value pass)
 };
+
+// bf16 values of dims lane * DPL .. + DPL - 1 read from an address (2 or 4 bytes).
+template <int DPL>
+__device__ __forceinline__ void load_vdims(const char* p, float (&v)[DPL]) {
+    if constexpr (DPL == 1) {
+        v[0] = bf_to_f(*(const uint16_t*)p);
+    } else {
+        const uint32_t u = *(const uint32_t*)p;
+        v[0] = bf_lo(u);
+        v[1] = bf_hi(u);
+    }
+}
 
 // K/V groups of an attention item in the LDS ring: block(t0) gives the groups
 // from t0 on (at most kAttnBlockGroups of them, so one wrap at most).
+template <int HD>
 struct RingKV {
     const char* ring;
     uint32_t S, nchunks;  // stream byte of the item's first group (group t = [K 1 KB][V 1 KB]), ring size
     struct Block {
         const char* ring;
         uint32_t base, ring_bytes;  // ring byte of group t0
-        __device__ __forceinline__ uint4 at(uint32_t off) const {
-            uint32_t a = base + off + lane_id() * 16u;
-            a = a >= ring_bytes ? a - ring_bytes : a;
-            return *(const uint4*)(ring + a);
+        __device__ __forceinline__ uint32_t addr(uint32_t off) const {
+            const uint32_t a = base + off;
+            return a >= ring_bytes ? a - ring_bytes : a;
         }
-        __device__ __forceinline__ uint4 k(int t) const { return at((uint32_t)t * 2048u); }
-        __device__ __forceinline__ uint4 v(int t) const { return at((uint32_t)t * 2048u + 1024u); }
+        // this lane's 16-byte piece of K in group t (score-pass mapping)
+        __device__ __forceinline__ uint4 k(int t) const {
+            return *(const uint4*)(ring + addr((uint32_t)t * 2048u + lane_id() * 16u));
+        }
+        // this lane's 16-byte piece of V in group t (score-pass mapping)
+        __device__ __forceinline__ uint4 vp(int t) const {
+            return *(const uint4*)(ring + addr((uint32_t)t * 2048u + 1024u + lane_id() * 16u));
+        }
+        // this lane's dims of V at position slot `slot` of group t (value-pass mapping)
+        __device__ __forceinline__ void v(int t, int slot, float (&out)[AttnGeom<HD>::DPL]) const {
+            constexpr int DPL = AttnGeom<HD>::DPL;
+            load_vdims<DPL>(ring + addr((uint32_t)t * 2048u + 1024u + (uint32_t)slot * (HD * 2u) +
+                                        (uint32_t)lane_id() * (DPL * 2u)),
+                            out);
+        }
     };
     __device__ __forceinline__ Block block(int t0) const {
         const uint32_t x = S + (uint32_t)t0 * 2048u;
         return Block{ring, ((x >> 10) % nchunks) * 1024u + (x & 1023u), nchunks * 1024u};
     }
-    // (cos, sin) entries i0 .. i0 + 7 of the position's RoPE row, the chunk before group 0
-    __device__ __forceinline__ void rope(int i0, float2 (&cs)[8]) const {
+    // (cos, sin) entry i of the position's RoPE row (the chunk before group 0)
+    __device__ __forceinline__ float2 rope_at(int i) const {
         const uint32_t x = S - 1024u;
-        const float4* q = (const float4*)(ring + ((x >> 10) % nchunks) * 1024u + (uint32_t)i0 * 8u);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float4 v = q[e];
-            cs[2 * e] = make_float2(v.x, v.y);
-            cs[2 * e + 1] = make_float2(v.z, v.w);
-        }
+        return *(const float2*)(ring + ((x >> 10) % nchunks) * 1024u + (uint32_t)i * 8u);
     }
 };
 
@@ -369,22 +541,29 @@ template <int HD>
 struct GlobalKV {
     const uint16_t *kb, *vb;  // cache rows of (layer, b, g): [S][HD]
     int s0, last;             // first position of the split, last valid cached position
-    __device__ __forceinline__ size_t off(int t) const {
-        int j = s0 + t * AttnGeom<HD>::PPW + lane_id() / AttnGeom<HD>::LPP;
+    const float2* rope_row;   // (cos, sin) row of the position
+    __device__ __forceinline__ int pos(int t, int slot) const {
+        int j = s0 + t * AttnGeom<HD>::PPW + slot;
         if (j > last) j = last;
         if (j < 0) j = 0;
-        return (size_t)j * HD + 8 * (lane_id() % AttnGeom<HD>::LPP);
+        return j;
     }
-    const float2* rope_row;   // (cos, sin) row of the position
-    __device__ __forceinline__ void rope(int i0, float2 (&cs)[8]) const {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cs[e] = rope_row[i0 + e];
-    }
+    __device__ __forceinline__ float2 rope_at(int i) const { return rope_row[i]; }
     struct Block {
         const GlobalKV* kv;
         int t0;
-        __device__ __forceinline__ uint4 k(int t) const { return *(const uint4*)(kv->kb + kv->off(t0 + t)); }
-        __device__ __forceinline__ uint4 v(int t) const { return *(const uint4*)(kv->vb + kv->off(t0 + t)); }
+        __device__ __forceinline__ uint4 k(int t) const {
+            constexpr int LPP = AttnGeom<HD>::LPP;
+            return *(const uint4*)(kv->kb + (size_t)kv->pos(t0 + t, lane_id() / LPP) * HD + 8 * (lane_id() % LPP));
+        }
+        __device__ __forceinline__ uint4 vp(int t) const {
+            constexpr int LPP = AttnGeom<HD>::LPP;
+            return *(const uint4*)(kv->vb + (size_t)kv->pos(t0 + t, lane_id() / LPP) * HD + 8 * (lane_id() % LPP));
+        }
+        __device__ __forceinline__ void v(int t, int slot, float (&out)[AttnGeom<HD>::DPL]) const {
+            constexpr int DPL = AttnGeom<HD>::DPL;
+            load_vdims<DPL>((const char*)(kv->vb + (size_t)kv->pos(t0 + t, slot) * HD + lane_id() * DPL), out);
+        }
     };
     __device__ __forceinline__ Block block(int t0) const { return Block{this, t0}; }
 };
@@ -408,30 +587,31 @@ __device__ __forceinline__ SplitRange split_range(int p, int s, int nsplit) {
     return r;
 }
 
-__device__ __forceinline__ void lse_merge(float& m, float& l, float* acc, float m2, float l2, const float* acc2) {
+// Merge the softmax partial (m2, l2, acc2) into (m, l, acc); empty partials
+// (maximum -inf) contribute nothing.
+template <int N>
+__device__ __forceinline__ void lse_merge(float& m, float& l, float (&acc)[N], float m2, float l2,
+                                          const float (&acc2)[N]) {
     const float mm = fmaxf(m, m2);
     if (mm == -INFINITY) return;  // both empty
     const float c1 = (m == -INFINITY) ? 0.f : expf(m - mm);
     const float c2 = (m2 == -INFINITY) ? 0.f : expf(m2 - mm);
     l = l * c1 + l2 * c2;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = acc[e] * c1 + acc2[e] * c2;
+    for (int e = 0; e < N; ++e) acc[e] = acc[e] * c1 + acc2[e] * c2;
     m = mm;
 }
 
-// RoPE of the 8 dims [dl, dl+8) of one head whose raw fp32 values start at `raw`
-// (LDS): rotate-half pairs (i, i + HD/2) turn by the angles whose (cos, sin) the
-// lane holds in cs (entries dl mod HD/2 .. + 7 of the position's table row).
-template <int HD>
-__device__ __forceinline__ void rope8(const float* raw, const float2 (&cs)[8], int dl, float* out) {
+// Rotate-half RoPE of dim i of one head whose raw fp32 values start at `raw`
+// (LDS): pair (i, i + HD/2) turns by the angle of table entry i mod HD/2.  Every
+// read is issued on both halves' paths (no branch around a load), so the reads
+// of all dims overlap.
+template <int HD, class KV>
+__device__ __forceinline__ float rope_dim(const float* raw, const KV& kv, int i) {
     constexpr int half = HD / 2;
-    const bool lo = dl < half;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int i = dl + e, ii = lo ? i : i - half;
-        const float a = raw[ii], b = raw[ii + half];
-        out[e] = lo ? fmaf(a, cs[e].x, -(b * cs[e].y)) : fmaf(a, cs[e].y, b * cs[e].x);
-    }
+    const float x = raw[i], y = raw[i ^ half];  // i ^ half: the partner dim
+    const float2 cs = kv.rope_at(i & (half - 1));
+    return i < half ? fmaf(x, cs.x, -(y * cs.y)) : fmaf(y, cs.y, x * cs.x);
 }
 
 // Sum over the groups of `LPP` consecutive lanes (8 or 16) with DPP: quad
@@ -447,6 +627,41 @@ __device__ __forceinline__ float group_sum_dpp(float v) {
     return v;
 }
 
+// group_sum_dpp of N values at once (steps interleaved, results identical).
+template <int LPP, int N>
+__device__ __forceinline__ void group_sum_dpp_n(float (&v)[N]) {
+    static_assert(LPP == 8 || LPP == 16, "8 or 16 lanes per position");
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += __builtin_amdgcn_update_dpp(0.0f, v[i], 0xB1, 0xF, 0xF, false);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += __builtin_amdgcn_update_dpp(0.0f, v[i], 0x4E, 0xF, 0xF, false);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += __builtin_amdgcn_update_dpp(0.0f, v[i], 0x141, 0xF, 0xF, false);
+    if (LPP == 16) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] += __builtin_amdgcn_update_dpp(0.0f, v[i], 0x140, 0xF, 0xF, false);
+    }
+}
+
+// wave_maxf of N values at once (steps interleaved, results identical).
+template <int N>
+__device__ __forceinline__ void wave_max_n(float (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], __builtin_amdgcn_update_dpp(-INFINITY, v[i], 0xB1, 0xF, 0xF, false));
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], __builtin_amdgcn_update_dpp(-INFINITY, v[i], 0x4E, 0xF, 0xF, false));
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], __builtin_amdgcn_update_dpp(-INFINITY, v[i], 0x141, 0xF, 0xF, false));
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], __builtin_amdgcn_update_dpp(-INFINITY, v[i], 0x140, 0xF, 0xF, false));
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], __builtin_amdgcn_update_dpp(-INFINITY, v[i], 0x142, 0xA, 0xF, false));
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], __builtin_amdgcn_update_dpp(-INFINITY, v[i], 0x143, 0xC, 0xF, false));
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 63));
+}
+
 // Maximum over the 64 lanes (DPP tree as wave_total), returned to every lane.
 __device__ __forceinline__ float wave_maxf(float v) {
     v = fmaxf(v, __builtin_amdgcn_update_dpp(-INFINITY, v, 0xB1, 0xF, 0xF, false));
@@ -458,33 +673,29 @@ __device__ __forceinline__ float wave_maxf(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// LDS floats one attention item needs: staged q/k/v, per-head scores of one
-// block of position groups (plus the group of the new position), and the
-// partials of every split when this item merges them.
-template <int HD>
-__host__ __device__ constexpr uint32_t attn_lds_floats(int G, int nsplit) {
-    return (uint32_t)((G + 2) * HD + kComputeWaves * (kAttnBlockGroups + 1) * (64 / (HD / 8)) +
-                      nsplit * G * (HD + 2) + 4);
-}
+static_assert(kAttnBlockGroups % kComputeWaves == 0, "groups of a block are dealt evenly to the waves");
 
-// Runs one attention item (sequence b, KV head g, split s) with `nw` waves of the
-// workgroup, which all call it.  Wave j handles q head j of the group end to end:
-// it scores every position of the split block by block (block = kAttnBlockGroups
-// groups of PPW positions; lanes = (position slot, 8 dims), the per-position dot
-// summed over the slot's lanes with DPP), exponentiates against the running
-// maximum (two-pass softmax inside a block, rescaled across blocks), and
-// accumulates the probability-weighted V per (slot, dims), summed over the slots
-// at the end.  `need(t)` waits for ring group t; `release(t)` frees ring groups
-// before t; `barrier()` synchronises the waves.  The new position (its K rotated
-// and rounded to bf16, appended to the cache) joins as one extra group.  Writes
-// the attention output (tagged) or, when split, the item's (max, sum, output)
-// partial; the last split to arrive merges all partials in split order.
+// Runs one attention item (sequence b, KV head g, split s) with the nw == 4 compute
+// waves of the workgroup, which all call it.
+//  1. stage the raw q (G heads), k and v of the position (tagged words);
+//  2. wave h rotates q head h, wave 0 also k; the new K (rotated) and V are
+//     rounded to bf16, appended to the cache and kept in LDS;
+//  3. block by block (kAttnBlockGroups groups), wave w scores groups t0 + w,
+//     t0 + w + 4, ... for every head, exponentiates against its running maximum
+//     and accumulates the weighted V (the new position is one extra group);
+//  4. the four wave partials of head h are merged by wave h, in wave order.
+// `need(t)` waits for ring group t; `release(t)` frees ring groups before t;
+// `barrier()` synchronises the waves.  Writes the attention output (tagged) or,
+// when split, the item's (max, sum, output) partial; the last split to arrive
+// merges all partials in split order.
 template <int HD, class KV, class Need, class Release, class Barrier, class Mark>
 __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int layer, int b, int g, int s, int p,
                                           const KV& kv, Need& need, Release& release, Barrier& barrier, float* xs,
                                           int wave, int nw, Spin& spin, Mark& mark) {
     using Geo = AttnGeom<HD>;
-    constexpr int LPP = Geo::LPP, PPW = Geo::PPW;
+    constexpr int LPP = Geo::LPP, PPW = Geo::PPW, DPL = Geo::DPL;
+    constexpr int GW = kAttnBlockGroups / kComputeWaves;  // groups per wave per block
+    static_assert(GW * PPW <= kAttnWavePositions, "a wave's positions of one block fit its score area");
     const int lane = lane_id();
     const int ps = lane / LPP;
     const int dl = 8 * (lane % LPP);
@@ -494,136 +705,253 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
     const uint32_t tag_in = phase_tag(tag0, layer, 0) ^ ((P.inject && layer == 0) ? 0x80000000u : 0u);
     const uint32_t tag_out = phase_tag(tag0, layer, 1);
     const uint32_t stride = HD + 2;
-    constexpr int kSlots = (kAttnBlockGroups + 1) * PPW;
+
+    // LDS: raw q [G][HD], k [HD], v [HD]; rotated q [G][HD]; new K and V (bf16);
+    // scores [wave][64][4]; wave partials [wave][G][2 + 4 HD]; split partials [split][G][HD + 2].
+    float* q_raw = xs;
+    float* k_raw = q_raw + G * HD;
+    float* v_raw = k_raw + HD;
+    float* q_rot = v_raw + HD;
+    uint16_t* k_new = (uint16_t*)(q_rot + G * HD);
+    uint16_t* v_new = k_new + HD;
+    float* sc = (float*)(v_new + HD) + wave * kAttnWavePositions * kMaxGroup;
+    float* wpart = (float*)(v_new + HD) + kComputeWaves * kAttnWavePositions * kMaxGroup;
+    float* spart = wpart + kComputeWaves * G * (4 * HD + 2);
+    uint32_t* flag = (uint32_t*)(spart + P.nsplit * G * stride);
 
     // the (cos, sin) row of position p (for the ring: the item's first chunk)
     if (!need(-1)) return false;
-    float2 cs[8];
-    kv.rope(dl < HD / 2 ? dl : dl - HD / 2, cs);
-    float* q_raw = xs;
-    float* k_raw = xs + G * HD;
-    float* v_raw = k_raw + HD;
-    float* sc = v_raw + HD + wave * kSlots;                // this wave's scores / weights
-    float* spart = v_raw + HD + kComputeWaves * kSlots;    // [nsplit][G][HD + 2]
-    uint32_t* flag = (uint32_t*)(spart + P.nsplit * G * stride);
     {
         const uint64_t* row = P.qkv + (size_t)b * P.qkv_rows;
-        float ss = 0.f;
-        bool ok = stage_tagged<false>(row + (size_t)g * G * HD, (uint32_t)(G * HD), tag_in, q_raw, nullptr, wave, nw,
-                                      spin, ss);
-        ok = ok && stage_tagged<false>(row + (size_t)(P.Hq + g) * HD, HD, tag_in, k_raw, nullptr, wave, nw, spin, ss);
-        ok = ok && stage_tagged<false>(row + (size_t)(P.Hq + P.Hkv + g) * HD, HD, tag_in, v_raw, nullptr, wave, nw,
-                                       spin, ss);
-        if (!ok) return false;
+        float ss[1] = {0.f};
+        const StageSeg sg[3] = {{row + (size_t)g * G * HD, q_raw, nullptr, (uint32_t)(G * HD), 1u, 0u, 0u, tag_in},
+                                {row + (size_t)(P.Hq + g) * HD, k_raw, nullptr, (uint32_t)HD, 1u, 0u, 0u, tag_in},
+                                {row + (size_t)(P.Hq + P.Hkv + g) * HD, v_raw, nullptr, (uint32_t)HD, 1u, 0u, 0u, tag_in}};
+        if (!stage_segs<kStagePassWords, 1, 3>(sg, wave, nw, spin, ss)) return false;
     }
     if (!barrier()) return false;
     mark(0);
 
-    // Rotations on every path (waves without a q head rotate a neighbour's values,
-    // unused): the (cos, sin) loads are consumed here, before any store, so no
-    // load stays pending past this instruction.
-    const int j = wave;  // q head of this wave
-    float q[8];
-    rope8<HD>(q_raw + j * HD, cs, dl, q);
-    // the new position: K rotated, K and V rounded to bf16 as the cache holds them
-    float kr[8];
-    rope8<HD>(k_raw, cs, dl, kr);
-    const uint4 kn = make_uint4(pack_bf2(kr[0], kr[1]), pack_bf2(kr[2], kr[3]), pack_bf2(kr[4], kr[5]),
-                                pack_bf2(kr[6], kr[7]));
-    const uint4 vn = make_uint4(pack_bf2(v_raw[dl], v_raw[dl + 1]), pack_bf2(v_raw[dl + 2], v_raw[dl + 3]),
-                                pack_bf2(v_raw[dl + 4], v_raw[dl + 5]), pack_bf2(v_raw[dl + 6], v_raw[dl + 7]));
-    if (R.has_new && wave == 0 && ps == 0) {  // KV append at position p (read by later steps)
-        const size_t row = ((((size_t)layer * P.kv_b + b) * P.Hkv + g) * P.S + p) * HD + dl;
-        *(uint4*)(P.kcache + row) = kn;
-        *(uint4*)(P.vcache + row) = vn;
-    }
-    const int ngr = R.ngroups + (R.has_new ? 1 : 0);  // ring groups, then the new position's group
-    float m_run = -INFINITY, l_run = 0.f, acc[8];
+    // rotations (lane -> dims lane * DPL + j) and the KV append
+    if (wave < G) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    if (j < G) {
-        for (int t0 = 0; t0 < ngr; t0 += kAttnBlockGroups) {
-            const int t1 = min(ngr, t0 + kAttnBlockGroups);
-            const auto blk = kv.block(t0);
-            // every ring group of the block resident (one wait per block)
-            if (t0 < R.ngroups && !need(min(t1, R.ngroups) - 1)) return false;
-            // scores of the block, four groups per step so their LDS reads overlap
-            float mx = -INFINITY;
-            for (int t = t0; t < t1; t += 4) {
-                uint4 kp[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int tt = t + u;
-                    kp[u] = (tt < R.ngroups && tt < t1) ? blk.k(tt - t0) : kn;
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int tt = t + u;
-                    if (tt < t1) {
-                        float v = group_sum_dpp<LPP>(qk8(q, kp[u])) * scale;
-                        const bool valid = tt == R.ngroups ? ps == 0 : tt * PPW + ps < R.ncached;
-                        v = valid ? v : -INFINITY;
-                        if (dl == 0) sc[(tt - t0) * PPW + ps] = v;
-                        mx = fmaxf(mx, v);
-                    }
-                }
-            }
-            mx = wave_maxf(mx);
-            const float m_new = fmaxf(m_run, mx);
-            // weights against the running maximum, and their sum
-            float l_blk = 0.f;
-            for (int i = lane; i < (t1 - t0) * PPW; i += 64) {
-                const float v = sc[i];
-                const float e = v == -INFINITY ? 0.f : expf(v - m_new);
-                sc[i] = e;
-                l_blk += e;
-            }
-            l_blk = wave_total(l_blk);
-            // rescale what earlier blocks accumulated, then add this block's weighted V
-            const float c = m_run == -INFINITY ? 0.f : expf(m_run - m_new);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] *= c;
-            l_run = l_run * c + l_blk;
-            m_run = m_new;
-            for (int t = t0; t < t1; t += 4) {
-                uint4 vp[4];
-                float w[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int tt = t + u;
-                    vp[u] = (tt < R.ngroups && tt < t1) ? blk.v(tt - t0) : vn;
-                    w[u] = tt < t1 ? sc[(tt - t0) * PPW + ps] : 0.f;
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    acc[0] = fmaf(w[u], bf_lo(vp[u].x), acc[0]);
-                    acc[1] = fmaf(w[u], bf_hi(vp[u].x), acc[1]);
-                    acc[2] = fmaf(w[u], bf_lo(vp[u].y), acc[2]);
-                    acc[3] = fmaf(w[u], bf_hi(vp[u].y), acc[3]);
-                    acc[4] = fmaf(w[u], bf_lo(vp[u].z), acc[4]);
-                    acc[5] = fmaf(w[u], bf_hi(vp[u].z), acc[5]);
-                    acc[6] = fmaf(w[u], bf_lo(vp[u].w), acc[6]);
-                    acc[7] = fmaf(w[u], bf_hi(vp[u].w), acc[7]);
-                }
-            }
-            release(min(t1, R.ngroups));
+        for (int j = 0; j < DPL; ++j) {
+            const int i = lane * DPL + j;
+            q_rot[wave * HD + i] = rope_dim<HD>(q_raw + wave * HD, kv, i);
         }
-        // sum the position slots (lanes with equal dims)
+    }
+    if (wave == 0) {
+        uint32_t kw = 0, vw = 0;
 #pragma unroll
-        for (int msk = LPP; msk < 64; msk <<= 1)
+        for (int j = 0; j < DPL; ++j) {
+            const int i = lane * DPL + j;
+            const uint32_t kb16 = f_to_bf(rope_dim<HD>(k_raw, kv, i));
+            const uint32_t vb16 = f_to_bf(v_raw[i]);
+            k_new[i] = (uint16_t)kb16;
+            v_new[i] = (uint16_t)vb16;
+            kw |= kb16 << (16 * j);
+            vw |= vb16 << (16 * j);
+        }
+        if (R.has_new) {  // KV append at position p (read by later steps)
+            const size_t row = ((((size_t)layer * P.kv_b + b) * P.Hkv + g) * P.S + p) * HD + lane * DPL;
+            if constexpr (DPL == 1) {
+                P.kcache[row] = (uint16_t)kw;
+                P.vcache[row] = (uint16_t)vw;
+            } else {
+                *(uint32_t*)(P.kcache + row) = kw;
+                *(uint32_t*)(P.vcache + row) = vw;
+            }
+        }
+    }
+    if (!barrier()) return false;
+
+    // this lane's 8 dims of every rotated q head, and of the new K and V
+    float q[kMaxGroup][8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], msk, 64);
-    } else {
-        release(R.ngroups);
+    for (int h = 0; h < kMaxGroup; ++h) {
+        const int hh = h < G ? h : 0;
+        const float4 a = *(const float4*)(q_rot + hh * HD + dl);
+        const float4 c = *(const float4*)(q_rot + hh * HD + dl + 4);
+        q[h][0] = a.x; q[h][1] = a.y; q[h][2] = a.z; q[h][3] = a.w;
+        q[h][4] = c.x; q[h][5] = c.y; q[h][6] = c.z; q[h][7] = c.w;
+    }
+    const uint4 kn = *(const uint4*)(k_new + dl);
+    const uint4 vn = *(const uint4*)(v_new + dl);
+
+    const int ngr = R.ngroups + (R.has_new ? 1 : 0);  // ring groups, then the new position's group
+    // running maximum and sum per head (wave-uniform), weighted V per (slot, 8 dims)
+    float m_run[kMaxGroup], l_run[kMaxGroup], acc[kMaxGroup][8];
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+        m_run[h] = -INFINITY;
+        l_run[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    }
+    for (int t0 = 0; t0 < ngr; t0 += kAttnBlockGroups) {
+        const int t1 = min(ngr, t0 + kAttnBlockGroups);
+        const auto blk = kv.block(t0);
+        // every ring group of the block resident (one wait per block)
+        if (t0 < R.ngroups && !need(min(t1, R.ngroups) - 1)) return false;
+        // this wave's groups of the block: t0 + wave + 4 i, i < ngw
+        const int first = t0 + wave;
+        const int ngw = first < t1 ? (t1 - first + kComputeWaves - 1) / kComputeWaves : 0;
+        // scores of every head, two groups per step.  Loads are issued for every
+        // step, from a clamped group when the step is past the wave's groups or is
+        // the new position, and the values selected afterwards.
+        float mx[kMaxGroup];
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h) mx[h] = -INFINITY;
+        for (int i = 0; i < ngw; i += 2) {
+            uint4 kp[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int tt = first + kComputeWaves * (i + u);
+                const uint4 kr = blk.k(min(tt, t1 - 1) - t0);
+                kp[u] = (tt < R.ngroups) ? kr : kn;
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int tt = first + kComputeWaves * (i + u);
+                const bool valid = (i + u < ngw) && (tt == R.ngroups ? ps == 0 : tt * PPW + ps < R.ncached);
+                float v4[kMaxGroup];
+#pragma unroll
+                for (int h = 0; h < kMaxGroup; ++h) v4[h] = qk8(q[h], kp[u]);
+                group_sum_dpp_n<LPP, kMaxGroup>(v4);
+#pragma unroll
+                for (int h = 0; h < kMaxGroup; ++h) {
+                    const float v = (valid && h < G) ? v4[h] * scale : -INFINITY;
+                    v4[h] = v;
+                    mx[h] = fmaxf(mx[h], v);
+                }
+                if (dl == 0 && i + u < ngw)
+                    *(float4*)(sc + ((i + u) * PPW + ps) * kMaxGroup) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+            }
+        }
+        const int npw = ngw * PPW;  // this wave's positions in the block
+        float m_new[kMaxGroup], c[kMaxGroup];
+        wave_max_n<kMaxGroup>(mx);
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h) {
+            m_new[h] = fmaxf(m_run[h], mx[h]);
+            c[h] = m_run[h] == -INFINITY ? 0.f : expf(m_run[h] - m_new[h]);
+        }
+        // weights against the running maximum (lane = position), and their sums
+        float l_blk[kMaxGroup];
+        {
+            float4 e4 = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (lane < npw) {
+                const float4 v = *(const float4*)(sc + lane * kMaxGroup);
+                e4.x = v.x == -INFINITY ? 0.f : expf(v.x - m_new[0]);
+                e4.y = v.y == -INFINITY ? 0.f : expf(v.y - m_new[1]);
+                e4.z = v.z == -INFINITY ? 0.f : expf(v.z - m_new[2]);
+                e4.w = v.w == -INFINITY ? 0.f : expf(v.w - m_new[3]);
+                *(float4*)(sc + lane * kMaxGroup) = e4;
+            }
+            l_blk[0] = e4.x;
+            l_blk[1] = e4.y;
+            l_blk[2] = e4.z;
+            l_blk[3] = e4.w;
+            wave_total_n<kMaxGroup>(l_blk);
+        }
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h) {
+            l_run[h] = l_run[h] * c[h] + l_blk[h];
+            m_run[h] = m_new[h];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] *= c[h];
+        }
+        // weighted V: lane (slot, 8 dims) takes its slot's position of each group
+        for (int i = 0; i < ngw; i += 2) {
+            uint4 vp[2];
+            float4 w4[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int tt = first + kComputeWaves * (i + u);
+                const uint4 vr = blk.vp(min(tt, t1 - 1) - t0);
+                const float4 w = *(const float4*)(sc + (min(i + u, ngw - 1) * PPW + ps) * kMaxGroup);
+                vp[u] = (tt < R.ngroups) ? vr : vn;
+                w4[u] = (i + u < ngw) ? w : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const float wv[4] = {w4[u].x, w4[u].y, w4[u].z, w4[u].w};
+                const float v8[8] = {bf_lo(vp[u].x), bf_hi(vp[u].x), bf_lo(vp[u].y), bf_hi(vp[u].y),
+                                     bf_lo(vp[u].z), bf_hi(vp[u].z), bf_lo(vp[u].w), bf_hi(vp[u].w)};
+#pragma unroll
+                for (int h = 0; h < kMaxGroup; ++h)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(wv[h], v8[e], acc[h][e]);
+            }
+        }
+        release(min(t1, R.ngroups));
     }
     mark(1);
+
+    // Wave partials -> LDS: the slots of a 16-lane row are summed with DPP (8
+    // lanes per position: the two slots of the row), then each row's 8-dim pieces
+    // are stored; [wave][head]: maximum, sum, 4 rows of HD.
+    constexpr uint32_t wstride = 2 + 4 * HD;
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (LPP == 8) acc[h][e] += __builtin_amdgcn_update_dpp(0.0f, acc[h][e], 0x128, 0xF, 0xF, false);  // row_ror:8
+    const int row = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+        if (h < G) {
+            float* dst = wpart + (size_t)(wave * G + h) * wstride;
+            if (lane == 0) {
+                dst[0] = m_run[h];
+                dst[1] = l_run[h];
+            }
+            if (LPP == 16 || (lane & 8) == 0) {
+                float* r = dst + 2 + row * HD + dl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) r[e] = acc[h][e];
+            }
+        }
+    }
+    if (!barrier()) return false;
+    const int j = wave;  // q head this wave merges and writes (lane -> dims lane * DPL + e)
+    float mm = -INFINITY, ll = 0.f, aa[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) aa[e] = 0.f;
+    if (j < G) {
+        float pm[kComputeWaves], pl[kComputeWaves], pa[kComputeWaves][DPL];
+#pragma unroll
+        for (int w = 0; w < kComputeWaves; ++w) {
+            const float* src = wpart + (size_t)(w * G + j) * wstride;
+            pm[w] = src[0];
+            pl[w] = src[1];
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) {
+                const int d = lane * DPL + e;
+                pa[w][e] = (src[2 + d] + src[2 + HD + d]) + (src[2 + 2 * HD + d] + src[2 + 3 * HD + d]);
+            }
+        }
+        // one common maximum, then every wave's share scaled to it (waves whose
+        // maximum is -inf saw no position and contribute nothing)
+#pragma unroll
+        for (int w = 0; w < kComputeWaves; ++w) mm = fmaxf(mm, pm[w]);
+        if (mm != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kComputeWaves; ++w) {
+                const float cw = pm[w] == -INFINITY ? 0.f : expf(pm[w] - mm);
+                ll = fmaf(pl[w], cw, ll);
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) aa[e] = fmaf(pa[w][e], cw, aa[e]);
+            }
+        }
+    }
     uint64_t* out_b = P.attn + (size_t)b * P.Hq * HD;
     if (P.nsplit == 1) {
-        if (j < G && ps == 0) {
-            const float inv = 1.0f / l_run;
-            uint64_t* o = out_b + (size_t)(g * G + j) * HD + dl;
+        if (j < G) {
+            const float inv = 1.0f / ll;
+            uint64_t* o = out_b + (size_t)(g * G + j) * HD + lane * DPL;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) st_tagged(o + e, acc[e] * inv, tag_out);
+            for (int e = 0; e < DPL; ++e) st_tagged(o + e, aa[e] * inv, tag_out);
         }
         mark(2);
         return true;
@@ -632,14 +960,14 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
     const size_t pstride = (size_t)G * stride;
     uint64_t* part = P.attn_part + (((size_t)b * P.Hkv + g) * P.nsplit) * pstride;
     uint32_t* tk = P.attn_ticket + (((size_t)layer * P.B + b) * P.Hkv + g) * kCtrStride;
-    if (j < G && ps == 0) {
+    if (j < G) {
         uint64_t* dst = part + (size_t)s * pstride + (size_t)j * stride;
-        if (dl == 0) {
-            st_tagged(dst, m_run, tag_out);
-            st_tagged(dst + 1, l_run, tag_out);
+        if (lane == 0) {
+            st_tagged(dst, mm, tag_out);
+            st_tagged(dst + 1, ll, tag_out);
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) st_tagged(dst + 2 + dl + e, acc[e], tag_out);
+        for (int e = 0; e < DPL; ++e) st_tagged(dst + 2 + lane * DPL + e, aa[e], tag_out);
     }
     if (!barrier()) return false;  // every head's partial is issued
     if (wave == 0) {
@@ -655,27 +983,27 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
     }
     // last arrival: every wave stages the partials, wave j merges head j in split order
     {
-        float ss = 0.f;
-        if (!stage_tagged<false>(part, (uint32_t)(P.nsplit * pstride), tag_out, spart, nullptr, wave, nw, spin, ss))
-            return false;
+        float ss[1] = {0.f};
+        const StageSeg sg[1] = {{part, spart, nullptr, (uint32_t)(P.nsplit * pstride), 1u, 0u, 0u, tag_out}};
+        if (!stage_segs<kStagePassWords, 1, 1>(sg, wave, nw, spin, ss)) return false;
     }
     if (!barrier()) return false;
-    if (j < G && ps == 0) {
+    if (j < G) {
         const float* s0p = spart + (size_t)j * stride;
-        float mm = s0p[0], ll = s0p[1], aa[8];
+        float m2 = s0p[0], l2 = s0p[1], a2[DPL];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) aa[e] = s0p[2 + dl + e];
+        for (int e = 0; e < DPL; ++e) a2[e] = s0p[2 + lane * DPL + e];
         for (int sp = 1; sp < P.nsplit; ++sp) {
             const float* src = spart + (size_t)sp * pstride + (size_t)j * stride;
-            float a2[8];
+            float a3[DPL];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a2[e] = src[2 + dl + e];
-            lse_merge(mm, ll, aa, src[0], src[1], a2);
+            for (int e = 0; e < DPL; ++e) a3[e] = src[2 + lane * DPL + e];
+            lse_merge(m2, l2, a2, src[0], src[1], a3);
         }
-        const float inv = 1.0f / ll;
-        uint64_t* o = out_b + (size_t)(g * G + j) * HD + dl;
+        const float inv = 1.0f / l2;
+        uint64_t* o = out_b + (size_t)(g * G + j) * HD + lane * DPL;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) st_tagged(o + e, aa[e] * inv, tag_out);
+        for (int e = 0; e < DPL; ++e) st_tagged(o + e, a2[e] * inv, tag_out);
     }
     if (wave == 0 && lane == 0) __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     mark(2);

@@ -28,8 +28,20 @@ constexpr int kMaxBatch = 8;
 constexpr int kMaxGroup = 4;                        // q heads per KV head
 constexpr uint32_t kMaxResidRows = 64;              // O / DOWN rows per instruction
 constexpr uint32_t kCtrStride = 32;                 // uint32 per counter (128 B apart)
-constexpr int kStageWords = 16;                     // tagged words per lane in flight when staging
+constexpr int kStageWords = 16;                     // tagged words per lane in flight (argmax reduce)
+constexpr int kStagePassWords = 4;                  // tagged words per lane per staging pass (two in flight)
+constexpr int kStagePassWordsWide = 8;              // the same for the wide inputs of O and DOWN
 constexpr int kAttnBlockGroups = 32;                // KV position groups (2 KB each) one attention pass holds
+constexpr int kAttnWavePositions = 64;              // positions one wave scores per block (its score area)
+
+// LDS floats one attention item uses: raw q (G heads), k and v; rotated q; the new
+// K and V as bf16; the scores of every wave ([wave][position][kMaxGroup]); the wave
+// partials ([wave][G]: maximum, sum, four 16-lane rows of HD); when the item
+// merges splits, the split partials ([split][G]: maximum, sum, HD); one flag word.
+__host__ __device__ constexpr size_t attn_lds_floats(int G, int HD, int nsplit) {
+    return (size_t)(2 * G * HD + 3 * HD + kComputeWaves * kAttnWavePositions * kMaxGroup +
+                    kComputeWaves * G * (4 * HD + 2) + nsplit * G * (HD + 2) + 4);
+}
 
 enum Op : uint16_t {
     OP_QKV = 1,     // RMSNorm + rows of [Wq; Wk; Wv] -> raw q/k/v (fp32)

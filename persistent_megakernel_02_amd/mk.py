@@ -24,7 +24,7 @@ MK_MODE_MEGAKERNEL, MK_MODE_GRAPH = 0, 1
 EXPORTS = ["mk_query_sizes", "mk_create", "mk_kv_layout", "mk_prefill", "mk_set_context_len", "mk_decode_step",
            "mk_get_context_len", "mk_reset", "mk_debug_inject", "mk_status_string", "mk_last_error",
            "mk_plan_inspect", "mk_kernels_per_step", "mk_destroy", "mk_bench_stream_read", "mk_bench_copy",
-           "mk_bench_sync", "mk_read_trace", "mk_bench_lds_stream", "mk_bench_pingpong", "mk_bench_edge"]
+           "mk_bench_sync", "mk_read_trace", "mk_bench_lds_stream", "mk_bench_pingpong", "mk_bench_edge", "mk_bench_lds_contention"]
 
 
 class mk_model_config(ctypes.Structure):
@@ -88,11 +88,12 @@ def lib():
         L.mk_bench_sync.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
         L.mk_bench_pingpong.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
         L.mk_bench_edge.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, sz, vp, vp, vp]
+        L.mk_bench_lds_contention.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, sz, vp, vp]
         L.mk_read_trace.argtypes = [vp, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(i32)]
         L.mk_bench_lds_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, sz, ctypes.c_int, vp, vp]
         for n in ("mk_query_sizes", "mk_create", "mk_kv_layout", "mk_prefill", "mk_set_context_len",
                   "mk_get_context_len", "mk_decode_step", "mk_reset", "mk_debug_inject", "mk_plan_inspect",
-                  "mk_destroy", "mk_bench_stream_read", "mk_bench_copy", "mk_bench_sync", "mk_read_trace", "mk_bench_lds_stream", "mk_bench_pingpong", "mk_bench_edge"):
+                  "mk_destroy", "mk_bench_stream_read", "mk_bench_copy", "mk_bench_sync", "mk_read_trace", "mk_bench_lds_stream", "mk_bench_pingpong", "mk_bench_edge", "mk_bench_lds_contention"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -247,7 +248,7 @@ class Decoder:
         self._check(lib().mk_debug_inject(self.h, fault, arg), "mk_debug_inject")
 
     def read_trace(self):
-        """Timeline of the last megakernel step: uint32 [n_cu, records, 8] (see mk.h)."""
+        """Timeline of the last megakernel step: uint32 [n_cu, records, TRACE_WORDS] (see mk.h)."""
         n, per = ctypes.c_size_t(0), ctypes.c_int32(0)
         self._check(lib().mk_read_trace(self.h, None, 0, ctypes.byref(n), ctypes.byref(per)), "mk_read_trace")
         buf = np.zeros(n.value // 4, np.uint32)
