@@ -193,3 +193,62 @@ def test_llama1b_b1_graph_matches_megakernel_bitwise(llama1b):
         d.close()
     for x, y in zip(outs[0][1], outs[1][1]):
         assert np.array_equal(x, y)
+
+
+def _fill_context(cfg, orc, dec, ctx, seed):
+    """Synthetic context: positions < ctx of every sequence get seeded N(0, 1) bf16
+    K and V, in the oracle's cache and (the same values) in the device cache."""
+    torch = _torch()
+    orc.set_context(ctx, lambda k, v: I.fill_kv_context(cfg, k, v, orc.batch, ctx, seed))
+    kd, vd = dec.kv_views()
+    kd.copy_(torch.from_numpy(orc.k_cache.view(np.int16)).to(kd.device))
+    vd.copy_(torch.from_numpy(orc.v_cache.view(np.int16)).to(vd.device))
+    dec.set_context_len([ctx] * orc.batch)
+    torch.cuda.synchronize()
+
+
+def test_llama1b_b2_long_context():
+    """Batch 2 on the 1B shape over a 2000-position synthetic context: the
+    attention of every (sequence, KV head) is split over several compute units
+    and merged; greedy tokens and logits are checked for 6 steps."""
+    cfg = I.LLAMA_1B
+    w = I.make_weights(cfg, seed=4)
+    B, ctx, steps, S = 2, 2000, 6, 2016
+    start = I.make_prompt(cfg, B, 1, seed=4)[:, 0]
+    orc = O.Oracle(cfg, w, B, S)
+    print("case 1B b2 ctx=2000 megakernel", flush=True)
+    d = _decoder(cfg, w, B, S, 0)
+    _fill_context(cfg, orc, d, ctx, seed=4)
+    torch = _torch()
+    ref_t, ref_l, got_t, got_l = [], [], [], []
+    tok = start.astype(np.int32)
+    for _ in range(steps):
+        nxt, logits = orc.step(tok)
+        g_n, g_l = d.decode_step(torch.from_numpy(tok).to(d.device))
+        ref_t.append(nxt.copy())
+        ref_l.append(logits.copy())
+        got_t.append(g_n.cpu().numpy().copy())
+        got_l.append(g_l.cpu().numpy().copy())
+        tok = nxt.astype(np.int32)
+    _, near = compare(ref_t, ref_l, got_t, got_l, "1B b2 ctx=2000")
+    assert near <= 1
+    assert d.context_len() == [ctx + steps] * B
+    d.close()
+
+
+def test_llama8b_b1_prefix():
+    """The 8B shape (32 layers, hidden 4096, head_dim 128, untied head) at batch
+    1: 6 prompt tokens and 4 greedy steps against the oracle."""
+    cfg = I.LLAMA_8B
+    t0 = time.time()
+    w = I.make_weights(cfg, seed=0)
+    prompt = I.make_prompt(cfg, 1, 6, seed=0)
+    print(f"8B weights generated in {time.time() - t0:.1f}s", flush=True)
+    rt_, rl = oracle_run(cfg, w, prompt, 4, 16)
+    print(f"8B oracle done in {time.time() - t0:.1f}s", flush=True)
+    print("case 8B b1 megakernel", flush=True)
+    d = _decoder(cfg, w, 1, 16, 0)
+    gt, gl = gpu_run(d, prompt, rt_, 4)
+    _, near = compare(rt_, rl, gt, gl, "8B b1 megakernel")
+    assert near <= 1
+    d.close()
