@@ -54,15 +54,17 @@ __device__ __forceinline__ const uint16_t* seq_row(const Params& P, const DevLay
 
 // Rows [0, nrows) of the block in batches of R rows per wave (rows of a short
 // last batch repeat its first row; their results are not used).
+// `col0`: first column of the rows (a column slice of DOWN), rb: bytes per row used.
 template <int B, int R, int OP, class X, class Epi>
 __device__ __forceinline__ void conv_rows(const Params& P, const DevLayer& Lw, uint32_t begin, uint32_t nrows,
-                                          uint32_t rb, const X& x, Epi& epi) {
+                                          uint32_t rb, const X& x, Epi& epi, uint32_t col0 = 0) {
     const int wave = threadIdx.x >> 6;
     for (uint32_t r0 = (uint32_t)wave * R; r0 < nrows; r0 += (uint32_t)R * kConvWaves) {
         const uint32_t nr = min((uint32_t)R, nrows - r0);
         GlobalBatch<R> rows;
 #pragma unroll
-        for (int i = 0; i < R; ++i) rows.row[i] = seq_row<OP>(P, Lw, begin, r0 + ((uint32_t)i < nr ? (uint32_t)i : 0u));
+        for (int i = 0; i < R; ++i)
+            rows.row[i] = seq_row<OP>(P, Lw, begin, r0 + ((uint32_t)i < nr ? (uint32_t)i : 0u)) + col0;
         float res[R][B];
         rows_dot<B, R>(rows, (int)(rb >> 4), x, res);
         epi(r0, nr, res);
@@ -71,11 +73,11 @@ __device__ __forceinline__ void conv_rows(const Params& P, const DevLayer& Lw, u
 
 template <int B, int OP, class X, class Epi>
 __device__ __forceinline__ void conv_rows_auto(const Params& P, const DevLayer& Lw, uint32_t begin, uint32_t nrows,
-                                               uint32_t rb, const X& x, Epi& epi) {
-    const int R = rows_per_batch(rb);
-    if (R >= 4) conv_rows<B, 4, OP>(P, Lw, begin, nrows, rb, x, epi);
-    else if (R == 2 || OP == OP_GATEUP) conv_rows<B, 2, OP>(P, Lw, begin, nrows, rb, x, epi);
-    else conv_rows<B, 1, OP>(P, Lw, begin, nrows, rb, x, epi);
+                                               uint32_t rb, const X& x, Epi& epi, uint32_t col0 = 0) {
+    const int R = rows_per_batch(rb, B);
+    if (R >= 4) conv_rows<B, 4, OP>(P, Lw, begin, nrows, rb, x, epi, col0);
+    else if (R == 2 || OP == OP_GATEUP) conv_rows<B, 2, OP>(P, Lw, begin, nrows, rb, x, epi, col0);
+    else conv_rows<B, 1, OP>(P, Lw, begin, nrows, rb, x, epi, col0);
 }
 
 // RMSNorm + rows: QKV, GATEUP (row pairs) and the LM head.
@@ -121,8 +123,9 @@ __global__ void __launch_bounds__(kConvThreads) k_norm_gemv(Params P, StepArgs A
     if (OP == OP_QKV) {
         const uint32_t tag_out = phase_tag(A.tag0, layer, 0);
         auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
-            for (uint32_t i = 0; i < nr; ++i)
-                if (lane < B)
+            #pragma unroll
+            for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i)
+                if (i < nr && lane < B)
                     st_tagged(P.qkv + (size_t)lane * P.qkv_rows + begin + r0 + i,
                               pick<B>(res[i], lane) * pick<B>(r, lane), tag_out);
         };
@@ -130,7 +133,9 @@ __global__ void __launch_bounds__(kConvThreads) k_norm_gemv(Params P, StepArgs A
     } else if (OP == OP_GATEUP) {
         const uint32_t tag_out = phase_tag(A.tag0, layer, 3);
         auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
-            for (uint32_t i = 0; i + 1 < nr; i += 2) {
+            #pragma unroll
+            for (uint32_t i = 0; i + 1 < (uint32_t)(sizeof(res) / sizeof(res[0])); i += 2) {
+                if (i + 1 >= nr) break;
                 const uint32_t f = begin + (r0 + i) / 2u;
                 if (lane < B) {
                     const float rr = pick<B>(r, lane);
@@ -150,7 +155,9 @@ __global__ void __launch_bounds__(kConvThreads) k_norm_gemv(Params P, StepArgs A
             best_i[b] = 0x7FFFFFFF;
         }
         auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
-            for (uint32_t i = 0; i < nr; ++i) {
+            #pragma unroll
+            for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i) {
+                if (i >= nr) break;
                 const int32_t row = (int32_t)(begin + r0 + i);
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
@@ -187,32 +194,50 @@ __global__ void __launch_bounds__(kConvThreads) k_proj(Params P, StepArgs A, int
     const uint32_t tag_out = is_down ? phase_tag(A.tag0, layer, 4) : phase_tag(A.tag0, layer, 2);
     const uint32_t begin = blockIdx.x * kRowsPerBlock;
     const uint32_t count = min(kRowsPerBlock, (uint32_t)P.d - begin);
-    float* hres = xs + B * K;
-    float ss[1] = {0.f};
-    const StageSeg sx = {is_down ? P.act : P.attn, xs, nullptr, K, (uint32_t)B, K, K, tag_x};
-    if (!is_down && layer == 0) {
+    // DOWN runs over P.down_slices column slices of its input; partial sums wait in LDS
+    const uint32_t ns = is_down ? (uint32_t)P.down_slices : 1u, Ks = K / ns;
+    float* hres = xs + B * Ks;
+    float* part = hres + B * count;
+    for (uint32_t ks = 0; ks < ns; ++ks) {
+        if (ks > 0) __syncthreads();  // every wave is done with the previous slice
+        float ss[1] = {0.f};
+        const StageSeg sx = {(is_down ? P.act : P.attn) + ks * Ks, xs, nullptr, Ks, (uint32_t)B, K, Ks, tag_x};
+        if (ks > 0) {
+            const StageSeg sg[1] = {sx};
+            if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kConvWaves, spin, ss)) return;
+        } else if (!is_down && layer == 0) {
 #pragma unroll
-        for (int b = 0; b < B; ++b)
-            stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * P.d + begin, count, hres + b * count,
-                       nullptr, wave, kConvWaves, ss[0]);
-        const StageSeg sg[1] = {sx};
-        if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kConvWaves, spin, ss)) return;
-    } else {
-        const StageSeg sg[2] = {sx, {P.h + begin, hres, nullptr, count, (uint32_t)B, (uint32_t)P.d, count, tag_res}};
-        if (!stage_segs<kStagePassWordsWide, 1, 2>(sg, wave, kConvWaves, spin, ss)) return;
-    }
-    __syncthreads();
-    const XLds x{xs, K};
-    auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
-        for (uint32_t i = 0; i < nr; ++i) {
-            const uint32_t row = begin + r0 + i;
-            if (lane < B)
-                st_tagged(P.h + (size_t)lane * P.d + row, hres[lane * count + r0 + i] + pick<B>(res[i], lane),
-                          tag_out);
+            for (int b = 0; b < B; ++b)
+                stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * P.d + begin, count, hres + b * count,
+                           nullptr, wave, kConvWaves, ss[0]);
+            const StageSeg sg[1] = {sx};
+            if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kConvWaves, spin, ss)) return;
+        } else {
+            const StageSeg sg[2] = {sx, {P.h + begin, hres, nullptr, count, (uint32_t)B, (uint32_t)P.d, count, tag_res}};
+            if (!stage_segs<kStagePassWordsWide, 1, 2>(sg, wave, kConvWaves, spin, ss)) return;
         }
-    };
-    if (is_down) conv_rows_auto<B, OP_DOWN>(P, Lw, begin, count, K * 2u, x, epi);
-    else conv_rows_auto<B, OP_O>(P, Lw, begin, count, K * 2u, x, epi);
+        __syncthreads();
+        const XLds x{xs, Ks};
+        const bool last = ks + 1 == ns;
+        auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
+            #pragma unroll
+            for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i) {
+                if (i >= nr) break;
+                const uint32_t j = r0 + i;
+                if (lane < B) {
+                    float v = pick<B>(res[i], lane);
+                    if (ks > 0) v = part[lane * count + j] + v;
+                    if (!last) {
+                        part[lane * count + j] = v;
+                    } else {
+                        st_tagged(P.h + (size_t)lane * P.d + begin + j, hres[lane * count + j] + v, tag_out);
+                    }
+                }
+            }
+        };
+        if (is_down) conv_rows_auto<B, OP_DOWN>(P, Lw, begin, count, Ks * 2u, x, epi, ks * Ks);
+        else conv_rows_auto<B, OP_O>(P, Lw, begin, count, Ks * 2u, x, epi);
+    }
 }
 
 template <int HD>
@@ -277,9 +302,13 @@ hipError_t prepare_conventional(const Params& P) {
     if (P.hd == 64) {
         if (P.B == 1) return prepare_t<1, 64>(P.x_bytes);
         if (P.B == 2) return prepare_t<2, 64>(P.x_bytes);
+        if (P.B == 4) return prepare_t<4, 64>(P.x_bytes);
+        if (P.B == 8) return prepare_t<8, 64>(P.x_bytes);
     } else if (P.hd == 128) {
         if (P.B == 1) return prepare_t<1, 128>(P.x_bytes);
         if (P.B == 2) return prepare_t<2, 128>(P.x_bytes);
+        if (P.B == 4) return prepare_t<4, 128>(P.x_bytes);
+        if (P.B == 8) return prepare_t<8, 128>(P.x_bytes);
     }
     return hipErrorInvalidValue;
 }
@@ -288,9 +317,13 @@ hipError_t launch_conventional(const Params& P, const StepArgs& A, hipStream_t s
     if (P.hd == 64) {
         if (P.B == 1) return launch_step_t<1, 64>(P, A, stream);
         if (P.B == 2) return launch_step_t<2, 64>(P, A, stream);
+        if (P.B == 4) return launch_step_t<4, 64>(P, A, stream);
+        if (P.B == 8) return launch_step_t<8, 64>(P, A, stream);
     } else if (P.hd == 128) {
         if (P.B == 1) return launch_step_t<1, 128>(P, A, stream);
         if (P.B == 2) return launch_step_t<2, 128>(P, A, stream);
+        if (P.B == 4) return launch_step_t<4, 128>(P, A, stream);
+        if (P.B == 8) return launch_step_t<8, 128>(P, A, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -56,7 +56,9 @@ size_t x_floats(const mk_model_config* c, const mk_runtime_config* rt, int nspli
     const size_t B = (size_t)rt->max_batch, hd = (size_t)c->head_dim, G = (size_t)(c->n_q_heads / c->n_kv_heads);
     size_t n = B * (size_t)c->hidden;
     n = std::max(n, B * ((size_t)c->n_q_heads * hd + kMaxResidRows));
-    n = std::max(n, B * ((size_t)c->ffn + kMaxResidRows));
+    // DOWN: one column slice of the input, the residual rows and the partial sums
+    const int ns = std::max(1, down_slices_for((int)B, c->ffn));
+    n = std::max(n, B * ((size_t)(c->ffn / ns) + 2 * kMaxResidRows));
     return std::max(n, attn_lds_floats((int)G, (int)hd, nsplit));
 }
 
@@ -106,7 +108,9 @@ mk_status validate(const mk_model_config* c, const mk_runtime_config* rt, std::s
     if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.0)) return fail(MK_E_INVALID, "rms_eps and rope_theta must be > 0");
     if (rt->max_batch < 1 || rt->max_batch > kMaxBatch) return fail(MK_E_UNSUPPORTED, "max_batch must be 1..8");
     if (!megakernel_supports(rt->max_batch, c->head_dim))
-        return fail(MK_E_UNSUPPORTED, "this build runs batch 1 and 2");
+        return fail(MK_E_UNSUPPORTED, "this build runs batch 1, 2, 4 and 8");
+    if (down_slices_for(rt->max_batch, c->ffn) == 0)
+        return fail(MK_E_UNSUPPORTED, "the DOWN input of this batch needs column slices of whole 1 KB chunks");
     if (rt->max_seq < 1 || rt->max_seq > (1 << 20)) return fail(MK_E_INVALID, "max_seq out of range");
     if (rt->mode != MK_MODE_MEGAKERNEL && rt->mode != MK_MODE_GRAPH) return fail(MK_E_INVALID, "unknown mode");
     if (rt->num_cus < 0 || rt->num_cus > kMaxCus) return fail(MK_E_INVALID, "num_cus out of range");
@@ -453,6 +457,7 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
     P.Hkv = cfg->n_kv_heads;
     P.hd = cfg->head_dim;
     P.F = cfg->ffn;
+    P.down_slices = down_slices_for(rt->max_batch, cfg->ffn);
     P.V = cfg->vocab;
     P.B = rt->max_batch;
     P.S = rt->max_seq;

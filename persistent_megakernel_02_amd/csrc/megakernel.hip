@@ -206,9 +206,10 @@ struct Stream {
     const char *p0, *p1, *p2;
     const char* head;     // ATTN: the (cos, sin) row streamed as chunk 0 ahead of the groups
     uint32_t end0, end1;  // ranges: chunk ends of the first two ranges
-    uint32_t per_shift;   // interleaved: log2(chunks of each matrix per turn)
+    uint32_t per_shift;   // interleaved: log2(chunks of each matrix per turn); sliced: log2(chunks per row slice)
     int ncached;          // ATTN: valid positions of the split
-    bool inter, attn;
+    uint32_t nrow, row_bytes, slice_bytes;  // sliced (DOWN over column slices): rows, row stride, slice width
+    bool inter, attn, sliced;
 };
 
 template <int HD>
@@ -216,6 +217,8 @@ __device__ __forceinline__ bool setup_stream(const Params& P, const Instr& in, c
                                              Stream& S) {
     S.inter = false;
     S.attn = false;
+    S.sliced = false;
+    S.nrow = S.row_bytes = S.slice_bytes = 0;
     S.ncached = 0;
     S.per_shift = 0;
     S.p1 = S.p2 = S.head = nullptr;
@@ -239,7 +242,19 @@ __device__ __forceinline__ bool setup_stream(const Params& P, const Instr& in, c
             return true;
         }
         case OP_O: rb = (uint32_t)(P.Hq * HD) * 2u; S.p0 = (const char*)Lw.wo + (size_t)in.begin * rb; break;
-        case OP_DOWN: rb = (uint32_t)P.F * 2u; S.p0 = (const char*)Lw.w_down + (size_t)in.begin * rb; break;
+        case OP_DOWN:
+            rb = (uint32_t)P.F * 2u;
+            S.p0 = (const char*)Lw.w_down + (size_t)in.begin * rb;
+            if (P.down_slices > 1) {
+                // slice-major: the rows' first column slices, then their second, ...
+                S.sliced = true;
+                S.nrow = in.count;
+                S.row_bytes = rb;
+                S.slice_bytes = rb / (uint32_t)P.down_slices;
+                S.per_shift = (uint32_t)__builtin_ctz(S.slice_bytes / kChunk);
+                return (S.slice_bytes & (kChunk - 1u)) == 0 && ((S.slice_bytes / kChunk) & (S.slice_bytes / kChunk - 1u)) == 0;
+            }
+            break;
         case OP_HEAD: rb = (uint32_t)P.d * 2u; S.p0 = (const char*)P.head + (size_t)in.begin * rb; break;
         case OP_GATEUP: {
             rb = (uint32_t)P.d * 2u;
@@ -275,6 +290,12 @@ __device__ __forceinline__ bool setup_stream(const Params& P, const Instr& in, c
 template <int HD>
 __device__ __forceinline__ const char* stream_chunk(const Stream& S, uint32_t c, uint32_t& voff) {
     const uint32_t lane16 = (uint32_t)lane_id() * 16u;
+    if (S.sliced) {
+        const uint32_t seg = c >> S.per_shift, within = c & ((1u << S.per_shift) - 1u);
+        const uint32_t slice = seg / S.nrow, row = seg - slice * S.nrow;
+        voff = row * S.row_bytes + slice * S.slice_bytes + within * kChunk + lane16;
+        return S.p0;
+    }
     if (!S.inter) {
         if (c < S.end0) {
             voff = c * kChunk + lane16;
@@ -518,7 +539,7 @@ template <int B, class Epi>
 __device__ __forceinline__ bool gemv_ring_auto(const Params& P, Ctl* ctl, const char* ring, uint32_t S, uint32_t rb,
                                                uint32_t nrows, const XLds& x, int wave, uint32_t& lw, Epi& epi,
                                                bool pairs) {
-    const int R = rows_per_batch(rb);
+    const int R = rows_per_batch(rb, B);
     if (R >= 4) return gemv_ring<B, 4>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
     if (R == 2 || pairs) return gemv_ring<B, 2>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
     return gemv_ring<B, 1>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
@@ -584,8 +605,9 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                 if (in.op == OP_QKV) {
                     const uint32_t tag_out = phase_tag(A.tag0, layer, 0);
                     auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
-                        for (uint32_t i = 0; i < nr; ++i)
-                            if (lane < B)
+                        #pragma unroll
+                        for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i)
+                            if (i < nr && lane < B)
                                 st_tagged(P.qkv + (size_t)lane * P.qkv_rows + in.begin + r0 + i,
                                           pick<B>(res[i], lane) * pick<B>(r, lane), tag_out);
                     };
@@ -593,7 +615,9 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                 } else if (in.op == OP_GATEUP) {
                     const uint32_t tag_out = phase_tag(A.tag0, layer, 3);
                     auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
-                        for (uint32_t i = 0; i + 1 < nr; i += 2) {
+                        #pragma unroll
+                        for (uint32_t i = 0; i + 1 < (uint32_t)(sizeof(res) / sizeof(res[0])); i += 2) {
+                            if (i + 1 >= nr) break;
                             const uint32_t f = in.begin + (r0 + i) / 2u;
                             if (lane < B) {
                                 const float rr = pick<B>(r, lane);
@@ -614,7 +638,9 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                         best_i[b] = 0x7FFFFFFF;
                     }
                     auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
-                        for (uint32_t i = 0; i < nr; ++i) {
+                        #pragma unroll
+                        for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i) {
+                            if (i >= nr) break;
                             const int32_t row = (int32_t)(in.begin + r0 + i);
 #pragma unroll
                             for (int b = 0; b < B; ++b) {
@@ -646,34 +672,56 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                 const uint32_t tag_x = is_o ? phase_tag(A.tag0, layer, 1) : phase_tag(A.tag0, layer, 3);
                 const uint32_t tag_res = is_o ? phase_tag(A.tag0, layer - 1, 4) : phase_tag(A.tag0, layer, 2);
                 const uint32_t tag_out = is_o ? phase_tag(A.tag0, layer, 2) : phase_tag(A.tag0, layer, 4);
-                float* hres = xs + B * K;  // [B][count] residual rows before this op
-                float ss[1] = {0.f};
-                const StageSeg sx = {is_o ? P.attn : P.act, xs, nullptr, K, (uint32_t)B, K, K, tag_x};
-                if (is_o && layer == 0) {
-                    // the residual is the token embedding: no wait
+                // DOWN runs over P.down_slices column slices of its input (the stream is
+                // slice-major); partial sums of the rows wait in LDS between slices
+                const uint32_t ns = is_o ? 1u : (uint32_t)P.down_slices, Ks = K / ns;
+                float* hres = xs + B * Ks;         // [B][count] residual rows before this op
+                float* part = hres + B * in.count;  // [B][count] partial sums
+                for (uint32_t ks = 0; ks < ns && ok; ++ks) {
+                    if (ks > 0 && !barrier()) return;  // every wave is done with the previous slice
+                    float ss[1] = {0.f};
+                    const StageSeg sx = {(is_o ? P.attn : P.act) + ks * Ks, xs, nullptr, Ks, (uint32_t)B, K, Ks,
+                                         tag_x};
+                    if (ks > 0) {
+                        const StageSeg sg[1] = {sx};
+                        if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kComputeWaves, spin, ss)) return;
+                    } else if (is_o && layer == 0) {
+                        // the residual is the token embedding: no wait
 #pragma unroll
-                    for (int b = 0; b < B; ++b)
-                        stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * P.d + in.begin, in.count,
-                                   hres + b * in.count, nullptr, wave, kComputeWaves, ss[0]);
-                    const StageSeg sg[1] = {sx};
-                    if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kComputeWaves, spin, ss)) return;
-                } else {
-                    const StageSeg sg[2] = {sx, {P.h + in.begin, hres, nullptr, in.count, (uint32_t)B, (uint32_t)P.d,
-                                                 in.count, tag_res}};
-                    if (!stage_segs<kStagePassWordsWide, 1, 2>(sg, wave, kComputeWaves, spin, ss)) return;
-                }
-                if (!barrier()) return;
-                if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
-                const XLds x{xs, K};
-                auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
-                    for (uint32_t i = 0; i < nr; ++i) {
-                        const uint32_t row = in.begin + r0 + i;
-                        if (lane < B)
-                            st_tagged(P.h + (size_t)lane * P.d + row,
-                                      hres[lane * in.count + r0 + i] + pick<B>(res[i], lane), tag_out);
+                        for (int b = 0; b < B; ++b)
+                            stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * P.d + in.begin,
+                                       in.count, hres + b * in.count, nullptr, wave, kComputeWaves, ss[0]);
+                        const StageSeg sg[1] = {sx};
+                        if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kComputeWaves, spin, ss)) return;
+                    } else {
+                        const StageSeg sg[2] = {sx, {P.h + in.begin, hres, nullptr, in.count, (uint32_t)B,
+                                                     (uint32_t)P.d, in.count, tag_res}};
+                        if (!stage_segs<kStagePassWordsWide, 1, 2>(sg, wave, kComputeWaves, spin, ss)) return;
                     }
-                };
-                ok = gemv_ring_auto<B>(P, ctl, ring, S, K * 2u, in.count, x, wave, land_wait, epi, false);
+                    if (!barrier()) return;
+                    if (tr && lane == 0 && ks == 0) tr[2] = (uint32_t)now_ticks();
+                    const XLds x{xs, Ks};
+                    const bool last = ks + 1 == ns;
+                    auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
+                        #pragma unroll
+                        for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i) {
+                            if (i >= nr) break;
+                            const uint32_t j = r0 + i;
+                            if (lane < B) {
+                                float v = pick<B>(res[i], lane);
+                                if (ks > 0) v = part[lane * in.count + j] + v;
+                                if (!last) {
+                                    part[lane * in.count + j] = v;
+                                } else {
+                                    st_tagged(P.h + (size_t)lane * P.d + in.begin + j, hres[lane * in.count + j] + v,
+                                              tag_out);
+                                }
+                            }
+                        }
+                    };
+                    ok = gemv_ring_auto<B>(P, ctl, ring, S + ks * in.count * Ks * 2u, Ks * 2u, in.count, x, wave,
+                                           land_wait, epi, false);
+                }
                 break;
             }
             case OP_ATTN: {
@@ -761,13 +809,17 @@ hipError_t launch_megakernel(const Params& P, const StepArgs& A, hipStream_t str
     if (P.hd == 64) {
         if (P.B == 1) return launch_t<1, 64>(P, A, stream);
         if (P.B == 2) return launch_t<2, 64>(P, A, stream);
+        if (P.B == 4) return launch_t<4, 64>(P, A, stream);
+        if (P.B == 8) return launch_t<8, 64>(P, A, stream);
     } else if (P.hd == 128) {
         if (P.B == 1) return launch_t<1, 128>(P, A, stream);
         if (P.B == 2) return launch_t<2, 128>(P, A, stream);
+        if (P.B == 4) return launch_t<4, 128>(P, A, stream);
+        if (P.B == 8) return launch_t<8, 128>(P, A, stream);
     }
     return hipErrorInvalidValue;
 }
 
-bool megakernel_supports(int B, int hd) { return (B == 1 || B == 2) && (hd == 64 || hd == 128); }
+bool megakernel_supports(int B, int hd) { return (B == 1 || B == 2 || B == 4 || B == 8) && (hd == 64 || hd == 128); }
 
 }  // namespace mk

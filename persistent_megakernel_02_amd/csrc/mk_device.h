@@ -431,14 +431,21 @@ __device__ __forceinline__ void rows_dot(const Rows& rows, int np, const X& x, f
 }
 
 // Rows of one compute wave's batch for a row of `rb` bytes: about 8 KB per wave.
-__host__ __device__ constexpr int rows_per_batch(uint32_t rb) { return rb <= 2048u ? 4 : rb <= 4096u ? 2 : 1; }
+// From batch 4 on, one row per batch keeps the B accumulators and x pieces in registers.
+__host__ __device__ constexpr int rows_per_batch(uint32_t rb, int B = 1) {
+    return B >= 4 ? 1 : rb <= 2048u ? 4 : rb <= 4096u ? 2 : 1;
+}
 
+// a[i] for a per-lane i < B.  The empty asm between the selects keeps the chain
+// of v_cndmask: folded into a table lookup it would index a private array.
 template <int B>
 __device__ __forceinline__ float pick(const float (&a)[B], int i) {
     float v = a[0];
 #pragma unroll
-    for (int b = 1; b < B; ++b)
-        if (i == b) v = a[b];
+    for (int b = 1; b < B; ++b) {
+        v = (i == b) ? a[b] : v;
+        asm volatile("" : "+v"(v));
+    }
     return v;
 }
 
@@ -1024,8 +1031,10 @@ __device__ __forceinline__ bool head_publish(const Params& P, const StepArgs& A,
         uint64_t* dst = P.head_part + ((size_t)slot * P.B + lane) * 2;
         int32_t i = bi[0];
 #pragma unroll
-        for (int b = 1; b < B; ++b)
-            if (lane == b) i = bi[b];
+        for (int b = 1; b < B; ++b) {
+            i = (lane == b) ? bi[b] : i;
+            asm volatile("" : "+v"(i));
+        }
         st_tagged(dst, pick<B>(bv, lane), tag);
         st_tagged(dst + 1, __int_as_float(i), tag);
     }

@@ -22,7 +22,7 @@ constexpr int kThreads = 64 * (kComputeWaves + kLoaderWaves);
 constexpr uint32_t kChunk = 1024;                   // one loader issue: 64 lanes x 16 B
 constexpr uint32_t kLdsBytes = 160 * 1024;          // LDS of one gfx950 compute unit
 constexpr uint32_t kStaticLds = 1024;               // reserved for the control block
-constexpr uint32_t kMinRingChunks = 64;
+constexpr uint32_t kMinRingChunks = 72;             // >= one attention block (2 x 32 KV chunks) + its RoPE chunk
 constexpr int kLoaderLag = 8;                       // chunks in flight per loader wave (vmcnt <= 63)
 constexpr int kMaxBatch = 8;
 constexpr int kMaxGroup = 4;                        // q heads per KV head
@@ -32,7 +32,22 @@ constexpr int kStageWords = 16;                     // tagged words per lane in 
 constexpr int kStagePassWords = 4;                  // tagged words per lane per staging pass (two in flight)
 constexpr int kStagePassWordsWide = 8;              // the same for the wide inputs of O and DOWN
 constexpr int kAttnBlockGroups = 32;                // KV position groups (2 KB each) one attention pass holds
+static_assert(kMinRingChunks >= 2 * kAttnBlockGroups + 1, "an attention block and its RoPE chunk fit the ring");
 constexpr int kAttnWavePositions = 64;              // positions one wave scores per block (its score area)
+constexpr uint32_t kDownSliceBytes = 64 * 1024;     // largest fp32 DOWN input slice (all batch rows) staged at once
+
+// Column slices of the DOWN projection: the fewest (a power of two) whose input
+// slice, B rows of F / slices fp32 values, fits kDownSliceBytes; 0 if the slices
+// would not be whole 1 KB chunks of a weight row.
+__host__ __device__ constexpr int down_slices_for(int B, int F) {
+    int n = 1;
+    while ((size_t)B * (size_t)(F / n) * 4u > kDownSliceBytes && n < 64) n *= 2;
+    if (n > 1) {
+        const int chunks = F % n ? 0 : (F / n) * 2 / 1024;  // 1 KB chunks per row slice: a power of two
+        if (chunks == 0 || ((F / n) * 2) % 1024 != 0 || (chunks & (chunks - 1)) != 0) return 0;
+    }
+    return n;
+}
 
 // LDS floats one attention item uses: raw q (G heads), k and v; rotated q; the new
 // K and V as bf16; the scores of every wave ([wave][position][kMaxGroup]); the wave
@@ -98,6 +113,8 @@ struct Params {
     // shape
     int32_t L, d, Hq, Hkv, hd, F, V, B, S, G;  // G = Hq / Hkv
     int32_t qkv_rows, nsplit, n_cu, kv_b;      // kv_b = max_batch of the cache layout
+    int32_t down_slices;                       // DOWN runs over F in this many column slices (power of 2)
+    int32_t pad_ds;
     float eps, attn_scale;
     // weights
     const DevLayer* layers;

@@ -80,7 +80,7 @@ def test_runtime_validation():
     assert st == mk.MK_OK and ws_tr > mk.mk_query_sizes(c, rt())[1]
 
 
-LDS_BYTES, LDS_STATIC, CHUNK, MIN_RING = 160 * 1024, 1024, 1024, 64
+LDS_BYTES, LDS_STATIC, CHUNK, MIN_RING = 160 * 1024, 1024, 1024, 72
 
 
 def staged_bytes(cfg, batch):

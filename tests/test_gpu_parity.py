@@ -252,3 +252,72 @@ def test_llama8b_b1_prefix():
     _, near = compare(rt_, rl, gt, gl, "8B b1 megakernel")
     assert near <= 1
     d.close()
+
+
+@pytest.mark.parametrize("B", [4, 8])
+def test_tiny_batch_4_8(B):
+    """Batches of 4 and 8 sequences (different prompts) in both modes; the two
+    modes agree bit for bit."""
+    cfg = I.TINY
+    w = I.make_weights(cfg, seed=6)
+    prompt = I.make_prompt(cfg, B, 6, seed=7)
+    rt_, rl = oracle_run(cfg, w, prompt, 10, 20)
+    outs = []
+    for mode in (0, 1):
+        print(f"case tiny b{B} mode={mode}", flush=True)
+        d = _decoder(cfg, w, B, 20, mode)
+        gt, gl = gpu_run(d, prompt, rt_, 10)
+        compare(rt_, rl, gt, gl, f"tiny b{B} mode={mode}")
+        outs.append(gl)
+        d.close()
+    for x, y in zip(outs[0], outs[1]):
+        assert np.array_equal(x, y)
+
+
+def test_down_column_slices():
+    """A wide FFN at batch 8 (hidden 256, ffn 4096) whose DOWN input does not fit
+    the LDS budget at once: DOWN runs over column slices with partial sums."""
+    import persistent_megakernel_02_amd.mk as mk
+
+    cfg = I.replace(I.TINY, ffn=4096)
+    B = 8
+    assert mk.lib() is not None
+    w = I.make_weights(cfg, seed=8)
+    prompt = I.make_prompt(cfg, B, 4, seed=8)
+    rt_, rl = oracle_run(cfg, w, prompt, 6, 16)
+    for mode in (0, 1):
+        print(f"case wide-ffn b8 mode={mode}", flush=True)
+        d = _decoder(cfg, w, B, 16, mode)
+        gt, gl = gpu_run(d, prompt, rt_, 6)
+        compare(rt_, rl, gt, gl, f"wide-ffn b8 mode={mode}")
+        d.close()
+
+
+@pytest.mark.parametrize("B,ctx", [(4, 8192), (8, 8192)])
+def test_llama1b_batch_long_context(B, ctx):
+    """The 1B shape at batch 4 and 8 over an 8192-position synthetic context:
+    split attention and sliced DOWN, 3 steps."""
+    cfg = I.LLAMA_1B
+    w = I.make_weights(cfg, seed=9)
+    steps, S = 3, ctx + 8
+    start = I.make_prompt(cfg, B, 1, seed=9)[:, 0]
+    orc = O.Oracle(cfg, w, B, S)
+    print(f"case 1B b{B} ctx={ctx} megakernel", flush=True)
+    d = _decoder(cfg, w, B, S, 0)
+    t0 = time.time()
+    _fill_context(cfg, orc, d, ctx, seed=9)
+    print(f"context filled in {time.time() - t0:.1f}s", flush=True)
+    torch = _torch()
+    ref_t, ref_l, got_t, got_l = [], [], [], []
+    tok = start.astype(np.int32)
+    for _ in range(steps):
+        nxt, logits = orc.step(tok)
+        g_n, g_l = d.decode_step(torch.from_numpy(tok).to(d.device))
+        ref_t.append(nxt.copy())
+        ref_l.append(logits.copy())
+        got_t.append(g_n.cpu().numpy().copy())
+        got_l.append(g_l.cpu().numpy().copy())
+        tok = nxt.astype(np.int32)
+    _, near = compare(ref_t, ref_l, got_t, got_l, f"1B b{B} ctx={ctx}")
+    assert near <= 1
+    d.close()
