@@ -74,8 +74,9 @@ def profile_run(args) -> int:
     cfg = I.LLAMA_1B
     dev = torch.device("cuda:0")
     w = I.make_weights(cfg, seed=args.seed)
-    prompt = torch.from_numpy(I.make_prompt(cfg, 1, args.prompt, seed=args.seed)).to(dev)
-    dec = mk.Decoder(cfg, w, max_batch=1, max_seq=args.prompt + args.horizon + 1, device="cuda:0")
+    n_prompt, horizon = WORKLOADS["1b"]["prompt"], WORKLOADS["1b"]["horizon"]
+    prompt = torch.from_numpy(I.make_prompt(cfg, 1, n_prompt, seed=args.seed)).to(dev)
+    dec = mk.Decoder(cfg, w, max_batch=1, max_seq=n_prompt + horizon + 1, device="cuda:0")
     tok, logits = dec.prefill(prompt)
     for _ in range(args.steps):
         dec.decode_step(tok, tok, logits)
@@ -87,7 +88,7 @@ def profile_run(args) -> int:
     for _ in range(2):
         mk.bench_copy(b, a)
     torch.cuda.synchronize()
-    log(f"profile run: prefill {args.prompt} + {args.steps} decode steps, 2 copies of {nb} B")
+    log(f"profile run: prefill {n_prompt} + {args.steps} decode steps, 2 copies of {nb} B")
     return 0
 
 
@@ -96,15 +97,34 @@ def log(msg: str) -> None:
 
 
 def step_bytes(cfg, batch: int, positions) -> int:
-    """Algorithmic HBM bytes of one decode step: every weight byte once, the
-    token's embedding row, the K/V of the cached positions read once per
-    (sequence, KV head), the new K/V written, the fp32 logits written."""
+    """Algorithmic HBM bytes of one decode step: every weight byte once, each
+    sequence's embedding row, the K/V of its cached positions read once per
+    (sequence, KV head), its new K/V written, the fp32 logits written.
+    `positions`: the position each sequence decodes at this step (one per sequence,
+    or a single value shared by all)."""
     kv_pos = cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim * 2
+    pos = [int(p) for p in positions]
+    if len(pos) == 1:
+        pos = pos * batch
     b = cfg.weight_bytes() + batch * cfg.hidden * 2
-    b += sum(int(p) for p in positions) * kv_pos  # cached positions 0..p-1 read
-    b += batch * kv_pos                            # position p written
+    b += sum(pos) * kv_pos     # cached positions 0..p-1 read
+    b += batch * kv_pos        # position p written
     b += batch * cfg.vocab * 4
     return b
+
+
+# Workloads: model, batch, prompt tokens (or a synthetic context), decode steps
+# per horizon.  "1b" is the headline one.
+WORKLOADS = {
+    "1b": dict(model="LLAMA_1B", batch=1, prompt=32, ctx=0, horizon=128,
+               text="llama-3.2-1b-shape decode, batch 1, 32 prompt tokens then greedy steps"),
+    "1b-b4": dict(model="LLAMA_1B", batch=4, prompt=0, ctx=8192, horizon=128,
+                  text="llama-3.2-1b-shape decode, batch 4, 8192-position synthetic bf16 KV context per sequence"),
+    "1b-b8": dict(model="LLAMA_1B", batch=8, prompt=0, ctx=8192, horizon=128,
+                  text="llama-3.2-1b-shape decode, batch 8, 8192-position synthetic bf16 KV context per sequence"),
+    "8b": dict(model="LLAMA_8B", batch=1, prompt=128, ctx=0, horizon=256,
+               text="llama-3-8b-shape decode, batch 1, 128 prompt tokens then greedy steps"),
+}
 
 
 def main() -> int:
@@ -112,8 +132,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--prompt", type=int, default=32)
-    ap.add_argument("--horizon", type=int, default=128, help="decode steps before the context is reset to the prompt")
+    ap.add_argument("--config", default="1b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-graph", action="store_true", help="skip the one-kernel-per-op comparison")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-steps", type=int, default=24)
@@ -137,27 +156,44 @@ def main() -> int:
     import persistent_megakernel_02_amd.inputs as I
     import persistent_megakernel_02_amd.mk as mk
 
-    cfg = I.LLAMA_1B
-    B, P, H = 1, args.prompt, args.horizon
+    W = WORKLOADS[args.config]
+    cfg = getattr(I, W["model"])
+    B, H, CTX = W["batch"], W["horizon"], W["ctx"]
+    P = W["prompt"] if CTX == 0 else CTX  # position of the first timed step
     max_seq = P + H + 1
     dev = torch.device("cuda:0")
     t0 = time.time()
     w = I.make_weights(cfg, seed=args.seed)
-    prompt = I.make_prompt(cfg, B, P, seed=args.seed)
+    prompt = I.make_prompt(cfg, B, max(1, W["prompt"]), seed=args.seed)
     log(f"weights generated in {time.time() - t0:.1f}s")
     dw = mk.upload_weights(w, dev)
     torch.cuda.synchronize()
     prompt_dev = torch.from_numpy(prompt).to(dev)
+    kv_host = None
+    if CTX:
+        shape = (cfg.n_layers, B, cfg.n_kv_heads, max_seq, cfg.head_dim)
+        kv_host = (np.zeros(shape, np.uint16), np.zeros(shape, np.uint16))
+        I.fill_kv_context(cfg, kv_host[0], kv_host[1], B, CTX, seed=args.seed)
+        log(f"synthetic context of {CTX} positions filled in {time.time() - t0:.1f}s")
 
     def run_path(mode: int, label: str):
         dec = mk.Decoder(cfg, w, max_batch=B, max_seq=max_seq, mode=mode, device="cuda:0", device_weights=dw)
         st = dec.stream
         tok = torch.zeros(B, dtype=torch.int32, device=dev)
         logits = torch.empty((B, cfg.vocab), dtype=torch.float32, device=dev)
+        if kv_host is not None:
+            kd, vd = dec.kv_views()
+            kd.copy_(torch.from_numpy(kv_host[0].view(np.int16)))
+            vd.copy_(torch.from_numpy(kv_host[1].view(np.int16)))
+            torch.cuda.synchronize()
 
         def start_horizon():
-            dec.set_context_len([0] * B)
-            dec.prefill(prompt_dev, logits, tok)
+            if CTX:
+                dec.set_context_len([CTX] * B)
+                tok.copy_(prompt_dev[:, 0])
+            else:
+                dec.set_context_len([0] * B)
+                dec.prefill(prompt_dev, logits, tok)
 
         # warmup
         start_horizon()
@@ -211,7 +247,7 @@ def main() -> int:
         return us, positions, kps, per_h, pct
 
     us_mk, positions, kps_mk, per_h, pct_mk = run_path(mk.MK_MODE_MEGAKERNEL, "megakernel")
-    bytes_step = [step_bytes(cfg, B, [p]) for p in positions]
+    bytes_step = [step_bytes(cfg, B, [p]) for p in positions]  # every sequence at position p
     mean_bytes = float(np.mean(bytes_step))
     gbs = mean_bytes / (us_mk * 1e-6) / 1e9
 
@@ -241,24 +277,31 @@ def main() -> int:
         import oracle as O
 
         orc = O.Oracle(cfg, w, B, max_seq)
-        t1 = time.time()
-        nxt, _ = orc.prefill(prompt[:, :4])
-        orc.pos[:] = P
+        nsteps = args.cpu_steps if B == 1 and cfg is I.LLAMA_1B else 4
+        if CTX:
+            orc.set_context(CTX, lambda k, v: (np.copyto(k, kv_host[0]), np.copyto(v, kv_host[1])))
+            nxt = prompt[:, 0]
+        else:
+            nxt, _ = orc.prefill(prompt[:, :4])
+            orc.pos[:] = P
         t2 = time.time()
-        for _ in range(args.cpu_steps):
+        for _ in range(nsteps):
             nxt, _ = orc.step(nxt)
         t3 = time.time()
-        cpu_us = (t3 - t2) * 1e6 / args.cpu_steps
-        cpu = {"value": round(cpu_us, 1), "unit": "us/token", "cores": O.threads(), "kind": "oracle",
-               "sample": f"{args.cpu_steps} batch-1 decode steps of the same 1B-shape model at positions "
-                         f"{P}..{P + args.cpu_steps - 1} (fp64-accumulated C oracle, OpenMP over rows)"}
-        log(f"cpu oracle: {cpu_us / 1000:.1f} ms/token on {O.threads()} threads")
+        cpu_us = (t3 - t2) * 1e6 / nsteps
+        cpu = {"value": round(cpu_us, 1), "unit": "us/token" if B == 1 else "us/step", "cores": O.threads(),
+               "kind": "oracle",
+               "sample": f"{nsteps} batch-{B} decode steps of the same {cfg.name} model at positions "
+                         f"{P}..{P + nsteps - 1} (fp64-accumulated C oracle, OpenMP over rows)"}
+        log(f"cpu oracle: {cpu_us / 1000:.1f} ms/step on {O.threads()} threads")
 
-    traffic, traffic_src = counter_traffic()
+    traffic, traffic_src = counter_traffic() if args.config == "1b" else (None, "counters taken for the 1b workload only")
+    headline = args.config == "1b"
     out = {
-        "metric": "decode us/token at batch 1 (Llama-3.2-1B shape) + % of peak HBM BW",
+        "metric": "decode us/token at batch 1 (Llama-3.2-1B shape) + % of peak HBM BW" if headline
+        else f"decode us/step ({W['text']}) + % of peak HBM BW",
         "value": round(us_mk, 2),
-        "unit": "us/token",
+        "unit": "us/token" if B == 1 else "us/step",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -268,10 +311,10 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "llama-3.2-1b-shape decode, batch 1, 32 prompt tokens then greedy steps, "
-                               "random bf16 weights N(0,0.02)", "batch": B, "prompt": P, "horizon": H,
+        "config": {"workload": W["text"] + ", random bf16 weights N(0,0.02)", "batch": B,
+                   "prompt": W["prompt"], "context": CTX, "horizon": H,
                    "layers": cfg.n_layers, "hidden": cfg.hidden, "vocab": cfg.vocab},
-        "tokens_per_s": round(1e6 / us_mk, 1),
+        "tokens_per_s": round(B * 1e6 / us_mk, 1),
         "us_per_token_p50": round(pct_mk[0], 2),
         "us_per_token_p95": round(pct_mk[1], 2),
         "pct_peak_hbm": round(100.0 * gbs / HBM_PEAK_GBS, 2),
@@ -286,7 +329,7 @@ def main() -> int:
                                                      "pct_peak_hbm": round(100.0 * mean_bytes / (us_graph * 1e-6)
                                                                            / 1e9 / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic if headline else None,
                      "bytes_per_launch": int(mean_bytes), "traffic_source": traffic_src},
         "cpu_baseline": cpu,
     }
