@@ -133,6 +133,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--config", default="1b", choices=sorted(WORKLOADS))
+    ap.add_argument("--gemv", default="auto", choices=["auto", "valu", "mfma"],
+                    help="GEMV arithmetic of the persistent kernel (auto: matrix cores from batch 4)")
     ap.add_argument("--no-graph", action="store_true", help="skip the one-kernel-per-op comparison")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-steps", type=int, default=24)
@@ -176,8 +178,11 @@ def main() -> int:
         I.fill_kv_context(cfg, kv_host[0], kv_host[1], B, CTX, seed=args.seed)
         log(f"synthetic context of {CTX} positions filled in {time.time() - t0:.1f}s")
 
+    gemv = {"auto": mk.MK_GEMV_AUTO, "valu": mk.MK_GEMV_VALU, "mfma": mk.MK_GEMV_MFMA}[args.gemv]
+
     def run_path(mode: int, label: str):
-        dec = mk.Decoder(cfg, w, max_batch=B, max_seq=max_seq, mode=mode, device="cuda:0", device_weights=dw)
+        dec = mk.Decoder(cfg, w, max_batch=B, max_seq=max_seq, mode=mode, device="cuda:0", device_weights=dw,
+                         gemv_kind=gemv if mode == mk.MK_MODE_MEGAKERNEL else mk.MK_GEMV_AUTO)
         st = dec.stream
         tok = torch.zeros(B, dtype=torch.int32, device=dev)
         logits = torch.empty((B, cfg.vocab), dtype=torch.float32, device=dev)
@@ -246,6 +251,8 @@ def main() -> int:
             f"p50 {pct[0]:.1f} p95 {pct[1]:.1f}")
         return us, positions, kps, per_h, pct
 
+    gemv_used = mk.mk_plan_inspect(mk.model_config(cfg), mk.runtime_config(B, max_seq, gemv_kind=gemv),
+                                   torch.cuda.get_device_properties(dev).multi_processor_count)[1]["gemv_kind"]
     us_mk, positions, kps_mk, per_h, pct_mk = run_path(mk.MK_MODE_MEGAKERNEL, "megakernel")
     bytes_step = [step_bytes(cfg, B, [p]) for p in positions]  # every sequence at position p
     mean_bytes = float(np.mean(bytes_step))
@@ -313,7 +320,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": W["text"] + ", random bf16 weights N(0,0.02)", "batch": B,
                    "prompt": W["prompt"], "context": CTX, "horizon": H,
-                   "layers": cfg.n_layers, "hidden": cfg.hidden, "vocab": cfg.vocab},
+                   "layers": cfg.n_layers, "hidden": cfg.hidden, "vocab": cfg.vocab,
+                   "gemv": "mfma" if gemv_used == mk.MK_GEMV_MFMA else "valu"},
         "tokens_per_s": round(B * 1e6 / us_mk, 1),
         "us_per_token_p50": round(pct_mk[0], 2),
         "us_per_token_p95": round(pct_mk[1], 2),

@@ -66,6 +66,16 @@ typedef enum {
     MK_MODE_GRAPH = 1       /* one kernel per op, replayed as a hipGraph [ROOT] */
 } mk_mode;
 
+/* GEMV arithmetic of the persistent mode.  Both read every weight once and
+ * accumulate in fp32.  VALU: fp32 dot products of bf16 rows with the fp32
+ * activations.  MFMA: v_mfma_f32_16x16x32_bf16 tiles of 16 rows x 32 columns
+ * against the activations split into bf16 parts (3 parts at batch 1, 2 and 4,
+ * 2 at batch 8: 24 or 16 mantissa bits of each fp32 activation), summed in
+ * fp32.  AUTO takes VALU (faster at every supported batch on the 1B shape as
+ * measured).  MK_MODE_GRAPH always computes with VALU; MK_GEMV_MFMA with it, or
+ * where the parts area leaves too small a weight ring, is MK_E_UNSUPPORTED. */
+typedef enum { MK_GEMV_AUTO = 0, MK_GEMV_VALU = 1, MK_GEMV_MFMA = 2 } mk_gemv_kind;
+
 /* Model shape.  n_experts == 0 selects the dense SwiGLU FFN (ffn = its width);
  * MoE decoders are not supported by this version (MK_E_UNSUPPORTED). */
 typedef struct {
@@ -100,7 +110,7 @@ typedef struct {
                                  mode needs num_cus <= the device's compute units (one
                                  resident workgroup each), else mk_create answers
                                  MK_E_UNSUPPORTED */
-    int32_t gemv_kind;        /* 0 auto, 1 VALU dot (the only kind in this version) */
+    int32_t gemv_kind;        /* mk_gemv_kind: how the weight-streaming GEMVs compute */
     uint32_t spin_timeout_ms; /* watchdog of every device spin-wait; 0 = 2000 ms */
     int32_t trace;            /* 1: record a per-instruction timeline (mk_read_trace) */
     int32_t attn_splits;      /* KV splits per (sequence, KV head); 0 = automatic */
@@ -168,7 +178,8 @@ const char* mk_last_error(const mk_handle* h);
  * `cap` int64 values: [0] compute units, [1] instructions, [2] LDS ring chunks
  * (1 KB each), [3] max instructions on one CU, [4] weight bytes per step,
  * [5] verifier result (0 = ok), [6] attention splits, [7] phases, [8] LDS bytes of
- * staged activations, [9] LM-head instructions. */
+ * staged activations, [9] LM-head instructions, [10] the GEMV kind in effect
+ * (MK_GEMV_VALU or MK_GEMV_MFMA). */
 mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* rt, int32_t num_cus, int64_t* out,
                           int32_t cap);
 

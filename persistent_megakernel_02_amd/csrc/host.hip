@@ -50,10 +50,51 @@ struct Plan {
     size_t max_per_cu = 0;
 };
 
+uint32_t ring_chunks_for(size_t x_bytes) {
+    const size_t avail = kLdsBytes - kStaticLds;
+    return x_bytes >= avail ? 0u : (uint32_t)((avail - x_bytes) / kChunk);
+}
+
+size_t x_floats_kind(const mk_model_config* c, const mk_runtime_config* rt, int nsplit, bool mfma);
+
+// Row lengths of the matrix-core instructions are whole tile units.
+bool mfma_shapes_ok(const mk_model_config* c, int B) {
+    return c->hidden % kMfmaUnitCols == 0 && (c->n_q_heads * c->head_dim) % kMfmaUnitCols == 0 &&
+           down_slices_for(B, c->ffn, true) != 0;
+}
+
+// Smallest batch at which automatic selection takes the matrix cores (measured:
+// VALU is faster at every supported batch, so automatic selection never does).
+constexpr int kMfmaAutoMinBatch = kMaxBatch + 1;
+
+// GEMV kind of a runtime configuration: the matrix cores run in the megakernel
+// only; automatic selection takes them from kMfmaAutoMinBatch on where their
+// activation area (bf16 parts: 6 bytes per element at 3 parts) leaves the weight
+// ring room.
+bool use_mfma(const mk_model_config* c, const mk_runtime_config* rt) {
+    if (rt->mode != MK_MODE_MEGAKERNEL) return false;
+    if (rt->gemv_kind == 1) return false;
+    if (rt->gemv_kind == 2) return true;
+    if (rt->max_batch < kMfmaAutoMinBatch || !mfma_shapes_ok(c, rt->max_batch)) return false;
+    return ring_chunks_for((x_floats_kind(c, rt, 1, true) * 4 + 15) & ~(size_t)15) >= kMinRingChunks;
+}
+
 // LDS floats of activations one instruction stages (x rows, residual rows of
 // O / DOWN, or an attention item's area).
-size_t x_floats(const mk_model_config* c, const mk_runtime_config* rt, int nsplit) {
+size_t x_floats_kind(const mk_model_config* c, const mk_runtime_config* rt, int nsplit, bool mfma) {
     const size_t B = (size_t)rt->max_batch, hd = (size_t)c->head_dim, G = (size_t)(c->n_q_heads / c->n_kv_heads);
+    if (mfma) {
+        // bf16 parts of the input (one column slice for DOWN), the residual rows and
+        // partial sums of O / DOWN, and the cross-wave partial tiles at the end
+        const int b = (int)B;
+        const int ns = std::max(1, down_slices_for(b, c->ffn, true));
+        const size_t resid = 2 * B * kMaxResidRows * 4;
+        size_t bytes = parts_bytes(b, c->hidden);
+        bytes = std::max(bytes, parts_bytes(b, c->n_q_heads * c->head_dim) + resid);
+        bytes = std::max(bytes, parts_bytes(b, c->ffn / ns) + resid);
+        bytes += mfma_red_bytes(b);
+        return std::max((bytes + 3) / 4, attn_lds_floats((int)G, (int)hd, nsplit));
+    }
     size_t n = B * (size_t)c->hidden;
     n = std::max(n, B * ((size_t)c->n_q_heads * hd + kMaxResidRows));
     // DOWN: one column slice of the input, the residual rows and the partial sums
@@ -63,12 +104,7 @@ size_t x_floats(const mk_model_config* c, const mk_runtime_config* rt, int nspli
 }
 
 size_t x_bytes_for(const mk_model_config* c, const mk_runtime_config* rt, int nsplit) {
-    return (x_floats(c, rt, nsplit) * 4 + 15) & ~(size_t)15;
-}
-
-uint32_t ring_chunks_for(size_t x_bytes) {
-    const size_t avail = kLdsBytes - kStaticLds;
-    return x_bytes >= avail ? 0u : (uint32_t)((avail - x_bytes) / kChunk);
+    return (x_floats_kind(c, rt, nsplit, use_mfma(c, rt)) * 4 + 15) & ~(size_t)15;
 }
 
 // Most KV splits whose merge area still leaves the minimum weight ring (0: none).
@@ -109,12 +145,16 @@ mk_status validate(const mk_model_config* c, const mk_runtime_config* rt, std::s
     if (rt->max_batch < 1 || rt->max_batch > kMaxBatch) return fail(MK_E_UNSUPPORTED, "max_batch must be 1..8");
     if (!megakernel_supports(rt->max_batch, c->head_dim))
         return fail(MK_E_UNSUPPORTED, "this build runs batch 1, 2, 4 and 8");
-    if (down_slices_for(rt->max_batch, c->ffn) == 0)
+    if (rt->gemv_kind < 0 || rt->gemv_kind > 2) return fail(MK_E_UNSUPPORTED, "gemv_kind must be 0, 1 or 2");
+    if (rt->gemv_kind == 2 && rt->mode != MK_MODE_MEGAKERNEL)
+        return fail(MK_E_UNSUPPORTED, "the matrix-core GEMV runs in the megakernel only");
+    if (rt->gemv_kind == 2 && !mfma_shapes_ok(c, rt->max_batch))
+        return fail(MK_E_UNSUPPORTED, "matrix-core GEMV rows must be whole tile units of columns");
+    if (down_slices_for(rt->max_batch, c->ffn, use_mfma(c, rt)) == 0)
         return fail(MK_E_UNSUPPORTED, "the DOWN input of this batch needs column slices of whole 1 KB chunks");
     if (rt->max_seq < 1 || rt->max_seq > (1 << 20)) return fail(MK_E_INVALID, "max_seq out of range");
     if (rt->mode != MK_MODE_MEGAKERNEL && rt->mode != MK_MODE_GRAPH) return fail(MK_E_INVALID, "unknown mode");
     if (rt->num_cus < 0 || rt->num_cus > kMaxCus) return fail(MK_E_INVALID, "num_cus out of range");
-    if (rt->gemv_kind < 0 || rt->gemv_kind > 1) return fail(MK_E_UNSUPPORTED, "gemv_kind must be 0 or 1");
     if (rt->trace != 0 && rt->trace != 1) return fail(MK_E_INVALID, "trace must be 0 or 1");
     if (rt->attn_splits < 0 || rt->attn_splits > kMaxSplits) return fail(MK_E_INVALID, "attn_splits out of range");
     // the activations one instruction stages must leave room for the weight ring
@@ -386,10 +426,10 @@ mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* r
     const int64_t per_layer = (cfg->n_q_heads + 2 * cfg->n_kv_heads) * hd * d + d * cfg->n_q_heads * hd +
                               3 * (int64_t)cfg->ffn * d + 2 * d;
     const size_t xb = x_bytes_for(cfg, rt, pl.nsplit);
-    int64_t vals[10] = {num_cus, (int64_t)pl.instrs.size(), (int64_t)ring_chunks_for(xb), (int64_t)pl.max_per_cu,
+    int64_t vals[11] = {num_cus, (int64_t)pl.instrs.size(), (int64_t)ring_chunks_for(xb), (int64_t)pl.max_per_cu,
                         2 * (cfg->n_layers * per_layer + (int64_t)cfg->vocab * d + d), verify_plan(cfg, rt, pl),
-                        pl.nsplit, pl.phases, (int64_t)xb, (int64_t)pl.n_head};
-    for (int i = 0; i < cap && i < 10; ++i) out[i] = vals[i];
+                        pl.nsplit, pl.phases, (int64_t)xb, (int64_t)pl.n_head, use_mfma(cfg, rt) ? 2 : 1};
+    for (int i = 0; i < cap && i < 11; ++i) out[i] = vals[i];
     return MK_OK;
 }
 
@@ -457,7 +497,8 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
     P.Hkv = cfg->n_kv_heads;
     P.hd = cfg->head_dim;
     P.F = cfg->ffn;
-    P.down_slices = down_slices_for(rt->max_batch, cfg->ffn);
+    P.gemv_mfma = use_mfma(cfg, rt) ? 1 : 0;
+    P.down_slices = down_slices_for(rt->max_batch, cfg->ffn, P.gemv_mfma != 0);
     P.V = cfg->vocab;
     P.B = rt->max_batch;
     P.S = rt->max_seq;

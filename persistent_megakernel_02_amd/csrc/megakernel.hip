@@ -62,9 +62,13 @@ __device__ __forceinline__ uint32_t align_chunk(uint32_t b) { return (b + kChunk
 // stream arithmetic that depends on it stays on the scalar unit.
 __device__ __forceinline__ int ctx_of(const int32_t* ctx, int b) { return __builtin_amdgcn_readfirstlane(ctx[b]); }
 
-// Bytes of the CU stream that instruction `in` consumes (whole chunks).
-template <int HD>
+__device__ __forceinline__ bool is_gemv(uint32_t op) { return op != OP_ATTN; }
+
+// Bytes of the CU stream that instruction `in` consumes (whole chunks).  With the
+// matrix cores (MF) a GEMV streams whole 16-row tiles of 1 KB chunks.
+template <int HD, bool MF = false>
 __device__ __forceinline__ uint32_t instr_bytes(const Params& P, const Instr& in, const int32_t* ctx) {
+    if (MF && is_gemv(in.op)) return mfma_geo<HD>(P, in).chunks() * kChunk;
     switch (in.op) {
         case OP_QKV:
         case OP_HEAD: return align_chunk(in.count * (uint32_t)P.d * 2u);
@@ -334,7 +338,7 @@ __device__ __forceinline__ uint32_t landed_prefix(const Ctl* ctl) {
     return m;
 }
 
-template <int HD>
+template <int HD, bool MF>
 __device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* ring, int k, uint32_t q0, uint32_t q1,
                                             const int32_t* ctx) {
     const uint32_t N = P.ring_chunks;
@@ -404,7 +408,7 @@ __device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* rin
     };
     for (uint32_t i = q0; i < q1 && !stop; ++i) {
         const Instr in = ld_const(P.instrs + i);
-        const uint32_t nch = instr_bytes<HD>(P, in, ctx) / kChunk;
+        const uint32_t nch = instr_bytes<HD, MF>(P, in, ctx) / kChunk;
         if (k == 0 && P.trace && lane_id() == 0 && i > q0) {
             uint32_t* rec = P.trace + ((size_t)blockIdx.x * P.trace_stride + (i - 1 - q0)) * kTraceWords;
             rec[5] = (uint32_t)now_ticks();
@@ -415,7 +419,58 @@ __device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* rin
         if (c < ce) {
             const DevLayer Lw = ld_const(P.layers + (in.layer < P.L ? in.layer : 0));
             Stream S;
-            if (setup_stream<HD>(P, in, Lw, ctx, S)) {
+            if (MF && is_gemv(in.op)) {
+                // tile-major chunks: slot l holds row rr = l / PPR of the chunk (tile
+                // row r = h R + rr), piece (l % PPR) ^ (r % PPR) of its run.  Lanes
+                // past the last row re-read the last row: every chunk must be one
+                // load in flight, since the landed count is derived from vmcnt and a
+                // chunk without a load would let an older one be published early.
+                // This loader takes every fourth chunk, so within each unit it always
+                // takes chunks h0 and h0 + 4 (two chunks when a unit has eight): its
+                // lanes' rows and pieces are fixed for the instruction, and the unit
+                // (slice s, group g, k-unit ku, tile tl of the group) advances by
+                // counters.  Rows other than QKV's lie at a fixed stride per tile from
+                // their tile-0 row.
+                const MfmaGeo g = mfma_geo<HD>(P, in);
+                const uint32_t ks = g.K / g.slices, lane = (uint32_t)lane_id();
+                const uint32_t rr = lane / kMfmaPiecesPerRow, pp = lane % kMfmaPiecesPerRow;
+                const uint32_t G4 = g.T >> 2, m = g.T - 4u * G4, ngroups = G4 + (m ? 1u : 0u);
+                const uint32_t h0 = c - cb;  // < 4 <= chunks per unit
+                const uint32_t r0 = h0 * kMfmaChunkRows + rr, r1 = (h0 + 4u) * kMfmaChunkRows + rr;
+                const uint32_t pc0 = (pp ^ (r0 % kMfmaPiecesPerRow)) * 16u, pc1 = (pp ^ (r1 % kMfmaPiecesPerRow)) * 16u;
+                const bool linear = in.op != OP_QKV;
+                const char* b0 = (const char*)gemv_row(P, Lw, in, r0);
+                const char* b1 = (const char*)gemv_row(P, Lw, in, r1);
+                const uint64_t tile_stride = in.op == OP_GATEUP ? 8ull * P.d * 2u : 16ull * g.K * 2u;
+                const char* last_row = (const char*)gemv_row(P, Lw, in, g.nrows - 1u);
+                uint32_t hs = 0, sl = 0, grp = 0, ku = 0, tl = 0, gsize = G4 ? 4u : m;
+                for (; c < ce; ) {
+                    if (c >= limit && !make_room()) {
+                        stop = true;
+                        break;
+                    }
+                    const uint32_t t = grp * 4u + tl, r = hs ? r1 : r0, j = t * 16u + r;
+                    const uint32_t colb = (sl * ks + ku * (32u * kMfmaUnitKb)) * 2u + (hs ? pc1 : pc0);
+                    const char* src = j >= g.nrows ? last_row
+                                      : linear     ? (hs ? b1 : b0) + t * tile_stride
+                                                   : (const char*)gemv_row(P, Lw, in, j);
+                    dma_chunk(src + colb, slot);
+                    advance();
+                    if (kMfmaUnitChunks == 8u && hs == 0u) {
+                        hs = 1u;
+                        continue;
+                    }
+                    hs = 0u;
+                    if (++tl == gsize) {
+                        tl = 0;
+                        if (++ku == g.KU) {
+                            ku = 0;
+                            if (++grp == ngroups) grp = 0, ++sl;
+                            gsize = grp < G4 ? 4u : m;
+                        }
+                    }
+                }
+            } else if (setup_stream<HD>(P, in, Lw, ctx, S)) {
                 for (; c < ce; ) {
                     if (c >= limit && !make_room()) {
                         stop = true;
@@ -545,7 +600,295 @@ __device__ __forceinline__ bool gemv_ring_auto(const Params& P, Ctl* ctl, const 
     return gemv_ring<B, 1>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
 }
 
+// Matrix-core GEMV over one column slice of an instruction whose tile-major
+// chunks start at stream byte S0.  Full groups: wave w owns tile 4 g + w and
+// every k-unit of it; the last group of m < 4 tiles is shared: wave w takes the
+// units v = w, w + 4, ... of the group and the four partial tiles are added in
+// wave order through `red` (behind a barrier of the compute waves).  epi(t, v)
+// gets tile t's sums (combine_parts layout).  k-blocks are taken kMfmaBatchKb at
+// a time: one wait for the last of their chunks, all operand reads issued
+// together, and alternate k-blocks go to two accumulators, so neither the LDS
+// latency nor the accumulation chain is paid per k-block.
+constexpr uint32_t kMfmaBatchKb = 8;
+constexpr uint32_t kMfmaBatchUnits = kMfmaBatchKb >= kMfmaUnitKb ? kMfmaBatchKb / kMfmaUnitKb : 1u;
+
+// Operand A of k-block e of the unit whose first chunk sits at ring slot s0 (of
+// N): this lane's tile row r = l % 16 in chunk r / R, piece 4 e + l / 16 at its
+// XOR-swizzled slot.
+__device__ __forceinline__ uint4 unit_a(const char* ring, uint32_t s0, uint32_t N, uint32_t e) {
+    const uint32_t l = (uint32_t)lane_id(), r = l & 15u, p = e * 4u + (l >> 4);
+    uint32_t ci = s0 + r / kMfmaChunkRows;
+    ci = ci >= N ? ci - N : ci;
+    const uint32_t slot = (r % kMfmaChunkRows) * kMfmaPiecesPerRow + (p ^ (r % kMfmaPiecesPerRow));
+    return *(const uint4*)(ring + ci * kChunk + slot * 16u);
+}
+
+template <int B, int PRT, class Epi>
+__device__ __forceinline__ bool gemv_mfma_ring(const Params& P, Ctl* ctl, const char* ring, uint32_t S0,
+                                               const MfmaGeo& g, const char* area, char* red, int wave, uint32_t& lw,
+                                               Epi& epi, CwBarrier& barrier) {
+    constexpr uint32_t PB = (uint32_t)(PRT * B), PBP = (uint32_t)parts_pitch(B);
+    constexpr uint32_t U = kMfmaBatchUnits, KBU = kMfmaUnitKb, NC = kMfmaUnitChunks;
+    const uint32_t c0 = S0 / kChunk, N = P.ring_chunks;
+    const uint32_t G4 = g.T >> 2;
+    for (uint32_t grp = 0; grp < G4; ++grp) {
+        floatx4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = d0;
+        const uint32_t cb = c0 + NC * (grp * 4u * g.KU + (uint32_t)wave);  // first chunk of k-unit 0
+        for (uint32_t k0 = 0; k0 < g.KU; k0 += U) {
+            const uint32_t n = min(U, g.KU - k0);
+            set_consumed(ctl, wave, cb + k0 * 4u * NC);
+            if (!wait_landed(P, ctl, cb + (k0 + n - 1u) * 4u * NC + NC, lw)) return false;
+            uint4 a[U * KBU];
+            bf16x8_t b[U * KBU];
+#pragma unroll
+            for (uint32_t u = 0; u < U; ++u)
+                if (u < n) {
+                    const uint32_t s0 = (cb + (k0 + u) * 4u * NC) % N;
+#pragma unroll
+                    for (uint32_t e = 0; e < KBU; ++e) {
+                        a[u * KBU + e] = unit_a(ring, s0, N, e);
+                        b[u * KBU + e] = load_parts(area, (k0 + u) * KBU + e, PB, PBP);
+                    }
+                }
+#pragma unroll
+            for (uint32_t u = 0; u < U; ++u)
+                if (u < n) {
+#pragma unroll
+                    for (uint32_t e = 0; e < KBU; ++e) {
+                        if (e & 1u) d1 = mfma_acc(a[u * KBU + e], b[u * KBU + e], d1);
+                        else d0 = mfma_acc(a[u * KBU + e], b[u * KBU + e], d0);
+                    }
+                }
+        }
+        epi(grp * 4u + (uint32_t)wave, combine_parts<PRT>(d0 + d1));
+    }
+    const uint32_t m = g.T - 4u * G4;
+    if (m) {
+        floatx4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = d0, d2 = d0;
+        const uint32_t base = c0 + NC * G4 * 4u * g.KU, total = m * g.KU;  // units of the last group
+        for (uint32_t v0 = (uint32_t)wave; v0 < total; v0 += 4u * U) {
+            const uint32_t n = min(U, (total - v0 + 3u) / 4u);  // units v0, v0 + 4, ... below total
+            set_consumed(ctl, wave, base + NC * v0);
+            if (!wait_landed(P, ctl, base + NC * (v0 + 4u * (n - 1u)) + NC, lw)) return false;
+            uint4 a[U * KBU];
+            bf16x8_t b[U * KBU];
+#pragma unroll
+            for (uint32_t i = 0; i < U; ++i)
+                if (i < n) {
+                    const uint32_t v = v0 + 4u * i, ku = v / m, s0 = (base + NC * v) % N;
+#pragma unroll
+                    for (uint32_t e = 0; e < KBU; ++e) {
+                        a[i * KBU + e] = unit_a(ring, s0, N, e);
+                        b[i * KBU + e] = load_parts(area, ku * KBU + e, PB, PBP);
+                    }
+                }
+#pragma unroll
+            for (uint32_t i = 0; i < U; ++i)
+                if (i < n) {
+                    const uint32_t v = v0 + 4u * i, t = v - (v / m) * m;
+                    floatx4_t x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
+#pragma unroll
+                    for (uint32_t e = 0; e < KBU; ++e) {
+                        if (e & 1u) x1 = mfma_acc(a[i * KBU + e], b[i * KBU + e], x1);
+                        else x0 = mfma_acc(a[i * KBU + e], b[i * KBU + e], x0);
+                    }
+                    const floatx4_t x = x0 + x1;
+                    if (t == 0) d0 += x;
+                    else if (t == 1) d1 += x;
+                    else d2 += x;
+                }
+        }
+        red_store<PB>(red, wave, 0, d0);
+        if (m > 1) red_store<PB>(red, wave, 1, d1);
+        if (m > 2) red_store<PB>(red, wave, 2, d2);
+        if (!barrier()) return false;
+        if ((uint32_t)wave < m) epi(4u * G4 + (uint32_t)wave, combine_parts<PRT>(red_sum<PB>(red, (uint32_t)wave)));
+    }
+    return true;
+}
+
+// Lane of a combined tile: holds rows 4 (lane / 16) + r of batch row b when it is
+// the part-0 lane of b (column PRT b).
+template <int B, int PRT>
+__device__ __forceinline__ bool mfma_lane(int& b, uint32_t& row4) {
+    const uint32_t l = (uint32_t)lane_id(), j = l & 15u;
+    b = (int)(j / (uint32_t)PRT);
+    row4 = (l >> 4) * 4u;
+    return j % (uint32_t)PRT == 0u && j < (uint32_t)(PRT * B);
+}
+
+// One GEMV instruction (QKV, O, GATEUP, DOWN or the LM head) on the matrix cores:
+// the staged activations land as bf16 parts at the start of the activation
+// area, the cross-wave partial tiles at its end.  Same epilogues as the VALU
+// path; each used lane of a combined tile owns four consecutive rows of one
+// batch row.
 template <int B, int HD>
+__device__ __forceinline__ bool mfma_instr(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs,
+                                        int wave, const Instr& in, uint32_t S, Spin& spin, CwBarrier& barrier,
+                                        uint32_t& land_wait, uint32_t* tr) {
+    constexpr int PRT = mfma_parts(B);
+    constexpr uint32_t PB = (uint32_t)(PRT * B);
+    const int lane = lane_id();
+    const int layer = in.layer;
+    const DevLayer Lw = ld_const(P.layers + (layer < P.L ? layer : 0));
+    char* area = (char*)xs;
+    char* red = (char*)xs + P.x_bytes - mfma_red_bytes(B);
+    const MfmaGeo g = mfma_geo<HD>(P, in);
+    int lb;
+    uint32_t row4;
+    const bool lane_ok = mfma_lane<B, PRT>(lb, row4);
+    lb = lb < B ? lb : B - 1;
+    if (in.op == OP_O || in.op == OP_DOWN) {
+        const bool is_o = in.op == OP_O;
+        const uint32_t K = is_o ? (uint32_t)(P.Hq * HD) : (uint32_t)P.F;
+        const uint32_t tag_x = is_o ? phase_tag(A.tag0, layer, 1) : phase_tag(A.tag0, layer, 3);
+        const uint32_t tag_res = is_o ? phase_tag(A.tag0, layer - 1, 4) : phase_tag(A.tag0, layer, 2);
+        const uint32_t tag_out = is_o ? phase_tag(A.tag0, layer, 2) : phase_tag(A.tag0, layer, 4);
+        const uint32_t ns = g.slices, Ks = K / ns;
+        float* hres = (float*)(area + parts_bytes(B, (int)Ks));  // [B][count] residual rows
+        float* part = hres + B * in.count;                        // [B][count] partial sums
+        for (uint32_t ks = 0; ks < ns; ++ks) {
+            if (ks > 0 && !barrier()) return false;
+            float ss[1] = {0.f};
+            const StageSeg sx = {(is_o ? P.attn : P.act) + ks * Ks, (float*)area, nullptr, Ks, (uint32_t)B, K, Ks,
+                                 tag_x, (uint32_t)PRT};
+            if (ks > 0) {
+                const StageSeg sg[1] = {sx};
+                if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kComputeWaves, spin, ss)) return false;
+            } else if (is_o && layer == 0) {
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+                    stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * P.d + in.begin, in.count,
+                               hres + b * in.count, nullptr, wave, kComputeWaves, ss[0]);
+                const StageSeg sg[1] = {sx};
+                if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kComputeWaves, spin, ss)) return false;
+            } else {
+                const StageSeg sg[2] = {sx, {P.h + in.begin, hres, nullptr, in.count, (uint32_t)B, (uint32_t)P.d,
+                                             in.count, tag_res, 0u}};
+                if (!stage_segs<kStagePassWordsWide, 1, 2>(sg, wave, kComputeWaves, spin, ss)) return false;
+            }
+            if (!barrier()) return false;
+            if (tr && lane == 0 && ks == 0) tr[2] = (uint32_t)now_ticks();
+            const bool last = ks + 1 == ns;
+            auto epi = [&](uint32_t t, floatx4_t v) {
+                if (!lane_ok) return;
+#pragma unroll
+                for (uint32_t r = 0; r < 4u; ++r) {
+                    const uint32_t j = t * 16u + row4 + r;
+                    if (j < in.count) {
+                        float x = v[r];
+                        if (ks > 0) x = part[lb * in.count + j] + x;
+                        if (!last) part[lb * in.count + j] = x;
+                        else st_tagged(P.h + (size_t)lb * P.d + in.begin + j, hres[lb * in.count + j] + x, tag_out);
+                    }
+                }
+            };
+            if (!gemv_mfma_ring<B, PRT>(P, ctl, ring, S + ks * g.T * g.KU * kMfmaUnitChunks * kChunk, g, area, red, wave, land_wait,
+                                        epi, barrier))
+                return false;
+        }
+        return true;
+    }
+    // QKV, GATEUP, HEAD: RMSNorm of the residual stream, then the rows
+    const uint16_t* gain = in.op == OP_QKV ? Lw.attn_norm : in.op == OP_GATEUP ? Lw.mlp_norm : P.final_norm;
+    const uint32_t tag_in = in.op == OP_QKV      ? phase_tag(A.tag0, layer - 1, 4)
+                            : in.op == OP_GATEUP ? phase_tag(A.tag0, layer, 2)
+                                                 : phase_tag(A.tag0, P.L - 1, 4);
+    const uint32_t d = (uint32_t)P.d;
+    float ss[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) ss[b] = 0.f;
+    if (in.op == OP_QKV && layer == 0) {
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+            stage_bf16_parts<PRT>(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * d, d, area, (uint32_t)b,
+                                  (uint32_t)parts_pitch(B), gain, wave, kComputeWaves, ss[b]);
+    } else {
+        const StageSeg sg[1] = {{P.h, (float*)area, gain, d, (uint32_t)B, d, d, tag_in, (uint32_t)PRT}};
+        if (!stage_segs<kStagePassWords, B, 1>(sg, wave, kComputeWaves, spin, ss)) return false;
+    }
+    wave_total_n<B>(ss);
+    if (lane == 0) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) ctl->ss[b][wave] = ss[b];
+    }
+    if (!barrier()) return false;
+    float r[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) r[b] = rms_scale(ctl->ss[b], kComputeWaves, P.d, P.eps);
+    const float rl = pick<B>(r, lb);
+    if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
+    if (in.op == OP_QKV) {
+        const uint32_t tag_out = phase_tag(A.tag0, layer, 0);
+        auto epi = [&](uint32_t t, floatx4_t v) {
+            if (!lane_ok) return;
+#pragma unroll
+            for (uint32_t rr = 0; rr < 4u; ++rr) {
+                const uint32_t j = t * 16u + row4 + rr;
+                if (j < g.nrows) st_tagged(P.qkv + (size_t)lb * P.qkv_rows + in.begin + j, v[rr] * rl, tag_out);
+            }
+        };
+        return gemv_mfma_ring<B, PRT>(P, ctl, ring, S, g, area, red, wave, land_wait, epi, barrier);
+    }
+    if (in.op == OP_GATEUP) {
+        const uint32_t tag_out = phase_tag(A.tag0, layer, 3);
+        auto epi = [&](uint32_t t, floatx4_t v) {
+            if (!lane_ok) return;
+#pragma unroll
+            for (uint32_t pr = 0; pr < 2u; ++pr) {
+                const uint32_t j = t * 16u + row4 + 2u * pr;  // gate row j, up row j + 1
+                if (j + 1u < g.nrows)
+                    st_tagged(P.act + (size_t)lb * P.F + in.begin + j / 2u,
+                              silu_mul(v[2 * pr] * rl, v[2 * pr + 1] * rl), tag_out);
+            }
+        };
+        return gemv_mfma_ring<B, PRT>(P, ctl, ring, S, g, area, red, wave, land_wait, epi, barrier);
+    }
+    // LM head: logits, and each lane's best row of its batch row
+    float bv = -INFINITY;
+    int32_t bi = 0x7FFFFFFF;
+    bool nan_seen = false;
+    auto epi = [&](uint32_t t, floatx4_t v) {
+        if (!lane_ok) return;
+#pragma unroll
+        for (uint32_t rr = 0; rr < 4u; ++rr) {
+            const uint32_t j = t * 16u + row4 + rr;
+            if (j < g.nrows) {
+                const float x = v[rr] * rl;
+                const int32_t row = (int32_t)(in.begin + j);
+                if (x != x) nan_seen = true;
+                if (head_better(x, row, bv, bi)) {
+                    bv = x;
+                    bi = row;
+                }
+                A.logits[(size_t)lb * P.V + row] = x;
+            }
+        }
+    };
+    if (!gemv_mfma_ring<B, PRT>(P, ctl, ring, S, g, area, red, wave, land_wait, epi, barrier)) return false;
+    // the four lanes of a column (lane % 16) hold disjoint rows of one batch row
+#pragma unroll
+    for (int msk = 16; msk <= 32; msk <<= 1) {
+        const float ov = __shfl_xor(bv, msk, 64);
+        const int32_t oi = __shfl_xor(bi, msk, 64);
+        if (head_better(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    }
+    float best_v[B];
+    int32_t best_i[B];
+    const bool any_nan = __any(nan_seen);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        best_v[b] = any_nan ? __int_as_float(0x7FC00000)
+                            : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), PRT * b));
+        best_i[b] = __builtin_amdgcn_readlane(bi, PRT * b);
+    }
+    return head_publish<B>(P, A, in.slot * kComputeWaves + (uint32_t)wave, best_v, best_i, spin);
+}
+
+template <int B, int HD, bool MF>
 __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs, int wave,
                              uint32_t q0, uint32_t q1, const int32_t* ctx) {
     const int lane = lane_id();
@@ -554,7 +897,7 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
     CwBarrier barrier{ctl, &P, 0u};
     for (uint32_t qi = q0; qi < q1; ++qi, ++k) {
         const Instr in = ld_const(P.instrs + qi);
-        const uint32_t bytes = instr_bytes<HD>(P, in, ctx);
+        const uint32_t bytes = instr_bytes<HD, MF>(P, in, ctx);
         uint32_t* tr =
             (P.trace && wave == 0) ? P.trace + ((size_t)blockIdx.x * P.trace_stride + k) * kTraceWords : nullptr;
         if (tr && lane == 0) {
@@ -568,7 +911,9 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
         const int layer = in.layer;
         const DevLayer Lw = ld_const(P.layers + (layer < P.L ? layer : 0));
         bool ok = true;
-        switch (in.op) {
+        if (MF && is_gemv(in.op)) {
+            ok = mfma_instr<B, HD>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr);
+        } else switch (in.op) {
             case OP_QKV:
             case OP_GATEUP:
             case OP_HEAD: {
@@ -759,7 +1104,7 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
     }
 }
 
-template <int B, int HD>
+template <int B, int HD, bool MF>
 __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs A) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     __shared__ Ctl ctl;
@@ -776,9 +1121,9 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
     __syncthreads();
     const uint32_t q0 = ld_const(P.queue_off + blockIdx.x), q1 = ld_const(P.queue_off + blockIdx.x + 1);
     if (wave >= kComputeWaves) {
-        loader_wave<HD>(P, &ctl, ring, wave - kComputeWaves, q0, q1, ctl.ctx);
+        loader_wave<HD, MF>(P, &ctl, ring, wave - kComputeWaves, q0, q1, ctl.ctx);
     } else {
-        compute_wave<B, HD>(P, A, &ctl, ring, xs, wave, q0, q1, ctl.ctx);
+        compute_wave<B, HD, MF>(P, A, &ctl, ring, xs, wave, q0, q1, ctl.ctx);
     }
 }
 
@@ -789,13 +1134,14 @@ size_t megakernel_lds_bytes(const Params& P) { return (size_t)P.ring_chunks * kC
 
 template <int B, int HD>
 static hipError_t launch_t(const Params& P, const StepArgs& A, hipStream_t stream) {
-    const void* fn = (const void*)mk_megakernel<B, HD>;
+    const void* fn = P.gemv_mfma ? (const void*)mk_megakernel<B, HD, true> : (const void*)mk_megakernel<B, HD, false>;
     const size_t lds = megakernel_lds_bytes(P);
-    static size_t configured = 0;
-    if (configured < lds) {
+    static size_t configured[2] = {0, 0};  // per kernel (VALU, matrix cores)
+    size_t& cfgd = configured[P.gemv_mfma ? 1 : 0];
+    if (cfgd < lds) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        configured = lds;
+        cfgd = lds;
     }
     void* args[] = {(void*)&P, (void*)&A};
     // A plain launch: one workgroup fills a compute unit's LDS, and the host

@@ -183,6 +183,168 @@ struct Spin {
 };
 
 // ---------------------------------------------------------------------------------------------
+// GEMV on the matrix cores (v_mfma_f32_16x16x32_bf16).  A tile is 16 consecutive
+// rows of an instruction's row sequence; a k-block is 32 columns.  Operand A is
+// the weights: lane l holds row l % 16, columns 8 (l / 16) .. + 7 of the k-block
+// (16 bytes).  Operand B holds the activations split into PRT bf16 parts
+// x = x_1 + x_2 (+ x_3), each exact as a bf16 product with a weight: column
+// j = PRT b + p of B is part p of batch row b (lanes with j >= PRT B hold zeros).
+// D[i][j] (lane l: rows 4 (l / 16) + r, column l % 16) summed over the parts of
+// batch row b is the dot product of row i with x_b, accumulated in fp32.
+// Three parts carry 24 mantissa bits (the fp32 value up to rounding of the sum);
+// two parts, used from batch 6 on where 3 B columns exceed 16, carry 16.
+// ---------------------------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+// Row j of an instruction's row sequence: QKV [Wq; Wk; Wv] rows from `begin`;
+// GATEUP gate row, up row of f = begin + j / 2; the others rows from `begin`.
+template <int OP>
+__device__ __forceinline__ const uint16_t* gemv_row_ptr(const Params& P, const DevLayer& Lw, uint32_t begin,
+                                                        uint32_t j) {
+    if (OP == OP_QKV) {
+        const uint32_t row = begin + j, nq = (uint32_t)(P.Hq * P.hd), nk = (uint32_t)(P.Hkv * P.hd);
+        return row < nq ? Lw.wq + (size_t)row * P.d
+             : row < nq + nk ? Lw.wk + (size_t)(row - nq) * P.d
+                             : Lw.wv + (size_t)(row - nq - nk) * P.d;
+    } else if (OP == OP_GATEUP) {
+        return ((j & 1u) ? Lw.w_up : Lw.w_gate) + (size_t)(begin + (j >> 1)) * P.d;
+    } else if (OP == OP_HEAD) {
+        return P.head + (size_t)(begin + j) * P.d;
+    } else if (OP == OP_O) {
+        return Lw.wo + (size_t)(begin + j) * (P.Hq * P.hd);
+    } else {
+        return Lw.w_down + (size_t)(begin + j) * P.F;
+    }
+}
+
+// Byte offset in the activation-parts area of column j (part p of batch row b is
+// column PRT b + p) of element k: [k-block][k-group of 8][slot j < pitch][8 bf16].
+__device__ __forceinline__ uint32_t part_offset(uint32_t k, uint32_t j, uint32_t pitch) {
+    return ((((k >> 5) * 4u + ((k >> 3) & 3u)) * pitch + j) * 8u + (k & 7u)) * 2u;
+}
+
+// Splits v into PRT bf16 parts (round to nearest even at each step) and stores
+// them for element k of batch row b.
+template <int PRT>
+__device__ __forceinline__ void store_parts(char* area, uint32_t k, uint32_t b, uint32_t pitch, float v) {
+    float rem = v;
+#pragma unroll
+    for (int p = 0; p < PRT; ++p) {
+        const uint32_t h = f_to_bf(rem);
+        *(uint16_t*)(area + part_offset(k, (uint32_t)PRT * b + (uint32_t)p, pitch)) = (uint16_t)h;
+        rem = rem - __uint_as_float(h << 16);
+    }
+}
+
+// Operand B of k-block kb for this lane (zeros past the PB used columns).
+__device__ __forceinline__ bf16x8_t load_parts(const char* area, uint32_t kb, uint32_t PB, uint32_t pitch) {
+    const uint32_t l = (uint32_t)lane_id(), j = l & 15u, kg = l >> 4;
+    uint4 u = make_uint4(0u, 0u, 0u, 0u);
+    if (j < PB) u = *(const uint4*)(area + (((kb * 4u + kg) * pitch + j) * 16u));
+    return __builtin_bit_cast(bf16x8_t, u);
+}
+
+__device__ __forceinline__ floatx4_t mfma_acc(uint4 a, bf16x8_t b, floatx4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), b, c, 0, 0, 0);
+}
+
+// Sum of the PRT part columns into the lane of part 0 (lanes j = PRT b): the
+// neighbours' values come over with DPP row shifts.  Other lanes hold partial sums.
+template <int PRT>
+__device__ __forceinline__ floatx4_t combine_parts(floatx4_t d) {
+    floatx4_t s;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float v1 = __builtin_amdgcn_update_dpp(0.0f, d[r], 0x101, 0xF, 0xF, false);  // row_shl:1
+        float t = d[r] + v1;
+        if (PRT == 3) t += __builtin_amdgcn_update_dpp(0.0f, d[r], 0x102, 0xF, 0xF, false);  // row_shl:2
+        s[r] = t;
+    }
+    return s;
+}
+
+// Tile-major chunks of a matrix-core GEMV instruction, column slice by column
+// slice.  A chunk holds R = kMfmaChunkRows rows of a tile, each row's 1024 /
+// kMfmaChunkRows bytes whole (the weight loads read whole 128-byte lines and
+// longer runs of a row); a unit is the 16 / kMfmaChunkRows chunks that make up
+// 16 rows (one tile) x kMfmaUnitKb k-blocks of 32 columns.  Units run
+// k-unit-major over groups of four tiles (the four waves, one tile each, consume
+// the stream in step), then over the last group of m < 4 tiles the same way.  In
+// a chunk, piece p (16 bytes) of its row rr (row r = 16-row tile row) sits at
+// slot rr * PPR + (p ^ (r % PPR)), PPR = pieces per chunk row: the XOR spreads
+// the sixteen lanes that read one column of pieces over different LDS banks.
+constexpr uint32_t kMfmaPiecesPerRow = 64u / kMfmaChunkRows;
+constexpr uint32_t kMfmaUnitChunks = 16u / kMfmaChunkRows;
+constexpr uint32_t kMfmaUnitKb = kMfmaPiecesPerRow / 4u;  // k-blocks of 32 columns per unit
+// 4 or 8 chunks per unit: a loader (every fourth chunk) takes one or two of each
+static_assert(kMfmaChunkRows == 2 || kMfmaChunkRows == 4, "chunk rows");
+
+struct MfmaGeo {
+    uint32_t nrows, T, KU, slices, K;  // rows, tiles, k-units per slice, slices, row length
+    __device__ __forceinline__ uint32_t chunks() const { return slices * T * KU * kMfmaUnitChunks; }
+    // chunk c of the instruction -> slice s, tile t, k-unit ku, chunk h of the unit
+    __device__ __forceinline__ void locate(uint32_t c, uint32_t& s, uint32_t& t, uint32_t& ku, uint32_t& h) const {
+        const uint32_t per = T * KU * kMfmaUnitChunks;
+        s = c / per;
+        const uint32_t u = c - s * per, v = u / kMfmaUnitChunks, G4 = T >> 2, full = G4 * 4u * KU;
+        h = u % kMfmaUnitChunks;
+        if (v < full) {
+            const uint32_t g = v / (4u * KU), w = v - g * 4u * KU;
+            ku = w >> 2;
+            t = g * 4u + (w & 3u);
+        } else {
+            const uint32_t m = T - 4u * G4, w = v - full;
+            ku = w / m;
+            t = 4u * G4 + (w - ku * m);
+        }
+    }
+};
+
+template <int HD>
+__device__ __forceinline__ MfmaGeo mfma_geo(const Params& P, const Instr& in) {
+    MfmaGeo g;
+    g.nrows = in.op == OP_GATEUP ? 2u * in.count : in.count;
+    g.K = in.op == OP_O ? (uint32_t)(P.Hq * HD) : in.op == OP_DOWN ? (uint32_t)P.F : (uint32_t)P.d;
+    g.slices = in.op == OP_DOWN ? (uint32_t)P.down_slices : 1u;
+    g.KU = g.K / g.slices / (32u * kMfmaUnitKb);
+    g.T = (g.nrows + 15u) / 16u;
+    return g;
+}
+
+// Row j of instruction `in`'s row sequence, by op.
+__device__ __forceinline__ const uint16_t* gemv_row(const Params& P, const DevLayer& Lw, const Instr& in, uint32_t j) {
+    switch (in.op) {
+        case OP_QKV: return gemv_row_ptr<OP_QKV>(P, Lw, in.begin, j);
+        case OP_GATEUP: return gemv_row_ptr<OP_GATEUP>(P, Lw, in.begin, j);
+        case OP_O: return gemv_row_ptr<OP_O>(P, Lw, in.begin, j);
+        case OP_DOWN: return gemv_row_ptr<OP_DOWN>(P, Lw, in.begin, j);
+        default: return gemv_row_ptr<OP_HEAD>(P, Lw, in.begin, j);
+    }
+}
+
+// Partial tile of wave w: used lanes store their 4 sums; the owner adds the four
+// waves' partials in wave order (unused lanes give zeros).
+template <int PB>
+__device__ __forceinline__ void red_store(char* red, int w, uint32_t t, floatx4_t d) {
+    const uint32_t l = (uint32_t)lane_id(), j = l & 15u, kg = l >> 4;
+    if (j < (uint32_t)PB) *(floatx4_t*)(red + ((((uint32_t)w * 3u + t) * 4u + kg) * PB + j) * 16u) = d;
+}
+template <int PB>
+__device__ __forceinline__ floatx4_t red_sum(const char* red, uint32_t t) {
+    const uint32_t l = (uint32_t)lane_id(), j = l & 15u, kg = l >> 4;
+    floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+    if (j < (uint32_t)PB) {
+#pragma unroll
+        for (uint32_t w = 0; w < 4u; ++w) {
+            const floatx4_t v = *(const floatx4_t*)(red + (((w * 3u + t) * 4u + kg) * PB + j) * 16u);
+            s = w == 0 ? v : s + v;
+        }
+    }
+    return s;
+}
+
+// ---------------------------------------------------------------------------------------------
 // Staging of tagged activations into LDS.  A segment is `rows` rows of n tagged
 // words (row r at src + r * src_stride) that land as fp32 at dst + r * dst_stride,
 // optionally times a bf16 gain g[i] (the RMSNorm weight).  The segments of one
@@ -199,6 +361,7 @@ struct StageSeg {
     const uint16_t* g;  // gain, or nullptr
     uint32_t n, rows, src_stride, dst_stride;
     uint32_t tag;       // tag the words must carry
+    uint32_t parts;     // 0: fp32 rows at dst; 2 or 3: bf16 parts for the matrix cores in the area at dst
 };
 
 // Element e of the concatenated segments resolved to its row's source, target,
@@ -207,10 +370,13 @@ struct StageSeg {
 // per-lane value, which would move it to scratch memory).
 struct StageLoc {
     const uint64_t* src;  // the tagged word
-    float* dst;           // where its value lands
+    float* dst;           // where its value lands (fp32 rows), or the parts area
     const uint16_t* g;    // its gain, or nullptr
     uint32_t tag;
     uint32_t row;
+    uint32_t idx;         // element index within the row
+    uint32_t parts;       // 0, or the number of bf16 parts (area of parts * rows columns)
+    uint32_t pitch;       // slots per row of the parts area
 };
 
 template <class T>
@@ -227,7 +393,7 @@ struct StageMap {
     const uint64_t* src[NS];
     float* dst[NS];
     const uint16_t* g[NS];
-    uint32_t n[NS], rows[NS], ss[NS], ds[NS], tag[NS], end[NS];
+    uint32_t n[NS], rows[NS], ss[NS], ds[NS], tag[NS], end[NS], parts[NS];
     uint32_t total;
     __device__ __forceinline__ explicit StageMap(const StageSeg (&s)[NS]) {
         uint32_t t = 0;
@@ -240,6 +406,7 @@ struct StageMap {
             ss[i] = uniform_u(s[i].src_stride);
             ds[i] = uniform_u(s[i].dst_stride);
             tag[i] = uniform_u(s[i].tag);
+            parts[i] = uniform_u(s[i].parts);
             rows[i] = uniform_u(s[i].rows);
             t += n[i] * rows[i];
             end[i] = t;
@@ -250,7 +417,7 @@ struct StageMap {
         const uint64_t* sp = src[0];
         float* dp = dst[0];
         const uint16_t* gp = g[0];
-        uint32_t nn = n[0], nr = rows[0], s1 = ss[0], d1 = ds[0], tg = tag[0], e0 = 0;
+        uint32_t nn = n[0], nr = rows[0], s1 = ss[0], d1 = ds[0], tg = tag[0], pt = parts[0], e0 = 0;
 #pragma unroll
         for (int k = 1; k < NS; ++k) {
             const bool in = e >= end[k - 1];
@@ -262,6 +429,7 @@ struct StageMap {
             s1 = in ? ss[k] : s1;
             d1 = in ? ds[k] : d1;
             tg = in ? tag[k] : tg;
+            pt = in ? parts[k] : pt;
             e0 = in ? end[k - 1] : e0;
         }
         // row of element x of the segment by comparisons (at most kMaxBatch rows):
@@ -271,7 +439,8 @@ struct StageMap {
 #pragma unroll
         for (int k = 1; k < kMaxBatch; ++k) r += ((uint32_t)k < nr && x >= (uint32_t)k * nn) ? 1u : 0u;
         const uint32_t i = x - r * nn;
-        return StageLoc{sp + (size_t)r * s1 + i, dp + (size_t)r * d1 + i, gp ? gp + i : nullptr, tg, r};
+        return StageLoc{sp + (size_t)r * s1 + i, pt ? dp : dp + (size_t)r * d1 + i, gp ? gp + i : nullptr, tg, r, i,
+                        pt, (pt * nr) | 1u};
     }
 };
 
@@ -321,14 +490,16 @@ __device__ __forceinline__ bool stage_segs(const StageSeg (&sg)[NS], int w, int 
             if (e < total) {
                 const StageLoc L = map.locate(e);
                 const float x = tv_val(v[k]);
+                float y = x;
                 if (L.g) {
 #pragma unroll
                     for (int rr = 0; rr < R; ++rr)
                         if (rr == (int)L.row) ss[rr] = fmaf(x, x, ss[rr]);
-                    *L.dst = x * bf_to_f((uint16_t)gv[k]);
-                } else {
-                    *L.dst = x;
+                    y = x * bf_to_f((uint16_t)gv[k]);
                 }
+                if (L.parts == 3u) store_parts<3>((char*)L.dst, L.idx, L.row, L.pitch, y);
+                else if (L.parts == 2u) store_parts<2>((char*)L.dst, L.idx, L.row, L.pitch, y);
+                else *L.dst = y;
             }
         }
         return true;
@@ -357,6 +528,20 @@ __device__ __forceinline__ void stage_bf16(const uint16_t* __restrict__ src, uin
         const float x = bf_to_f(src[e]);
         ss = fmaf(x, x, ss);
         dst[e] = g ? x * bf_to_f(g[e]) : x;
+    }
+}
+
+// As stage_bf16, into the bf16 parts of batch row b for the matrix cores.
+template <int PRT>
+__device__ __forceinline__ void stage_bf16_parts(const uint16_t* __restrict__ src, uint32_t n, char* area, uint32_t b,
+                                                 uint32_t pitch, const uint16_t* __restrict__ g, int w, int nw,
+                                                 float& ss) {
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint32_t step = 64u * (uint32_t)nw;
+    for (uint32_t e = 64u * (uint32_t)w + lane; e < n; e += step) {
+        const float x = bf_to_f(src[e]);
+        ss = fmaf(x, x, ss);
+        store_parts<PRT>(area, e, b, pitch, g ? x * bf_to_f(g[e]) : x);
     }
 }
 

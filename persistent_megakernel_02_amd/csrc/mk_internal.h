@@ -36,11 +36,34 @@ static_assert(kMinRingChunks >= 2 * kAttnBlockGroups + 1, "an attention block an
 constexpr int kAttnWavePositions = 64;              // positions one wave scores per block (its score area)
 constexpr uint32_t kDownSliceBytes = 64 * 1024;     // largest fp32 DOWN input slice (all batch rows) staged at once
 
+// Matrix-core GEMV: bf16 parts of each activation (3 while 3 B columns fit the
+// 16 of a tile, else 2) and the LDS bytes of the parts of K activations of B rows.
+// Rows of a 16-row matrix-core tile per 1 KB weight chunk, and the columns of a
+// tile's unit (16 rows x kMfmaUnitCols, 16 / kMfmaChunkRows chunks): every row
+// length of a matrix-core instruction is a multiple of kMfmaUnitCols.
+constexpr int kMfmaChunkRows = 2;
+constexpr int kMfmaUnitCols = 512 / kMfmaChunkRows;
+__host__ __device__ constexpr int mfma_parts(int B) { return 3 * B <= 16 ? 3 : 2; }
+// 16-byte slots per (k-block, k-group) row of the parts area: the PRT * B used
+// columns rounded up to an odd count, so the eight k-groups that 64 consecutive
+// elements fall in start in eight different LDS bank groups.
+__host__ __device__ constexpr int parts_pitch(int B) { return (mfma_parts(B) * B) | 1; }
+__host__ __device__ constexpr size_t parts_bytes(int B, int K) { return (size_t)2 * parts_pitch(B) * K; }
+constexpr uint32_t kMfmaPartsBytes = 72 * 1024;     // largest parts area of a DOWN column slice
+// Partial tiles of a matrix-core GEMV instruction summed across the waves:
+// [wave][tile < 3][k-group][used column] x 16 bytes.
+__host__ __device__ constexpr size_t mfma_red_bytes(int B) { return (size_t)4 * 3 * 4 * (mfma_parts(B) * B) * 16; }
+
 // Column slices of the DOWN projection: the fewest (a power of two) whose input
-// slice, B rows of F / slices fp32 values, fits kDownSliceBytes; 0 if the slices
-// would not be whole 1 KB chunks of a weight row.
-__host__ __device__ constexpr int down_slices_for(int B, int F) {
+// slice fits the LDS budget (fp32: B rows of F / slices values in kDownSliceBytes;
+// matrix cores: their parts in kMfmaPartsBytes); 0 if the slices would not be
+// whole 1 KB chunks (VALU) or whole units of kMfmaUnitCols columns (matrix cores) of a row.
+__host__ __device__ constexpr int down_slices_for(int B, int F, bool mfma = false) {
     int n = 1;
+    if (mfma) {
+        while (parts_bytes(B, F / n) > kMfmaPartsBytes && n < 64) n *= 2;
+        return (F % n == 0 && (F / n) % kMfmaUnitCols == 0) ? n : 0;
+    }
     while ((size_t)B * (size_t)(F / n) * 4u > kDownSliceBytes && n < 64) n *= 2;
     if (n > 1) {
         const int chunks = F % n ? 0 : (F / n) * 2 / 1024;  // 1 KB chunks per row slice: a power of two
@@ -114,7 +137,7 @@ struct Params {
     int32_t L, d, Hq, Hkv, hd, F, V, B, S, G;  // G = Hq / Hkv
     int32_t qkv_rows, nsplit, n_cu, kv_b;      // kv_b = max_batch of the cache layout
     int32_t down_slices;                       // DOWN runs over F in this many column slices (power of 2)
-    int32_t pad_ds;
+    int32_t gemv_mfma;                         // 1: GEMVs on the matrix cores (tile-major weight chunks)
     float eps, attn_scale;
     // weights
     const DevLayer* layers;

@@ -20,6 +20,7 @@ TRACE_WORDS = 12  # uint32 per trace record (include/mk.h, mk_read_trace)
 
 MK_OK, MK_E_INVALID, MK_E_UNSUPPORTED, MK_E_CAPACITY, MK_E_HIP, MK_E_DEVICE_TIMEOUT, MK_E_STATE, MK_E_DEVICE_NAN = range(8)
 MK_MODE_MEGAKERNEL, MK_MODE_GRAPH = 0, 1
+MK_GEMV_AUTO, MK_GEMV_VALU, MK_GEMV_MFMA = 0, 1, 2
 
 EXPORTS = ["mk_query_sizes", "mk_create", "mk_kv_layout", "mk_prefill", "mk_set_context_len", "mk_decode_step",
            "mk_get_context_len", "mk_reset", "mk_debug_inject", "mk_status_string", "mk_last_error",
@@ -119,10 +120,11 @@ def model_config(cfg) -> mk_model_config:
 
 
 def runtime_config(max_batch: int, max_seq: int, mode: int = MK_MODE_MEGAKERNEL, num_cus: int = 0,
-                   spin_timeout_ms: int = 0, attn_splits: int = 0, trace: int = 0) -> mk_runtime_config:
+                   spin_timeout_ms: int = 0, attn_splits: int = 0, trace: int = 0,
+                   gemv_kind: int = MK_GEMV_AUTO) -> mk_runtime_config:
     r = mk_runtime_config()
     r.max_batch, r.max_seq, r.mode, r.num_cus = max_batch, max_seq, mode, num_cus
-    r.gemv_kind, r.spin_timeout_ms, r.trace, r.attn_splits = 0, spin_timeout_ms, trace, attn_splits
+    r.gemv_kind, r.spin_timeout_ms, r.trace, r.attn_splits = gemv_kind, spin_timeout_ms, trace, attn_splits
     return r
 
 
@@ -134,7 +136,7 @@ def mk_query_sizes(cfg: mk_model_config, rt: mk_runtime_config):
 
 def mk_plan_inspect(cfg: mk_model_config, rt: mk_runtime_config, num_cus: int):
     keys = ["cus", "instructions", "ring_chunks", "max_per_cu", "weight_bytes", "verify", "attn_splits", "phases",
-            "x_bytes", "head_instructions"]
+            "x_bytes", "head_instructions", "gemv_kind"]
     out = (ctypes.c_int64 * len(keys))()
     st = lib().mk_plan_inspect(ctypes.byref(cfg), ctypes.byref(rt), num_cus, out, len(keys))
     return st, dict(zip(keys, list(out)))
@@ -156,7 +158,8 @@ class Decoder:
 
     def __init__(self, cfg, weights, max_batch: int, max_seq: int, mode: int = MK_MODE_MEGAKERNEL,
                  device: str = "cuda:0", num_cus: int = 0, spin_timeout_ms: int = 0, attn_splits: int = 0,
-                 device_weights: Optional[Dict[str, object]] = None, trace: int = 0):
+                 device_weights: Optional[Dict[str, object]] = None, trace: int = 0,
+                 gemv_kind: int = 0):
         import torch
 
         self.torch = torch
@@ -165,7 +168,7 @@ class Decoder:
         self.B = max_batch
         self.max_seq = max_seq
         self._c = model_config(cfg)
-        self._rt = runtime_config(max_batch, max_seq, mode, num_cus, spin_timeout_ms, attn_splits, trace)
+        self._rt = runtime_config(max_batch, max_seq, mode, num_cus, spin_timeout_ms, attn_splits, trace, gemv_kind)
         st, ws, kv = mk_query_sizes(self._c, self._rt)
         if st != MK_OK:
             raise MKError(st, "mk_query_sizes")

@@ -130,6 +130,55 @@ def test_schedule_balances_bytes():
         assert max(per) - min(per) <= 1 and sum(per) == R
 
 
+def test_gemv_kind_validation():
+    c = mk.model_config(I.TINY)
+    assert mk.mk_query_sizes(c, mk.runtime_config(1, 64, gemv_kind=3))[0] == mk.MK_E_UNSUPPORTED
+    assert mk.mk_query_sizes(c, mk.runtime_config(1, 64, gemv_kind=-1))[0] == mk.MK_E_UNSUPPORTED
+    # the matrix-core GEMV runs in the persistent mode only
+    graph_mfma = mk.runtime_config(1, 64, mk.MK_MODE_GRAPH, gemv_kind=mk.MK_GEMV_MFMA)
+    assert mk.mk_query_sizes(c, graph_mfma)[0] == mk.MK_E_UNSUPPORTED
+    for b in (1, 2, 4, 8):
+        for kind in (mk.MK_GEMV_AUTO, mk.MK_GEMV_VALU, mk.MK_GEMV_MFMA):
+            assert mk.mk_query_sizes(c, mk.runtime_config(b, 64, gemv_kind=kind))[0] == mk.MK_OK
+
+
+def parts_bytes(batch, k):
+    """bf16 parts of `batch` fp32 rows of k values: 3 parts while 3 * batch
+    columns fit one 16-column matrix-core tile, else 2; at least parts * batch
+    bf16 per element (the area pads its rows to an odd number of 16-byte slots)."""
+    return 2 * (3 if 3 * batch <= 16 else 2) * batch * k
+
+
+@pytest.mark.parametrize("batch", [1, 2, 4, 8])
+def test_mfma_activation_area(batch):
+    """The matrix-core GEMV stages bf16 parts of the activations (plus cross-wave
+    partial tiles); the area still leaves at least the minimum weight ring."""
+    cfg = I.LLAMA_1B
+    st, info = mk.mk_plan_inspect(mk.model_config(cfg), mk.runtime_config(batch, 200, gemv_kind=mk.MK_GEMV_MFMA),
+                                  256)
+    assert st == mk.MK_OK and info["verify"] == 0
+    assert info["x_bytes"] >= max(parts_bytes(batch, cfg.hidden), parts_bytes(batch, cfg.n_q_heads * cfg.head_dim))
+    assert info["ring_chunks"] == (LDS_BYTES - LDS_STATIC - info["x_bytes"]) // CHUNK >= MIN_RING
+
+
+def test_gemv_kind_in_effect():
+    """Automatic selection takes VALU at every batch (the faster kind on the 1B
+    shape at batch 1, 4 and 8 by measurement); MFMA runs where it is asked for and
+    its parts area fits; it is refused where three bf16 parts of the hidden state
+    would leave too small a ring (hidden 4096 at batch 4: 96 KB of parts against
+    64 KB of fp32 for VALU)."""
+    c = mk.model_config(I.LLAMA_1B)
+    for b in (1, 2, 4, 8):
+        assert mk.mk_plan_inspect(c, mk.runtime_config(b, 200), 256)[1]["gemv_kind"] == mk.MK_GEMV_VALU
+        mf = mk.mk_plan_inspect(c, mk.runtime_config(b, 200, gemv_kind=mk.MK_GEMV_MFMA), 256)[1]
+        assert mf["gemv_kind"] == mk.MK_GEMV_MFMA
+    graph = mk.runtime_config(8, 200, mk.MK_MODE_GRAPH)
+    assert mk.mk_plan_inspect(c, graph, 256)[1]["gemv_kind"] == mk.MK_GEMV_VALU
+    wide = mk.model_config(I.replace(I.LLAMA_1B, hidden=4096))
+    assert mk.mk_query_sizes(wide, mk.runtime_config(4, 200, gemv_kind=mk.MK_GEMV_VALU))[0] == mk.MK_OK
+    assert mk.mk_query_sizes(wide, mk.runtime_config(4, 200, gemv_kind=mk.MK_GEMV_MFMA))[0] == mk.MK_E_UNSUPPORTED
+
+
 def test_plan_inspect_rejects_bad_cu_count():
     assert mk.mk_plan_inspect(mk.model_config(I.TINY), rt(), 0)[0] == mk.MK_E_INVALID
     assert mk.mk_plan_inspect(mk.model_config(I.TINY), rt(), 5000)[0] == mk.MK_E_INVALID

@@ -172,12 +172,13 @@ def test_llama1b_b1_full_horizon(llama1b):
     t0 = time.time()
     rt_, rl = oracle_run(I.LLAMA_1B, w, prompt, 128, 161)
     print(f"oracle 160 forward passes in {time.time() - t0:.1f}s", flush=True)
-    print("case 1B b1 megakernel", flush=True)
-    d = _decoder(I.LLAMA_1B, w, 1, 161, 0)
-    gt, gl = gpu_run(d, prompt, rt_, 128)
-    worst, near = compare(rt_, rl, gt, gl, "1B b1 megakernel")
-    assert near <= 2
-    d.close()
+    for kind, name in ((1, "VALU"), (2, "MFMA")):
+        print(f"case 1B b1 megakernel gemv={name}", flush=True)
+        d = _decoder(I.LLAMA_1B, w, 1, 161, 0, gemv_kind=kind)
+        gt, gl = gpu_run(d, prompt, rt_, 128)
+        worst, near = compare(rt_, rl, gt, gl, f"1B b1 megakernel gemv={name}")
+        assert near <= 2
+        d.close()
 
 
 def test_llama1b_b1_graph_matches_megakernel_bitwise(llama1b):
@@ -188,7 +189,7 @@ def test_llama1b_b1_graph_matches_megakernel_bitwise(llama1b):
     outs = []
     for mode in (0, 1):
         print(f"case 1B b1 mode={mode} bitwise", flush=True)
-        d = _decoder(I.LLAMA_1B, w, 1, 64, mode)
+        d = _decoder(I.LLAMA_1B, w, 1, 64, mode, gemv_kind=1 if mode == 0 else 0)
         outs.append(gpu_run(d, prompt, [toks[:, t] for t in range(24)], 24))
         d.close()
     for x, y in zip(outs[0][1], outs[1][1]):
@@ -263,15 +264,59 @@ def test_tiny_batch_4_8(B):
     prompt = I.make_prompt(cfg, B, 6, seed=7)
     rt_, rl = oracle_run(cfg, w, prompt, 10, 20)
     outs = []
-    for mode in (0, 1):
-        print(f"case tiny b{B} mode={mode}", flush=True)
-        d = _decoder(cfg, w, B, 20, mode)
+    for mode, kind in ((0, 1), (1, 0), (0, 2)):
+        print(f"case tiny b{B} mode={mode} gemv={kind}", flush=True)
+        d = _decoder(cfg, w, B, 20, mode, gemv_kind=kind)
         gt, gl = gpu_run(d, prompt, rt_, 10)
-        compare(rt_, rl, gt, gl, f"tiny b{B} mode={mode}")
+        compare(rt_, rl, gt, gl, f"tiny b{B} mode={mode} gemv={kind}")
         outs.append(gl)
         d.close()
+    # VALU in both modes: same tile functions in the same order
     for x, y in zip(outs[0], outs[1]):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("B,cus", [(1, 0), (2, 0), (4, 0), (8, 0), (1, 7), (4, 7), (8, 7)])
+def test_tiny_mfma_gemv(B, cus):
+    """The matrix-core GEMV at every batch size, on all compute units (one or two
+    tiles per instruction: the shared last group) and on 7 (many full groups of
+    four tiles per instruction)."""
+    cfg = I.TINY
+    w = I.make_weights(cfg, seed=10)
+    prompt = I.make_prompt(cfg, B, 6, seed=11)
+    rt_, rl = oracle_run(cfg, w, prompt, 8, 20)
+    print(f"case tiny b{B} cus={cus} gemv=MFMA", flush=True)
+    d = _decoder(cfg, w, B, 20, 0, gemv_kind=2, num_cus=cus)
+    gt, gl = gpu_run(d, prompt, rt_, 8)
+    _, near = compare(rt_, rl, gt, gl, f"tiny b{B} cus={cus} gemv=MFMA")
+    assert near == 0
+    d.close()
+
+
+def test_mfma_two_layer_1b_run_to_run():
+    """Two layers of the 1B shape with the full vocabulary on the matrix cores,
+    three runs of 10 positions: every run matches the oracle and the runs agree
+    bit for bit.  (Regression: a loader chunk whose rows all lay past the end of
+    an instruction issued no load, which let an older chunk be published as
+    landed before its data arrived; it showed as an occasional perturbed step.)"""
+    cfg = I.replace(I.LLAMA_1B, n_layers=2)
+    w = I.make_weights(cfg, seed=0)
+    prompt = I.make_prompt(cfg, 1, 1, seed=0)
+    rt_, rl = oracle_run(cfg, w, prompt, 9, 16)
+    outs = []
+    for rep in range(3):
+        print(f"case 1B two layers gemv=MFMA rep {rep}", flush=True)
+        d = _decoder(cfg, w, 1, 16, 0, gemv_kind=2)
+        gt, gl = gpu_run(d, prompt, rt_, 9)
+        d.close()
+        outs.append(gl)
+    for gl in outs:
+        worst = max(float(np.abs(a - b).max()) for a, b in zip(rl, gl))
+        assert worst <= 1e-3, worst
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+    for a, b in zip(outs[0], outs[2]):
+        assert np.array_equal(a, b)
 
 
 def test_down_column_slices():
@@ -285,25 +330,26 @@ def test_down_column_slices():
     w = I.make_weights(cfg, seed=8)
     prompt = I.make_prompt(cfg, B, 4, seed=8)
     rt_, rl = oracle_run(cfg, w, prompt, 6, 16)
-    for mode in (0, 1):
-        print(f"case wide-ffn b8 mode={mode}", flush=True)
-        d = _decoder(cfg, w, B, 16, mode)
+    for mode, kind in ((0, 1), (0, 2), (1, 0)):
+        print(f"case wide-ffn b8 mode={mode} gemv={kind}", flush=True)
+        d = _decoder(cfg, w, B, 16, mode, gemv_kind=kind)
         gt, gl = gpu_run(d, prompt, rt_, 6)
-        compare(rt_, rl, gt, gl, f"wide-ffn b8 mode={mode}")
+        compare(rt_, rl, gt, gl, f"wide-ffn b8 mode={mode} gemv={kind}")
         d.close()
 
 
-@pytest.mark.parametrize("B,ctx", [(4, 8192), (8, 8192)])
-def test_llama1b_batch_long_context(B, ctx):
+@pytest.mark.parametrize("B,ctx,kind", [(4, 8192, 0), (8, 8192, 0), (8, 8192, 2)],
+                         ids=["b4-auto", "b8-auto", "b8-mfma"])
+def test_llama1b_batch_long_context(B, ctx, kind):
     """The 1B shape at batch 4 and 8 over an 8192-position synthetic context:
-    split attention and sliced DOWN, 3 steps."""
+    split attention and sliced DOWN, 3 steps; at batch 8 also on the matrix cores."""
     cfg = I.LLAMA_1B
     w = I.make_weights(cfg, seed=9)
     steps, S = 3, ctx + 8
     start = I.make_prompt(cfg, B, 1, seed=9)[:, 0]
     orc = O.Oracle(cfg, w, B, S)
-    print(f"case 1B b{B} ctx={ctx} megakernel", flush=True)
-    d = _decoder(cfg, w, B, S, 0)
+    print(f"case 1B b{B} ctx={ctx} megakernel gemv={kind}", flush=True)
+    d = _decoder(cfg, w, B, S, 0, gemv_kind=kind)
     t0 = time.time()
     _fill_context(cfg, orc, d, ctx, seed=9)
     print(f"context filled in {time.time() - t0:.1f}s", flush=True)
