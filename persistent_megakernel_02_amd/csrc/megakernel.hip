@@ -421,54 +421,81 @@ __device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* rin
             Stream S;
             if (MF && is_gemv(in.op)) {
                 // tile-major chunks: slot l holds row rr = l / PPR of the chunk (tile
-                // row r = h R + rr), piece (l % PPR) ^ (r % PPR) of its run.  Lanes
-                // past the last row re-read the last row: every chunk must be one
-                // load in flight, since the landed count is derived from vmcnt and a
-                // chunk without a load would let an older one be published early.
-                // This loader takes every fourth chunk, so within each unit it always
-                // takes chunks h0 and h0 + 4 (two chunks when a unit has eight): its
-                // lanes' rows and pieces are fixed for the instruction, and the unit
-                // (slice s, group g, k-unit ku, tile tl of the group) advances by
-                // counters.  Rows other than QKV's lie at a fixed stride per tile from
-                // their tile-0 row.
+                // row r), piece (l % PPR) ^ (r % PPR) of its run.  Rows past the end
+                // (only in a last-group chunk) re-read the last row: every chunk must
+                // be one load in flight, since the landed count is derived from
+                // vmcnt and a chunk without a load would let an older one be
+                // published early.  Per slice, the full groups and the last group
+                // are walked as two regions.  In the full groups this loader takes
+                // chunks h0 and h0 + 4 of every unit (h0 = its phase at the region
+                // start; the region is a multiple of four chunks long), so its lanes'
+                // rows are fixed and a chunk's address is a lane base plus a uniform
+                // tile and column offset.
                 const MfmaGeo g = mfma_geo<HD>(P, in);
                 const uint32_t ks = g.K / g.slices, lane = (uint32_t)lane_id();
                 const uint32_t rr = lane / kMfmaPiecesPerRow, pp = lane % kMfmaPiecesPerRow;
-                const uint32_t G4 = g.T >> 2, m = g.T - 4u * G4, ngroups = G4 + (m ? 1u : 0u);
-                const uint32_t h0 = c - cb;  // < 4 <= chunks per unit
-                const uint32_t r0 = h0 * kMfmaChunkRows + rr, r1 = (h0 + 4u) * kMfmaChunkRows + rr;
-                const uint32_t pc0 = (pp ^ (r0 % kMfmaPiecesPerRow)) * 16u, pc1 = (pp ^ (r1 % kMfmaPiecesPerRow)) * 16u;
-                const bool linear = in.op != OP_QKV;
-                const char* b0 = (const char*)gemv_row(P, Lw, in, r0);
-                const char* b1 = (const char*)gemv_row(P, Lw, in, r1);
-                const uint64_t tile_stride = in.op == OP_GATEUP ? 8ull * P.d * 2u : 16ull * g.K * 2u;
-                const char* last_row = (const char*)gemv_row(P, Lw, in, g.nrows - 1u);
-                uint32_t hs = 0, sl = 0, grp = 0, ku = 0, tl = 0, gsize = G4 ? 4u : m;
-                for (; c < ce; ) {
-                    if (c >= limit && !make_room()) {
-                        stop = true;
-                        break;
-                    }
-                    const uint32_t t = grp * 4u + tl, r = hs ? r1 : r0, j = t * 16u + r;
-                    const uint32_t colb = (sl * ks + ku * (32u * kMfmaUnitKb)) * 2u + (hs ? pc1 : pc0);
-                    const char* src = j >= g.nrows ? last_row
-                                      : linear     ? (hs ? b1 : b0) + t * tile_stride
-                                                   : (const char*)gemv_row(P, Lw, in, j);
-                    dma_chunk(src + colb, slot);
-                    advance();
-                    if (kMfmaUnitChunks == 8u && hs == 0u) {
-                        hs = 1u;
-                        continue;
-                    }
-                    hs = 0u;
-                    if (++tl == gsize) {
-                        tl = 0;
-                        if (++ku == g.KU) {
-                            ku = 0;
-                            if (++grp == ngroups) grp = 0, ++sl;
-                            gsize = grp < G4 ? 4u : m;
+                const bool qkv = in.op == OP_QKV, gu = in.op == OP_GATEUP;
+                const char* ra = (const char*)gemv_row(P, Lw, in, 0u);
+                const char* rb = (const char*)gemv_row(P, Lw, in, gu ? 1u : 0u);
+                const uint32_t shift = gu ? 1u : 0u;
+                const uint64_t stride = (uint64_t)(gu ? (uint32_t)P.d : g.K) * 2u;
+                auto row_ptr = [&](uint32_t j) -> const char* {  // row j of the instruction
+                    return qkv ? (const char*)gemv_row(P, Lw, in, j)
+                               : ((j & shift) ? rb : ra) + (uint64_t)(j >> shift) * stride;
+                };
+                const uint64_t tile_stride = (uint64_t)stride * (16u >> shift);  // rows of one tile
+                const uint32_t FC = g.full_chunks(), LC = g.KU * g.CR;
+                for (uint32_t sl = 0, rs = cb; sl < g.slices && !stop && c < ce; ++sl) {
+                    const uint32_t col0 = sl * ks * 2u;
+                    if (FC && c < rs + FC) {
+                        const uint32_t h0 = c - rs;  // < 4
+                        const uint32_t r0 = h0 * kMfmaChunkRows + rr, r1 = (h0 + 4u) * kMfmaChunkRows + rr;
+                        const uint32_t p0 = col0 + (pp ^ (r0 % kMfmaPiecesPerRow)) * 16u;
+                        const uint32_t p1 = col0 + (pp ^ (r1 % kMfmaPiecesPerRow)) * 16u;
+                        const char* b0 = row_ptr(r0) + p0;
+                        const char* b1 = row_ptr(r1) + p1;
+                        uint32_t hs = 0, tl = 0, ku = 0, grp = 0;
+                        for (; c < rs + FC; ) {
+                            if (c >= limit && !make_room()) {
+                                stop = true;
+                                break;
+                            }
+                            const uint32_t t = grp * 4u + tl, kc = ku * (64u * kMfmaUnitKb);
+                            // QKV rows span three matrices: their address is taken per chunk
+                            const char* src = qkv ? row_ptr(t * 16u + (hs ? r1 : r0)) + (hs ? p1 : p0) + kc
+                                                  : (hs ? b1 : b0) + (uint64_t)t * tile_stride + kc;
+                            dma_chunk(src, slot);
+                            advance();
+                            if (kMfmaUnitChunks == 8u && hs == 0u) {
+                                hs = 1u;
+                                continue;
+                            }
+                            hs = 0u;
+                            if (++tl == 4u) {
+                                tl = 0;
+                                if (++ku == g.KU) ku = 0, ++grp;
+                            }
                         }
                     }
+                    rs += FC;
+                    if (stop) break;
+                    // the last group: CR chunks per k-unit holding its rows in order
+                    if (c < rs + LC) {
+                        uint32_t x = c - rs, ku = x / g.CR, ch = x - ku * g.CR;
+                        for (; c < rs + LC; ) {
+                            if (c >= limit && !make_room()) {
+                                stop = true;
+                                break;
+                            }
+                            const uint32_t gr = ch * kMfmaChunkRows + rr, r = gr & 15u;
+                            const uint32_t j = min(g.G4 * 64u + gr, g.nrows - 1u);
+                            dma_chunk(row_ptr(j) + col0 + ku * (64u * kMfmaUnitKb) + (pp ^ (r % kMfmaPiecesPerRow)) * 16u,
+                                      slot);
+                            advance();
+                            for (ch += kLoaderWaves; ch >= g.CR; ch -= g.CR) ++ku;
+                        }
+                    }
+                    rs += LC;
                 }
             } else if (setup_stream<HD>(P, in, Lw, ctx, S)) {
                 for (; c < ce; ) {
@@ -602,13 +629,15 @@ __device__ __forceinline__ bool gemv_ring_auto(const Params& P, Ctl* ctl, const 
 
 // Matrix-core GEMV over one column slice of an instruction whose tile-major
 // chunks start at stream byte S0.  Full groups: wave w owns tile 4 g + w and
-// every k-unit of it; the last group of m < 4 tiles is shared: wave w takes the
-// units v = w, w + 4, ... of the group and the four partial tiles are added in
-// wave order through `red` (behind a barrier of the compute waves).  epi(t, v)
-// gets tile t's sums (combine_parts layout).  k-blocks are taken kMfmaBatchKb at
-// a time: one wait for the last of their chunks, all operand reads issued
-// together, and alternate k-blocks go to two accumulators, so neither the LDS
-// latency nor the accumulation chain is paid per k-block.
+// every k-unit of it.  The last group of m tiles is shared: wave w takes the
+// units v = w, w + 4, ... (v = ku m + tile) and the four partial tiles are added
+// in wave order through `red` (behind a barrier of the compute waves); a partial
+// tile's unit has fewer chunks, and the rows past the end read whatever follows
+// (their sums are never stored).  epi(t, v) gets tile t's sums (combine_parts
+// layout).  Units are taken kMfmaBatchUnits at a time: one wait for the last of
+// their chunks, all operand reads issued together, and alternate k-blocks go to
+// two accumulators, so neither the LDS latency nor the accumulation chain is
+// paid per k-block.
 constexpr uint32_t kMfmaBatchKb = 8;
 constexpr uint32_t kMfmaBatchUnits = kMfmaBatchKb >= kMfmaUnitKb ? kMfmaBatchKb / kMfmaUnitKb : 1u;
 
@@ -630,8 +659,7 @@ __device__ __forceinline__ bool gemv_mfma_ring(const Params& P, Ctl* ctl, const 
     constexpr uint32_t PB = (uint32_t)(PRT * B), PBP = (uint32_t)parts_pitch(B);
     constexpr uint32_t U = kMfmaBatchUnits, KBU = kMfmaUnitKb, NC = kMfmaUnitChunks;
     const uint32_t c0 = S0 / kChunk, N = P.ring_chunks;
-    const uint32_t G4 = g.T >> 2;
-    for (uint32_t grp = 0; grp < G4; ++grp) {
+    for (uint32_t grp = 0; grp < g.G4; ++grp) {
         floatx4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = d0;
         const uint32_t cb = c0 + NC * (grp * 4u * g.KU + (uint32_t)wave);  // first chunk of k-unit 0
         for (uint32_t k0 = 0; k0 < g.KU; k0 += U) {
@@ -662,20 +690,30 @@ __device__ __forceinline__ bool gemv_mfma_ring(const Params& P, Ctl* ctl, const 
         }
         epi(grp * 4u + (uint32_t)wave, combine_parts<PRT>(d0 + d1));
     }
-    const uint32_t m = g.T - 4u * G4;
+    const uint32_t m = g.m;
     if (m) {
-        floatx4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = d0, d2 = d0;
-        const uint32_t base = c0 + NC * G4 * 4u * g.KU, total = m * g.KU;  // units of the last group
+        floatx4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = d0, d2 = d0, d3 = d0;
+        const uint32_t base = c0 + g.full_chunks(), total = m * g.KU;  // units of the last group
+        // first chunk and chunk count of unit v (k-unit v / m, tile v % m)
+        auto ustart = [&](uint32_t v, uint32_t& cnt) -> uint32_t {
+            const uint32_t ku = v / m, t = v - ku * m;
+            cnt = min(NC, g.CR - t * NC);
+            return base + ku * g.CR + t * NC;
+        };
         for (uint32_t v0 = (uint32_t)wave; v0 < total; v0 += 4u * U) {
             const uint32_t n = min(U, (total - v0 + 3u) / 4u);  // units v0, v0 + 4, ... below total
-            set_consumed(ctl, wave, base + NC * v0);
-            if (!wait_landed(P, ctl, base + NC * (v0 + 4u * (n - 1u)) + NC, lw)) return false;
+            uint32_t cnt0, cntl;
+            const uint32_t first = ustart(v0, cnt0), lastc = ustart(v0 + 4u * (n - 1u), cntl);
+            set_consumed(ctl, wave, first);
+            if (!wait_landed(P, ctl, lastc + cntl, lw)) return false;
             uint4 a[U * KBU];
             bf16x8_t b[U * KBU];
 #pragma unroll
             for (uint32_t i = 0; i < U; ++i)
                 if (i < n) {
-                    const uint32_t v = v0 + 4u * i, ku = v / m, s0 = (base + NC * v) % N;
+                    const uint32_t v = v0 + 4u * i, ku = v / m;
+                    uint32_t cnt;
+                    const uint32_t s0 = ustart(v, cnt) % N;
 #pragma unroll
                     for (uint32_t e = 0; e < KBU; ++e) {
                         a[i * KBU + e] = unit_a(ring, s0, N, e);
@@ -695,14 +733,16 @@ __device__ __forceinline__ bool gemv_mfma_ring(const Params& P, Ctl* ctl, const 
                     const floatx4_t x = x0 + x1;
                     if (t == 0) d0 += x;
                     else if (t == 1) d1 += x;
-                    else d2 += x;
+                    else if (t == 2) d2 += x;
+                    else d3 += x;
                 }
         }
-        red_store<PB>(red, wave, 0, d0);
-        if (m > 1) red_store<PB>(red, wave, 1, d1);
-        if (m > 2) red_store<PB>(red, wave, 2, d2);
+        red_store<B, PRT>(red, wave, 0, combine_parts<PRT>(d0));
+        if (m > 1) red_store<B, PRT>(red, wave, 1, combine_parts<PRT>(d1));
+        if (m > 2) red_store<B, PRT>(red, wave, 2, combine_parts<PRT>(d2));
+        if (m > 3) red_store<B, PRT>(red, wave, 3, combine_parts<PRT>(d3));
         if (!barrier()) return false;
-        if ((uint32_t)wave < m) epi(4u * G4 + (uint32_t)wave, combine_parts<PRT>(red_sum<PB>(red, (uint32_t)wave)));
+        if ((uint32_t)wave < m) epi(4u * g.G4 + (uint32_t)wave, red_sum<B, PRT>(red, (uint32_t)wave));
     }
     return true;
 }
@@ -783,7 +823,7 @@ __device__ __forceinline__ bool mfma_instr(const Params& P, const StepArgs& A, C
                     }
                 }
             };
-            if (!gemv_mfma_ring<B, PRT>(P, ctl, ring, S + ks * g.T * g.KU * kMfmaUnitChunks * kChunk, g, area, red, wave, land_wait,
+            if (!gemv_mfma_ring<B, PRT>(P, ctl, ring, S + ks * g.slice_chunks() * kChunk, g, area, red, wave, land_wait,
                                         epi, barrier))
                 return false;
         }
@@ -888,6 +928,30 @@ __device__ __forceinline__ bool mfma_instr(const Params& P, const StepArgs& A, C
     return head_publish<B>(P, A, in.slot * kComputeWaves + (uint32_t)wave, best_v, best_i, spin);
 }
 
+// One attention item (sequence, KV head, split) as an instruction.
+template <int B, int HD>
+__device__ __forceinline__ bool attn_instr(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs,
+                                           int wave, const Instr& in, uint32_t S, Spin& spin, CwBarrier& barrier,
+                                           uint32_t& land_wait, uint32_t* tr, const int32_t* ctx) {
+    const int lane = lane_id();
+    const int per_b = P.Hkv * P.nsplit;
+    const int b = (int)in.begin / per_b, g = ((int)in.begin % per_b) / P.nsplit, s = (int)in.begin % P.nsplit;
+    // stream: [RoPE row 1 KB][group 0: K 1 KB, V 1 KB][group 1] ...
+    const RingKV<HD> kv{ring, S + kChunk, P.ring_chunks};
+    auto need = [&](int t) -> bool {  // group t resident (K and V chunks); t = -1: the RoPE row
+        return wait_landed(P, ctl, (S + kChunk + (uint32_t)(t + 1) * 2048u) / kChunk, land_wait);
+    };
+    auto release = [&](int t) {  // groups before t no longer needed by this wave
+        set_consumed(ctl, wave, (S + kChunk + (uint32_t)t * 2048u) / kChunk);
+    };
+    if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
+    auto mark = [&](int m) {
+        if (tr && lane == 0) tr[9 + m] = (uint32_t)now_ticks();
+    };
+    return attn_item<HD>(P, A.tag0, in.layer, b, g, s, ctx_of(ctx, b), kv, need, release, barrier, xs, wave,
+                         kComputeWaves, spin, mark);
+}
+
 template <int B, int HD, bool MF>
 __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs, int wave,
                              uint32_t q0, uint32_t q1, const int32_t* ctx) {
@@ -911,8 +975,10 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
         const int layer = in.layer;
         const DevLayer Lw = ld_const(P.layers + (layer < P.L ? layer : 0));
         bool ok = true;
-        if (MF && is_gemv(in.op)) {
-            ok = mfma_instr<B, HD>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr);
+        // (the matrix-core kernel carries no VALU GEMV code: a smaller kernel)
+        if constexpr (MF) {
+            if (is_gemv(in.op)) ok = mfma_instr<B, HD>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr);
+            else ok = attn_instr<B, HD>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr, ctx);
         } else switch (in.op) {
             case OP_QKV:
             case OP_GATEUP:
@@ -1069,26 +1135,7 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                 }
                 break;
             }
-            case OP_ATTN: {
-                const int per_b = P.Hkv * P.nsplit;
-                const int b = (int)in.begin / per_b, g = ((int)in.begin % per_b) / P.nsplit,
-                          s = (int)in.begin % P.nsplit;
-                // stream: [RoPE row 1 KB][group 0: K 1 KB, V 1 KB][group 1] ...
-                const RingKV<HD> kv{ring, S + kChunk, P.ring_chunks};
-                auto need = [&](int t) -> bool {  // group t resident (K and V chunks); t = -1: the RoPE row
-                    return wait_landed(P, ctl, (S + kChunk + (uint32_t)(t + 1) * 2048u) / kChunk, land_wait);
-                };
-                auto release = [&](int t) {  // groups before t no longer needed by this wave
-                    set_consumed(ctl, wave, (S + kChunk + (uint32_t)t * 2048u) / kChunk);
-                };
-                if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
-                auto mark = [&](int m) {
-                    if (tr && lane == 0) tr[9 + m] = (uint32_t)now_ticks();
-                };
-                ok = attn_item<HD>(P, A.tag0, layer, b, g, s, ctx_of(ctx, b), kv, need, release, barrier, xs, wave,
-                                   kComputeWaves, spin, mark);
-                break;
-            }
+            case OP_ATTN: ok = attn_instr<B, HD>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr, ctx); break;
             default: break;
         }
         if (!ok || lds_ld(&ctl->abort)) return;

@@ -265,15 +265,19 @@ __device__ __forceinline__ floatx4_t combine_parts(floatx4_t d) {
 }
 
 // Tile-major chunks of a matrix-core GEMV instruction, column slice by column
-// slice.  A chunk holds R = kMfmaChunkRows rows of a tile, each row's 1024 /
-// kMfmaChunkRows bytes whole (the weight loads read whole 128-byte lines and
-// longer runs of a row); a unit is the 16 / kMfmaChunkRows chunks that make up
-// 16 rows (one tile) x kMfmaUnitKb k-blocks of 32 columns.  Units run
-// k-unit-major over groups of four tiles (the four waves, one tile each, consume
-// the stream in step), then over the last group of m < 4 tiles the same way.  In
-// a chunk, piece p (16 bytes) of its row rr (row r = 16-row tile row) sits at
-// slot rr * PPR + (p ^ (r % PPR)), PPR = pieces per chunk row: the XOR spreads
-// the sixteen lanes that read one column of pieces over different LDS banks.
+// slice.  A chunk holds R = kMfmaChunkRows rows of a tile, each row's 1024 / R
+// bytes whole (the weight loads read whole 128-byte lines and longer runs of a
+// row).  Within a slice:
+//  - full groups: four full tiles (16 rows) in step, one per wave.  A unit is one
+//    tile's 16 rows x kMfmaUnitCols columns (16 / R chunks); units run
+//    k-unit-major, then tile of the group;
+//  - the last group: the remaining nrows - 64 G4 rows (up to four tiles, the last
+//    one partial), k-unit-major, CR = ceil(rows / R) chunks per k-unit holding
+//    the group's rows in order, so no row past the end is streamed (a chunk may
+//    end past it: those rows re-read the last row).
+// In a chunk, piece p (16 bytes) of its row rr (tile row r) sits at slot
+// rr * PPR + (p ^ (r % PPR)), PPR = pieces per chunk row: the XOR spreads the
+// sixteen lanes that read one column of pieces over different LDS banks.
 constexpr uint32_t kMfmaPiecesPerRow = 64u / kMfmaChunkRows;
 constexpr uint32_t kMfmaUnitChunks = 16u / kMfmaChunkRows;
 constexpr uint32_t kMfmaUnitKb = kMfmaPiecesPerRow / 4u;  // k-blocks of 32 columns per unit
@@ -281,24 +285,13 @@ constexpr uint32_t kMfmaUnitKb = kMfmaPiecesPerRow / 4u;  // k-blocks of 32 colu
 static_assert(kMfmaChunkRows == 2 || kMfmaChunkRows == 4, "chunk rows");
 
 struct MfmaGeo {
-    uint32_t nrows, T, KU, slices, K;  // rows, tiles, k-units per slice, slices, row length
-    __device__ __forceinline__ uint32_t chunks() const { return slices * T * KU * kMfmaUnitChunks; }
-    // chunk c of the instruction -> slice s, tile t, k-unit ku, chunk h of the unit
-    __device__ __forceinline__ void locate(uint32_t c, uint32_t& s, uint32_t& t, uint32_t& ku, uint32_t& h) const {
-        const uint32_t per = T * KU * kMfmaUnitChunks;
-        s = c / per;
-        const uint32_t u = c - s * per, v = u / kMfmaUnitChunks, G4 = T >> 2, full = G4 * 4u * KU;
-        h = u % kMfmaUnitChunks;
-        if (v < full) {
-            const uint32_t g = v / (4u * KU), w = v - g * 4u * KU;
-            ku = w >> 2;
-            t = g * 4u + (w & 3u);
-        } else {
-            const uint32_t m = T - 4u * G4, w = v - full;
-            ku = w / m;
-            t = 4u * G4 + (w - ku * m);
-        }
-    }
+    uint32_t nrows, KU, slices, K;  // rows, k-units per slice, slices, row length
+    uint32_t G4;                    // full groups of four full tiles
+    uint32_t m;                     // tiles of the last group (0 to 4, the last may be partial)
+    uint32_t CR;                    // chunks per k-unit of the last group
+    __device__ __forceinline__ uint32_t full_chunks() const { return G4 * 4u * KU * kMfmaUnitChunks; }
+    __device__ __forceinline__ uint32_t slice_chunks() const { return full_chunks() + KU * CR; }
+    __device__ __forceinline__ uint32_t chunks() const { return slices * slice_chunks(); }
 };
 
 template <int HD>
@@ -308,7 +301,10 @@ __device__ __forceinline__ MfmaGeo mfma_geo(const Params& P, const Instr& in) {
     g.K = in.op == OP_O ? (uint32_t)(P.Hq * HD) : in.op == OP_DOWN ? (uint32_t)P.F : (uint32_t)P.d;
     g.slices = in.op == OP_DOWN ? (uint32_t)P.down_slices : 1u;
     g.KU = g.K / g.slices / (32u * kMfmaUnitKb);
-    g.T = (g.nrows + 15u) / 16u;
+    g.G4 = g.nrows / 64u;
+    const uint32_t rest = g.nrows - 64u * g.G4;
+    g.m = (rest + 15u) / 16u;
+    g.CR = (rest + kMfmaChunkRows - 1u) / kMfmaChunkRows;
     return g;
 }
 
@@ -323,21 +319,22 @@ __device__ __forceinline__ const uint16_t* gemv_row(const Params& P, const DevLa
     }
 }
 
-// Partial tile of wave w: used lanes store their 4 sums; the owner adds the four
-// waves' partials in wave order (unused lanes give zeros).
-template <int PB>
+// Partial tile t of wave w after combine_parts: the part-0 lane of each batch row
+// stores its 4 sums; the owner adds the four waves' partials in wave order.
+template <int B, int PRT>
 __device__ __forceinline__ void red_store(char* red, int w, uint32_t t, floatx4_t d) {
     const uint32_t l = (uint32_t)lane_id(), j = l & 15u, kg = l >> 4;
-    if (j < (uint32_t)PB) *(floatx4_t*)(red + ((((uint32_t)w * 3u + t) * 4u + kg) * PB + j) * 16u) = d;
+    if (j % (uint32_t)PRT == 0u && j < (uint32_t)(PRT * B))
+        *(floatx4_t*)(red + ((((uint32_t)w * 4u + t) * 4u + kg) * B + j / PRT) * 16u) = d;
 }
-template <int PB>
+template <int B, int PRT>
 __device__ __forceinline__ floatx4_t red_sum(const char* red, uint32_t t) {
     const uint32_t l = (uint32_t)lane_id(), j = l & 15u, kg = l >> 4;
     floatx4_t s = {0.f, 0.f, 0.f, 0.f};
-    if (j < (uint32_t)PB) {
+    if (j % (uint32_t)PRT == 0u && j < (uint32_t)(PRT * B)) {
 #pragma unroll
         for (uint32_t w = 0; w < 4u; ++w) {
-            const floatx4_t v = *(const floatx4_t*)(red + (((w * 3u + t) * 4u + kg) * PB + j) * 16u);
+            const floatx4_t v = *(const floatx4_t*)(red + (((w * 4u + t) * 4u + kg) * B + j / PRT) * 16u);
             s = w == 0 ? v : s + v;
         }
     }

@@ -51,8 +51,8 @@ __host__ __device__ constexpr int parts_pitch(int B) { return (mfma_parts(B) * B
 __host__ __device__ constexpr size_t parts_bytes(int B, int K) { return (size_t)2 * parts_pitch(B) * K; }
 constexpr uint32_t kMfmaPartsBytes = 72 * 1024;     // largest parts area of a DOWN column slice
 // Partial tiles of a matrix-core GEMV instruction summed across the waves:
-// [wave][tile < 3][k-group][used column] x 16 bytes.
-__host__ __device__ constexpr size_t mfma_red_bytes(int B) { return (size_t)4 * 3 * 4 * (mfma_parts(B) * B) * 16; }
+// [wave][tile < 4][k-group][batch row] x 16 bytes.
+__host__ __device__ constexpr size_t mfma_red_bytes(int B) { return (size_t)4 * 4 * 4 * B * 16; }
 
 // Column slices of the DOWN projection: the fewest (a power of two) whose input
 // slice fits the LDS budget (fp32: B rows of F / slices values in kDownSliceBytes;
