@@ -106,7 +106,14 @@ def step_bytes(cfg, batch: int, positions) -> int:
     pos = [int(p) for p in positions]
     if len(pos) == 1:
         pos = pos * batch
-    b = cfg.weight_bytes() + batch * cfg.hidden * 2
+    w = cfg.weight_bytes()
+    if cfg.is_moe:
+        # only the selected experts stream: the expected number of distinct experts
+        # among batch x top_k uniform choices (the routing is data dependent)
+        E, k = cfg.n_experts, cfg.top_k
+        distinct = E * (1.0 - (1.0 - k / E) ** batch)
+        w -= int(round((E - distinct) * 3 * cfg.expert_ffn * cfg.hidden * 2)) * cfg.n_layers
+    b = w + batch * cfg.hidden * 2
     b += sum(pos) * kv_pos     # cached positions 0..p-1 read
     b += batch * kv_pos        # position p written
     b += batch * cfg.vocab * 4
@@ -124,6 +131,9 @@ WORKLOADS = {
                   text="llama-3.2-1b-shape decode, batch 8, 8192-position synthetic bf16 KV context per sequence"),
     "8b": dict(model="LLAMA_8B", batch=1, prompt=128, ctx=0, horizon=256,
                text="llama-3-8b-shape decode, batch 1, 128 prompt tokens then greedy steps"),
+    "moe-b4": dict(model="MOE", batch=4, prompt=0, ctx=4096, horizon=128,
+                   text="synthetic MoE decode (64 experts, top 6, one shared), batch 4, 4096-position synthetic "
+                        "bf16 KV context per sequence"),
 }
 
 
@@ -259,7 +269,7 @@ def main() -> int:
     gbs = mean_bytes / (us_mk * 1e-6) / 1e9
 
     us_graph = kps_graph = pct_graph = None
-    if not args.no_graph:
+    if not args.no_graph and not cfg.is_moe:  # the one-kernel-per-op path has no MoE kernels
         us_graph, _, kps_graph, _, pct_graph = run_path(mk.MK_MODE_GRAPH, "hipGraph one-kernel-per-op")
 
     # streaming-read ceiling on a buffer the size of the step

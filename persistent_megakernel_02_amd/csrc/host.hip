@@ -75,6 +75,7 @@ bool use_mfma(const mk_model_config* c, const mk_runtime_config* rt) {
     if (rt->mode != MK_MODE_MEGAKERNEL) return false;
     if (rt->gemv_kind == 1) return false;
     if (rt->gemv_kind == 2) return true;
+    if (c->n_experts) return false;
     if (rt->max_batch < kMfmaAutoMinBatch || !mfma_shapes_ok(c, rt->max_batch)) return false;
     return ring_chunks_for((x_floats_kind(c, rt, 1, true) * 4 + 15) & ~(size_t)15) >= kMinRingChunks;
 }
@@ -97,6 +98,14 @@ size_t x_floats_kind(const mk_model_config* c, const mk_runtime_config* rt, int 
     }
     size_t n = B * (size_t)c->hidden;
     n = std::max(n, B * ((size_t)c->n_q_heads * hd + kMaxResidRows));
+    if (c->n_experts > 0) {
+        // EGU: x rows and the router logits; EDOWN: one expert's SwiGLU rows, the
+        // residual rows, their sums and the router logits
+        const size_t E = (size_t)c->n_experts;
+        n = std::max(n, B * ((size_t)c->hidden + E));
+        n = std::max(n, B * ((size_t)c->expert_ffn + 2 * kMaxResidRows + E) + B * (E + 1));
+        return std::max(n, attn_lds_floats((int)G, (int)hd, nsplit));
+    }
     // DOWN: one column slice of the input, the residual rows and the partial sums
     const int ns = std::max(1, down_slices_for((int)B, c->ffn));
     n = std::max(n, B * ((size_t)(c->ffn / ns) + 2 * kMaxResidRows));
@@ -134,12 +143,24 @@ mk_status validate(const mk_model_config* c, const mk_runtime_config* rt, std::s
     if (c->n_layers <= 0 || c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
         c->vocab <= 0)
         return fail(MK_E_INVALID, "non-positive model dimension");
-    if (c->n_experts != 0) return fail(MK_E_UNSUPPORTED, "MoE decoders are not supported by this build");
-    if (c->ffn <= 0) return fail(MK_E_INVALID, "ffn must be positive");
+    const bool moe = c->n_experts != 0;
+    if (moe) {
+        if (c->n_experts < 0 || c->top_k <= 0 || c->top_k > c->n_experts || c->expert_ffn <= 0 ||
+            c->n_shared_experts < 0)
+            return fail(MK_E_INVALID, "MoE: need 0 < top_k <= n_experts, expert_ffn > 0, n_shared >= 0");
+        if (c->n_experts > kMaxExperts || c->top_k > kMaxTopK || c->n_shared_experts > 1)
+            return fail(MK_E_UNSUPPORTED, "MoE: at most 64 experts, top_k <= 8 and one shared expert");
+        if (c->expert_ffn % 512 || c->hidden % 512 || ((c->hidden / 512) & (c->hidden / 512 - 1)))
+            return fail(MK_E_UNSUPPORTED, "MoE: expert rows must be whole 1 KB chunks (power-of-two per hidden row)");
+        if (rt->mode != MK_MODE_MEGAKERNEL) return fail(MK_E_UNSUPPORTED, "MoE runs in the persistent mode only");
+        if (rt->gemv_kind == 2) return fail(MK_E_UNSUPPORTED, "MoE runs on the VALU GEMV");
+    } else if (c->ffn <= 0) {
+        return fail(MK_E_INVALID, "ffn must be positive");
+    }
     if (c->head_dim != 64 && c->head_dim != 128) return fail(MK_E_UNSUPPORTED, "head_dim must be 64 or 128");
     if (c->n_q_heads % c->n_kv_heads) return fail(MK_E_UNSUPPORTED, "n_q_heads must be a multiple of n_kv_heads");
     if (c->n_q_heads / c->n_kv_heads > kMaxGroup) return fail(MK_E_UNSUPPORTED, "more than 4 q heads per KV head");
-    if (c->hidden % 256 || c->ffn % 64) return fail(MK_E_UNSUPPORTED, "hidden % 256 and ffn % 64 must be 0");
+    if (c->hidden % 256 || (!moe && c->ffn % 64)) return fail(MK_E_UNSUPPORTED, "hidden % 256 and ffn % 64 must be 0");
     if (c->n_q_heads * c->head_dim > 16384) return fail(MK_E_UNSUPPORTED, "attention width above 16384");
     if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.0)) return fail(MK_E_INVALID, "rms_eps and rope_theta must be > 0");
     if (rt->max_batch < 1 || rt->max_batch > kMaxBatch) return fail(MK_E_UNSUPPORTED, "max_batch must be 1..8");
@@ -150,7 +171,7 @@ mk_status validate(const mk_model_config* c, const mk_runtime_config* rt, std::s
         return fail(MK_E_UNSUPPORTED, "the matrix-core GEMV runs in the megakernel only");
     if (rt->gemv_kind == 2 && !mfma_shapes_ok(c, rt->max_batch))
         return fail(MK_E_UNSUPPORTED, "matrix-core GEMV rows must be whole tile units of columns");
-    if (down_slices_for(rt->max_batch, c->ffn, use_mfma(c, rt)) == 0)
+    if (!moe && down_slices_for(rt->max_batch, c->ffn, use_mfma(c, rt)) == 0)
         return fail(MK_E_UNSUPPORTED, "the DOWN input of this batch needs column slices of whole 1 KB chunks");
     if (rt->max_seq < 1 || rt->max_seq > (1 << 20)) return fail(MK_E_INVALID, "max_seq out of range");
     if (rt->mode != MK_MODE_MEGAKERNEL && rt->mode != MK_MODE_GRAPH) return fail(MK_E_INVALID, "unknown mode");
@@ -209,8 +230,16 @@ Plan build_plan(const mk_model_config* c, const mk_runtime_config* rt, int n_cu)
         for (uint32_t it = 0; it < items; ++it) q[it % n_cu].push_back(mk_instr(OP_ATTN, l, it, 1));
         ++pl.phases;
         gemv_phase(OP_O, l, (uint32_t)c->hidden, kMaxResidRows);
-        gemv_phase(OP_GATEUP, l, (uint32_t)c->ffn, all);
-        gemv_phase(OP_DOWN, l, (uint32_t)c->hidden, kMaxResidRows);
+        if (c->n_experts) {
+            // router rows; then on every CU its f-range of every selected expert;
+            // then its rows of every selected expert's down projection
+            gemv_phase(OP_ROUTE, l, (uint32_t)c->n_experts, all);
+            gemv_phase(OP_EGU, l, (uint32_t)c->expert_ffn, all);
+            gemv_phase(OP_EDOWN, l, (uint32_t)c->hidden, kMaxResidRows);
+        } else {
+            gemv_phase(OP_GATEUP, l, (uint32_t)c->ffn, all);
+            gemv_phase(OP_DOWN, l, (uint32_t)c->hidden, kMaxResidRows);
+        }
     }
     gemv_phase(OP_HEAD, L, (uint32_t)c->vocab, all);
     pl.qoff.resize(n_cu + 1);
@@ -230,20 +259,25 @@ Plan build_plan(const mk_model_config* c, const mk_runtime_config* rt, int n_cu)
 int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Plan& pl) {
     const int L = c->n_layers, B = rt->max_batch;
     const uint32_t qkv_rows = (uint32_t)((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim);
-    const int nphase = L * kPhasesPerLayer + 1;
+    // sub-phases per layer: QKV, ATTN, O, ROUTE (MoE), GATEUP / EGU, DOWN / EDOWN
+    constexpr int kSub = 6;
+    const bool moe = c->n_experts != 0;
+    const int nphase = L * kSub + 1;
     std::vector<std::vector<uint8_t>> seen(nphase);
     auto phase_of = [&](const Instr& in) -> int {
-        if (in.op == OP_HEAD) return L * kPhasesPerLayer;
-        const int k = in.op == OP_QKV ? 0 : in.op == OP_ATTN ? 1 : in.op == OP_O ? 2 : in.op == OP_GATEUP ? 3 : 4;
-        return in.layer * kPhasesPerLayer + k;
+        if (in.op == OP_HEAD) return L * kSub;
+        const int k = in.op == OP_QKV ? 0 : in.op == OP_ATTN ? 1 : in.op == OP_O ? 2 : in.op == OP_ROUTE ? 3
+                    : (in.op == OP_GATEUP || in.op == OP_EGU) ? 4 : 5;
+        return in.layer * kSub + k;
     };
     auto extent = [&](int ph) -> uint32_t {
-        if (ph == L * kPhasesPerLayer) return (uint32_t)c->vocab;
-        switch (ph % kPhasesPerLayer) {
+        if (ph == L * kSub) return (uint32_t)c->vocab;
+        switch (ph % kSub) {
             case 0: return qkv_rows;
             case 1: return (uint32_t)(B * c->n_kv_heads * pl.nsplit);
             case 2: return (uint32_t)c->hidden;
-            case 3: return (uint32_t)c->ffn;
+            case 3: return moe ? (uint32_t)c->n_experts : 0u;
+            case 4: return moe ? (uint32_t)c->expert_ffn : (uint32_t)c->ffn;
             default: return (uint32_t)c->hidden;
         }
     };
@@ -254,14 +288,16 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
         int last = -1;
         for (uint32_t i = pl.qoff[cu]; i < pl.qoff[cu + 1]; ++i) {
             const Instr& in = pl.instrs[i];
-            if (in.op < OP_QKV || in.op > OP_HEAD) return 1;
+            if (in.op < OP_QKV || in.op > OP_EDOWN) return 1;
+            const bool moe_op = in.op == OP_ROUTE || in.op == OP_EGU || in.op == OP_EDOWN;
+            if (moe_op != moe && in.op != OP_QKV && in.op != OP_ATTN && in.op != OP_O && in.op != OP_HEAD) return 1;
             if (in.op != OP_HEAD && in.layer >= L) return 2;
             const int ph = phase_of(in);
             if (ph < last) return 3;  // queue not in phase order
             last = ph;
             const uint32_t ext = extent(ph);
             if (in.count == 0 || in.begin + in.count > ext || in.begin + in.count < in.begin) return 5;
-            if ((in.op == OP_O || in.op == OP_DOWN) && in.count > kMaxResidRows) return 4;
+            if ((in.op == OP_O || in.op == OP_DOWN || in.op == OP_EDOWN) && in.count > kMaxResidRows) return 4;
             for (uint32_t r = in.begin; r < in.begin + in.count; ++r) {
                 if (seen[ph][r]) return 6;  // covered twice
                 seen[ph][r] = 1;
@@ -280,7 +316,7 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
 
 struct Layout {
     size_t state, tickets, instrs, qoff, layers, rope, h, qkv, attn, act, attn_part, head_part, logits_scr, tok_scr,
-        trace, trace_bytes, total;
+        trace, trace_bytes, route, eact, eptr, total;
     size_t head_slots;  // argmax partial slots (per sequence)
 };
 
@@ -292,8 +328,9 @@ void plan_counts(const mk_model_config* c, const mk_runtime_config* rt, int n, i
     const size_t items = (size_t)rt->max_batch * c->n_kv_heads * nsplit;
     const size_t d_rows = ((size_t)c->hidden + n - 1) / n;
     const size_t od = (d_rows + kMaxResidRows - 1) / kMaxResidRows;  // O / DOWN instructions per CU
-    *per_cu = (size_t)c->n_layers * (2 + 2 * od + (items + n - 1) / n) + 1;
-    *total = (size_t)c->n_layers * (2 * (size_t)n + items + 2 * od * (size_t)n) + (size_t)n;
+    const size_t route = c->n_experts ? 1 : 0;  // at most one router instruction per CU and layer
+    *per_cu = (size_t)c->n_layers * (2 + route + 2 * od + (items + n - 1) / n) + 1;
+    *total = (size_t)c->n_layers * ((2 + route) * (size_t)n + items + 2 * od * (size_t)n) + (size_t)n;
 }
 
 Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, int nsplit) {
@@ -318,7 +355,11 @@ Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, i
     lo.h = take(B * d * 8);
     lo.qkv = take(B * qkv_rows * 8);
     lo.attn = take(B * c->n_q_heads * hd * 8);
-    lo.act = take(B * c->ffn * 8);
+    lo.act = take(B * (size_t)std::max(c->ffn, 0) * 8);
+    const size_t nx = c->n_experts ? (size_t)(c->n_shared_experts + c->n_experts) : 0;
+    lo.route = take(B * (size_t)c->n_experts * 8);
+    lo.eact = take(nx * B * (size_t)c->expert_ffn * 8);
+    lo.eptr = take((size_t)c->n_layers * 3 * nx * 8);
     lo.attn_part = take(B * c->n_kv_heads * nsplit * G * (hd + 2) * 8);
     const size_t conv_blocks = ((size_t)c->vocab + 15) / 16;
     lo.head_slots = std::max((size_t)n_cu, conv_blocks) * kComputeWaves;
@@ -423,8 +464,11 @@ mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* r
     if ((uint32_t)cfg->vocab < (uint32_t)num_cus) return MK_E_UNSUPPORTED;
     Plan pl = build_plan(cfg, rt, num_cus);
     const int64_t d = cfg->hidden, hd = cfg->head_dim;
-    const int64_t per_layer = (cfg->n_q_heads + 2 * cfg->n_kv_heads) * hd * d + d * cfg->n_q_heads * hd +
-                              3 * (int64_t)cfg->ffn * d + 2 * d;
+    const int64_t ffn_w = cfg->n_experts
+                              ? (int64_t)cfg->n_experts * d +
+                                    (int64_t)(cfg->n_shared_experts + cfg->n_experts) * 3 * cfg->expert_ffn * d
+                              : 3 * (int64_t)cfg->ffn * d;
+    const int64_t per_layer = (cfg->n_q_heads + 2 * cfg->n_kv_heads) * hd * d + d * cfg->n_q_heads * hd + ffn_w + 2 * d;
     const size_t xb = x_bytes_for(cfg, rt, pl.nsplit);
     int64_t vals[11] = {num_cus, (int64_t)pl.instrs.size(), (int64_t)ring_chunks_for(xb), (int64_t)pl.max_per_cu,
                         2 * (cfg->n_layers * per_layer + (int64_t)cfg->vocab * d + d), verify_plan(cfg, rt, pl),
@@ -442,9 +486,14 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
     if (!w || !w->tok_embedding || !w->final_norm || !w->layers || !d_workspace || !d_kv) return MK_E_INVALID;
     for (int l = 0; l < cfg->n_layers; ++l) {
         const mk_layer_weights& Lw = w->layers[l];
-        if (!Lw.attn_norm || !Lw.wq || !Lw.wk || !Lw.wv || !Lw.wo || !Lw.mlp_norm || !Lw.w_gate || !Lw.w_up ||
-            !Lw.w_down)
-            return MK_E_INVALID;
+        if (!Lw.attn_norm || !Lw.wq || !Lw.wk || !Lw.wv || !Lw.wo || !Lw.mlp_norm) return MK_E_INVALID;
+        if (cfg->n_experts == 0 && (!Lw.w_gate || !Lw.w_up || !Lw.w_down)) return MK_E_INVALID;
+        if (cfg->n_experts) {
+            if (!Lw.router || !Lw.e_gate || !Lw.e_up || !Lw.e_down) return MK_E_INVALID;
+            if (cfg->n_shared_experts && (!Lw.s_gate || !Lw.s_up || !Lw.s_down)) return MK_E_INVALID;
+            for (int e = 0; e < cfg->n_experts; ++e)
+                if (!Lw.e_gate[e] || !Lw.e_up[e] || !Lw.e_down[e]) return MK_E_INVALID;
+        }
     }
     if (!cfg->tied_embeddings && !w->lm_head) return MK_E_INVALID;
     size_t need_ws = 0, need_kv = 0;
@@ -498,7 +547,11 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
     P.hd = cfg->head_dim;
     P.F = cfg->ffn;
     P.gemv_mfma = use_mfma(cfg, rt) ? 1 : 0;
-    P.down_slices = down_slices_for(rt->max_batch, cfg->ffn, P.gemv_mfma != 0);
+    P.down_slices = cfg->n_experts ? 1 : down_slices_for(rt->max_batch, cfg->ffn, P.gemv_mfma != 0);
+    P.E = cfg->n_experts;
+    P.top_k = cfg->top_k;
+    P.n_shared = cfg->n_experts ? cfg->n_shared_experts : 0;
+    P.Fe = cfg->expert_ffn;
     P.V = cfg->vocab;
     P.B = rt->max_batch;
     P.S = rt->max_seq;
@@ -526,6 +579,9 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
     P.act = (uint64_t*)(ws + lo.act);
     P.attn_part = (uint64_t*)(ws + lo.attn_part);
     P.head_part = (uint64_t*)(ws + lo.head_part);
+    P.route = (uint64_t*)(ws + lo.route);
+    P.eact = (uint64_t*)(ws + lo.eact);
+    P.eptr = (const uint16_t* const*)(ws + lo.eptr);
     P.attn_ticket = (uint32_t*)(ws + lo.tickets);
     P.head_ticket = P.attn_ticket + (size_t)cfg->n_layers * rt->max_batch * cfg->n_kv_heads * kCtrStride;
     P.state = (DevState*)(ws + lo.state);
@@ -566,7 +622,21 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
         const mk_layer_weights& Lw = w->layers[l];
         dl[l] = DevLayer{(const uint16_t*)Lw.attn_norm, (const uint16_t*)Lw.wq,     (const uint16_t*)Lw.wk,
                          (const uint16_t*)Lw.wv,        (const uint16_t*)Lw.wo,     (const uint16_t*)Lw.mlp_norm,
-                         (const uint16_t*)Lw.w_gate,    (const uint16_t*)Lw.w_up,   (const uint16_t*)Lw.w_down};
+                         (const uint16_t*)Lw.w_gate,    (const uint16_t*)Lw.w_up,   (const uint16_t*)Lw.w_down,
+                         (const uint16_t*)Lw.router};
+    }
+    // MoE expert table [L][gate, up, down][shared (if any), experts 0..E-1]
+    const int nx = cfg->n_experts ? cfg->n_shared_experts + cfg->n_experts : 0;
+    std::vector<const void*> ep((size_t)cfg->n_layers * 3 * nx);
+    for (int l = 0; l < cfg->n_layers && nx; ++l) {
+        const mk_layer_weights& Lw = w->layers[l];
+        for (int m = 0; m < 3; ++m) {
+            const void* const* routed = m == 0 ? Lw.e_gate : m == 1 ? Lw.e_up : Lw.e_down;
+            const void* shared = m == 0 ? Lw.s_gate : m == 1 ? Lw.s_up : Lw.s_down;
+            const void** row = ep.data() + ((size_t)l * 3 + m) * nx;
+            for (int x = 0; x < cfg->n_shared_experts; ++x) row[x] = shared;
+            for (int e = 0; e < cfg->n_experts; ++e) row[cfg->n_shared_experts + e] = routed[e];
+        }
     }
     // RoPE table: angle p * theta^(-2i/hd) in double, cos/sin rounded to fp32
     std::vector<float> rope((size_t)rt->max_seq * cfg->head_dim);
@@ -587,6 +657,7 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
     cp(lo.qoff, h->plan.qoff.data(), h->plan.qoff.size() * 4);
     cp(lo.layers, dl.data(), dl.size() * sizeof(DevLayer));
     cp(lo.rope, rope.data(), rope.size() * 4);
+    cp(lo.eptr, ep.data(), ep.size() * sizeof(void*));
     if (e == hipSuccess) e = hipMemsetAsync(d_kv, 0, need_kv, h->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
     if (e != hipSuccess) {

@@ -38,6 +38,10 @@ struct Ctl {
     uint32_t abort;                      // set when a wave gives up (error)
     int32_t ctx[kMaxBatch];              // context lengths at launch
     float ss[kMaxBatch][kComputeWaves];  // RMSNorm partials of the current instruction
+    // MoE: the selected experts of the current EGU / EDOWN instruction, published
+    // by compute wave 0 for the loaders (moe_seq = queue index + 1 once valid)
+    uint32_t moe_seq, moe_n;
+    uint8_t moe_list[kMaxExperts + 1];  // expert-table slots, shared first, then ascending experts
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -62,7 +66,17 @@ __device__ __forceinline__ uint32_t align_chunk(uint32_t b) { return (b + kChunk
 // stream arithmetic that depends on it stays on the scalar unit.
 __device__ __forceinline__ int ctx_of(const int32_t* ctx, int b) { return __builtin_amdgcn_readfirstlane(ctx[b]); }
 
-__device__ __forceinline__ bool is_gemv(uint32_t op) { return op != OP_ATTN; }
+// GEMV instructions of the dense decoder (the ones the matrix-core kernel runs)
+__device__ __forceinline__ bool is_gemv(uint32_t op) {
+    return op == OP_QKV || op == OP_O || op == OP_GATEUP || op == OP_DOWN || op == OP_HEAD;
+}
+__device__ __forceinline__ bool is_moe_expert(uint32_t op) { return op == OP_EGU || op == OP_EDOWN; }
+
+// Stream bytes of an MoE expert instruction with n selected expert slots: per slot
+// the CU's (gate, up) row pairs (EGU) or its down rows (EDOWN), whole rows.
+__device__ __forceinline__ uint32_t moe_bytes(const Params& P, const Instr& in, uint32_t n) {
+    return in.op == OP_EGU ? n * 2u * in.count * (uint32_t)P.d * 2u : n * in.count * (uint32_t)P.Fe * 2u;
+}
 
 // Bytes of the CU stream that instruction `in` consumes (whole chunks).  With the
 // matrix cores (MF) a GEMV streams whole 16-row tiles of 1 KB chunks.
@@ -71,6 +85,7 @@ __device__ __forceinline__ uint32_t instr_bytes(const Params& P, const Instr& in
     if (MF && is_gemv(in.op)) return mfma_geo<HD>(P, in).chunks() * kChunk;
     switch (in.op) {
         case OP_QKV:
+        case OP_ROUTE:
         case OP_HEAD: return align_chunk(in.count * (uint32_t)P.d * 2u);
         case OP_O: return align_chunk(in.count * (uint32_t)(P.Hq * HD) * 2u);
         case OP_GATEUP: return align_chunk(2u * in.count * (uint32_t)P.d * 2u);
@@ -122,11 +137,12 @@ __device__ __forceinline__ const char* chunk_src(const Params& P, const Instr& i
             if (r >= in.count) { r = 0; col = 0; }
             return (const char*)(Lw.w_down + (size_t)(in.begin + r) * P.F) + col;
         }
-        case OP_HEAD: {
+        case OP_HEAD:
+        case OP_ROUTE: {
             const uint32_t rb = (uint32_t)P.d * 2u;
             uint32_t r = off / rb, col = off - r * rb;
             if (r >= in.count) { r = 0; col = 0; }
-            return (const char*)(P.head + (size_t)(in.begin + r) * P.d) + col;
+            return (const char*)((in.op == OP_HEAD ? P.head : Lw.router) + (size_t)(in.begin + r) * P.d) + col;
         }
         case OP_ATTN: {
             constexpr uint32_t rbkv = HD * 2u;
@@ -260,6 +276,7 @@ __device__ __forceinline__ bool setup_stream(const Params& P, const Instr& in, c
             }
             break;
         case OP_HEAD: rb = (uint32_t)P.d * 2u; S.p0 = (const char*)P.head + (size_t)in.begin * rb; break;
+        case OP_ROUTE: rb = (uint32_t)P.d * 2u; S.p0 = (const char*)Lw.router + (size_t)in.begin * rb; break;
         case OP_GATEUP: {
             rb = (uint32_t)P.d * 2u;
             const uint32_t cpr = rb / kChunk;
@@ -406,9 +423,39 @@ __device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* rin
             publish(issued - (uint32_t)kLoaderLag);
         }
     };
+    // MoE expert instructions: the streamed experts are known only once the compute
+    // waves have routed.  Retire every chunk in flight first (the compute waves may
+    // still need them to reach this instruction), then wait for the published list.
+    auto wait_moe = [&](uint32_t want) -> bool {
+        if (issued != landed) {
+            wait_vmcnt<0>();
+            publish(issued);
+        }
+        const uint64_t t0 = now_ticks();
+        uint32_t polls = 0;
+        while (lds_ld(&ctl->moe_seq) != want) {
+            if (lds_ld(&ctl->abort)) return false;
+            if ((++polls & 255u) == 0 && now_ticks() - t0 > P.spin_ticks) {
+                raise_error_impl(P.state, P.host_err, &ctl->abort, DERR_TIMEOUT, 0xFFFFFFFCu, want);
+                return false;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        return true;
+    };
     for (uint32_t i = q0; i < q1 && !stop; ++i) {
         const Instr in = ld_const(P.instrs + i);
-        const uint32_t nch = instr_bytes<HD, MF>(P, in, ctx) / kChunk;
+        uint32_t nch;
+        if (!MF && is_moe_expert(in.op)) {
+            if (!wait_moe(i + 1u)) {
+                stop = true;
+                break;
+            }
+            nch = moe_bytes(P, in, lds_ld(&ctl->moe_n)) / kChunk;
+        } else {
+            nch = instr_bytes<HD, MF>(P, in, ctx) / kChunk;
+        }
         if (k == 0 && P.trace && lane_id() == 0 && i > q0) {
             uint32_t* rec = P.trace + ((size_t)blockIdx.x * P.trace_stride + (i - 1 - q0)) * kTraceWords;
             rec[5] = (uint32_t)now_ticks();
@@ -496,6 +543,43 @@ __device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* rin
                         }
                     }
                     rs += LC;
+                }
+            } else if (!MF && is_moe_expert(in.op)) {
+                // selected expert slot a, chunk w of its rows; the slot's matrices come
+                // from the expert table (gate and up rows interleaved as in GATEUP)
+                const bool egu = in.op == OP_EGU;
+                const uint32_t n = lds_ld(&ctl->moe_n), nx = (uint32_t)(P.n_shared + P.E);
+                const uint32_t rb = egu ? (uint32_t)P.d * 2u : (uint32_t)P.Fe * 2u;
+                const uint32_t per = (egu ? 2u * in.count : in.count) * rb / kChunk;
+                const uint16_t* const* tab = P.eptr + (size_t)in.layer * 3u * nx;
+                auto slot_stream = [&](uint32_t a, Stream& X) {
+                    const uint32_t x = __builtin_amdgcn_readfirstlane((uint32_t)ctl->moe_list[a]);
+                    X.attn = X.sliced = false;
+                    X.end0 = X.end1 = 0xFFFFFFFFu;
+                    X.p1 = X.p2 = X.head = nullptr;
+                    if (egu) {
+                        X.p0 = (const char*)(ld_const(tab + x) + (size_t)in.begin * P.d);
+                        X.p1 = (const char*)(ld_const(tab + nx + x) + (size_t)in.begin * P.d);
+                        X.per_shift = (uint32_t)__builtin_ctz(rb / kChunk);
+                        X.inter = true;
+                    } else {
+                        X.p0 = (const char*)(ld_const(tab + 2u * nx + x) + (size_t)in.begin * P.Fe);
+                        X.inter = false;
+                    }
+                };
+                uint32_t a = (c - cb) / per, w = (c - cb) - a * per;
+                if (a < n) slot_stream(a, S);
+                for (; c < ce; ) {
+                    if (c >= limit && !make_room()) {
+                        stop = true;
+                        break;
+                    }
+                    uint32_t voff;
+                    const char* base = uniform_ptr(stream_chunk<HD>(S, w, voff));
+                    dma_chunk_s(base, voff, slot);
+                    advance();
+                    for (w += NL; w >= per && a < n; w -= per)
+                        if (++a < n) slot_stream(a, S);
                 }
             } else if (setup_stream<HD>(P, in, Lw, ctx, S)) {
                 for (; c < ce; ) {
@@ -928,6 +1012,200 @@ __device__ __forceinline__ bool mfma_instr(const Params& P, const StepArgs& A, C
     return head_publish<B>(P, A, in.slot * kComputeWaves + (uint32_t)wave, best_v, best_i, spin);
 }
 
+// ------------------------------------------------------------------------------------------------
+// MoE FFN (the synthetic MoE decoder's layers): router logits (OP_ROUTE), then on
+// every CU the selected experts' (gate, up) rows of its f-range (OP_EGU) and
+// their down rows of its output rows (OP_EDOWN).  Each CU routes for itself from
+// the router logits, so every CU derives the same selected set; only the
+// selected experts' rows are streamed.
+// ------------------------------------------------------------------------------------------------
+
+// Top-k routing of one sequence; lane e < E holds the router logit of expert e.
+// Probabilities are the softmax evaluated in double and rounded to fp32; the k
+// largest are selected, ties to the lower expert index (NaN never wins).
+// Returns the selected-expert mask; `prob` = this lane's probability.
+__device__ __forceinline__ uint64_t route_topk(float z, int E, int K, float& prob) {
+    const int lane = lane_id();
+    const bool valid = lane < E;
+    float m = valid ? z : -INFINITY;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const double ex = valid ? exp((double)z - (double)m) : 0.0;
+    double Z = ex;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) Z += __shfl_xor(Z, o, 64);
+    prob = valid ? (float)(ex / Z) : -1.0f;
+    const uint64_t valid_mask = E >= 64 ? ~0ull : ((1ull << E) - 1ull);
+    uint64_t sel = 0;
+    for (int t = 0; t < K; ++t) {
+        const float v = ((sel >> lane) & 1ull) || !valid ? -2.0f : prob;
+        float best = v;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) best = fmaxf(best, __shfl_xor(best, o, 64));
+        uint64_t cand = __ballot(v == best) & valid_mask & ~sel;
+        if (!cand) cand = valid_mask & ~sel;  // NaN probabilities: the lowest index not yet taken
+        sel |= 1ull << __builtin_ctzll(cand);
+    }
+    return sel;
+}
+
+// Routes the B sequences from the router logits at zeta [B][E] (LDS); returns the
+// union of the selected sets and, per sequence, the mask and this lane's
+// probability.  Wave 0 publishes the expert-table slots of the union (shared
+// first) for the loaders and the other waves; the caller's barrier orders it.
+template <int B>
+__device__ __forceinline__ uint32_t moe_route(const Params& P, Ctl* ctl, const float* zeta, int wave, uint32_t qi,
+                                              uint64_t (&sel)[B], float (&prob)[B]) {
+    const int lane = lane_id();
+    uint64_t U = 0;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const float z = lane < P.E ? zeta[b * P.E + lane] : 0.f;
+        sel[b] = route_topk(z, P.E, P.top_k, prob[b]);
+        U |= sel[b];
+    }
+    const uint32_t n = (uint32_t)P.n_shared + (uint32_t)__builtin_popcountll(U);
+    if (wave == 0 && lane == 0) {
+        uint32_t a = 0;
+        for (int x = 0; x < P.n_shared; ++x) ctl->moe_list[a++] = (uint8_t)x;
+        for (uint64_t u = U; u; u &= u - 1ull) ctl->moe_list[a++] = (uint8_t)(P.n_shared + __builtin_ctzll(u));
+        ctl->moe_n = n;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        lds_st(&ctl->moe_seq, qi + 1u);
+    }
+    return n;
+}
+
+// OP_EGU: x = RMSNorm(h after O) * g; route; then for every selected slot the
+// CU's (gate, up) row pairs of f-range [begin, begin + count): SwiGLU outputs.
+template <int B>
+__device__ __forceinline__ bool moe_egu(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs,
+                                        int wave, const Instr& in, uint32_t qi, uint32_t S, Spin& spin,
+                                        CwBarrier& barrier, uint32_t& land_wait, uint32_t* tr, uint32_t& bytes) {
+    const int lane = lane_id();
+    const int layer = in.layer;
+    const DevLayer Lw = ld_const(P.layers + layer);
+    const uint32_t d = (uint32_t)P.d, E = (uint32_t)P.E;
+    const uint32_t tag_o = phase_tag(A.tag0, layer, 2);
+    float* zeta = xs + B * d;
+    float ss[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) ss[b] = 0.f;
+    const StageSeg sg[2] = {{P.h, xs, Lw.mlp_norm, d, (uint32_t)B, d, d, tag_o, 0u},
+                            {P.route, zeta, nullptr, E, (uint32_t)B, E, E, tag_o, 0u}};
+    if (!stage_segs<kStagePassWords, B, 2>(sg, wave, kComputeWaves, spin, ss)) return false;
+    wave_total_n<B>(ss);
+    if (lane == 0) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) ctl->ss[b][wave] = ss[b];
+    }
+    if (!barrier()) return false;
+    float r[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) r[b] = rms_scale(ctl->ss[b], kComputeWaves, P.d, P.eps);
+    uint64_t sel[B];
+    float prob[B];
+    const uint32_t n = moe_route<B>(P, ctl, zeta, wave, qi, sel, prob);
+    if (!barrier()) return false;  // the slot list is visible
+    if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
+    bytes = moe_bytes(P, in, n);
+    const uint32_t per = 2u * in.count, tag_out = phase_tag(A.tag0, layer, 3);
+    auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
+        #pragma unroll
+        for (uint32_t i = 0; i + 1 < (uint32_t)(sizeof(res) / sizeof(res[0])); i += 2) {
+            if (i + 1 >= nr) break;
+            const uint32_t j = r0 + i, a = j / per, f = in.begin + (j - a * per) / 2u;
+            const uint32_t x = ctl->moe_list[a];
+            if (lane < B) {
+                const float rr = pick<B>(r, lane);
+                st_tagged(P.eact + ((size_t)x * P.B + lane) * P.Fe + f,
+                          silu_mul(pick<B>(res[i], lane) * rr, pick<B>(res[i + 1], lane) * rr), tag_out);
+            }
+        }
+    };
+    return gemv_ring_auto<B>(P, ctl, ring, S, d * 2u, n * per, XLds{xs, d}, wave, land_wait, epi, true);
+}
+
+// OP_EDOWN: route again (same logits, same result); for every selected slot in
+// order (shared, then ascending experts) stage its SwiGLU rows and add its down
+// rows [begin, begin + count), weighted by the sequence's probability (1 for the
+// shared expert, 0 where the sequence did not select it); then h += the sum.
+template <int B>
+__device__ __forceinline__ bool moe_edown(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs,
+                                          int wave, const Instr& in, uint32_t qi, uint32_t S, Spin& spin,
+                                          CwBarrier& barrier, uint32_t& land_wait, uint32_t* tr, uint32_t& bytes) {
+    const int lane = lane_id();
+    const int layer = in.layer;
+    const uint32_t E = (uint32_t)P.E, Fe = (uint32_t)P.Fe, cnt = in.count;
+    const uint32_t tag_o = phase_tag(A.tag0, layer, 2), tag_a = phase_tag(A.tag0, layer, 3);
+    float* hres = xs + B * Fe;    // [B][cnt] residual rows after O
+    float* acc = hres + B * cnt;  // [B][cnt] weighted expert sums
+    float* zeta = acc + B * cnt;  // [B][E] router logits
+    float* wtab = zeta + B * E;   // [slot][B] weights of the selected slots
+    {
+        float ss[1] = {0.f};
+        const StageSeg sg[2] = {{P.route, zeta, nullptr, E, (uint32_t)B, E, E, tag_o, 0u},
+                                {P.h + in.begin, hres, nullptr, cnt, (uint32_t)B, (uint32_t)P.d, cnt, tag_o, 0u}};
+        if (!stage_segs<kStagePassWordsWide, 1, 2>(sg, wave, kComputeWaves, spin, ss)) return false;
+    }
+    if (!barrier()) return false;
+    uint32_t n;
+    {
+        uint64_t sel[B];
+        float prob[B];
+        n = moe_route<B>(P, ctl, zeta, wave, qi, sel, prob);
+        if (wave == 0) {
+            // weight of slot a for sequence b: 1 (shared), its probability where b
+            // selected the expert, else 0; lane e writes expert e's slot
+            uint64_t U = 0;
+#pragma unroll
+            for (int b = 0; b < B; ++b) U |= sel[b];
+            const bool mine = lane < P.E && ((U >> lane) & 1ull);
+            const uint32_t slot = (uint32_t)P.n_shared + (uint32_t)__builtin_popcountll(U & ((1ull << lane) - 1ull));
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                if (mine) wtab[slot * B + b] = ((sel[b] >> lane) & 1ull) ? prob[b] : 0.f;
+                if (lane < P.n_shared) wtab[lane * B + b] = 1.0f;
+            }
+            for (uint32_t i = (uint32_t)lane; i < B * cnt; i += 64u) acc[i] = 0.f;
+        }
+    }
+    if (!barrier()) return false;  // the slot list, the weights and the zeroed sums are visible
+    if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
+    bytes = moe_bytes(P, in, n);
+    const uint32_t rb = Fe * 2u;
+    for (uint32_t a = 0; a < n; ++a) {
+        const uint32_t x = __builtin_amdgcn_readfirstlane((uint32_t)ctl->moe_list[a]);
+        float wgt[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) wgt[b] = wtab[a * B + b];
+        if (a > 0 && !barrier()) return false;  // every wave is done with the previous slot's rows
+        float ss[1] = {0.f};
+        const StageSeg sa[1] = {{P.eact + (size_t)x * P.B * Fe, xs, nullptr, Fe, (uint32_t)B, Fe, Fe, tag_a, 0u}};
+        if (!stage_segs<kStagePassWordsWide, 1, 1>(sa, wave, kComputeWaves, spin, ss)) return false;
+        if (!barrier()) return false;
+        auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
+            #pragma unroll
+            for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i) {
+                if (i >= nr) break;
+                if (lane < B) {
+                    const float wv = pick<B>(wgt, lane);
+                    if (wv != 0.f) acc[lane * cnt + r0 + i] += wv * pick<B>(res[i], lane);
+                }
+            }
+        };
+        if (!gemv_ring_auto<B>(P, ctl, ring, S + a * cnt * rb, rb, cnt, XLds{xs, Fe}, wave, land_wait, epi, false))
+            return false;
+    }
+    if (!barrier()) return false;
+    const uint32_t tag_out = phase_tag(A.tag0, layer, 4);
+    for (uint32_t i = (uint32_t)(wave * 64 + lane); i < B * cnt; i += 64u * kComputeWaves) {
+        const uint32_t b = i / cnt, j = i - b * cnt;
+        st_tagged(P.h + (size_t)b * P.d + in.begin + j, hres[i] + acc[i], tag_out);
+    }
+    return true;
+}
+
 // One attention item (sequence, KV head, split) as an instruction.
 template <int B, int HD>
 __device__ __forceinline__ bool attn_instr(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs,
@@ -961,7 +1239,7 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
     CwBarrier barrier{ctl, &P, 0u};
     for (uint32_t qi = q0; qi < q1; ++qi, ++k) {
         const Instr in = ld_const(P.instrs + qi);
-        const uint32_t bytes = instr_bytes<HD, MF>(P, in, ctx);
+        uint32_t bytes = instr_bytes<HD, MF>(P, in, ctx);  // MoE expert instructions set it once routed
         uint32_t* tr =
             (P.trace && wave == 0) ? P.trace + ((size_t)blockIdx.x * P.trace_stride + k) * kTraceWords : nullptr;
         if (tr && lane == 0) {
@@ -978,15 +1256,22 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
         // (the matrix-core kernel carries no VALU GEMV code: a smaller kernel)
         if constexpr (MF) {
             if (is_gemv(in.op)) ok = mfma_instr<B, HD>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr);
-            else ok = attn_instr<B, HD>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr, ctx);
+            else if (in.op == OP_ATTN) ok = attn_instr<B, HD>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr, ctx);
         } else switch (in.op) {
+            case OP_EGU:
+                ok = moe_egu<B>(P, A, ctl, ring, xs, wave, in, qi, S, spin, barrier, land_wait, tr, bytes);
+                break;
+            case OP_EDOWN:
+                ok = moe_edown<B>(P, A, ctl, ring, xs, wave, in, qi, S, spin, barrier, land_wait, tr, bytes);
+                break;
             case OP_QKV:
             case OP_GATEUP:
+            case OP_ROUTE:
             case OP_HEAD: {
-                const uint16_t* gain = in.op == OP_QKV ? Lw.attn_norm : in.op == OP_GATEUP ? Lw.mlp_norm : P.final_norm;
-                const uint32_t tag_in = in.op == OP_QKV      ? phase_tag(A.tag0, layer - 1, 4)
-                                        : in.op == OP_GATEUP ? phase_tag(A.tag0, layer, 2)
-                                                             : phase_tag(A.tag0, P.L - 1, 4);
+                const uint16_t* gain = in.op == OP_QKV ? Lw.attn_norm : in.op == OP_HEAD ? P.final_norm : Lw.mlp_norm;
+                const uint32_t tag_in = in.op == OP_QKV    ? phase_tag(A.tag0, layer - 1, 4)
+                                        : in.op == OP_HEAD ? phase_tag(A.tag0, P.L - 1, 4)
+                                                           : phase_tag(A.tag0, layer, 2);
                 const uint32_t d = (uint32_t)P.d;
                 float ss[B];
 #pragma unroll
@@ -1020,6 +1305,17 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                         for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i)
                             if (i < nr && lane < B)
                                 st_tagged(P.qkv + (size_t)lane * P.qkv_rows + in.begin + r0 + i,
+                                          pick<B>(res[i], lane) * pick<B>(r, lane), tag_out);
+                    };
+                    ok = gemv_ring_auto<B>(P, ctl, ring, S, rb, nrows, x, wave, land_wait, epi, false);
+                } else if (in.op == OP_ROUTE) {
+                    // router logits of experts begin.., tagged like the residual after O
+                    const uint32_t tag_out = phase_tag(A.tag0, layer, 2);
+                    auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
+                        #pragma unroll
+                        for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i)
+                            if (i < nr && lane < B)
+                                st_tagged(P.route + (size_t)lane * P.E + in.begin + r0 + i,
                                           pick<B>(res[i], lane) * pick<B>(r, lane), tag_out);
                     };
                     ok = gemv_ring_auto<B>(P, ctl, ring, S, rb, nrows, x, wave, land_wait, epi, false);
@@ -1163,6 +1459,8 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
         for (int w = 0; w < kComputeWaves; ++w) ctl.consumed[w] = 0;
         ctl.bar = 0;
         ctl.abort = 0;
+        ctl.moe_seq = 0;
+        ctl.moe_n = 0;
     }
     if (threadIdx.x < kMaxBatch) ctl.ctx[threadIdx.x] = (int)threadIdx.x < B ? P.state->ctx_len[threadIdx.x] : 0;
     __syncthreads();

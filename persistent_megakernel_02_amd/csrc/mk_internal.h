@@ -88,13 +88,21 @@ enum Op : uint16_t {
     OP_GATEUP = 4,  // RMSNorm + (gate, up) row pairs -> silu(g) * u (fp32)
     OP_DOWN = 5,    // rows of Wdown, residual add
     OP_HEAD = 6,    // final RMSNorm + LM-head rows + argmax partials
+    OP_ROUTE = 7,   // MoE: RMSNorm + router rows -> router logits (fp32)
+    OP_EGU = 8,     // MoE: RMSNorm + top-k routing + (gate, up) row pairs of the selected experts
+    OP_EDOWN = 9,   // MoE: top-k routing + down rows of the selected experts, weighted sum, residual add
 };
 
-constexpr int kPhasesPerLayer = 5;  // QKV, ATTN, O, GATEUP, DOWN
+// MoE limits: the selected-expert set of a layer is one 64-bit mask.
+constexpr int kMaxExperts = 64;
+constexpr int kMaxTopK = 8;
+
+constexpr int kPhasesPerLayer = 5;  // QKV, ATTN, O, GATEUP (MoE: ROUTE, EGU), DOWN (MoE: EDOWN)
 
 // Tag of the values a phase writes in one step: tag0 + layer * 5 + k + 1 with
-// k = 0 QKV output, 1 attention output (and split partials), 2 residual after O,
-// 3 SwiGLU output, 4 residual after DOWN; the LM-head partials use L * 5 + 1.
+// k = 0 QKV output, 1 attention output (and split partials), 2 residual after O
+// (and the MoE router logits, a buffer of their own), 3 SwiGLU output, 4 residual
+// after DOWN; the LM-head partials use L * 5 + 1.
 // tag0 = epoch * (5 L + 2) (mod 2^32) with the epoch counting steps and never
 // reset, so a value left from an earlier step never carries a current tag.
 __host__ __device__ constexpr uint32_t phase_tag(uint32_t tag0, int layer, int k) {
@@ -114,6 +122,7 @@ static_assert(sizeof(Instr) == 16, "instruction record is 16 bytes");
 
 struct DevLayer {
     const uint16_t *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *w_gate, *w_up, *w_down;
+    const uint16_t* router;  // MoE [E, d], else nullptr
 };
 
 // Device-resident state (in the workspace).
@@ -138,6 +147,7 @@ struct Params {
     int32_t qkv_rows, nsplit, n_cu, kv_b;      // kv_b = max_batch of the cache layout
     int32_t down_slices;                       // DOWN runs over F in this many column slices (power of 2)
     int32_t gemv_mfma;                         // 1: GEMVs on the matrix cores (tile-major weight chunks)
+    int32_t E, top_k, n_shared, Fe;            // MoE: experts, selected per token, shared experts, expert width
     float eps, attn_scale;
     // weights
     const DevLayer* layers;
@@ -152,6 +162,9 @@ struct Params {
     uint64_t* act;        // [B][F] SwiGLU output
     uint64_t* attn_part;  // [B][Hkv][nsplit][G][hd + 2] split partials (m, l, o)
     uint64_t* head_part;  // [n_head_slots][B][2] argmax partials (value, index)
+    uint64_t* route;      // MoE [B][E] router logits
+    uint64_t* eact;       // MoE [n_shared + E][B][Fe] SwiGLU outputs of the experts
+    const uint16_t* const* eptr;  // MoE [L][3 (gate, up, down)][n_shared + E] expert matrices (shared first)
     uint32_t* attn_ticket;  // [L][B][Hkv] * kCtrStride, reset by the merger
     uint32_t* head_ticket;  // kCtrStride, reset by the reducer
     DevState* state;

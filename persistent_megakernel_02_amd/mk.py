@@ -178,8 +178,16 @@ class Decoder:
         L = self.cfg.n_layers
         layers = (mk_layer_weights * L)()
         for l in range(L):
-            for n in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down"):
-                setattr(layers[l], n, dw["layers"][l][n].data_ptr())
+            dl = dw["layers"][l]
+            for n in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down", "router", "s_gate",
+                      "s_up", "s_down"):
+                if n in dl:
+                    setattr(layers[l], n, dl[n].data_ptr())
+            for n in ("e_gate", "e_up", "e_down"):  # host arrays of per-expert device pointers
+                if n in dl:
+                    arr = (ctypes.c_void_p * len(dl[n]))(*[t.data_ptr() for t in dl[n]])
+                    self._keep.append(arr)
+                    setattr(layers[l], n, ctypes.cast(arr, ctypes.c_void_p))
         self._layers = layers
         w = mk_weights()
         w.tok_embedding = dw["embed"].data_ptr()
@@ -284,7 +292,13 @@ def upload_weights(weights, device) -> Dict[str, object]:
     out: Dict[str, object] = {"embed": dev(weights.embed), "final_norm": dev(weights.final_norm),
                               "lm_head": dev(weights.lm_head) if weights.lm_head is not None else None, "layers": []}
     for L in weights.layers:
-        out["layers"].append({k: dev(v) for k, v in L.items() if isinstance(v, np.ndarray)})
+        d = {}
+        for k, v in L.items():
+            if isinstance(v, np.ndarray):
+                d[k] = dev(v)
+            elif isinstance(v, (list, tuple)):  # per-expert matrices
+                d[k] = [dev(a) for a in v]
+        out["layers"].append(d)
     return out
 
 

@@ -54,7 +54,7 @@ def test_query_sizes_kv_bytes_match_layout():
     ("n_kv_heads", 5, mk.MK_E_UNSUPPORTED),
     ("hidden", 300, mk.MK_E_UNSUPPORTED),
     ("n_layers", 0, mk.MK_E_INVALID),
-    ("n_experts", 64, mk.MK_E_UNSUPPORTED),
+    ("n_experts", 64, mk.MK_E_INVALID),  # an MoE model needs top_k and expert_ffn
 ])
 def test_query_sizes_rejects_bad_shapes(field, value, status):
     c = mk.model_config(I.LLAMA_1B)
@@ -177,6 +177,42 @@ def test_gemv_kind_in_effect():
     wide = mk.model_config(I.replace(I.LLAMA_1B, hidden=4096))
     assert mk.mk_query_sizes(wide, mk.runtime_config(4, 200, gemv_kind=mk.MK_GEMV_VALU))[0] == mk.MK_OK
     assert mk.mk_query_sizes(wide, mk.runtime_config(4, 200, gemv_kind=mk.MK_GEMV_MFMA))[0] == mk.MK_E_UNSUPPORTED
+
+
+SMALL_MOE = I.replace(I.TINY, name="small-moe", hidden=512, n_q_heads=8, n_kv_heads=4, ffn=0, n_experts=8,
+                      top_k=2, n_shared=1, expert_ffn=512, tied=False)
+
+
+def test_moe_validation():
+    c = mk.model_config(I.MOE)
+    assert mk.mk_query_sizes(c, rt(4, 4200))[0] == mk.MK_OK
+    # the persistent mode and the VALU GEMV only
+    assert mk.mk_query_sizes(c, rt(4, 4200, mode=mk.MK_MODE_GRAPH))[0] == mk.MK_E_UNSUPPORTED
+    assert mk.mk_query_sizes(c, mk.runtime_config(4, 4200, gemv_kind=mk.MK_GEMV_MFMA))[0] == mk.MK_E_UNSUPPORTED
+    # batch 8 would stage 8 x 4096 fp32 activations (128 KB) next to the ring
+    assert mk.mk_query_sizes(c, rt(8, 4200))[0] == mk.MK_E_UNSUPPORTED
+    for field, value, status in (("n_experts", 65, mk.MK_E_INVALID), ("top_k", 9, mk.MK_E_UNSUPPORTED),
+                                 ("top_k", 0, mk.MK_E_INVALID), ("n_shared_experts", 2, mk.MK_E_UNSUPPORTED),
+                                 ("expert_ffn", 1000, mk.MK_E_UNSUPPORTED)):
+        bad = mk.model_config(I.MOE)
+        setattr(bad, field, value)
+        if field == "n_experts":  # 65 experts with top_k 6 passes the first check, not the 64-expert mask
+            assert mk.mk_query_sizes(bad, rt(4, 4200))[0] == mk.MK_E_UNSUPPORTED
+        else:
+            assert mk.mk_query_sizes(bad, rt(4, 4200))[0] == status, field
+
+
+@pytest.mark.parametrize("cfg,batch", [(I.MOE, 4), (I.MOE, 1), (SMALL_MOE, 4)], ids=["moe-b4", "moe-b1", "small-b4"])
+@pytest.mark.parametrize("cus", [256, 7])
+def test_moe_schedule_verifies(cfg, batch, cus):
+    st, info = mk.mk_plan_inspect(mk.model_config(cfg), rt(batch, 300), cus)
+    assert st == mk.MK_OK
+    assert info["verify"] == 0
+    # per layer: QKV, ATTN, O, ROUTE, EGU, EDOWN; then the LM head
+    assert info["phases"] == 6 * cfg.n_layers + 1
+    assert info["weight_bytes"] == cfg.weight_bytes()
+    assert info["ring_chunks"] >= MIN_RING
+    assert info["gemv_kind"] == mk.MK_GEMV_VALU
 
 
 def test_plan_inspect_rejects_bad_cu_count():

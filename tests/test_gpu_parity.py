@@ -255,6 +255,63 @@ def test_llama8b_b1_prefix():
     d.close()
 
 
+SMALL_MOE = I.replace(I.TINY, name="small-moe", hidden=512, n_q_heads=8, n_kv_heads=4, ffn=0, n_experts=8,
+                      top_k=2, n_shared=1, expert_ffn=512, tied=False)
+
+
+@pytest.mark.parametrize("B,cus", [(1, 0), (2, 0), (4, 0), (4, 7), (1, 1)])
+def test_small_moe_parity(B, cus):
+    """A two-layer MoE decoder (8 experts, top 2, one shared expert): router,
+    per-CU top-k, the selected experts' gate/up and down rows, the weighted
+    combine; against the oracle on 256, 7 and 1 CUs."""
+    cfg = SMALL_MOE
+    w = I.make_weights(cfg, seed=12)
+    prompt = I.make_prompt(cfg, B, 6, seed=13)
+    rt_, rl = oracle_run(cfg, w, prompt, 10, 20)
+    print(f"case small MoE b{B} cus={cus}", flush=True)
+    d = _decoder(cfg, w, B, 20, 0, num_cus=cus)
+    gt, gl = gpu_run(d, prompt, rt_, 10)
+    _, near = compare(rt_, rl, gt, gl, f"small MoE b{B} cus={cus}")
+    assert near == 0
+    d.close()
+
+
+def test_moe_b4_long_context():
+    """The synthetic MoE shape (8 layers, hidden 4096, 64 experts, top 6, one
+    shared, expert width 1536) at batch 4 over a 4096-position synthetic context,
+    2 steps; the oracle's routing is checked for near ties first (a near tie could
+    select a different expert on either side)."""
+    cfg = I.MOE
+    B, ctx, steps = 4, 4096, 2
+    t0 = time.time()
+    w = I.make_weights(cfg, seed=14)
+    print(f"MoE weights generated in {time.time() - t0:.1f}s", flush=True)
+    start = I.make_prompt(cfg, B, 1, seed=14)[:, 0]
+    orc = O.Oracle(cfg, w, B, ctx + 8)
+    d = _decoder(cfg, w, B, ctx + 8, 0)
+    _fill_context(cfg, orc, d, ctx, seed=14)
+    torch = _torch()
+    ref_t, ref_l, got_t, got_l = [], [], [], []
+    tok = start.astype(np.int32)
+    for _ in range(steps):
+        nxt, logits, sel, prob = orc.step(tok, moe_trace=True)
+        # k-th and (k+1)-th probabilities of every routing decision well apart
+        srt = -np.sort(-prob, axis=-1)
+        gap = float((srt[..., cfg.top_k - 1] - srt[..., cfg.top_k]).min())
+        print(f"smallest top-k probability gap {gap:.3e}", flush=True)
+        assert gap > 1e-5
+        g_n, g_l = d.decode_step(torch.from_numpy(tok).to(d.device))
+        ref_t.append(nxt.copy())
+        ref_l.append(logits.copy())
+        got_t.append(g_n.cpu().numpy().copy())
+        got_l.append(g_l.cpu().numpy().copy())
+        tok = nxt.astype(np.int32)
+    print(f"MoE done in {time.time() - t0:.1f}s", flush=True)
+    _, near = compare(ref_t, ref_l, got_t, got_l, f"MoE b{B} ctx={ctx}")
+    assert near <= 1
+    d.close()
+
+
 @pytest.mark.parametrize("B", [4, 8])
 def test_tiny_batch_4_8(B):
     """Batches of 4 and 8 sequences (different prompts) in both modes; the two
