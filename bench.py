@@ -26,6 +26,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # Kernel sources whose hash keys the committed counter summary: the summary's
 # traffic figure is reported only while these files are unchanged.
 KERNEL_SOURCES = ["persistent_megakernel_02_amd/csrc/megakernel.hip",
+                  "persistent_megakernel_02_amd/csrc/megakernel_impl.h",
+                  "persistent_megakernel_02_amd/csrc/mk_kernels_valu.hip",
                   "persistent_megakernel_02_amd/csrc/mk_device.h",
                   "persistent_megakernel_02_amd/csrc/mk_internal.h",
                   "persistent_megakernel_02_amd/csrc/host.hip"]

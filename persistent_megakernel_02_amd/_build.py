@@ -9,14 +9,15 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmk.so")
-SOURCES = ["host.hip", "megakernel.hip", "conventional.hip", "bench_kernels.hip"]
+SOURCES = ["mk_kernels_valu.hip", "mk_kernels_mfma.hip", "mk_kernels_moe.hip", "host.hip", "megakernel.hip",
+           "conventional.hip", "bench_kernels.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          # packed fp32 VALU forms stay off (v_pk_fma_f32 and friends)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
+def build(verbose: bool = False, jobs: int = 7) -> str:
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
 

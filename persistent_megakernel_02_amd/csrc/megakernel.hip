@@ -1,1488 +1,30 @@
-// The persistent decode megakernel: one launch runs a whole decode step.
-//
-// Design (page "斯坦福团队新作让Llama1B实现毫秒级推理获Karpathy盛赞", section
-// "Megakernel：从零设计的深度融合方案", re-made for CDNA4):
-//  - one workgroup per compute unit walks that CU's instruction queue, built on
-//    the host before launch (the per-SM plan);
-//  - shared memory cut into pages lets the next instructions' weights load while
-//    the current one computes: LOADER waves stream the CU's weight and KV bytes
-//    HBM -> LDS with 16-byte-per-lane direct-to-LDS loads
-//    (global_load_lds_dwordx4) into a ring of 1 KB chunks that fills every byte
-//    of LDS the activations do not need, ahead of the four COMPUTE waves, and
-//    keep streaming while those wait on other compute units.  One wave's
-//    direct-to-LDS issue rate tops out near 16 GB/s, below a compute unit's
-//    share of HBM bandwidth, so the stream is dealt to kLoaderWaves waves:
-//    chunk c of the CU stream belongs to loader c mod kLoaderWaves;
-//  - dependencies travel with the data: every cross-CU activation is a tagged
-//    word (see mk_internal.h) and an instruction first stages its inputs into
-//    LDS, polling until every tag names the current step and phase;
-//  - every spin is bounded by a watchdog (s_memrealtime, 100 MHz): on expiry the
-//    CU records an error and all waves leave, so a launch always terminates.
-//
-// A loader's vector-memory instructions are only these LDS loads, so its vmcnt
-// counter counts exactly its chunks in flight; after `s_waitcnt vmcnt(N)` it
-// publishes, in LDS, the first of its own chunks not yet resident (its j-th chunk
-// is stream chunk j * kLoaderWaves + k), and the stream prefix resident in the
-// ring is the minimum over the loaders.  Compute waves publish, per wave, the
-// first stream chunk they still need; loaders reuse ring space below the minimum.
+// Host-side launch of the persistent decode megakernel (page
+// "斯坦福团队新作让Llama1B实现毫秒级推理获Karpathy盛赞", section
+// "Megakernel：从零设计的深度融合方案": one launch per decode step).  The kernel
+// templates live in megakernel_impl.h; each kind is instantiated in its own
+// translation unit (mk_kernels_valu.hip, mk_kernels_mfma.hip, mk_kernels_moe.hip)
+// so that a kernel carries only its own code paths.
 #include <hip/hip_runtime.h>
 
-#include "mk_device.h"
+#include "mk_internal.h"
 
 namespace mk {
 
-struct Ctl {
-    uint32_t landed[kLoaderWaves];       // loader k: first stream chunk of its own not yet resident
-    uint32_t consumed[kComputeWaves];    // first chunk each compute wave still needs
-    uint32_t bar;                        // compute-wave barrier arrivals (monotonic)
-    uint32_t abort;                      // set when a wave gives up (error)
-    int32_t ctx[kMaxBatch];              // context lengths at launch
-    float ss[kMaxBatch][kComputeWaves];  // RMSNorm partials of the current instruction
-    // MoE: the selected experts of the current EGU / EDOWN instruction, published
-    // by compute wave 0 for the loaders (moe_seq = queue index + 1 once valid)
-    uint32_t moe_seq, moe_n;
-    uint8_t moe_list[kMaxExperts + 1];  // expert-table slots, shared first, then ascending experts
-};
+const void* kernel_valu(int B, int hd);
+const void* kernel_mfma(int B, int hd);
+const void* kernel_moe(int B, int hd);
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-__device__ __forceinline__ uint32_t lds_ld(const uint32_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ __forceinline__ void lds_st(uint32_t* p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-// s_waitcnt vmcnt(N) (gfx9 encoding: expcnt and lgkmcnt left unconstrained).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ uint32_t align_chunk(uint32_t b) { return (b + kChunk - 1u) & ~(kChunk - 1u); }
-
-// Context length of sequence b (LDS copy made at launch), wave-uniform so the
-// stream arithmetic that depends on it stays on the scalar unit.
-__device__ __forceinline__ int ctx_of(const int32_t* ctx, int b) { return __builtin_amdgcn_readfirstlane(ctx[b]); }
-
-// GEMV instructions of the dense decoder (the ones the matrix-core kernel runs)
-__device__ __forceinline__ bool is_gemv(uint32_t op) {
-    return op == OP_QKV || op == OP_O || op == OP_GATEUP || op == OP_DOWN || op == OP_HEAD;
-}
-__device__ __forceinline__ bool is_moe_expert(uint32_t op) { return op == OP_EGU || op == OP_EDOWN; }
-
-// Stream bytes of an MoE expert instruction with n selected expert slots: per slot
-// the CU's (gate, up) row pairs (EGU) or its down rows (EDOWN), whole rows.
-__device__ __forceinline__ uint32_t moe_bytes(const Params& P, const Instr& in, uint32_t n) {
-    return in.op == OP_EGU ? n * 2u * in.count * (uint32_t)P.d * 2u : n * in.count * (uint32_t)P.Fe * 2u;
-}
-
-// Bytes of the CU stream that instruction `in` consumes (whole chunks).  With the
-// matrix cores (MF) a GEMV streams whole 16-row tiles of 1 KB chunks.
-template <int HD, bool MF = false>
-__device__ __forceinline__ uint32_t instr_bytes(const Params& P, const Instr& in, const int32_t* ctx) {
-    if (MF && is_gemv(in.op)) return mfma_geo<HD>(P, in).chunks() * kChunk;
-    switch (in.op) {
-        case OP_QKV:
-        case OP_ROUTE:
-        case OP_HEAD: return align_chunk(in.count * (uint32_t)P.d * 2u);
-        case OP_O: return align_chunk(in.count * (uint32_t)(P.Hq * HD) * 2u);
-        case OP_GATEUP: return align_chunk(2u * in.count * (uint32_t)P.d * 2u);
-        case OP_DOWN: return align_chunk(in.count * (uint32_t)P.F * 2u);
-        case OP_ATTN: {
-            const int per_b = P.Hkv * P.nsplit;
-            const int b = (int)in.begin / per_b, s = (int)in.begin % P.nsplit;
-            const SplitRange R = split_range<HD>(ctx_of(ctx, b), s, P.nsplit);
-            return (1u + (uint32_t)R.ngroups * 2u) * kChunk;  // RoPE row of position p, then the K/V groups
-        }
-        default: return 0;
-    }
-}
-
-// Global source address of this lane's 16 bytes of chunk c of instruction `in`
-// (rows packed back to back; lanes past the end re-read the first row).  Used
-// for rows that are not a whole number of chunks.
-template <int HD>
-__device__ __forceinline__ const char* chunk_src(const Params& P, const Instr& in, const DevLayer& Lw, uint32_t c,
-                                                 const int32_t* ctx) {
-    const uint32_t off = c * kChunk + (uint32_t)lane_id() * 16u;
-    switch (in.op) {
-        case OP_QKV: {
-            const uint32_t rb = (uint32_t)P.d * 2u;
-            uint32_t r = off / rb, col = off - r * rb;
-            if (r >= in.count) { r = 0; col = 0; }
-            const uint32_t row = in.begin + r, nq = (uint32_t)(P.Hq * HD), nk = (uint32_t)(P.Hkv * HD);
-            const uint16_t* base = row < nq ? Lw.wq + (size_t)row * P.d
-                                 : row < nq + nk ? Lw.wk + (size_t)(row - nq) * P.d
-                                                 : Lw.wv + (size_t)(row - nq - nk) * P.d;
-            return (const char*)base + col;
-        }
-        case OP_O: {
-            const uint32_t K = (uint32_t)(P.Hq * HD), rb = K * 2u;
-            uint32_t r = off / rb, col = off - r * rb;
-            if (r >= in.count) { r = 0; col = 0; }
-            return (const char*)(Lw.wo + (size_t)(in.begin + r) * K) + col;
-        }
-        case OP_GATEUP: {
-            const uint32_t rb = (uint32_t)P.d * 2u;
-            uint32_t j = off / rb, col = off - j * rb;
-            if (j >= 2u * in.count) { j = 0; col = 0; }
-            const uint16_t* W = (j & 1u) ? Lw.w_up : Lw.w_gate;
-            return (const char*)(W + (size_t)(in.begin + (j >> 1)) * P.d) + col;
-        }
-        case OP_DOWN: {
-            const uint32_t rb = (uint32_t)P.F * 2u;
-            uint32_t r = off / rb, col = off - r * rb;
-            if (r >= in.count) { r = 0; col = 0; }
-            return (const char*)(Lw.w_down + (size_t)(in.begin + r) * P.F) + col;
-        }
-        case OP_HEAD:
-        case OP_ROUTE: {
-            const uint32_t rb = (uint32_t)P.d * 2u;
-            uint32_t r = off / rb, col = off - r * rb;
-            if (r >= in.count) { r = 0; col = 0; }
-            return (const char*)((in.op == OP_HEAD ? P.head : Lw.router) + (size_t)(in.begin + r) * P.d) + col;
-        }
-        case OP_ATTN: {
-            constexpr uint32_t rbkv = HD * 2u;
-            const int per_b = P.Hkv * P.nsplit;
-            const int b = (int)in.begin / per_b, g = ((int)in.begin % per_b) / P.nsplit, s = (int)in.begin % P.nsplit;
-            const int p = ctx_of(ctx, b);
-            if (c == 0) {  // (cos, sin) row of position p: HD / 2 float2, lanes past it re-read its start
-                const uint32_t lo = (uint32_t)lane_id() * 16u;
-                return (const char*)(P.rope + (size_t)p * (HD / 2)) + (lo < HD * 4u ? lo : 0u);
-            }
-            const SplitRange R = split_range<HD>(p, s, P.nsplit);
-            const uint32_t o = off - kChunk;
-            const uint32_t t = o >> 11, w = o & 2047u, inner = w & 1023u;
-            int pos = R.s0 + (int)(t * AttnGeom<HD>::PPW + inner / rbkv);
-            uint32_t col = inner % rbkv;
-            if (pos >= R.s0 + R.ncached) { pos = R.s0; col = 0; }
-            const uint16_t* cache = (w >= 1024u) ? P.vcache : P.kcache;
-            return (const char*)(cache + ((((size_t)in.layer * P.kv_b + b) * P.Hkv + g) * P.S + pos) * HD) + col;
-        }
-        default: return (const char*)P.embed;
-    }
-}
-
-__device__ __forceinline__ uint32_t min_consumed(const Ctl* ctl) {
-    uint32_t m = lds_ld(&ctl->consumed[0]);
-#pragma unroll
-    for (int w = 1; w < kComputeWaves; ++w) m = min(m, lds_ld(&ctl->consumed[w]));
-    return m;
-}
-
-// One 1 KB chunk HBM -> LDS: each lane moves 16 bytes from `src` to
-// lds_addr + 16 * lane.  Written as one asm block (M0 is set and consumed inside
-// it, the instruction has no destination register) so the compiler neither
-// counts it nor guards later LDS accesses with vmcnt waits: this wave's vmcnt is
-// managed explicitly by the loader.
-// Weight and KV bytes are read once per step, so the loads carry the
-// non-temporal hint: in a measured dependency edge under full streaming this
-// kept the exchanged words faster to reach (about 0.7 us less per edge).
-__device__ __forceinline__ void dma_chunk(const char* src, uint32_t lds_addr) {
-    asm volatile(
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off nt"
-        :
-        : "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src)
-        : "memory");
-}
-
-// Same transfer with a wave-uniform base in SGPRs and a per-lane 32-bit offset.
-// The base usually comes out of v_readfirstlane, a VALU write of an SGPR, and a
-// VMEM instruction that reads such an SGPR as its address needs five wait
-// states after the write (CDNA3/CDNA4 ISA, manually inserted wait states).  The
-// compiler does not look inside asm for hazards, so the block supplies them
-// itself; the same s_nop also covers the one wait state after the M0 write.
-__device__ __forceinline__ void dma_chunk_s(const char* base, uint32_t voff, uint32_t lds_addr) {
-    asm volatile(
-        "s_nop 4\n\t"
-        "global_load_lds_dwordx4 %0, %1 offset:0 nt"
-        :
-        : "v"(voff), "s"(base), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
-        : "memory");
-}
-
-__device__ __forceinline__ const char* uniform_ptr(const char* p) {
-    const uint64_t v = (uint64_t)p;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return (const char*)(((uint64_t)hi << 32) | lo);
-}
-
-// Byte model of an instruction's stream on the fast path.  Consecutive rows of a
-// row-major matrix are consecutive bytes, so every stream is one of:
-//  - up to three contiguous byte ranges read in order (QKV: the q, k and v rows
-//    of the tile; O, DOWN, HEAD: one range);
-//  - two matrices interleaved row by row (GATEUP: gate row r then up row r),
-//    2^per_shift chunks of each in turn;
-//  - the K and V blocks of consecutive position groups interleaved (ATTN), one
-//    chunk each, lanes past the cached positions re-reading the block start.
-// Only pointers and chunk counts, all wave-uniform: the address of any chunk is
-// a few scalar operations, so a loader can take every kLoaderWaves-th chunk.
-struct Stream {
-    const char *p0, *p1, *p2;
-    const char* head;     // ATTN: the (cos, sin) row streamed as chunk 0 ahead of the groups
-    uint32_t end0, end1;  // ranges: chunk ends of the first two ranges
-    uint32_t per_shift;   // interleaved: log2(chunks of each matrix per turn); sliced: log2(chunks per row slice)
-    int ncached;          // ATTN: valid positions of the split
-    uint32_t nrow, row_bytes, slice_bytes;  // sliced (DOWN over column slices): rows, row stride, slice width
-    bool inter, attn, sliced;
-};
-
-template <int HD>
-__device__ __forceinline__ bool setup_stream(const Params& P, const Instr& in, const DevLayer& Lw, const int32_t* ctx,
-                                             Stream& S) {
-    S.inter = false;
-    S.attn = false;
-    S.sliced = false;
-    S.nrow = S.row_bytes = S.slice_bytes = 0;
-    S.ncached = 0;
-    S.per_shift = 0;
-    S.p1 = S.p2 = S.head = nullptr;
-    S.end0 = S.end1 = 0xFFFFFFFFu;
-    uint32_t rb = 0;
-    switch (in.op) {
-        case OP_QKV: {
-            rb = (uint32_t)P.d * 2u;
-            if (rb & (kChunk - 1u)) return false;
-            const uint32_t cpr = rb / kChunk;
-            const uint32_t nq = (uint32_t)(P.Hq * HD), nk = (uint32_t)(P.Hkv * HD);
-            const uint32_t r0 = in.begin, r1 = in.begin + in.count;
-            const uint32_t q0 = min(r0, nq), q1 = min(r1, nq);
-            const uint32_t k0 = min(max(r0, nq), nq + nk) - nq, k1 = min(max(r1, nq), nq + nk) - nq;
-            const uint32_t v0 = max(r0, nq + nk) - nq - nk;
-            S.p0 = (const char*)Lw.wq + (size_t)q0 * rb;
-            S.p1 = (const char*)Lw.wk + (size_t)k0 * rb;
-            S.p2 = (const char*)Lw.wv + (size_t)v0 * rb;
-            S.end0 = (q1 - q0) * cpr;
-            S.end1 = S.end0 + (k1 - k0) * cpr;
-            return true;
-        }
-        case OP_O: rb = (uint32_t)(P.Hq * HD) * 2u; S.p0 = (const char*)Lw.wo + (size_t)in.begin * rb; break;
-        case OP_DOWN:
-            rb = (uint32_t)P.F * 2u;
-            S.p0 = (const char*)Lw.w_down + (size_t)in.begin * rb;
-            if (P.down_slices > 1) {
-                // slice-major: the rows' first column slices, then their second, ...
-                S.sliced = true;
-                S.nrow = in.count;
-                S.row_bytes = rb;
-                S.slice_bytes = rb / (uint32_t)P.down_slices;
-                S.per_shift = (uint32_t)__builtin_ctz(S.slice_bytes / kChunk);
-                return (S.slice_bytes & (kChunk - 1u)) == 0 && ((S.slice_bytes / kChunk) & (S.slice_bytes / kChunk - 1u)) == 0;
-            }
-            break;
-        case OP_HEAD: rb = (uint32_t)P.d * 2u; S.p0 = (const char*)P.head + (size_t)in.begin * rb; break;
-        case OP_ROUTE: rb = (uint32_t)P.d * 2u; S.p0 = (const char*)Lw.router + (size_t)in.begin * rb; break;
-        case OP_GATEUP: {
-            rb = (uint32_t)P.d * 2u;
-            const uint32_t cpr = rb / kChunk;
-            if ((rb & (kChunk - 1u)) || (cpr & (cpr - 1u))) return false;  // whole, power-of-two chunks per row
-            S.p0 = (const char*)Lw.w_gate + (size_t)in.begin * rb;
-            S.p1 = (const char*)Lw.w_up + (size_t)in.begin * rb;
-            S.per_shift = (uint32_t)__builtin_ctz(cpr);
-            S.inter = true;
-            return true;
-        }
-        case OP_ATTN: {
-            const int per_b = P.Hkv * P.nsplit;
-            const int b = (int)in.begin / per_b, g = ((int)in.begin % per_b) / P.nsplit, s = (int)in.begin % P.nsplit;
-            const int p = ctx_of(ctx, b);
-            const SplitRange Rg = split_range<HD>(p, s, P.nsplit);
-            const size_t base = ((((size_t)in.layer * P.kv_b + b) * P.Hkv + g) * P.S + Rg.s0) * HD;
-            S.p0 = (const char*)(P.kcache + base);
-            S.p1 = (const char*)(P.vcache + base);
-            S.head = (const char*)(P.rope + (size_t)p * (HD / 2));
-            S.ncached = Rg.ncached;
-            S.inter = true;
-            S.attn = true;
-            return true;
-        }
-        default: return false;
-    }
-    return (rb & (kChunk - 1u)) == 0;  // fast path needs whole chunks per row
-}
-
-// Wave-uniform base and per-lane offset of chunk c (instruction-relative) of a
-// fast-path stream.
-template <int HD>
-__device__ __forceinline__ const char* stream_chunk(const Stream& S, uint32_t c, uint32_t& voff) {
-    const uint32_t lane16 = (uint32_t)lane_id() * 16u;
-    if (S.sliced) {
-        const uint32_t seg = c >> S.per_shift, within = c & ((1u << S.per_shift) - 1u);
-        const uint32_t slice = seg / S.nrow, row = seg - slice * S.nrow;
-        voff = row * S.row_bytes + slice * S.slice_bytes + within * kChunk + lane16;
-        return S.p0;
-    }
-    if (!S.inter) {
-        if (c < S.end0) {
-            voff = c * kChunk + lane16;
-            return S.p0;
-        }
-        if (c < S.end1) {
-            voff = (c - S.end0) * kChunk + lane16;
-            return S.p1;
-        }
-        voff = (c - S.end1) * kChunk + lane16;
-        return S.p2;
-    }
-    if (S.attn) {
-        if (c == 0) {  // the (cos, sin) row: HD * 4 bytes, lanes past it re-read its start
-            voff = lane16 < (uint32_t)HD * 4u ? lane16 : 0u;
-            return S.head;
-        }
-        c -= 1u;
-    }
-    const uint32_t pair = c >> (S.per_shift + 1u);
-    const uint32_t within = c & ((2u << S.per_shift) - 1u);
-    const uint32_t off = ((pair << S.per_shift) + (within & ((1u << S.per_shift) - 1u))) * kChunk;
-    bool valid = true;
-    if (S.attn) valid = (int)(pair * AttnGeom<HD>::PPW) + lane_id() / AttnGeom<HD>::LPP < S.ncached;
-    voff = off + (valid ? lane16 : 0u);
-    return (within >> S.per_shift) ? S.p1 : S.p0;
-}
-
-// ------------------------------------------------------------------------------------------------
-// loader waves
-// ------------------------------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t landed_prefix(const Ctl* ctl) {
-    uint32_t m = lds_ld(&ctl->landed[0]);
-#pragma unroll
-    for (int k = 1; k < kLoaderWaves; ++k) m = min(m, lds_ld(&ctl->landed[k]));
-    return m;
-}
-
-template <int HD, bool MF>
-__device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* ring, int k, uint32_t q0, uint32_t q1,
-                                            const int32_t* ctx) {
-    const uint32_t N = P.ring_chunks;
-    const uint32_t NL = (uint32_t)kLoaderWaves;
-    const uint32_t ring_base = (uint32_t)(size_t)(lds_ptr_t)ring;
-    const uint32_t ring_end = ring_base + N * kChunk;
-    uint32_t issued = 0, landed = 0;  // this loader's own chunks
-    uint32_t limit = N;               // stream chunks below it may be written
-    uint32_t cb = 0;                  // stream index of the current instruction's first chunk
-    uint32_t c = (uint32_t)k;         // stream index of this loader's next chunk (c = k mod NL)
-    uint32_t slot = ring_base + ((uint32_t)k % N) * kChunk;  // LDS address of ring slot c mod N
-    bool stop = false;
-    uint32_t stall = 0;
-    auto publish = [&](uint32_t n) {
-        landed = n;
-        lds_st(&ctl->landed[k], n * NL + (uint32_t)k);
-    };
-    // Ring full: retire this loader's chunks in flight in steps (so compute waves
-    // can free space without the pipe draining), then sleep until space appears.
-    auto make_room = [&]() -> bool {
-        const uint32_t ts = P.trace ? (uint32_t)now_ticks() : 0u;
-        uint64_t t0 = 0;
-        uint32_t polls = 0;
-        bool ok = true;
-        for (;;) {
-            limit = __builtin_amdgcn_readfirstlane(min_consumed(ctl)) + N;
-            if (c < limit) break;
-            const uint32_t fly = issued - landed;
-            if (fly > 12u) {
-                wait_vmcnt<12>();
-                publish(issued - 12u);
-            } else if (fly > 4u) {
-                wait_vmcnt<4>();
-                publish(issued - 4u);
-            } else if (fly > 0u) {
-                wait_vmcnt<0>();
-                publish(issued);
-            } else {
-                if (lds_ld(&ctl->abort)) {
-                    ok = false;
-                    break;
-                }
-                if (polls++ == 0) t0 = now_ticks();
-                if ((polls & 255u) == 0 && now_ticks() - t0 > P.spin_ticks) {
-                    raise_error_impl(P.state, P.host_err, &ctl->abort, DERR_TIMEOUT, 0xFFFFFFFDu, issued);
-                    ok = false;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-        }
-        if (P.trace) stall += (uint32_t)now_ticks() - ts;
-        return ok;
-    };
-    // after each issue: next own chunk and slot, and keep at most kLoaderLag in
-    // flight.  (Throttling the loaders while the compute waves poll for their
-    // inputs measured slower: the polls barely sped up and the stream lost more.)
-    auto advance = [&]() {
-        c += NL;
-        slot += NL * kChunk;
-        if (slot >= ring_end) slot -= N * kChunk;
-        ++issued;
-        if (issued - landed > (uint32_t)kLoaderLag) {
-            wait_vmcnt<kLoaderLag>();
-            publish(issued - (uint32_t)kLoaderLag);
-        }
-    };
-    // MoE expert instructions: the streamed experts are known only once the compute
-    // waves have routed.  Retire every chunk in flight first (the compute waves may
-    // still need them to reach this instruction), then wait for the published list.
-    auto wait_moe = [&](uint32_t want) -> bool {
-        if (issued != landed) {
-            wait_vmcnt<0>();
-            publish(issued);
-        }
-        const uint64_t t0 = now_ticks();
-        uint32_t polls = 0;
-        while (lds_ld(&ctl->moe_seq) != want) {
-            if (lds_ld(&ctl->abort)) return false;
-            if ((++polls & 255u) == 0 && now_ticks() - t0 > P.spin_ticks) {
-                raise_error_impl(P.state, P.host_err, &ctl->abort, DERR_TIMEOUT, 0xFFFFFFFCu, want);
-                return false;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        return true;
-    };
-    for (uint32_t i = q0; i < q1 && !stop; ++i) {
-        const Instr in = ld_const(P.instrs + i);
-        uint32_t nch;
-        if (!MF && is_moe_expert(in.op)) {
-            if (!wait_moe(i + 1u)) {
-                stop = true;
-                break;
-            }
-            nch = moe_bytes(P, in, lds_ld(&ctl->moe_n)) / kChunk;
-        } else {
-            nch = instr_bytes<HD, MF>(P, in, ctx) / kChunk;
-        }
-        if (k == 0 && P.trace && lane_id() == 0 && i > q0) {
-            uint32_t* rec = P.trace + ((size_t)blockIdx.x * P.trace_stride + (i - 1 - q0)) * kTraceWords;
-            rec[5] = (uint32_t)now_ticks();
-            rec[7] = stall;
-        }
-        stall = 0;
-        const uint32_t ce = cb + nch;
-        if (c < ce) {
-            const DevLayer Lw = ld_const(P.layers + (in.layer < P.L ? in.layer : 0));
-            Stream S;
-            if (MF && is_gemv(in.op)) {
-                // tile-major chunks: slot l holds row rr = l / PPR of the chunk (tile
-                // row r), piece (l % PPR) ^ (r % PPR) of its run.  Rows past the end
-                // (only in a last-group chunk) re-read the last row: every chunk must
-                // be one load in flight, since the landed count is derived from
-                // vmcnt and a chunk without a load would let an older one be
-                // published early.  Per slice, the full groups and the last group
-                // are walked as two regions.  In the full groups this loader takes
-                // chunks h0 and h0 + 4 of every unit (h0 = its phase at the region
-                // start; the region is a multiple of four chunks long), so its lanes'
-                // rows are fixed and a chunk's address is a lane base plus a uniform
-                // tile and column offset.
-                const MfmaGeo g = mfma_geo<HD>(P, in);
-                const uint32_t ks = g.K / g.slices, lane = (uint32_t)lane_id();
-                const uint32_t rr = lane / kMfmaPiecesPerRow, pp = lane % kMfmaPiecesPerRow;
-                const bool qkv = in.op == OP_QKV, gu = in.op == OP_GATEUP;
-                const char* ra = (const char*)gemv_row(P, Lw, in, 0u);
-                const char* rb = (const char*)gemv_row(P, Lw, in, gu ? 1u : 0u);
-                const uint32_t shift = gu ? 1u : 0u;
-                const uint64_t stride = (uint64_t)(gu ? (uint32_t)P.d : g.K) * 2u;
-                auto row_ptr = [&](uint32_t j) -> const char* {  // row j of the instruction
-                    return qkv ? (const char*)gemv_row(P, Lw, in, j)
-                               : ((j & shift) ? rb : ra) + (uint64_t)(j >> shift) * stride;
-                };
-                const uint64_t tile_stride = (uint64_t)stride * (16u >> shift);  // rows of one tile
-                const uint32_t FC = g.full_chunks(), LC = g.KU * g.CR;
-                for (uint32_t sl = 0, rs = cb; sl < g.slices && !stop && c < ce; ++sl) {
-                    const uint32_t col0 = sl * ks * 2u;
-                    if (FC && c < rs + FC) {
-                        const uint32_t h0 = c - rs;  // < 4
-                        const uint32_t r0 = h0 * kMfmaChunkRows + rr, r1 = (h0 + 4u) * kMfmaChunkRows + rr;
-                        const uint32_t p0 = col0 + (pp ^ (r0 % kMfmaPiecesPerRow)) * 16u;
-                        const uint32_t p1 = col0 + (pp ^ (r1 % kMfmaPiecesPerRow)) * 16u;
-                        const char* b0 = row_ptr(r0) + p0;
-                        const char* b1 = row_ptr(r1) + p1;
-                        uint32_t hs = 0, tl = 0, ku = 0, grp = 0;
-                        for (; c < rs + FC; ) {
-                            if (c >= limit && !make_room()) {
-                                stop = true;
-                                break;
-                            }
-                            const uint32_t t = grp * 4u + tl, kc = ku * (64u * kMfmaUnitKb);
-                            // QKV rows span three matrices: their address is taken per chunk
-                            const char* src = qkv ? row_ptr(t * 16u + (hs ? r1 : r0)) + (hs ? p1 : p0) + kc
-                                                  : (hs ? b1 : b0) + (uint64_t)t * tile_stride + kc;
-                            dma_chunk(src, slot);
-                            advance();
-                            if (kMfmaUnitChunks == 8u && hs == 0u) {
-                                hs = 1u;
-                                continue;
-                            }
-                            hs = 0u;
-                            if (++tl == 4u) {
-                                tl = 0;
-                                if (++ku == g.KU) ku = 0, ++grp;
-                            }
-                        }
-                    }
-                    rs += FC;
-                    if (stop) break;
-                    // the last group: CR chunks per k-unit holding its rows in order
-                    if (c < rs + LC) {
-                        uint32_t x = c - rs, ku = x / g.CR, ch = x - ku * g.CR;
-                        for (; c < rs + LC; ) {
-                            if (c >= limit && !make_room()) {
-                                stop = true;
-                                break;
-                            }
-                            const uint32_t gr = ch * kMfmaChunkRows + rr, r = gr & 15u;
-                            const uint32_t j = min(g.G4 * 64u + gr, g.nrows - 1u);
-                            dma_chunk(row_ptr(j) + col0 + ku * (64u * kMfmaUnitKb) + (pp ^ (r % kMfmaPiecesPerRow)) * 16u,
-                                      slot);
-                            advance();
-                            for (ch += kLoaderWaves; ch >= g.CR; ch -= g.CR) ++ku;
-                        }
-                    }
-                    rs += LC;
-                }
-            } else if (!MF && is_moe_expert(in.op)) {
-                // selected expert slot a, chunk w of its rows; the slot's matrices come
-                // from the expert table (gate and up rows interleaved as in GATEUP)
-                const bool egu = in.op == OP_EGU;
-                const uint32_t n = lds_ld(&ctl->moe_n), nx = (uint32_t)(P.n_shared + P.E);
-                const uint32_t rb = egu ? (uint32_t)P.d * 2u : (uint32_t)P.Fe * 2u;
-                const uint32_t per = (egu ? 2u * in.count : in.count) * rb / kChunk;
-                const uint16_t* const* tab = P.eptr + (size_t)in.layer * 3u * nx;
-                auto slot_stream = [&](uint32_t a, Stream& X) {
-                    const uint32_t x = __builtin_amdgcn_readfirstlane((uint32_t)ctl->moe_list[a]);
-                    X.attn = X.sliced = false;
-                    X.end0 = X.end1 = 0xFFFFFFFFu;
-                    X.p1 = X.p2 = X.head = nullptr;
-                    if (egu) {
-                        X.p0 = (const char*)(ld_const(tab + x) + (size_t)in.begin * P.d);
-                        X.p1 = (const char*)(ld_const(tab + nx + x) + (size_t)in.begin * P.d);
-                        X.per_shift = (uint32_t)__builtin_ctz(rb / kChunk);
-                        X.inter = true;
-                    } else {
-                        X.p0 = (const char*)(ld_const(tab + 2u * nx + x) + (size_t)in.begin * P.Fe);
-                        X.inter = false;
-                    }
-                };
-                uint32_t a = (c - cb) / per, w = (c - cb) - a * per;
-                if (a < n) slot_stream(a, S);
-                for (; c < ce; ) {
-                    if (c >= limit && !make_room()) {
-                        stop = true;
-                        break;
-                    }
-                    uint32_t voff;
-                    const char* base = uniform_ptr(stream_chunk<HD>(S, w, voff));
-                    dma_chunk_s(base, voff, slot);
-                    advance();
-                    for (w += NL; w >= per && a < n; w -= per)
-                        if (++a < n) slot_stream(a, S);
-                }
-            } else if (setup_stream<HD>(P, in, Lw, ctx, S)) {
-                for (; c < ce; ) {
-                    if (c >= limit && !make_room()) {
-                        stop = true;
-                        break;
-                    }
-                    uint32_t voff;
-                    const char* base = uniform_ptr(stream_chunk<HD>(S, c - cb, voff));
-                    dma_chunk_s(base, voff, slot);
-                    advance();
-                }
-            } else {
-                for (; c < ce; ) {
-                    if (c >= limit && !make_room()) {
-                        stop = true;
-                        break;
-                    }
-                    dma_chunk(chunk_src<HD>(P, in, Lw, c - cb, ctx), slot);
-                    advance();
-                }
-            }
-        }
-        cb = ce;
-    }
-    wait_vmcnt<0>();
-    landed = issued;
-    lds_st(&ctl->landed[k], 0xFFFFFFFFu);  // every chunk of this loader is resident
-    if (k == 0 && P.trace && q1 > q0 && lane_id() == 0) {
-        P.trace[((size_t)blockIdx.x * P.trace_stride + (q1 - 1 - q0)) * kTraceWords + 5] = (uint32_t)now_ticks();
-        P.trace[((size_t)blockIdx.x * P.trace_stride + (q1 - 1 - q0)) * kTraceWords + 7] = stall;
-    }
-}
-
-// ------------------------------------------------------------------------------------------------
-// compute waves
-// ------------------------------------------------------------------------------------------------
-// Wait until the loader has `need` chunks resident; adds the ticks spent waiting
-// to `waited` (read only by the trace).
-__device__ __forceinline__ bool wait_landed(const Params& P, Ctl* ctl, uint32_t need, uint32_t& waited) {
-    if (landed_prefix(ctl) >= need) {
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        return true;
-    }
-    const uint64_t t0 = now_ticks();
-    uint32_t polls = 0;
-    bool ok = true;
-    while (landed_prefix(ctl) < need) {
-        if (lds_ld(&ctl->abort)) {
-            ok = false;
-            break;
-        }
-        if ((++polls & 255u) == 0 && now_ticks() - t0 > P.spin_ticks) {
-            raise_error_impl(P.state, P.host_err, &ctl->abort, DERR_TIMEOUT, 0xFFFFFFFFu, need);
-            ok = false;
-            break;
-        }
-        __builtin_amdgcn_s_sleep(0);
-    }
-    waited += (uint32_t)(now_ticks() - t0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    return ok;
-}
-
-__device__ __forceinline__ void set_consumed(Ctl* ctl, int wave, uint32_t chunk) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    lds_st(&ctl->consumed[wave], chunk);
-}
-
-// Barrier of the compute waves only (the loader wave never joins s_barrier).
-// False when the workgroup aborted or the watchdog expired.
-struct CwBarrier {
-    Ctl* ctl;
-    const Params* P;
-    uint32_t gen;
-    __device__ __forceinline__ bool operator()() {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        if (lane_id() == 0) __hip_atomic_fetch_add(&ctl->bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        const uint32_t target = (++gen) * (uint32_t)kComputeWaves;
-        const uint64_t t0 = now_ticks();
-        uint32_t polls = 0;
-        while (lds_ld(&ctl->bar) < target) {
-            if (lds_ld(&ctl->abort)) return false;
-            if ((++polls & 255u) == 0 && now_ticks() - t0 > P->spin_ticks) {
-                raise_error_impl(P->state, P->host_err, &ctl->abort, DERR_TIMEOUT, 0xFFFFFFFEu, target);
-                return false;
-            }
-            __builtin_amdgcn_s_sleep(0);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        return true;
-    }
-};
-
-// Ring byte address of stream byte x.
-__device__ __forceinline__ uint32_t ring_addr(uint32_t x, uint32_t nchunks) {
-    return ((x >> 10) % nchunks) * kChunk + (x & (kChunk - 1u));
-}
-
-// Rows [0, nrows) of the current instruction from the ring in batches of R
-// consecutive rows; batch t goes to compute wave t mod kComputeWaves, so the
-// four waves work on neighbouring rows and the ring span stays small.
-template <int B, int R, class Epi>
-__device__ __forceinline__ bool gemv_ring(const Params& P, Ctl* ctl, const char* ring, uint32_t S, uint32_t rb,
-                                          uint32_t nrows, const XLds& x, int wave, uint32_t& lw, Epi& epi) {
-    const int np = (int)(rb >> 4);
-    const uint32_t ring_bytes = P.ring_chunks * kChunk;
-    for (uint32_t r0 = (uint32_t)wave * R; r0 < nrows; r0 += (uint32_t)R * kComputeWaves) {
-        const uint32_t nr = min((uint32_t)R, nrows - r0);
-        const uint32_t off = S + r0 * rb;
-        set_consumed(ctl, wave, off / kChunk);
-        if (!wait_landed(P, ctl, (off + nr * rb + kChunk - 1u) / kChunk, lw)) return false;
-        const RingBatch rows{ring, ring_addr(off, P.ring_chunks), rb, ring_bytes};
-        float res[R][B];
-        rows_dot<B, R>(rows, np, x, res);
-        epi(r0, nr, res);
-    }
-    return true;
-}
-
-// Batch size by row length; GATEUP keeps a (gate, up) pair inside one batch.
-template <int B, class Epi>
-__device__ __forceinline__ bool gemv_ring_auto(const Params& P, Ctl* ctl, const char* ring, uint32_t S, uint32_t rb,
-                                               uint32_t nrows, const XLds& x, int wave, uint32_t& lw, Epi& epi,
-                                               bool pairs) {
-    const int R = rows_per_batch(rb, B);
-    if (R >= 4) return gemv_ring<B, 4>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
-    if (R == 2 || pairs) return gemv_ring<B, 2>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
-    return gemv_ring<B, 1>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
-}
-
-// Matrix-core GEMV over one column slice of an instruction whose tile-major
-// chunks start at stream byte S0.  Full groups: wave w owns tile 4 g + w and
-// every k-unit of it.  The last group of m tiles is shared: wave w takes the
-// units v = w, w + 4, ... (v = ku m + tile) and the four partial tiles are added
-// in wave order through `red` (behind a barrier of the compute waves); a partial
-// tile's unit has fewer chunks, and the rows past the end read whatever follows
-// (their sums are never stored).  epi(t, v) gets tile t's sums (combine_parts
-// layout).  Units are taken kMfmaBatchUnits at a time: one wait for the last of
-// their chunks, all operand reads issued together, and alternate k-blocks go to
-// two accumulators, so neither the LDS latency nor the accumulation chain is
-// paid per k-block.
-constexpr uint32_t kMfmaBatchKb = 8;
-constexpr uint32_t kMfmaBatchUnits = kMfmaBatchKb >= kMfmaUnitKb ? kMfmaBatchKb / kMfmaUnitKb : 1u;
-
-// Operand A of k-block e of the unit whose first chunk sits at ring slot s0 (of
-// N): this lane's tile row r = l % 16 in chunk r / R, piece 4 e + l / 16 at its
-// XOR-swizzled slot.
-__device__ __forceinline__ uint4 unit_a(const char* ring, uint32_t s0, uint32_t N, uint32_t e) {
-    const uint32_t l = (uint32_t)lane_id(), r = l & 15u, p = e * 4u + (l >> 4);
-    uint32_t ci = s0 + r / kMfmaChunkRows;
-    ci = ci >= N ? ci - N : ci;
-    const uint32_t slot = (r % kMfmaChunkRows) * kMfmaPiecesPerRow + (p ^ (r % kMfmaPiecesPerRow));
-    return *(const uint4*)(ring + ci * kChunk + slot * 16u);
-}
-
-template <int B, int PRT, class Epi>
-__device__ __forceinline__ bool gemv_mfma_ring(const Params& P, Ctl* ctl, const char* ring, uint32_t S0,
-                                               const MfmaGeo& g, const char* area, char* red, int wave, uint32_t& lw,
-                                               Epi& epi, CwBarrier& barrier) {
-    constexpr uint32_t PB = (uint32_t)(PRT * B), PBP = (uint32_t)parts_pitch(B);
-    constexpr uint32_t U = kMfmaBatchUnits, KBU = kMfmaUnitKb, NC = kMfmaUnitChunks;
-    const uint32_t c0 = S0 / kChunk, N = P.ring_chunks;
-    for (uint32_t grp = 0; grp < g.G4; ++grp) {
-        floatx4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = d0;
-        const uint32_t cb = c0 + NC * (grp * 4u * g.KU + (uint32_t)wave);  // first chunk of k-unit 0
-        for (uint32_t k0 = 0; k0 < g.KU; k0 += U) {
-            const uint32_t n = min(U, g.KU - k0);
-            set_consumed(ctl, wave, cb + k0 * 4u * NC);
-            if (!wait_landed(P, ctl, cb + (k0 + n - 1u) * 4u * NC + NC, lw)) return false;
-            uint4 a[U * KBU];
-            bf16x8_t b[U * KBU];
-#pragma unroll
-            for (uint32_t u = 0; u < U; ++u)
-                if (u < n) {
-                    const uint32_t s0 = (cb + (k0 + u) * 4u * NC) % N;
-#pragma unroll
-                    for (uint32_t e = 0; e < KBU; ++e) {
-                        a[u * KBU + e] = unit_a(ring, s0, N, e);
-                        b[u * KBU + e] = load_parts(area, (k0 + u) * KBU + e, PB, PBP);
-                    }
-                }
-#pragma unroll
-            for (uint32_t u = 0; u < U; ++u)
-                if (u < n) {
-#pragma unroll
-                    for (uint32_t e = 0; e < KBU; ++e) {
-                        if (e & 1u) d1 = mfma_acc(a[u * KBU + e], b[u * KBU + e], d1);
-                        else d0 = mfma_acc(a[u * KBU + e], b[u * KBU + e], d0);
-                    }
-                }
-        }
-        epi(grp * 4u + (uint32_t)wave, combine_parts<PRT>(d0 + d1));
-    }
-    const uint32_t m = g.m;
-    if (m) {
-        floatx4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = d0, d2 = d0, d3 = d0;
-        const uint32_t base = c0 + g.full_chunks(), total = m * g.KU;  // units of the last group
-        // first chunk and chunk count of unit v (k-unit v / m, tile v % m)
-        auto ustart = [&](uint32_t v, uint32_t& cnt) -> uint32_t {
-            const uint32_t ku = v / m, t = v - ku * m;
-            cnt = min(NC, g.CR - t * NC);
-            return base + ku * g.CR + t * NC;
-        };
-        for (uint32_t v0 = (uint32_t)wave; v0 < total; v0 += 4u * U) {
-            const uint32_t n = min(U, (total - v0 + 3u) / 4u);  // units v0, v0 + 4, ... below total
-            uint32_t cnt0, cntl;
-            const uint32_t first = ustart(v0, cnt0), lastc = ustart(v0 + 4u * (n - 1u), cntl);
-            set_consumed(ctl, wave, first);
-            if (!wait_landed(P, ctl, lastc + cntl, lw)) return false;
-            uint4 a[U * KBU];
-            bf16x8_t b[U * KBU];
-#pragma unroll
-            for (uint32_t i = 0; i < U; ++i)
-                if (i < n) {
-                    const uint32_t v = v0 + 4u * i, ku = v / m;
-                    uint32_t cnt;
-                    const uint32_t s0 = ustart(v, cnt) % N;
-#pragma unroll
-                    for (uint32_t e = 0; e < KBU; ++e) {
-                        a[i * KBU + e] = unit_a(ring, s0, N, e);
-                        b[i * KBU + e] = load_parts(area, ku * KBU + e, PB, PBP);
-                    }
-                }
-#pragma unroll
-            for (uint32_t i = 0; i < U; ++i)
-                if (i < n) {
-                    const uint32_t v = v0 + 4u * i, t = v - (v / m) * m;
-                    floatx4_t x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
-#pragma unroll
-                    for (uint32_t e = 0; e < KBU; ++e) {
-                        if (e & 1u) x1 = mfma_acc(a[i * KBU + e], b[i * KBU + e], x1);
-                        else x0 = mfma_acc(a[i * KBU + e], b[i * KBU + e], x0);
-                    }
-                    const floatx4_t x = x0 + x1;
-                    if (t == 0) d0 += x;
-                    else if (t == 1) d1 += x;
-                    else if (t == 2) d2 += x;
-                    else d3 += x;
-                }
-        }
-        red_store<B, PRT>(red, wave, 0, combine_parts<PRT>(d0));
-        if (m > 1) red_store<B, PRT>(red, wave, 1, combine_parts<PRT>(d1));
-        if (m > 2) red_store<B, PRT>(red, wave, 2, combine_parts<PRT>(d2));
-        if (m > 3) red_store<B, PRT>(red, wave, 3, combine_parts<PRT>(d3));
-        if (!barrier()) return false;
-        if ((uint32_t)wave < m) epi(4u * g.G4 + (uint32_t)wave, red_sum<B, PRT>(red, (uint32_t)wave));
-    }
-    return true;
-}
-
-// Lane of a combined tile: holds rows 4 (lane / 16) + r of batch row b when it is
-// the part-0 lane of b (column PRT b).
-template <int B, int PRT>
-__device__ __forceinline__ bool mfma_lane(int& b, uint32_t& row4) {
-    const uint32_t l = (uint32_t)lane_id(), j = l & 15u;
-    b = (int)(j / (uint32_t)PRT);
-    row4 = (l >> 4) * 4u;
-    return j % (uint32_t)PRT == 0u && j < (uint32_t)(PRT * B);
-}
-
-// One GEMV instruction (QKV, O, GATEUP, DOWN or the LM head) on the matrix cores:
-// the staged activations land as bf16 parts at the start of the activation
-// area, the cross-wave partial tiles at its end.  Same epilogues as the VALU
-// path; each used lane of a combined tile owns four consecutive rows of one
-// batch row.
-template <int B, int HD>
-__device__ __forceinline__ bool mfma_instr(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs,
-                                        int wave, const Instr& in, uint32_t S, Spin& spin, CwBarrier& barrier,
-                                        uint32_t& land_wait, uint32_t* tr) {
-    constexpr int PRT = mfma_parts(B);
-    constexpr uint32_t PB = (uint32_t)(PRT * B);
-    const int lane = lane_id();
-    const int layer = in.layer;
-    const DevLayer Lw = ld_const(P.layers + (layer < P.L ? layer : 0));
-    char* area = (char*)xs;
-    char* red = (char*)xs + P.x_bytes - mfma_red_bytes(B);
-    const MfmaGeo g = mfma_geo<HD>(P, in);
-    int lb;
-    uint32_t row4;
-    const bool lane_ok = mfma_lane<B, PRT>(lb, row4);
-    lb = lb < B ? lb : B - 1;
-    if (in.op == OP_O || in.op == OP_DOWN) {
-        const bool is_o = in.op == OP_O;
-        const uint32_t K = is_o ? (uint32_t)(P.Hq * HD) : (uint32_t)P.F;
-        const uint32_t tag_x = is_o ? phase_tag(A.tag0, layer, 1) : phase_tag(A.tag0, layer, 3);
-        const uint32_t tag_res = is_o ? phase_tag(A.tag0, layer - 1, 4) : phase_tag(A.tag0, layer, 2);
-        const uint32_t tag_out = is_o ? phase_tag(A.tag0, layer, 2) : phase_tag(A.tag0, layer, 4);
-        const uint32_t ns = g.slices, Ks = K / ns;
-        float* hres = (float*)(area + parts_bytes(B, (int)Ks));  // [B][count] residual rows
-        float* part = hres + B * in.count;                        // [B][count] partial sums
-        for (uint32_t ks = 0; ks < ns; ++ks) {
-            if (ks > 0 && !barrier()) return false;
-            float ss[1] = {0.f};
-            const StageSeg sx = {(is_o ? P.attn : P.act) + ks * Ks, (float*)area, nullptr, Ks, (uint32_t)B, K, Ks,
-                                 tag_x, (uint32_t)PRT};
-            if (ks > 0) {
-                const StageSeg sg[1] = {sx};
-                if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kComputeWaves, spin, ss)) return false;
-            } else if (is_o && layer == 0) {
-#pragma unroll
-                for (int b = 0; b < B; ++b)
-                    stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * P.d + in.begin, in.count,
-                               hres + b * in.count, nullptr, wave, kComputeWaves, ss[0]);
-                const StageSeg sg[1] = {sx};
-                if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kComputeWaves, spin, ss)) return false;
-            } else {
-                const StageSeg sg[2] = {sx, {P.h + in.begin, hres, nullptr, in.count, (uint32_t)B, (uint32_t)P.d,
-                                             in.count, tag_res, 0u}};
-                if (!stage_segs<kStagePassWordsWide, 1, 2>(sg, wave, kComputeWaves, spin, ss)) return false;
-            }
-            if (!barrier()) return false;
-            if (tr && lane == 0 && ks == 0) tr[2] = (uint32_t)now_ticks();
-            const bool last = ks + 1 == ns;
-            auto epi = [&](uint32_t t, floatx4_t v) {
-                if (!lane_ok) return;
-#pragma unroll
-                for (uint32_t r = 0; r < 4u; ++r) {
-                    const uint32_t j = t * 16u + row4 + r;
-                    if (j < in.count) {
-                        float x = v[r];
-                        if (ks > 0) x = part[lb * in.count + j] + x;
-                        if (!last) part[lb * in.count + j] = x;
-                        else st_tagged(P.h + (size_t)lb * P.d + in.begin + j, hres[lb * in.count + j] + x, tag_out);
-                    }
-                }
-            };
-            if (!gemv_mfma_ring<B, PRT>(P, ctl, ring, S + ks * g.slice_chunks() * kChunk, g, area, red, wave, land_wait,
-                                        epi, barrier))
-                return false;
-        }
-        return true;
-    }
-    // QKV, GATEUP, HEAD: RMSNorm of the residual stream, then the rows
-    const uint16_t* gain = in.op == OP_QKV ? Lw.attn_norm : in.op == OP_GATEUP ? Lw.mlp_norm : P.final_norm;
-    const uint32_t tag_in = in.op == OP_QKV      ? phase_tag(A.tag0, layer - 1, 4)
-                            : in.op == OP_GATEUP ? phase_tag(A.tag0, layer, 2)
-                                                 : phase_tag(A.tag0, P.L - 1, 4);
-    const uint32_t d = (uint32_t)P.d;
-    float ss[B];
-#pragma unroll
-    for (int b = 0; b < B; ++b) ss[b] = 0.f;
-    if (in.op == OP_QKV && layer == 0) {
-#pragma unroll
-        for (int b = 0; b < B; ++b)
-            stage_bf16_parts<PRT>(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * d, d, area, (uint32_t)b,
-                                  (uint32_t)parts_pitch(B), gain, wave, kComputeWaves, ss[b]);
-    } else {
-        const StageSeg sg[1] = {{P.h, (float*)area, gain, d, (uint32_t)B, d, d, tag_in, (uint32_t)PRT}};
-        if (!stage_segs<kStagePassWords, B, 1>(sg, wave, kComputeWaves, spin, ss)) return false;
-    }
-    wave_total_n<B>(ss);
-    if (lane == 0) {
-#pragma unroll
-        for (int b = 0; b < B; ++b) ctl->ss[b][wave] = ss[b];
-    }
-    if (!barrier()) return false;
-    float r[B];
-#pragma unroll
-    for (int b = 0; b < B; ++b) r[b] = rms_scale(ctl->ss[b], kComputeWaves, P.d, P.eps);
-    const float rl = pick<B>(r, lb);
-    if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
-    if (in.op == OP_QKV) {
-        const uint32_t tag_out = phase_tag(A.tag0, layer, 0);
-        auto epi = [&](uint32_t t, floatx4_t v) {
-            if (!lane_ok) return;
-#pragma unroll
-            for (uint32_t rr = 0; rr < 4u; ++rr) {
-                const uint32_t j = t * 16u + row4 + rr;
-                if (j < g.nrows) st_tagged(P.qkv + (size_t)lb * P.qkv_rows + in.begin + j, v[rr] * rl, tag_out);
-            }
-        };
-        return gemv_mfma_ring<B, PRT>(P, ctl, ring, S, g, area, red, wave, land_wait, epi, barrier);
-    }
-    if (in.op == OP_GATEUP) {
-        const uint32_t tag_out = phase_tag(A.tag0, layer, 3);
-        auto epi = [&](uint32_t t, floatx4_t v) {
-            if (!lane_ok) return;
-#pragma unroll
-            for (uint32_t pr = 0; pr < 2u; ++pr) {
-                const uint32_t j = t * 16u + row4 + 2u * pr;  // gate row j, up row j + 1
-                if (j + 1u < g.nrows)
-                    st_tagged(P.act + (size_t)lb * P.F + in.begin + j / 2u,
-                              silu_mul(v[2 * pr] * rl, v[2 * pr + 1] * rl), tag_out);
-            }
-        };
-        return gemv_mfma_ring<B, PRT>(P, ctl, ring, S, g, area, red, wave, land_wait, epi, barrier);
-    }
-    // LM head: logits, and each lane's best row of its batch row
-    float bv = -INFINITY;
-    int32_t bi = 0x7FFFFFFF;
-    bool nan_seen = false;
-    auto epi = [&](uint32_t t, floatx4_t v) {
-        if (!lane_ok) return;
-#pragma unroll
-        for (uint32_t rr = 0; rr < 4u; ++rr) {
-            const uint32_t j = t * 16u + row4 + rr;
-            if (j < g.nrows) {
-                const float x = v[rr] * rl;
-                const int32_t row = (int32_t)(in.begin + j);
-                if (x != x) nan_seen = true;
-                if (head_better(x, row, bv, bi)) {
-                    bv = x;
-                    bi = row;
-                }
-                A.logits[(size_t)lb * P.V + row] = x;
-            }
-        }
-    };
-    if (!gemv_mfma_ring<B, PRT>(P, ctl, ring, S, g, area, red, wave, land_wait, epi, barrier)) return false;
-    // the four lanes of a column (lane % 16) hold disjoint rows of one batch row
-#pragma unroll
-    for (int msk = 16; msk <= 32; msk <<= 1) {
-        const float ov = __shfl_xor(bv, msk, 64);
-        const int32_t oi = __shfl_xor(bi, msk, 64);
-        if (head_better(ov, oi, bv, bi)) {
-            bv = ov;
-            bi = oi;
-        }
-    }
-    float best_v[B];
-    int32_t best_i[B];
-    const bool any_nan = __any(nan_seen);
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-        best_v[b] = any_nan ? __int_as_float(0x7FC00000)
-                            : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), PRT * b));
-        best_i[b] = __builtin_amdgcn_readlane(bi, PRT * b);
-    }
-    return head_publish<B>(P, A, in.slot * kComputeWaves + (uint32_t)wave, best_v, best_i, spin);
-}
-
-// ------------------------------------------------------------------------------------------------
-// MoE FFN (the synthetic MoE decoder's layers): router logits (OP_ROUTE), then on
-// every CU the selected experts' (gate, up) rows of its f-range (OP_EGU) and
-// their down rows of its output rows (OP_EDOWN).  Each CU routes for itself from
-// the router logits, so every CU derives the same selected set; only the
-// selected experts' rows are streamed.
-// ------------------------------------------------------------------------------------------------
-
-// Top-k routing of one sequence; lane e < E holds the router logit of expert e.
-// Probabilities are the softmax evaluated in double and rounded to fp32; the k
-// largest are selected, ties to the lower expert index (NaN never wins).
-// Returns the selected-expert mask; `prob` = this lane's probability.
-__device__ __forceinline__ uint64_t route_topk(float z, int E, int K, float& prob) {
-    const int lane = lane_id();
-    const bool valid = lane < E;
-    float m = valid ? z : -INFINITY;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    const double ex = valid ? exp((double)z - (double)m) : 0.0;
-    double Z = ex;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) Z += __shfl_xor(Z, o, 64);
-    prob = valid ? (float)(ex / Z) : -1.0f;
-    const uint64_t valid_mask = E >= 64 ? ~0ull : ((1ull << E) - 1ull);
-    uint64_t sel = 0;
-    for (int t = 0; t < K; ++t) {
-        const float v = ((sel >> lane) & 1ull) || !valid ? -2.0f : prob;
-        float best = v;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) best = fmaxf(best, __shfl_xor(best, o, 64));
-        uint64_t cand = __ballot(v == best) & valid_mask & ~sel;
-        if (!cand) cand = valid_mask & ~sel;  // NaN probabilities: the lowest index not yet taken
-        sel |= 1ull << __builtin_ctzll(cand);
-    }
-    return sel;
-}
-
-// Routes the B sequences from the router logits at zeta [B][E] (LDS); returns the
-// union of the selected sets and, per sequence, the mask and this lane's
-// probability.  Wave 0 publishes the expert-table slots of the union (shared
-// first) for the loaders and the other waves; the caller's barrier orders it.
-template <int B>
-__device__ __forceinline__ uint32_t moe_route(const Params& P, Ctl* ctl, const float* zeta, int wave, uint32_t qi,
-                                              uint64_t (&sel)[B], float (&prob)[B]) {
-    const int lane = lane_id();
-    uint64_t U = 0;
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-        const float z = lane < P.E ? zeta[b * P.E + lane] : 0.f;
-        sel[b] = route_topk(z, P.E, P.top_k, prob[b]);
-        U |= sel[b];
-    }
-    const uint32_t n = (uint32_t)P.n_shared + (uint32_t)__builtin_popcountll(U);
-    if (wave == 0 && lane == 0) {
-        uint32_t a = 0;
-        for (int x = 0; x < P.n_shared; ++x) ctl->moe_list[a++] = (uint8_t)x;
-        for (uint64_t u = U; u; u &= u - 1ull) ctl->moe_list[a++] = (uint8_t)(P.n_shared + __builtin_ctzll(u));
-        ctl->moe_n = n;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        lds_st(&ctl->moe_seq, qi + 1u);
-    }
-    return n;
-}
-
-// OP_EGU: x = RMSNorm(h after O) * g; route; then for every selected slot the
-// CU's (gate, up) row pairs of f-range [begin, begin + count): SwiGLU outputs.
-template <int B>
-__device__ __forceinline__ bool moe_egu(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs,
-                                        int wave, const Instr& in, uint32_t qi, uint32_t S, Spin& spin,
-                                        CwBarrier& barrier, uint32_t& land_wait, uint32_t* tr, uint32_t& bytes) {
-    const int lane = lane_id();
-    const int layer = in.layer;
-    const DevLayer Lw = ld_const(P.layers + layer);
-    const uint32_t d = (uint32_t)P.d, E = (uint32_t)P.E;
-    const uint32_t tag_o = phase_tag(A.tag0, layer, 2);
-    float* zeta = xs + B * d;
-    float ss[B];
-#pragma unroll
-    for (int b = 0; b < B; ++b) ss[b] = 0.f;
-    const StageSeg sg[2] = {{P.h, xs, Lw.mlp_norm, d, (uint32_t)B, d, d, tag_o, 0u},
-                            {P.route, zeta, nullptr, E, (uint32_t)B, E, E, tag_o, 0u}};
-    if (!stage_segs<kStagePassWords, B, 2>(sg, wave, kComputeWaves, spin, ss)) return false;
-    wave_total_n<B>(ss);
-    if (lane == 0) {
-#pragma unroll
-        for (int b = 0; b < B; ++b) ctl->ss[b][wave] = ss[b];
-    }
-    if (!barrier()) return false;
-    float r[B];
-#pragma unroll
-    for (int b = 0; b < B; ++b) r[b] = rms_scale(ctl->ss[b], kComputeWaves, P.d, P.eps);
-    uint64_t sel[B];
-    float prob[B];
-    const uint32_t n = moe_route<B>(P, ctl, zeta, wave, qi, sel, prob);
-    if (!barrier()) return false;  // the slot list is visible
-    if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
-    bytes = moe_bytes(P, in, n);
-    const uint32_t per = 2u * in.count, tag_out = phase_tag(A.tag0, layer, 3);
-    auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
-        #pragma unroll
-        for (uint32_t i = 0; i + 1 < (uint32_t)(sizeof(res) / sizeof(res[0])); i += 2) {
-            if (i + 1 >= nr) break;
-            const uint32_t j = r0 + i, a = j / per, f = in.begin + (j - a * per) / 2u;
-            const uint32_t x = ctl->moe_list[a];
-            if (lane < B) {
-                const float rr = pick<B>(r, lane);
-                st_tagged(P.eact + ((size_t)x * P.B + lane) * P.Fe + f,
-                          silu_mul(pick<B>(res[i], lane) * rr, pick<B>(res[i + 1], lane) * rr), tag_out);
-            }
-        }
-    };
-    return gemv_ring_auto<B>(P, ctl, ring, S, d * 2u, n * per, XLds{xs, d}, wave, land_wait, epi, true);
-}
-
-// OP_EDOWN: route again (same logits, same result); for every selected slot in
-// order (shared, then ascending experts) stage its SwiGLU rows and add its down
-// rows [begin, begin + count), weighted by the sequence's probability (1 for the
-// shared expert, 0 where the sequence did not select it); then h += the sum.
-template <int B>
-__device__ __forceinline__ bool moe_edown(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs,
-                                          int wave, const Instr& in, uint32_t qi, uint32_t S, Spin& spin,
-                                          CwBarrier& barrier, uint32_t& land_wait, uint32_t* tr, uint32_t& bytes) {
-    const int lane = lane_id();
-    const int layer = in.layer;
-    const uint32_t E = (uint32_t)P.E, Fe = (uint32_t)P.Fe, cnt = in.count;
-    const uint32_t tag_o = phase_tag(A.tag0, layer, 2), tag_a = phase_tag(A.tag0, layer, 3);
-    float* hres = xs + B * Fe;    // [B][cnt] residual rows after O
-    float* acc = hres + B * cnt;  // [B][cnt] weighted expert sums
-    float* zeta = acc + B * cnt;  // [B][E] router logits
-    float* wtab = zeta + B * E;   // [slot][B] weights of the selected slots
-    {
-        float ss[1] = {0.f};
-        const StageSeg sg[2] = {{P.route, zeta, nullptr, E, (uint32_t)B, E, E, tag_o, 0u},
-                                {P.h + in.begin, hres, nullptr, cnt, (uint32_t)B, (uint32_t)P.d, cnt, tag_o, 0u}};
-        if (!stage_segs<kStagePassWordsWide, 1, 2>(sg, wave, kComputeWaves, spin, ss)) return false;
-    }
-    if (!barrier()) return false;
-    uint32_t n;
-    {
-        uint64_t sel[B];
-        float prob[B];
-        n = moe_route<B>(P, ctl, zeta, wave, qi, sel, prob);
-        if (wave == 0) {
-            // weight of slot a for sequence b: 1 (shared), its probability where b
-            // selected the expert, else 0; lane e writes expert e's slot
-            uint64_t U = 0;
-#pragma unroll
-            for (int b = 0; b < B; ++b) U |= sel[b];
-            const bool mine = lane < P.E && ((U >> lane) & 1ull);
-            const uint32_t slot = (uint32_t)P.n_shared + (uint32_t)__builtin_popcountll(U & ((1ull << lane) - 1ull));
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                if (mine) wtab[slot * B + b] = ((sel[b] >> lane) & 1ull) ? prob[b] : 0.f;
-                if (lane < P.n_shared) wtab[lane * B + b] = 1.0f;
-            }
-            for (uint32_t i = (uint32_t)lane; i < B * cnt; i += 64u) acc[i] = 0.f;
-        }
-    }
-    if (!barrier()) return false;  // the slot list, the weights and the zeroed sums are visible
-    if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
-    bytes = moe_bytes(P, in, n);
-    const uint32_t rb = Fe * 2u;
-    for (uint32_t a = 0; a < n; ++a) {
-        const uint32_t x = __builtin_amdgcn_readfirstlane((uint32_t)ctl->moe_list[a]);
-        float wgt[B];
-#pragma unroll
-        for (int b = 0; b < B; ++b) wgt[b] = wtab[a * B + b];
-        if (a > 0 && !barrier()) return false;  // every wave is done with the previous slot's rows
-        float ss[1] = {0.f};
-        const StageSeg sa[1] = {{P.eact + (size_t)x * P.B * Fe, xs, nullptr, Fe, (uint32_t)B, Fe, Fe, tag_a, 0u}};
-        if (!stage_segs<kStagePassWordsWide, 1, 1>(sa, wave, kComputeWaves, spin, ss)) return false;
-        if (!barrier()) return false;
-        auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
-            #pragma unroll
-            for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i) {
-                if (i >= nr) break;
-                if (lane < B) {
-                    const float wv = pick<B>(wgt, lane);
-                    if (wv != 0.f) acc[lane * cnt + r0 + i] += wv * pick<B>(res[i], lane);
-                }
-            }
-        };
-        if (!gemv_ring_auto<B>(P, ctl, ring, S + a * cnt * rb, rb, cnt, XLds{xs, Fe}, wave, land_wait, epi, false))
-            return false;
-    }
-    if (!barrier()) return false;
-    const uint32_t tag_out = phase_tag(A.tag0, layer, 4);
-    for (uint32_t i = (uint32_t)(wave * 64 + lane); i < B * cnt; i += 64u * kComputeWaves) {
-        const uint32_t b = i / cnt, j = i - b * cnt;
-        st_tagged(P.h + (size_t)b * P.d + in.begin + j, hres[i] + acc[i], tag_out);
-    }
-    return true;
-}
-
-// One attention item (sequence, KV head, split) as an instruction.
-template <int B, int HD>
-__device__ __forceinline__ bool attn_instr(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs,
-                                           int wave, const Instr& in, uint32_t S, Spin& spin, CwBarrier& barrier,
-                                           uint32_t& land_wait, uint32_t* tr, const int32_t* ctx) {
-    const int lane = lane_id();
-    const int per_b = P.Hkv * P.nsplit;
-    const int b = (int)in.begin / per_b, g = ((int)in.begin % per_b) / P.nsplit, s = (int)in.begin % P.nsplit;
-    // stream: [RoPE row 1 KB][group 0: K 1 KB, V 1 KB][group 1] ...
-    const RingKV<HD> kv{ring, S + kChunk, P.ring_chunks};
-    auto need = [&](int t) -> bool {  // group t resident (K and V chunks); t = -1: the RoPE row
-        return wait_landed(P, ctl, (S + kChunk + (uint32_t)(t + 1) * 2048u) / kChunk, land_wait);
-    };
-    auto release = [&](int t) {  // groups before t no longer needed by this wave
-        set_consumed(ctl, wave, (S + kChunk + (uint32_t)t * 2048u) / kChunk);
-    };
-    if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
-    auto mark = [&](int m) {
-        if (tr && lane == 0) tr[9 + m] = (uint32_t)now_ticks();
-    };
-    return attn_item<HD>(P, A.tag0, in.layer, b, g, s, ctx_of(ctx, b), kv, need, release, barrier, xs, wave,
-                         kComputeWaves, spin, mark);
-}
-
-template <int B, int HD, bool MF>
-__device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs, int wave,
-                             uint32_t q0, uint32_t q1, const int32_t* ctx) {
-    const int lane = lane_id();
-    uint32_t S = 0, k = 0;
-    Spin spin(&P, &ctl->abort);
-    CwBarrier barrier{ctl, &P, 0u};
-    for (uint32_t qi = q0; qi < q1; ++qi, ++k) {
-        const Instr in = ld_const(P.instrs + qi);
-        uint32_t bytes = instr_bytes<HD, MF>(P, in, ctx);  // MoE expert instructions set it once routed
-        uint32_t* tr =
-            (P.trace && wave == 0) ? P.trace + ((size_t)blockIdx.x * P.trace_stride + k) * kTraceWords : nullptr;
-        if (tr && lane == 0) {
-            tr[0] = (uint32_t)in.op | ((uint32_t)in.layer << 16);
-            tr[1] = (uint32_t)now_ticks();
-        }
-        // every wave has finished reading the previous instruction's staged inputs
-        if (!barrier()) return;
-        if (tr && lane == 0) tr[8] = (uint32_t)now_ticks();
-        uint32_t land_wait = 0;
-        const int layer = in.layer;
-        const DevLayer Lw = ld_const(P.layers + (layer < P.L ? layer : 0));
-        bool ok = true;
-        // (the matrix-core kernel carries no VALU GEMV code: a smaller kernel)
-        if constexpr (MF) {
-            if (is_gemv(in.op)) ok = mfma_instr<B, HD>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr);
-            else if (in.op == OP_ATTN) ok = attn_instr<B, HD>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr, ctx);
-        } else switch (in.op) {
-            case OP_EGU:
-                ok = moe_egu<B>(P, A, ctl, ring, xs, wave, in, qi, S, spin, barrier, land_wait, tr, bytes);
-                break;
-            case OP_EDOWN:
-                ok = moe_edown<B>(P, A, ctl, ring, xs, wave, in, qi, S, spin, barrier, land_wait, tr, bytes);
-                break;
-            case OP_QKV:
-            case OP_GATEUP:
-            case OP_ROUTE:
-            case OP_HEAD: {
-                const uint16_t* gain = in.op == OP_QKV ? Lw.attn_norm : in.op == OP_HEAD ? P.final_norm : Lw.mlp_norm;
-                const uint32_t tag_in = in.op == OP_QKV    ? phase_tag(A.tag0, layer - 1, 4)
-                                        : in.op == OP_HEAD ? phase_tag(A.tag0, P.L - 1, 4)
-                                                           : phase_tag(A.tag0, layer, 2);
-                const uint32_t d = (uint32_t)P.d;
-                float ss[B];
-#pragma unroll
-                for (int b = 0; b < B; ++b) ss[b] = 0.f;
-                if (in.op == OP_QKV && layer == 0) {
-#pragma unroll
-                    for (int b = 0; b < B; ++b)
-                        stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * d, d, xs + b * d, gain, wave,
-                                   kComputeWaves, ss[b]);
-                } else {
-                    const StageSeg sg[1] = {{P.h, xs, gain, d, (uint32_t)B, d, d, tag_in}};
-                    if (!stage_segs<kStagePassWords, B, 1>(sg, wave, kComputeWaves, spin, ss)) return;
-                }
-                wave_total_n<B>(ss);
-                if (lane == 0) {
-#pragma unroll
-                    for (int b = 0; b < B; ++b) ctl->ss[b][wave] = ss[b];
-                }
-                if (!barrier()) return;
-                float r[B];
-#pragma unroll
-                for (int b = 0; b < B; ++b) r[b] = rms_scale(ctl->ss[b], kComputeWaves, P.d, P.eps);
-                if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
-                const uint32_t rb = d * 2u;
-                const XLds x{xs, d};
-                const uint32_t nrows = in.op == OP_GATEUP ? 2u * in.count : in.count;
-                if (in.op == OP_QKV) {
-                    const uint32_t tag_out = phase_tag(A.tag0, layer, 0);
-                    auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
-                        #pragma unroll
-                        for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i)
-                            if (i < nr && lane < B)
-                                st_tagged(P.qkv + (size_t)lane * P.qkv_rows + in.begin + r0 + i,
-                                          pick<B>(res[i], lane) * pick<B>(r, lane), tag_out);
-                    };
-                    ok = gemv_ring_auto<B>(P, ctl, ring, S, rb, nrows, x, wave, land_wait, epi, false);
-                } else if (in.op == OP_ROUTE) {
-                    // router logits of experts begin.., tagged like the residual after O
-                    const uint32_t tag_out = phase_tag(A.tag0, layer, 2);
-                    auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
-                        #pragma unroll
-                        for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i)
-                            if (i < nr && lane < B)
-                                st_tagged(P.route + (size_t)lane * P.E + in.begin + r0 + i,
-                                          pick<B>(res[i], lane) * pick<B>(r, lane), tag_out);
-                    };
-                    ok = gemv_ring_auto<B>(P, ctl, ring, S, rb, nrows, x, wave, land_wait, epi, false);
-                } else if (in.op == OP_GATEUP) {
-                    const uint32_t tag_out = phase_tag(A.tag0, layer, 3);
-                    auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
-                        #pragma unroll
-                        for (uint32_t i = 0; i + 1 < (uint32_t)(sizeof(res) / sizeof(res[0])); i += 2) {
-                            if (i + 1 >= nr) break;
-                            const uint32_t f = in.begin + (r0 + i) / 2u;
-                            if (lane < B) {
-                                const float rr = pick<B>(r, lane);
-                                st_tagged(P.act + (size_t)lane * P.F + f,
-                                          silu_mul(pick<B>(res[i], lane) * rr, pick<B>(res[i + 1], lane) * rr),
-                                          tag_out);
-                            }
-                        }
-                    };
-                    ok = gemv_ring_auto<B>(P, ctl, ring, S, rb, nrows, x, wave, land_wait, epi, true);
-                } else {
-                    float best_v[B];
-                    int32_t best_i[B];
-                    bool nan_seen = false;
-#pragma unroll
-                    for (int b = 0; b < B; ++b) {
-                        best_v[b] = -INFINITY;
-                        best_i[b] = 0x7FFFFFFF;
-                    }
-                    auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
-                        #pragma unroll
-                        for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i) {
-                            if (i >= nr) break;
-                            const int32_t row = (int32_t)(in.begin + r0 + i);
-#pragma unroll
-                            for (int b = 0; b < B; ++b) {
-                                const float v = res[i][b] * r[b];
-                                if (v != v) nan_seen = true;
-                                if (head_better(v, row, best_v[b], best_i[b])) {
-                                    best_v[b] = v;
-                                    best_i[b] = row;
-                                }
-                            }
-                            if (lane < B) A.logits[(size_t)lane * P.V + row] = pick<B>(res[i], lane) * pick<B>(r, lane);
-                        }
-                    };
-                    ok = gemv_ring_auto<B>(P, ctl, ring, S, rb, nrows, x, wave, land_wait, epi, false);
-                    if (ok) {
-                        if (nan_seen) {
-#pragma unroll
-                            for (int b = 0; b < B; ++b) best_v[b] = __int_as_float(0x7FC00000);
-                        }
-                        ok = head_publish<B>(P, A, in.slot * kComputeWaves + (uint32_t)wave, best_v, best_i, spin);
-                    }
-                }
-                break;
-            }
-            case OP_O:
-            case OP_DOWN: {
-                const bool is_o = in.op == OP_O;
-                const uint32_t K = is_o ? (uint32_t)(P.Hq * HD) : (uint32_t)P.F;
-                const uint32_t tag_x = is_o ? phase_tag(A.tag0, layer, 1) : phase_tag(A.tag0, layer, 3);
-                const uint32_t tag_res = is_o ? phase_tag(A.tag0, layer - 1, 4) : phase_tag(A.tag0, layer, 2);
-                const uint32_t tag_out = is_o ? phase_tag(A.tag0, layer, 2) : phase_tag(A.tag0, layer, 4);
-                // DOWN runs over P.down_slices column slices of its input (the stream is
-                // slice-major); partial sums of the rows wait in LDS between slices
-                const uint32_t ns = is_o ? 1u : (uint32_t)P.down_slices, Ks = K / ns;
-                float* hres = xs + B * Ks;         // [B][count] residual rows before this op
-                float* part = hres + B * in.count;  // [B][count] partial sums
-                for (uint32_t ks = 0; ks < ns && ok; ++ks) {
-                    if (ks > 0 && !barrier()) return;  // every wave is done with the previous slice
-                    float ss[1] = {0.f};
-                    const StageSeg sx = {(is_o ? P.attn : P.act) + ks * Ks, xs, nullptr, Ks, (uint32_t)B, K, Ks,
-                                         tag_x};
-                    if (ks > 0) {
-                        const StageSeg sg[1] = {sx};
-                        if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kComputeWaves, spin, ss)) return;
-                    } else if (is_o && layer == 0) {
-                        // the residual is the token embedding: no wait
-#pragma unroll
-                        for (int b = 0; b < B; ++b)
-                            stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * P.d + in.begin,
-                                       in.count, hres + b * in.count, nullptr, wave, kComputeWaves, ss[0]);
-                        const StageSeg sg[1] = {sx};
-                        if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kComputeWaves, spin, ss)) return;
-                    } else {
-                        const StageSeg sg[2] = {sx, {P.h + in.begin, hres, nullptr, in.count, (uint32_t)B,
-                                                     (uint32_t)P.d, in.count, tag_res}};
-                        if (!stage_segs<kStagePassWordsWide, 1, 2>(sg, wave, kComputeWaves, spin, ss)) return;
-                    }
-                    if (!barrier()) return;
-                    if (tr && lane == 0 && ks == 0) tr[2] = (uint32_t)now_ticks();
-                    const XLds x{xs, Ks};
-                    const bool last = ks + 1 == ns;
-                    auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
-                        #pragma unroll
-                        for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i) {
-                            if (i >= nr) break;
-                            const uint32_t j = r0 + i;
-                            if (lane < B) {
-                                float v = pick<B>(res[i], lane);
-                                if (ks > 0) v = part[lane * in.count + j] + v;
-                                if (!last) {
-                                    part[lane * in.count + j] = v;
-                                } else {
-                                    st_tagged(P.h + (size_t)lane * P.d + in.begin + j, hres[lane * in.count + j] + v,
-                                              tag_out);
-                                }
-                            }
-                        }
-                    };
-                    ok = gemv_ring_auto<B>(P, ctl, ring, S + ks * in.count * Ks * 2u, Ks * 2u, in.count, x, wave,
-                                           land_wait, epi, false);
-                }
-                break;
-            }
-            case OP_ATTN: ok = attn_instr<B, HD>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr, ctx); break;
-            default: break;
-        }
-        if (!ok || lds_ld(&ctl->abort)) return;
-        if (tr && lane == 0) {
-            tr[3] = (uint32_t)now_ticks();
-            tr[6] = land_wait;
-        }
-        if (P.trace && wave > 0 && in.op != OP_ATTN && lane == 0)  // the other waves' compute ends
-            P.trace[((size_t)blockIdx.x * P.trace_stride + k) * kTraceWords + 8 + wave] = (uint32_t)now_ticks();
-        S += bytes;
-        set_consumed(ctl, wave, S / kChunk);
-        if (tr && lane == 0) tr[4] = (uint32_t)now_ticks();
-    }
-}
-
-template <int B, int HD, bool MF>
-__global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs A) {
-    extern __shared__ __attribute__((aligned(16))) char lds[];
-    __shared__ Ctl ctl;
-    char* ring = lds;
-    float* xs = (float*)(lds + (size_t)P.ring_chunks * kChunk);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (threadIdx.x == 0) {
-        for (int k = 0; k < kLoaderWaves; ++k) ctl.landed[k] = (uint32_t)k;
-        for (int w = 0; w < kComputeWaves; ++w) ctl.consumed[w] = 0;
-        ctl.bar = 0;
-        ctl.abort = 0;
-        ctl.moe_seq = 0;
-        ctl.moe_n = 0;
-    }
-    if (threadIdx.x < kMaxBatch) ctl.ctx[threadIdx.x] = (int)threadIdx.x < B ? P.state->ctx_len[threadIdx.x] : 0;
-    __syncthreads();
-    const uint32_t q0 = ld_const(P.queue_off + blockIdx.x), q1 = ld_const(P.queue_off + blockIdx.x + 1);
-    if (wave >= kComputeWaves) {
-        loader_wave<HD, MF>(P, &ctl, ring, wave - kComputeWaves, q0, q1, ctl.ctx);
-    } else {
-        compute_wave<B, HD, MF>(P, A, &ctl, ring, xs, wave, q0, q1, ctl.ctx);
-    }
-}
-
-// ------------------------------------------------------------------------------------------------
-// host-side launch
-// ------------------------------------------------------------------------------------------------
 size_t megakernel_lds_bytes(const Params& P) { return (size_t)P.ring_chunks * kChunk + P.x_bytes; }
 
-template <int B, int HD>
-static hipError_t launch_t(const Params& P, const StepArgs& A, hipStream_t stream) {
-    const void* fn = P.gemv_mfma ? (const void*)mk_megakernel<B, HD, true> : (const void*)mk_megakernel<B, HD, false>;
+hipError_t launch_megakernel(const Params& P, const StepArgs& A, hipStream_t stream) {
+    const int kind = P.E > 0 ? 2 : P.gemv_mfma ? 1 : 0;
+    const void* fn = kind == 2 ? kernel_moe(P.B, P.hd) : kind == 1 ? kernel_mfma(P.B, P.hd) : kernel_valu(P.B, P.hd);
+    if (!fn) return hipErrorInvalidValue;
+    // dynamic LDS above the default is allowed per kernel once
+    static size_t configured[3][2][4] = {};
+    const int bi = P.B == 1 ? 0 : P.B == 2 ? 1 : P.B == 4 ? 2 : 3;
+    size_t& cfgd = configured[kind][P.hd == 128 ? 1 : 0][bi];
     const size_t lds = megakernel_lds_bytes(P);
-    static size_t configured[2] = {0, 0};  // per kernel (VALU, matrix cores)
-    size_t& cfgd = configured[P.gemv_mfma ? 1 : 0];
     if (cfgd < lds) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -1494,21 +36,6 @@ static hipError_t launch_t(const Params& P, const StepArgs& A, hipStream_t strea
     // grid is resident at once.  (A cooperative launch guarantees the same but
     // measured about 18 us more between consecutive steps.)
     return hipLaunchKernel(fn, dim3(P.n_cu), dim3(kThreads), args, lds, stream);
-}
-
-hipError_t launch_megakernel(const Params& P, const StepArgs& A, hipStream_t stream) {
-    if (P.hd == 64) {
-        if (P.B == 1) return launch_t<1, 64>(P, A, stream);
-        if (P.B == 2) return launch_t<2, 64>(P, A, stream);
-        if (P.B == 4) return launch_t<4, 64>(P, A, stream);
-        if (P.B == 8) return launch_t<8, 64>(P, A, stream);
-    } else if (P.hd == 128) {
-        if (P.B == 1) return launch_t<1, 128>(P, A, stream);
-        if (P.B == 2) return launch_t<2, 128>(P, A, stream);
-        if (P.B == 4) return launch_t<4, 128>(P, A, stream);
-        if (P.B == 8) return launch_t<8, 128>(P, A, stream);
-    }
-    return hipErrorInvalidValue;
 }
 
 bool megakernel_supports(int B, int hd) { return (B == 1 || B == 2 || B == 4 || B == 8) && (hd == 64 || hd == 128); }
