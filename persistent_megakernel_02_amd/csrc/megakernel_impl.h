@@ -1287,7 +1287,7 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                                    kComputeWaves, ss[b]);
                 } else {
                     const StageSeg sg[1] = {{P.h, xs, gain, d, (uint32_t)B, d, d, tag_in}};
-                    if (!stage_segs<kStagePassWords, B, 1>(sg, wave, kComputeWaves, spin, ss)) return;
+                    if (!stage_segs<stage_words<B>(), B, 1>(sg, wave, kComputeWaves, spin, ss)) return;
                 }
                 wave_total_n<B>(ss);
                 if (lane == 0) {
@@ -1395,7 +1395,7 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                                          tag_x};
                     if (ks > 0) {
                         const StageSeg sg[1] = {sx};
-                        if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kComputeWaves, spin, ss)) return;
+                        if (!stage_segs<stage_words_wide<B>(), 1, 1>(sg, wave, kComputeWaves, spin, ss)) return;
                     } else if (is_o && layer == 0) {
                         // the residual is the token embedding: no wait
 #pragma unroll
@@ -1403,11 +1403,11 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                             stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * P.d + in.begin,
                                        in.count, hres + b * in.count, nullptr, wave, kComputeWaves, ss[0]);
                         const StageSeg sg[1] = {sx};
-                        if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kComputeWaves, spin, ss)) return;
+                        if (!stage_segs<stage_words_wide<B>(), 1, 1>(sg, wave, kComputeWaves, spin, ss)) return;
                     } else {
                         const StageSeg sg[2] = {sx, {P.h + in.begin, hres, nullptr, in.count, (uint32_t)B,
                                                      (uint32_t)P.d, in.count, tag_res}};
-                        if (!stage_segs<kStagePassWordsWide, 1, 2>(sg, wave, kComputeWaves, spin, ss)) return;
+                        if (!stage_segs<stage_words_wide<B>(), 1, 2>(sg, wave, kComputeWaves, spin, ss)) return;
                     }
                     if (!barrier()) return;
                     if (tr && lane == 0 && ks == 0) tr[2] = (uint32_t)now_ticks();
