@@ -179,7 +179,8 @@ const char* mk_last_error(const mk_handle* h);
  * (1 KB each), [3] max instructions on one CU, [4] weight bytes per step,
  * [5] verifier result (0 = ok), [6] attention splits, [7] phases, [8] LDS bytes of
  * staged activations, [9] LM-head instructions, [10] the GEMV kind in effect
- * (MK_GEMV_VALU or MK_GEMV_MFMA). */
+ * (MK_GEMV_VALU or MK_GEMV_MFMA), [11] q-head groups per attention item (1, or
+ * the q heads per KV head when one position split leaves compute units idle). */
 mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* rt, int32_t num_cus, int64_t* out,
                           int32_t cap);
 

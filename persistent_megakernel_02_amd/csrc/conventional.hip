@@ -258,7 +258,7 @@ __global__ void __launch_bounds__(kConvThreads) k_attn(Params P, StepArgs A, int
     BlockBarrier barrier;
     Spin spin(&P, nullptr);
     auto mark = [](int) {};
-    attn_item<HD>(P, A.tag0, layer, b, g, s, p, kv, need, release, barrier, xs, wave, kConvWaves, spin, mark);
+    attn_item<HD>(P, A.tag0, layer, b, g, s, 0, P.G, p, kv, need, release, barrier, xs, wave, kConvWaves, spin, mark);
 }
 
 // ------------------------------------------------------------------------------------------------

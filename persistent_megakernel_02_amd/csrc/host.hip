@@ -48,6 +48,7 @@ struct Plan {
     int n_cu = 0, nsplit = 1;
     int phases = 0;
     size_t max_per_cu = 0;
+    int hsplit = 1;
 };
 
 uint32_t ring_chunks_for(size_t x_bytes) {
@@ -134,6 +135,15 @@ int auto_splits(const mk_model_config* c, const mk_runtime_config* rt, int n_cu)
     return std::max(1, std::min(std::min(by_cu, by_len), std::min(kMaxSplits, max_splits_lds(c, rt))));
 }
 
+// q-head groups per attention item: with one position split and no more items
+// than compute units, every q head of a KV head becomes an item of its own (the
+// K/V of the group is streamed once per item; the append is done by head 0's).
+int auto_hsplit(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, int nsplit) {
+    const int G = c->n_q_heads / c->n_kv_heads;
+    if (rt->mode != MK_MODE_MEGAKERNEL || nsplit != 1 || G < 1) return 1;
+    return (int64_t)rt->max_batch * c->n_kv_heads * G <= n_cu ? G : 1;
+}
+
 mk_status validate(const mk_model_config* c, const mk_runtime_config* rt, std::string* why) {
     auto fail = [&](mk_status s, const char* m) {
         if (why) *why = m;
@@ -199,6 +209,7 @@ Plan build_plan(const mk_model_config* c, const mk_runtime_config* rt, int n_cu)
     Plan pl;
     pl.n_cu = n_cu;
     pl.nsplit = auto_splits(c, rt, n_cu);
+    pl.hsplit = auto_hsplit(c, rt, n_cu, pl.nsplit);
     const int L = c->n_layers, B = rt->max_batch;
     const uint32_t qkv_rows = (uint32_t)((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim);
     std::vector<std::vector<Instr>> q(n_cu);
@@ -226,7 +237,7 @@ Plan build_plan(const mk_model_config* c, const mk_runtime_config* rt, int n_cu)
     const uint32_t all = 0xFFFFFFFFu;
     for (int l = 0; l < L; ++l) {
         gemv_phase(OP_QKV, l, qkv_rows, all);
-        const uint32_t items = (uint32_t)(B * c->n_kv_heads * pl.nsplit);
+        const uint32_t items = (uint32_t)(B * c->n_kv_heads * pl.nsplit * pl.hsplit);
         for (uint32_t it = 0; it < items; ++it) q[it % n_cu].push_back(mk_instr(OP_ATTN, l, it, 1));
         ++pl.phases;
         gemv_phase(OP_O, l, (uint32_t)c->hidden, kMaxResidRows);
@@ -274,7 +285,7 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
         if (ph == L * kSub) return (uint32_t)c->vocab;
         switch (ph % kSub) {
             case 0: return qkv_rows;
-            case 1: return (uint32_t)(B * c->n_kv_heads * pl.nsplit);
+            case 1: return (uint32_t)(B * c->n_kv_heads * pl.nsplit * pl.hsplit);
             case 2: return (uint32_t)c->hidden;
             case 3: return moe ? (uint32_t)c->n_experts : 0u;
             case 4: return moe ? (uint32_t)c->expert_ffn : (uint32_t)c->ffn;
@@ -325,7 +336,7 @@ inline size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 // Instruction counts of a plan on n compute units (total and the longest queue).
 void plan_counts(const mk_model_config* c, const mk_runtime_config* rt, int n, int nsplit, size_t* total,
                  size_t* per_cu) {
-    const size_t items = (size_t)rt->max_batch * c->n_kv_heads * nsplit;
+    const size_t items = (size_t)rt->max_batch * c->n_kv_heads * nsplit * auto_hsplit(c, rt, n, nsplit);
     const size_t d_rows = ((size_t)c->hidden + n - 1) / n;
     const size_t od = (d_rows + kMaxResidRows - 1) / kMaxResidRows;  // O / DOWN instructions per CU
     const size_t route = c->n_experts ? 1 : 0;  // at most one router instruction per CU and layer
@@ -470,10 +481,10 @@ mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* r
                               : 3 * (int64_t)cfg->ffn * d;
     const int64_t per_layer = (cfg->n_q_heads + 2 * cfg->n_kv_heads) * hd * d + d * cfg->n_q_heads * hd + ffn_w + 2 * d;
     const size_t xb = x_bytes_for(cfg, rt, pl.nsplit);
-    int64_t vals[11] = {num_cus, (int64_t)pl.instrs.size(), (int64_t)ring_chunks_for(xb), (int64_t)pl.max_per_cu,
+    int64_t vals[12] = {num_cus, (int64_t)pl.instrs.size(), (int64_t)ring_chunks_for(xb), (int64_t)pl.max_per_cu,
                         2 * (cfg->n_layers * per_layer + (int64_t)cfg->vocab * d + d), verify_plan(cfg, rt, pl),
-                        pl.nsplit, pl.phases, (int64_t)xb, (int64_t)pl.n_head, use_mfma(cfg, rt) ? 2 : 1};
-    for (int i = 0; i < cap && i < 11; ++i) out[i] = vals[i];
+                        pl.nsplit, pl.phases, (int64_t)xb, (int64_t)pl.n_head, use_mfma(cfg, rt) ? 2 : 1, pl.hsplit};
+    for (int i = 0; i < cap && i < 12; ++i) out[i] = vals[i];
     return MK_OK;
 }
 
@@ -558,6 +569,7 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
     P.G = cfg->n_q_heads / cfg->n_kv_heads;
     P.qkv_rows = (cfg->n_q_heads + 2 * cfg->n_kv_heads) * cfg->head_dim;
     P.nsplit = h->plan.nsplit;
+    P.hsplit = h->plan.hsplit;
     P.n_cu = n_cu;
     P.kv_b = rt->max_batch;
     P.eps = cfg->rms_eps;

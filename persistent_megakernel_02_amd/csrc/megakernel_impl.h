@@ -95,9 +95,8 @@ __device__ __forceinline__ uint32_t instr_bytes(const Params& P, const Instr& in
         case OP_GATEUP: return align_chunk(2u * in.count * (uint32_t)P.d * 2u);
         case OP_DOWN: return align_chunk(in.count * (uint32_t)P.F * 2u);
         case OP_ATTN: {
-            const int per_b = P.Hkv * P.nsplit;
-            const int b = (int)in.begin / per_b, s = (int)in.begin % P.nsplit;
-            const SplitRange R = split_range<HD>(ctx_of(ctx, b), s, P.nsplit);
+            const AttnItem it = attn_item_of(P, in.begin);
+            const SplitRange R = split_range<HD>(ctx_of(ctx, it.b), it.s, P.nsplit);
             return (1u + (uint32_t)R.ngroups * 2u) * kChunk;  // RoPE row of position p, then the K/V groups
         }
         default: return 0;
@@ -150,8 +149,8 @@ __device__ __forceinline__ const char* chunk_src(const Params& P, const Instr& i
         }
         case OP_ATTN: {
             constexpr uint32_t rbkv = HD * 2u;
-            const int per_b = P.Hkv * P.nsplit;
-            const int b = (int)in.begin / per_b, g = ((int)in.begin % per_b) / P.nsplit, s = (int)in.begin % P.nsplit;
+            const AttnItem it = attn_item_of(P, in.begin);
+            const int b = it.b, g = it.g, s = it.s;
             const int p = ctx_of(ctx, b);
             if (c == 0) {  // (cos, sin) row of position p: HD / 2 float2, lanes past it re-read its start
                 const uint32_t lo = (uint32_t)lane_id() * 16u;
@@ -292,8 +291,8 @@ __device__ __forceinline__ bool setup_stream(const Params& P, const Instr& in, c
             return true;
         }
         case OP_ATTN: {
-            const int per_b = P.Hkv * P.nsplit;
-            const int b = (int)in.begin / per_b, g = ((int)in.begin % per_b) / P.nsplit, s = (int)in.begin % P.nsplit;
+            const AttnItem it = attn_item_of(P, in.begin);
+            const int b = it.b, g = it.g, s = it.s;
             const int p = ctx_of(ctx, b);
             const SplitRange Rg = split_range<HD>(p, s, P.nsplit);
             const size_t base = ((((size_t)in.layer * P.kv_b + b) * P.Hkv + g) * P.S + Rg.s0) * HD;
@@ -1216,8 +1215,8 @@ __device__ __forceinline__ bool attn_instr(const Params& P, const StepArgs& A, C
                                            int wave, const Instr& in, uint32_t S, Spin& spin, CwBarrier& barrier,
                                            uint32_t& land_wait, uint32_t* tr, const int32_t* ctx) {
     const int lane = lane_id();
-    const int per_b = P.Hkv * P.nsplit;
-    const int b = (int)in.begin / per_b, g = ((int)in.begin % per_b) / P.nsplit, s = (int)in.begin % P.nsplit;
+    const AttnItem it = attn_item_of(P, in.begin);
+    const int b = it.b, g = it.g, s = it.s;
     // stream: [RoPE row 1 KB][group 0: K 1 KB, V 1 KB][group 1] ...
     const RingKV<HD> kv{ring, S + kChunk, P.ring_chunks};
     auto need = [&](int t) -> bool {  // group t resident (K and V chunks); t = -1: the RoPE row
@@ -1230,7 +1229,7 @@ __device__ __forceinline__ bool attn_instr(const Params& P, const StepArgs& A, C
     auto mark = [&](int m) {
         if (tr && lane == 0) tr[9 + m] = (uint32_t)now_ticks();
     };
-    return attn_item<HD>(P, A.tag0, in.layer, b, g, s, ctx_of(ctx, b), kv, need, release, barrier, xs, wave,
+    return attn_item<HD>(P, A.tag0, in.layer, b, g, s, it.h0, it.gh, ctx_of(ctx, b), kv, need, release, barrier, xs, wave,
                          kComputeWaves, spin, mark);
 }
 

@@ -667,6 +667,22 @@ __device__ __forceinline__ bool head_better(float v, int32_t i, float bv, int32_
 // with DPP.  Value pass: lane -> dims lane * DPL .. + DPL - 1, one position at a
 // time, so no reduction across lanes is needed.
 // ---------------------------------------------------------------------------------------------
+// Attention item id -> (sequence b, KV head g, split s, q heads h0 .. h0 + gh - 1):
+// item = ((b * Hkv + g) * nsplit + s) * hsplit + q-head group.
+struct AttnItem {
+    int b, g, s, h0, gh;
+};
+__device__ __forceinline__ AttnItem attn_item_of(const Params& P, uint32_t item) {
+    const int hs = (int)item % P.hsplit, it = (int)item / P.hsplit, per_b = P.Hkv * P.nsplit;
+    AttnItem r;
+    r.b = it / per_b;
+    r.g = (it % per_b) / P.nsplit;
+    r.s = it % P.nsplit;
+    r.gh = P.G / P.hsplit;
+    r.h0 = hs * r.gh;
+    return r;
+}
+
 template <int HD>
 struct AttnGeom {
     static constexpr int LPP = HD / 8;    // lanes per position (score pass)
@@ -878,7 +894,7 @@ static_assert(kAttnBlockGroups % kComputeWaves == 0, "groups of a block are deal
 // when split, the item's (max, sum, output) partial; the last split to arrive
 // merges all partials in split order.
 template <int HD, class KV, class Need, class Release, class Barrier, class Mark>
-__device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int layer, int b, int g, int s, int p,
+__device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int layer, int b, int g, int s, int h0, int gh, int p,
                                           const KV& kv, Need& need, Release& release, Barrier& barrier, float* xs,
                                           int wave, int nw, Spin& spin, Mark& mark) {
     using Geo = AttnGeom<HD>;
@@ -888,7 +904,7 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
     const int lane = lane_id();
     const int ps = lane / LPP;
     const int dl = 8 * (lane % LPP);
-    const int G = P.G;
+    const int G = gh;  // q heads h0 .. h0 + gh - 1 of the KV head's P.G
     const SplitRange R = split_range<HD>(p, s, P.nsplit);
     const float scale = P.attn_scale;
     const uint32_t tag_in = phase_tag(tag0, layer, 0) ^ ((P.inject && layer == 0) ? 0x80000000u : 0u);
@@ -913,7 +929,7 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
     {
         const uint64_t* row = P.qkv + (size_t)b * P.qkv_rows;
         float ss[1] = {0.f};
-        const StageSeg sg[3] = {{row + (size_t)g * G * HD, q_raw, nullptr, (uint32_t)(G * HD), 1u, 0u, 0u, tag_in},
+        const StageSeg sg[3] = {{row + (size_t)(g * P.G + h0) * HD, q_raw, nullptr, (uint32_t)(G * HD), 1u, 0u, 0u, tag_in},
                                 {row + (size_t)(P.Hq + g) * HD, k_raw, nullptr, (uint32_t)HD, 1u, 0u, 0u, tag_in},
                                 {row + (size_t)(P.Hq + P.Hkv + g) * HD, v_raw, nullptr, (uint32_t)HD, 1u, 0u, 0u, tag_in}};
         if (!stage_segs<kStagePassWords, 1, 3>(sg, wave, nw, spin, ss)) return false;
@@ -941,7 +957,7 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
             kw |= kb16 << (16 * j);
             vw |= vb16 << (16 * j);
         }
-        if (R.has_new) {  // KV append at position p (read by later steps)
+        if (R.has_new && h0 == 0) {  // KV append at position p (read by later steps), once per KV head
             const size_t row = ((((size_t)layer * P.kv_b + b) * P.Hkv + g) * P.S + p) * HD + lane * DPL;
             if constexpr (DPL == 1) {
                 P.kcache[row] = (uint16_t)kw;
@@ -1138,7 +1154,7 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
     if (P.nsplit == 1) {
         if (j < G) {
             const float inv = 1.0f / ll;
-            uint64_t* o = out_b + (size_t)(g * G + j) * HD + lane * DPL;
+            uint64_t* o = out_b + (size_t)(g * P.G + h0 + j) * HD + lane * DPL;
 #pragma unroll
             for (int e = 0; e < DPL; ++e) st_tagged(o + e, aa[e] * inv, tag_out);
         }
@@ -1190,7 +1206,7 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
             lse_merge(m2, l2, a2, src[0], src[1], a3);
         }
         const float inv = 1.0f / l2;
-        uint64_t* o = out_b + (size_t)(g * G + j) * HD + lane * DPL;
+        uint64_t* o = out_b + (size_t)(g * P.G + h0 + j) * HD + lane * DPL;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) st_tagged(o + e, a2[e] * inv, tag_out);
     }

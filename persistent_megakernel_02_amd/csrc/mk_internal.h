@@ -152,6 +152,7 @@ struct Params {
     // shape
     int32_t L, d, Hq, Hkv, hd, F, V, B, S, G;  // G = Hq / Hkv
     int32_t qkv_rows, nsplit, n_cu, kv_b;      // kv_b = max_batch of the cache layout
+    int32_t hsplit;                            // attention items per (sequence, KV head, split): q-head groups
     int32_t down_slices;                       // DOWN runs over F in this many column slices (power of 2)
     int32_t gemv_mfma;                         // 1: GEMVs on the matrix cores (tile-major weight chunks)
     int32_t E, top_k, n_shared, Fe;            // MoE: experts, selected per token, shared experts, expert width

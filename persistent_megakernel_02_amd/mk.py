@@ -136,7 +136,7 @@ def mk_query_sizes(cfg: mk_model_config, rt: mk_runtime_config):
 
 def mk_plan_inspect(cfg: mk_model_config, rt: mk_runtime_config, num_cus: int):
     keys = ["cus", "instructions", "ring_chunks", "max_per_cu", "weight_bytes", "verify", "attn_splits", "phases",
-            "x_bytes", "head_instructions", "gemv_kind"]
+            "x_bytes", "head_instructions", "gemv_kind", "attn_hsplit"]
     out = (ctypes.c_int64 * len(keys))()
     st = lib().mk_plan_inspect(ctypes.byref(cfg), ctypes.byref(rt), num_cus, out, len(keys))
     return st, dict(zip(keys, list(out)))

@@ -103,7 +103,10 @@ def test_schedule_verifies(cfg, cus, batch):
     assert info["weight_bytes"] == cfg.weight_bytes()
     assert info["x_bytes"] >= staged_bytes(cfg, batch)
     assert info["ring_chunks"] == (LDS_BYTES - LDS_STATIC - info["x_bytes"]) // CHUNK >= MIN_RING
-    items = batch * cfg.n_kv_heads * info["attn_splits"]
+    items = batch * cfg.n_kv_heads * info["attn_splits"] * info["attn_hsplit"]
+    G = cfg.n_q_heads // cfg.n_kv_heads
+    # one item per q head when a single position split leaves CUs idle
+    assert info["attn_hsplit"] == (G if info["attn_splits"] == 1 and batch * cfg.n_kv_heads * G <= cus else 1)
     od = -(-(-(-cfg.hidden // cus)) // 64)  # O / DOWN instructions per CU (<= 64 rows each)
     assert info["instructions"] <= cfg.n_layers * (2 * cus + items + 2 * od * cus) + cus
     assert info["head_instructions"] == min(cus, cfg.vocab)
@@ -112,8 +115,10 @@ def test_schedule_verifies(cfg, cus, batch):
 def test_schedule_one_tile_per_cu_per_matrix():
     st, info = mk.mk_plan_inspect(mk.model_config(I.LLAMA_1B), rt(1, 161), 256)
     assert st == mk.MK_OK
-    # 16 layers x (QKV, O, gate/up, down) one tile on each CU, attention items, LM head
-    items = 8 * info["attn_splits"]
+    # 16 layers x (QKV, O, gate/up, down) one tile on each CU, attention items (one
+    # per q head: 32), LM head
+    assert info["attn_splits"] == 1 and info["attn_hsplit"] == 4
+    items = 8 * info["attn_splits"] * info["attn_hsplit"]
     assert info["instructions"] == 16 * (4 * 256 + items) + 256
     assert info["max_per_cu"] == 16 * 5 + 1
 
