@@ -237,6 +237,27 @@ __device__ __forceinline__ void store_parts(char* area, uint32_t k, uint32_t b, 
     }
 }
 
+// store_parts for a pair of lanes (2 l, 2 l + 1) holding elements k, k + 1 of one
+// batch row (staging hands consecutive elements to consecutive lanes, and a parts
+// segment has an even number of elements per row): each part is converted with
+// the hardware round-to-nearest-even, the odd lane's value moves over with a DPP
+// row shift and the even lane stores both as one 32-bit word.  Both lanes of a
+// pair must be active.
+__device__ __forceinline__ void store_parts_pair(char* area, uint32_t k, uint32_t b, uint32_t pitch, uint32_t prt,
+                                                 float v) {
+    const bool even = (lane_id() & 1) == 0;
+    float rem = v;
+#pragma unroll
+    for (uint32_t p = 0; p < 3u; ++p) {
+        if (p < prt) {
+            const uint32_t h = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)rem);
+            rem = rem - __uint_as_float(h << 16);
+            const uint32_t hn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, 0x101, 0xF, 0xF, false);  // row_shl:1
+            if (even) *(uint32_t*)(area + part_offset(k, prt * b + p, pitch)) = h | (hn << 16);
+        }
+    }
+}
+
 // Operand B of k-block kb for this lane (zeros past the PB used columns).
 __device__ __forceinline__ bf16x8_t load_parts(const char* area, uint32_t kb, uint32_t PB, uint32_t pitch) {
     const uint32_t l = (uint32_t)lane_id(), j = l & 15u, kg = l >> 4;
@@ -494,8 +515,7 @@ __device__ __forceinline__ bool stage_segs(const StageSeg (&sg)[NS], int w, int 
                         if (rr == (int)L.row) ss[rr] = fmaf(x, x, ss[rr]);
                     y = x * bf_to_f((uint16_t)gv[k]);
                 }
-                if (L.parts == 3u) store_parts<3>((char*)L.dst, L.idx, L.row, L.pitch, y);
-                else if (L.parts == 2u) store_parts<2>((char*)L.dst, L.idx, L.row, L.pitch, y);
+                if (L.parts) store_parts_pair((char*)L.dst, L.idx, L.row, L.pitch, L.parts, y);
                 else *L.dst = y;
             }
         }
