@@ -237,6 +237,39 @@ def test_llama1b_b2_long_context():
     d.close()
 
 
+@pytest.mark.parametrize("mode", [0, 1], ids=["megakernel", "graph"])
+def test_ragged_contexts(mode):
+    """Four sequences at very different positions (0, 5, 300, 1100 cached
+    positions) with position splits sized for the longest: short sequences leave
+    whole splits empty, and one sequence starts from an empty cache."""
+    cfg = I.TINY
+    B, S, steps = 4, 1200, 3
+    lens = [0, 5, 300, 1100]
+    w = I.make_weights(cfg, seed=15)
+    start = I.make_prompt(cfg, B, 1, seed=15)[:, 0]
+    orc = O.Oracle(cfg, w, B, S)
+    d = _decoder(cfg, w, B, S, mode)
+    torch = _torch()
+    _fill_context(cfg, orc, d, max(lens), seed=15)
+    orc.pos[:] = lens  # each sequence sees only its own first lens[b] positions
+    d.set_context_len(lens)
+    print(f"case ragged contexts {lens} mode={mode}", flush=True)
+    ref_t, ref_l, got_t, got_l = [], [], [], []
+    tok = start.astype(np.int32)
+    for _ in range(steps):
+        nxt, logits = orc.step(tok)
+        g_n, g_l = d.decode_step(torch.from_numpy(tok).to(d.device))
+        ref_t.append(nxt.copy())
+        ref_l.append(logits.copy())
+        got_t.append(g_n.cpu().numpy().copy())
+        got_l.append(g_l.cpu().numpy().copy())
+        tok = nxt.astype(np.int32)
+    _, near = compare(ref_t, ref_l, got_t, got_l, f"ragged contexts mode={mode}")
+    assert near == 0
+    assert d.context_len() == [n + steps for n in lens]
+    d.close()
+
+
 def test_llama8b_b1_prefix():
     """The 8B shape (32 layers, hidden 4096, head_dim 128, untied head) at batch
     1: 6 prompt tokens and 4 greedy steps against the oracle."""
