@@ -3,9 +3,9 @@
  *
  * One call of mk_decode_step runs one whole low-batch decode step of a
  * Llama-style decoder - embedding lookup; per layer RMSNorm, QKV projection with
- * RoPE, GQA attention over the KV cache, O-projection with residual, SwiGLU MLP;
- * final norm, LM head and greedy argmax - as ONE persistent kernel launch with
- * no kernel boundaries.
+ * RoPE, GQA attention over the KV cache, O-projection with residual, SwiGLU MLP
+ * or routed mixture of experts; final norm, LM head and greedy argmax - as ONE
+ * persistent kernel launch with no kernel boundaries.
  *
  * Sources (no API is printed on them; they fix the behaviour):
  *  [MK]  page "斯坦福团队新作让Llama1B实现毫秒级推理获Karpathy盛赞" (m.youleyou.com),
@@ -24,6 +24,9 @@
  *        is opt-in and falls back to the normal path at high concurrency; the
  *        headline workload is Llama-3.2-1B, batch 1, 32 prompt tokens, 128
  *        greedy tokens.
+ *  [MOE] same page, sections "两千四百次启停" and "AMD 先落了一子": decoders
+ *        whose layers are mostly mixture-of-experts, with the expert layers
+ *        (batch 4 and 8) fused into the resident kernel like the rest.
  *
  * Conventions
  *  - Every device pointer is CALLER-OWNED and borrowed until mk_destroy: weights,
@@ -76,8 +79,14 @@ typedef enum {
  * where the parts area leaves too small a weight ring, is MK_E_UNSUPPORTED. */
 typedef enum { MK_GEMV_AUTO = 0, MK_GEMV_VALU = 1, MK_GEMV_MFMA = 2 } mk_gemv_kind;
 
-/* Model shape.  n_experts == 0 selects the dense SwiGLU FFN (ffn = its width);
- * MoE decoders are not supported by this version (MK_E_UNSUPPORTED). */
+/* Model shape.  n_experts == 0 selects the dense SwiGLU FFN (ffn = its width).
+ * n_experts > 0 selects a routed mixture of experts [MOE]: router logits, softmax
+ * (in double, rounded to fp32), the top_k experts per sequence (ties to the lower
+ * index), each a SwiGLU of width expert_ffn, plus n_shared_experts (0 or 1) with
+ * weight 1; the expert outputs are added weighted by their probabilities in
+ * ascending expert order.  MoE limits: n_experts <= 64, top_k <= 8, expert_ffn and
+ * hidden multiples of 512 (hidden / 512 a power of two), the persistent mode and
+ * the VALU GEMV only; otherwise MK_E_UNSUPPORTED. */
 typedef struct {
     int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
     int32_t tied_embeddings; /* 1: the LM head is the token embedding */
@@ -87,12 +96,14 @@ typedef struct {
 } mk_model_config;
 
 /* Device pointers of one layer (bf16).  wq [Hq*hd, d], wk/wv [Hkv*hd, d],
- * wo [d, Hq*hd], w_gate/w_up [ffn, d], w_down [d, ffn], norms [d]. */
+ * wo [d, Hq*hd], w_gate/w_up [ffn, d], w_down [d, ffn], norms [d].  A dense model
+ * leaves the MoE fields NULL; an MoE model leaves w_gate/w_up/w_down NULL. */
 typedef struct {
     const void *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *w_gate, *w_up, *w_down;
-    const void* router;
-    const void *const *e_gate, *const *e_up, *const *e_down;
-    const void *s_gate, *s_up, *s_down;
+    const void* router;                                     /* MoE [n_experts, d] */
+    const void *const *e_gate, *const *e_up, *const *e_down; /* MoE: HOST arrays [n_experts] of device
+                                                                pointers ([Fe, d], [Fe, d], [d, Fe]) */
+    const void *s_gate, *s_up, *s_down;                     /* MoE shared expert (if any) */
 } mk_layer_weights;
 
 typedef struct {
