@@ -31,12 +31,13 @@ constexpr uint32_t kCtrStride = 32;                 // uint32 per counter (128 B
 constexpr int kStageWords = 16;                     // tagged words per lane in flight (argmax reduce)
 constexpr int kStagePassWords = 4;                  // tagged words per lane per staging pass (two in flight)
 constexpr int kStagePassWordsWide = 8;              // the same for the wide inputs of O and DOWN
-// The persistent kernel's dense VALU path at batch 1 has the registers for twice
-// the words per pass of the RMSNorm inputs (a 2048-wide input then takes one pass
-// per lane); wider passes of the O / DOWN inputs would spill.  The per-lane
+// The persistent kernel's dense VALU path up to batch 4 has the registers for
+// twice the words per pass of the RMSNorm inputs (a 2048-wide input at batch 1 then
+// takes one pass per lane); batch 8, and wider passes of the O / DOWN inputs, would
+// spill.  The per-lane
 // element order does not depend on the pass width, so the sums of squares are the
 // same bits either way.
-template <int B> constexpr int stage_words() { return B == 1 ? 2 * kStagePassWords : kStagePassWords; }
+template <int B> constexpr int stage_words() { return B <= 4 ? 2 * kStagePassWords : kStagePassWords; }
 template <int B> constexpr int stage_words_wide() { return kStagePassWordsWide; }
 constexpr int kAttnBlockGroups = 32;                // KV position groups (2 KB each) one attention pass holds
 static_assert(kMinRingChunks >= 2 * kAttnBlockGroups + 1, "an attention block and its RoPE chunk fit the ring");
