@@ -1096,7 +1096,7 @@ __device__ __forceinline__ bool moe_egu(const Params& P, const StepArgs& A, Ctl*
     for (int b = 0; b < B; ++b) ss[b] = 0.f;
     const StageSeg sg[2] = {{P.h, xs, Lw.mlp_norm, d, (uint32_t)B, d, d, tag_o, 0u},
                             {P.route, zeta, nullptr, E, (uint32_t)B, E, E, tag_o, 0u}};
-    if (!stage_segs<kStagePassWords, B, 2>(sg, wave, kComputeWaves, spin, ss)) return false;
+    if (!stage_segs<stage_words<B>(), B, 2>(sg, wave, kComputeWaves, spin, ss)) return false;
     wave_total_n<B>(ss);
     if (lane == 0) {
 #pragma unroll
