@@ -900,16 +900,17 @@ __device__ __forceinline__ float wave_maxf(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-static_assert(kAttnBlockGroups % kComputeWaves == 0, "groups of a block are dealt evenly to the waves");
+static_assert(kAttnBlockGroups % (2 * kComputeWaves) == 0, "groups of a block (full or half) are dealt evenly to the waves");
 
 // Runs one attention item (sequence b, KV head g, split s) with the nw == 4 compute
 // waves of the workgroup, which all call it.
 //  1. stage the raw q (G heads), k and v of the position (tagged words);
 //  2. wave h rotates q head h, wave 0 also k; the new K (rotated) and V are
 //     rounded to bf16, appended to the cache and kept in LDS;
-//  3. block by block (kAttnBlockGroups groups), wave w scores groups t0 + w,
-//     t0 + w + 4, ... for every head, exponentiates against its running maximum
-//     and accumulates the weighted V (the new position is one extra group);
+//  3. block by block (kAttnBlockGroups groups, half that when the split is
+//     longer), wave w scores groups t0 + w, t0 + w + 4, ... for every head as
+//     they land, exponentiates against its running maximum and accumulates the
+//     weighted V (the new position is one extra group);
 //  4. the four wave partials of head h are merged by wave h, in wave order.
 // `need(t)` waits for ring group t; `release(t)` frees ring groups before t;
 // `barrier()` synchronises the waves.  Writes the attention output (tagged) or,
@@ -1015,26 +1016,34 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     }
-    for (int t0 = 0; t0 < ngr; t0 += kAttnBlockGroups) {
-        const int t1 = min(ngr, t0 + kAttnBlockGroups);
+    // A split of at most kAttnBlockGroups groups is one block (one rescale); a
+    // longer one goes in half-size blocks, so the ring holds the next block
+    // streaming in while the waves work on the current one.
+    const int bg = ngr <= kAttnBlockGroups ? kAttnBlockGroups : kAttnBlockGroups / 2;
+    for (int t0 = 0; t0 < ngr; t0 += bg) {
+        const int t1 = min(ngr, t0 + bg);
         const auto blk = kv.block(t0);
-        // every ring group of the block resident (one wait per block)
-        if (t0 < R.ngroups && !need(min(t1, R.ngroups) - 1)) return false;
         // this wave's groups of the block: t0 + wave + 4 i, i < ngw
         const int first = t0 + wave;
         const int ngw = first < t1 ? (t1 - first + kComputeWaves - 1) / kComputeWaves : 0;
-        // scores of every head, two groups per step.  Loads are issued for every
-        // step, from a clamped group when the step is past the wave's groups or is
-        // the new position, and the values selected afterwards.
+        const int own_last = first + kComputeWaves * (ngw - 1);
+        // scores of every head, two groups per step.  Each step first waits for its
+        // own ring groups only: the loader fills a block in stream order, so a wave
+        // starts on the groups that have landed while the rest arrive.  Loads are
+        // issued for every step, from the wave's last group when the step is past
+        // its groups (so they read resident data) or from the new position's slot,
+        // and the values selected afterwards.
         float mx[kMaxGroup];
 #pragma unroll
         for (int h = 0; h < kMaxGroup; ++h) mx[h] = -INFINITY;
         for (int i = 0; i < ngw; i += 2) {
+            const int tl = min(first + kComputeWaves * min(i + 1, ngw - 1), R.ngroups - 1);
+            if (tl >= t0 && !need(tl)) return false;
             uint4 kp[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int tt = first + kComputeWaves * (i + u);
-                const uint4 kr = blk.k(min(tt, t1 - 1) - t0);
+                const uint4 kr = blk.k(min(tt, own_last) - t0);
                 kp[u] = (tt < R.ngroups) ? kr : kn;
             }
 #pragma unroll
@@ -1095,7 +1104,7 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int tt = first + kComputeWaves * (i + u);
-                const uint4 vr = blk.vp(min(tt, t1 - 1) - t0);
+                const uint4 vr = blk.vp(min(tt, own_last) - t0);
                 const float4 w = *(const float4*)(sc + (min(i + u, ngw - 1) * PPW + ps) * kMaxGroup);
                 vp[u] = (tt < R.ngroups) ? vr : vn;
                 w4[u] = (i + u < ngw) ? w : make_float4(0.f, 0.f, 0.f, 0.f);

@@ -23,7 +23,7 @@ constexpr uint32_t kChunk = 1024;                   // one loader issue: 64 lane
 constexpr uint32_t kLdsBytes = 160 * 1024;          // LDS of one gfx950 compute unit
 constexpr uint32_t kStaticLds = 1024;               // reserved for the control block
 constexpr uint32_t kMinRingChunks = 72;             // >= one attention block (2 x 32 KV chunks) + its RoPE chunk
-constexpr int kLoaderLag = 8;                       // chunks in flight per loader wave (vmcnt <= 63)
+constexpr int kLoaderLag = 4;                       // chunks in flight per loader wave (deeper queues slow the polls)
 constexpr int kMaxBatch = 8;
 constexpr int kMaxGroup = 4;                        // q heads per KV head
 constexpr uint32_t kMaxResidRows = 64;              // O / DOWN rows per instruction
