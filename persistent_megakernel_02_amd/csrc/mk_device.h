@@ -633,11 +633,10 @@ __device__ __forceinline__ void rows_dot(const Rows& rows, int np, const X& x, f
 }
 
 // Rows of one compute wave's batch for a row of `rb` bytes: about 8 KB per wave.
-// At batch 4 two rows share each x piece read from LDS (one row per batch left the
-// wave waiting on LDS reads of x); at batch 8 one row keeps the accumulators and x
-// pieces in registers.
+// From batch 4 on two rows share each x piece read from LDS (one row per batch
+// left the wave waiting on LDS reads of x).
 __host__ __device__ constexpr int rows_per_batch(uint32_t rb, int B = 1) {
-    return B >= 8 ? 1 : B == 4 ? 2 : rb <= 2048u ? 4 : rb <= 4096u ? 2 : 1;
+    return B >= 4 ? 2 : rb <= 2048u ? 4 : rb <= 4096u ? 2 : 1;
 }
 
 // a[i] for a per-lane i < B.  The empty asm between the selects keeps the chain
