@@ -703,11 +703,64 @@ __device__ __forceinline__ bool gemv_ring(const Params& P, Ctl* ctl, const char*
     return true;
 }
 
+// Long rows at small batches stream through the ring in segments: a wave waits
+// for kSegBytes of its row, accumulates them and frees them, so the four waves
+// hold four segments rather than four whole rows (at 8 to 28 KB a row, most of
+// the ring) and start on a row's first segment while the loader streams the rest.
+// Each lane still accumulates its pieces in ascending order, so every row's value
+// is the one rows_dot gives.  R = 2 (GATEUP): the wave takes the gate row, then
+// the up row of its pair.
+constexpr uint32_t kSegBytes = 4096;
+constexpr uint32_t kSegRowBytes = 8192;  // rows at least this long, at batch 1 and 2
+template <int B, int R, class Epi>
+__device__ __forceinline__ bool gemv_ring_seg(const Params& P, Ctl* ctl, const char* ring, uint32_t S, uint32_t rb,
+                                              uint32_t nrows, const XLds& x, int wave, uint32_t& lw, Epi& epi) {
+    const uint32_t ring_bytes = P.ring_chunks * kChunk;
+    const uint32_t np = rb >> 4, lane = (uint32_t)lane_id();
+    constexpr uint32_t SP = kSegBytes / 16u;  // pieces per segment (a multiple of 64)
+    for (uint32_t r0 = (uint32_t)wave * R; r0 < nrows; r0 += (uint32_t)R * kComputeWaves) {
+        float res[R][B];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const uint32_t off = S + (r0 + (uint32_t)i) * rb;
+            const RingBatch row{ring, ring_addr(off, P.ring_chunks), rb, ring_bytes};
+            float acc[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[b] = 0.f;
+            for (uint32_t s0 = 0; s0 < np; s0 += SP) {
+                const uint32_t s1 = min(np, s0 + SP);
+                set_consumed(ctl, wave, (off + s0 * 16u) / kChunk);
+                if (!wait_landed(P, ctl, (off + s1 * 16u + kChunk - 1u) / kChunk, lw)) return false;
+#pragma unroll 2
+                for (uint32_t p = s0 + lane; p < s1; p += 64u) {
+                    const uint4 w = row.piece(0u, p);
+                    float4 xa[B], xb[B];
+#pragma unroll
+                    for (int b = 0; b < B; ++b) x.piece(b, p, xa[b], xb[b]);
+#pragma unroll
+                    for (int b = 0; b < B; ++b) acc[b] = dot8(w, xa[b], xb[b], acc[b]);
+                }
+            }
+            wave_total_n<B>(acc);
+#pragma unroll
+            for (int b = 0; b < B; ++b) res[i][b] = acc[b];
+        }
+        epi(r0, (uint32_t)R, res);
+    }
+    return true;
+}
+
 // Batch size by row length; GATEUP keeps a (gate, up) pair inside one batch.
 template <int B, class Epi>
 __device__ __forceinline__ bool gemv_ring_auto(const Params& P, Ctl* ctl, const char* ring, uint32_t S, uint32_t rb,
                                                uint32_t nrows, const XLds& x, int wave, uint32_t& lw, Epi& epi,
                                                bool pairs) {
+    if constexpr (B <= 2) {
+        if (rb >= kSegRowBytes) {
+            if (pairs) return gemv_ring_seg<B, 2>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
+            return gemv_ring_seg<B, 1>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
+        }
+    }
     const int R = rows_per_batch(rb, B);
     if (R >= 4) return gemv_ring<B, 4>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
     if (R == 2 || pairs) return gemv_ring<B, 2>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
