@@ -710,8 +710,8 @@ __device__ __forceinline__ bool gemv_ring(const Params& P, Ctl* ctl, const char*
 // Each lane still accumulates its pieces in ascending order, so every row's value
 // is the one rows_dot gives.  R = 2 (GATEUP): the wave takes the gate row, then
 // the up row of its pair.
-constexpr uint32_t kSegBytes = 4096;
-constexpr uint32_t kSegRowBytes = 8192;  // rows at least this long, at batch 1 and 2
+constexpr uint32_t kSegBytes = 8192;     // measured: 2 KB and 16 KB segments were slower, 4 KB too
+constexpr uint32_t kSegRowBytes = 8192;  // rows at least this long, at batch 1 and 2 (4 KB rows: slower)
 template <int B, int R, class Epi>
 __device__ __forceinline__ bool gemv_ring_seg(const Params& P, Ctl* ctl, const char* ring, uint32_t S, uint32_t rb,
                                               uint32_t nrows, const XLds& x, int wave, uint32_t& lw, Epi& epi) {
