@@ -358,9 +358,10 @@ __device__ __forceinline__ uint32_t landed_prefix(const Ctl* ctl) {
     return m;
 }
 
-template <int HD, bool MF, bool MOE>
+template <int B, int HD, bool MF, bool MOE>
 __device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* ring, int k, uint32_t q0, uint32_t q1,
                                             const int32_t* ctx) {
+    constexpr int LAG = loader_lag<B>();
     const uint32_t N = P.ring_chunks;
     const uint32_t NL = (uint32_t)kLoaderWaves;
     const uint32_t ring_base = (uint32_t)(size_t)(lds_ptr_t)ring;
@@ -413,7 +414,7 @@ __device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* rin
         if (P.trace) stall += (uint32_t)now_ticks() - ts;
         return ok;
     };
-    // after each issue: next own chunk and slot, and keep at most kLoaderLag in
+    // after each issue: next own chunk and slot, and keep at most LAG in
     // flight.  (Throttling the loaders while the compute waves poll for their
     // inputs measured slower: the polls barely sped up and the stream lost more.)
     auto advance = [&]() {
@@ -421,9 +422,9 @@ __device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* rin
         slot += NL * kChunk;
         if (slot >= ring_end) slot -= N * kChunk;
         ++issued;
-        if (issued - landed > (uint32_t)kLoaderLag) {
-            wait_vmcnt<kLoaderLag>();
-            publish(issued - (uint32_t)kLoaderLag);
+        if (issued - landed > (uint32_t)LAG) {
+            wait_vmcnt<LAG>();
+            publish(issued - (uint32_t)LAG);
         }
     };
     // MoE expert instructions: the streamed experts are known only once the compute
@@ -1522,7 +1523,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
     __syncthreads();
     const uint32_t q0 = ld_const(P.queue_off + blockIdx.x), q1 = ld_const(P.queue_off + blockIdx.x + 1);
     if (wave >= kComputeWaves) {
-        loader_wave<HD, MF, MOE>(P, &ctl, ring, wave - kComputeWaves, q0, q1, ctl.ctx);
+        loader_wave<B, HD, MF, MOE>(P, &ctl, ring, wave - kComputeWaves, q0, q1, ctl.ctx);
     } else {
         compute_wave<B, HD, MF, MOE>(P, A, &ctl, ring, xs, wave, q0, q1, ctl.ctx);
     }

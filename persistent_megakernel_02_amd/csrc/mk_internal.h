@@ -24,6 +24,8 @@ constexpr uint32_t kLdsBytes = 160 * 1024;          // LDS of one gfx950 compute
 constexpr uint32_t kStaticLds = 1024;               // reserved for the control block
 constexpr uint32_t kMinRingChunks = 72;             // >= one attention block (2 x 32 KV chunks) + its RoPE chunk
 constexpr int kLoaderLag = 4;                       // chunks in flight per loader wave (deeper queues slow the polls)
+// The same by batch: at batch 1 and 2 (long rows streamed in segments) six measured best.
+template <int B> constexpr int loader_lag() { return B <= 2 ? 6 : kLoaderLag; }
 constexpr int kMaxBatch = 8;
 constexpr int kMaxGroup = 4;                        // q heads per KV head
 constexpr uint32_t kMaxResidRows = 64;              // O / DOWN rows per instruction
