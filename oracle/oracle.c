@@ -292,6 +292,76 @@ int orc_step(const orc_cfg* c, const orc_weights* w, orc_cache* kv, int32_t B, c
     return rc;
 }
 
+/* P tokens per sequence in one layer-major pass: token t of sequence b sits at
+ * position pos[b] + t.  Per layer the K/V of every new position are written into
+ * the cache first; the query at position p then attends to cache positions 0..p,
+ * so each position sees exactly what P single-position steps would have given it
+ * (same primitives, same order inside every dot product).  Writes the logits of
+ * each sequence's last position [B][V] and its greedy token next[B]. */
+int orc_prefill(const orc_cfg* c, const orc_weights* w, orc_cache* kv, int32_t B, int32_t P, const int32_t* pos,
+                const int32_t* tokens, float* logits, int32_t* next) {
+    if (!valid_cfg(c) || B <= 0 || B > kv->batch || P <= 0) return ORC_E_ARG;
+    for (int32_t b = 0; b < B; ++b) {
+        if (pos[b] < 0 || pos[b] + P > kv->max_seq) return ORC_E_ARG;
+        for (int32_t t = 0; t < P; ++t)
+            if (tokens[(int64_t)b * P + t] < 0 || tokens[(int64_t)b * P + t] >= c->vocab) return ORC_E_ARG;
+    }
+    const int32_t d = c->hidden, Hq = c->n_q_heads, Hkv = c->n_kv_heads, hd = c->head_dim;
+    const int32_t group = Hq / Hkv, S = kv->max_seq, n = B * P;
+    int32_t* trace_sel = g_moe_sel; /* the per-step MoE trace is sized for one position per sequence */
+    float* trace_prob = g_moe_prob;
+    g_moe_sel = 0;
+    g_moe_prob = 0;
+    float* h = (float*)malloc(sizeof(float) * (size_t)n * d);
+    float* x = (float*)malloc(sizeof(float) * (size_t)n * d);
+    float* q = (float*)malloc(sizeof(float) * (size_t)n * Hq * hd);
+    float* k = (float*)malloc(sizeof(float) * (size_t)n * Hkv * hd);
+    float* v = (float*)malloc(sizeof(float) * (size_t)n * Hkv * hd);
+    float* o = (float*)malloc(sizeof(float) * (size_t)n * Hq * hd);
+    float* ao = (float*)malloc(sizeof(float) * (size_t)n * d);
+    float* hl = (float*)malloc(sizeof(float) * (size_t)B * d);
+    for (int32_t r = 0; r < n; ++r)
+        for (int32_t i = 0; i < d; ++i) h[(int64_t)r * d + i] = bf_to_f(w->embed[(int64_t)tokens[r] * d + i]);
+    for (int32_t l = 0; l < c->n_layers; ++l) {
+        const orc_layer* lw = &w->layers[l];
+        for (int32_t r = 0; r < n; ++r) orc_rmsnorm(h + (int64_t)r * d, lw->attn_norm, d, c->rms_eps, x + (int64_t)r * d);
+        gemv(lw->wq, Hq * hd, d, x, d, n, q, Hq * hd);
+        gemv(lw->wk, Hkv * hd, d, x, d, n, k, Hkv * hd);
+        gemv(lw->wv, Hkv * hd, d, x, d, n, v, Hkv * hd);
+        for (int32_t r = 0; r < n; ++r) {
+            const int32_t b = r / P, p = pos[b] + r % P;
+            for (int32_t hh = 0; hh < Hq; ++hh) orc_rope(q + ((int64_t)r * Hq + hh) * hd, hd, p, c->rope_theta);
+            for (int32_t g = 0; g < Hkv; ++g) {
+                float* kg = k + ((int64_t)r * Hkv + g) * hd;
+                float* vg = v + ((int64_t)r * Hkv + g) * hd;
+                orc_rope(kg, hd, p, c->rope_theta);
+                int64_t base = ((((int64_t)l * kv->batch + b) * Hkv + g) * S + p) * hd;
+                for (int32_t i = 0; i < hd; ++i) {
+                    kv->k[base + i] = orc_bf16_bits(kg[i]);
+                    kv->v[base + i] = orc_bf16_bits(vg[i]);
+                }
+            }
+        }
+#pragma omp parallel for schedule(dynamic) collapse(2)
+        for (int32_t r = 0; r < n; ++r)
+            for (int32_t hh = 0; hh < Hq; ++hh) {
+                const int32_t b = r / P, p = pos[b] + r % P, g = hh / group;
+                int64_t base = (((int64_t)l * kv->batch + b) * Hkv + g) * S * hd;
+                orc_attend(q + ((int64_t)r * Hq + hh) * hd, kv->k + base, kv->v + base, hd, p + 1, hd,
+                           o + ((int64_t)r * Hq + hh) * hd);
+            }
+        gemv(lw->wo, d, Hq * hd, o, Hq * hd, n, ao, d);
+        for (int64_t i = 0; i < (int64_t)n * d; ++i) h[i] = (float)((double)h[i] + (double)ao[i]);
+        ffn_block(c, lw, l, n, h);
+    }
+    for (int32_t b = 0; b < B; ++b) memcpy(hl + (int64_t)b * d, h + ((int64_t)b * P + P - 1) * d, sizeof(float) * d);
+    int rc = head_logits(c, w, B, hl, logits, next);
+    free(h); free(x); free(q); free(k); free(v); free(o); free(ao); free(hl);
+    g_moe_sel = trace_sel;
+    g_moe_prob = trace_prob;
+    return rc;
+}
+
 int orc_sequence(const orc_cfg* c, const orc_weights* w, const int32_t* tokens, int32_t n, float* logits) {
     if (!valid_cfg(c) || n <= 0) return ORC_E_ARG;
     for (int32_t t = 0; t < n; ++t)

@@ -66,6 +66,13 @@ typedef struct {
 int orc_step(const orc_cfg* c, const orc_weights* w, orc_cache* kv, int32_t B, const int32_t* pos,
              const int32_t* tok, float* logits, int32_t* next);
 
+/* P tokens per sequence [B][P] in one layer-major pass (token t of sequence b at
+ * position pos[b] + t); K/V of the new positions are written into the cache.
+ * Equal, bit for bit, to P calls of orc_step.  Writes the logits of the last
+ * position [B][V] and the greedy tokens next[B]. */
+int orc_prefill(const orc_cfg* c, const orc_weights* w, orc_cache* kv, int32_t B, int32_t P, const int32_t* pos,
+                const int32_t* tokens, float* logits, int32_t* next);
+
 /* Optional per-layer MoE trace of the step above: sel [L][B][top_k] expert ids
  * (ascending) and prob [L][B][E] router probabilities.  NULL disables. */
 void orc_set_moe_trace(int32_t* sel, float* prob);

@@ -1,11 +1,16 @@
 """GPU parity of the decode step against the CPU oracle, through the C ABI.
 
-The oracle decodes greedily; the GPU is fed the oracle's tokens (teacher
-forcing) and must, at every step, produce the oracle's greedy token and logits
-within max |err| <= 2e-2.  A token mismatch is accepted only as a near tie:
-the oracle's own logits for both tokens lie within the tolerance of each other
-and the GPU's token is the argmax of the GPU's logits.  Several tokens are then
-correct, the rest of the horizon still gets compared.
+The oracle decodes greedily.  Most tests feed the GPU the oracle's tokens
+(teacher forcing) and require, at every step, logits within max |err| <= 2e-2
+and the oracle's greedy token.  A token that differs is accepted only as a
+near tie: the oracle's own top-1 margin over the GPU's token must be below
+NEAR_TIE = 1e-3 (ties closer than the fp32 accumulation noise of a 2048-term
+dot product can legitimately resolve either way), and the GPU's token must be
+the argmax of the GPU's logits.  Every such flip is printed with its step,
+sequence, margin and both sides' logits; the tests bound how many there may be
+(none on the headline path).  One test runs the headline workload free-running
+on the device exactly as the benchmark does (each step's output token buffer is
+the next step's input) and checks it against the oracle's own greedy chain.
 """
 import os
 import time
@@ -19,6 +24,7 @@ import persistent_megakernel_02_amd.inputs as I
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
+NEAR_TIE = 1e-3
 
 
 def _torch():
@@ -54,20 +60,37 @@ def gpu_run(dec, prompt, ref_tok, steps):
     return toks, rows
 
 
-def compare(ref_tok, ref_log, got_tok, got_log, label):
-    worst, near = 0.0, 0
+def top2_margin(row):
+    """Oracle logit of the top token minus the runner-up's."""
+    i = int(np.argmax(row))
+    rest = np.delete(row, i)
+    return float(row[i] - rest.max())
+
+
+def compare(ref_tok, ref_log, got_tok, got_log, label, max_flips=0):
+    """Logits within TOL at every step; tokens equal except near ties (oracle
+    margin < NEAR_TIE, the GPU token is the GPU logits' argmax), at most max_flips
+    of them.  Returns (worst logit error, list of flips)."""
+    worst, flips, tightest = 0.0, [], float("inf")
     for t, (rt_, rl, gt, gl) in enumerate(zip(ref_tok, ref_log, got_tok, got_log)):
         err = float(np.abs(rl - gl).max())
         worst = max(worst, err)
         assert err <= TOL, f"{label} step {t}: max |logit err| {err:.3e}"
         for b in range(rt_.shape[0]):
+            tightest = min(tightest, top2_margin(rl[b]))
             if rt_[b] != gt[b]:
-                margin = float(rl[b, rt_[b]] - rl[b, gt[b]])
-                assert margin <= 2 * TOL, f"{label} step {t} seq {b}: token {gt[b]} vs {rt_[b]}, margin {margin}"
-                assert gl[b, gt[b]] == gl[b].max()
-                near += 1
-    print(f"{label}: {len(ref_tok)} steps, max |logit err| {worst:.3e}, near-tie token flips {near}")
-    return worst, near
+                r, g = int(rt_[b]), int(gt[b])
+                margin = float(rl[b, r] - rl[b, g])
+                flips.append((t, b, r, g, margin))
+                print(f"{label}: step {t} seq {b}: oracle token {r} vs GPU token {g}; oracle logits "
+                      f"{rl[b, r]:.6f} / {rl[b, g]:.6f} (margin {margin:.3e}), GPU logits {gl[b, r]:.6f} / "
+                      f"{gl[b, g]:.6f}", flush=True)
+                assert margin < NEAR_TIE, f"{label} step {t} seq {b}: flip with oracle margin {margin:.3e}"
+                assert gl[b, g] == gl[b].max()
+    print(f"{label}: {len(ref_tok)} steps, max |logit err| {worst:.3e}, smallest oracle top-2 margin "
+          f"{tightest:.3e}, near-tie flips {len(flips)}", flush=True)
+    assert len(flips) <= max_flips, f"{label}: {len(flips)} near-tie flips (at most {max_flips})"
+    return worst, flips
 
 
 @pytest.fixture(scope="module")
@@ -91,8 +114,7 @@ def test_tiny_parity(tiny, mode):
     print(f"case tiny mode={mode}", flush=True)
     dec = _decoder(I.TINY, w, 1, 32, mode)
     gt, gl = gpu_run(dec, prompt, rt_, 16)
-    _, near = compare(rt_, rl, gt, gl, f"tiny mode={mode}")
-    assert near == 0
+    compare(rt_, rl, gt, gl, f"tiny mode={mode}")
     assert dec.context_len() == [24]
     dec.close()
 
@@ -166,19 +188,59 @@ def llama1b():
     return w, prompt
 
 
-def test_llama1b_b1_full_horizon(llama1b):
-    """The headline workload: 32 prompt tokens, 128 greedy steps, batch 1."""
+@pytest.fixture(scope="module")
+def llama1b_chain(llama1b):
+    """The oracle's greedy chain of the headline workload: 32 prompt tokens, then 128 steps."""
     w, prompt = llama1b
     t0 = time.time()
     rt_, rl = oracle_run(I.LLAMA_1B, w, prompt, 128, 161)
-    print(f"oracle 160 forward passes in {time.time() - t0:.1f}s", flush=True)
-    for kind, name in ((1, "VALU"), (2, "MFMA")):
-        print(f"case 1B b1 megakernel gemv={name}", flush=True)
-        d = _decoder(I.LLAMA_1B, w, 1, 161, 0, gemv_kind=kind)
-        gt, gl = gpu_run(d, prompt, rt_, 128)
-        worst, near = compare(rt_, rl, gt, gl, f"1B b1 megakernel gemv={name}")
-        assert near <= 2
-        d.close()
+    print(f"oracle 32-token prefill + 128 steps in {time.time() - t0:.1f}s", flush=True)
+    return rt_, rl
+
+
+@pytest.mark.parametrize("kind,name,flips", [(1, "VALU", 0), (2, "MFMA", 1)], ids=["valu", "mfma"])
+def test_llama1b_b1_full_horizon(llama1b, llama1b_chain, kind, name, flips):
+    """The headline workload, teacher-forced: 32 prompt tokens, 128 greedy steps,
+    batch 1, every step's logits and token against the oracle."""
+    w, prompt = llama1b
+    rt_, rl = llama1b_chain
+    print(f"case 1B b1 megakernel gemv={name}", flush=True)
+    d = _decoder(I.LLAMA_1B, w, 1, 161, 0, gemv_kind=kind)
+    gt, gl = gpu_run(d, prompt, rt_, 128)
+    compare(rt_, rl, gt, gl, f"1B b1 megakernel gemv={name}", max_flips=flips)
+    d.close()
+
+
+def test_llama1b_b1_free_running_device_chain(llama1b, llama1b_chain):
+    """The headline workload exactly as the benchmark runs it: prefill, then 128
+    decode steps whose token input is the previous step's output buffer on the
+    device (no host round trip); each step writes its own logits row.  The GPU's
+    chain must be the oracle's greedy chain: every step's logits within TOL and
+    the argmax of every step's GPU logits (lowest index on ties) equal to the
+    oracle's token; the last token left in the buffer is the oracle's last."""
+    torch = _torch()
+    w, prompt = llama1b
+    rt_, rl = llama1b_chain
+    V = I.LLAMA_1B.vocab
+    print("case 1B b1 free-running device chain", flush=True)
+    d = _decoder(I.LLAMA_1B, w, 1, 161, 0)
+    tok = torch.zeros(1, dtype=torch.int32, device=d.device)
+    rows = torch.empty((129, 1, V), dtype=torch.float32, device=d.device)
+    d.prefill(torch.from_numpy(prompt).to(d.device), rows[0], tok)
+    for t in range(128):
+        d.decode_step(tok, tok, rows[t + 1])
+    torch.cuda.synchronize()
+    got = rows.cpu().numpy()
+    last = int(tok.cpu().numpy()[0])
+    d.close()
+    worst = 0.0
+    for t in range(129):
+        err = float(np.abs(got[t] - rl[t]).max())
+        worst = max(worst, err)
+        assert err <= TOL, f"step {t}: max |logit err| {err:.3e}"
+        assert int(np.argmax(got[t][0])) == int(rt_[t][0]), f"step {t}: chain left the oracle's greedy chain"
+    assert last == int(rt_[128][0])
+    print(f"free-running chain: 129 tokens identical, max |logit err| {worst:.3e}", flush=True)
 
 
 def test_llama1b_b1_graph_matches_megakernel_bitwise(llama1b):
@@ -231,8 +293,7 @@ def test_llama1b_b2_long_context():
         got_t.append(g_n.cpu().numpy().copy())
         got_l.append(g_l.cpu().numpy().copy())
         tok = nxt.astype(np.int32)
-    _, near = compare(ref_t, ref_l, got_t, got_l, "1B b2 ctx=2000")
-    assert near <= 1
+    compare(ref_t, ref_l, got_t, got_l, "1B b2 ctx=2000")
     assert d.context_len() == [ctx + steps] * B
     d.close()
 
@@ -264,27 +325,29 @@ def test_ragged_contexts(mode):
         got_t.append(g_n.cpu().numpy().copy())
         got_l.append(g_l.cpu().numpy().copy())
         tok = nxt.astype(np.int32)
-    _, near = compare(ref_t, ref_l, got_t, got_l, f"ragged contexts mode={mode}")
-    assert near == 0
+    compare(ref_t, ref_l, got_t, got_l, f"ragged contexts mode={mode}")
     assert d.context_len() == [n + steps for n in lens]
     d.close()
 
 
-def test_llama8b_b1_prefix():
+@pytest.mark.timeout(900)
+def test_llama8b_b1_config_positions():
     """The 8B shape (32 layers, hidden 4096, head_dim 128, untied head) at batch
-    1: 6 prompt tokens and 4 greedy steps against the oracle."""
+    1 at its workload's positions: a 128-token prompt, then 16 greedy steps
+    (positions 128..143), teacher-forced, against the oracle."""
     cfg = I.LLAMA_8B
+    P, steps = 128, 16
     t0 = time.time()
     w = I.make_weights(cfg, seed=0)
-    prompt = I.make_prompt(cfg, 1, 6, seed=0)
+    prompt = I.make_prompt(cfg, 1, P, seed=0)
     print(f"8B weights generated in {time.time() - t0:.1f}s", flush=True)
-    rt_, rl = oracle_run(cfg, w, prompt, 4, 16)
-    print(f"8B oracle done in {time.time() - t0:.1f}s", flush=True)
+    rt_, rl = oracle_run(cfg, w, prompt, steps, P + steps + 1)
+    print(f"8B oracle prefill + {steps} steps done in {time.time() - t0:.1f}s", flush=True)
     print("case 8B b1 megakernel", flush=True)
-    d = _decoder(cfg, w, 1, 16, 0)
-    gt, gl = gpu_run(d, prompt, rt_, 4)
-    _, near = compare(rt_, rl, gt, gl, "8B b1 megakernel")
-    assert near <= 1
+    d = _decoder(cfg, w, 1, P + steps + 1, 0)
+    gt, gl = gpu_run(d, prompt, rt_, steps)
+    compare(rt_, rl, gt, gl, "8B b1 megakernel")
+    assert d.context_len() == [P + steps]
     d.close()
 
 
@@ -304,18 +367,18 @@ def test_small_moe_parity(B, cus):
     print(f"case small MoE b{B} cus={cus}", flush=True)
     d = _decoder(cfg, w, B, 20, 0, num_cus=cus)
     gt, gl = gpu_run(d, prompt, rt_, 10)
-    _, near = compare(rt_, rl, gt, gl, f"small MoE b{B} cus={cus}")
-    assert near == 0
+    compare(rt_, rl, gt, gl, f"small MoE b{B} cus={cus}")
     d.close()
 
 
+@pytest.mark.timeout(600)
 def test_moe_b4_long_context():
     """The synthetic MoE shape (8 layers, hidden 4096, 64 experts, top 6, one
     shared, expert width 1536) at batch 4 over a 4096-position synthetic context,
-    2 steps; the oracle's routing is checked for near ties first (a near tie could
+    8 steps; the oracle's routing is checked for near ties first (a near tie could
     select a different expert on either side)."""
     cfg = I.MOE
-    B, ctx, steps = 4, 4096, 2
+    B, ctx, steps = 4, 4096, 8
     t0 = time.time()
     w = I.make_weights(cfg, seed=14)
     print(f"MoE weights generated in {time.time() - t0:.1f}s", flush=True)
@@ -340,8 +403,7 @@ def test_moe_b4_long_context():
         got_l.append(g_l.cpu().numpy().copy())
         tok = nxt.astype(np.int32)
     print(f"MoE done in {time.time() - t0:.1f}s", flush=True)
-    _, near = compare(ref_t, ref_l, got_t, got_l, f"MoE b{B} ctx={ctx}")
-    assert near <= 1
+    compare(ref_t, ref_l, got_t, got_l, f"MoE b{B} ctx={ctx}")
     d.close()
 
 
@@ -378,8 +440,7 @@ def test_tiny_mfma_gemv(B, cus):
     print(f"case tiny b{B} cus={cus} gemv=MFMA", flush=True)
     d = _decoder(cfg, w, B, 20, 0, gemv_kind=2, num_cus=cus)
     gt, gl = gpu_run(d, prompt, rt_, 8)
-    _, near = compare(rt_, rl, gt, gl, f"tiny b{B} cus={cus} gemv=MFMA")
-    assert near == 0
+    compare(rt_, rl, gt, gl, f"tiny b{B} cus={cus} gemv=MFMA")
     d.close()
 
 
@@ -428,14 +489,15 @@ def test_down_column_slices():
         d.close()
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("B,ctx,kind", [(4, 8192, 0), (8, 8192, 0), (8, 8192, 2)],
                          ids=["b4-auto", "b8-auto", "b8-mfma"])
 def test_llama1b_batch_long_context(B, ctx, kind):
     """The 1B shape at batch 4 and 8 over an 8192-position synthetic context:
-    split attention and sliced DOWN, 3 steps; at batch 8 also on the matrix cores."""
+    split attention and sliced DOWN, 8 steps; at batch 8 also on the matrix cores."""
     cfg = I.LLAMA_1B
     w = I.make_weights(cfg, seed=9)
-    steps, S = 3, ctx + 8
+    steps, S = 8, ctx + 16
     start = I.make_prompt(cfg, B, 1, seed=9)[:, 0]
     orc = O.Oracle(cfg, w, B, S)
     print(f"case 1B b{B} ctx={ctx} megakernel gemv={kind}", flush=True)
@@ -454,6 +516,5 @@ def test_llama1b_batch_long_context(B, ctx, kind):
         got_t.append(g_n.cpu().numpy().copy())
         got_l.append(g_l.cpu().numpy().copy())
         tok = nxt.astype(np.int32)
-    _, near = compare(ref_t, ref_l, got_t, got_l, f"1B b{B} ctx={ctx}")
-    assert near <= 1
+    compare(ref_t, ref_l, got_t, got_l, f"1B b{B} ctx={ctx}")
     d.close()

@@ -484,3 +484,81 @@ def test_one_layer_attention_composition():
         xf = O.rmsnorm(hh, w.final_norm, cfg.rms_eps)
         want = (bits_to_f32(w.head).astype(np.float64) @ xf.astype(np.float64)).astype(np.float32)
         assert ulp_diff(logits[0], want).max() <= 1
+
+
+# ---------------------------------------------------------------------------------------------
+# pins of two readings the other tests leave open
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("hd", [64, 128])
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_attention_scale_two_position_sigmoid(hd, sign):
+    """Scores are q.K_j / sqrt(hd).  Two positions with K_0 = 0 and K_1 = c e_0 and
+    one-hot values V_0 = e_0, V_1 = e_1 make the output a logistic function of one
+    score: o_1 = sigma(s_1) and o_0 = sigma(-s_1) with s_1 = fp32(q_0 c / sqrt(hd)).
+    A scale of 1, 1/hd or sqrt(hd), or a dropped exponent, gives another value."""
+    q = np.zeros(hd, np.float32)
+    q[0] = 2.0
+    q[5] = -3.0  # a component the keys never see
+    K = np.zeros((2, hd), np.uint16)
+    K[1, 0] = O.bf16_bits(4.0 * sign)
+    V = np.zeros((2, hd), np.uint16)
+    V[0, 0] = 0x3F80
+    V[1, 1] = 0x3F80
+    o = O.attend(q, K, V)
+    s1 = np.longdouble(np.float32(np.float64(8.0 * sign) / np.sqrt(np.float64(hd))))
+    sig = 1 / (1 + np.exp(-s1))
+    assert ulp_diff(o[1], np.float32(sig)) <= 1
+    assert ulp_diff(o[0], np.float32(1 - sig)) <= 1
+    assert not np.delete(o, [0, 1]).any()
+    if hd == 64:  # s_1 = +-1 exactly: sigma(1) = 0.7310585786..., sigma(-1) = 0.2689414213...
+        assert abs(float(o[1]) - (0.7310585786300049 if sign > 0 else 0.2689414213699951)) < 1e-7
+
+
+def test_moe_weights_are_not_renormalised():
+    """All router logits equal: every probability is exactly 1/E = 0.125, top-2
+    takes experts 0 and 1 (ties to the lower index), and their probabilities sum to
+    0.25.  Without renormalisation the FFN adds shared + 0.125 y_0 + 0.125 y_1; a
+    renormalising router would weight both experts by 0.5."""
+    cfg, w = _tiny_moe(top_k=2)
+    L = w.layers[0]
+    L["router"] = np.zeros_like(L["router"])
+    orc = O.Oracle(cfg, w, 1, 4)
+    h = bits_to_f32(I.normal_bf16(I.key(23, 1), (1, cfg.hidden), 0.0, 1.0))
+    out = orc.ffn(0, h)
+    x = O.rmsnorm(h[0], L["mlp_norm"], cfg.rms_eps)
+    sel, prob = O.route(np.zeros(8, np.float32), 2)
+    assert list(sel) == [0, 1] and np.all(prob == np.float32(0.125))
+    y = _expert(None, x, L["s_gate"], L["s_up"], L["s_down"]).astype(np.float64)
+    y0 = _expert(None, x, L["e_gate"][0], L["e_up"][0], L["e_down"][0]).astype(np.float64)
+    y1 = _expert(None, x, L["e_gate"][1], L["e_up"][1], L["e_down"][1]).astype(np.float64)
+    want = (h[0].astype(np.float64) + (y + 0.125 * y0 + 0.125 * y1).astype(np.float32).astype(np.float64))
+    assert ulp_diff(out[0], want.astype(np.float32)).max() <= 1
+    renorm = (h[0].astype(np.float64) + (y + 0.5 * y0 + 0.5 * y1).astype(np.float32).astype(np.float64))
+    assert np.abs(out[0].astype(np.float64) - renorm).max() > 1e-3
+
+
+@pytest.mark.parametrize("cfg_name", ["tiny", "moe"])
+def test_layer_major_prefill_equals_single_steps(cfg_name):
+    """orc_prefill (all prompt positions per layer at once, K/V written into the
+    cache first, causal attention over the cache) gives the same logits, tokens
+    and cache bits as feeding the prompt one position at a time, also when the
+    sequences already hold a context."""
+    if cfg_name == "tiny":
+        cfg = I.TINY
+    else:
+        cfg, _ = _tiny_moe(top_k=2)
+        cfg = I.replace(cfg, n_layers=2)
+    w = I.make_weights(cfg, seed=31)
+    B, P = 2, 9
+    prompt = I.make_prompt(cfg, B, P + 3, seed=32)
+    a = O.Oracle(cfg, w, B, 16)
+    b = O.Oracle(cfg, w, B, 16)
+    # a context of 3 positions first, fed by single steps on both sides
+    for t in range(3):
+        a.step(prompt[:, t])
+        b.step(prompt[:, t])
+    ta, la = a.prefill(prompt[:, 3:], batched=True)
+    tb, lb = b.prefill(prompt[:, 3:], batched=False)
+    assert np.array_equal(la, lb) and np.array_equal(ta, tb)
+    assert np.array_equal(a.k_cache, b.k_cache) and np.array_equal(a.v_cache, b.v_cache)
+    assert list(a.pos) == list(b.pos) == [P + 3] * B
