@@ -66,7 +66,12 @@ typedef enum {
 
 typedef enum {
     MK_MODE_MEGAKERNEL = 0, /* one persistent launch per step [MK] */
-    MK_MODE_GRAPH = 1       /* one kernel per op, replayed as a hipGraph [ROOT] */
+    MK_MODE_GRAPH = 1,      /* one kernel per op, replayed as a hipGraph [ROOT] */
+    MK_MODE_ENV = 2         /* opt-in from the environment [LOW: the resident decode
+                               kernel is off by default and enabled by an environment
+                               variable]: MK_MEGAKERNEL=1 selects MK_MODE_MEGAKERNEL,
+                               anything else (or unset) MK_MODE_GRAPH; read by
+                               mk_query_sizes, mk_plan_inspect and mk_create */
 } mk_mode;
 
 /* GEMV arithmetic of the persistent mode.  Both read every weight once and
@@ -143,36 +148,65 @@ mk_status mk_query_sizes(const mk_model_config* cfg, const mk_runtime_config* rt
 mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_runtime_config* rt, void* d_workspace,
                     size_t workspace_bytes, void* d_kv, size_t kv_bytes, void* stream, mk_handle** out);
 
-/* Element strides of the K (and V) cache [L][B][Hkv][S][hd]; the V cache starts
- * kv_bytes / 2 bytes after K.  strides_out[0..4] for L, B, Hkv, S, hd. */
+/* Layout of the caller's KV cache, which the step reads for attention and
+ * appends to [MK: attention is one of the fused per-layer instructions; LOW: the
+ * workload decodes against the cache its prompt left].  strides_out[0..4]
+ * (host array of 5, written) are the element strides of the K cache
+ * [L][B][Hkv][S][hd] (bf16 elements) for L, B, Hkv, S, hd; the V cache has the
+ * same layout and starts kv_bytes / 2 bytes after K.  Host only, no device work.
+ * MK_E_INVALID for a NULL argument. */
 mk_status mk_kv_layout(const mk_handle* h, int64_t strides_out[5]);
 
-/* Feed a prompt: d_tokens [B, P] int32 row-major on the device.  Runs P decode
- * steps (positions continue from the current context lengths), then writes the
- * logits of the last position to d_logits [B, V] and the greedy tokens to
- * d_next [B].  B must equal max_batch. */
+/* Feed a prompt [LOW: the headline workload first consumes a 32-token prompt,
+ * then decodes greedily].  d_tokens: device int32 [B, P] row-major, read only.
+ * Runs P decode steps in the handle's mode (each one launch in the persistent
+ * mode [MK]); positions continue from the current context lengths and every
+ * context grows by P.  Writes the last position's logits to d_logits (device
+ * fp32 [B, V]) and its greedy tokens to d_next (device int32 [B]); the other
+ * positions' logits land in the workspace.  Enqueued on `stream`; returns after
+ * host-side checks.  B must equal max_batch (the schedule, the staging areas and
+ * the kernel are built for max_batch sequences and every weight byte is read
+ * once for all of them, so fewer sequences would cost the same launch: pad the
+ * batch instead), else MK_E_INVALID; MK_E_CAPACITY if a context would pass
+ * max_seq; MK_E_STATE / MK_E_DEVICE_* when a device error is latched. */
 mk_status mk_prefill(mk_handle* h, const int32_t* d_tokens, int32_t B, int32_t P, float* d_logits,
                      int32_t* d_next, void* stream);
 
-/* Set the context length of each sequence (host array [B]) after the caller
- * filled the KV cache directly (e.g. a synthetic context).  Enqueued on the
- * handle's creation stream. */
+/* Set the context length of each sequence after the caller filled the KV cache
+ * directly (e.g. a synthetic context) [LOW: the low-concurrency measurements
+ * include long contexts].  h_lens: host int32 [B], each 0..max_seq, copied.
+ * The new lengths are uploaded on the handle's creation stream, which is then
+ * synchronised.  B must equal max_batch (MK_E_INVALID), a length outside
+ * 0..max_seq is MK_E_CAPACITY. */
 mk_status mk_set_context_len(mk_handle* h, const int32_t* h_lens, int32_t B);
 
-/* One decode step: d_tokens_in [B] at positions ctx_len[b]; writes the greedy
- * tokens d_tokens_out [B] and logits d_logits [B, V]; every context grows by one.
- * d_tokens_in may alias d_tokens_out, so steps chain without the host.
- * MK_E_CAPACITY if a sequence is full; B must equal max_batch. */
+/* One decode step as ONE persistent kernel launch in MK_MODE_MEGAKERNEL [MK: the
+ * whole forward pass fused into one kernel, per-CU instruction plans built
+ * before launch, data-carried completion signals instead of a grid barrier], or
+ * as the replay of a graph of one kernel per op in MK_MODE_GRAPH [ROOT].
+ * d_tokens_in: device int32 [B], the token of each sequence at position
+ * ctx_len[b]; d_tokens_out: device int32 [B], the greedy tokens (lowest id on
+ * ties); d_logits: device fp32 [B, V].  d_tokens_in may alias d_tokens_out, so
+ * steps chain on the device without the host.  Every context grows by one.
+ * Enqueued on `stream`; returns after host-side checks.  MK_E_CAPACITY if a
+ * sequence is full; B must equal max_batch (see mk_prefill), else MK_E_INVALID;
+ * a device error of an earlier step (watchdog, NaN logit) is reported here as
+ * MK_E_DEVICE_TIMEOUT / MK_E_DEVICE_NAN and latches the handle. */
 mk_status mk_decode_step(mk_handle* h, const int32_t* d_tokens_in, int32_t B, int32_t* d_tokens_out,
                          float* d_logits, void* stream);
 
 /* Host mirror of the context lengths (what the enqueued steps will have reached). */
 mk_status mk_get_context_len(const mk_handle* h, int32_t* h_lens, int32_t B);
 
-/* Clear the merge tickets and a latched device error (enqueued on `stream`); the
- * host mirror of the context lengths is re-read from the device.  The step
- * counter behind the value tags keeps counting, so values an aborted step left
- * behind never satisfy a later step. */
+/* Recover after a device error [MK: nothing is decided at run time, so a step
+ * that failed leaves only stale values and tickets behind].  Synchronises
+ * `stream`, re-reads the context lengths from the device into the host mirror,
+ * clears the merge tickets and the latched error, and synchronises again.  The
+ * step counter behind the value tags keeps counting, so values an aborted step
+ * left behind never satisfy a later step.  MK_E_HIP if a runtime call fails.
+ * A handle without the host-mapped error word (its pinned allocation failed)
+ * gets the device error it cleared returned (MK_E_DEVICE_TIMEOUT /
+ * MK_E_DEVICE_NAN), MK_OK if none. */
 mk_status mk_reset(mk_handle* h, void* stream);
 
 /* Test hook: fault 1 = the next step runs with a 1 ms watchdog and its layer-0
@@ -191,7 +225,9 @@ const char* mk_last_error(const mk_handle* h);
  * [5] verifier result (0 = ok), [6] attention splits, [7] phases, [8] LDS bytes of
  * staged activations, [9] LM-head instructions, [10] the GEMV kind in effect
  * (MK_GEMV_VALU or MK_GEMV_MFMA), [11] q-head groups per attention item (1, or
- * the q heads per KV head when one position split leaves compute units idle). */
+ * the q heads per KV head when one position split leaves compute units idle),
+ * [12] the most ring chunks one compute wave holds while it waits for its data
+ * (mk_create refuses a configuration where this exceeds [2]). */
 mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* rt, int32_t num_cus, int64_t* out,
                           int32_t cap);
 

@@ -64,29 +64,14 @@ int mk_bench_pingpong(int flavor, int peer, int rounds, void* d_words, void* d_o
 int mk_bench_edge(int n_wg, int words, int rounds, int stream, const void* d_src, size_t src_bytes, void* d_data,
                   void* d_out, void* hstream);
 
-/* How much a weight stream slows LDS-bound compute on the same compute unit:
- * n_wg (1..256) co-resident workgroups of four compute and four streaming waves.
- * The compute waves run `iters` steps of four 16-byte LDS reads and 16 FMAs;
- * meanwhile the streaming waves read d_src (src_bytes >= n_wg * 4 KB) with mode
- * 0: nothing; 1: direct-to-LDS loads, eight 1 KB loads in flight per wave; 2:
- * plain 16-byte loads into registers.  d_out: four zeroed uint64 = {ticks (100
- * MHz) of workgroup 0's compute wave 0, KB streamed by its first streaming wave,
- * unused, unused}.  Returns 0, 1 on bad arguments, 4 on launch error. */
-int mk_bench_lds_contention(int mode, int iters, int n_wg, const void* d_src, size_t src_bytes, void* d_out,
-                            void* stream);
-
-/* HBM -> LDS streaming rate of the direct-to-LDS 16-byte-per-lane load:
- * n_wg workgroups of `waves` waves; each wave streams its share of d_src 1 KB
- * per load with `lag` loads in flight (lag in {4,12,24,32,40,48,60} for 1 wave,
- * {12,24,48} for 2, {12,24} for 4).  gran == 0: each wave reads one contiguous
- * share; gran > 0: blocks of `gran` KB dealt round-robin over the waves (the
- * share must be a whole number of blocks).  probe > 0: every probe-th load is
- * followed by an LDS read the wave waits for (lgkmcnt(0)), to show whether the
- * direct-to-LDS loads in flight hold that counter too.  d_out: two uint64, [0] =
- * ticks (100 MHz) of workgroup 0.  Returns 0, 1 on unsupported arguments, 4 on
- * launch error. */
-int mk_bench_lds_stream(int lag, int waves, int gran, int probe, const void* d_src, size_t bytes, int n_wg,
-                        void* d_out, void* stream);
+/* Launch gap of a captured graph [page "斯坦福团队新作让Llama1B实现毫秒级推理获Karpathy盛赞",
+ * section "传统推理方式效率低下的根源剖析": every kernel boundary costs a launch gap
+ * even with graphs]: captures n_kernels (1..4096) empty kernels of `blocks`
+ * workgroups, replays the graph once untimed and `reps` times timed on `stream`
+ * (synchronised), and writes the mean microseconds per kernel to the host float
+ * *h_us_per_kernel.  d_sink: a device int the kernels could write (they never
+ * do).  Returns 0, 1 on bad arguments, 4 on a runtime error. */
+int mk_bench_graph_gap(int n_kernels, int reps, int blocks, void* d_sink, float* h_us_per_kernel, void* stream);
 
 #ifdef __cplusplus
 }

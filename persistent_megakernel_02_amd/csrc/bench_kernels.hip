@@ -384,141 +384,46 @@ extern "C" int mk_bench_edge(int n_wg, int words, int rounds, int stream, const 
 }
 
 // ------------------------------------------------------------------------------------------------
-// How much a weight stream slows LDS-bound compute on the same compute unit.
-// Four compute waves run `iters` steps of (four 16-byte LDS reads, 32 FMAs
-// that use them); four streaming waves meanwhile read `src` with mode 0: nothing;
-// mode 1: direct-to-LDS loads (eight 1 KB loads in flight per wave); mode 2: the
-// same bytes into registers with plain 16-byte loads.  out[0] = ticks (100 MHz)
-// of wave 0 of workgroup 0 for its steps, out[1] = KB streamed by workgroup 0's
-// first streaming wave, out[2] = a checksum that keeps the arithmetic alive.
+// Gap per kernel of a captured graph: a graph of n empty kernels replayed `reps`
+// times; the time per kernel is what one op of the one-kernel-per-op path pays
+// in launch and boundary cost before it does any work.
 // ------------------------------------------------------------------------------------------------
 namespace {
-__global__ void __launch_bounds__(512) k_lds_contention(int mode, int iters, const char* src, size_t src_kb,
-                                                        uint64_t* out) {
-    __shared__ __attribute__((aligned(1024))) char ring[4 * 8 * 1024];
-    __shared__ __attribute__((aligned(16))) float tile[4][2048];
-    __shared__ uint32_t done;
-    const int n = gridDim.x, wg = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int i = tid; i < 4 * 2048; i += 512) (&tile[0][0])[i] = (float)(i & 255) * 1e-3f;
-    if (tid == 0) done = 0;
-    __syncthreads();
-    if (wave >= 4) {
-        const int sw = wave - 4;
-        const uint32_t base = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)ring + sw * 8192u;
-        const size_t streams = (size_t)n * 4, sid = (size_t)wg * 4 + sw;
-        const size_t per = src_kb / streams;
-        uint64_t kb = 0;
-        uint32_t acc = 0;
-        if (mode != 0 && per > 0) {
-            for (uint32_t guard = 0; guard < (1u << 24); ++guard) {
-                if (__hip_atomic_load(&done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) break;
-                const size_t c = sid * per + (guard % per);
-                if (mode == 1) {
-                    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
-                                 :
-                                 : "{m0}"(__builtin_amdgcn_readfirstlane(base + (guard & 7u) * 1024u)),
-                                   "v"(src + c * 1024 + lane * 16)
-                                 : "memory");
-                    __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8));
-                } else {
-                    const uint4 v = *(const uint4*)(src + c * 1024 + lane * 16);
-                    acc ^= v.x ^ v.y ^ v.z ^ v.w;
-                }
-                ++kb;
+__global__ void __launch_bounds__(64) k_empty(int* sink, int v) {
+    if (v == 0x7FFFFFFF && threadIdx.x == 0) *sink = v;  // never true; keeps a body
+}
+}  // namespace
+
+extern "C" int mk_bench_graph_gap(int n_kernels, int reps, int blocks, void* d_sink, float* h_us_per_kernel,
+                                  void* stream) {
+    if (n_kernels < 1 || n_kernels > 4096 || reps < 1 || blocks < 1 || blocks > 65536 || !d_sink || !h_us_per_kernel)
+        return 1;
+    hipStream_t st = (hipStream_t)stream;
+    hipStream_t cap = nullptr;
+    hipGraph_t g = nullptr;
+    hipGraphExec_t ge = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    int rc = 4;
+    if (hipStreamCreateWithFlags(&cap, hipStreamNonBlocking) != hipSuccess) return 4;
+    if (hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal) == hipSuccess) {
+        for (int i = 0; i < n_kernels; ++i) hipLaunchKernelGGL(k_empty, dim3(blocks), dim3(64), 0, cap, (int*)d_sink, i);
+        if (hipStreamEndCapture(cap, &g) == hipSuccess && hipGraphInstantiate(&ge, g, nullptr, nullptr, 0) == hipSuccess &&
+            hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
+            bool ok = hipGraphLaunch(ge, st) == hipSuccess && hipStreamSynchronize(st) == hipSuccess;  // warm-up
+            ok = ok && hipEventRecord(e0, st) == hipSuccess;
+            for (int r = 0; r < reps && ok; ++r) ok = hipGraphLaunch(ge, st) == hipSuccess;
+            ok = ok && hipEventRecord(e1, st) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+            float ms = 0.f;
+            if (ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess) {
+                *h_us_per_kernel = ms * 1000.0f / (float)((double)reps * n_kernels);
+                rc = 0;
             }
         }
-        __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
-        if (wg == 0 && sw == 0 && lane == 0) out[1] = kb;
-        if (acc == 0x9E3779B9u) out[3] = acc;
-        return;
     }
-    const float* t = tile[wave];
-    float a0 = 0.f, a1 = 0.f;
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    for (int it = 0; it < iters; ++it) {
-        const int o = ((it * 16 + lane) * 8) & 2047;
-        const float4 x0 = *(const float4*)(t + o);
-        const float4 x1 = *(const float4*)(t + ((o + 512) & 2047));
-        const float4 x2 = *(const float4*)(t + ((o + 1024) & 2047));
-        const float4 x3 = *(const float4*)(t + ((o + 1536) & 2047));
-        a0 = fmaf(x0.x, x1.x, a0); a1 = fmaf(x0.y, x1.y, a1); a0 = fmaf(x0.z, x1.z, a0); a1 = fmaf(x0.w, x1.w, a1);
-        a0 = fmaf(x2.x, x3.x, a0); a1 = fmaf(x2.y, x3.y, a1); a0 = fmaf(x2.z, x3.z, a0); a1 = fmaf(x2.w, x3.w, a1);
-        a0 = fmaf(x0.x, x3.x, a0); a1 = fmaf(x0.y, x3.y, a1); a0 = fmaf(x0.z, x3.z, a0); a1 = fmaf(x0.w, x3.w, a1);
-        a0 = fmaf(x2.x, x1.x, a0); a1 = fmaf(x2.y, x1.y, a1); a0 = fmaf(x2.z, x1.z, a0); a1 = fmaf(x2.w, x1.w, a1);
-    }
-    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
-    if (lane == 0 && wave == 0) __hip_atomic_store(&done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (wg == 0 && wave == 0 && lane == 0) out[0] = t1 - t0;
-    if (a0 + a1 == 123456.f) out[2] = 1;
-}
-}  // namespace
-
-extern "C" int mk_bench_lds_contention(int mode, int iters, int n_wg, const void* d_src, size_t src_bytes,
-                                       void* d_out, void* stream) {
-    if (mode < 0 || mode > 2 || iters < 1 || n_wg < 1 || n_wg > 256 || !d_out ||
-        (mode && (!d_src || src_bytes < (size_t)n_wg * 4 * 1024)))
-        return 1;
-    int m = mode, it = iters;
-    size_t kb = mode ? src_bytes / 1024 : 0;
-    void* args[] = {&m, &it, (void*)&d_src, &kb, &d_out};
-    hipError_t e = hipLaunchCooperativeKernel((const void*)k_lds_contention, dim3(n_wg), dim3(512), args, 0,
-                                              (hipStream_t)stream);
-    return e == hipSuccess ? 0 : 4;
-}
-
-// ------------------------------------------------------------------------------------------------
-// HBM -> LDS streaming rate of the direct-to-LDS load the decode loader uses:
-// every workgroup (one per CU) runs WAVES waves; each wave streams its share of
-// `src` 1 KB at a time into a private 32 KB LDS ring with LAG loads in flight.
-// out[0] = ticks of workgroup 0.
-// ------------------------------------------------------------------------------------------------
-namespace {
-template <int LAG, int WAVES>
-__global__ void __launch_bounds__(64 * WAVES) k_lds_stream(const char* src, size_t bytes, uint32_t gran,
-                                                           uint32_t probe, uint64_t* out) {
-    __shared__ __attribute__((aligned(1024))) char ring[WAVES * 32 * 1024];
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const size_t streams = (size_t)gridDim.x * WAVES, s = (size_t)blockIdx.x * WAVES + wave;
-    const size_t per = bytes / 1024 / streams;
-    const uint32_t base = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)ring + wave * 32768u;
-    const char* lane_src = src + (threadIdx.x & 63) * 16;
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    for (size_t c = 0; c < per; ++c) {
-        // stream s owns chunks [s * per, (s + 1) * per) (gran == 0), or blocks of
-        // `gran` chunks dealt round-robin over the streams
-        const size_t chunk = gran == 0 ? s * per + c : ((c / gran) * streams + s) * gran + c % gran;
-        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                     :
-                     : "{m0}"(__builtin_amdgcn_readfirstlane(base + (uint32_t)(c & 31) * 1024u)),
-                       "v"(lane_src + chunk * 1024)
-                     : "memory");
-        __builtin_amdgcn_s_waitcnt((LAG & 15) | ((LAG >> 4) << 14) | (7 << 4) | (15 << 8));
-        if (probe && (c % probe) == 0) {
-            // one LDS read whose value is needed at once: s_waitcnt lgkmcnt(0)
-            const uint32_t v = __hip_atomic_load((const uint32_t*)(ring + 32768 * WAVES - 64), __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (v == 0xDEADBEEFu) out[1] = v;
-        }
-    }
-    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
-    __syncthreads();
-    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
-    if (blockIdx.x == 0 && threadIdx.x == 0) out[0] = t1 - t0;
-}
-}  // namespace
-
-extern "C" int mk_bench_lds_stream(int lag, int waves, int gran, int probe, const void* d_src, size_t bytes,
-                                   int n_wg, void* d_out, void* stream) {
-    if (!d_src || !d_out || n_wg < 1 || gran < 0 || probe < 0 || bytes < (size_t)n_wg * waves * 1024) return 1;
-    const size_t per = bytes / 1024 / ((size_t)n_wg * waves);
-    if (gran > 0 && per % (size_t)gran) return 1;  // whole blocks per stream keep every chunk in range
-    const void* f = nullptr;
-#define MK_LS(L, W) if (lag == L && waves == W) f = (const void*)k_lds_stream<L, W>;
-    MK_LS(4, 1) MK_LS(12, 1) MK_LS(24, 1) MK_LS(32, 1) MK_LS(40, 1) MK_LS(48, 1) MK_LS(60, 1)
-    MK_LS(12, 2) MK_LS(24, 2) MK_LS(48, 2) MK_LS(12, 4) MK_LS(24, 4)
-#undef MK_LS
-    if (!f) return 1;
-    uint32_t g = (uint32_t)gran, pr = (uint32_t)probe;
-    void* args[] = {&d_src, &bytes, &g, &pr, &d_out};
-    return hipLaunchKernel(f, dim3(n_wg), dim3(64 * waves), args, 0, (hipStream_t)stream) == hipSuccess ? 0 : 4;
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (ge) (void)hipGraphExecDestroy(ge);
+    if (g) (void)hipGraphDestroy(g);
+    (void)hipStreamDestroy(cap);
+    return rc;
 }

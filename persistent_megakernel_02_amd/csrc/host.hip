@@ -5,7 +5,9 @@
 // Scheduling follows the page "斯坦福团队新作让Llama1B实现毫秒级推理获Karpathy盛赞",
 // section "Megakernel：从零设计的深度融合方案": before launch every compute unit gets
 // an ordered plan of composite instructions and each dependency is fixed
-// statically as (counter, number of producers); nothing is decided at run time.
+// statically as (producer phase, value tag): an instruction reads the values
+// of an earlier phase only once each one carries its phase's tag for this step;
+// nothing is decided at run time.
 // Every weight matrix is split by rows into one contiguous tile per compute unit
 // (equal bytes per CU, so no CU forms a straggling tail - the wave-quantisation
 // effect the page "大模型吐一个字，显卡要启停两千四百次", section "两千四百次启停",
@@ -26,6 +28,7 @@
 
 namespace mk {
 hipError_t launch_megakernel(const Params& P, const StepArgs& A, hipStream_t stream);
+hipError_t prepare_megakernel(const Params& P);
 bool megakernel_supports(int B, int hd);
 size_t megakernel_lds_bytes(const Params& P);
 hipError_t launch_conventional(const Params& P, const StepArgs& A, hipStream_t stream);
@@ -142,6 +145,38 @@ int auto_hsplit(const mk_model_config* c, const mk_runtime_config* rt, int n_cu,
     const int G = c->n_q_heads / c->n_kv_heads;
     if (rt->mode != MK_MODE_MEGAKERNEL || nsplit != 1 || G < 1) return 1;
     return (int64_t)rt->max_batch * c->n_kv_heads * G <= n_cu ? G : 1;
+}
+
+// The loader writes stream chunk c into ring slot c mod N only once every compute
+// wave's mark (the first chunk it still needs) is above c - N.  A wave that waits
+// for a row batch keeps its mark at the batch start, so one batch must fit the
+// ring; and waves never hold a mark across a barrier inside an instruction (they
+// move it to a region's end when they leave a GEMV region), so the slowest wave
+// can always be served and no wait can close a cycle.  The stretch one wave
+// holds, by instruction kind:
+//  - a VALU row batch: ring_batch_rows rows (8 KB segments of long rows at batch
+//    1 and 2), plus one chunk because packed rows may start inside a chunk;
+//  - a matrix-core unit (16 rows x kMfmaUnitCols columns): 16 / kMfmaChunkRows chunks;
+//  - an attention block: its RoPE chunk and kAttnBlockGroups groups of a K and a
+//    V chunk (a long split goes in half blocks, a wave at most one half block ahead).
+// Returns the largest of these for the configuration (chunks).
+uint32_t max_wave_span(const mk_model_config* c, const mk_runtime_config* rt) {
+    const int B = rt->max_batch;
+    uint32_t span = 1u + 2u * (uint32_t)kAttnBlockGroups;
+    if (use_mfma(c, rt)) return std::max(span, 16u / (uint32_t)kMfmaChunkRows);
+    auto gemv = [&](uint32_t rb, bool pairs) { span = std::max(span, ring_batch_span(rb, B, pairs)); };
+    const uint32_t d2 = (uint32_t)c->hidden * 2u;
+    gemv(d2, false);                                                // QKV, LM head, MoE router
+    gemv((uint32_t)(c->n_q_heads * c->head_dim) * 2u, false);       // O
+    if (c->n_experts) {
+        gemv(d2, true);                                             // expert (gate, up) pairs
+        gemv((uint32_t)c->expert_ffn * 2u, false);                  // expert DOWN
+    } else {
+        gemv(d2, true);                                             // (gate, up) pairs
+        const int ns = std::max(1, down_slices_for(B, c->ffn));
+        gemv((uint32_t)(c->ffn / ns) * 2u, false);                  // DOWN column slice
+    }
+    return span;
 }
 
 mk_status validate(const mk_model_config* c, const mk_runtime_config* rt, std::string* why) {
@@ -373,7 +408,7 @@ Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, i
     lo.eptr = take((size_t)c->n_layers * 3 * nx * 8);
     lo.attn_part = take(B * c->n_kv_heads * nsplit * G * (hd + 2) * 8);
     const size_t conv_blocks = ((size_t)c->vocab + 15) / 16;
-    lo.head_slots = std::max((size_t)n_cu, conv_blocks) * kComputeWaves;
+    lo.head_slots = std::max((size_t)n_cu, conv_blocks) * (kComputeWaves + kLoaderWaves);
     lo.head_part = take(lo.head_slots * B * 2 * 8);
     lo.logits_scr = take(B * c->vocab * 4);
     lo.tok_scr = take(B * 4);
@@ -381,6 +416,16 @@ Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, i
     lo.trace = take(lo.trace_bytes);
     lo.total = off;
     return lo;
+}
+
+// MK_MODE_ENV resolved: the persistent kernel only when the environment opts in.
+mk_runtime_config resolve_mode(const mk_runtime_config* rt) {
+    mk_runtime_config r = *rt;
+    if (r.mode == MK_MODE_ENV) {
+        const char* v = std::getenv("MK_MEGAKERNEL");
+        r.mode = (v && std::strcmp(v, "1") == 0) ? MK_MODE_MEGAKERNEL : MK_MODE_GRAPH;
+    }
+    return r;
 }
 
 int device_cus() {
@@ -406,6 +451,9 @@ struct mk_handle {
     void* kv = nullptr;
     size_t kv_bytes = 0;
     hipStream_t stream = nullptr;
+    hipStream_t last_stream = nullptr;  // stream of the last enqueued step (mk_destroy waits for it)
+    bool used = false;
+    int static_dev = -1;  // >= 0: the workspace is a static array of that device (none yet)
     std::vector<int32_t> ctx;
     uint32_t epoch = 0;
     HostErr* host_err = nullptr;
@@ -451,9 +499,11 @@ const char* mk_status_string(mk_status s) {
 
 const char* mk_last_error(const mk_handle* h) { return h ? h->last_error.c_str() : "null handle"; }
 
-mk_status mk_query_sizes(const mk_model_config* cfg, const mk_runtime_config* rt, size_t* workspace_bytes,
+mk_status mk_query_sizes(const mk_model_config* cfg, const mk_runtime_config* rt_in, size_t* workspace_bytes,
                          size_t* kv_bytes) {
-    if (!workspace_bytes || !kv_bytes) return MK_E_INVALID;
+    if (!workspace_bytes || !kv_bytes || !rt_in) return MK_E_INVALID;
+    const mk_runtime_config rt_r = resolve_mode(rt_in);
+    const mk_runtime_config* rt = &rt_r;
     mk_status s = validate(cfg, rt, nullptr);
     if (s != MK_OK) return s;
     // the compute-unit count may be resolved only at mk_create: size for every count up to the bound
@@ -466,9 +516,11 @@ mk_status mk_query_sizes(const mk_model_config* cfg, const mk_runtime_config* rt
     return MK_OK;
 }
 
-mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* rt, int32_t num_cus, int64_t* out,
+mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* rt_in, int32_t num_cus, int64_t* out,
                           int32_t cap) {
-    if (!out || cap < 0) return MK_E_INVALID;
+    if (!out || cap < 0 || !rt_in) return MK_E_INVALID;
+    const mk_runtime_config rt_r = resolve_mode(rt_in);
+    const mk_runtime_config* rt = &rt_r;
     mk_status s = validate(cfg, rt, nullptr);
     if (s != MK_OK) return s;
     if (num_cus <= 0 || num_cus > kMaxCus) return MK_E_INVALID;
@@ -481,17 +533,25 @@ mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* r
                               : 3 * (int64_t)cfg->ffn * d;
     const int64_t per_layer = (cfg->n_q_heads + 2 * cfg->n_kv_heads) * hd * d + d * cfg->n_q_heads * hd + ffn_w + 2 * d;
     const size_t xb = x_bytes_for(cfg, rt, pl.nsplit);
-    int64_t vals[12] = {num_cus, (int64_t)pl.instrs.size(), (int64_t)ring_chunks_for(xb), (int64_t)pl.max_per_cu,
+    int64_t vals[13] = {num_cus, (int64_t)pl.instrs.size(), (int64_t)ring_chunks_for(xb), (int64_t)pl.max_per_cu,
                         2 * (cfg->n_layers * per_layer + (int64_t)cfg->vocab * d + d), verify_plan(cfg, rt, pl),
-                        pl.nsplit, pl.phases, (int64_t)xb, (int64_t)pl.n_head, use_mfma(cfg, rt) ? 2 : 1, pl.hsplit};
-    for (int i = 0; i < cap && i < 12; ++i) out[i] = vals[i];
+                        pl.nsplit, pl.phases, (int64_t)xb, (int64_t)pl.n_head, use_mfma(cfg, rt) ? 2 : 1, pl.hsplit,
+                        (int64_t)max_wave_span(cfg, rt)};
+    for (int i = 0; i < cap && i < 13; ++i) out[i] = vals[i];
     return MK_OK;
 }
 
-mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_runtime_config* rt, void* d_workspace,
-                    size_t workspace_bytes, void* d_kv, size_t kv_bytes, void* stream, mk_handle** out) {
-    if (!out) return MK_E_INVALID;
+}  // extern "C"
+
+// mk_create; static_dev >= 0 would mark a workspace in a static device array (no
+// size query of every CU count, no pinned error word).
+static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, const mk_runtime_config* rt_in,
+                             void* d_workspace, size_t workspace_bytes, void* d_kv, size_t kv_bytes, void* stream,
+                             mk_handle** out, int static_dev) {
+    if (!out || !rt_in) return MK_E_INVALID;
     *out = nullptr;
+    const mk_runtime_config rt_r = resolve_mode(rt_in);
+    const mk_runtime_config* rt = &rt_r;
     mk_status s = validate(cfg, rt, nullptr);
     if (s != MK_OK) return s;
     if (!w || !w->tok_embedding || !w->final_norm || !w->layers || !d_workspace || !d_kv) return MK_E_INVALID;
@@ -529,19 +589,21 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
         return MK_E_INVALID;
     }
     h->lo = layout(cfg, rt, n_cu, h->plan.nsplit);
-    if (workspace_bytes < h->lo.total || workspace_bytes < need_ws || kv_bytes < need_kv) {
+    if (workspace_bytes < h->lo.total || (static_dev < 0 && workspace_bytes < need_ws) || kv_bytes < need_kv) {
         delete h;
-        return MK_E_INVALID;
+        return static_dev < 0 ? MK_E_INVALID : MK_E_CAPACITY;
     }
     h->ws = (char*)d_workspace;
     h->ws_bytes = workspace_bytes;
     h->kv = d_kv;
     h->kv_bytes = kv_bytes;
     h->ctx.assign(rt->max_batch, 0);
+    h->static_dev = static_dev;
 
-    // pinned, device-visible error word
-    if (hipHostMalloc((void**)&h->host_err, sizeof(HostErr), hipHostMallocMapped | hipHostMallocCoherent) !=
-        hipSuccess) {
+    // pinned, device-visible error word (not for a static workspace: an allocation)
+    if (static_dev >= 0 ||
+        hipHostMalloc((void**)&h->host_err, sizeof(HostErr), hipHostMallocMapped | hipHostMallocCoherent) !=
+            hipSuccess) {
         h->host_err = nullptr;
     } else {
         std::memset(h->host_err, 0, sizeof(HostErr));
@@ -602,8 +664,11 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
     P.queue_off = (const uint32_t*)(ws + lo.qoff);
     P.x_bytes = (uint32_t)x_bytes_for(cfg, rt, h->plan.nsplit);
     P.ring_chunks = ring_chunks_for(P.x_bytes);
-    P.n_head_slots = rt->mode == MK_MODE_MEGAKERNEL ? h->plan.n_head * (uint32_t)kComputeWaves
-                                                    : (uint32_t)conventional_head_blocks(P) * (uint32_t)kComputeWaves;
+    // argmax partials: one per wave that computes LM-head rows (all eight waves of a
+    // CU in the VALU and MoE kernels, the four compute waves on the matrix cores)
+    P.n_head_slots = rt->mode == MK_MODE_MEGAKERNEL
+                         ? h->plan.n_head * (uint32_t)(P.gemv_mfma ? kComputeWaves : kComputeWaves + kLoaderWaves)
+                         : (uint32_t)conventional_head_blocks(P) * (uint32_t)kComputeWaves;
     auto give_up = [&](mk_status st) {
         if (h->host_err) (void)hipHostFree(h->host_err);
         delete h;
@@ -612,6 +677,10 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
     if (P.ring_chunks < kMinRingChunks || P.n_head_slots > lo.head_slots ||
         h->plan.instrs.size() * sizeof(Instr) > lo.qoff - lo.instrs)
         return give_up(MK_E_UNSUPPORTED);
+    if (rt->mode == MK_MODE_MEGAKERNEL && max_wave_span(cfg, rt) > P.ring_chunks) {
+        h->last_error = "a compute wave's row batch does not fit the LDS ring";
+        return give_up(MK_E_UNSUPPORTED);
+    }
     if (rt->trace) {
         P.trace = (uint32_t*)(ws + lo.trace);
         P.trace_stride = (uint32_t)(lo.trace_bytes / ((size_t)n_cu * kTraceWords * 4));
@@ -622,6 +691,16 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
         const hipError_t pe = prepare_conventional(P);
         if (pe != hipSuccess) {
             hip_fail(h, pe, "prepare_conventional");
+            return give_up(MK_E_HIP);
+        }
+    } else {
+        const hipError_t pe = prepare_megakernel(P);
+        if (pe == hipErrorInvalidConfiguration) {
+            h->last_error = "one workgroup of the persistent kernel does not fit a compute unit";
+            return give_up(MK_E_UNSUPPORTED);
+        }
+        if (pe != hipSuccess) {
+            hip_fail(h, pe, "prepare_megakernel");
             return give_up(MK_E_HIP);
         }
     }
@@ -680,6 +759,13 @@ mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_ru
     }
     *out = h;
     return MK_OK;
+}
+
+extern "C" {
+
+mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_runtime_config* rt, void* d_workspace,
+                    size_t workspace_bytes, void* d_kv, size_t kv_bytes, void* stream, mk_handle** out) {
+    return create_impl(cfg, w, rt, d_workspace, workspace_bytes, d_kv, kv_bytes, stream, out, -1);
 }
 
 mk_status mk_kv_layout(const mk_handle* h, int64_t strides_out[5]) {
@@ -765,6 +851,8 @@ static mk_status run_step(mk_handle* h, const int32_t* tok_in, int32_t stride, i
         HIPCHK(h, hipGraphLaunch(h->gexec, st));
     }
     for (int b = 0; b < h->rt.max_batch; ++b) h->ctx[b] += 1;
+    h->last_stream = st;
+    h->used = true;
     return MK_OK;
 }
 
@@ -819,6 +907,9 @@ mk_status mk_reset(mk_handle* h, void* stream) {
     DevState ds;
     HIPCHK(h, hipMemcpy(&ds, h->ws + h->lo.state, sizeof(ds), hipMemcpyDeviceToHost));
     for (int b = 0; b < h->rt.max_batch; ++b) h->ctx[b] = ds.ctx_len[b];
+    // a handle without the host-mapped error word learns of a device error here
+    const mk_status cleared = (!h->host_err && ds.error) ? (ds.error == DERR_NAN ? MK_E_DEVICE_NAN : MK_E_DEVICE_TIMEOUT)
+                                                         : MK_OK;
     // tickets back to zero; the step counter (tag base) keeps counting, so values
     // left by an aborted step never match a later step's tags
     HIPCHK(h, hipMemsetAsync(h->ws + h->lo.tickets, 0,
@@ -829,7 +920,7 @@ mk_status mk_reset(mk_handle* h, void* stream) {
     h->latched = false;
     h->latched_status = MK_OK;
     h->last_error.clear();
-    return MK_OK;
+    return cleared;
 }
 
 mk_status mk_debug_inject(mk_handle* h, int32_t fault, int32_t arg) {
@@ -863,6 +954,10 @@ int32_t mk_kernels_per_step(const mk_handle* h) {
 
 mk_status mk_destroy(mk_handle* h) {
     if (!h) return MK_E_INVALID;
+    // work enqueued on the handle's stream may still write the pinned error word
+    // or replay the graph: let it finish before either is freed
+    (void)hipStreamSynchronize(h->stream);
+    if (h->used && h->last_stream != h->stream) (void)hipStreamSynchronize(h->last_stream);
     if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
     if (h->graph) (void)hipGraphDestroy(h->graph);
     if (h->host_err) (void)hipHostFree(h->host_err);

@@ -46,6 +46,9 @@ struct Ctl {
     // by compute wave 0 for the loaders (moe_seq = queue index + 1 once valid)
     uint32_t moe_seq, moe_n;
     uint8_t moe_list[kMaxExperts + 1];  // expert-table slots, shared first, then ascending experts
+    // LM head: queue index + 1 once the final-norm input is staged and its statistics
+    // are in ss (published by compute wave 0 for the loader waves, which join the head)
+    uint32_t head_seq;
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -88,9 +91,9 @@ template <int HD, bool MF = false>
 __device__ __forceinline__ uint32_t instr_bytes(const Params& P, const Instr& in, const int32_t* ctx) {
     if (MF && is_gemv(in.op)) return mfma_geo<HD>(P, in).chunks() * kChunk;
     switch (in.op) {
+        case OP_HEAD: return 0;  // all eight waves stream the LM head into registers (head_direct)
         case OP_QKV:
-        case OP_ROUTE:
-        case OP_HEAD: return align_chunk(in.count * (uint32_t)P.d * 2u);
+        case OP_ROUTE: return align_chunk(in.count * (uint32_t)P.d * 2u);
         case OP_O: return align_chunk(in.count * (uint32_t)(P.Hq * HD) * 2u);
         case OP_GATEUP: return align_chunk(2u * in.count * (uint32_t)P.d * 2u);
         case OP_DOWN: return align_chunk(in.count * (uint32_t)P.F * 2u);
@@ -105,7 +108,9 @@ __device__ __forceinline__ uint32_t instr_bytes(const Params& P, const Instr& in
 
 // Global source address of this lane's 16 bytes of chunk c of instruction `in`
 // (rows packed back to back; lanes past the end re-read the first row).  Used
-// for rows that are not a whole number of chunks.
+// for rows that are not a whole number of chunks.  (No kind streams the LM head
+// through the ring: the VALU and MoE kernels read it into registers, the
+// matrix-core kernel lays it out tile-major.)
 template <int HD>
 __device__ __forceinline__ const char* chunk_src(const Params& P, const Instr& in, const DevLayer& Lw, uint32_t c,
                                                  const int32_t* ctx) {
@@ -140,12 +145,11 @@ __device__ __forceinline__ const char* chunk_src(const Params& P, const Instr& i
             if (r >= in.count) { r = 0; col = 0; }
             return (const char*)(Lw.w_down + (size_t)(in.begin + r) * P.F) + col;
         }
-        case OP_HEAD:
         case OP_ROUTE: {
             const uint32_t rb = (uint32_t)P.d * 2u;
             uint32_t r = off / rb, col = off - r * rb;
             if (r >= in.count) { r = 0; col = 0; }
-            return (const char*)((in.op == OP_HEAD ? P.head : Lw.router) + (size_t)(in.begin + r) * P.d) + col;
+            return (const char*)(Lw.router + (size_t)(in.begin + r) * P.d) + col;
         }
         case OP_ATTN: {
             constexpr uint32_t rbkv = HD * 2u;
@@ -264,7 +268,7 @@ __device__ __forceinline__ bool setup_stream(const Params& P, const Instr& in, c
             S.end1 = S.end0 + (k1 - k0) * cpr;
             return true;
         }
-        case OP_O: rb = (uint32_t)(P.Hq * HD) * 2u; S.p0 = (const char*)Lw.wo + (size_t)in.begin * rb; break;
+        case OP_O: rb = (uint32_t)(P.Hq * HD) * 2u; S.p0 = (const char*)uniform_p(Lw.wo) + (size_t)in.begin * rb; break;
         case OP_DOWN:
             rb = (uint32_t)P.F * 2u;
             S.p0 = (const char*)Lw.w_down + (size_t)in.begin * rb;
@@ -278,8 +282,7 @@ __device__ __forceinline__ bool setup_stream(const Params& P, const Instr& in, c
                 return (S.slice_bytes & (kChunk - 1u)) == 0 && ((S.slice_bytes / kChunk) & (S.slice_bytes / kChunk - 1u)) == 0;
             }
             break;
-        case OP_HEAD: rb = (uint32_t)P.d * 2u; S.p0 = (const char*)P.head + (size_t)in.begin * rb; break;
-        case OP_ROUTE: rb = (uint32_t)P.d * 2u; S.p0 = (const char*)Lw.router + (size_t)in.begin * rb; break;
+        case OP_ROUTE: rb = (uint32_t)P.d * 2u; S.p0 = (const char*)uniform_p(Lw.router) + (size_t)in.begin * rb; break;
         case OP_GATEUP: {
             rb = (uint32_t)P.d * 2u;
             const uint32_t cpr = rb / kChunk;
@@ -358,9 +361,11 @@ __device__ __forceinline__ uint32_t landed_prefix(const Ctl* ctl) {
     return m;
 }
 
+// Returns the queue index of the LM-head instruction when this kernel kind has
+// the loader waves join it (head_direct), else q1.
 template <int B, int HD, bool MF, bool MOE>
-__device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* ring, int k, uint32_t q0, uint32_t q1,
-                                            const int32_t* ctx) {
+__device__ __forceinline__ uint32_t loader_wave(const Params& P, Ctl* ctl, char* ring, int k, uint32_t q0, uint32_t q1,
+                                                const int32_t* ctx) {
     constexpr int LAG = loader_lag<B>();
     const uint32_t N = P.ring_chunks;
     const uint32_t NL = (uint32_t)kLoaderWaves;
@@ -448,8 +453,13 @@ __device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* rin
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         return true;
     };
+    uint32_t head_at = q1;
     for (uint32_t i = q0; i < q1 && !stop; ++i) {
         const Instr in = ld_const(P.instrs + i);
+        if (!MF && in.op == OP_HEAD) {  // the last instruction of every queue
+            head_at = i;
+            break;
+        }
         uint32_t nch;
         if (MOE && is_moe_expert(in.op)) {
             if (!wait_moe(i + 1u)) {
@@ -612,10 +622,12 @@ __device__ __forceinline__ void loader_wave(const Params& P, Ctl* ctl, char* rin
     wait_vmcnt<0>();
     landed = issued;
     lds_st(&ctl->landed[k], 0xFFFFFFFFu);  // every chunk of this loader is resident
+    const uint32_t last = head_at < q1 ? head_at : q1 - 1;
     if (k == 0 && P.trace && q1 > q0 && lane_id() == 0) {
-        P.trace[((size_t)blockIdx.x * P.trace_stride + (q1 - 1 - q0)) * kTraceWords + 5] = (uint32_t)now_ticks();
-        P.trace[((size_t)blockIdx.x * P.trace_stride + (q1 - 1 - q0)) * kTraceWords + 7] = stall;
+        P.trace[((size_t)blockIdx.x * P.trace_stride + (last - q0)) * kTraceWords + 5] = (uint32_t)now_ticks();
+        P.trace[((size_t)blockIdx.x * P.trace_stride + (last - q0)) * kTraceWords + 7] = stall;
     }
+    return stop ? q1 : head_at;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -678,6 +690,20 @@ struct CwBarrier {
     }
 };
 
+// A wave leaving a region of the stream (one GEMV over a column slice, one
+// expert's rows) moves its mark to the region's end before any barrier that
+// follows inside the same instruction: it needs nothing before it again.
+// Without this a wave that had no rows in the region (fewer row batches than
+// waves) would keep its mark at the region's start, and since the loader only
+// reuses ring slots below the smallest mark, the waves with rows would wait for
+// chunks the loader may not issue once the instruction is longer than the ring.
+// The chunk holding the end byte stays protected.  (Called by the instruction
+// code, not inside the GEMV loops: there the extra live values pushed the VALU
+// kernel past its 256 registers into scratch.)
+__device__ __forceinline__ void release_region(Ctl* ctl, int wave, uint32_t end_byte) {
+    set_consumed(ctl, wave, end_byte / kChunk);
+}
+
 // Ring byte address of stream byte x.
 __device__ __forceinline__ uint32_t ring_addr(uint32_t x, uint32_t nchunks) {
     return ((x >> 10) % nchunks) * kChunk + (x & (kChunk - 1u));
@@ -711,8 +737,6 @@ __device__ __forceinline__ bool gemv_ring(const Params& P, Ctl* ctl, const char*
 // Each lane still accumulates its pieces in ascending order, so every row's value
 // is the one rows_dot gives.  R = 2 (GATEUP): the wave takes the gate row, then
 // the up row of its pair.
-constexpr uint32_t kSegBytes = 8192;     // measured: 2 KB and 16 KB segments were slower, 4 KB too
-constexpr uint32_t kSegRowBytes = 8192;  // rows at least this long, at batch 1 and 2 (4 KB rows: slower)
 template <int B, int R, class Epi>
 __device__ __forceinline__ bool gemv_ring_seg(const Params& P, Ctl* ctl, const char* ring, uint32_t S, uint32_t rb,
                                               uint32_t nrows, const XLds& x, int wave, uint32_t& lw, Epi& epi) {
@@ -756,16 +780,128 @@ template <int B, class Epi>
 __device__ __forceinline__ bool gemv_ring_auto(const Params& P, Ctl* ctl, const char* ring, uint32_t S, uint32_t rb,
                                                uint32_t nrows, const XLds& x, int wave, uint32_t& lw, Epi& epi,
                                                bool pairs) {
-    if constexpr (B <= 2) {
-        if (rb >= kSegRowBytes) {
-            if (pairs) return gemv_ring_seg<B, 2>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
-            return gemv_ring_seg<B, 1>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
+    if (segmented_rows(rb, B)) {
+        if (pairs) return gemv_ring_seg<B, 2>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
+        return gemv_ring_seg<B, 1>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
+    }
+    const int R = ring_batch_rows(rb, B, pairs);
+    if (R == 4) return gemv_ring<B, 4>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
+    if (R == 2) return gemv_ring<B, 2>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
+    return gemv_ring<B, 1>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
+}
+
+// ------------------------------------------------------------------------------------------------
+// LM head, streamed straight into registers by all eight waves of the CU (the
+// four loader waves join the four compute waves).  The head has no dependency
+// edge inside it, so the LDS ring, which exists to keep the weight stream going
+// while instructions wait on other compute units, buys nothing here, and its
+// coupling of loader and consumers capped the head near 4.5 TB/s.  Wave hw of 8
+// takes rows hw, hw + 8, ... of the instruction in 4 KB segments; lane l loads
+// pieces l, l + 64, l + 128, l + 192 of each segment with non-temporal loads,
+// four segments ahead at batch 1 (two at batch 2-4, one at batch 8, where the
+// registers hold the batch's accumulators and activations), so 128 KB (64, 32
+// KB) stream per CU at once.  Each lane accumulates
+// its pieces in ascending order and wave_total reduces in its fixed tree: the
+// logits are bit for bit those of the ring GEMV (rows_dot).  `ready()` supplies
+// the RMSNorm scales once the final-norm input is staged: the compute waves
+// stage it there, the loader waves wait for it.  With PRE the first segments are
+// issued before ready() (the loader waves, which arrive early and wait on a
+// flag); the compute waves issue after their staging, whose registers would
+// otherwise sit next to the loads in flight and spill.  One instantiation serves
+// every hidden size (segments per row at run time): one per size pushed the
+// persistent kernel past its registers.
+// ------------------------------------------------------------------------------------------------
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt16(const uint4* p) {
+    const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int B, bool PRE, class Ready>
+__device__ __forceinline__ bool head_direct(const Params& P, const StepArgs& A, const float* xs, const Instr& in, int hw,
+                                            Spin& spin, Ready& ready) {
+    constexpr int NW = kComputeWaves + kLoaderWaves;
+    constexpr int G = 4;  // pieces per lane of one 4 KB segment of a row
+    constexpr int D = B == 1 ? 4 : B <= 4 ? 2 : 1;  // segments in flight per wave (fewer next to B accumulators)
+    const uint32_t d = (uint32_t)P.d, np = d >> 3, lane = (uint32_t)lane_id();
+    const uint32_t nseg = (np + 64u * G - 1u) / (64u * G);  // segments per row
+    const uint32_t nrow = in.count > (uint32_t)hw ? (in.count - (uint32_t)hw + NW - 1u) / NW : 0u;
+    const uint32_t nu = nrow * nseg;                          // this wave's (row, segment) units
+    const uint4* base = (const uint4*)(P.head + ((size_t)in.begin + (uint32_t)hw) * d);
+    const size_t row_stride = (size_t)NW * np;  // uint4 between this wave's consecutive rows
+    uint4 w[D][G];
+    // unit u = (row t, segment sg): pieces sg * 64 G + 64 g + lane of the row
+    auto issue = [&](uint32_t u, uint4 (&dst)[G]) {
+        const uint32_t t = u / nseg, sg = u - t * nseg;
+        const uint4* rp = base + (size_t)t * row_stride;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const uint32_t p = sg * (64u * G) + 64u * (uint32_t)g + lane;
+            dst[g] = ld_nt16(rp + (p < np ? p : 0u));  // lanes past a short row re-read its start
+        }
+    };
+    float r[B];
+    if (!PRE && !ready(r)) return false;
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        if ((uint32_t)i < nu) issue((uint32_t)i, w[i]);
+    if (PRE && !ready(r)) return false;
+    const XLds x{xs, d};
+    float best_v[B], acc[B];
+    int32_t best_i[B];
+    bool nan_seen = false;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        best_v[b] = -INFINITY;
+        best_i[b] = 0x7FFFFFFF;
+        acc[b] = 0.f;
+    }
+    for (uint32_t u0 = 0; u0 < nu; u0 += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {  // (no break: w must stay register-indexed)
+            const uint32_t u = u0 + (uint32_t)i;
+            if (u < nu) {
+                uint4 cur[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) cur[g] = w[i][g];
+                if (u + D < nu) issue(u + D, w[i]);
+                const uint32_t t = u / nseg, sg = u - t * nseg;
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const uint32_t p = sg * (64u * G) + 64u * (uint32_t)g + lane;
+                    if (p < np) {
+#pragma unroll
+                        for (int b = 0; b < B; ++b) {
+                            float4 xa, xb;
+                            x.piece(b, p, xa, xb);
+                            acc[b] = dot8(cur[g], xa, xb, acc[b]);
+                        }
+                    }
+                }
+                if (sg + 1u == nseg) {  // the row is complete
+                    wave_total_n<B>(acc);
+                    const int32_t row = (int32_t)(in.begin + (uint32_t)hw + t * NW);
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        const float v = acc[b] * r[b];
+                        if (v != v) nan_seen = true;
+                        if (head_better(v, row, best_v[b], best_i[b])) {
+                            best_v[b] = v;
+                            best_i[b] = row;
+                        }
+                    }
+                    if (lane < B) A.logits[(size_t)lane * P.V + row] = pick<B>(acc, lane) * pick<B>(r, lane);
+#pragma unroll
+                    for (int b = 0; b < B; ++b) acc[b] = 0.f;
+                }
+            }
         }
     }
-    const int R = rows_per_batch(rb, B);
-    if (R >= 4) return gemv_ring<B, 4>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
-    if (R == 2 || pairs) return gemv_ring<B, 2>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
-    return gemv_ring<B, 1>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
+    if (nan_seen) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) best_v[b] = __int_as_float(0x7FC00000);
+    }
+    return head_publish<B>(P, A, in.slot * (uint32_t)NW + (uint32_t)hw, best_v, best_i, spin);
 }
 
 // Matrix-core GEMV over one column slice of an instruction whose tile-major
@@ -882,9 +1018,11 @@ __device__ __forceinline__ bool gemv_mfma_ring(const Params& P, Ctl* ctl, const 
         if (m > 1) red_store<B, PRT>(red, wave, 1, combine_parts<PRT>(d1));
         if (m > 2) red_store<B, PRT>(red, wave, 2, combine_parts<PRT>(d2));
         if (m > 3) red_store<B, PRT>(red, wave, 3, combine_parts<PRT>(d3));
+        release_region(ctl, wave, (c0 + g.slice_chunks()) * kChunk);  // before the barrier: no wave may hold the slice
         if (!barrier()) return false;
         if ((uint32_t)wave < m) epi(4u * g.G4 + (uint32_t)wave, red_sum<B, PRT>(red, (uint32_t)wave));
     }
+    release_region(ctl, wave, (c0 + g.slice_chunks()) * kChunk);
     return true;
 }
 
@@ -1253,6 +1391,7 @@ __device__ __forceinline__ bool moe_edown(const Params& P, const StepArgs& A, Ct
         };
         if (!gemv_ring_auto<B>(P, ctl, ring, S + a * cnt * rb, rb, cnt, XLds{xs, Fe}, wave, land_wait, epi, false))
             return false;
+        release_region(ctl, wave, S + (a + 1u) * cnt * rb);
     }
     if (!barrier()) return false;
     const uint32_t tag_out = phase_tag(A.tag0, layer, 4);
@@ -1294,8 +1433,13 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
     uint32_t S = 0, k = 0;
     Spin spin(&P, &ctl->abort);
     CwBarrier barrier{ctl, &P, 0u};
+    uint32_t head_qi = q1;
     for (uint32_t qi = q0; qi < q1; ++qi, ++k) {
         const Instr in = ld_const(P.instrs + qi);
+        if (!MF && in.op == OP_HEAD) {  // the last instruction of every queue: after the loop
+            head_qi = qi;
+            break;
+        }
         uint32_t bytes = instr_bytes<HD, MF>(P, in, ctx);  // MoE expert instructions set it once routed
         uint32_t* tr =
             (P.trace && wave == 0) ? P.trace + ((size_t)blockIdx.x * P.trace_stride + k) * kTraceWords : nullptr;
@@ -1323,12 +1467,11 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                 break;
             case OP_QKV:
             case OP_GATEUP:
-            case OP_ROUTE:
-            case OP_HEAD: {
-                const uint16_t* gain = in.op == OP_QKV ? Lw.attn_norm : in.op == OP_HEAD ? P.final_norm : Lw.mlp_norm;
-                const uint32_t tag_in = in.op == OP_QKV    ? phase_tag(A.tag0, layer - 1, 4)
-                                        : in.op == OP_HEAD ? phase_tag(A.tag0, P.L - 1, 4)
-                                                           : phase_tag(A.tag0, layer, 2);
+            case OP_ROUTE: {
+                // (the gain pointer is chosen on the scalar unit: a plain select of the two
+                // loaded pointers was lowered through a private array, i.e. scratch memory)
+                const uint16_t* gain = uniform_p(in.op == OP_QKV ? Lw.attn_norm : Lw.mlp_norm);
+                const uint32_t tag_in = in.op == OP_QKV ? phase_tag(A.tag0, layer - 1, 4) : phase_tag(A.tag0, layer, 2);
                 const uint32_t d = (uint32_t)P.d;
                 float ss[B];
 #pragma unroll
@@ -1485,6 +1628,7 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                     };
                     ok = gemv_ring_auto<B>(P, ctl, ring, S + ks * in.count * Ks * 2u, Ks * 2u, in.count, x, wave,
                                            land_wait, epi, false);
+                    if (ns > 1) release_region(ctl, wave, S + (ks + 1u) * in.count * Ks * 2u);
                 }
                 break;
             }
@@ -1502,6 +1646,51 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
         set_consumed(ctl, wave, S / kChunk);
         if (tr && lane == 0) tr[4] = (uint32_t)now_ticks();
     }
+    if constexpr (!MF) {
+        // The LM head runs outside the instruction loop: its row loads are issued
+        // ahead, and inside the loop the compiler would have to assume some may
+        // still be in flight at the back edge, guarding every later write of their
+        // registers (in the GEMV row loops) with a vmcnt wait.
+        if (head_qi < q1) {
+            const Instr in = ld_const(P.instrs + head_qi);
+            const uint32_t qi = head_qi;
+            uint32_t* tr =
+                (P.trace && wave == 0) ? P.trace + ((size_t)blockIdx.x * P.trace_stride + k) * kTraceWords : nullptr;
+            if (tr && lane == 0) {
+                tr[0] = (uint32_t)in.op | ((uint32_t)in.layer << 16);
+                tr[1] = (uint32_t)now_ticks();
+            }
+            if (!barrier()) return;
+            if (tr && lane == 0) tr[8] = (uint32_t)now_ticks();
+            // stage the final-norm input, then publish it to the loader waves, which
+            // join the head
+            const uint32_t d = (uint32_t)P.d;
+            auto ready = [&](float (&r)[B]) -> bool {
+                float ss[B];
+#pragma unroll
+                for (int b = 0; b < B; ++b) ss[b] = 0.f;
+                const StageSeg sg[1] = {{P.h, xs, P.final_norm, d, (uint32_t)B, d, d, phase_tag(A.tag0, P.L - 1, 4)}};
+                if (!stage_segs<stage_words<B>(), B, 1>(sg, wave, kComputeWaves, spin, ss)) return false;
+                wave_total_n<B>(ss);
+                if (lane == 0) {
+#pragma unroll
+                    for (int b = 0; b < B; ++b) ctl->ss[b][wave] = ss[b];
+                }
+                if (!barrier()) return false;
+#pragma unroll
+                for (int b = 0; b < B; ++b) r[b] = rms_scale(ctl->ss[b], kComputeWaves, P.d, P.eps);
+                if (wave == 0 && lane == 0) {
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                    lds_st(&ctl->head_seq, qi + 1u);
+                }
+                if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
+                return true;
+            };
+            const bool ok = head_direct<B, false>(P, A, xs, in, wave, spin, ready);
+            if (!ok || lds_ld(&ctl->abort)) return;
+            if (tr && lane == 0) tr[3] = tr[4] = (uint32_t)now_ticks();
+        }
+    }
 }
 
 template <int B, int HD, bool MF, bool MOE>
@@ -1518,12 +1707,48 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
         ctl.abort = 0;
         ctl.moe_seq = 0;
         ctl.moe_n = 0;
+        ctl.head_seq = 0;
     }
     if (threadIdx.x < kMaxBatch) ctl.ctx[threadIdx.x] = (int)threadIdx.x < B ? P.state->ctx_len[threadIdx.x] : 0;
     __syncthreads();
     const uint32_t q0 = ld_const(P.queue_off + blockIdx.x), q1 = ld_const(P.queue_off + blockIdx.x + 1);
     if (wave >= kComputeWaves) {
-        loader_wave<B, HD, MF, MOE>(P, &ctl, ring, wave - kComputeWaves, q0, q1, ctl.ctx);
+        const uint32_t hi = loader_wave<B, HD, MF, MOE>(P, &ctl, ring, wave - kComputeWaves, q0, q1, ctl.ctx);
+        if constexpr (!MF) {
+            if (hi < q1) {
+                // join the LM head once the compute waves have staged its input
+                const Instr in = ld_const(P.instrs + hi);
+                Spin spin(&P, &ctl.abort);
+                auto ready = [&](float (&r)[B]) -> bool {
+                    // Like the loaders' other waits this ends on the workgroup's own abort
+                    // flag or the watchdog, not on an error latched by an earlier step (it
+                    // spans most of the step, long enough to see one).  The loaders arrive
+                    // long before the compute waves, so the watchdog counts from the compute
+                    // waves' last barrier: it measures a lack of progress, not the step.
+                    uint64_t t0 = now_ticks();
+                    uint32_t polls = 0, seen = lds_ld(&ctl.bar);
+                    while (lds_ld(&ctl.head_seq) != hi + 1u) {
+                        if (lds_ld(&ctl.abort)) return false;
+                        if ((++polls & 255u) == 0) {
+                            const uint32_t b = lds_ld(&ctl.bar);
+                            if (b != seen) {
+                                seen = b;
+                                t0 = now_ticks();
+                            } else if (now_ticks() - t0 > P.spin_ticks) {
+                                raise_error_impl(P.state, P.host_err, &ctl.abort, DERR_TIMEOUT, 0xFFFFFFFBu, hi);
+                                return false;
+                            }
+                        }
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+                    for (int b = 0; b < B; ++b) r[b] = rms_scale(ctl.ss[b], kComputeWaves, P.d, P.eps);
+                    return true;
+                };
+                (void)head_direct<B, true>(P, A, xs, in, wave, spin, ready);
+            }
+        }
     } else {
         compute_wave<B, HD, MF, MOE>(P, A, &ctl, ring, xs, wave, q0, q1, ctl.ctx);
     }

@@ -524,15 +524,22 @@ __device__ __forceinline__ bool stage_segs(const StageSeg (&sg)[NS], int w, int 
     uint64_t va[K], vb[K];
     uint32_t ga[K], gb[K];
     issue(0u, va, ga);
+    bool ok = true;
     for (uint32_t p0 = 0;; p0 += 2u * per_pass) {
         issue(p0 + per_pass, vb, gb);
-        if (!finish(p0, va, ga)) return false;
+        if (!(ok = finish(p0, va, ga))) break;
         if (p0 + per_pass >= total) break;
         issue(p0 + 2u * per_pass, va, ga);
-        if (!finish(p0 + per_pass, vb, gb)) return false;
+        if (!(ok = finish(p0 + per_pass, vb, gb))) break;
         if (p0 + 2u * per_pass >= total) break;
     }
-    return true;
+    // The pass issued ahead of the last one is never read.  Retire it here: left
+    // pending, the compiler must assume loads into those registers may still be
+    // in flight wherever they are next written, and inside the GEMV row loops that
+    // follow it guards such writes with a vmcnt wait on every row batch, which
+    // then waits for the previous batch's write-through result stores as well.
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
+    return ok;
 }
 
 // Same from a bf16 row that needs no wait (the token embedding of layer 0);
@@ -630,13 +637,6 @@ __device__ __forceinline__ void rows_dot(const Rows& rows, int np, const X& x, f
     for (int i = 0; i < R; ++i)
 #pragma unroll
         for (int b = 0; b < B; ++b) out[i][b] = t[i * B + b];
-}
-
-// Rows of one compute wave's batch for a row of `rb` bytes: about 8 KB per wave.
-// From batch 4 on two rows share each x piece read from LDS (one row per batch
-// left the wave waiting on LDS reads of x).
-__host__ __device__ constexpr int rows_per_batch(uint32_t rb, int B = 1) {
-    return B >= 4 ? 2 : rb <= 2048u ? 4 : rb <= 4096u ? 2 : 1;
 }
 
 // a[i] for a per-lane i < B.  The empty asm between the selects keeps the chain

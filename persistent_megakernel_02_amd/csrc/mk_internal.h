@@ -82,6 +82,35 @@ __host__ __device__ constexpr int down_slices_for(int B, int F, bool mfma = fals
     return n;
 }
 
+// Rows of one compute wave's batch for a row of `rb` bytes: about 8 KB per wave.
+// From batch 4 on two rows share each x piece read from LDS (one row per batch
+// left the wave waiting on LDS reads of x).
+__host__ __device__ constexpr int rows_per_batch(uint32_t rb, int B = 1) {
+    return B >= 4 ? 2 : rb <= 2048u ? 4 : rb <= 4096u ? 2 : 1;
+}
+
+// Long rows at batch 1 and 2 stream through the ring in segments of kSegBytes
+// (measured: 2 KB and 16 KB segments were slower, 4 KB too; 4 KB rows segmented:
+// slower).
+constexpr uint32_t kSegBytes = 8192;
+constexpr uint32_t kSegRowBytes = 8192;
+__host__ __device__ constexpr bool segmented_rows(uint32_t rb, int B) { return B <= 2 && rb >= kSegRowBytes; }
+
+// Rows of a wave's batch in the persistent kernel's ring GEMV (1, 2 or 4); a
+// (gate, up) pair always shares one batch.
+__host__ __device__ constexpr int ring_batch_rows(uint32_t rb, int B, bool pairs) {
+    return rows_per_batch(rb, B) >= 4 ? 4 : (rows_per_batch(rb, B) == 2 || pairs) ? 2 : 1;
+}
+
+// Chunks of the ring one compute wave holds at most while it waits for a row
+// batch of `rb`-byte rows: from the chunk its mark names (the batch start) to the
+// chunk holding the batch end.  Rows are packed back to back, so a batch may
+// start inside a chunk.
+__host__ __device__ constexpr uint32_t ring_batch_span(uint32_t rb, int B, bool pairs) {
+    return segmented_rows(rb, B) ? kSegBytes / kChunk + 1u
+                                 : ((uint32_t)ring_batch_rows(rb, B, pairs) * rb + kChunk - 1u) / kChunk + 1u;
+}
+
 // LDS floats one attention item uses: raw q (G heads), k and v; rotated q; the new
 // K and V as bf16; the scores of every wave ([wave][position][kMaxGroup]); the wave
 // partials ([wave][G]: maximum, sum, four 16-lane rows of HD); when the item

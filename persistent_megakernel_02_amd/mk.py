@@ -8,8 +8,11 @@ is missing the import raises.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import sys
+import weakref
 from typing import Dict, List, Optional, Sequence
 
 import numpy as np
@@ -19,13 +22,13 @@ LIB_PATH = os.path.join(_HERE, "libmk.so")
 TRACE_WORDS = 12  # uint32 per trace record (include/mk.h, mk_read_trace)
 
 MK_OK, MK_E_INVALID, MK_E_UNSUPPORTED, MK_E_CAPACITY, MK_E_HIP, MK_E_DEVICE_TIMEOUT, MK_E_STATE, MK_E_DEVICE_NAN = range(8)
-MK_MODE_MEGAKERNEL, MK_MODE_GRAPH = 0, 1
+MK_MODE_MEGAKERNEL, MK_MODE_GRAPH, MK_MODE_ENV = 0, 1, 2
 MK_GEMV_AUTO, MK_GEMV_VALU, MK_GEMV_MFMA = 0, 1, 2
 
 EXPORTS = ["mk_query_sizes", "mk_create", "mk_kv_layout", "mk_prefill", "mk_set_context_len", "mk_decode_step",
            "mk_get_context_len", "mk_reset", "mk_debug_inject", "mk_status_string", "mk_last_error",
            "mk_plan_inspect", "mk_kernels_per_step", "mk_destroy", "mk_bench_stream_read", "mk_bench_copy",
-           "mk_bench_sync", "mk_read_trace", "mk_bench_lds_stream", "mk_bench_pingpong", "mk_bench_edge", "mk_bench_lds_contention"]
+           "mk_bench_sync", "mk_read_trace", "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap"]
 
 
 class mk_model_config(ctypes.Structure):
@@ -54,6 +57,23 @@ class mk_runtime_config(ctypes.Structure):
 
 
 _lib = None
+
+# Handles still open when the interpreter exits are destroyed from an atexit hook:
+# Python runs it before it tears down modules and before the HIP runtime's own
+# exit handlers, so mk_destroy still has a live runtime.  A Decoder collected
+# during interpreter finalisation makes no library call at all.
+_live: "weakref.WeakSet[Decoder]" = weakref.WeakSet()
+
+
+def _close_live_handles() -> None:
+    for d in list(_live):
+        try:
+            d.close()
+        except Exception:
+            pass
+
+
+atexit.register(_close_live_handles)
 
 
 def lib():
@@ -89,12 +109,12 @@ def lib():
         L.mk_bench_sync.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
         L.mk_bench_pingpong.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
         L.mk_bench_edge.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, sz, vp, vp, vp]
-        L.mk_bench_lds_contention.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, sz, vp, vp]
         L.mk_read_trace.argtypes = [vp, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(i32)]
-        L.mk_bench_lds_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, sz, ctypes.c_int, vp, vp]
+        L.mk_bench_graph_gap.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ctypes.POINTER(ctypes.c_float), vp]
         for n in ("mk_query_sizes", "mk_create", "mk_kv_layout", "mk_prefill", "mk_set_context_len",
                   "mk_get_context_len", "mk_decode_step", "mk_reset", "mk_debug_inject", "mk_plan_inspect",
-                  "mk_destroy", "mk_bench_stream_read", "mk_bench_copy", "mk_bench_sync", "mk_read_trace", "mk_bench_lds_stream", "mk_bench_pingpong", "mk_bench_edge", "mk_bench_lds_contention"):
+                  "mk_destroy", "mk_bench_stream_read", "mk_bench_copy", "mk_bench_sync", "mk_read_trace",
+                  "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -136,7 +156,7 @@ def mk_query_sizes(cfg: mk_model_config, rt: mk_runtime_config):
 
 def mk_plan_inspect(cfg: mk_model_config, rt: mk_runtime_config, num_cus: int):
     keys = ["cus", "instructions", "ring_chunks", "max_per_cu", "weight_bytes", "verify", "attn_splits", "phases",
-            "x_bytes", "head_instructions", "gemv_kind", "attn_hsplit"]
+            "x_bytes", "head_instructions", "gemv_kind", "attn_hsplit", "max_wave_span"]
     out = (ctypes.c_int64 * len(keys))()
     st = lib().mk_plan_inspect(ctypes.byref(cfg), ctypes.byref(rt), num_cus, out, len(keys))
     return st, dict(zip(keys, list(out)))
@@ -195,15 +215,17 @@ class Decoder:
         w.final_norm = dw["final_norm"].data_ptr()
         w.layers = layers
         self._w = w
-        self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
         self.kv = torch.empty(kv, dtype=torch.uint8, device=self.device)
         self.stream = torch.cuda.current_stream(self.device)
         h = ctypes.c_void_p()
-        st = lib().mk_create(ctypes.byref(self._c), ctypes.byref(w), ctypes.byref(self._rt), self.workspace.data_ptr(),
-                             ws, self.kv.data_ptr(), kv, self.stream.cuda_stream, ctypes.byref(h))
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
+        st = lib().mk_create(ctypes.byref(self._c), ctypes.byref(w), ctypes.byref(self._rt),
+                             self.workspace.data_ptr(), ws, self.kv.data_ptr(), kv, self.stream.cuda_stream,
+                             ctypes.byref(h))
         if st != MK_OK:
             raise MKError(st, "mk_create")
         self.h = h
+        _live.add(self)
         self.tok = torch.zeros(max_batch, dtype=torch.int32, device=self.device)
         self.logits = torch.empty((max_batch, cfg.vocab), dtype=torch.float32, device=self.device)
 
@@ -274,8 +296,12 @@ class Decoder:
         if getattr(self, "h", None):
             lib().mk_destroy(self.h)
             self.h = None
+        _live.discard(self)
 
-    def __del__(self):
+    def __del__(self, _finalizing=sys.is_finalizing):
+        # (bound at definition: module globals such as `sys` may already be None here)
+        if _finalizing():
+            return  # the atexit hook has closed every live handle already
         try:
             self.close()
         except Exception:

@@ -223,3 +223,75 @@ def test_moe_schedule_verifies(cfg, batch, cus):
 def test_plan_inspect_rejects_bad_cu_count():
     assert mk.mk_plan_inspect(mk.model_config(I.TINY), rt(), 0)[0] == mk.MK_E_INVALID
     assert mk.mk_plan_inspect(mk.model_config(I.TINY), rt(), 5000)[0] == mk.MK_E_INVALID
+
+
+def _expected_span(cfg, batch, mfma):
+    """Ring chunks one compute wave holds at most, written out from the kernel's
+    batch rules: rows of <= 2 KB go four to a batch, <= 4 KB two, longer one (two
+    rows from batch 4 on); a (gate, up) pair shares a batch; rows of >= 8 KB at
+    batch 1-2 stream in 8 KB segments; +1 chunk for a batch starting inside a
+    chunk; a matrix-core unit is 8 chunks; an attention block is its RoPE chunk
+    and 32 groups of a K and a V chunk."""
+    def batch_span(rb, pairs):
+        if batch <= 2 and rb >= 8192:
+            return 8 + 1
+        r = 2 if batch >= 4 else (4 if rb <= 2048 else 2 if rb <= 4096 else 1)
+        if pairs:
+            r = max(r, 2)
+        return -(-(r * rb) // 1024) + 1
+    span = 1 + 2 * 32
+    if mfma:
+        return max(span, 8)
+    d2 = 2 * cfg.hidden
+    spans = [batch_span(d2, False), batch_span(2 * cfg.n_q_heads * cfg.head_dim, False), batch_span(d2, True)]
+    if cfg.n_experts:
+        spans.append(batch_span(2 * cfg.expert_ffn, False))
+    else:
+        ns = 1
+        while batch * (cfg.ffn // ns) * 4 > 64 * 1024 and ns < 64:
+            ns *= 2
+        spans.append(batch_span(2 * (cfg.ffn // ns), False))
+    return max([span] + spans)
+
+
+@pytest.mark.parametrize("cfg", [I.TINY, I.LLAMA_1B, I.LLAMA_8B, I.MOE,
+                                 I.replace(I.TINY, name="wide-ffn", ffn=4096)], ids=lambda c: c.name)
+@pytest.mark.parametrize("batch", [1, 2, 4, 8])
+@pytest.mark.parametrize("cus", [1, 7, 37, 80, 256, 304])
+@pytest.mark.parametrize("kind", [mk.MK_GEMV_VALU, mk.MK_GEMV_MFMA], ids=["valu", "mfma"])
+def test_ring_span_fits_every_supported_plan(cfg, batch, cus, kind):
+    """Deadlock freedom of the weight ring: the loader may write a chunk only
+    within ring_chunks of the smallest compute-wave mark, and a wave waits for
+    its whole row batch (or segment, matrix-core unit, attention block) with its
+    mark at the batch start, so that stretch must fit the ring.  Every plan that
+    the library accepts satisfies it, and the library reports the stretch."""
+    st, info = mk.mk_plan_inspect(mk.model_config(cfg), mk.runtime_config(batch, 200, gemv_kind=kind), cus)
+    if st != mk.MK_OK:
+        assert st == mk.MK_E_UNSUPPORTED
+        return
+    assert info["max_wave_span"] == _expected_span(cfg, batch, info["gemv_kind"] == mk.MK_GEMV_MFMA)
+    assert info["max_wave_span"] <= info["ring_chunks"]
+
+
+def test_dense_persistent_kernels_use_no_scratch():
+    """The dense VALU persistent kernel (the headline path) keeps its values in
+    registers at every batch and head size: a spill to scratch memory puts
+    global-memory traffic (and vmcnt waits) inside the inner loops, and one did
+    cost 14 % of the 1B batch-1 step.  The budget is 256 VGPRs per wave (two waves
+    per SIMD); the build records what the compiler allocated.  The matrix-core
+    and MoE kinds are listed with their scratch bytes (known spills at batch >= 2)."""
+    import json
+
+    from persistent_megakernel_02_amd import _build
+
+    if not os.path.exists(_build.RESOURCES):
+        pytest.skip("library built without the resource report")
+    res = json.load(open(_build.RESOURCES))
+    mega = {k: v for k, v in res.items() if "mk_megakernel" in k}
+    assert len(mega) == 24, sorted(mega)  # 3 kinds x 4 batches x 2 head sizes
+    assert all(v["vgpr"] <= 256 and v["occupancy"] >= 2 for v in mega.values())
+    dense = {k: v for k, v in mega.items() if k.endswith("Lb0ELb0EEEvNS_6ParamsENS_8StepArgsE")}
+    assert len(dense) == 8
+    assert all(v["scratch"] == 0 for v in dense.values()), dense
+    print({k: v["scratch"] for k, v in mega.items() if v["scratch"]})
+
