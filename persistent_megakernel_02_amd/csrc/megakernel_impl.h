@@ -798,18 +798,15 @@ __device__ __forceinline__ bool gemv_ring_auto(const Params& P, Ctl* ctl, const 
 // coupling of loader and consumers capped the head near 4.5 TB/s.  Wave hw of 8
 // takes rows hw, hw + 8, ... of the instruction in 4 KB segments; lane l loads
 // pieces l, l + 64, l + 128, l + 192 of each segment with non-temporal loads,
-// four segments ahead at batch 1 (two at batch 2-4, one at batch 8, where the
+// four segments ahead at batch 1 (two at batch 2, one from batch 4, where the
 // registers hold the batch's accumulators and activations), so 128 KB (64, 32
 // KB) stream per CU at once.  Each lane accumulates
 // its pieces in ascending order and wave_total reduces in its fixed tree: the
-// logits are bit for bit those of the ring GEMV (rows_dot).  `ready()` supplies
-// the RMSNorm scales once the final-norm input is staged: the compute waves
-// stage it there, the loader waves wait for it.  With PRE the first segments are
-// issued before ready() (the loader waves, which arrive early and wait on a
-// flag); the compute waves issue after their staging, whose registers would
-// otherwise sit next to the loads in flight and spill.  One instantiation serves
-// every hidden size (segments per row at run time): one per size pushed the
-// persistent kernel past its registers.
+// logits are bit for bit those of the ring GEMV (rows_dot).  The first segments
+// are issued before `ready()`, which waits for the staged final-norm input and
+// supplies its RMSNorm scales.  One instantiation serves every hidden size
+// (segments per row at run time): one per size pushed the persistent kernel
+// past its registers.
 // ------------------------------------------------------------------------------------------------
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_nt16(const uint4* p) {
@@ -817,12 +814,12 @@ __device__ __forceinline__ uint4 ld_nt16(const uint4* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int B, bool PRE, class Ready>
+template <int B, class Ready>
 __device__ __forceinline__ bool head_direct(const Params& P, const StepArgs& A, const float* xs, const Instr& in, int hw,
                                             Spin& spin, Ready& ready) {
     constexpr int NW = kComputeWaves + kLoaderWaves;
     constexpr int G = 4;  // pieces per lane of one 4 KB segment of a row
-    constexpr int D = B == 1 ? 4 : B <= 4 ? 2 : 1;  // segments in flight per wave (fewer next to B accumulators)
+    constexpr int D = B == 1 ? 4 : B == 2 ? 2 : 1;  // segments in flight per wave (fewer next to B accumulators)
     const uint32_t d = (uint32_t)P.d, np = d >> 3, lane = (uint32_t)lane_id();
     const uint32_t nseg = (np + 64u * G - 1u) / (64u * G);  // segments per row
     const uint32_t nrow = in.count > (uint32_t)hw ? (in.count - (uint32_t)hw + NW - 1u) / NW : 0u;
@@ -841,11 +838,10 @@ __device__ __forceinline__ bool head_direct(const Params& P, const StepArgs& A, 
         }
     };
     float r[B];
-    if (!PRE && !ready(r)) return false;
 #pragma unroll
     for (int i = 0; i < D; ++i)
         if ((uint32_t)i < nu) issue((uint32_t)i, w[i]);
-    if (PRE && !ready(r)) return false;
+    if (!ready(r)) return false;
     const XLds x{xs, d};
     float best_v[B], acc[B];
     int32_t best_i[B];
@@ -1426,9 +1422,12 @@ __device__ __forceinline__ bool attn_instr(const Params& P, const StepArgs& A, C
                          kComputeWaves, spin, mark);
 }
 
+// Returns the queue index of the LM-head instruction once its input is staged
+// and published (the caller runs its rows: head_instr), or q1 (none in this kind,
+// or the workgroup stopped).
 template <int B, int HD, bool MF, bool MOE>
-__device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs, int wave,
-                             uint32_t q0, uint32_t q1, const int32_t* ctx) {
+__device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring,
+                                                 float* xs, int wave, uint32_t q0, uint32_t q1, const int32_t* ctx) {
     const int lane = lane_id();
     uint32_t S = 0, k = 0;
     Spin spin(&P, &ctl->abort);
@@ -1436,10 +1435,6 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
     uint32_t head_qi = q1;
     for (uint32_t qi = q0; qi < q1; ++qi, ++k) {
         const Instr in = ld_const(P.instrs + qi);
-        if (!MF && in.op == OP_HEAD) {  // the last instruction of every queue: after the loop
-            head_qi = qi;
-            break;
-        }
         uint32_t bytes = instr_bytes<HD, MF>(P, in, ctx);  // MoE expert instructions set it once routed
         uint32_t* tr =
             (P.trace && wave == 0) ? P.trace + ((size_t)blockIdx.x * P.trace_stride + k) * kTraceWords : nullptr;
@@ -1448,7 +1443,7 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
             tr[1] = (uint32_t)now_ticks();
         }
         // every wave has finished reading the previous instruction's staged inputs
-        if (!barrier()) return;
+        if (!barrier()) return q1;
         if (tr && lane == 0) tr[8] = (uint32_t)now_ticks();
         uint32_t land_wait = 0;
         const int layer = in.layer;
@@ -1467,11 +1462,15 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                 break;
             case OP_QKV:
             case OP_GATEUP:
-            case OP_ROUTE: {
-                // (the gain pointer is chosen on the scalar unit: a plain select of the two
+            case OP_ROUTE:
+            case OP_HEAD: {
+                // (the gain pointer is chosen on the scalar unit: a plain select of the
                 // loaded pointers was lowered through a private array, i.e. scratch memory)
-                const uint16_t* gain = uniform_p(in.op == OP_QKV ? Lw.attn_norm : Lw.mlp_norm);
-                const uint32_t tag_in = in.op == OP_QKV ? phase_tag(A.tag0, layer - 1, 4) : phase_tag(A.tag0, layer, 2);
+                const uint16_t* gain =
+                    uniform_p(in.op == OP_QKV ? Lw.attn_norm : in.op == OP_HEAD ? P.final_norm : Lw.mlp_norm);
+                const uint32_t tag_in = in.op == OP_QKV    ? phase_tag(A.tag0, layer - 1, 4)
+                                        : in.op == OP_HEAD ? phase_tag(A.tag0, P.L - 1, 4)
+                                                           : phase_tag(A.tag0, layer, 2);
                 const uint32_t d = (uint32_t)P.d;
                 float ss[B];
 #pragma unroll
@@ -1483,18 +1482,28 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                                    kComputeWaves, ss[b]);
                 } else {
                     const StageSeg sg[1] = {{P.h, xs, gain, d, (uint32_t)B, d, d, tag_in}};
-                    if (!stage_segs<stage_words<B>(), B, 1>(sg, wave, kComputeWaves, spin, ss)) return;
+                    if (!stage_segs<stage_words<B>(), B, 1>(sg, wave, kComputeWaves, spin, ss)) return q1;
                 }
                 wave_total_n<B>(ss);
                 if (lane == 0) {
 #pragma unroll
                     for (int b = 0; b < B; ++b) ctl->ss[b][wave] = ss[b];
                 }
-                if (!barrier()) return;
+                if (!barrier()) return q1;
                 float r[B];
 #pragma unroll
                 for (int b = 0; b < B; ++b) r[b] = rms_scale(ctl->ss[b], kComputeWaves, P.d, P.eps);
                 if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
+                if (in.op == OP_HEAD) {
+                    // the LM-head input is staged: publish it to the loader waves; all
+                    // eight waves stream the rows after the loop (head_instr)
+                    if (wave == 0 && lane == 0) {
+                        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                        lds_st(&ctl->head_seq, qi + 1u);
+                    }
+                    head_qi = qi;
+                    break;
+                }
                 const uint32_t rb = d * 2u;
                 const XLds x{xs, d};
                 const uint32_t nrows = in.op == OP_GATEUP ? 2u * in.count : in.count;
@@ -1535,40 +1544,6 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                         }
                     };
                     ok = gemv_ring_auto<B>(P, ctl, ring, S, rb, nrows, x, wave, land_wait, epi, true);
-                } else {
-                    float best_v[B];
-                    int32_t best_i[B];
-                    bool nan_seen = false;
-#pragma unroll
-                    for (int b = 0; b < B; ++b) {
-                        best_v[b] = -INFINITY;
-                        best_i[b] = 0x7FFFFFFF;
-                    }
-                    auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
-                        #pragma unroll
-                        for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i) {
-                            if (i >= nr) break;
-                            const int32_t row = (int32_t)(in.begin + r0 + i);
-#pragma unroll
-                            for (int b = 0; b < B; ++b) {
-                                const float v = res[i][b] * r[b];
-                                if (v != v) nan_seen = true;
-                                if (head_better(v, row, best_v[b], best_i[b])) {
-                                    best_v[b] = v;
-                                    best_i[b] = row;
-                                }
-                            }
-                            if (lane < B) A.logits[(size_t)lane * P.V + row] = pick<B>(res[i], lane) * pick<B>(r, lane);
-                        }
-                    };
-                    ok = gemv_ring_auto<B>(P, ctl, ring, S, rb, nrows, x, wave, land_wait, epi, false);
-                    if (ok) {
-                        if (nan_seen) {
-#pragma unroll
-                            for (int b = 0; b < B; ++b) best_v[b] = __int_as_float(0x7FC00000);
-                        }
-                        ok = head_publish<B>(P, A, in.slot * kComputeWaves + (uint32_t)wave, best_v, best_i, spin);
-                    }
                 }
                 break;
             }
@@ -1585,13 +1560,13 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                 float* hres = xs + B * Ks;         // [B][count] residual rows before this op
                 float* part = hres + B * in.count;  // [B][count] partial sums
                 for (uint32_t ks = 0; ks < ns && ok; ++ks) {
-                    if (ks > 0 && !barrier()) return;  // every wave is done with the previous slice
+                    if (ks > 0 && !barrier()) return q1;  // every wave is done with the previous slice
                     float ss[1] = {0.f};
                     const StageSeg sx = {(is_o ? P.attn : P.act) + ks * Ks, xs, nullptr, Ks, (uint32_t)B, K, Ks,
                                          tag_x};
                     if (ks > 0) {
                         const StageSeg sg[1] = {sx};
-                        if (!stage_segs<stage_words_wide<B>(), 1, 1>(sg, wave, kComputeWaves, spin, ss)) return;
+                        if (!stage_segs<stage_words_wide<B>(), 1, 1>(sg, wave, kComputeWaves, spin, ss)) return q1;
                     } else if (is_o && layer == 0) {
                         // the residual is the token embedding: no wait
 #pragma unroll
@@ -1599,13 +1574,13 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
                             stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * P.d + in.begin,
                                        in.count, hres + b * in.count, nullptr, wave, kComputeWaves, ss[0]);
                         const StageSeg sg[1] = {sx};
-                        if (!stage_segs<stage_words_wide<B>(), 1, 1>(sg, wave, kComputeWaves, spin, ss)) return;
+                        if (!stage_segs<stage_words_wide<B>(), 1, 1>(sg, wave, kComputeWaves, spin, ss)) return q1;
                     } else {
                         const StageSeg sg[2] = {sx, {P.h + in.begin, hres, nullptr, in.count, (uint32_t)B,
                                                      (uint32_t)P.d, in.count, tag_res}};
-                        if (!stage_segs<stage_words_wide<B>(), 1, 2>(sg, wave, kComputeWaves, spin, ss)) return;
+                        if (!stage_segs<stage_words_wide<B>(), 1, 2>(sg, wave, kComputeWaves, spin, ss)) return q1;
                     }
-                    if (!barrier()) return;
+                    if (!barrier()) return q1;
                     if (tr && lane == 0 && ks == 0) tr[2] = (uint32_t)now_ticks();
                     const XLds x{xs, Ks};
                     const bool last = ks + 1 == ns;
@@ -1635,7 +1610,8 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
             case OP_ATTN: ok = attn_instr<B, HD>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr, ctx); break;
             default: break;
         }
-        if (!ok || lds_ld(&ctl->abort)) return;
+        if (!ok || lds_ld(&ctl->abort)) return q1;
+        if (head_qi < q1) break;  // the head's rows run after the loop
         if (tr && lane == 0) {
             tr[3] = (uint32_t)now_ticks();
             tr[6] = land_wait;
@@ -1646,51 +1622,50 @@ __device__ __forceinline__ void compute_wave(const Params& P, const StepArgs& A,
         set_consumed(ctl, wave, S / kChunk);
         if (tr && lane == 0) tr[4] = (uint32_t)now_ticks();
     }
-    if constexpr (!MF) {
-        // The LM head runs outside the instruction loop: its row loads are issued
-        // ahead, and inside the loop the compiler would have to assume some may
-        // still be in flight at the back edge, guarding every later write of their
-        // registers (in the GEMV row loops) with a vmcnt wait.
-        if (head_qi < q1) {
-            const Instr in = ld_const(P.instrs + head_qi);
-            const uint32_t qi = head_qi;
-            uint32_t* tr =
-                (P.trace && wave == 0) ? P.trace + ((size_t)blockIdx.x * P.trace_stride + k) * kTraceWords : nullptr;
-            if (tr && lane == 0) {
-                tr[0] = (uint32_t)in.op | ((uint32_t)in.layer << 16);
-                tr[1] = (uint32_t)now_ticks();
+    return head_qi;
+}
+
+// The LM-head instruction (VALU and MoE kinds): the compute waves have staged its
+// input in their instruction loop (the staging shared with QKV and GATEUP) and
+// published it; then all eight waves stream its rows, in one inlined copy of the
+// code for both wave kinds (the kernel is far larger than the instruction cache
+// already).  The rows run outside the compute waves' instruction loop: their
+// loads are issued ahead, and inside the loop the compiler would have to assume
+// some may still be in flight at the back edge, guarding every later write of
+// their registers (in the GEMV row loops) with a vmcnt wait.
+template <int B>
+__device__ __forceinline__ void head_instr(const Params& P, const StepArgs& A, Ctl* ctl, float* xs, int wave,
+                                           uint32_t qi) {
+    const Instr in = ld_const(P.instrs + qi);
+    Spin spin(&P, &ctl->abort);
+    auto ready = [&](float (&r)[B]) -> bool {
+        // The loader waves wait for the input.  Like their other waits this ends on
+        // the workgroup's own abort flag or the watchdog, not on an error latched by
+        // an earlier step (it spans most of the step, long enough to see one), and
+        // the watchdog counts from the compute waves' last barrier: it measures a
+        // lack of progress, not the step.
+        uint64_t t0 = now_ticks();
+        uint32_t polls = 0, seen = lds_ld(&ctl->bar);
+        while (lds_ld(&ctl->head_seq) != qi + 1u) {
+            if (lds_ld(&ctl->abort)) return false;
+            if ((++polls & 255u) == 0) {
+                const uint32_t b = lds_ld(&ctl->bar);
+                if (b != seen) {
+                    seen = b;
+                    t0 = now_ticks();
+                } else if (now_ticks() - t0 > P.spin_ticks) {
+                    raise_error_impl(P.state, P.host_err, &ctl->abort, DERR_TIMEOUT, 0xFFFFFFFBu, qi);
+                    return false;
+                }
             }
-            if (!barrier()) return;
-            if (tr && lane == 0) tr[8] = (uint32_t)now_ticks();
-            // stage the final-norm input, then publish it to the loader waves, which
-            // join the head
-            const uint32_t d = (uint32_t)P.d;
-            auto ready = [&](float (&r)[B]) -> bool {
-                float ss[B];
-#pragma unroll
-                for (int b = 0; b < B; ++b) ss[b] = 0.f;
-                const StageSeg sg[1] = {{P.h, xs, P.final_norm, d, (uint32_t)B, d, d, phase_tag(A.tag0, P.L - 1, 4)}};
-                if (!stage_segs<stage_words<B>(), B, 1>(sg, wave, kComputeWaves, spin, ss)) return false;
-                wave_total_n<B>(ss);
-                if (lane == 0) {
-#pragma unroll
-                    for (int b = 0; b < B; ++b) ctl->ss[b][wave] = ss[b];
-                }
-                if (!barrier()) return false;
-#pragma unroll
-                for (int b = 0; b < B; ++b) r[b] = rms_scale(ctl->ss[b], kComputeWaves, P.d, P.eps);
-                if (wave == 0 && lane == 0) {
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-                    lds_st(&ctl->head_seq, qi + 1u);
-                }
-                if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
-                return true;
-            };
-            const bool ok = head_direct<B, false>(P, A, xs, in, wave, spin, ready);
-            if (!ok || lds_ld(&ctl->abort)) return;
-            if (tr && lane == 0) tr[3] = tr[4] = (uint32_t)now_ticks();
+            __builtin_amdgcn_s_sleep(2);
         }
-    }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+        for (int b = 0; b < B; ++b) r[b] = rms_scale(ctl->ss[b], kComputeWaves, P.d, P.eps);
+        return true;
+    };
+    (void)head_direct<B>(P, A, xs, in, wave, spin, ready);
 }
 
 template <int B, int HD, bool MF, bool MOE>
@@ -1712,45 +1687,14 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
     if (threadIdx.x < kMaxBatch) ctl.ctx[threadIdx.x] = (int)threadIdx.x < B ? P.state->ctx_len[threadIdx.x] : 0;
     __syncthreads();
     const uint32_t q0 = ld_const(P.queue_off + blockIdx.x), q1 = ld_const(P.queue_off + blockIdx.x + 1);
+    uint32_t hi;
     if (wave >= kComputeWaves) {
-        const uint32_t hi = loader_wave<B, HD, MF, MOE>(P, &ctl, ring, wave - kComputeWaves, q0, q1, ctl.ctx);
-        if constexpr (!MF) {
-            if (hi < q1) {
-                // join the LM head once the compute waves have staged its input
-                const Instr in = ld_const(P.instrs + hi);
-                Spin spin(&P, &ctl.abort);
-                auto ready = [&](float (&r)[B]) -> bool {
-                    // Like the loaders' other waits this ends on the workgroup's own abort
-                    // flag or the watchdog, not on an error latched by an earlier step (it
-                    // spans most of the step, long enough to see one).  The loaders arrive
-                    // long before the compute waves, so the watchdog counts from the compute
-                    // waves' last barrier: it measures a lack of progress, not the step.
-                    uint64_t t0 = now_ticks();
-                    uint32_t polls = 0, seen = lds_ld(&ctl.bar);
-                    while (lds_ld(&ctl.head_seq) != hi + 1u) {
-                        if (lds_ld(&ctl.abort)) return false;
-                        if ((++polls & 255u) == 0) {
-                            const uint32_t b = lds_ld(&ctl.bar);
-                            if (b != seen) {
-                                seen = b;
-                                t0 = now_ticks();
-                            } else if (now_ticks() - t0 > P.spin_ticks) {
-                                raise_error_impl(P.state, P.host_err, &ctl.abort, DERR_TIMEOUT, 0xFFFFFFFBu, hi);
-                                return false;
-                            }
-                        }
-                        __builtin_amdgcn_s_sleep(2);
-                    }
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-#pragma unroll
-                    for (int b = 0; b < B; ++b) r[b] = rms_scale(ctl.ss[b], kComputeWaves, P.d, P.eps);
-                    return true;
-                };
-                (void)head_direct<B, true>(P, A, xs, in, wave, spin, ready);
-            }
-        }
+        hi = loader_wave<B, HD, MF, MOE>(P, &ctl, ring, wave - kComputeWaves, q0, q1, ctl.ctx);
     } else {
-        compute_wave<B, HD, MF, MOE>(P, A, &ctl, ring, xs, wave, q0, q1, ctl.ctx);
+        hi = compute_wave<B, HD, MF, MOE>(P, A, &ctl, ring, xs, wave, q0, q1, ctl.ctx);
+    }
+    if constexpr (!MF) {
+        if (hi < q1) head_instr<B>(P, A, &ctl, xs, wave, hi);
     }
 }
 

@@ -521,25 +521,28 @@ __device__ __forceinline__ bool stage_segs(const StageSeg (&sg)[NS], int w, int 
         }
         return true;
     };
+    // A pass is issued only when it will be read, and the exit retires every load
+    // explicitly (vmcnt(0), cheap since nothing unread is in flight): the compiler's
+    // wait analysis cannot tie the `more` tests together, so without the explicit
+    // wait it would take loads into these registers as possibly pending wherever
+    // they are next written, and inside the GEMV row loops that follow it would
+    // guard such writes with a vmcnt wait on every row batch, which also waits for
+    // the previous batch's write-through result stores.
     uint64_t va[K], vb[K];
     uint32_t ga[K], gb[K];
     issue(0u, va, ga);
-    bool ok = true;
     for (uint32_t p0 = 0;; p0 += 2u * per_pass) {
-        issue(p0 + per_pass, vb, gb);
-        if (!(ok = finish(p0, va, ga))) break;
-        if (p0 + per_pass >= total) break;
-        issue(p0 + 2u * per_pass, va, ga);
-        if (!(ok = finish(p0 + per_pass, vb, gb))) break;
-        if (p0 + 2u * per_pass >= total) break;
+        const bool more = p0 + per_pass < total;
+        if (more) issue(p0 + per_pass, vb, gb);
+        if (!finish(p0, va, ga)) return false;
+        if (!more) break;
+        const bool more2 = p0 + 2u * per_pass < total;
+        if (more2) issue(p0 + 2u * per_pass, va, ga);
+        if (!finish(p0 + per_pass, vb, gb)) return false;
+        if (!more2) break;
     }
-    // The pass issued ahead of the last one is never read.  Retire it here: left
-    // pending, the compiler must assume loads into those registers may still be
-    // in flight wherever they are next written, and inside the GEMV row loops that
-    // follow it guards such writes with a vmcnt wait on every row batch, which
-    // then waits for the previous batch's write-through result stores as well.
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
-    return ok;
+    return true;
 }
 
 // Same from a bf16 row that needs no wait (the token embedding of layer 0);
