@@ -148,6 +148,25 @@ mk_status mk_query_sizes(const mk_model_config* cfg, const mk_runtime_config* rt
 mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_runtime_config* rt, void* d_workspace,
                     size_t workspace_bytes, void* d_kv, size_t kv_bytes, void* stream, mk_handle** out);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): mk_create with the
+ * workspace taken from a static device array of MK_STATIC_WORKSPACE_BYTES that
+ * the library holds on every device it runs on until the process ends.  The
+ * caller still provides the weights and the KV cache (kv_bytes as from
+ * mk_query_sizes).  The call allocates no device or pinned host memory (it
+ * builds the schedule in host memory, clears the array and uploads the schedule
+ * and RoPE table on `stream`, then synchronises it).  Persistent mode only
+ * (MK_MODE_MEGAKERNEL, or MK_MODE_ENV resolving to it), else MK_E_UNSUPPORTED;
+ * a configuration whose workspace exceeds the array is MK_E_CAPACITY; one live
+ * handle per device uses the array, a second is MK_E_STATE until the first is
+ * destroyed (calls on handles that overlapped on one device would race on it).
+ * Such a handle has no host-mapped error word (that would be an allocation): a
+ * device error (watchdog, NaN logit) stays latched on the device and is
+ * returned by the next mk_reset, which clears it. */
+#define MK_STATIC_WORKSPACE_BYTES (32u << 20)
+mk_status mk_create_static(const mk_model_config* cfg, const mk_weights* w, const mk_runtime_config* rt, void* d_kv,
+                           size_t kv_bytes, void* stream, mk_handle** out);
+
 /* Layout of the caller's KV cache, which the step reads for attention and
  * appends to [MK: attention is one of the fused per-layer instructions; LOW: the
  * workload decodes against the cache its prompt left].  strides_out[0..4]
@@ -204,9 +223,8 @@ mk_status mk_get_context_len(const mk_handle* h, int32_t* h_lens, int32_t B);
  * clears the merge tickets and the latched error, and synchronises again.  The
  * step counter behind the value tags keeps counting, so values an aborted step
  * left behind never satisfy a later step.  MK_E_HIP if a runtime call fails.
- * A handle without the host-mapped error word (its pinned allocation failed)
- * gets the device error it cleared returned (MK_E_DEVICE_TIMEOUT /
- * MK_E_DEVICE_NAN), MK_OK if none. */
+ * For a handle of mk_create_static (no host-mapped error word) it returns the
+ * device error it cleared (MK_E_DEVICE_TIMEOUT / MK_E_DEVICE_NAN), MK_OK if none. */
 mk_status mk_reset(mk_handle* h, void* stream);
 
 /* Test hook: fault 1 = the next step runs with a 1 ms watchdog and its layer-0

@@ -19,6 +19,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -453,7 +454,7 @@ struct mk_handle {
     hipStream_t stream = nullptr;
     hipStream_t last_stream = nullptr;  // stream of the last enqueued step (mk_destroy waits for it)
     bool used = false;
-    int static_dev = -1;  // >= 0: the workspace is a static array of that device (none yet)
+    int static_dev = -1;  // >= 0: the workspace is that device's static array (mk_create_static)
     std::vector<int32_t> ctx;
     uint32_t epoch = 0;
     HostErr* host_err = nullptr;
@@ -467,6 +468,19 @@ struct mk_handle {
     const void *g_in = nullptr, *g_out = nullptr, *g_logits = nullptr;
     int32_t inject = 0;
 };
+
+// Workspace of the handles made by mk_create_static, for callers that cannot
+// allocate device memory.  Each device the library runs on holds its own copy
+// for the life of the process.  Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[MK_STATIC_WORKSPACE_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices];   // device address of `scratch` on each device, once known
+bool g_static_busy[kMaxDevices];   // a live handle of mk_create_static uses that device's array
+}  // namespace
 
 static mk_status hip_fail(mk_handle* h, hipError_t e, const char* what) {
     if (h) {
@@ -543,8 +557,8 @@ mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* r
 
 }  // extern "C"
 
-// mk_create; static_dev >= 0 would mark a workspace in a static device array (no
-// size query of every CU count, no pinned error word).
+// mk_create, and mk_create_static with static_dev >= 0 (the workspace is that
+// device's static array: no size query of every CU count, no pinned error word).
 static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, const mk_runtime_config* rt_in,
                              void* d_workspace, size_t workspace_bytes, void* d_kv, size_t kv_bytes, void* stream,
                              mk_handle** out, int static_dev) {
@@ -600,7 +614,7 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
     h->ctx.assign(rt->max_batch, 0);
     h->static_dev = static_dev;
 
-    // pinned, device-visible error word (not for a static workspace: an allocation)
+    // pinned, device-visible error word (not for mk_create_static: an allocation)
     if (static_dev >= 0 ||
         hipHostMalloc((void**)&h->host_err, sizeof(HostErr), hipHostMallocMapped | hipHostMallocCoherent) !=
             hipSuccess) {
@@ -766,6 +780,43 @@ extern "C" {
 mk_status mk_create(const mk_model_config* cfg, const mk_weights* w, const mk_runtime_config* rt, void* d_workspace,
                     size_t workspace_bytes, void* d_kv, size_t kv_bytes, void* stream, mk_handle** out) {
     return create_impl(cfg, w, rt, d_workspace, workspace_bytes, d_kv, kv_bytes, stream, out, -1);
+}
+
+mk_status mk_create_static(const mk_model_config* cfg, const mk_weights* w, const mk_runtime_config* rt_in, void* d_kv,
+                           size_t kv_bytes, void* stream, mk_handle** out) {
+    if (!out || !rt_in || !cfg) return MK_E_INVALID;
+    *out = nullptr;
+    const mk_runtime_config rt = resolve_mode(rt_in);
+    if (rt.mode != MK_MODE_MEGAKERNEL) return MK_E_UNSUPPORTED;
+    mk_status s = validate(cfg, &rt, nullptr);
+    if (s != MK_OK) return s;
+    // the workspace this handle lays out, against the array (host-only arithmetic)
+    const int n_cu = resolve_cus(&rt);
+    if (n_cu <= 0 || n_cu > kMaxCus) return MK_E_UNSUPPORTED;
+    if (layout(cfg, &rt, n_cu, auto_splits(cfg, &rt, n_cu)).total > (size_t)MK_STATIC_WORKSPACE_BYTES)
+        return MK_E_CAPACITY;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MK_E_HIP;
+    void* ptr = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_static_mu);
+        if (g_static_busy[dev]) return MK_E_STATE;  // one live handle per device shares the array
+        if (!g_static_ptr[dev]) {
+            // once per device, with that device current: the array's device address
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MK_E_HIP;
+            g_static_ptr[dev] = ptr;
+        }
+        ptr = g_static_ptr[dev];
+        g_static_busy[dev] = true;
+    }
+    // create_impl zeroes the workspace before the first step, so nothing an earlier
+    // handle left in the array survives
+    s = create_impl(cfg, w, &rt, ptr, (size_t)MK_STATIC_WORKSPACE_BYTES, d_kv, kv_bytes, stream, out, dev);
+    if (s != MK_OK) {
+        std::lock_guard<std::mutex> lock(g_static_mu);
+        g_static_busy[dev] = false;
+    }
+    return s;
 }
 
 mk_status mk_kv_layout(const mk_handle* h, int64_t strides_out[5]) {
@@ -961,6 +1012,10 @@ mk_status mk_destroy(mk_handle* h) {
     if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
     if (h->graph) (void)hipGraphDestroy(h->graph);
     if (h->host_err) (void)hipHostFree(h->host_err);
+    if (h->static_dev >= 0) {
+        std::lock_guard<std::mutex> lock(g_static_mu);
+        g_static_busy[h->static_dev] = false;
+    }
     delete h;
     return MK_OK;
 }

@@ -25,7 +25,7 @@ MK_OK, MK_E_INVALID, MK_E_UNSUPPORTED, MK_E_CAPACITY, MK_E_HIP, MK_E_DEVICE_TIME
 MK_MODE_MEGAKERNEL, MK_MODE_GRAPH, MK_MODE_ENV = 0, 1, 2
 MK_GEMV_AUTO, MK_GEMV_VALU, MK_GEMV_MFMA = 0, 1, 2
 
-EXPORTS = ["mk_query_sizes", "mk_create", "mk_kv_layout", "mk_prefill", "mk_set_context_len", "mk_decode_step",
+EXPORTS = ["mk_query_sizes", "mk_create", "mk_create_static", "mk_kv_layout", "mk_prefill", "mk_set_context_len", "mk_decode_step",
            "mk_get_context_len", "mk_reset", "mk_debug_inject", "mk_status_string", "mk_last_error",
            "mk_plan_inspect", "mk_kernels_per_step", "mk_destroy", "mk_bench_stream_read", "mk_bench_copy",
            "mk_bench_sync", "mk_read_trace", "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap"]
@@ -88,6 +88,8 @@ def lib():
                                      ctypes.POINTER(sz), ctypes.POINTER(sz)]
         L.mk_create.argtypes = [ctypes.POINTER(mk_model_config), ctypes.POINTER(mk_weights),
                                 ctypes.POINTER(mk_runtime_config), vp, sz, vp, sz, vp, ctypes.POINTER(vp)]
+        L.mk_create_static.argtypes = [ctypes.POINTER(mk_model_config), ctypes.POINTER(mk_weights),
+                                       ctypes.POINTER(mk_runtime_config), vp, sz, vp, ctypes.POINTER(vp)]
         L.mk_kv_layout.argtypes = [vp, ctypes.POINTER(ctypes.c_int64)]
         L.mk_prefill.argtypes = [vp, vp, i32, i32, vp, vp, vp]
         L.mk_set_context_len.argtypes = [vp, ctypes.POINTER(i32), i32]
@@ -111,7 +113,7 @@ def lib():
         L.mk_bench_edge.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, sz, vp, vp, vp]
         L.mk_read_trace.argtypes = [vp, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(i32)]
         L.mk_bench_graph_gap.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ctypes.POINTER(ctypes.c_float), vp]
-        for n in ("mk_query_sizes", "mk_create", "mk_kv_layout", "mk_prefill", "mk_set_context_len",
+        for n in ("mk_query_sizes", "mk_create", "mk_create_static", "mk_kv_layout", "mk_prefill", "mk_set_context_len",
                   "mk_get_context_len", "mk_decode_step", "mk_reset", "mk_debug_inject", "mk_plan_inspect",
                   "mk_destroy", "mk_bench_stream_read", "mk_bench_copy", "mk_bench_sync", "mk_read_trace",
                   "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap"):
@@ -179,7 +181,7 @@ class Decoder:
     def __init__(self, cfg, weights, max_batch: int, max_seq: int, mode: int = MK_MODE_MEGAKERNEL,
                  device: str = "cuda:0", num_cus: int = 0, spin_timeout_ms: int = 0, attn_splits: int = 0,
                  device_weights: Optional[Dict[str, object]] = None, trace: int = 0,
-                 gemv_kind: int = 0):
+                 gemv_kind: int = 0, static_workspace: bool = False):
         import torch
 
         self.torch = torch
@@ -218,12 +220,20 @@ class Decoder:
         self.kv = torch.empty(kv, dtype=torch.uint8, device=self.device)
         self.stream = torch.cuda.current_stream(self.device)
         h = ctypes.c_void_p()
-        self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
-        st = lib().mk_create(ctypes.byref(self._c), ctypes.byref(w), ctypes.byref(self._rt),
-                             self.workspace.data_ptr(), ws, self.kv.data_ptr(), kv, self.stream.cuda_stream,
-                             ctypes.byref(h))
-        if st != MK_OK:
-            raise MKError(st, "mk_create")
+        if static_workspace:
+            # the library's static per-device workspace (mk_create_static): no workspace tensor
+            self.workspace = None
+            st = lib().mk_create_static(ctypes.byref(self._c), ctypes.byref(w), ctypes.byref(self._rt),
+                                        self.kv.data_ptr(), kv, self.stream.cuda_stream, ctypes.byref(h))
+            if st != MK_OK:
+                raise MKError(st, "mk_create_static")
+        else:
+            self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
+            st = lib().mk_create(ctypes.byref(self._c), ctypes.byref(w), ctypes.byref(self._rt),
+                                 self.workspace.data_ptr(), ws, self.kv.data_ptr(), kv, self.stream.cuda_stream,
+                                 ctypes.byref(h))
+            if st != MK_OK:
+                raise MKError(st, "mk_create")
         self.h = h
         _live.add(self)
         self.tok = torch.zeros(max_batch, dtype=torch.int32, device=self.device)

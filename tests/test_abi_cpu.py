@@ -300,3 +300,19 @@ def test_dense_persistent_kernels_use_no_scratch():
     assert all(v["scratch"] <= 16 for v in dense.values()), dense
     print({k: v["scratch"] for k, v in mega.items() if v["scratch"]})
 
+
+def test_static_create_refuses_on_the_host():
+    """mk_create_static decides what it cannot do before it touches the device:
+    the one-kernel-per-op mode, and a workspace larger than the static array (a
+    long RoPE table), are refused with no HIP call."""
+    L = mk.lib()
+    cfg = mk.model_config(I.LLAMA_1B)
+    w = mk.mk_weights()
+    h = ctypes.c_void_p()
+    graph = mk.runtime_config(1, 161, mode=mk.MK_MODE_GRAPH)
+    assert L.mk_create_static(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(graph), None, 0, None,
+                              ctypes.byref(h)) == mk.MK_E_UNSUPPORTED
+    big = mk.runtime_config(1, 1 << 20)  # RoPE table alone: 2^20 positions x 32 x 8 bytes = 256 MB
+    assert L.mk_create_static(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(big), None, 0, None,
+                              ctypes.byref(h)) == mk.MK_E_CAPACITY
+    assert h.value is None
