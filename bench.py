@@ -98,23 +98,72 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def step_bytes(cfg, batch: int, positions) -> int:
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def micro_benchmarks(dev, n_cu: int) -> dict:
+    """The synchronisation and launch costs the persistent kernel is built
+    around: the gap one kernel boundary costs inside a replayed hipGraph, an
+    all-to-all dependency round over every CU with a counter + fences and with
+    tagged words, the one-way CU-to-CU latency across and within an XCD, and one
+    dependency edge at the decode step's sizes idle and under a full weight
+    stream.  Every figure is a mean over many rounds, in microseconds."""
+    import torch
+
+    import persistent_megakernel_02_amd.mk as mk
+
+    out = {"graph_gap_us_per_kernel": round(mk.bench_graph_gap(1000, 10, n_cu), 3)}
+    for name, mode in (("counter_fences", 0), ("tagged_words", 4)):
+        r = mk.bench_sync(mode, n_cu, 2000)
+        if r["mismatches"]:
+            raise RuntimeError(f"sync benchmark mode {mode}: {r['mismatches']} mismatches")
+        out[f"all_to_all_round_us_{name}"] = round(r["us_per_round"], 3)
+    for name, peer in (("cross_xcd", 1), ("same_xcd", 8)):
+        r = mk.bench_pingpong(peer, 20000)
+        if r["lost"]:
+            raise RuntimeError(f"pingpong benchmark peer {peer}: {r['lost']} lost waits")
+        out[f"one_way_us_{name}"] = round(r["us_one_way"], 3)
+        out[f"one_way_xcc_{name}"] = r["xcc"]
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)  # 1 GiB: beyond the 256 MiB last-level cache
+    for words in (8, 32):
+        for name, s in (("idle", None), ("streaming", src)):
+            r = mk.bench_edge(n_cu, words, 1000, s)
+            if r["mismatches"]:
+                raise RuntimeError(f"edge benchmark {words} words: {r['mismatches']} mismatches")
+            out[f"edge_us_{n_cu * words}_words_{name}"] = round(r["us_per_round"], 3)
+    del src
+    return out
+
+
+def expert_bytes(cfg) -> int:
+    """Bytes of one expert's gate, up and down matrices (bf16)."""
+    return 3 * cfg.expert_ffn * cfg.hidden * 2
+
+
+def step_bytes(cfg, batch: int, positions, slots_per_step: float = 0.0) -> int:
     """Algorithmic HBM bytes of one decode step: every weight byte once, each
     sequence's embedding row, the K/V of its cached positions read once per
     (sequence, KV head), its new K/V written, the fp32 logits written.
     `positions`: the position each sequence decodes at this step (one per sequence,
-    or a single value shared by all)."""
+    or a single value shared by all).  MoE: only the streamed expert slots count,
+    `slots_per_step` of them summed over the layers (the shared experts plus the
+    union the router selected, as the kernel counts them)."""
     kv_pos = cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim * 2
     pos = [int(p) for p in positions]
     if len(pos) == 1:
         pos = pos * batch
     w = cfg.weight_bytes()
     if cfg.is_moe:
-        # only the selected experts stream: the expected number of distinct experts
-        # among batch x top_k uniform choices (the routing is data dependent)
-        E, k = cfg.n_experts, cfg.top_k
-        distinct = E * (1.0 - (1.0 - k / E) ** batch)
-        w -= int(round((E - distinct) * 3 * cfg.expert_ffn * cfg.hidden * 2)) * cfg.n_layers
+        w -= (cfg.n_experts + cfg.n_shared) * expert_bytes(cfg) * cfg.n_layers
+        w += int(round(slots_per_step * expert_bytes(cfg)))
     b = w + batch * cfg.hidden * 2
     b += sum(pos) * kv_pos     # cached positions 0..p-1 read
     b += batch * kv_pos        # position p written
@@ -150,6 +199,7 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="skip the one-kernel-per-op comparison")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-steps", type=int, default=24)
+    ap.add_argument("--no-micro", action="store_true", help="skip the synchronisation / launch micro-benchmarks")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--profile-run", action="store_true",
                     help="untimed workload for rocprofv3 counter runs (no JSON line)")
@@ -224,10 +274,12 @@ def main() -> int:
         torch.cuda.synchronize()
         # timed: horizons of <= H steps from the prompt; events on the launch stream
         total_ms, left, positions, per_h = 0.0, args.steps, [], []
+        slots = 0
         while left > 0:
             n = min(left, H)
             start_horizon()
             torch.cuda.synchronize()
+            slots0 = dec.moe_slots() if cfg.is_moe else 0
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(st)
@@ -235,6 +287,8 @@ def main() -> int:
                 dec.decode_step(tok, tok, logits)
             e1.record(st)
             e1.synchronize()
+            if cfg.is_moe:
+                slots += dec.moe_slots() - slots0
             ms = e0.elapsed_time(e1)
             total_ms += ms
             per_h.append(ms * 1000.0 / n)
@@ -261,18 +315,19 @@ def main() -> int:
         pct = (float(np.percentile(per_step, 50)), float(np.percentile(per_step, 95)))
         log(f"{label}: {us:.1f} us/token over {args.steps} steps ({kps} kernels/step), "
             f"p50 {pct[0]:.1f} p95 {pct[1]:.1f}")
-        return us, positions, kps, per_h, pct
+        return us, positions, kps, per_h, pct, slots / args.steps
 
     gemv_used = mk.mk_plan_inspect(mk.model_config(cfg), mk.runtime_config(B, max_seq, gemv_kind=gemv),
                                    torch.cuda.get_device_properties(dev).multi_processor_count)[1]["gemv_kind"]
-    us_mk, positions, kps_mk, per_h, pct_mk = run_path(mk.MK_MODE_MEGAKERNEL, "megakernel")
-    bytes_step = [step_bytes(cfg, B, [p]) for p in positions]  # every sequence at position p
+    us_mk, positions, kps_mk, per_h, pct_mk, slots_step = run_path(mk.MK_MODE_MEGAKERNEL, "megakernel")
+    # every sequence at position p; MoE: the expert slots the kernel counted, mean per step
+    bytes_step = [step_bytes(cfg, B, [p], slots_step) for p in positions]
     mean_bytes = float(np.mean(bytes_step))
     gbs = mean_bytes / (us_mk * 1e-6) / 1e9
 
     us_graph = kps_graph = pct_graph = None
     if not args.no_graph and not cfg.is_moe:  # the one-kernel-per-op path has no MoE kernels
-        us_graph, _, kps_graph, _, pct_graph = run_path(mk.MK_MODE_GRAPH, "hipGraph one-kernel-per-op")
+        us_graph, _, kps_graph, _, pct_graph, _ = run_path(mk.MK_MODE_GRAPH, "hipGraph one-kernel-per-op")
 
     # streaming-read ceiling on a buffer the size of the step
     buf = torch.empty(int(mean_bytes) // 16 * 16, dtype=torch.uint8, device=dev)
@@ -290,6 +345,11 @@ def main() -> int:
     ceil_gbs = buf.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del buf
     log(f"streaming-read ceiling: {ceil_gbs:.0f} GB/s")
+
+    micro = None
+    if not args.no_micro and args.config == "1b":
+        micro = micro_benchmarks(dev, torch.cuda.get_device_properties(dev).multi_processor_count)
+        log(f"micro-benchmarks: {micro}")
 
     cpu = None
     if not args.no_cpu:
@@ -309,7 +369,7 @@ def main() -> int:
         t3 = time.time()
         cpu_us = (t3 - t2) * 1e6 / nsteps
         cpu = {"value": round(cpu_us, 1), "unit": "us/token" if B == 1 else "us/step", "cores": O.threads(),
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": cpu_model(),
                "sample": f"{nsteps} batch-{B} decode steps of the same {cfg.name} model at positions "
                          f"{P}..{P + nsteps - 1} (fp64-accumulated C oracle, OpenMP over rows)"}
         log(f"cpu oracle: {cpu_us / 1000:.1f} ms/step on {O.threads()} threads")
@@ -333,7 +393,8 @@ def main() -> int:
         "config": {"workload": W["text"] + ", random bf16 weights N(0,0.02)", "batch": B,
                    "prompt": W["prompt"], "context": CTX, "horizon": H,
                    "layers": cfg.n_layers, "hidden": cfg.hidden, "vocab": cfg.vocab,
-                   "gemv": "mfma" if gemv_used == mk.MK_GEMV_MFMA else "valu"},
+                   "gemv": "mfma" if gemv_used == mk.MK_GEMV_MFMA else "valu",
+                   "expert_slots_per_step": round(slots_step, 2) if cfg.is_moe else None},
         "tokens_per_s": round(B * 1e6 / us_mk, 1),
         "us_per_token_p50": round(pct_mk[0], 2),
         "us_per_token_p95": round(pct_mk[1], 2),
@@ -352,6 +413,7 @@ def main() -> int:
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic if headline else None,
                      "bytes_per_launch": int(mean_bytes), "traffic_source": traffic_src},
         "cpu_baseline": cpu,
+        "micro": micro,
     }
     print(json.dumps(out), flush=True)
     return 0

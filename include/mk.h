@@ -259,6 +259,16 @@ mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* r
  * byte size) is set.  Synchronises the handle's creation stream. */
 mk_status mk_read_trace(mk_handle* h, void* h_buf, size_t bytes, size_t* written, int32_t* records_per_cu);
 
+/* Expert slots the MoE layers have streamed since mk_create: per (step, MoE
+ * layer) the shared experts plus the union of the experts the batch's sequences
+ * selected [page "大模型吐一个字，显卡要启停两千四百次", section "两千四百次启停":
+ * only the selected experts' weights are read].  Times the bytes of one
+ * expert's three matrices, it is the expert weight traffic of those steps, so a
+ * difference of two readings gives the exact algorithmic bytes of the steps in
+ * between.  Dense models read 0.  Synchronises the streams the handle ran on;
+ * *out is left unchanged on error. */
+mk_status mk_moe_slots(mk_handle* h, uint64_t* out);
+
 /* Number of kernel launches one decode step makes in the handle's mode. */
 int32_t mk_kernels_per_step(const mk_handle* h);
 

@@ -17,8 +17,9 @@ extern "C" {
 #endif
 
 /* Read `bytes` (multiple of 16, 16-byte aligned) from device memory d_src with
- * 16-byte vector loads over the whole device; d_sink is a device word the kernel
- * may write.  Enqueued on `stream` (hipStream_t).  Returns 0, 1 on bad arguments,
+ * non-temporal 16-byte vector loads over the whole device (16 workgroups per CU,
+ * each reading one contiguous slice with 16 loads in flight per thread); d_sink
+ * is a device word the kernel may write.  Enqueued on `stream` (hipStream_t).  Returns 0, 1 on bad arguments,
  * 4 on a launch error. */
 int mk_bench_stream_read(const void* d_src, size_t bytes, void* d_sink, void* stream);
 

@@ -974,6 +974,16 @@ mk_status mk_reset(mk_handle* h, void* stream) {
     return cleared;
 }
 
+mk_status mk_moe_slots(mk_handle* h, uint64_t* out) {
+    if (!h || !out) return MK_E_INVALID;
+    if (h->used) HIPCHK(h, hipStreamSynchronize(h->last_stream));
+    HIPCHK(h, hipStreamSynchronize(h->stream));
+    unsigned long long v = 0;
+    HIPCHK(h, hipMemcpy(&v, h->ws + h->lo.state + offsetof(DevState, moe_slots), sizeof(v), hipMemcpyDeviceToHost));
+    *out = (uint64_t)v;
+    return MK_OK;
+}
+
 mk_status mk_debug_inject(mk_handle* h, int32_t fault, int32_t arg) {
     (void)arg;
     if (!h) return MK_E_INVALID;

@@ -775,6 +775,50 @@ __device__ __forceinline__ bool gemv_ring_seg(const Params& P, Ctl* ctl, const c
     return true;
 }
 
+// Batch 1, rows of 64 NPL pieces (NPL = 4: 4 KB, the hidden size of 2048): each
+// lane only ever reads the NPL pieces lane, lane + 64, ... of x, so they stay in
+// registers for the whole instruction (32 floats), and a row batch reads only
+// weights from the ring: all R x NPL pieces are requested at once, so a batch
+// waits on the LDS once instead of once per piece pair.  Each lane accumulates
+// its pieces in ascending order and wave_total reduces in its fixed tree: the
+// same bits as rows_dot.  Used for the QKV and O rows; the (gate, up) pairs keep
+// gemv_ring, which measured faster there (the pair stream is loader bound, and
+// this loop's tighter polling of the ring slowed it).
+template <int R, int NPL, class Epi>
+__device__ __forceinline__ bool gemv_ring_xreg(const Params& P, Ctl* ctl, const char* ring, uint32_t S, uint32_t rb,
+                                               uint32_t nrows, const XLds& x, int wave, uint32_t& lw, Epi& epi) {
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint32_t ring_bytes = P.ring_chunks * kChunk;
+    float4 xa[NPL], xb[NPL];
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) x.piece(0, lane + 64u * (uint32_t)k, xa[k], xb[k]);
+    for (uint32_t r0 = (uint32_t)wave * R; r0 < nrows; r0 += (uint32_t)R * kComputeWaves) {
+        const uint32_t nr = min((uint32_t)R, nrows - r0);
+        const uint32_t off = S + r0 * rb;
+        set_consumed(ctl, wave, off / kChunk);
+        if (!wait_landed(P, ctl, (off + nr * rb + kChunk - 1u) / kChunk, lw)) return false;
+        const RingBatch rows{ring, ring_addr(off, P.ring_chunks), rb, ring_bytes};
+        uint4 w[R][NPL];
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+            for (int k = 0; k < NPL; ++k) w[i][k] = rows.piece((uint32_t)i, lane + 64u * (uint32_t)k);
+        float acc[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int k = 0; k < NPL; ++k)
+#pragma unroll
+            for (int i = 0; i < R; ++i) acc[i] = dot8(w[i][k], xa[k], xb[k], acc[i]);
+        wave_total_n<R>(acc);
+        float res[R][1];
+#pragma unroll
+        for (int i = 0; i < R; ++i) res[i][0] = acc[i];
+        epi(r0, nr, res);
+    }
+    return true;
+}
+
 // Batch size by row length; GATEUP keeps a (gate, up) pair inside one batch.
 template <int B, class Epi>
 __device__ __forceinline__ bool gemv_ring_auto(const Params& P, Ctl* ctl, const char* ring, uint32_t S, uint32_t rb,
@@ -785,6 +829,10 @@ __device__ __forceinline__ bool gemv_ring_auto(const Params& P, Ctl* ctl, const 
         return gemv_ring_seg<B, 1>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
     }
     const int R = ring_batch_rows(rb, B, pairs);
+    if constexpr (B == 1) {
+        if (rb == 64u * 4u * 16u && R == 2 && !pairs)
+            return gemv_ring_xreg<2, 4>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
+    }
     if (R == 4) return gemv_ring<B, 4>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
     if (R == 2) return gemv_ring<B, 2>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
     return gemv_ring<B, 1>(P, ctl, ring, S, rb, nrows, x, wave, lw, epi);
@@ -1297,6 +1345,10 @@ __device__ __forceinline__ bool moe_egu(const Params& P, const StepArgs& A, Ctl*
     uint64_t sel[B];
     float prob[B];
     const uint32_t n = moe_route<B>(P, ctl, zeta, wave, qi, sel, prob);
+    // the instruction holding the layer's first expert rows counts the slots the
+    // layer streams (every CU derives the same set)
+    if (in.begin == 0 && wave == 0 && lane == 0)
+        __hip_atomic_fetch_add(&P.state->moe_slots, (unsigned long long)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (!barrier()) return false;  // the slot list is visible
     if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
     bytes = moe_bytes(P, in, n);
@@ -1635,7 +1687,7 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
 // their registers (in the GEMV row loops) with a vmcnt wait.
 template <int B>
 __device__ __forceinline__ void head_instr(const Params& P, const StepArgs& A, Ctl* ctl, float* xs, int wave,
-                                           uint32_t qi) {
+                                           uint32_t q0, uint32_t qi) {
     const Instr in = ld_const(P.instrs + qi);
     Spin spin(&P, &ctl->abort);
     auto ready = [&](float (&r)[B]) -> bool {
@@ -1665,7 +1717,11 @@ __device__ __forceinline__ void head_instr(const Params& P, const StepArgs& A, C
         for (int b = 0; b < B; ++b) r[b] = rms_scale(ctl->ss[b], kComputeWaves, P.d, P.eps);
         return true;
     };
-    (void)head_direct<B>(P, A, xs, in, wave, spin, ready);
+    const bool ok = head_direct<B>(P, A, xs, in, wave, spin, ready);
+    if (ok && P.trace && wave == 0 && lane_id() == 0) {  // compute end and end of the head's record
+        uint32_t* tr = P.trace + ((size_t)blockIdx.x * P.trace_stride + (qi - q0)) * kTraceWords;
+        tr[3] = tr[4] = (uint32_t)now_ticks();
+    }
 }
 
 template <int B, int HD, bool MF, bool MOE>
@@ -1694,7 +1750,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
         hi = compute_wave<B, HD, MF, MOE>(P, A, &ctl, ring, xs, wave, q0, q1, ctl.ctx);
     }
     if constexpr (!MF) {
-        if (hi < q1) head_instr<B>(P, A, &ctl, xs, wave, hi);
+        if (hi < q1) head_instr<B>(P, A, &ctl, xs, wave, q0, hi);
     }
 }
 

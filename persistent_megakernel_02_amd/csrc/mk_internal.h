@@ -169,7 +169,8 @@ struct DevState {
     int32_t ctx_len[kMaxBatch];
     uint32_t error;  // first device error code (0 = none)
     uint32_t err_info[3];
-    uint32_t pad[20];
+    unsigned long long moe_slots;  // expert slots streamed by MoE layers, summed over layers and steps
+    uint32_t pad[18];
 };
 
 // Host-mapped error report (pinned host memory written by the device).

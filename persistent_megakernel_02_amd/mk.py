@@ -28,7 +28,7 @@ MK_GEMV_AUTO, MK_GEMV_VALU, MK_GEMV_MFMA = 0, 1, 2
 EXPORTS = ["mk_query_sizes", "mk_create", "mk_create_static", "mk_kv_layout", "mk_prefill", "mk_set_context_len", "mk_decode_step",
            "mk_get_context_len", "mk_reset", "mk_debug_inject", "mk_status_string", "mk_last_error",
            "mk_plan_inspect", "mk_kernels_per_step", "mk_destroy", "mk_bench_stream_read", "mk_bench_copy",
-           "mk_bench_sync", "mk_read_trace", "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap"]
+           "mk_bench_sync", "mk_read_trace", "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap", "mk_moe_slots"]
 
 
 class mk_model_config(ctypes.Structure):
@@ -113,10 +113,11 @@ def lib():
         L.mk_bench_edge.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, sz, vp, vp, vp]
         L.mk_read_trace.argtypes = [vp, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(i32)]
         L.mk_bench_graph_gap.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ctypes.POINTER(ctypes.c_float), vp]
+        L.mk_moe_slots.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64)]
         for n in ("mk_query_sizes", "mk_create", "mk_create_static", "mk_kv_layout", "mk_prefill", "mk_set_context_len",
                   "mk_get_context_len", "mk_decode_step", "mk_reset", "mk_debug_inject", "mk_plan_inspect",
                   "mk_destroy", "mk_bench_stream_read", "mk_bench_copy", "mk_bench_sync", "mk_read_trace",
-                  "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap"):
+                  "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap", "mk_moe_slots"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -302,6 +303,12 @@ class Decoder:
     def kernels_per_step(self) -> int:
         return int(lib().mk_kernels_per_step(self.h))
 
+    def moe_slots(self) -> int:
+        """Expert slots streamed by the MoE layers since creation (mk_moe_slots)."""
+        v = ctypes.c_uint64(0)
+        self._check(lib().mk_moe_slots(self.h, ctypes.byref(v)), "mk_moe_slots")
+        return int(v.value)
+
     def close(self):
         if getattr(self, "h", None):
             lib().mk_destroy(self.h)
@@ -345,3 +352,69 @@ def bench_stream_read(src, sink, stream=None) -> int:
 
 def bench_copy(dst, src, stream=None) -> int:
     return lib().mk_bench_copy(dst.data_ptr(), src.data_ptr(), src.numel() * src.element_size(), _stream_ptr(stream))
+
+
+def _bench_check(rc: int, name: str) -> None:
+    if rc != 0:
+        raise MKError(MK_E_INVALID if rc == 1 else MK_E_HIP, name)
+
+
+def bench_sync(mode: int, n_wg: int, rounds: int, device="cuda:0") -> Dict[str, float]:
+    """All-to-all dependency rounds of n_wg co-resident workgroups (mode 0: one
+    counter with agent-scope release/acquire fences; 4: tagged {value, round}
+    words, the decode step's protocol).  Returns microseconds per round and the
+    data mismatches seen."""
+    import torch
+
+    ctr = torch.zeros(64 + n_wg, dtype=torch.int32, device=device)
+    data = torch.zeros(2 * n_wg * 64, dtype=torch.int64, device=device)
+    out = torch.zeros(2, dtype=torch.int64, device=device)
+    _bench_check(lib().mk_bench_sync(mode, n_wg, rounds, ctr.data_ptr(), data.data_ptr(), out.data_ptr(),
+                                     _stream_ptr(None)), "mk_bench_sync")
+    torch.cuda.synchronize()
+    ticks, bad = (int(x) for x in out.cpu())
+    return {"us_per_round": ticks * 0.01 / rounds, "mismatches": bad}
+
+
+def bench_pingpong(peer: int, rounds: int, flavor: int = 0, device="cuda:0") -> Dict[str, float]:
+    """One-way latency of an 8-byte word bounced between workgroup 0 and `peer`
+    (agent-scope relaxed atomics for flavor 0).  Returns microseconds one way,
+    lost waits, and the XCC of each side."""
+    import torch
+
+    words = torch.zeros(64, dtype=torch.int64, device=device)
+    out = torch.zeros(4, dtype=torch.int64, device=device)
+    _bench_check(lib().mk_bench_pingpong(flavor, peer, rounds, words.data_ptr(), out.data_ptr(),
+                                         _stream_ptr(None)), "mk_bench_pingpong")
+    torch.cuda.synchronize()
+    ticks, lost, x0, x1 = (int(x) for x in out.cpu())
+    return {"us_one_way": ticks * 0.01 / rounds / 2.0, "lost": lost, "xcc": [x0, x1]}
+
+
+def bench_edge(n_wg: int, words: int, rounds: int, src=None, device="cuda:0") -> Dict[str, float]:
+    """One dependency edge at the decode step's size: every workgroup publishes
+    `words` tagged words and gathers all n_wg * words; with `src` (a uint8 device
+    tensor) four waves per workgroup stream it non-temporally into LDS meanwhile.
+    Returns microseconds per round and mismatches."""
+    import torch
+
+    data = torch.zeros(2 * n_wg * words, dtype=torch.int64, device=device)
+    out = torch.zeros(3, dtype=torch.int64, device=device)
+    s_ptr, s_bytes, mode = (None, 0, 0) if src is None else (src.data_ptr(), src.numel(), 2)
+    _bench_check(lib().mk_bench_edge(n_wg, words, rounds, mode, s_ptr, s_bytes, data.data_ptr(), out.data_ptr(),
+                                     _stream_ptr(None)), "mk_bench_edge")
+    torch.cuda.synchronize()
+    ticks, bad, kb = (int(x) for x in out.cpu())
+    return {"us_per_round": ticks * 0.01 / rounds, "mismatches": bad, "kb_streamed_wg0": kb}
+
+
+def bench_graph_gap(n_kernels: int, reps: int, blocks: int, device="cuda:0") -> float:
+    """Mean microseconds per kernel of a captured graph of n_kernels empty kernels."""
+    import torch
+
+    sink = torch.zeros(1, dtype=torch.int32, device=device)
+    us = ctypes.c_float(0.0)
+    torch.cuda.synchronize()
+    _bench_check(lib().mk_bench_graph_gap(n_kernels, reps, blocks, sink.data_ptr(), ctypes.byref(us),
+                                          _stream_ptr(torch.cuda.current_stream())), "mk_bench_graph_gap")
+    return float(us.value)

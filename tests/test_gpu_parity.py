@@ -389,8 +389,11 @@ def test_moe_b4_long_context():
     torch = _torch()
     ref_t, ref_l, got_t, got_l = [], [], [], []
     tok = start.astype(np.int32)
+    slots0, want_slots = d.moe_slots(), 0
     for _ in range(steps):
         nxt, logits, sel, prob = orc.step(tok, moe_trace=True)
+        # expert slots streamed per layer: the shared experts plus the batch's union
+        want_slots += sum(cfg.n_shared + len(set(sel[l].ravel().tolist())) for l in range(cfg.n_layers))
         # k-th and (k+1)-th probabilities of every routing decision well apart
         srt = -np.sort(-prob, axis=-1)
         gap = float((srt[..., cfg.top_k - 1] - srt[..., cfg.top_k]).min())
@@ -404,6 +407,8 @@ def test_moe_b4_long_context():
         tok = nxt.astype(np.int32)
     print(f"MoE done in {time.time() - t0:.1f}s", flush=True)
     compare(ref_t, ref_l, got_t, got_l, f"MoE b{B} ctx={ctx}")
+    # the kernel's count of streamed expert slots (the bench's byte count) is the oracle's
+    assert d.moe_slots() - slots0 == want_slots
     d.close()
 
 
