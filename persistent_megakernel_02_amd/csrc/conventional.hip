@@ -14,7 +14,15 @@ namespace mk {
 
 constexpr int kConvWaves = kComputeWaves;  // same wave count per item as the megakernel
 constexpr int kConvThreads = 64 * kConvWaves;
-constexpr uint32_t kRowsPerBlock = 16;
+constexpr uint32_t kRowsPerBlock = 16;       // most rows of a projection per workgroup
+constexpr uint32_t kHeadRowsPerBlock = 128;  // LM-head rows per workgroup (the input staging amortised)
+
+// Rows per workgroup of a projection with `total` rows: at most kRowsPerBlock, and
+// few enough that the grid covers every CU.
+__host__ __device__ inline uint32_t rows_per_block(uint32_t total, int n_cu) {
+    const uint32_t per_cu = (total + (uint32_t)n_cu - 1u) / (uint32_t)n_cu;
+    return per_cu < 1u ? 1u : per_cu > kRowsPerBlock ? kRowsPerBlock : per_cu;
+}
 
 struct BlockBarrier {
     __device__ __forceinline__ bool operator()() {
@@ -82,7 +90,7 @@ __device__ __forceinline__ void conv_rows_auto(const Params& P, const DevLayer& 
 
 // RMSNorm + rows: QKV, GATEUP (row pairs) and the LM head.
 template <int B, int OP>
-__global__ void __launch_bounds__(kConvThreads) k_norm_gemv(Params P, StepArgs A, int layer) {
+__global__ void __launch_bounds__(kConvThreads) k_norm_gemv(Params P, StepArgs A, int layer, uint32_t rpb) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     __shared__ float ssp[kMaxBatch][kConvWaves];
     float* xs = (float*)lds;
@@ -116,8 +124,8 @@ __global__ void __launch_bounds__(kConvThreads) k_norm_gemv(Params P, StepArgs A
 #pragma unroll
     for (int b = 0; b < B; ++b) r[b] = rms_scale(ssp[b], kConvWaves, P.d, P.eps);
     const uint32_t total = OP == OP_QKV ? (uint32_t)P.qkv_rows : OP == OP_GATEUP ? (uint32_t)P.F : (uint32_t)P.V;
-    const uint32_t begin = blockIdx.x * kRowsPerBlock;
-    const uint32_t count = min(kRowsPerBlock, total - begin);
+    const uint32_t begin = blockIdx.x * rpb;
+    const uint32_t count = min(rpb, total - begin);
     const uint32_t nrows = OP == OP_GATEUP ? 2u * count : count;
     const XLds x{xs, d};
     if (OP == OP_QKV) {
@@ -182,7 +190,7 @@ __global__ void __launch_bounds__(kConvThreads) k_norm_gemv(Params P, StepArgs A
 
 // O projection (is_down = 0) or down projection (is_down = 1) with residual add.
 template <int B>
-__global__ void __launch_bounds__(kConvThreads) k_proj(Params P, StepArgs A, int layer, int is_down) {
+__global__ void __launch_bounds__(kConvThreads) k_proj(Params P, StepArgs A, int layer, int is_down, uint32_t rpb) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     float* xs = (float*)lds;
     const int wave = threadIdx.x >> 6, lane = lane_id();
@@ -192,8 +200,8 @@ __global__ void __launch_bounds__(kConvThreads) k_proj(Params P, StepArgs A, int
     const uint32_t tag_x = is_down ? phase_tag(A.tag0, layer, 3) : phase_tag(A.tag0, layer, 1);
     const uint32_t tag_res = is_down ? phase_tag(A.tag0, layer, 2) : phase_tag(A.tag0, layer - 1, 4);
     const uint32_t tag_out = is_down ? phase_tag(A.tag0, layer, 4) : phase_tag(A.tag0, layer, 2);
-    const uint32_t begin = blockIdx.x * kRowsPerBlock;
-    const uint32_t count = min(kRowsPerBlock, (uint32_t)P.d - begin);
+    const uint32_t begin = blockIdx.x * rpb;
+    const uint32_t count = min(rpb, (uint32_t)P.d - begin);
     // DOWN runs over P.down_slices column slices of its input; partial sums wait in LDS
     const uint32_t ns = is_down ? (uint32_t)P.down_slices : 1u, Ks = K / ns;
     float* hres = xs + B * Ks;
@@ -266,7 +274,7 @@ __global__ void __launch_bounds__(kConvThreads) k_attn(Params P, StepArgs A, int
 // ------------------------------------------------------------------------------------------------
 int conventional_kernels_per_step(const Params& P) { return P.L * kPhasesPerLayer + 1; }
 
-int conventional_head_blocks(const Params& P) { return (int)((P.V + kRowsPerBlock - 1) / kRowsPerBlock); }
+int conventional_head_blocks(const Params& P) { return (int)((P.V + kHeadRowsPerBlock - 1) / kHeadRowsPerBlock); }
 
 template <int B, int HD>
 static hipError_t prepare_t(size_t lds) {
@@ -283,18 +291,21 @@ template <int B, int HD>
 static hipError_t launch_step_t(const Params& P, const StepArgs& A, hipStream_t st) {
     const dim3 blk(kConvThreads);
     const size_t lds = P.x_bytes;
-    const int qkv_blocks = (int)((P.qkv_rows + kRowsPerBlock - 1) / kRowsPerBlock);
-    const int d_blocks = (int)((P.d + kRowsPerBlock - 1) / kRowsPerBlock);
-    const int f_blocks = (int)((P.F + kRowsPerBlock - 1) / kRowsPerBlock);
+    const uint32_t qkv_rpb = rows_per_block((uint32_t)P.qkv_rows, P.n_cu);
+    const uint32_t d_rpb = rows_per_block((uint32_t)P.d, P.n_cu), f_rpb = rows_per_block((uint32_t)P.F, P.n_cu);
+    const int qkv_blocks = (int)((P.qkv_rows + qkv_rpb - 1) / qkv_rpb);
+    const int d_blocks = (int)((P.d + d_rpb - 1) / d_rpb);
+    const int f_blocks = (int)((P.F + f_rpb - 1) / f_rpb);
     const int items = P.B * P.Hkv * P.nsplit;
     for (int l = 0; l < P.L; ++l) {
-        hipLaunchKernelGGL((k_norm_gemv<B, OP_QKV>), dim3(qkv_blocks), blk, lds, st, P, A, l);
+        hipLaunchKernelGGL((k_norm_gemv<B, OP_QKV>), dim3(qkv_blocks), blk, lds, st, P, A, l, qkv_rpb);
         hipLaunchKernelGGL(k_attn<HD>, dim3(items), blk, lds, st, P, A, l);
-        hipLaunchKernelGGL(k_proj<B>, dim3(d_blocks), blk, lds, st, P, A, l, 0);
-        hipLaunchKernelGGL((k_norm_gemv<B, OP_GATEUP>), dim3(f_blocks), blk, lds, st, P, A, l);
-        hipLaunchKernelGGL(k_proj<B>, dim3(d_blocks), blk, lds, st, P, A, l, 1);
+        hipLaunchKernelGGL(k_proj<B>, dim3(d_blocks), blk, lds, st, P, A, l, 0, d_rpb);
+        hipLaunchKernelGGL((k_norm_gemv<B, OP_GATEUP>), dim3(f_blocks), blk, lds, st, P, A, l, f_rpb);
+        hipLaunchKernelGGL(k_proj<B>, dim3(d_blocks), blk, lds, st, P, A, l, 1, d_rpb);
     }
-    hipLaunchKernelGGL((k_norm_gemv<B, OP_HEAD>), dim3(conventional_head_blocks(P)), blk, lds, st, P, A, P.L);
+    hipLaunchKernelGGL((k_norm_gemv<B, OP_HEAD>), dim3(conventional_head_blocks(P)), blk, lds, st, P, A, P.L,
+                       kHeadRowsPerBlock);
     return hipGetLastError();
 }
 
