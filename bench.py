@@ -182,8 +182,11 @@ WORKLOADS = {
                   text="llama-3.2-1b-shape decode, batch 8, 8192-position synthetic bf16 KV context per sequence"),
     "8b": dict(model="LLAMA_8B", batch=1, prompt=128, ctx=0, horizon=256,
                text="llama-3-8b-shape decode, batch 1, 128 prompt tokens then greedy steps"),
-    "moe-b4": dict(model="MOE", batch=4, prompt=0, ctx=4096, horizon=128,
+    "moe-b4": dict(model="MOE", batch=4, prompt=0, ctx=4096, horizon=64,
                    text="synthetic MoE decode (64 experts, top 6, one shared), batch 4, 4096-position synthetic "
+                        "bf16 KV context per sequence"),
+    "moe-b8": dict(model="MOE", batch=8, prompt=0, ctx=4096, horizon=64,
+                   text="synthetic MoE decode (64 experts, top 6, one shared), batch 8, 4096-position synthetic "
                         "bf16 KV context per sequence"),
 }
 

@@ -101,13 +101,19 @@ size_t x_floats_kind(const mk_model_config* c, const mk_runtime_config* rt, int 
         bytes += mfma_red_bytes(b);
         return std::max((bytes + 3) / 4, attn_lds_floats((int)G, (int)hd, nsplit));
     }
-    size_t n = B * (size_t)c->hidden;
-    n = std::max(n, B * ((size_t)c->n_q_heads * hd + kMaxResidRows));
+    const int xsl = std::max(1, x_slices_for((int)B, c->hidden, c->n_q_heads * c->head_dim, c->n_experts > 0));
+    const size_t dw = (size_t)c->hidden / xsl, ow = (size_t)c->n_q_heads * hd / xsl;
+    // QKV / router: one input slice (and, sliced, the partial sums of at most
+    // kMaxResidRows rows); O: one input slice, the residual rows (and partial sums)
+    size_t n = B * (dw + (xsl > 1 ? kMaxResidRows : 0));
+    n = std::max(n, B * (ow + (xsl > 1 ? 2 : 1) * kMaxResidRows));
     if (c->n_experts > 0) {
-        // EGU: x rows and the router logits; EDOWN: one expert's SwiGLU rows, the
+        // EGU: x rows (one slice) and the router logits, and sliced the partial sums
+        // of every selected slot's rows; EDOWN: one expert's SwiGLU rows, the
         // residual rows, their sums and the router logits
         const size_t E = (size_t)c->n_experts;
-        n = std::max(n, B * ((size_t)c->hidden + E));
+        const size_t slots = (size_t)c->n_shared_experts + std::min(E, B * (size_t)c->top_k);
+        n = std::max(n, B * (dw + E) + (xsl > 1 ? slots * 2 * kMaxEguSlicedRows * B : 0));
         n = std::max(n, B * ((size_t)c->expert_ffn + 2 * kMaxResidRows + E) + B * (E + 1));
         return std::max(n, attn_lds_floats((int)G, (int)hd, nsplit));
     }
@@ -166,9 +172,12 @@ uint32_t max_wave_span(const mk_model_config* c, const mk_runtime_config* rt) {
     uint32_t span = 1u + 2u * (uint32_t)kAttnBlockGroups;
     if (use_mfma(c, rt)) return std::max(span, 16u / (uint32_t)kMfmaChunkRows);
     auto gemv = [&](uint32_t rb, bool pairs) { span = std::max(span, ring_batch_span(rb, B, pairs)); };
-    const uint32_t d2 = (uint32_t)c->hidden * 2u;
-    gemv(d2, false);                                                // QKV, LM head, MoE router
-    gemv((uint32_t)(c->n_q_heads * c->head_dim) * 2u, false);       // O
+    const uint32_t xsl = (uint32_t)std::max(1, x_slices_for(B, c->hidden, c->n_q_heads * c->head_dim,
+                                                            c->n_experts > 0));
+    const uint32_t d2 = (uint32_t)c->hidden * 2u / xsl;             // one input slice
+    gemv(d2, false);                                                // QKV, MoE router
+    gemv((uint32_t)c->hidden * 2u, false);                          // LM head (streamed, never sliced)
+    gemv((uint32_t)(c->n_q_heads * c->head_dim) * 2u / xsl, false); // O
     if (c->n_experts) {
         gemv(d2, true);                                             // expert (gate, up) pairs
         gemv((uint32_t)c->expert_ffn * 2u, false);                  // expert DOWN
@@ -212,6 +221,14 @@ mk_status validate(const mk_model_config* c, const mk_runtime_config* rt, std::s
     if (rt->max_batch < 1 || rt->max_batch > kMaxBatch) return fail(MK_E_UNSUPPORTED, "max_batch must be 1..8");
     if (!megakernel_supports(rt->max_batch, c->head_dim))
         return fail(MK_E_UNSUPPORTED, "this build runs batch 1, 2, 4 and 8");
+    if (moe) {
+        // hidden 4096 at batch 8: the hidden-wide inputs go in column slices, and the
+        // LM-head input is staged over the (then idle) weight ring
+        if (x_slices_for(rt->max_batch, c->hidden, c->n_q_heads * c->head_dim, true) == 0)
+            return fail(MK_E_UNSUPPORTED, "MoE: the inputs of this batch need column slices of whole 1 KB chunks");
+        if ((size_t)rt->max_batch * c->hidden * 4 > kLdsBytes - kStaticLds)
+            return fail(MK_E_UNSUPPORTED, "the LM-head input of this batch exceeds the LDS");
+    }
     if (rt->gemv_kind < 0 || rt->gemv_kind > 2) return fail(MK_E_UNSUPPORTED, "gemv_kind must be 0, 1 or 2");
     if (rt->gemv_kind == 2 && rt->mode != MK_MODE_MEGAKERNEL)
         return fail(MK_E_UNSUPPORTED, "the matrix-core GEMV runs in the megakernel only");
@@ -271,8 +288,11 @@ Plan build_plan(const mk_model_config* c, const mk_runtime_config* rt, int n_cu)
         ++pl.phases;
     };
     const uint32_t all = 0xFFFFFFFFu;
+    // sliced inputs: partial sums of every row of an instruction wait in LDS, so
+    // instructions are cut to the rows that area holds
+    const bool sliced = x_slices_for(B, c->hidden, c->n_q_heads * c->head_dim, c->n_experts > 0) > 1;
     for (int l = 0; l < L; ++l) {
-        gemv_phase(OP_QKV, l, qkv_rows, all);
+        gemv_phase(OP_QKV, l, qkv_rows, sliced ? kMaxResidRows : all);
         const uint32_t items = (uint32_t)(B * c->n_kv_heads * pl.nsplit * pl.hsplit);
         for (uint32_t it = 0; it < items; ++it) q[it % n_cu].push_back(mk_instr(OP_ATTN, l, it, 1));
         ++pl.phases;
@@ -280,8 +300,8 @@ Plan build_plan(const mk_model_config* c, const mk_runtime_config* rt, int n_cu)
         if (c->n_experts) {
             // router rows; then on every CU its f-range of every selected expert;
             // then its rows of every selected expert's down projection
-            gemv_phase(OP_ROUTE, l, (uint32_t)c->n_experts, all);
-            gemv_phase(OP_EGU, l, (uint32_t)c->expert_ffn, all);
+            gemv_phase(OP_ROUTE, l, (uint32_t)c->n_experts, sliced ? kMaxResidRows : all);
+            gemv_phase(OP_EGU, l, (uint32_t)c->expert_ffn, sliced ? kMaxEguSlicedRows : all);
             gemv_phase(OP_EDOWN, l, (uint32_t)c->hidden, kMaxResidRows);
         } else {
             gemv_phase(OP_GATEUP, l, (uint32_t)c->ffn, all);
@@ -309,6 +329,7 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
     // sub-phases per layer: QKV, ATTN, O, ROUTE (MoE), GATEUP / EGU, DOWN / EDOWN
     constexpr int kSub = 6;
     const bool moe = c->n_experts != 0;
+    const bool sliced = x_slices_for(B, c->hidden, c->n_q_heads * c->head_dim, moe) > 1;
     const int nphase = L * kSub + 1;
     std::vector<std::vector<uint8_t>> seen(nphase);
     auto phase_of = [&](const Instr& in) -> int {
@@ -345,6 +366,8 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
             const uint32_t ext = extent(ph);
             if (in.count == 0 || in.begin + in.count > ext || in.begin + in.count < in.begin) return 5;
             if ((in.op == OP_O || in.op == OP_DOWN || in.op == OP_EDOWN) && in.count > kMaxResidRows) return 4;
+            if (sliced && (in.op == OP_QKV || in.op == OP_ROUTE) && in.count > kMaxResidRows) return 4;
+            if (sliced && in.op == OP_EGU && in.count > kMaxEguSlicedRows) return 4;
             for (uint32_t r = in.begin; r < in.begin + in.count; ++r) {
                 if (seen[ph][r]) return 6;  // covered twice
                 seen[ph][r] = 1;
@@ -373,11 +396,17 @@ inline size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 void plan_counts(const mk_model_config* c, const mk_runtime_config* rt, int n, int nsplit, size_t* total,
                  size_t* per_cu) {
     const size_t items = (size_t)rt->max_batch * c->n_kv_heads * nsplit * auto_hsplit(c, rt, n, nsplit);
-    const size_t d_rows = ((size_t)c->hidden + n - 1) / n;
-    const size_t od = (d_rows + kMaxResidRows - 1) / kMaxResidRows;  // O / DOWN instructions per CU
-    const size_t route = c->n_experts ? 1 : 0;  // at most one router instruction per CU and layer
-    *per_cu = (size_t)c->n_layers * (2 + route + 2 * od + (items + n - 1) / n) + 1;
-    *total = (size_t)c->n_layers * ((2 + route) * (size_t)n + items + 2 * od * (size_t)n) + (size_t)n;
+    // instructions per CU of a phase of `rows` rows cut at `max_rows`
+    auto cut = [&](size_t rows, size_t max_rows) { return ((rows + n - 1) / n + max_rows - 1) / max_rows; };
+    const size_t od = cut((size_t)c->hidden, kMaxResidRows);  // O / DOWN instructions per CU
+    const bool moe = c->n_experts > 0;
+    const bool sliced = x_slices_for(rt->max_batch, c->hidden, c->n_q_heads * c->head_dim, moe) > 1;
+    const size_t qkv_rows = (size_t)(c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim;
+    const size_t qkv = sliced ? cut(qkv_rows, kMaxResidRows) : 1;  // sliced inputs: cut instructions
+    const size_t route = !moe ? 0 : sliced ? cut((size_t)c->n_experts, kMaxResidRows) : 1;
+    const size_t ffn = sliced ? cut((size_t)c->expert_ffn, kMaxEguSlicedRows) : 1;  // GATEUP / EGU
+    *per_cu = (size_t)c->n_layers * (qkv + route + ffn + 2 * od + (items + n - 1) / n) + 1;
+    *total = (size_t)c->n_layers * ((qkv + route + ffn) * (size_t)n + items + 2 * od * (size_t)n) + (size_t)n;
 }
 
 Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, int nsplit) {
@@ -635,6 +664,7 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
     P.F = cfg->ffn;
     P.gemv_mfma = use_mfma(cfg, rt) ? 1 : 0;
     P.down_slices = cfg->n_experts ? 1 : down_slices_for(rt->max_batch, cfg->ffn, P.gemv_mfma != 0);
+    P.x_slices = x_slices_for(rt->max_batch, cfg->hidden, cfg->n_q_heads * cfg->head_dim, cfg->n_experts > 0);
     P.E = cfg->n_experts;
     P.top_k = cfg->top_k;
     P.n_shared = cfg->n_experts ? cfg->n_shared_experts : 0;
@@ -691,6 +721,10 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
     if (P.ring_chunks < kMinRingChunks || P.n_head_slots > lo.head_slots ||
         h->plan.instrs.size() * sizeof(Instr) > lo.qoff - lo.instrs)
         return give_up(MK_E_UNSUPPORTED);
+    if (P.x_slices > 1 && (size_t)P.B * P.d * 4 > (size_t)P.ring_chunks * kChunk + P.x_bytes) {
+        h->last_error = "the LM-head input does not fit the ring and staging area";
+        return give_up(MK_E_UNSUPPORTED);
+    }
     if (rt->mode == MK_MODE_MEGAKERNEL && max_wave_span(cfg, rt) > P.ring_chunks) {
         h->last_error = "a compute wave's row batch does not fit the LDS ring";
         return give_up(MK_E_UNSUPPORTED);

@@ -232,12 +232,25 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 struct Stream {
     const char *p0, *p1, *p2;
     const char* head;     // ATTN: the (cos, sin) row streamed as chunk 0 ahead of the groups
-    uint32_t end0, end1;  // ranges: chunk ends of the first two ranges
+    uint32_t end0, end1;  // ranges: chunk ends of the first two ranges; sliced: row ends of the first two
     uint32_t per_shift;   // interleaved: log2(chunks of each matrix per turn); sliced: log2(chunks per row slice)
     int ncached;          // ATTN: valid positions of the split
     uint32_t nrow, row_bytes, slice_bytes;  // sliced (DOWN over column slices): rows, row stride, slice width
     bool inter, attn, sliced;
 };
+
+// Slice-major order of an instruction's rows (row_bytes each) over ns column
+// slices: the rows' first slices, then their second, ...; row ranges keep their
+// bases (end0 / end1 in rows).  Slices are whole power-of-two chunk counts.
+__device__ __forceinline__ bool slice_stream(Stream& S, uint32_t nrow, uint32_t row_bytes, uint32_t ns) {
+    S.sliced = true;
+    S.nrow = nrow;
+    S.row_bytes = row_bytes;
+    S.slice_bytes = row_bytes / ns;
+    const uint32_t cps = S.slice_bytes / kChunk;
+    S.per_shift = (uint32_t)__builtin_ctz(cps);
+    return (S.slice_bytes & (kChunk - 1u)) == 0 && cps != 0 && (cps & (cps - 1u)) == 0;
+}
 
 template <int HD>
 __device__ __forceinline__ bool setup_stream(const Params& P, const Instr& in, const DevLayer& Lw, const int32_t* ctx,
@@ -264,25 +277,30 @@ __device__ __forceinline__ bool setup_stream(const Params& P, const Instr& in, c
             S.p0 = (const char*)Lw.wq + (size_t)q0 * rb;
             S.p1 = (const char*)Lw.wk + (size_t)k0 * rb;
             S.p2 = (const char*)Lw.wv + (size_t)v0 * rb;
+            if (P.x_slices > 1) {  // rows of the three matrices, slice-major
+                S.end0 = q1 - q0;
+                S.end1 = S.end0 + (k1 - k0);
+                return slice_stream(S, in.count, rb, (uint32_t)P.x_slices);
+            }
             S.end0 = (q1 - q0) * cpr;
             S.end1 = S.end0 + (k1 - k0) * cpr;
             return true;
         }
-        case OP_O: rb = (uint32_t)(P.Hq * HD) * 2u; S.p0 = (const char*)uniform_p(Lw.wo) + (size_t)in.begin * rb; break;
+        case OP_O:
+            rb = (uint32_t)(P.Hq * HD) * 2u;
+            S.p0 = (const char*)uniform_p(Lw.wo) + (size_t)in.begin * rb;
+            if (P.x_slices > 1) return slice_stream(S, in.count, rb, (uint32_t)P.x_slices);
+            break;
         case OP_DOWN:
             rb = (uint32_t)P.F * 2u;
             S.p0 = (const char*)Lw.w_down + (size_t)in.begin * rb;
-            if (P.down_slices > 1) {
-                // slice-major: the rows' first column slices, then their second, ...
-                S.sliced = true;
-                S.nrow = in.count;
-                S.row_bytes = rb;
-                S.slice_bytes = rb / (uint32_t)P.down_slices;
-                S.per_shift = (uint32_t)__builtin_ctz(S.slice_bytes / kChunk);
-                return (S.slice_bytes & (kChunk - 1u)) == 0 && ((S.slice_bytes / kChunk) & (S.slice_bytes / kChunk - 1u)) == 0;
-            }
+            if (P.down_slices > 1) return slice_stream(S, in.count, rb, (uint32_t)P.down_slices);
             break;
-        case OP_ROUTE: rb = (uint32_t)P.d * 2u; S.p0 = (const char*)uniform_p(Lw.router) + (size_t)in.begin * rb; break;
+        case OP_ROUTE:
+            rb = (uint32_t)P.d * 2u;
+            S.p0 = (const char*)uniform_p(Lw.router) + (size_t)in.begin * rb;
+            if (P.x_slices > 1) return slice_stream(S, in.count, rb, (uint32_t)P.x_slices);
+            break;
         case OP_GATEUP: {
             rb = (uint32_t)P.d * 2u;
             const uint32_t cpr = rb / kChunk;
@@ -319,9 +337,18 @@ __device__ __forceinline__ const char* stream_chunk(const Stream& S, uint32_t c,
     const uint32_t lane16 = (uint32_t)lane_id() * 16u;
     if (S.sliced) {
         const uint32_t seg = c >> S.per_shift, within = c & ((1u << S.per_shift) - 1u);
-        const uint32_t slice = seg / S.nrow, row = seg - slice * S.nrow;
+        const uint32_t slice = seg / S.nrow;
+        uint32_t row = seg - slice * S.nrow;
+        const char* base = S.p0;
+        if (row >= S.end1) {
+            base = S.p2;
+            row -= S.end1;
+        } else if (row >= S.end0) {
+            base = S.p1;
+            row -= S.end0;
+        }
         voff = row * S.row_bytes + slice * S.slice_bytes + within * kChunk + lane16;
-        return S.p0;
+        return base;
     }
     if (!S.inter) {
         if (c < S.end0) {
@@ -581,6 +608,35 @@ __device__ __forceinline__ uint32_t loader_wave(const Params& P, Ctl* ctl, char*
                         X.inter = false;
                     }
                 };
+                if (egu && P.x_slices > 1) {
+                    // sliced input: slice-major over every selected slot: slice s of
+                    // slot a's (gate, up) row pairs, cps chunks per row slice
+                    const uint32_t sb = rb / (uint32_t)P.x_slices, cps = sb / kChunk, pss = 2u * in.count * cps;
+                    uint32_t x0 = c - cb, s0 = x0 / (n * pss);
+                    x0 -= s0 * n * pss;
+                    uint32_t a = x0 / pss, w = x0 - a * pss;
+                    for (; c < ce; ) {
+                        if (c >= limit && !make_room()) {
+                            stop = true;
+                            break;
+                        }
+                        const uint32_t xs_ = __builtin_amdgcn_readfirstlane((uint32_t)ctl->moe_list[a]);
+                        const uint32_t j = w / (2u * cps), half = (w / cps) & 1u, within = w % cps;
+                        const char* base = (const char*)ld_const(tab + (half ? nx : 0u) + xs_);
+                        const uint32_t voff = (in.begin + j) * rb + s0 * sb + within * kChunk + (uint32_t)lane_id() * 16u;
+                        dma_chunk_s(uniform_ptr(base), voff, slot);
+                        advance();
+                        for (w += NL; w >= pss;) {
+                            w -= pss;
+                            if (++a == n) {
+                                a = 0;
+                                ++s0;
+                            }
+                        }
+                    }
+                    cb = ce;
+                    continue;
+                }
                 uint32_t a = (c - cb) / per, w = (c - cb) - a * per;
                 if (a < n) slot_stream(a, S);
                 for (; c < ce; ) {
@@ -1369,6 +1425,167 @@ __device__ __forceinline__ bool moe_egu(const Params& P, const StepArgs& A, Ctl*
     return gemv_ring_auto<B>(P, ctl, ring, S, d * 2u, n * per, XLds{xs, d}, wave, land_wait, epi, true);
 }
 
+// QKV or router rows over column slices of their RMSNorm input (MoE models whose
+// B x hidden fp32 input does not fit next to the weight ring: hidden 4096 at batch
+// 8).  Per slice the compute waves stage h * g of the slice (the sums of squares
+// accumulate over the slices) and add every row's dot product over the slice to
+// its partial sum in LDS; after the last slice the rows are scaled by the RMSNorm
+// factor and stored.  The stream is slice-major (the rows' first slices, then
+// their second, ...).  The dot product of a row is the slice sums added in slice
+// order: the same value as the unsliced GEMV up to fp32 rounding order.
+template <int B>
+__device__ __forceinline__ bool norm_gemv_sliced(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring,
+                                                 float* xs, int wave, const Instr& in, uint32_t S, Spin& spin,
+                                                 CwBarrier& barrier, uint32_t& land_wait, uint32_t* tr) {
+    const int lane = lane_id();
+    const int layer = in.layer;
+    const DevLayer Lw = ld_const(P.layers + layer);
+    const bool qkv = in.op == OP_QKV;
+    const uint16_t* gain = uniform_p(qkv ? Lw.attn_norm : Lw.mlp_norm);
+    const uint32_t tag_in = qkv ? phase_tag(A.tag0, layer - 1, 4) : phase_tag(A.tag0, layer, 2);
+    const uint32_t tag_out = qkv ? phase_tag(A.tag0, layer, 0) : phase_tag(A.tag0, layer, 2);
+    const uint32_t d = (uint32_t)P.d, ns = (uint32_t)P.x_slices, Ks = d / ns, cnt = in.count;
+    float* part = xs + B * Ks;  // [B][cnt] partial sums
+    float ss[B], r[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) ss[b] = r[b] = 0.f;
+    for (uint32_t ks = 0; ks < ns; ++ks) {
+        if (ks > 0 && !barrier()) return false;  // every wave is done with the previous slice
+        if (qkv && layer == 0) {
+#pragma unroll
+            for (int b = 0; b < B; ++b)
+                stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * d + ks * Ks, Ks, xs + b * Ks,
+                           gain + ks * Ks, wave, kComputeWaves, ss[b]);
+        } else {
+            const StageSeg sg[1] = {{P.h + ks * Ks, xs, gain + ks * Ks, Ks, (uint32_t)B, d, Ks, tag_in}};
+            if (!stage_segs<stage_words<B>(), B, 1>(sg, wave, kComputeWaves, spin, ss)) return false;
+        }
+        const bool last = ks + 1 == ns;
+        if (last) {
+            wave_total_n<B>(ss);
+            if (lane == 0) {
+#pragma unroll
+                for (int b = 0; b < B; ++b) ctl->ss[b][wave] = ss[b];
+            }
+        }
+        if (!barrier()) return false;
+        if (tr && lane == 0 && ks == 0) tr[2] = (uint32_t)now_ticks();
+        if (last) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) r[b] = rms_scale(ctl->ss[b], kComputeWaves, P.d, P.eps);
+        }
+        auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
+            #pragma unroll
+            for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i) {
+                if (i >= nr) break;
+                const uint32_t j = r0 + i;
+                if (lane < B) {
+                    float v = pick<B>(res[i], lane);
+                    if (ks > 0) v = part[lane * cnt + j] + v;
+                    if (!last) {
+                        part[lane * cnt + j] = v;
+                    } else {
+                        uint64_t* dst = qkv ? P.qkv + (size_t)lane * P.qkv_rows : P.route + (size_t)lane * P.E;
+                        st_tagged(dst + in.begin + j, v * pick<B>(r, lane), tag_out);
+                    }
+                }
+            }
+        };
+        if (!gemv_ring_auto<B>(P, ctl, ring, S + ks * cnt * Ks * 2u, Ks * 2u, cnt, XLds{xs, Ks}, wave, land_wait, epi,
+                               false))
+            return false;
+        release_region(ctl, wave, S + (ks + 1u) * cnt * Ks * 2u);
+    }
+    return true;
+}
+
+// OP_EGU over column slices of x (see norm_gemv_sliced): slice 0 also stages the
+// router logits and routes; per slice every selected slot's (gate, up) row pairs
+// add their dot products over the slice to partial sums in LDS; after the last
+// slice the SwiGLU outputs are stored.  The stream is slice-major over the slots.
+template <int B>
+__device__ __forceinline__ bool moe_egu_sliced(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring,
+                                               float* xs, int wave, const Instr& in, uint32_t qi, uint32_t S,
+                                               Spin& spin, CwBarrier& barrier, uint32_t& land_wait, uint32_t* tr,
+                                               uint32_t& bytes) {
+    const int lane = lane_id();
+    const int layer = in.layer;
+    const DevLayer Lw = ld_const(P.layers + layer);
+    const uint32_t d = (uint32_t)P.d, E = (uint32_t)P.E, ns = (uint32_t)P.x_slices, Ks = d / ns;
+    const uint32_t tag_o = phase_tag(A.tag0, layer, 2), tag_out = phase_tag(A.tag0, layer, 3);
+    const uint16_t* gain = uniform_p(Lw.mlp_norm);
+    float* zeta = xs + B * Ks;     // [B][E] router logits
+    float* part = zeta + B * E;    // [row][B] partial sums of every selected slot's rows
+    const uint32_t per = 2u * in.count;
+    float ss[B], r[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) ss[b] = r[b] = 0.f;
+    uint32_t n = 0;
+    for (uint32_t ks = 0; ks < ns; ++ks) {
+        if (ks > 0 && !barrier()) return false;  // every wave is done with the previous slice
+        const StageSeg sx = {P.h + ks * Ks, xs, gain + ks * Ks, Ks, (uint32_t)B, d, Ks, tag_o, 0u};
+        if (ks == 0) {
+            const StageSeg sg[2] = {sx, {P.route, zeta, nullptr, E, (uint32_t)B, E, E, tag_o, 0u}};
+            if (!stage_segs<stage_words<B>(), B, 2>(sg, wave, kComputeWaves, spin, ss)) return false;
+        } else {
+            const StageSeg sg[1] = {sx};
+            if (!stage_segs<stage_words<B>(), B, 1>(sg, wave, kComputeWaves, spin, ss)) return false;
+        }
+        const bool last = ks + 1 == ns;
+        if (last) {
+            wave_total_n<B>(ss);
+            if (lane == 0) {
+#pragma unroll
+                for (int b = 0; b < B; ++b) ctl->ss[b][wave] = ss[b];
+            }
+        }
+        if (!barrier()) return false;
+        if (ks == 0) {
+            uint64_t sel[B];
+            float prob[B];
+            n = moe_route<B>(P, ctl, zeta, wave, qi, sel, prob);
+            if (in.begin == 0 && wave == 0 && lane == 0)
+                __hip_atomic_fetch_add(&P.state->moe_slots, (unsigned long long)n, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            if (!barrier()) return false;  // the slot list is visible
+            if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
+            bytes = moe_bytes(P, in, n);
+        }
+        if (last) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) r[b] = rms_scale(ctl->ss[b], kComputeWaves, P.d, P.eps);
+        }
+        auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
+            #pragma unroll
+            for (uint32_t i = 0; i + 1 < (uint32_t)(sizeof(res) / sizeof(res[0])); i += 2) {
+                if (i + 1 >= nr) break;
+                const uint32_t j = r0 + i;
+                if (lane < B) {
+                    float g = pick<B>(res[i], lane), u = pick<B>(res[i + 1], lane);
+                    if (ks > 0) {
+                        g = part[j * B + lane] + g;
+                        u = part[(j + 1u) * B + lane] + u;
+                    }
+                    if (!last) {
+                        part[j * B + lane] = g;
+                        part[(j + 1u) * B + lane] = u;
+                    } else {
+                        const uint32_t a = j / per, f = in.begin + (j - a * per) / 2u;
+                        const uint32_t x = ctl->moe_list[a];
+                        const float rr = pick<B>(r, lane);
+                        st_tagged(P.eact + ((size_t)x * P.B + lane) * P.Fe + f, silu_mul(g * rr, u * rr), tag_out);
+                    }
+                }
+            }
+        };
+        const uint32_t sl = n * per * Ks * 2u;  // stream bytes of one slice over every slot
+        if (!gemv_ring_auto<B>(P, ctl, ring, S + ks * sl, Ks * 2u, n * per, XLds{xs, Ks}, wave, land_wait, epi, true))
+            return false;
+        release_region(ctl, wave, S + (ks + 1u) * sl);
+    }
+    return true;
+}
+
 // OP_EDOWN: route again (same logits, same result); for every selected slot in
 // order (shared, then ascending experts) stage its SwiGLU rows and add its down
 // rows [begin, begin + count), weighted by the sequence's probability (1 for the
@@ -1507,6 +1724,12 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
             else if (in.op == OP_ATTN) ok = attn_instr<B, HD>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr, ctx);
         } else switch (in.op) {
             case OP_EGU:
+                if constexpr (MOE && B == kMaxBatch) {
+                    if (P.x_slices > 1) {
+                        ok = moe_egu_sliced<B>(P, A, ctl, ring, xs, wave, in, qi, S, spin, barrier, land_wait, tr, bytes);
+                        break;
+                    }
+                }
                 if constexpr (MOE) ok = moe_egu<B>(P, A, ctl, ring, xs, wave, in, qi, S, spin, barrier, land_wait, tr, bytes);
                 break;
             case OP_EDOWN:
@@ -1516,6 +1739,12 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
             case OP_GATEUP:
             case OP_ROUTE:
             case OP_HEAD: {
+                if constexpr (MOE && B == kMaxBatch) {
+                    if (P.x_slices > 1 && in.op != OP_HEAD) {
+                        ok = norm_gemv_sliced<B>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr);
+                        break;
+                    }
+                }
                 // (the gain pointer is chosen on the scalar unit: a plain select of the
                 // loaded pointers was lowered through a private array, i.e. scratch memory)
                 const uint16_t* gain =
@@ -1533,7 +1762,17 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
                         stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * d, d, xs + b * d, gain, wave,
                                    kComputeWaves, ss[b]);
                 } else {
-                    const StageSeg sg[1] = {{P.h, xs, gain, d, (uint32_t)B, d, d, tag_in}};
+                    float* xd = xs;
+                    if constexpr (MOE && B == kMaxBatch) {
+                        if (in.op == OP_HEAD && P.x_slices > 1) {
+                            // the LM-head input is wider than the staging area: it goes
+                            // over the weight ring, idle once every loader has retired
+                            // its last chunk (the loaders stop streaming at the head)
+                            if (!wait_landed(P, ctl, 0xFFFFFFFFu, land_wait)) return q1;
+                            xd = (float*)const_cast<char*>(ring);
+                        }
+                    }
+                    const StageSeg sg[1] = {{P.h, xd, gain, d, (uint32_t)B, d, d, tag_in}};
                     if (!stage_segs<stage_words<B>(), B, 1>(sg, wave, kComputeWaves, spin, ss)) return q1;
                 }
                 wave_total_n<B>(ss);
@@ -1606,9 +1845,9 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
                 const uint32_t tag_x = is_o ? phase_tag(A.tag0, layer, 1) : phase_tag(A.tag0, layer, 3);
                 const uint32_t tag_res = is_o ? phase_tag(A.tag0, layer - 1, 4) : phase_tag(A.tag0, layer, 2);
                 const uint32_t tag_out = is_o ? phase_tag(A.tag0, layer, 2) : phase_tag(A.tag0, layer, 4);
-                // DOWN runs over P.down_slices column slices of its input (the stream is
+                // O runs over P.x_slices and DOWN over P.down_slices column slices of its input (the stream is
                 // slice-major); partial sums of the rows wait in LDS between slices
-                const uint32_t ns = is_o ? 1u : (uint32_t)P.down_slices, Ks = K / ns;
+                const uint32_t ns = is_o ? (uint32_t)P.x_slices : (uint32_t)P.down_slices, Ks = K / ns;
                 float* hres = xs + B * Ks;         // [B][count] residual rows before this op
                 float* part = hres + B * in.count;  // [B][count] partial sums
                 for (uint32_t ks = 0; ks < ns && ok; ++ks) {
@@ -1750,7 +1989,9 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
         hi = compute_wave<B, HD, MF, MOE>(P, A, &ctl, ring, xs, wave, q0, q1, ctl.ctx);
     }
     if constexpr (!MF) {
-        if (hi < q1) head_instr<B>(P, A, &ctl, xs, wave, q0, hi);
+        float* hx = xs;
+        if constexpr (MOE && B == kMaxBatch) hx = P.x_slices > 1 ? (float*)ring : xs;  // staged over the ring
+        if (hi < q1) head_instr<B>(P, A, &ctl, hx, wave, q0, hi);
     }
 }
 

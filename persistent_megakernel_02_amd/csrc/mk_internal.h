@@ -82,6 +82,19 @@ __host__ __device__ constexpr int down_slices_for(int B, int F, bool mfma = fals
     return n;
 }
 
+// Column slices of the hidden-wide and attention-wide GEMV inputs (QKV, router,
+// expert gate/up, O): 1, except for MoE models whose B x hidden fp32 input does
+// not fit the LDS next to the weight ring (hidden 4096 at batch 8): then the fewest
+// power-of-two slices of at most kDownSliceBytes (0: no such slicing).
+__host__ __device__ constexpr int x_slices_for(int B, int hidden, int attn_width, bool moe) {
+    if (!moe || (size_t)B * (size_t)hidden * 4u <= kDownSliceBytes) return 1;
+    const int a = down_slices_for(B, hidden), b = down_slices_for(B, attn_width);
+    return (a == 0 || b == 0) ? 0 : (a > b ? a : b);
+}
+// f values of one expert (gate, up) instruction when its input is sliced: the
+// partial sums of every selected slot's rows wait in LDS between slices.
+constexpr uint32_t kMaxEguSlicedRows = 6;
+
 // Rows of one compute wave's batch for a row of `rb` bytes: about 8 KB per wave.
 // From batch 4 on two rows share each x piece read from LDS (one row per batch
 // left the wave waiting on LDS reads of x).
@@ -187,6 +200,7 @@ struct Params {
     int32_t qkv_rows, nsplit, n_cu, kv_b;      // kv_b = max_batch of the cache layout
     int32_t hsplit;                            // attention items per (sequence, KV head, split): q-head groups
     int32_t down_slices;                       // DOWN runs over F in this many column slices (power of 2)
+    int32_t x_slices;                          // QKV, router, expert gate/up and O inputs: column slices (power of 2)
     int32_t gemv_mfma;                         // 1: GEMVs on the matrix cores (tile-major weight chunks)
     int32_t E, top_k, n_shared, Fe;            // MoE: experts, selected per token, shared experts, expert width
     float eps, attn_scale;

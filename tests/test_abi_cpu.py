@@ -194,8 +194,9 @@ def test_moe_validation():
     # the persistent mode and the VALU GEMV only
     assert mk.mk_query_sizes(c, rt(4, 4200, mode=mk.MK_MODE_GRAPH))[0] == mk.MK_E_UNSUPPORTED
     assert mk.mk_query_sizes(c, mk.runtime_config(4, 4200, gemv_kind=mk.MK_GEMV_MFMA))[0] == mk.MK_E_UNSUPPORTED
-    # batch 8 would stage 8 x 4096 fp32 activations (128 KB) next to the ring
-    assert mk.mk_query_sizes(c, rt(8, 4200))[0] == mk.MK_E_UNSUPPORTED
+    # batch 8: the 8 x 4096 fp32 inputs (128 KB) go in two column slices
+    assert mk.mk_query_sizes(c, rt(8, 4200))[0] == mk.MK_OK
+    assert mk.mk_query_sizes(c, rt(8, 4200, mode=mk.MK_MODE_GRAPH))[0] == mk.MK_E_UNSUPPORTED
     for field, value, status in (("n_experts", 65, mk.MK_E_INVALID), ("top_k", 9, mk.MK_E_UNSUPPORTED),
                                  ("top_k", 0, mk.MK_E_INVALID), ("n_shared_experts", 2, mk.MK_E_UNSUPPORTED),
                                  ("expert_ffn", 1000, mk.MK_E_UNSUPPORTED)):
@@ -207,7 +208,8 @@ def test_moe_validation():
             assert mk.mk_query_sizes(bad, rt(4, 4200))[0] == status, field
 
 
-@pytest.mark.parametrize("cfg,batch", [(I.MOE, 4), (I.MOE, 1), (SMALL_MOE, 4)], ids=["moe-b4", "moe-b1", "small-b4"])
+@pytest.mark.parametrize("cfg,batch", [(I.MOE, 4), (I.MOE, 1), (SMALL_MOE, 4), (I.MOE, 8)],
+                         ids=["moe-b4", "moe-b1", "small-b4", "moe-b8"])
 @pytest.mark.parametrize("cus", [256, 7])
 def test_moe_schedule_verifies(cfg, batch, cus):
     st, info = mk.mk_plan_inspect(mk.model_config(cfg), rt(batch, 300), cus)
@@ -243,7 +245,11 @@ def _expected_span(cfg, batch, mfma):
     if mfma:
         return max(span, 8)
     d2 = 2 * cfg.hidden
-    spans = [batch_span(d2, False), batch_span(2 * cfg.n_q_heads * cfg.head_dim, False), batch_span(d2, True)]
+    xs = 1  # MoE inputs of hidden width beyond 64 KB at this batch go in column slices
+    while cfg.n_experts and batch * (cfg.hidden // xs) * 4 > 64 * 1024:
+        xs *= 2
+    spans = [batch_span(d2 // xs, False), batch_span(d2, False),
+             batch_span(2 * cfg.n_q_heads * cfg.head_dim // xs, False), batch_span(d2 // xs, True)]
     if cfg.n_experts:
         spans.append(batch_span(2 * cfg.expert_ffn, False))
     else:

@@ -371,14 +371,37 @@ def test_small_moe_parity(B, cus):
     d.close()
 
 
+# hidden 4096: at batch 8 the hidden-wide inputs go in two column slices
+WIDE_MOE = I.replace(I.TINY, name="wide-moe", hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=0,
+                     n_experts=8, top_k=2, n_shared=1, expert_ffn=512, tied=False, vocab=4096)
+
+
+@pytest.mark.parametrize("cus", [0, 7])
+def test_wide_moe_batch8_sliced_inputs(cus):
+    """Batch 8 at hidden 4096: the QKV, router, expert gate/up and O inputs in
+    two column slices (partial sums in LDS between slices) and the LM-head input
+    staged over the idle weight ring; against the oracle on 256 CUs and on 7
+    (where QKV and the expert gate/up rows are cut into many instructions)."""
+    cfg = WIDE_MOE
+    w = I.make_weights(cfg, seed=21)
+    prompt = I.make_prompt(cfg, 8, 5, seed=22)
+    rt_, rl = oracle_run(cfg, w, prompt, 6, 16)
+    print(f"case wide MoE b8 cus={cus}", flush=True)
+    d = _decoder(cfg, w, 8, 16, 0, num_cus=cus)
+    gt, gl = gpu_run(d, prompt, rt_, 6)
+    compare(rt_, rl, gt, gl, f"wide MoE b8 cus={cus}")
+    d.close()
+
+
 @pytest.mark.timeout(600)
-def test_moe_b4_long_context():
+@pytest.mark.parametrize("B,steps", [(4, 8), (8, 4)])
+def test_moe_long_context(B, steps):
     """The synthetic MoE shape (8 layers, hidden 4096, 64 experts, top 6, one
-    shared, expert width 1536) at batch 4 over a 4096-position synthetic context,
-    8 steps; the oracle's routing is checked for near ties first (a near tie could
+    shared, expert width 1536) at batch 4 and 8 over a 4096-position synthetic
+    context; the oracle's routing is checked for near ties first (a near tie could
     select a different expert on either side)."""
     cfg = I.MOE
-    B, ctx, steps = 4, 4096, 8
+    ctx = 4096
     t0 = time.time()
     w = I.make_weights(cfg, seed=14)
     print(f"MoE weights generated in {time.time() - t0:.1f}s", flush=True)
