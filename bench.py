@@ -109,6 +109,35 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def prefill_latency(dec, prompt_dev, reps: int = 10) -> dict:
+    """Time to process the prompt (first token's latency without queueing): mk_prefill
+    (launches of up to 8 prompt positions in the persistent mode) against one decode
+    launch per prompt position; median over `reps`, µs, events on the launch stream."""
+    import numpy as np
+    import torch
+
+    B, P = prompt_dev.shape
+    out = {}
+    for name in ("multi_position", "one_position_per_launch"):
+        times = []
+        for r in range(reps + 2):
+            dec.set_context_len([0] * B)  # synchronises
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(dec.stream)
+            if name == "multi_position":
+                dec.prefill(prompt_dev)
+            else:
+                for t in range(P):
+                    dec.decode_step(prompt_dev[:, t].contiguous())
+            e1.record(dec.stream)
+            e1.synchronize()
+            if r >= 2:
+                times.append(e0.elapsed_time(e1) * 1000.0)
+        out[f"us_{name}"] = round(float(np.median(times)), 1)
+    out["prompt_tokens"] = int(P)
+    return out
+
+
 def micro_benchmarks(dev, n_cu: int) -> dict:
     """The synchronisation and launch costs the persistent kernel is built
     around: the gap one kernel boundary costs inside a replayed hipGraph, an
@@ -323,6 +352,12 @@ def main() -> int:
     gemv_used = mk.mk_plan_inspect(mk.model_config(cfg), mk.runtime_config(B, max_seq, gemv_kind=gemv),
                                    torch.cuda.get_device_properties(dev).multi_processor_count)[1]["gemv_kind"]
     us_mk, positions, kps_mk, per_h, pct_mk, slots_step = run_path(mk.MK_MODE_MEGAKERNEL, "megakernel")
+    prefill = None
+    if CTX == 0:
+        pdec = mk.Decoder(cfg, w, max_batch=B, max_seq=max_seq, device="cuda:0", device_weights=dw)
+        prefill = prefill_latency(pdec, prompt_dev)
+        pdec.close()
+        log(f"prefill of {prefill['prompt_tokens']} tokens: {prefill}")
     # every sequence at position p; MoE: the expert slots the kernel counted, mean per step
     bytes_step = [step_bytes(cfg, B, [p], slots_step) for p in positions]
     mean_bytes = float(np.mean(bytes_step))
@@ -417,6 +452,7 @@ def main() -> int:
                      "bytes_per_launch": int(mean_bytes), "traffic_source": traffic_src},
         "cpu_baseline": cpu,
         "micro": micro,
+        "prefill": prefill,
     }
     print(json.dumps(out), flush=True)
     return 0

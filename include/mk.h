@@ -177,10 +177,15 @@ mk_status mk_create_static(const mk_model_config* cfg, const mk_weights* w, cons
 mk_status mk_kv_layout(const mk_handle* h, int64_t strides_out[5]);
 
 /* Feed a prompt [LOW: the headline workload first consumes a 32-token prompt,
- * then decodes greedily].  d_tokens: device int32 [B, P] row-major, read only.
- * Runs P decode steps in the handle's mode (each one launch in the persistent
- * mode [MK]); positions continue from the current context lengths and every
- * context grows by P.  Writes the last position's logits to d_logits (device
+ * then decodes greedily; page "一个大内核不够：在哪里切分流式推理模型", section
+ * "为什么切在哪里比融不融更关键": the prompt is processed once, before the decode
+ * loop, and sets the first token's latency].  d_tokens: device int32 [B, P]
+ * row-major, read only.  In the persistent mode, when the handle carries the
+ * multi-position plan (see mk_verify_step), each sequence's prompt runs in
+ * launches of up to 8 positions (causal attention within the launch, every
+ * position's K/V appended); otherwise, and in the graph mode, it runs as P decode
+ * steps.  Positions continue from the current context lengths and every context
+ * grows by P.  Writes the last position's logits to d_logits (device
  * fp32 [B, V]) and its greedy tokens to d_next (device int32 [B]); the other
  * positions' logits land in the workspace.  Enqueued on `stream`; returns after
  * host-side checks.  B must equal max_batch (the schedule, the staging areas and
@@ -190,6 +195,25 @@ mk_status mk_kv_layout(const mk_handle* h, int64_t strides_out[5]);
  * max_seq; MK_E_STATE / MK_E_DEVICE_* when a device error is latched. */
 mk_status mk_prefill(mk_handle* h, const int32_t* d_tokens, int32_t B, int32_t P, float* d_logits,
                      int32_t* d_next, void* stream);
+
+/* Several positions of ONE sequence in one persistent launch [page
+ * "16块谷歌TPU v7跑Kimi K3，每秒跑出了709个Token，比老黄的GB200快了57%", section
+ * "不异16块芯片，TPU快57%": a draft model proposes several tokens and the target
+ * model checks them in one pass, accepting about six per pass].  d_tokens: device
+ * int32 [n], 1 <= n <= 8: tokens at positions ctx .. ctx + n - 1 of sequence
+ * `seq` (0 <= seq < max_batch), ctx its current context length.  Every position
+ * attends to the sequence's cache and to the earlier positions of the call
+ * (causal), and appends its K/V.  Writes the logits of every position to d_logits
+ * (device fp32 [n, V]) and their greedy tokens to d_next (device int32 [n]); the
+ * context grows by n (to accept fewer draft tokens, set the length back with
+ * mk_set_context_len; later steps overwrite the rejected positions).  The same
+ * launch serves mk_prefill.  Available in the persistent mode for configurations
+ * whose batch-8 layout fits (MK_E_UNSUPPORTED otherwise: hidden 4096 dense
+ * models); MK_E_INVALID for bad arguments, MK_E_CAPACITY past max_seq,
+ * MK_E_STATE / MK_E_DEVICE_* when a device error is latched.  Enqueued on
+ * `stream`. */
+mk_status mk_verify_step(mk_handle* h, int32_t seq, const int32_t* d_tokens, int32_t n, float* d_logits,
+                         int32_t* d_next, void* stream);
 
 /* Set the context length of each sequence after the caller filled the KV cache
  * directly (e.g. a synthetic context) [LOW: the low-concurrency measurements

@@ -16,8 +16,8 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmk.so")
-SOURCES = ["mk_kernels_valu.hip", "mk_kernels_mfma.hip", "mk_kernels_moe.hip", "host.hip", "megakernel.hip",
-           "conventional.hip", "bench_kernels.hip"]
+SOURCES = ["mk_kernels_valu.hip", "mk_kernels_mfma.hip", "mk_kernels_moe.hip", "mk_kernels_chunk.hip", "host.hip",
+           "megakernel.hip", "conventional.hip", "bench_kernels.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          # packed fp32 VALU forms stay off (v_pk_fma_f32 and friends)

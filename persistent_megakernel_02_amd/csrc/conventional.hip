@@ -108,7 +108,7 @@ __global__ void __launch_bounds__(kConvThreads) k_norm_gemv(Params P, StepArgs A
     if (OP == OP_QKV && layer == 0) {
 #pragma unroll
         for (int b = 0; b < B; ++b)
-            stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * d, d, xs + b * d, gain, wave, kConvWaves,
+            stage_bf16(P.embed + token_row(A, b, P.V) * d, d, xs + b * d, gain, wave, kConvWaves,
                        ss[b]);
     } else {
         const StageSeg sg[1] = {{P.h, xs, gain, d, (uint32_t)B, d, d, tag_in}};
@@ -216,7 +216,7 @@ __global__ void __launch_bounds__(kConvThreads) k_proj(Params P, StepArgs A, int
         } else if (!is_down && layer == 0) {
 #pragma unroll
             for (int b = 0; b < B; ++b)
-                stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * P.d + begin, count, hres + b * count,
+                stage_bf16(P.embed + token_row(A, b, P.V) * P.d + begin, count, hres + b * count,
                            nullptr, wave, kConvWaves, ss[0]);
             const StageSeg sg[1] = {sx};
             if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kConvWaves, spin, ss)) return;
@@ -256,7 +256,7 @@ __global__ void __launch_bounds__(kConvThreads) k_attn(Params P, StepArgs A, int
     const int item = blockIdx.x;
     const int per_b = P.Hkv * P.nsplit;
     const int b = item / per_b, g = (item % per_b) / P.nsplit, s = item % P.nsplit;
-    const int p = P.state->ctx_len[b];
+    const int p = P.ctx_len[b];
     const SplitRange R = split_range<HD>(p, s, P.nsplit);
     const size_t base = (((size_t)layer * P.kv_b + b) * P.Hkv + g) * (size_t)P.S * HD;
     const GlobalKV<HD> kv{P.kcache + base, P.vcache + base, R.s0, max(0, R.s0 + R.ncached - 1),
@@ -266,7 +266,8 @@ __global__ void __launch_bounds__(kConvThreads) k_attn(Params P, StepArgs A, int
     BlockBarrier barrier;
     Spin spin(&P, nullptr);
     auto mark = [](int) {};
-    attn_item<HD>(P, A.tag0, layer, b, g, s, 0, P.G, p, kv, need, release, barrier, xs, wave, kConvWaves, spin, mark);
+    attn_item<HD, false>(P, A.tag0, layer, b, g, s, 0, P.G, p, p, 1, b, true, kv, need, release, barrier, xs, wave, kConvWaves,
+                  spin, mark);
 }
 
 // ------------------------------------------------------------------------------------------------

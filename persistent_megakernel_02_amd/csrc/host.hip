@@ -60,7 +60,7 @@ uint32_t ring_chunks_for(size_t x_bytes) {
     return x_bytes >= avail ? 0u : (uint32_t)((avail - x_bytes) / kChunk);
 }
 
-size_t x_floats_kind(const mk_model_config* c, const mk_runtime_config* rt, int nsplit, bool mfma);
+size_t x_floats_kind(const mk_model_config* c, const mk_runtime_config* rt, int nsplit, bool mfma, int nnew = 1);
 
 // Row lengths of the matrix-core instructions are whole tile units.
 bool mfma_shapes_ok(const mk_model_config* c, int B) {
@@ -87,7 +87,7 @@ bool use_mfma(const mk_model_config* c, const mk_runtime_config* rt) {
 
 // LDS floats of activations one instruction stages (x rows, residual rows of
 // O / DOWN, or an attention item's area).
-size_t x_floats_kind(const mk_model_config* c, const mk_runtime_config* rt, int nsplit, bool mfma) {
+size_t x_floats_kind(const mk_model_config* c, const mk_runtime_config* rt, int nsplit, bool mfma, int nnew) {
     const size_t B = (size_t)rt->max_batch, hd = (size_t)c->head_dim, G = (size_t)(c->n_q_heads / c->n_kv_heads);
     if (mfma) {
         // bf16 parts of the input (one column slice for DOWN), the residual rows and
@@ -99,7 +99,7 @@ size_t x_floats_kind(const mk_model_config* c, const mk_runtime_config* rt, int 
         bytes = std::max(bytes, parts_bytes(b, c->n_q_heads * c->head_dim) + resid);
         bytes = std::max(bytes, parts_bytes(b, c->ffn / ns) + resid);
         bytes += mfma_red_bytes(b);
-        return std::max((bytes + 3) / 4, attn_lds_floats((int)G, (int)hd, nsplit));
+        return std::max((bytes + 3) / 4, attn_lds_floats((int)G, (int)hd, nsplit, nnew));
     }
     const int xsl = std::max(1, x_slices_for((int)B, c->hidden, c->n_q_heads * c->head_dim, c->n_experts > 0));
     const size_t dw = (size_t)c->hidden / xsl, ow = (size_t)c->n_q_heads * hd / xsl;
@@ -115,16 +115,17 @@ size_t x_floats_kind(const mk_model_config* c, const mk_runtime_config* rt, int 
         const size_t slots = (size_t)c->n_shared_experts + std::min(E, B * (size_t)c->top_k);
         n = std::max(n, B * (dw + E) + (xsl > 1 ? slots * 2 * kMaxEguSlicedRows * B : 0));
         n = std::max(n, B * ((size_t)c->expert_ffn + 2 * kMaxResidRows + E) + B * (E + 1));
-        return std::max(n, attn_lds_floats((int)G, (int)hd, nsplit));
+        return std::max(n, attn_lds_floats((int)G, (int)hd, nsplit, nnew));
     }
     // DOWN: one column slice of the input, the residual rows and the partial sums
     const int ns = std::max(1, down_slices_for((int)B, c->ffn));
     n = std::max(n, B * ((size_t)(c->ffn / ns) + 2 * kMaxResidRows));
-    return std::max(n, attn_lds_floats((int)G, (int)hd, nsplit));
+    return std::max(n, attn_lds_floats((int)G, (int)hd, nsplit, nnew));
 }
 
-size_t x_bytes_for(const mk_model_config* c, const mk_runtime_config* rt, int nsplit) {
-    return (x_floats_kind(c, rt, nsplit, use_mfma(c, rt)) * 4 + 15) & ~(size_t)15;
+// nnew: new positions one attention item holds (kChunkRows for a multi-position plan)
+size_t x_bytes_for(const mk_model_config* c, const mk_runtime_config* rt, int nsplit, int nnew = 1) {
+    return (x_floats_kind(c, rt, nsplit, use_mfma(c, rt), nnew) * 4 + 15) & ~(size_t)15;
 }
 
 // Most KV splits whose merge area still leaves the minimum weight ring (0: none).
@@ -437,8 +438,11 @@ Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, i
     lo.eact = take(nx * B * (size_t)c->expert_ffn * 8);
     lo.eptr = take((size_t)c->n_layers * 3 * nx * 8);
     lo.attn_part = take(B * c->n_kv_heads * nsplit * G * (hd + 2) * 8);
+    // argmax partial slots: one LM-head instruction per CU (persistent), or the
+    // one-kernel-per-op path's head workgroups (bounded by one per 16 rows)
     const size_t conv_blocks = ((size_t)c->vocab + 15) / 16;
-    lo.head_slots = std::max((size_t)n_cu, conv_blocks) * (kComputeWaves + kLoaderWaves);
+    lo.head_slots = (rt->mode == MK_MODE_GRAPH ? std::max((size_t)n_cu, conv_blocks) : (size_t)n_cu) *
+                    (kComputeWaves + kLoaderWaves);
     lo.head_part = take(lo.head_slots * B * 2 * 8);
     lo.logits_scr = take(B * c->vocab * 4);
     lo.tok_scr = take(B * 4);
@@ -468,6 +472,44 @@ int device_cus() {
 
 int resolve_cus(const mk_runtime_config* rt) { return rt->num_cus > 0 ? rt->num_cus : device_cus(); }
 
+// The multi-position plan of a persistent decode handle: kChunkRows rows of one
+// sequence per launch (prompt chunks, draft verification), VALU GEMVs, one
+// attention split per item.
+mk_runtime_config chunk_rt(const mk_runtime_config* rt) {
+    mk_runtime_config r = *rt;
+    r.max_batch = kChunkRows;
+    r.mode = MK_MODE_MEGAKERNEL;
+    r.gemv_kind = 1;
+    r.attn_splits = 1;
+    r.trace = 0;
+    return r;
+}
+
+// Whether a handle of this configuration carries the multi-position plan.
+bool chunk_supported(const mk_model_config* c, const mk_runtime_config* rt) {
+    if (rt->mode != MK_MODE_MEGAKERNEL) return false;
+    const mk_runtime_config r = chunk_rt(rt);
+    if (validate(c, &r, nullptr) != MK_OK) return false;
+    const uint32_t ring = ring_chunks_for(x_bytes_for(c, &r, 1, kChunkRows));
+    return ring >= kMinRingChunks && max_wave_span(c, &r) <= ring;
+}
+
+// Workspace bytes of a handle on n CUs: the decode plan's layout, then (when
+// supported) the multi-position plan's.
+size_t handle_bytes(const mk_model_config* c, const mk_runtime_config* rt, int n, Layout* main_lo, Layout* chunk_lo) {
+    const Layout m = layout(c, rt, n, auto_splits(c, rt, n));
+    size_t total = (m.total + 255) & ~(size_t)255;
+    Layout k{};
+    if (chunk_supported(c, rt)) {
+        const mk_runtime_config r = chunk_rt(rt);
+        k = layout(c, &r, n, 1);
+        total += k.total;
+    }
+    if (main_lo) *main_lo = m;
+    if (chunk_lo) *chunk_lo = k;
+    return total;
+}
+
 }  // namespace
 
 struct mk_handle {
@@ -491,6 +533,13 @@ struct mk_handle {
     bool latched = false;
     mk_status latched_status = MK_OK;
     std::string last_error;
+    // multi-position plan (persistent mode, when supported): its own workspace
+    // region after the decode plan's, the decode plan's KV cache and context lengths
+    bool chunk_ok = false;
+    Plan cplan;
+    Layout clo;
+    Params cP;
+    size_t coff = 0;
     // graph mode
     hipGraphExec_t gexec = nullptr;
     hipGraph_t graph = nullptr;
@@ -552,8 +601,7 @@ mk_status mk_query_sizes(const mk_model_config* cfg, const mk_runtime_config* rt
     // the compute-unit count may be resolved only at mk_create: size for every count up to the bound
     const int n_max = rt->num_cus > 0 ? rt->num_cus : kMaxCus;
     size_t ws = 0;
-    for (int n = rt->num_cus > 0 ? n_max : 1; n <= n_max; ++n)
-        ws = std::max(ws, layout(cfg, rt, n, auto_splits(cfg, rt, n)).total);
+    for (int n = rt->num_cus > 0 ? n_max : 1; n <= n_max; ++n) ws = std::max(ws, handle_bytes(cfg, rt, n, nullptr, nullptr));
     *workspace_bytes = ws;
     *kv_bytes = 2ull * cfg->n_layers * rt->max_batch * cfg->n_kv_heads * (size_t)rt->max_seq * cfg->head_dim * 2;
     return MK_OK;
@@ -631,7 +679,10 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
         delete h;
         return MK_E_INVALID;
     }
-    h->lo = layout(cfg, rt, n_cu, h->plan.nsplit);
+    const size_t hb = handle_bytes(cfg, rt, n_cu, &h->lo, &h->clo);
+    h->coff = (h->lo.total + 255) & ~(size_t)255;
+    h->chunk_ok = chunk_supported(cfg, rt);
+    if (h->chunk_ok && workspace_bytes < hb) h->chunk_ok = false;  // (a static array too small for it)
     if (workspace_bytes < h->lo.total || (static_dev < 0 && workspace_bytes < need_ws) || kv_bytes < need_kv) {
         delete h;
         return static_dev < 0 ? MK_E_INVALID : MK_E_CAPACITY;
@@ -703,6 +754,8 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
     P.attn_ticket = (uint32_t*)(ws + lo.tickets);
     P.head_ticket = P.attn_ticket + (size_t)cfg->n_layers * rt->max_batch * cfg->n_kv_heads * kCtrStride;
     P.state = (DevState*)(ws + lo.state);
+    P.ctx_len = (int32_t*)(ws + lo.state + offsetof(DevState, ctx_len));
+    P.chunk = 0;
     P.host_err = h->host_err_dev;
     P.instrs = (const Instr*)(ws + lo.instrs);
     P.queue_off = (const uint32_t*)(ws + lo.qoff);
@@ -755,6 +808,52 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
     const uint32_t tmo = rt->spin_timeout_ms ? rt->spin_timeout_ms : 2000u;
     P.spin_ticks = (uint64_t)tmo * 100000ull;
 
+    // ---- the multi-position plan: same weights, KV cache, context lengths and error
+    // state as the decode plan; its own schedule, activations and tickets
+    if (h->chunk_ok) {
+        const mk_runtime_config r8 = chunk_rt(rt);
+        h->cplan = build_plan(cfg, &r8, n_cu);
+        Params& C = h->cP;
+        C = P;
+        char* cb = ws + h->coff;
+        const Layout& cl = h->clo;
+        C.B = kChunkRows;
+        C.gemv_mfma = 0;
+        C.down_slices = cfg->n_experts ? 1 : down_slices_for(kChunkRows, cfg->ffn, false);
+        C.x_slices = x_slices_for(kChunkRows, cfg->hidden, cfg->n_q_heads * cfg->head_dim, cfg->n_experts > 0);
+        C.nsplit = h->cplan.nsplit;
+        C.hsplit = h->cplan.hsplit;
+        C.layers = (const DevLayer*)(cb + cl.layers);
+        C.rope = (const float2*)(cb + cl.rope);
+        C.h = (uint64_t*)(cb + cl.h);
+        C.qkv = (uint64_t*)(cb + cl.qkv);
+        C.attn = (uint64_t*)(cb + cl.attn);
+        C.act = (uint64_t*)(cb + cl.act);
+        C.attn_part = (uint64_t*)(cb + cl.attn_part);
+        C.head_part = (uint64_t*)(cb + cl.head_part);
+        C.route = (uint64_t*)(cb + cl.route);
+        C.eact = (uint64_t*)(cb + cl.eact);
+        C.eptr = (const uint16_t* const*)(cb + cl.eptr);
+        C.attn_ticket = (uint32_t*)(cb + cl.tickets);
+        C.head_ticket = C.attn_ticket + (size_t)cfg->n_layers * kChunkRows * cfg->n_kv_heads * kCtrStride;
+        C.instrs = (const Instr*)(cb + cl.instrs);
+        C.queue_off = (const uint32_t*)(cb + cl.qoff);
+        C.x_bytes = (uint32_t)x_bytes_for(cfg, &r8, C.nsplit, kChunkRows);
+        C.ring_chunks = ring_chunks_for(C.x_bytes);
+        C.n_head_slots = h->cplan.n_head * (uint32_t)(kComputeWaves + kLoaderWaves);
+        C.trace = nullptr;
+        C.trace_stride = 0;
+        C.inject = 0;
+        C.chunk = 1;
+        C.chunk_seq = 0;
+        h->chunk_ok = verify_plan(cfg, &r8, h->cplan) == 0 && C.nsplit == 1 && C.ring_chunks >= kMinRingChunks &&
+                      C.n_head_slots <= cl.head_slots &&
+                      h->cplan.instrs.size() * sizeof(Instr) <= cl.qoff - cl.instrs &&
+                      max_wave_span(cfg, &r8) <= C.ring_chunks &&
+                      (C.x_slices == 1 || (size_t)C.B * C.d * 4 <= (size_t)C.ring_chunks * kChunk + C.x_bytes) &&
+                      prepare_megakernel(C) == hipSuccess;
+    }
+
     // ---- uploads (synchronous; create is not on the hot path)
     std::vector<DevLayer> dl(cfg->n_layers);
     for (int l = 0; l < cfg->n_layers; ++l) {
@@ -791,12 +890,20 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
     auto cp = [&](size_t off, const void* src, size_t bytes) {
         if (e == hipSuccess && bytes) e = hipMemcpyAsync(ws + off, src, bytes, hipMemcpyHostToDevice, h->stream);
     };
-    if (e == hipSuccess) e = hipMemsetAsync(ws, 0, lo.total, h->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(ws, 0, h->chunk_ok ? h->coff + h->clo.total : lo.total, h->stream);
     cp(lo.instrs, h->plan.instrs.data(), h->plan.instrs.size() * sizeof(Instr));
     cp(lo.qoff, h->plan.qoff.data(), h->plan.qoff.size() * 4);
     cp(lo.layers, dl.data(), dl.size() * sizeof(DevLayer));
     cp(lo.rope, rope.data(), rope.size() * 4);
     cp(lo.eptr, ep.data(), ep.size() * sizeof(void*));
+    if (h->chunk_ok) {
+        const Layout& cl = h->clo;
+        cp(h->coff + cl.instrs, h->cplan.instrs.data(), h->cplan.instrs.size() * sizeof(Instr));
+        cp(h->coff + cl.qoff, h->cplan.qoff.data(), h->cplan.qoff.size() * 4);
+        cp(h->coff + cl.layers, dl.data(), dl.size() * sizeof(DevLayer));
+        cp(h->coff + cl.rope, rope.data(), rope.size() * 4);
+        cp(h->coff + cl.eptr, ep.data(), ep.size() * sizeof(void*));
+    }
     if (e == hipSuccess) e = hipMemsetAsync(d_kv, 0, need_kv, h->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
     if (e != hipSuccess) {
@@ -889,6 +996,7 @@ static mk_status run_step(mk_handle* h, const int32_t* tok_in, int32_t stride, i
     std::memset(&A, 0, sizeof(A));
     A.tok_in = tok_in;
     A.tok_stride = stride;
+    A.tok_rows = h->rt.max_batch;
     A.tok_out = tok_out;
     A.logits = logits;
     A.tag0 = (++h->epoch) * tags_per_step(h->cfg.n_layers);
@@ -950,6 +1058,29 @@ mk_status mk_decode_step(mk_handle* h, const int32_t* d_tokens_in, int32_t B, in
     return run_step(h, d_tokens_in, 1, d_tokens_out, d_logits, (hipStream_t)stream);
 }
 
+// One multi-position launch: rows 0..n-1 are tokens tok[0..n-1] of sequence seq at
+// positions ctx[seq] .. ctx[seq] + n - 1 (later rows repeat the last token, and
+// their results are ignored); logits and greedy tokens of all rows land in the
+// plan's scratch rows; the sequence advances by n on the device.
+static mk_status run_chunk(mk_handle* h, int seq, const int32_t* tok, int n, hipStream_t st) {
+    if (h->ctx[seq] + n > h->rt.max_seq) return MK_E_CAPACITY;
+    StepArgs A;
+    std::memset(&A, 0, sizeof(A));
+    A.tok_in = tok;
+    A.tok_stride = 1;
+    A.tok_rows = n;
+    A.tok_out = (int32_t*)(h->ws + h->coff + h->clo.tok_scr);
+    A.logits = (float*)(h->ws + h->coff + h->clo.logits_scr);
+    A.tag0 = (++h->epoch) * tags_per_step(h->cfg.n_layers);
+    Params C = h->cP;
+    C.chunk_seq = seq;
+    HIPCHK(h, launch_megakernel(C, A, st));
+    h->ctx[seq] += n;
+    h->last_stream = st;
+    h->used = true;
+    return MK_OK;
+}
+
 mk_status mk_prefill(mk_handle* h, const int32_t* d_tokens, int32_t B, int32_t P, float* d_logits, int32_t* d_next,
                      void* stream) {
     if (!h || !d_tokens || !d_logits || !d_next || P <= 0) return MK_E_INVALID;
@@ -958,6 +1089,26 @@ mk_status mk_prefill(mk_handle* h, const int32_t* d_tokens, int32_t B, int32_t P
     if (s != MK_OK) return s;
     for (int b = 0; b < B; ++b)
         if (h->ctx[b] + P > h->rt.max_seq) return MK_E_CAPACITY;
+    if (h->chunk_ok) {
+        // kChunkRows prompt positions per launch; the last one's logits and token
+        // are the sequence's
+        const hipStream_t st = (hipStream_t)stream;
+        const size_t V = (size_t)h->cfg.vocab;
+        const char* crow = h->ws + h->coff;
+        for (int b = 0; b < B; ++b) {
+            int n = 0;
+            for (int t0 = 0; t0 < P; t0 += n) {
+                n = std::min(kChunkRows, P - t0);
+                s = run_chunk(h, b, d_tokens + (size_t)b * P + t0, n, st);
+                if (s != MK_OK) return s;
+            }
+            HIPCHK(h, hipMemcpyAsync(d_logits + (size_t)b * V, crow + h->clo.logits_scr + (size_t)(n - 1) * V * 4, V * 4,
+                                     hipMemcpyDeviceToDevice, st));
+            HIPCHK(h, hipMemcpyAsync(d_next + b, crow + h->clo.tok_scr + (size_t)(n - 1) * 4, 4, hipMemcpyDeviceToDevice,
+                                     st));
+        }
+        return MK_OK;
+    }
     float* scr_logits = (float*)(h->ws + h->lo.logits_scr);
     int32_t* scr_tok = (int32_t*)(h->ws + h->lo.tok_scr);
     for (int t = 0; t < P; ++t) {
@@ -965,6 +1116,23 @@ mk_status mk_prefill(mk_handle* h, const int32_t* d_tokens, int32_t B, int32_t P
         s = run_step(h, d_tokens + t, P, last ? d_next : scr_tok, last ? d_logits : scr_logits, (hipStream_t)stream);
         if (s != MK_OK) return s;
     }
+    return MK_OK;
+}
+
+mk_status mk_verify_step(mk_handle* h, int32_t seq, const int32_t* d_tokens, int32_t n, float* d_logits,
+                         int32_t* d_next, void* stream) {
+    if (!h || !d_tokens || !d_logits || !d_next || n < 1 || n > kChunkRows) return MK_E_INVALID;
+    if (seq < 0 || seq >= h->rt.max_batch) return MK_E_INVALID;
+    if (!h->chunk_ok) return MK_E_UNSUPPORTED;
+    mk_status s = check_latched(h);
+    if (s != MK_OK) return s;
+    const hipStream_t st = (hipStream_t)stream;
+    s = run_chunk(h, seq, d_tokens, n, st);
+    if (s != MK_OK) return s;
+    const char* crow = h->ws + h->coff;
+    HIPCHK(h, hipMemcpyAsync(d_logits, crow + h->clo.logits_scr, (size_t)n * h->cfg.vocab * 4, hipMemcpyDeviceToDevice,
+                             st));
+    HIPCHK(h, hipMemcpyAsync(d_next, crow + h->clo.tok_scr, (size_t)n * 4, hipMemcpyDeviceToDevice, st));
     return MK_OK;
 }
 
@@ -999,6 +1167,9 @@ mk_status mk_reset(mk_handle* h, void* stream) {
     // left by an aborted step never match a later step's tags
     HIPCHK(h, hipMemsetAsync(h->ws + h->lo.tickets, 0,
                              ((size_t)h->cfg.n_layers * h->rt.max_batch * h->cfg.n_kv_heads + 1) * kCtrStride * 4, st));
+    if (h->chunk_ok)
+        HIPCHK(h, hipMemsetAsync(h->ws + h->coff + h->clo.tickets, 0,
+                                 ((size_t)h->cfg.n_layers * kChunkRows * h->cfg.n_kv_heads + 1) * kCtrStride * 4, st));
     HIPCHK(h, hipMemsetAsync(h->ws + h->lo.state + offsetof(DevState, error), 0, 16, st));
     HIPCHK(h, hipStreamSynchronize(st));
     if (h->host_err) std::memset(h->host_err, 0, sizeof(HostErr));

@@ -2,8 +2,8 @@
 // "斯坦福团队新作让Llama1B实现毫秒级推理获Karpathy盛赞", section
 // "Megakernel：从零设计的深度融合方案": one launch per decode step).  The kernel
 // templates live in megakernel_impl.h; each kind is instantiated in its own
-// translation unit (mk_kernels_valu.hip, mk_kernels_mfma.hip, mk_kernels_moe.hip)
-// so that a kernel carries only its own code paths.
+// translation unit (mk_kernels_valu.hip, mk_kernels_mfma.hip, mk_kernels_moe.hip,
+// mk_kernels_chunk.hip) so that a kernel carries only its own code paths.
 #include <hip/hip_runtime.h>
 
 #include "mk_internal.h"
@@ -13,10 +13,12 @@ namespace mk {
 const void* kernel_valu(int B, int hd);
 const void* kernel_mfma(int B, int hd);
 const void* kernel_moe(int B, int hd);
+const void* kernel_chunk(int hd, bool moe);
 
 size_t megakernel_lds_bytes(const Params& P) { return (size_t)P.ring_chunks * kChunk + P.x_bytes; }
 
 static const void* megakernel_fn(const Params& P) {
+    if (P.chunk) return P.B == kChunkRows && !P.gemv_mfma ? kernel_chunk(P.hd, P.E > 0) : nullptr;
     const int kind = P.E > 0 ? 2 : P.gemv_mfma ? 1 : 0;
     return kind == 2 ? kernel_moe(P.B, P.hd) : kind == 1 ? kernel_mfma(P.B, P.hd) : kernel_valu(P.B, P.hd);
 }

@@ -154,13 +154,13 @@ __device__ __forceinline__ const char* chunk_src(const Params& P, const Instr& i
         case OP_ATTN: {
             constexpr uint32_t rbkv = HD * 2u;
             const AttnItem it = attn_item_of(P, in.begin);
-            const int b = it.b, g = it.g, s = it.s;
-            const int p = ctx_of(ctx, b);
+            const int b = kv_seq(P, it.b), g = it.g, s = it.s;
+            const int pc = ctx_of(ctx, it.b), p = attn_pos(P, pc, it.b);
             if (c == 0) {  // (cos, sin) row of position p: HD / 2 float2, lanes past it re-read its start
                 const uint32_t lo = (uint32_t)lane_id() * 16u;
                 return (const char*)(P.rope + (size_t)p * (HD / 2)) + (lo < HD * 4u ? lo : 0u);
             }
-            const SplitRange R = split_range<HD>(p, s, P.nsplit);
+            const SplitRange R = split_range<HD>(pc, s, P.nsplit);
             const uint32_t o = off - kChunk;
             const uint32_t t = o >> 11, w = o & 2047u, inner = w & 1023u;
             int pos = R.s0 + (int)(t * AttnGeom<HD>::PPW + inner / rbkv);
@@ -313,9 +313,9 @@ __device__ __forceinline__ bool setup_stream(const Params& P, const Instr& in, c
         }
         case OP_ATTN: {
             const AttnItem it = attn_item_of(P, in.begin);
-            const int b = it.b, g = it.g, s = it.s;
-            const int p = ctx_of(ctx, b);
-            const SplitRange Rg = split_range<HD>(p, s, P.nsplit);
+            const int b = kv_seq(P, it.b), g = it.g, s = it.s;
+            const int pc = ctx_of(ctx, it.b), p = attn_pos(P, pc, it.b);
+            const SplitRange Rg = split_range<HD>(pc, s, P.nsplit);
             const size_t base = ((((size_t)in.layer * P.kv_b + b) * P.Hkv + g) * P.S + Rg.s0) * HD;
             S.p0 = (const char*)(P.kcache + base);
             S.p1 = (const char*)(P.vcache + base);
@@ -1177,7 +1177,7 @@ __device__ __forceinline__ bool mfma_instr(const Params& P, const StepArgs& A, C
             } else if (is_o && layer == 0) {
 #pragma unroll
                 for (int b = 0; b < B; ++b)
-                    stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * P.d + in.begin, in.count,
+                    stage_bf16(P.embed + token_row(A, b, P.V) * P.d + in.begin, in.count,
                                hres + b * in.count, nullptr, wave, kComputeWaves, ss[0]);
                 const StageSeg sg[1] = {sx};
                 if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kComputeWaves, spin, ss)) return false;
@@ -1220,7 +1220,7 @@ __device__ __forceinline__ bool mfma_instr(const Params& P, const StepArgs& A, C
     if (in.op == OP_QKV && layer == 0) {
 #pragma unroll
         for (int b = 0; b < B; ++b)
-            stage_bf16_parts<PRT>(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * d, d, area, (uint32_t)b,
+            stage_bf16_parts<PRT>(P.embed + token_row(A, b, P.V) * d, d, area, (uint32_t)b,
                                   (uint32_t)parts_pitch(B), gain, wave, kComputeWaves, ss[b]);
     } else {
         const StageSeg sg[1] = {{P.h, (float*)area, gain, d, (uint32_t)B, d, d, tag_in, (uint32_t)PRT}};
@@ -1454,7 +1454,7 @@ __device__ __forceinline__ bool norm_gemv_sliced(const Params& P, const StepArgs
         if (qkv && layer == 0) {
 #pragma unroll
             for (int b = 0; b < B; ++b)
-                stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * d + ks * Ks, Ks, xs + b * Ks,
+                stage_bf16(P.embed + token_row(A, b, P.V) * d + ks * Ks, Ks, xs + b * Ks,
                            gain + ks * Ks, wave, kComputeWaves, ss[b]);
         } else {
             const StageSeg sg[1] = {{P.h + ks * Ks, xs, gain + ks * Ks, Ks, (uint32_t)B, d, Ks, tag_in}};
@@ -1668,7 +1668,7 @@ __device__ __forceinline__ bool moe_edown(const Params& P, const StepArgs& A, Ct
 }
 
 // One attention item (sequence, KV head, split) as an instruction.
-template <int B, int HD>
+template <int B, int HD, bool CH>
 __device__ __forceinline__ bool attn_instr(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs,
                                            int wave, const Instr& in, uint32_t S, Spin& spin, CwBarrier& barrier,
                                            uint32_t& land_wait, uint32_t* tr, const int32_t* ctx) {
@@ -1687,14 +1687,18 @@ __device__ __forceinline__ bool attn_instr(const Params& P, const StepArgs& A, C
     auto mark = [&](int m) {
         if (tr && lane == 0) tr[9 + m] = (uint32_t)now_ticks();
     };
-    return attn_item<HD>(P, A.tag0, in.layer, b, g, s, it.h0, it.gh, ctx_of(ctx, b), kv, need, release, barrier, xs, wave,
+    const int pc = ctx_of(ctx, b);
+    // (decode kernels take the one-position values at compile time)
+    return attn_item<HD, CH>(P, A.tag0, in.layer, b, g, s, it.h0, it.gh, CH ? attn_pos(P, pc, b) : pc, pc,
+                             CH ? b + 1 : 1, CH ? kv_seq(P, b) : b, !CH || b < A.tok_rows, kv, need, release, barrier,
+                             xs, wave,
                          kComputeWaves, spin, mark);
 }
 
 // Returns the queue index of the LM-head instruction once its input is staged
 // and published (the caller runs its rows: head_instr), or q1 (none in this kind,
 // or the workgroup stopped).
-template <int B, int HD, bool MF, bool MOE>
+template <int B, int HD, bool MF, bool MOE, bool CH>
 __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring,
                                                  float* xs, int wave, uint32_t q0, uint32_t q1, const int32_t* ctx) {
     const int lane = lane_id();
@@ -1721,7 +1725,7 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
         // (the matrix-core kernel carries no VALU GEMV code: a smaller kernel)
         if constexpr (MF) {
             if (is_gemv(in.op)) ok = mfma_instr<B, HD>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr);
-            else if (in.op == OP_ATTN) ok = attn_instr<B, HD>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr, ctx);
+            else if (in.op == OP_ATTN) ok = attn_instr<B, HD, CH>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr, ctx);
         } else switch (in.op) {
             case OP_EGU:
                 if constexpr (MOE && B == kMaxBatch) {
@@ -1759,7 +1763,7 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
                 if (in.op == OP_QKV && layer == 0) {
 #pragma unroll
                     for (int b = 0; b < B; ++b)
-                        stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * d, d, xs + b * d, gain, wave,
+                        stage_bf16(P.embed + token_row(A, b, P.V) * d, d, xs + b * d, gain, wave,
                                    kComputeWaves, ss[b]);
                 } else {
                     float* xd = xs;
@@ -1862,7 +1866,7 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
                         // the residual is the token embedding: no wait
 #pragma unroll
                         for (int b = 0; b < B; ++b)
-                            stage_bf16(P.embed + token_row(A.tok_in, b, A.tok_stride, P.V) * P.d + in.begin,
+                            stage_bf16(P.embed + token_row(A, b, P.V) * P.d + in.begin,
                                        in.count, hres + b * in.count, nullptr, wave, kComputeWaves, ss[0]);
                         const StageSeg sg[1] = {sx};
                         if (!stage_segs<stage_words_wide<B>(), 1, 1>(sg, wave, kComputeWaves, spin, ss)) return q1;
@@ -1898,7 +1902,7 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
                 }
                 break;
             }
-            case OP_ATTN: ok = attn_instr<B, HD>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr, ctx); break;
+            case OP_ATTN: ok = attn_instr<B, HD, CH>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr, ctx); break;
             default: break;
         }
         if (!ok || lds_ld(&ctl->abort)) return q1;
@@ -1963,7 +1967,7 @@ __device__ __forceinline__ void head_instr(const Params& P, const StepArgs& A, C
     }
 }
 
-template <int B, int HD, bool MF, bool MOE>
+template <int B, int HD, bool MF, bool MOE, bool CH = false>
 __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs A) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     __shared__ Ctl ctl;
@@ -1979,14 +1983,16 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
         ctl.moe_n = 0;
         ctl.head_seq = 0;
     }
-    if (threadIdx.x < kMaxBatch) ctl.ctx[threadIdx.x] = (int)threadIdx.x < B ? P.state->ctx_len[threadIdx.x] : 0;
+    // context lengths at launch (a multi-position step: every row sees the sequence's cached length)
+    if (threadIdx.x < kMaxBatch)
+        ctl.ctx[threadIdx.x] = (int)threadIdx.x < B ? P.ctx_len[P.chunk ? P.chunk_seq : (int)threadIdx.x] : 0;
     __syncthreads();
     const uint32_t q0 = ld_const(P.queue_off + blockIdx.x), q1 = ld_const(P.queue_off + blockIdx.x + 1);
     uint32_t hi;
     if (wave >= kComputeWaves) {
         hi = loader_wave<B, HD, MF, MOE>(P, &ctl, ring, wave - kComputeWaves, q0, q1, ctl.ctx);
     } else {
-        hi = compute_wave<B, HD, MF, MOE>(P, A, &ctl, ring, xs, wave, q0, q1, ctl.ctx);
+        hi = compute_wave<B, HD, MF, MOE, CH>(P, A, &ctl, ring, xs, wave, q0, q1, ctl.ctx);
     }
     if constexpr (!MF) {
         float* hx = xs;
@@ -2012,6 +2018,14 @@ const void* kernel_of(int B, int hd) {
         if (B == 4) return (const void*)mk_megakernel<4, 128, MF, MOE>;
         if (B == 8) return (const void*)mk_megakernel<8, 128, MF, MOE>;
     }
+    return nullptr;
+}
+
+// Multi-position kernel (kChunkRows rows of one sequence, VALU GEMVs) for head_dim hd.
+template <bool MOE>
+const void* kernel_of_chunk(int hd) {
+    if (hd == 64) return (const void*)mk_megakernel<kChunkRows, 64, false, MOE, true>;
+    if (hd == 128) return (const void*)mk_megakernel<kChunkRows, 128, false, MOE, true>;
     return nullptr;
 }
 

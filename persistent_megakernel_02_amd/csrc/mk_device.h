@@ -108,8 +108,9 @@ __device__ __forceinline__ float group_sum(float v, int width) {
 
 // Token ids come from device memory; clamp so a bad id cannot index outside the
 // embedding table.
-__device__ __forceinline__ size_t token_row(const int32_t* tok, int b, int stride, int V) {
-    const int t = tok[b * stride];
+__device__ __forceinline__ size_t token_row(const StepArgs& A, int b, int V) {
+    const int r = b < A.tok_rows ? b : A.tok_rows - 1;  // rows past the given tokens repeat the last
+    const int t = A.tok_in[r * A.tok_stride];
     return (size_t)(t < 0 ? 0 : (t >= V ? V - 1 : t));
 }
 
@@ -766,6 +767,22 @@ struct RingKV {
     }
 };
 
+// RoPE table row of one position read straight from the table.
+struct GlobalRope {
+    const float2* row;
+    __device__ __forceinline__ float2 rope_at(int i) const { return row[i]; }
+};
+
+// Own position of row b of a step whose rows see `cached` positions: the cached
+// length in a decode step; cached + b in a multi-position step, clamped to the
+// cache (only ignored rows of a short chunk can pass its end).
+__device__ __forceinline__ int attn_pos(const Params& P, int cached, int b) {
+    const int p = cached + (P.chunk ? b : 0);
+    return p < P.S ? p : P.S - 1;
+}
+// KV-cache row (sequence) of step row b.
+__device__ __forceinline__ int kv_seq(const Params& P, int b) { return P.chunk ? P.chunk_seq : b; }
+
 template <int HD>
 struct GlobalKV {
     const uint16_t *kb, *vb;  // cache rows of (layer, b, g): [S][HD]
@@ -918,10 +935,19 @@ static_assert(kAttnBlockGroups % (2 * kComputeWaves) == 0, "groups of a block (f
 // `barrier()` synchronises the waves.  Writes the attention output (tagged) or,
 // when split, the item's (max, sum, output) partial; the last split to arrive
 // merges all partials in split order.
-template <int HD, class KV, class Need, class Release, class Barrier, class Mark>
+// Positions: p is the row's own position (RoPE of q, where its K/V is appended),
+// pc the cached positions it attends to from the cache (the context length at
+// launch), and the nnew new positions pc, pc + 1, ..., p are the rows b - nnew + 1
+// .. b of the step (one, p = pc, in a decode step; rows 0 .. b of one sequence in
+// a multi-position step), taken from this step's projections rather than the
+// cache; kvb is the cache row (sequence) and `append` says whether the row stores
+// its K/V.  CH: compiled for multi-position steps (nnew up to kChunkRows); the
+// decode kernels keep one new position and its smaller register and LDS footprint.
+template <int HD, bool CH, class KV, class Need, class Release, class Barrier, class Mark>
 __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int layer, int b, int g, int s, int h0, int gh, int p,
-                                          const KV& kv, Need& need, Release& release, Barrier& barrier, float* xs,
-                                          int wave, int nw, Spin& spin, Mark& mark) {
+                                          int pc, int nnew, int kvb, bool append, const KV& kv, Need& need,
+                                          Release& release, Barrier& barrier, float* xs, int wave, int nw, Spin& spin,
+                                          Mark& mark) {
     using Geo = AttnGeom<HD>;
     constexpr int LPP = Geo::LPP, PPW = Geo::PPW, DPL = Geo::DPL;
     constexpr int GW = kAttnBlockGroups / kComputeWaves;  // groups per wave per block
@@ -930,22 +956,28 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
     const int ps = lane / LPP;
     const int dl = 8 * (lane % LPP);
     const int G = gh;  // q heads h0 .. h0 + gh - 1 of the KV head's P.G
-    const SplitRange R = split_range<HD>(p, s, P.nsplit);
+    const SplitRange R = split_range<HD>(pc, s, P.nsplit);
+    constexpr int NM = CH ? kChunkRows : 1;                       // new-position rows the LDS layout holds
+    constexpr int NGM = CH ? (kChunkRows + PPW - 1) / PPW : 1;    // groups of new positions at most
+    static_assert(NGM <= 2, "new positions fill at most two groups");
+    if constexpr (!CH) nnew = 1;
+    const int NG = (nnew + PPW - 1) / PPW;  // groups of new positions
     const float scale = P.attn_scale;
     const uint32_t tag_in = phase_tag(tag0, layer, 0) ^ ((P.inject && layer == 0) ? 0x80000000u : 0u);
     const uint32_t tag_out = phase_tag(tag0, layer, 1);
     const uint32_t stride = HD + 2;
 
-    // LDS: raw q [G][HD], k [HD], v [HD]; rotated q [G][HD]; new K and V (bf16);
-    // scores [wave][64][4]; wave partials [wave][G][2 + 4 HD]; split partials [split][G][HD + 2].
+    // LDS: raw q [G][HD], k [NM][HD], v [NM][HD]; rotated q [G][HD]; new K and V
+    // (bf16, [NM][HD]); scores [wave][64][4]; wave partials [wave][G][2 + 4 HD];
+    // split partials [split][G][HD + 2].
     float* q_raw = xs;
     float* k_raw = q_raw + G * HD;
-    float* v_raw = k_raw + HD;
-    float* q_rot = v_raw + HD;
+    float* v_raw = k_raw + NM * HD;
+    float* q_rot = v_raw + NM * HD;
     uint16_t* k_new = (uint16_t*)(q_rot + G * HD);
-    uint16_t* v_new = k_new + HD;
-    float* sc = (float*)(v_new + HD) + wave * kAttnWavePositions * kMaxGroup;
-    float* wpart = (float*)(v_new + HD) + kComputeWaves * kAttnWavePositions * kMaxGroup;
+    uint16_t* v_new = k_new + NM * HD;
+    float* sc = (float*)(v_new + NM * HD) + wave * kAttnWavePositions * kMaxGroup;
+    float* wpart = (float*)(v_new + NM * HD) + kComputeWaves * kAttnWavePositions * kMaxGroup;
     float* spart = wpart + kComputeWaves * G * (4 * HD + 2);
     uint32_t* flag = (uint32_t*)(spart + P.nsplit * G * stride);
 
@@ -953,10 +985,13 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
     if (!need(-1)) return false;
     {
         const uint64_t* row = P.qkv + (size_t)b * P.qkv_rows;
+        const uint64_t* row0 = P.qkv + (size_t)(b - nnew + 1) * P.qkv_rows;  // first new-position row
+        const uint32_t nr = (uint32_t)nnew, qs = (uint32_t)P.qkv_rows;
         float ss[1] = {0.f};
         const StageSeg sg[3] = {{row + (size_t)(g * P.G + h0) * HD, q_raw, nullptr, (uint32_t)(G * HD), 1u, 0u, 0u, tag_in},
-                                {row + (size_t)(P.Hq + g) * HD, k_raw, nullptr, (uint32_t)HD, 1u, 0u, 0u, tag_in},
-                                {row + (size_t)(P.Hq + P.Hkv + g) * HD, v_raw, nullptr, (uint32_t)HD, 1u, 0u, 0u, tag_in}};
+                                {row0 + (size_t)(P.Hq + g) * HD, k_raw, nullptr, (uint32_t)HD, nr, qs, (uint32_t)HD, tag_in},
+                                {row0 + (size_t)(P.Hq + P.Hkv + g) * HD, v_raw, nullptr, (uint32_t)HD, nr, qs, (uint32_t)HD,
+                                 tag_in}};
         if (!stage_segs<kStagePassWords, 1, 3>(sg, wave, nw, spin, ss)) return false;
     }
     if (!barrier()) return false;
@@ -972,18 +1007,32 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
     }
     if (wave == 0) {
         uint32_t kw = 0, vw = 0;
+        if constexpr (CH) {
+            // earlier new positions of a multi-position step: K rotated at position
+            // pc + r (table rows read directly; the ring carries the row of p only)
+            for (int r = 0; r + 1 < nnew; ++r) {
+                const GlobalRope grp{P.rope + (size_t)min(pc + r, P.S - 1) * (HD / 2)};
+#pragma unroll
+                for (int j = 0; j < DPL; ++j) {
+                    const int i = lane * DPL + j;
+                    k_new[r * HD + i] = (uint16_t)f_to_bf(rope_dim<HD>(k_raw + r * HD, grp, i));
+                    v_new[r * HD + i] = (uint16_t)f_to_bf(v_raw[r * HD + i]);
+                }
+            }
+        }
+        const int own = nnew - 1;  // this row's new position
 #pragma unroll
         for (int j = 0; j < DPL; ++j) {
             const int i = lane * DPL + j;
-            const uint32_t kb16 = f_to_bf(rope_dim<HD>(k_raw, kv, i));
-            const uint32_t vb16 = f_to_bf(v_raw[i]);
-            k_new[i] = (uint16_t)kb16;
-            v_new[i] = (uint16_t)vb16;
+            const uint32_t kb16 = f_to_bf(rope_dim<HD>(k_raw + own * HD, kv, i));
+            const uint32_t vb16 = f_to_bf(v_raw[own * HD + i]);
+            k_new[own * HD + i] = (uint16_t)kb16;
+            v_new[own * HD + i] = (uint16_t)vb16;
             kw |= kb16 << (16 * j);
             vw |= vb16 << (16 * j);
         }
-        if (R.has_new && h0 == 0) {  // KV append at position p (read by later steps), once per KV head
-            const size_t row = ((((size_t)layer * P.kv_b + b) * P.Hkv + g) * P.S + p) * HD + lane * DPL;
+        if (R.has_new && h0 == 0 && append) {  // KV append at position p (read by later steps), once per KV head
+            const size_t row = ((((size_t)layer * P.kv_b + kvb) * P.Hkv + g) * P.S + p) * HD + lane * DPL;
             if constexpr (DPL == 1) {
                 P.kcache[row] = (uint16_t)kw;
                 P.vcache[row] = (uint16_t)vw;
@@ -1005,10 +1054,16 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
         q[h][0] = a.x; q[h][1] = a.y; q[h][2] = a.z; q[h][3] = a.w;
         q[h][4] = c.x; q[h][5] = c.y; q[h][6] = c.z; q[h][7] = c.w;
     }
-    const uint4 kn = *(const uint4*)(k_new + dl);
-    const uint4 vn = *(const uint4*)(v_new + dl);
+    // this lane's slot of the new positions' groups (slots past nnew repeat the last)
+    uint4 kn[NGM], vn[NGM];
+#pragma unroll
+    for (int n = 0; n < NGM; ++n) {
+        const int r = min(n * PPW + ps, nnew - 1);
+        kn[n] = *(const uint4*)(k_new + r * HD + dl);
+        vn[n] = *(const uint4*)(v_new + r * HD + dl);
+    }
 
-    const int ngr = R.ngroups + (R.has_new ? 1 : 0);  // ring groups, then the new position's group
+    const int ngr = R.ngroups + (R.has_new ? NG : 0);  // ring groups, then the new positions' groups
     // running maximum and sum per head (wave-uniform), weighted V per (slot, 8 dims)
     float m_run[kMaxGroup], l_run[kMaxGroup], acc[kMaxGroup][8];
 #pragma unroll
@@ -1046,12 +1101,13 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
             for (int u = 0; u < 2; ++u) {
                 const int tt = first + kComputeWaves * (i + u);
                 const uint4 kr = blk.k(min(tt, own_last) - t0);
-                kp[u] = (tt < R.ngroups) ? kr : kn;
+                kp[u] = (tt < R.ngroups) ? kr : (tt == R.ngroups ? kn[0] : kn[NGM - 1]);
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int tt = first + kComputeWaves * (i + u);
-                const bool valid = (i + u < ngw) && (tt == R.ngroups ? ps == 0 : tt * PPW + ps < R.ncached);
+                const bool valid = (i + u < ngw) && (tt >= R.ngroups ? (tt - R.ngroups) * PPW + ps < nnew
+                                                                      : tt * PPW + ps < R.ncached);
                 float v4[kMaxGroup];
 #pragma unroll
                 for (int h = 0; h < kMaxGroup; ++h) v4[h] = qk8(q[h], kp[u]);
@@ -1108,7 +1164,7 @@ __device__ __forceinline__ bool attn_item(const Params& P, uint32_t tag0, int la
                 const int tt = first + kComputeWaves * (i + u);
                 const uint4 vr = blk.vp(min(tt, own_last) - t0);
                 const float4 w = *(const float4*)(sc + (min(i + u, ngw - 1) * PPW + ps) * kMaxGroup);
-                vp[u] = (tt < R.ngroups) ? vr : vn;
+                vp[u] = (tt < R.ngroups) ? vr : (tt == R.ngroups ? vn[0] : vn[NGM - 1]);
                 w4[u] = (i + u < ngw) ? w : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
@@ -1324,7 +1380,11 @@ __device__ __forceinline__ bool head_publish(const Params& P, const StepArgs& A,
         }
         if (lane == 0) A.tok_out[b] = besti;
     }
-    if (lane < B) P.state->ctx_len[lane] = P.state->ctx_len[lane] + 1;
+    if (P.chunk) {
+        if (lane == 0) P.ctx_len[P.chunk_seq] = P.ctx_len[P.chunk_seq] + A.tok_rows;
+    } else if (lane < B) {
+        P.ctx_len[lane] = P.ctx_len[lane] + 1;
+    }
     if (lane == 0) __hip_atomic_store(P.head_ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (__any(nan_seen)) raise_error_impl(P.state, P.host_err, spin.abort_flag, DERR_NAN, 0, 0);
     return true;

@@ -128,8 +128,8 @@ __host__ __device__ constexpr uint32_t ring_batch_span(uint32_t rb, int B, bool 
 // K and V as bf16; the scores of every wave ([wave][position][kMaxGroup]); the wave
 // partials ([wave][G]: maximum, sum, four 16-lane rows of HD); when the item
 // merges splits, the split partials ([split][G]: maximum, sum, HD); one flag word.
-__host__ __device__ constexpr size_t attn_lds_floats(int G, int HD, int nsplit) {
-    return (size_t)(2 * G * HD + 3 * HD + kComputeWaves * kAttnWavePositions * kMaxGroup +
+__host__ __device__ constexpr size_t attn_lds_floats(int G, int HD, int nsplit, int nnew = 1) {
+    return (size_t)(2 * G * HD + 3 * nnew * HD + kComputeWaves * kAttnWavePositions * kMaxGroup +
                     kComputeWaves * G * (4 * HD + 2) + nsplit * G * (HD + 2) + 4);
 }
 
@@ -234,8 +234,16 @@ struct Params {
     uint64_t spin_ticks;        // watchdog in s_memrealtime ticks (100 MHz)
     uint32_t* trace;            // nullptr, or [n_cu][trace_stride][kTraceWords] records
     uint32_t trace_stride;      // records per CU
-    uint32_t pad_tr;
+    // Context lengths the step reads at launch and advances at its end (the decode
+    // handle's state).  chunk = 1: the B rows are consecutive positions of ONE
+    // sequence, chunk_seq, of the decode handle (its KV cache rows): row r sits at
+    // position ctx_len[chunk_seq] + r, attends to the cached positions and to rows
+    // 0..r, and the step advances that sequence by the rows it was given.
+    int32_t* ctx_len;
+    int32_t chunk, chunk_seq;
 };
+// Rows of a multi-position step (one sequence's prompt chunk or draft tokens).
+constexpr int kChunkRows = kMaxBatch;
 
 // Trace record of one instruction on one CU (s_memrealtime ticks, low 32 bits):
 // {op | layer << 16, start, inputs staged, compute end, end, loader issue end,
@@ -249,6 +257,7 @@ constexpr int kTraceWords = 12;
 struct StepArgs {
     const int32_t* tok_in;
     int32_t tok_stride;
+    int32_t tok_rows;  // rows with tokens; later rows repeat the last one (a multi-position step's short chunk)
     uint32_t tag0;
     int32_t* tok_out;
     float* logits;

@@ -28,7 +28,7 @@ MK_GEMV_AUTO, MK_GEMV_VALU, MK_GEMV_MFMA = 0, 1, 2
 EXPORTS = ["mk_query_sizes", "mk_create", "mk_create_static", "mk_kv_layout", "mk_prefill", "mk_set_context_len", "mk_decode_step",
            "mk_get_context_len", "mk_reset", "mk_debug_inject", "mk_status_string", "mk_last_error",
            "mk_plan_inspect", "mk_kernels_per_step", "mk_destroy", "mk_bench_stream_read", "mk_bench_copy",
-           "mk_bench_sync", "mk_read_trace", "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap", "mk_moe_slots"]
+           "mk_bench_sync", "mk_read_trace", "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap", "mk_moe_slots", "mk_verify_step"]
 
 
 class mk_model_config(ctypes.Structure):
@@ -114,10 +114,11 @@ def lib():
         L.mk_read_trace.argtypes = [vp, vp, sz, ctypes.POINTER(sz), ctypes.POINTER(i32)]
         L.mk_bench_graph_gap.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ctypes.POINTER(ctypes.c_float), vp]
         L.mk_moe_slots.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64)]
+        L.mk_verify_step.argtypes = [vp, i32, vp, i32, vp, vp, vp]
         for n in ("mk_query_sizes", "mk_create", "mk_create_static", "mk_kv_layout", "mk_prefill", "mk_set_context_len",
                   "mk_get_context_len", "mk_decode_step", "mk_reset", "mk_debug_inject", "mk_plan_inspect",
                   "mk_destroy", "mk_bench_stream_read", "mk_bench_copy", "mk_bench_sync", "mk_read_trace",
-                  "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap", "mk_moe_slots"):
+                  "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap", "mk_moe_slots", "mk_verify_step"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -302,6 +303,19 @@ class Decoder:
 
     def kernels_per_step(self) -> int:
         return int(lib().mk_kernels_per_step(self.h))
+
+    def verify_step(self, seq: int, tokens, logits_out=None, next_out=None):
+        """Tokens [n] (n <= 8) at the next positions of sequence `seq` in one launch;
+        returns (greedy tokens [n], logits [n, V]) and advances that sequence by n."""
+        import torch
+
+        n = int(tokens.numel())
+        logits_out = torch.empty((n, self.cfg.vocab), dtype=torch.float32, device=self.device) \
+            if logits_out is None else logits_out
+        next_out = torch.empty(n, dtype=torch.int32, device=self.device) if next_out is None else next_out
+        self._check(lib().mk_verify_step(self.h, int(seq), tokens.data_ptr(), n, logits_out.data_ptr(),
+                                         next_out.data_ptr(), self.stream.cuda_stream), "mk_verify_step")
+        return next_out, logits_out
 
     def moe_slots(self) -> int:
         """Expert slots streamed by the MoE layers since creation (mk_moe_slots)."""

@@ -46,10 +46,16 @@ def oracle_run(cfg, w, prompt, steps, max_seq):
     return toks, rows
 
 
-def gpu_run(dec, prompt, ref_tok, steps):
+def gpu_run(dec, prompt, ref_tok, steps, per_token=False):
+    """Prompt (mk_prefill, or one decode step per position with per_token), then
+    `steps` teacher-forced decode steps; the tokens and logits of each."""
     torch = _torch()
     p = torch.from_numpy(prompt).to(dec.device)
-    nxt, logits = dec.prefill(p)
+    if per_token:
+        for t in range(prompt.shape[1]):
+            nxt, logits = dec.decode_step(p[:, t].contiguous())
+    else:
+        nxt, logits = dec.prefill(p)
     toks, rows = [nxt.cpu().numpy().copy()], [logits.cpu().numpy().copy()]
     for t in range(steps):
         fed = torch.from_numpy(np.ascontiguousarray(ref_tok[t], np.int32)).to(dec.device)
@@ -121,11 +127,13 @@ def test_tiny_parity(tiny, mode):
 
 def test_tiny_megakernel_equals_graph_bitwise(tiny):
     w, prompt, (rt_, rl) = tiny
+    # (prompts one position per step in both modes: the persistent mode's
+    # multi-position prefill adds the attention terms in another order)
     d0 = _decoder(I.TINY, w, 1, 32, 0)
-    a = gpu_run(d0, prompt, rt_, 16)
+    a = gpu_run(d0, prompt, rt_, 16, per_token=True)
     d0.close()
     d1 = _decoder(I.TINY, w, 1, 32, 1)
-    b = gpu_run(d1, prompt, rt_, 16)
+    b = gpu_run(d1, prompt, rt_, 16, per_token=True)
     d1.close()
     for x, y in zip(a[1], b[1]):
         assert np.array_equal(x, y)
@@ -252,7 +260,7 @@ def test_llama1b_b1_graph_matches_megakernel_bitwise(llama1b):
     for mode in (0, 1):
         print(f"case 1B b1 mode={mode} bitwise", flush=True)
         d = _decoder(I.LLAMA_1B, w, 1, 64, mode, gemv_kind=1 if mode == 0 else 0)
-        outs.append(gpu_run(d, prompt, [toks[:, t] for t in range(24)], 24))
+        outs.append(gpu_run(d, prompt, [toks[:, t] for t in range(24)], 24, per_token=True))
         d.close()
     for x, y in zip(outs[0][1], outs[1][1]):
         assert np.array_equal(x, y)
@@ -447,7 +455,7 @@ def test_tiny_batch_4_8(B):
     for mode, kind in ((0, 1), (1, 0), (0, 2)):
         print(f"case tiny b{B} mode={mode} gemv={kind}", flush=True)
         d = _decoder(cfg, w, B, 20, mode, gemv_kind=kind)
-        gt, gl = gpu_run(d, prompt, rt_, 10)
+        gt, gl = gpu_run(d, prompt, rt_, 10, per_token=True)
         compare(rt_, rl, gt, gl, f"tiny b{B} mode={mode} gemv={kind}")
         outs.append(gl)
         d.close()
@@ -545,4 +553,75 @@ def test_llama1b_batch_long_context(B, ctx, kind):
         got_l.append(g_l.cpu().numpy().copy())
         tok = nxt.astype(np.int32)
     compare(ref_t, ref_l, got_t, got_l, f"1B b{B} ctx={ctx}")
+    d.close()
+
+
+@pytest.mark.parametrize("cfg_name,B,P", [("tiny", 2, 13), ("tiny", 1, 8), ("1b", 1, 19)])
+def test_multi_position_prefill(cfg_name, B, P):
+    """mk_prefill in the persistent mode runs each sequence's prompt in launches of
+    up to 8 positions (causal attention inside a launch, every position's K/V
+    appended); a short last chunk repeats its last token in the unused rows, which
+    neither append nor count.  The prompt's last logits and the decode steps that
+    follow match the oracle."""
+    cfg = I.TINY if cfg_name == "tiny" else I.replace(I.LLAMA_1B, n_layers=4)
+    w = I.make_weights(cfg, seed=40)
+    prompt = I.make_prompt(cfg, B, P, seed=41)
+    rt_, rl = oracle_run(cfg, w, prompt, 6, P + 8)
+    print(f"case multi-position prefill {cfg_name} b{B} P={P}", flush=True)
+    d = _decoder(cfg, w, B, P + 8, 0)
+    gt, gl = gpu_run(d, prompt, rt_, 6)
+    assert d.context_len() == [P + 6] * B
+    compare(rt_, rl, gt, gl, f"multi-position prefill {cfg_name} b{B} P={P}")
+    d.close()
+
+
+@pytest.mark.parametrize("cfg_name", ["tiny", "1b"])
+def test_verify_step_and_rollback(cfg_name):
+    """mk_verify_step: n draft tokens of one sequence in one launch give the logits
+    and greedy tokens the oracle gives feeding them one at a time; the context
+    grows by n; after rolling the context back to accept k of them, decoding
+    continues from position P + k as the oracle does.  On a two-sequence handle
+    the other sequence is untouched."""
+    torch = _torch()
+    cfg = I.TINY if cfg_name == "tiny" else I.replace(I.LLAMA_1B, n_layers=4)
+    w = I.make_weights(cfg, seed=50)
+    B, P, n, k = 2, 7, 6, 3
+    prompt = I.make_prompt(cfg, B, P, seed=51)
+    draft = I.make_prompt(cfg, 1, n, seed=52)[0]
+    S = P + n + 8
+    print(f"case verify step {cfg_name}", flush=True)
+    d = _decoder(cfg, w, B, S, 0)
+    d.prefill(torch.from_numpy(prompt).to(d.device))
+    nxt, logits = d.verify_step(1, torch.from_numpy(draft.astype(np.int32)).to(d.device))
+    got_l, got_t = logits.cpu().numpy(), nxt.cpu().numpy()
+    assert d.context_len() == [P, P + n]
+    # oracle: sequence 1 fed the draft one position at a time (sequence 0 fed its own
+    # last prompt token again: only sequence 1's rows are compared)
+    orc = O.Oracle(cfg, w, B, S)
+    orc.prefill(prompt)
+    ref_l, ref_t = [], []
+    for j in range(n):
+        o_next, o_logits = orc.step(np.array([prompt[0, -1], draft[j]], np.int32))
+        ref_l.append(o_logits[1:2].copy())
+        ref_t.append(o_next[1:2].copy())
+    compare(ref_t, ref_l, [got_t[j:j + 1] for j in range(n)], [got_l[j:j + 1] for j in range(n)],
+            f"verify {cfg_name}")
+    # accept k draft tokens: context back to P + k, then decode on from there
+    d.set_context_len([P, P + k])
+    orc2 = O.Oracle(cfg, w, B, S)
+    orc2.prefill(prompt)
+    for j in range(k):
+        orc2.step(np.array([prompt[0, -1], draft[j]], np.int32))
+    orc2.pos[0] = P  # sequence 0 stays at its prompt
+    feed = np.array([prompt[0, -1], draft[k]], np.int32)
+    steps_ref_t, steps_ref_l, steps_t, steps_l = [], [], [], []
+    for _ in range(3):
+        o_next, o_logits = orc2.step(feed)
+        g_next, g_logits = d.decode_step(torch.from_numpy(feed).to(d.device))
+        steps_ref_t.append(o_next.copy())
+        steps_ref_l.append(o_logits.copy())
+        steps_t.append(g_next.cpu().numpy().copy())
+        steps_l.append(g_logits.cpu().numpy().copy())
+        feed = o_next.astype(np.int32)
+    compare(steps_ref_t, steps_ref_l, steps_t, steps_l, f"after rollback {cfg_name}")
     d.close()
