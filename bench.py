@@ -138,6 +138,45 @@ def prefill_latency(dec, prompt_dev, reps: int = 10) -> dict:
     return out
 
 
+def cut_study(dec, start, steps: int = 64) -> dict:
+    """The decode step as k persistent launches (mk_set_cuts, equal layer runs):
+    measured µs/step for k = 1, 2, 4 and one launch per layer plus the LM head;
+    the cut planner, given the one- and two-launch figures (their difference is
+    one launch plus the prefetch lost at a cut), predicts the others and picks
+    the design."""
+    import numpy as np
+    import torch
+
+    import persistent_megakernel_02_amd.mk as mk
+
+    L = dec.cfg.n_layers
+    designs = {"1": [], "2": [L // 2], "4": [L // 4, L // 2, 3 * L // 4], str(L + 1): list(range(1, L + 1))}
+    measured = {}
+    for name, cuts in designs.items():
+        dec.set_cuts(cuts)
+        times = []
+        for rep_ in range(2):
+            tok = start()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(dec.stream)
+            for _ in range(steps):
+                dec.decode_step(tok, tok)
+            e1.record(dec.stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1000.0 / steps)
+        measured[name] = round(float(np.min(times)), 2)
+    dec.set_cuts([])
+    t1, t2 = measured["1"], measured["2"]
+    per_cut = t2 - t1
+    # every launch pays per_cut; the split of the rest between layers and head does not move the choice
+    body = (t1 - per_cut) / (L + 1)
+    plan = mk.plan_cuts([body] * L, launch_us=per_cut, head_us=body, refill_us=None)
+    predicted = {name: round(t1 + (len(cuts)) * per_cut, 2) for name, cuts in designs.items()}
+    return {"launches_per_step": list(designs), "measured_us": measured, "predicted_us": predicted,
+            "cost_per_cut_us": round(per_cut, 2), "planner_cuts": plan["cuts"],
+            "planner_predicted_us": round(plan["predicted_us"], 2)}
+
+
 def micro_benchmarks(dev, n_cu: int) -> dict:
     """The synchronisation and launch costs the persistent kernel is built
     around: the gap one kernel boundary costs inside a replayed hipGraph, an
@@ -352,12 +391,21 @@ def main() -> int:
     gemv_used = mk.mk_plan_inspect(mk.model_config(cfg), mk.runtime_config(B, max_seq, gemv_kind=gemv),
                                    torch.cuda.get_device_properties(dev).multi_processor_count)[1]["gemv_kind"]
     us_mk, positions, kps_mk, per_h, pct_mk, slots_step = run_path(mk.MK_MODE_MEGAKERNEL, "megakernel")
-    prefill = None
+    prefill = cuts = None
     if CTX == 0:
         pdec = mk.Decoder(cfg, w, max_batch=B, max_seq=max_seq, device="cuda:0", device_weights=dw)
         prefill = prefill_latency(pdec, prompt_dev)
-        pdec.close()
         log(f"prefill of {prefill['prompt_tokens']} tokens: {prefill}")
+        if args.config == "1b" and not args.no_micro:
+
+            def restart():
+                pdec.set_context_len([0] * B)
+                nxt, _ = pdec.prefill(prompt_dev)
+                return nxt
+
+            cuts = cut_study(pdec, restart)
+            log(f"cut study: {cuts}")
+        pdec.close()
     # every sequence at position p; MoE: the expert slots the kernel counted, mean per step
     bytes_step = [step_bytes(cfg, B, [p], slots_step) for p in positions]
     mean_bytes = float(np.mean(bytes_step))
@@ -453,6 +501,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "micro": micro,
         "prefill": prefill,
+        "cuts": cuts,
     }
     print(json.dumps(out), flush=True)
     return 0

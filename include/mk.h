@@ -293,6 +293,63 @@ mk_status mk_read_trace(mk_handle* h, void* h_buf, size_t bytes, size_t* written
  * *out is left unchanged on error. */
 mk_status mk_moe_slots(mk_handle* h, uint64_t* out);
 
+/* Cut each decode step into several persistent launches [page
+ * "一个大内核不够：在哪里切分流式推理模型", sections "为什么切在哪里比融不融更关键" and
+ * "规划器总览：只用常规画像排序切分": where the fused region ends is a design choice;
+ * a step may run as k >= 1 resident launches].  h_layers: host int32 [n], strictly
+ * increasing layer indices in 1..n_layers; a new launch starts before each of
+ * those layers (n_layers: the LM head runs alone).  n = 0 restores one launch per
+ * step.  Every launch runs its CUs' instructions of its layers in the usual order,
+ * so the results are bit for bit those of one launch; each cut costs a launch and
+ * the loss of the weights the loaders would have prefetched across it.  Persistent
+ * mode without the device trace only (MK_E_UNSUPPORTED); MK_E_INVALID for bad
+ * cuts or more than 63 of them.  Synchronises the handle's streams. */
+mk_status mk_set_cuts(mk_handle* h, const int32_t* h_layers, int32_t n);
+
+/* ---- Cut planner [page "一个大内核不够：在哪里切分流式推理模型", sections
+ * "规划器总览：只用常规画像排序切分", "瓦片图如何估计单次服务时间" and
+ * "事件图如何算出首次发布分数"]: candidate designs are scored by simulating their
+ * launches as an event graph up to the first release, from per-region service
+ * times; no candidate is run end to end.  Host only, no device work. */
+
+#define MK_EVENT_MAX_DEPS 8
+/* One event-graph task: it starts when its dependencies (earlier tasks) have
+ * finished and the previous task of its stream has finished, plus its dispatch
+ * cost, and runs for `duration`.  Tasks on different streams run side by side
+ * (their durations are the ones for the resources each stream is given). */
+typedef struct {
+    double duration;  /* service time (any unit, the same for all tasks) */
+    double dispatch;  /* launch / switch cost paid before it starts */
+    int32_t stream;   /* 0..1023 */
+    int32_t n_deps;   /* 0..MK_EVENT_MAX_DEPS */
+    int32_t deps[MK_EVENT_MAX_DEPS]; /* indices of earlier tasks */
+} mk_event_task;
+
+/* Finish time of every task (host double [n]), tasks in dependency order.
+ * MK_E_INVALID for a dependency on a later task, a negative time or a bad stream. */
+mk_status mk_event_sim(const mk_event_task* tasks, int32_t n, double* h_finish);
+
+/* Service table of a decode step: regions are the n_layers layers and the LM head. */
+typedef struct {
+    int32_t n_layers;
+    double launch_us;         /* dispatch of one persistent launch */
+    const double* layer_us;   /* [n_layers]: a layer inside a launch, its weights prefetched */
+    const double* refill_us;  /* [n_layers + 1] or NULL: extra time when a launch starts at that
+                                 region (nothing prefetched; index n_layers: the LM head) */
+    double head_us;           /* final norm, LM head and argmax */
+    double conventional_us;   /* the one-kernel-per-op step, 0 if not a candidate */
+} mk_cut_costs;
+
+/* Best design for the service table: one-kernel-per-op, or persistent launches
+ * starting at region 0 and at the *n_cuts regions written to h_cut_layers (host
+ * int32, room for n_layers; pass them to mk_set_cuts).  Every cut set is
+ * simulated up to 16 layers, beyond that the optimum of the same additive score
+ * is found by dynamic programming.  *predicted_us: the chosen design's step
+ * time; *single_launch_us: one persistent launch's; *use_conventional: 1 if the
+ * one-kernel-per-op path wins.  MK_E_INVALID for a bad table. */
+mk_status mk_plan_cuts(const mk_cut_costs* costs, int32_t* h_cut_layers, int32_t* n_cuts, double* predicted_us,
+                       double* single_launch_us, int32_t* use_conventional);
+
 /* Number of kernel launches one decode step makes in the handle's mode. */
 int32_t mk_kernels_per_step(const mk_handle* h);
 

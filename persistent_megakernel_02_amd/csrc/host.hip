@@ -387,7 +387,7 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
 
 struct Layout {
     size_t state, tickets, instrs, qoff, layers, rope, h, qkv, attn, act, attn_part, head_part, logits_scr, tok_scr,
-        trace, trace_bytes, route, eact, eptr, total;
+        trace, trace_bytes, route, eact, eptr, cuts, total;
     size_t head_slots;  // argmax partial slots (per sequence)
 };
 
@@ -448,6 +448,7 @@ Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, i
     lo.tok_scr = take(B * 4);
     lo.trace_bytes = rt->trace ? (size_t)n_cu * per_cu * kTraceWords * 4 : 0;
     lo.trace = take(lo.trace_bytes);
+    lo.cuts = rt->mode == MK_MODE_MEGAKERNEL ? take((size_t)kMaxCuts * n_cu * 2 * 4) : 0;  // per-launch queue ranges
     lo.total = off;
     return lo;
 }
@@ -535,6 +536,7 @@ struct mk_handle {
     std::string last_error;
     // multi-position plan (persistent mode, when supported): its own workspace
     // region after the decode plan's, the decode plan's KV cache and context lengths
+    int ncut = 1;  // persistent launches per decode step (mk_set_cuts)
     bool chunk_ok = false;
     Plan cplan;
     Layout clo;
@@ -1009,7 +1011,10 @@ static mk_status run_step(mk_handle* h, const int32_t* tok_in, int32_t stride, i
         h->inject = 0;
     }
     if (h->rt.mode == MK_MODE_MEGAKERNEL) {
-        HIPCHK(h, launch_megakernel(P, A, st));
+        for (int j = 0; j < h->ncut; ++j) {  // one launch, or the parts of a cut step in order
+            if (h->ncut > 1) P.cut_q = (const uint32_t*)(h->ws + h->lo.cuts) + (size_t)j * h->P.n_cu * 2;
+            HIPCHK(h, launch_megakernel(P, A, st));
+        }
     } else if (stride != 1 || P.inject) {
         // prompt positions (strided tokens) and the fault test run uncaptured
         HIPCHK(h, launch_conventional(P, A, st));
@@ -1213,9 +1218,49 @@ mk_status mk_read_trace(mk_handle* h, void* h_buf, size_t bytes, size_t* written
     return MK_OK;
 }
 
+mk_status mk_set_cuts(mk_handle* h, const int32_t* h_layers, int32_t n) {
+    if (!h || n < 0 || (n > 0 && !h_layers) || n >= kMaxCuts) return MK_E_INVALID;
+    if (h->rt.mode != MK_MODE_MEGAKERNEL || h->rt.trace) return MK_E_UNSUPPORTED;
+    const int L = h->cfg.n_layers;
+    for (int i = 0; i < n; ++i)
+        if (h_layers[i] < 1 || h_layers[i] > L || (i > 0 && h_layers[i] <= h_layers[i - 1])) return MK_E_INVALID;
+    if (n == 0) {
+        h->ncut = 1;
+        return MK_OK;
+    }
+    // launch j runs the instructions of phases [b_j, b_{j+1}): phase = layer * 6 +
+    // sub-phase (QKV, ATTN, O, ROUTE, GATEUP / EGU, DOWN / EDOWN), the LM head L * 6
+    constexpr int kSub = 6;
+    auto phase_of = [&](const Instr& in) -> int {
+        if (in.op == OP_HEAD) return L * kSub;
+        const int k = in.op == OP_QKV ? 0 : in.op == OP_ATTN ? 1 : in.op == OP_O ? 2 : in.op == OP_ROUTE ? 3
+                    : (in.op == OP_GATEUP || in.op == OP_EGU) ? 4 : 5;
+        return in.layer * kSub + k;
+    };
+    std::vector<int> bnd(1, 0);
+    for (int i = 0; i < n; ++i) bnd.push_back(h_layers[i] * kSub);
+    bnd.push_back(L * kSub + 1);
+    const int k = n + 1, ncu = h->P.n_cu;
+    std::vector<uint32_t> q((size_t)k * ncu * 2);
+    for (int cu = 0; cu < ncu; ++cu) {
+        const uint32_t a = h->plan.qoff[cu], e = h->plan.qoff[cu + 1];
+        uint32_t i = a;
+        for (int j = 0; j < k; ++j) {
+            q[((size_t)j * ncu + cu) * 2] = i;
+            while (i < e && phase_of(h->plan.instrs[i]) < bnd[j + 1]) ++i;
+            q[((size_t)j * ncu + cu) * 2 + 1] = i;
+        }
+    }
+    HIPCHK(h, hipStreamSynchronize(h->stream));
+    if (h->used) HIPCHK(h, hipStreamSynchronize(h->last_stream));
+    HIPCHK(h, hipMemcpy(h->ws + h->lo.cuts, q.data(), q.size() * 4, hipMemcpyHostToDevice));
+    h->ncut = k;
+    return MK_OK;
+}
+
 int32_t mk_kernels_per_step(const mk_handle* h) {
     if (!h) return -1;
-    return h->rt.mode == MK_MODE_MEGAKERNEL ? 1 : conventional_kernels_per_step(h->P);
+    return h->rt.mode == MK_MODE_MEGAKERNEL ? h->ncut : conventional_kernels_per_step(h->P);
 }
 
 mk_status mk_destroy(mk_handle* h) {
@@ -1232,6 +1277,120 @@ mk_status mk_destroy(mk_handle* h) {
         g_static_busy[h->static_dev] = false;
     }
     delete h;
+    return MK_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------------------------------
+// Cut planner [page "一个大内核不够：在哪里切分流式推理模型", sections "规划器总览：只用常规画像排序切分",
+// "瓦片图如何估计单次服务时间" and "事件图如何算出首次发布分数"]: candidates are scored by
+// simulating their launches as an event graph up to the first release; nothing is
+// run end to end.  For a decode step the regions are the layers and the LM head, the
+// candidates one-kernel-per-op or one persistent launch per run of regions, and the
+// release is the step's token.
+// ------------------------------------------------------------------------------------------------
+extern "C" {
+
+mk_status mk_event_sim(const mk_event_task* tasks, int32_t n, double* h_finish) {
+    if (!tasks || !h_finish || n < 0) return MK_E_INVALID;
+    std::vector<double> stream_free;
+    for (int32_t i = 0; i < n; ++i) {
+        const mk_event_task& t = tasks[i];
+        if (t.stream < 0 || t.stream >= 1024 || t.duration < 0 || t.dispatch < 0) return MK_E_INVALID;
+        if (t.n_deps < 0 || t.n_deps > MK_EVENT_MAX_DEPS) return MK_E_INVALID;
+        double ready = 0.0;
+        for (int32_t d = 0; d < t.n_deps; ++d) {
+            const int32_t j = t.deps[d];
+            if (j < 0 || j >= i) return MK_E_INVALID;  // dependencies come earlier (a DAG in order)
+            ready = std::max(ready, h_finish[j]);
+        }
+        if ((size_t)t.stream >= stream_free.size()) stream_free.resize(t.stream + 1, 0.0);
+        // the task waits for its inputs and for its stream, then pays its dispatch
+        const double start = std::max(ready, stream_free[t.stream]) + t.dispatch;
+        h_finish[i] = start + t.duration;
+        stream_free[t.stream] = h_finish[i];
+    }
+    return MK_OK;
+}
+
+// Score of one candidate: its launches on one stream as an event graph.
+static double score_cuts(const mk_cut_costs* c, const std::vector<int>& starts) {
+    const int L = c->n_layers;
+    std::vector<mk_event_task> ev;
+    for (size_t j = 0; j < starts.size(); ++j) {
+        const int a = starts[j], b = j + 1 < starts.size() ? starts[j + 1] : L + 1;  // regions [a, b), L = head
+        mk_event_task t;
+        std::memset(&t, 0, sizeof(t));
+        t.stream = 0;
+        t.dispatch = c->launch_us;
+        double d = c->refill_us ? c->refill_us[a] : 0.0;  // nothing prefetched at a launch's start
+        for (int r = a; r < b; ++r) d += r < L ? c->layer_us[r] : c->head_us;
+        t.duration = d;
+        if (j > 0) {
+            t.n_deps = 1;
+            t.deps[0] = (int32_t)j - 1;
+        }
+        ev.push_back(t);
+    }
+    std::vector<double> fin(ev.size());
+    if (mk_event_sim(ev.data(), (int32_t)ev.size(), fin.data()) != MK_OK) return NAN;  // a negative duration
+    return fin.back();
+}
+
+mk_status mk_plan_cuts(const mk_cut_costs* c, int32_t* h_cut_layers, int32_t* n_cuts, double* predicted_us,
+                       double* single_launch_us, int32_t* use_conventional) {
+    if (!c || !h_cut_layers || !n_cuts || !predicted_us || !single_launch_us || !use_conventional) return MK_E_INVALID;
+    const int L = c->n_layers;
+    if (L < 1 || L > 4096 || !c->layer_us || c->launch_us < 0) return MK_E_INVALID;
+    // regions 0..L (L: the LM head); a candidate is the set of regions that start a launch
+    // (region 0 always does).  Up to 16 regions every candidate is simulated; beyond,
+    // the best cut set is found by dynamic programming over the same additive score
+    // (one stream: the event graph of a candidate is a chain of its launches).
+    const int R = L + 1;
+    std::vector<int> best_starts{0};
+    double best = score_cuts(c, best_starts);
+    if (std::isnan(best)) return MK_E_INVALID;
+    *single_launch_us = best;
+    if (R - 1 <= 16) {
+        for (uint32_t m = 1; m < (1u << (R - 1)); ++m) {
+            std::vector<int> st{0};
+            for (int r = 1; r < R; ++r)
+                if (m & (1u << (r - 1))) st.push_back(r);
+            const double s = score_cuts(c, st);
+            if (std::isnan(s)) return MK_E_INVALID;
+            if (s < best) {
+                best = s;
+                best_starts = st;
+            }
+        }
+    } else {
+        auto region = [&](int r) { return r < L ? c->layer_us[r] : c->head_us; };
+        std::vector<double> f(R + 1, 1e300);
+        std::vector<int> from(R + 1, 0);
+        f[0] = 0.0;
+        for (int b = 1; b <= R; ++b) {
+            double run = 0.0;
+            for (int a = b - 1; a >= 0; --a) {
+                run += region(a);
+                const double s = f[a] + c->launch_us + (c->refill_us ? c->refill_us[a] : 0.0) + run;
+                if (s < f[b]) {
+                    f[b] = s;
+                    from[b] = a;
+                }
+            }
+        }
+        std::vector<int> st;
+        for (int b = R; b > 0; b = from[b]) st.push_back(from[b]);
+        std::reverse(st.begin(), st.end());
+        best_starts = st;
+        best = score_cuts(c, st);
+        if (std::isnan(best)) return MK_E_INVALID;
+    }
+    *use_conventional = c->conventional_us > 0 && c->conventional_us < best ? 1 : 0;
+    *predicted_us = *use_conventional ? c->conventional_us : best;
+    *n_cuts = (int32_t)best_starts.size() - 1;
+    for (size_t j = 1; j < best_starts.size(); ++j) h_cut_layers[j - 1] = best_starts[j];
     return MK_OK;
 }
 

@@ -1987,7 +1987,9 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
     if (threadIdx.x < kMaxBatch)
         ctl.ctx[threadIdx.x] = (int)threadIdx.x < B ? P.ctx_len[P.chunk ? P.chunk_seq : (int)threadIdx.x] : 0;
     __syncthreads();
-    const uint32_t q0 = ld_const(P.queue_off + blockIdx.x), q1 = ld_const(P.queue_off + blockIdx.x + 1);
+    // this launch's part of the CU's queue (all of it unless the step is cut into several launches)
+    const uint32_t* qr = P.cut_q ? P.cut_q + 2u * blockIdx.x : P.queue_off + blockIdx.x;
+    const uint32_t q0 = ld_const(qr), q1 = ld_const(qr + 1);
     uint32_t hi;
     if (wave >= kComputeWaves) {
         hi = loader_wave<B, HD, MF, MOE>(P, &ctl, ring, wave - kComputeWaves, q0, q1, ctl.ctx);

@@ -241,7 +241,12 @@ struct Params {
     // 0..r, and the step advances that sequence by the rows it was given.
     int32_t* ctx_len;
     int32_t chunk, chunk_seq;
+    // A step cut into several persistent launches: this launch runs instructions
+    // [cut_q[2 cu], cut_q[2 cu + 1]) of each CU's queue (nullptr: the whole queue).
+    const uint32_t* cut_q;
 };
+// Most persistent launches one decode step may be cut into.
+constexpr int kMaxCuts = 64;
 // Rows of a multi-position step (one sequence's prompt chunk or draft tokens).
 constexpr int kChunkRows = kMaxBatch;
 

@@ -28,7 +28,8 @@ MK_GEMV_AUTO, MK_GEMV_VALU, MK_GEMV_MFMA = 0, 1, 2
 EXPORTS = ["mk_query_sizes", "mk_create", "mk_create_static", "mk_kv_layout", "mk_prefill", "mk_set_context_len", "mk_decode_step",
            "mk_get_context_len", "mk_reset", "mk_debug_inject", "mk_status_string", "mk_last_error",
            "mk_plan_inspect", "mk_kernels_per_step", "mk_destroy", "mk_bench_stream_read", "mk_bench_copy",
-           "mk_bench_sync", "mk_read_trace", "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap", "mk_moe_slots", "mk_verify_step"]
+           "mk_bench_sync", "mk_read_trace", "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap", "mk_moe_slots", "mk_verify_step", "mk_set_cuts",
+           "mk_event_sim", "mk_plan_cuts"]
 
 
 class mk_model_config(ctypes.Structure):
@@ -48,6 +49,20 @@ class mk_layer_weights(ctypes.Structure):
 class mk_weights(ctypes.Structure):
     _fields_ = [("tok_embedding", ctypes.c_void_p), ("lm_head", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
                 ("layers", ctypes.POINTER(mk_layer_weights))]
+
+
+MK_EVENT_MAX_DEPS = 8
+
+
+class mk_event_task(ctypes.Structure):
+    _fields_ = [("duration", ctypes.c_double), ("dispatch", ctypes.c_double), ("stream", ctypes.c_int32),
+                ("n_deps", ctypes.c_int32), ("deps", ctypes.c_int32 * MK_EVENT_MAX_DEPS)]
+
+
+class mk_cut_costs(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("launch_us", ctypes.c_double),
+                ("layer_us", ctypes.POINTER(ctypes.c_double)), ("refill_us", ctypes.POINTER(ctypes.c_double)),
+                ("head_us", ctypes.c_double), ("conventional_us", ctypes.c_double)]
 
 
 class mk_runtime_config(ctypes.Structure):
@@ -115,10 +130,15 @@ def lib():
         L.mk_bench_graph_gap.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ctypes.POINTER(ctypes.c_float), vp]
         L.mk_moe_slots.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64)]
         L.mk_verify_step.argtypes = [vp, i32, vp, i32, vp, vp, vp]
+        L.mk_set_cuts.argtypes = [vp, vp, i32]
+        L.mk_event_sim.argtypes = [vp, i32, vp]
+        L.mk_plan_cuts.argtypes = [ctypes.POINTER(mk_cut_costs), vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double),
+                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
         for n in ("mk_query_sizes", "mk_create", "mk_create_static", "mk_kv_layout", "mk_prefill", "mk_set_context_len",
                   "mk_get_context_len", "mk_decode_step", "mk_reset", "mk_debug_inject", "mk_plan_inspect",
                   "mk_destroy", "mk_bench_stream_read", "mk_bench_copy", "mk_bench_sync", "mk_read_trace",
-                  "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap", "mk_moe_slots", "mk_verify_step"):
+                  "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap", "mk_moe_slots", "mk_verify_step", "mk_set_cuts",
+                  "mk_event_sim", "mk_plan_cuts"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -317,6 +337,12 @@ class Decoder:
                                          next_out.data_ptr(), self.stream.cuda_stream), "mk_verify_step")
         return next_out, logits_out
 
+    def set_cuts(self, layers: Sequence[int]):
+        """Run each decode step as len(layers) + 1 persistent launches, a new one
+        starting before each listed layer (mk_set_cuts); [] restores one launch."""
+        arr = (ctypes.c_int32 * max(1, len(layers)))(*[int(x) for x in layers])
+        self._check(lib().mk_set_cuts(self.h, arr, len(layers)), "mk_set_cuts")
+
     def moe_slots(self) -> int:
         """Expert slots streamed by the MoE layers since creation (mk_moe_slots)."""
         v = ctypes.c_uint64(0)
@@ -432,3 +458,37 @@ def bench_graph_gap(n_kernels: int, reps: int, blocks: int, device="cuda:0") -> 
     _bench_check(lib().mk_bench_graph_gap(n_kernels, reps, blocks, sink.data_ptr(), ctypes.byref(us),
                                           _stream_ptr(torch.cuda.current_stream())), "mk_bench_graph_gap")
     return float(us.value)
+
+
+def event_sim(tasks) -> list:
+    """Finish times of event-graph tasks: each a dict(duration, dispatch=0, stream=0,
+    deps=()) in dependency order (mk_event_sim)."""
+    arr = (mk_event_task * len(tasks))()
+    for t, d in zip(arr, tasks):
+        t.duration, t.dispatch, t.stream = float(d["duration"]), float(d.get("dispatch", 0.0)), int(d.get("stream", 0))
+        deps = list(d.get("deps", ()))
+        t.n_deps = len(deps)
+        for i, j in enumerate(deps):
+            t.deps[i] = int(j)
+    out = (ctypes.c_double * max(1, len(tasks)))()
+    st = lib().mk_event_sim(arr, len(tasks), out)
+    if st != MK_OK:
+        raise MKError(st, "mk_event_sim")
+    return [float(out[i]) for i in range(len(tasks))]
+
+
+def plan_cuts(layer_us, launch_us: float, head_us: float, refill_us=None, conventional_us: float = 0.0) -> dict:
+    """Best design of a decode step from its service table (mk_plan_cuts)."""
+    L = len(layer_us)
+    lay = (ctypes.c_double * L)(*layer_us)
+    ref = (ctypes.c_double * (L + 1))(*refill_us) if refill_us is not None else None
+    c = mk_cut_costs(L, float(launch_us), lay, ref, float(head_us), float(conventional_us))
+    cuts = (ctypes.c_int32 * L)()
+    n, conv = ctypes.c_int32(0), ctypes.c_int32(0)
+    pred, single = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    st = lib().mk_plan_cuts(ctypes.byref(c), cuts, ctypes.byref(n), ctypes.byref(pred), ctypes.byref(single),
+                            ctypes.byref(conv))
+    if st != MK_OK:
+        raise MKError(st, "mk_plan_cuts")
+    return {"cuts": [int(cuts[i]) for i in range(n.value)], "predicted_us": pred.value,
+            "single_launch_us": single.value, "conventional": bool(conv.value)}

@@ -625,3 +625,25 @@ def test_verify_step_and_rollback(cfg_name):
         feed = o_next.astype(np.int32)
     compare(steps_ref_t, steps_ref_l, steps_t, steps_l, f"after rollback {cfg_name}")
     d.close()
+
+
+@pytest.mark.parametrize("cfg_name,cuts", [("tiny", [1]), ("tiny", [1, 2]), ("1b4", [1, 2, 3, 4]), ("1b4", [2])])
+def test_cut_steps_are_bitwise_one_launch(cfg_name, cuts):
+    """mk_set_cuts: a decode step run as several persistent launches (a new one
+    before each listed layer; n_layers = the LM head alone) gives the one-launch
+    logits and tokens bit for bit, and matches the oracle."""
+    cfg = I.TINY if cfg_name == "tiny" else I.replace(I.LLAMA_1B, n_layers=4)
+    w = I.make_weights(cfg, seed=60)
+    prompt = I.make_prompt(cfg, 1, 5, seed=61)
+    rt_, rl = oracle_run(cfg, w, prompt, 6, 16)
+    outs = []
+    for c in ([], cuts):
+        print(f"case cut step {cfg_name} cuts={c}", flush=True)
+        d = _decoder(cfg, w, 1, 16, 0)
+        d.set_cuts(c)
+        assert d.kernels_per_step() == len(c) + 1
+        outs.append(gpu_run(d, prompt, rt_, 6))
+        d.close()
+    compare(rt_, rl, outs[1][0], outs[1][1], f"cut step {cfg_name} cuts={cuts}")
+    for x, y in zip(outs[0][1], outs[1][1]):
+        assert np.array_equal(x, y)
