@@ -74,6 +74,12 @@ int mk_bench_edge(int n_wg, int words, int rounds, int stream, const void* d_src
  * do).  Returns 0, 1 on bad arguments, 4 on a runtime error. */
 int mk_bench_graph_gap(int n_kernels, int reps, int blocks, void* d_sink, float* h_us_per_kernel, void* stream);
 
+/* The device math of the decode step, elementwise, for error measurements:
+ * fn 0 expf, 1 sqrtf, 2 1.0f / x, 3 1.0f / sqrtf(x), 4 x / (1 + expf(-x)) (silu),
+ * the expressions the kernel uses.  d_x, d_y: device fp32 [n].  Enqueued on
+ * `stream`.  Returns 0, 1 on bad arguments, 4 on a launch error. */
+int mk_bench_device_math(int fn, const void* d_x, void* d_y, size_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -447,3 +447,35 @@ extern "C" int mk_bench_graph_gap(int n_kernels, int reps, int blocks, void* d_s
     (void)hipStreamDestroy(cap);
     return rc;
 }
+
+// ------------------------------------------------------------------------------------------------
+// The device math the decode step uses, evaluated elementwise so its error can be
+// measured against double precision: fn 0 expf (softmax weights), 1 sqrtf, 2 the
+// fp32 divide 1 / x, 3 the RMSNorm scale 1 / sqrtf(x), 4 silu(z) = z / (1 + expf(-z)).
+// The expressions are the ones the kernel's code uses (same compiler flags).
+// ------------------------------------------------------------------------------------------------
+namespace {
+__global__ void __launch_bounds__(256) k_device_math(int fn, const float* __restrict__ x, float* __restrict__ y,
+                                                     size_t n) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const float v = x[i];
+    float r;
+    switch (fn) {
+        case 0: r = expf(v); break;
+        case 1: r = sqrtf(v); break;
+        case 2: r = 1.0f / v; break;
+        case 3: r = 1.0f / sqrtf(v); break;
+        default: r = v / (1.0f + expf(-v)); break;
+    }
+    y[i] = r;
+}
+}  // namespace
+
+extern "C" int mk_bench_device_math(int fn, const void* d_x, void* d_y, size_t n, void* stream) {
+    if (fn < 0 || fn > 4 || !d_x || !d_y || n == 0) return 1;
+    const size_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(k_device_math, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, fn,
+                       (const float*)d_x, (float*)d_y, n);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}

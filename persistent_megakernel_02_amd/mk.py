@@ -29,7 +29,7 @@ EXPORTS = ["mk_query_sizes", "mk_create", "mk_create_static", "mk_kv_layout", "m
            "mk_get_context_len", "mk_reset", "mk_debug_inject", "mk_status_string", "mk_last_error",
            "mk_plan_inspect", "mk_kernels_per_step", "mk_destroy", "mk_bench_stream_read", "mk_bench_copy",
            "mk_bench_sync", "mk_read_trace", "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap", "mk_moe_slots", "mk_verify_step", "mk_set_cuts",
-           "mk_event_sim", "mk_plan_cuts"]
+           "mk_event_sim", "mk_plan_cuts", "mk_bench_device_math"]
 
 
 class mk_model_config(ctypes.Structure):
@@ -132,13 +132,14 @@ def lib():
         L.mk_verify_step.argtypes = [vp, i32, vp, i32, vp, vp, vp]
         L.mk_set_cuts.argtypes = [vp, vp, i32]
         L.mk_event_sim.argtypes = [vp, i32, vp]
+        L.mk_bench_device_math.argtypes = [ctypes.c_int, vp, vp, sz, vp]
         L.mk_plan_cuts.argtypes = [ctypes.POINTER(mk_cut_costs), vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
         for n in ("mk_query_sizes", "mk_create", "mk_create_static", "mk_kv_layout", "mk_prefill", "mk_set_context_len",
                   "mk_get_context_len", "mk_decode_step", "mk_reset", "mk_debug_inject", "mk_plan_inspect",
                   "mk_destroy", "mk_bench_stream_read", "mk_bench_copy", "mk_bench_sync", "mk_read_trace",
                   "mk_bench_pingpong", "mk_bench_edge", "mk_bench_graph_gap", "mk_moe_slots", "mk_verify_step", "mk_set_cuts",
-                  "mk_event_sim", "mk_plan_cuts"):
+                  "mk_event_sim", "mk_plan_cuts", "mk_bench_device_math"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -492,3 +493,14 @@ def plan_cuts(layer_us, launch_us: float, head_us: float, refill_us=None, conven
         raise MKError(st, "mk_plan_cuts")
     return {"cuts": [int(cuts[i]) for i in range(n.value)], "predicted_us": pred.value,
             "single_launch_us": single.value, "conventional": bool(conv.value)}
+
+
+def device_math(fn: int, x):
+    """The decode step's device math on a CUDA fp32 tensor (mk_bench_device_math)."""
+    import torch
+
+    y = torch.empty_like(x)
+    _bench_check(lib().mk_bench_device_math(fn, x.data_ptr(), y.data_ptr(), x.numel(), _stream_ptr(None)),
+                 "mk_bench_device_math")
+    torch.cuda.synchronize()
+    return y
