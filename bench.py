@@ -365,8 +365,9 @@ def main() -> int:
             per_h.append(ms * 1000.0 / n)
             positions.extend(range(P, P + n))
             left -= n
-        # separate pass with an event after every step, for the percentiles
-        per_step = []
+        # separate pass with an event after every step, for the percentiles and the
+        # time against the context length
+        per_step, per_pos = [], []
         left = args.steps
         while left > 0:
             n = min(left, H)
@@ -379,6 +380,7 @@ def main() -> int:
                 ev[i + 1].record(st)
             ev[-1].synchronize()
             per_step.extend(ev[i].elapsed_time(ev[i + 1]) * 1000.0 for i in range(n))
+            per_pos.extend((P + i, ev[i].elapsed_time(ev[i + 1]) * 1000.0) for i in range(n))
             left -= n
         kps = dec.kernels_per_step()
         dec.close()
@@ -386,11 +388,18 @@ def main() -> int:
         pct = (float(np.percentile(per_step, 50)), float(np.percentile(per_step, 95)))
         log(f"{label}: {us:.1f} us/token over {args.steps} steps ({kps} kernels/step), "
             f"p50 {pct[0]:.1f} p95 {pct[1]:.1f}")
-        return us, positions, kps, per_h, pct, slots / args.steps
+        # mean step time over quarters of the horizon (the context grows by one per step)
+        by_pos = {}
+        q = max(1, H // 4)
+        for a in range(P, P + H, q):
+            vals = [t for p_, t in per_pos if a <= p_ < a + q]
+            if vals:
+                by_pos[f"{a}-{a + q - 1}"] = round(float(np.mean(vals)), 2)
+        return us, positions, kps, per_h, pct, slots / args.steps, by_pos
 
     gemv_used = mk.mk_plan_inspect(mk.model_config(cfg), mk.runtime_config(B, max_seq, gemv_kind=gemv),
                                    torch.cuda.get_device_properties(dev).multi_processor_count)[1]["gemv_kind"]
-    us_mk, positions, kps_mk, per_h, pct_mk, slots_step = run_path(mk.MK_MODE_MEGAKERNEL, "megakernel")
+    us_mk, positions, kps_mk, per_h, pct_mk, slots_step, by_pos = run_path(mk.MK_MODE_MEGAKERNEL, "megakernel")
     prefill = cuts = None
     if CTX == 0:
         pdec = mk.Decoder(cfg, w, max_batch=B, max_seq=max_seq, device="cuda:0", device_weights=dw)
@@ -413,7 +422,7 @@ def main() -> int:
 
     us_graph = kps_graph = pct_graph = None
     if not args.no_graph and not cfg.is_moe:  # the one-kernel-per-op path has no MoE kernels
-        us_graph, _, kps_graph, _, pct_graph, _ = run_path(mk.MK_MODE_GRAPH, "hipGraph one-kernel-per-op")
+        us_graph, _, kps_graph, _, pct_graph, _, _ = run_path(mk.MK_MODE_GRAPH, "hipGraph one-kernel-per-op")
 
     # streaming-read ceiling on a buffer the size of the step
     buf = torch.empty(int(mean_bytes) // 16 * 16, dtype=torch.uint8, device=dev)
@@ -489,6 +498,7 @@ def main() -> int:
         "stream_read_ceiling_gbs": round(ceil_gbs, 1),
         "kernels_per_step": kps_mk,
         "us_per_token_per_horizon": [round(x, 2) for x in per_h],
+        "us_per_step_by_position": by_pos,
         "graph_path": None if us_graph is None else {"us_per_token": round(us_graph, 2),
                                                      "p50": round(pct_graph[0], 2),
                                                      "p95": round(pct_graph[1], 2),
