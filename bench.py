@@ -458,14 +458,16 @@ def main() -> int:
         else:
             nxt, _ = orc.prefill(prompt[:, :4])
             orc.pos[:] = P
-        t2 = time.time()
+        step_us = []
         for _ in range(nsteps):
+            t2 = time.time()
             nxt, _ = orc.step(nxt)
-        t3 = time.time()
-        cpu_us = (t3 - t2) * 1e6 / nsteps
+            step_us.append((time.time() - t2) * 1e6)
+        cpu_us = float(np.median(step_us))  # median over the sampled steps
         cpu = {"value": round(cpu_us, 1), "unit": "us/token" if B == 1 else "us/step", "cores": O.threads(),
                "kind": "oracle", "cpu_model": cpu_model(),
-               "sample": f"{nsteps} batch-{B} decode steps of the same {cfg.name} model at positions "
+               "tokens_per_s": round(B * 1e6 / cpu_us, 2),
+               "sample": f"median of {nsteps} batch-{B} decode steps of the same {cfg.name} model at positions "
                          f"{P}..{P + nsteps - 1} (fp64-accumulated C oracle, OpenMP over rows)"}
         log(f"cpu oracle: {cpu_us / 1000:.1f} ms/step on {O.threads()} threads")
 
