@@ -109,12 +109,14 @@ size_t x_floats_kind(const mk_model_config* c, const mk_runtime_config* rt, int 
     n = std::max(n, B * (ow + (xsl > 1 ? 2 : 1) * kMaxResidRows));
     if (c->n_experts > 0) {
         // EGU: x rows (one slice) and the router logits, and sliced the partial sums
-        // of every selected slot's rows; EDOWN: one expert's SwiGLU rows, the
-        // residual rows, their sums and the router logits
+        // of every selected slot's rows; EPART: the router logits and one slot's
+        // SwiGLU rows; EDOWN: the router logits, the slots' weights, the residual rows
+        // and every slot's outputs of its rows
         const size_t E = (size_t)c->n_experts;
         const size_t slots = (size_t)c->n_shared_experts + std::min(E, B * (size_t)c->top_k);
         n = std::max(n, B * (dw + E) + (xsl > 1 ? slots * 2 * kMaxEguSlicedRows * B : 0));
-        n = std::max(n, B * ((size_t)c->expert_ffn + 2 * kMaxResidRows + E) + B * (E + 1));
+        n = std::max(n, B * ((size_t)c->expert_ffn + E));
+        n = std::max(n, B * E + (slots + 1) * B + B * kMaxEredRows + slots * B * kMaxEredRows);
         return std::max(n, attn_lds_floats((int)G, (int)hd, nsplit, nnew));
     }
     // DOWN: one column slice of the input, the residual rows and the partial sums
@@ -299,11 +301,14 @@ Plan build_plan(const mk_model_config* c, const mk_runtime_config* rt, int n_cu)
         ++pl.phases;
         gemv_phase(OP_O, l, (uint32_t)c->hidden, kMaxResidRows);
         if (c->n_experts) {
-            // router rows; then on every CU its f-range of every selected expert;
-            // then its rows of every selected expert's down projection
+            // router rows; then on every CU its f-range of every selected expert; then
+            // its share of the (selected expert, down row) pairs (begin: the CU); then
+            // the weighted combine of its output rows
             gemv_phase(OP_ROUTE, l, (uint32_t)c->n_experts, sliced ? kMaxResidRows : all);
             gemv_phase(OP_EGU, l, (uint32_t)c->expert_ffn, sliced ? kMaxEguSlicedRows : all);
-            gemv_phase(OP_EDOWN, l, (uint32_t)c->hidden, kMaxResidRows);
+            for (int cu = 0; cu < n_cu; ++cu) q[cu].push_back(mk_instr(OP_EPART, l, (uint32_t)cu, 1));
+            ++pl.phases;
+            gemv_phase(OP_EDOWN, l, (uint32_t)c->hidden, kMaxEredRows);
         } else {
             gemv_phase(OP_GATEUP, l, (uint32_t)c->ffn, all);
             gemv_phase(OP_DOWN, l, (uint32_t)c->hidden, kMaxResidRows);
@@ -327,8 +332,8 @@ Plan build_plan(const mk_model_config* c, const mk_runtime_config* rt, int n_cu)
 int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Plan& pl) {
     const int L = c->n_layers, B = rt->max_batch;
     const uint32_t qkv_rows = (uint32_t)((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim);
-    // sub-phases per layer: QKV, ATTN, O, ROUTE (MoE), GATEUP / EGU, DOWN / EDOWN
-    constexpr int kSub = 6;
+    // sub-phases per layer: QKV, ATTN, O, ROUTE (MoE), GATEUP / EGU, EPART (MoE), DOWN / EDOWN
+    constexpr int kSub = 7;
     const bool moe = c->n_experts != 0;
     const bool sliced = x_slices_for(B, c->hidden, c->n_q_heads * c->head_dim, moe) > 1;
     const int nphase = L * kSub + 1;
@@ -336,7 +341,7 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
     auto phase_of = [&](const Instr& in) -> int {
         if (in.op == OP_HEAD) return L * kSub;
         const int k = in.op == OP_QKV ? 0 : in.op == OP_ATTN ? 1 : in.op == OP_O ? 2 : in.op == OP_ROUTE ? 3
-                    : (in.op == OP_GATEUP || in.op == OP_EGU) ? 4 : 5;
+                    : (in.op == OP_GATEUP || in.op == OP_EGU) ? 4 : in.op == OP_EPART ? 5 : 6;
         return in.layer * kSub + k;
     };
     auto extent = [&](int ph) -> uint32_t {
@@ -347,6 +352,7 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
             case 2: return (uint32_t)c->hidden;
             case 3: return moe ? (uint32_t)c->n_experts : 0u;
             case 4: return moe ? (uint32_t)c->expert_ffn : (uint32_t)c->ffn;
+            case 5: return moe ? (uint32_t)pl.n_cu : 0u;  // one expert-down share per CU
             default: return (uint32_t)c->hidden;
         }
     };
@@ -357,8 +363,8 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
         int last = -1;
         for (uint32_t i = pl.qoff[cu]; i < pl.qoff[cu + 1]; ++i) {
             const Instr& in = pl.instrs[i];
-            if (in.op < OP_QKV || in.op > OP_EDOWN) return 1;
-            const bool moe_op = in.op == OP_ROUTE || in.op == OP_EGU || in.op == OP_EDOWN;
+            if (in.op < OP_QKV || in.op > OP_EPART) return 1;
+            const bool moe_op = in.op == OP_ROUTE || in.op == OP_EGU || in.op == OP_EDOWN || in.op == OP_EPART;
             if (moe_op != moe && in.op != OP_QKV && in.op != OP_ATTN && in.op != OP_O && in.op != OP_HEAD) return 1;
             if (in.op != OP_HEAD && in.layer >= L) return 2;
             const int ph = phase_of(in);
@@ -366,7 +372,9 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
             last = ph;
             const uint32_t ext = extent(ph);
             if (in.count == 0 || in.begin + in.count > ext || in.begin + in.count < in.begin) return 5;
-            if ((in.op == OP_O || in.op == OP_DOWN || in.op == OP_EDOWN) && in.count > kMaxResidRows) return 4;
+            if ((in.op == OP_O || in.op == OP_DOWN) && in.count > kMaxResidRows) return 4;
+            if (in.op == OP_EDOWN && in.count > kMaxEredRows) return 4;
+            if (in.op == OP_EPART && (in.begin != (uint32_t)cu || in.count != 1)) return 4;
             if (sliced && (in.op == OP_QKV || in.op == OP_ROUTE) && in.count > kMaxResidRows) return 4;
             if (sliced && in.op == OP_EGU && in.count > kMaxEguSlicedRows) return 4;
             for (uint32_t r = in.begin; r < in.begin + in.count; ++r) {
@@ -387,7 +395,7 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
 
 struct Layout {
     size_t state, tickets, instrs, qoff, layers, rope, h, qkv, attn, act, attn_part, head_part, logits_scr, tok_scr,
-        trace, trace_bytes, route, eact, eptr, cuts, total;
+        trace, trace_bytes, route, eact, eptr, cuts, epart, total;
     size_t head_slots;  // argmax partial slots (per sequence)
 };
 
@@ -406,8 +414,10 @@ void plan_counts(const mk_model_config* c, const mk_runtime_config* rt, int n, i
     const size_t qkv = sliced ? cut(qkv_rows, kMaxResidRows) : 1;  // sliced inputs: cut instructions
     const size_t route = !moe ? 0 : sliced ? cut((size_t)c->n_experts, kMaxResidRows) : 1;
     const size_t ffn = sliced ? cut((size_t)c->expert_ffn, kMaxEguSlicedRows) : 1;  // GATEUP / EGU
-    *per_cu = (size_t)c->n_layers * (qkv + route + ffn + 2 * od + (items + n - 1) / n) + 1;
-    *total = (size_t)c->n_layers * ((qkv + route + ffn) * (size_t)n + items + 2 * od * (size_t)n) + (size_t)n;
+    // MoE: one expert-down share per CU, and combine instructions of kMaxEredRows rows
+    const size_t epart = moe ? 1 : 0, down = moe ? cut((size_t)c->hidden, kMaxEredRows) : od;
+    *per_cu = (size_t)c->n_layers * (qkv + route + ffn + epart + od + down + (items + n - 1) / n) + 1;
+    *total = (size_t)c->n_layers * ((qkv + route + ffn + epart + od + down) * (size_t)n + items) + (size_t)n;
 }
 
 Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, int nsplit) {
@@ -436,6 +446,9 @@ Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, i
     const size_t nx = c->n_experts ? (size_t)(c->n_shared_experts + c->n_experts) : 0;
     lo.route = take(B * (size_t)c->n_experts * 8);
     lo.eact = take(nx * B * (size_t)c->expert_ffn * 8);
+    // selected slots of a layer at most: the shared experts and B x top_k routed ones
+    const size_t slots = c->n_experts ? (size_t)c->n_shared_experts + std::min((size_t)c->n_experts, B * c->top_k) : 0;
+    lo.epart = take(slots * B * d * 8);
     lo.eptr = take((size_t)c->n_layers * 3 * nx * 8);
     lo.attn_part = take(B * c->n_kv_heads * nsplit * G * (hd + 2) * 8);
     // argmax partial slots: one LM-head instruction per CU (persistent), or the
@@ -753,6 +766,7 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
     P.route = (uint64_t*)(ws + lo.route);
     P.eact = (uint64_t*)(ws + lo.eact);
     P.eptr = (const uint16_t* const*)(ws + lo.eptr);
+    P.epart = (uint64_t*)(ws + lo.epart);
     P.attn_ticket = (uint32_t*)(ws + lo.tickets);
     P.head_ticket = P.attn_ticket + (size_t)cfg->n_layers * rt->max_batch * cfg->n_kv_heads * kCtrStride;
     P.state = (DevState*)(ws + lo.state);
@@ -835,6 +849,7 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
         C.head_part = (uint64_t*)(cb + cl.head_part);
         C.route = (uint64_t*)(cb + cl.route);
         C.eact = (uint64_t*)(cb + cl.eact);
+        C.epart = (uint64_t*)(cb + cl.epart);
         C.eptr = (const uint16_t* const*)(cb + cl.eptr);
         C.attn_ticket = (uint32_t*)(cb + cl.tickets);
         C.head_ticket = C.attn_ticket + (size_t)cfg->n_layers * kChunkRows * cfg->n_kv_heads * kCtrStride;
@@ -1228,13 +1243,13 @@ mk_status mk_set_cuts(mk_handle* h, const int32_t* h_layers, int32_t n) {
         h->ncut = 1;
         return MK_OK;
     }
-    // launch j runs the instructions of phases [b_j, b_{j+1}): phase = layer * 6 +
-    // sub-phase (QKV, ATTN, O, ROUTE, GATEUP / EGU, DOWN / EDOWN), the LM head L * 6
-    constexpr int kSub = 6;
+    // launch j runs the instructions of phases [b_j, b_{j+1}): phase = layer * 7 +
+    // sub-phase (QKV, ATTN, O, ROUTE, GATEUP / EGU, EPART, DOWN / EDOWN), the LM head L * 7
+    constexpr int kSub = 7;
     auto phase_of = [&](const Instr& in) -> int {
         if (in.op == OP_HEAD) return L * kSub;
         const int k = in.op == OP_QKV ? 0 : in.op == OP_ATTN ? 1 : in.op == OP_O ? 2 : in.op == OP_ROUTE ? 3
-                    : (in.op == OP_GATEUP || in.op == OP_EGU) ? 4 : 5;
+                    : (in.op == OP_GATEUP || in.op == OP_EGU) ? 4 : in.op == OP_EPART ? 5 : 6;
         return in.layer * kSub + k;
     };
     std::vector<int> bnd(1, 0);

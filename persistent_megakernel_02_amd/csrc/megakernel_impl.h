@@ -77,12 +77,16 @@ __device__ __forceinline__ int ctx_of(const int32_t* ctx, int b) { return __buil
 __device__ __forceinline__ bool is_gemv(uint32_t op) {
     return op == OP_QKV || op == OP_O || op == OP_GATEUP || op == OP_DOWN || op == OP_HEAD;
 }
-__device__ __forceinline__ bool is_moe_expert(uint32_t op) { return op == OP_EGU || op == OP_EDOWN; }
+__device__ __forceinline__ bool is_moe_expert(uint32_t op) { return op == OP_EGU || op == OP_EPART; }
 
 // Stream bytes of an MoE expert instruction with n selected expert slots: per slot
-// the CU's (gate, up) row pairs (EGU) or its down rows (EDOWN), whole rows.
+// the CU's (gate, up) row pairs (EGU), or the down rows of the CU's share of the
+// (slot, row) pairs (EPART); whole rows.
 __device__ __forceinline__ uint32_t moe_bytes(const Params& P, const Instr& in, uint32_t n) {
-    return in.op == OP_EGU ? n * 2u * in.count * (uint32_t)P.d * 2u : n * in.count * (uint32_t)P.Fe * 2u;
+    if (in.op == OP_EGU) return n * 2u * in.count * (uint32_t)P.d * 2u;
+    uint32_t t0, t1;
+    moe_part_range(n, (uint32_t)P.d, P.n_cu, (int)in.begin, &t0, &t1);
+    return (t1 - t0) * (uint32_t)P.Fe * 2u;
 }
 
 // Bytes of the CU stream that instruction `in` consumes (whole chunks).  With the
@@ -585,30 +589,53 @@ __device__ __forceinline__ uint32_t loader_wave(const Params& P, Ctl* ctl, char*
                     }
                     rs += LC;
                 }
-            } else if (MOE && is_moe_expert(in.op)) {
-                // selected expert slot a, chunk w of its rows; the slot's matrices come
-                // from the expert table (gate and up rows interleaved as in GATEUP)
-                const bool egu = in.op == OP_EGU;
+            } else if (MOE && in.op == OP_EPART) {
+                // the CU's (selected slot, down row) pairs [t0, t1) in slot-major order:
+                // per slot a run of consecutive rows of its down matrix, cpr chunks a row
                 const uint32_t n = lds_ld(&ctl->moe_n), nx = (uint32_t)(P.n_shared + P.E);
-                const uint32_t rb = egu ? (uint32_t)P.d * 2u : (uint32_t)P.Fe * 2u;
-                const uint32_t per = (egu ? 2u * in.count : in.count) * rb / kChunk;
+                const uint16_t* const* tab = P.eptr + ((size_t)in.layer * 3u + 2u) * nx;
+                const uint32_t d = (uint32_t)P.d, cpr = (uint32_t)P.Fe * 2u / kChunk;
+                uint32_t t0, t1;
+                moe_part_range(n, d, P.n_cu, (int)in.begin, &t0, &t1);
+                const uint32_t w = c - cb, r = w / cpr;
+                uint32_t wc = w - r * cpr, a = (t0 + r) / d, i = t0 + r - a * d;
+                const char* base =
+                    (const char*)ld_const(tab + __builtin_amdgcn_readfirstlane((uint32_t)ctl->moe_list[a]));
+                for (; c < ce; ) {
+                    if (c >= limit && !make_room()) {
+                        stop = true;
+                        break;
+                    }
+                    dma_chunk_s(uniform_ptr(base), (i * cpr + wc) * kChunk + (uint32_t)lane_id() * 16u, slot);
+                    advance();
+                    for (wc += NL; wc >= cpr;) {
+                        wc -= cpr;
+                        if (++i == d) {
+                            i = 0;
+                            if (++a < n)
+                                base = (const char*)ld_const(
+                                    tab + __builtin_amdgcn_readfirstlane((uint32_t)ctl->moe_list[a]));
+                        }
+                    }
+                }
+            } else if (MOE && in.op == OP_EGU) {
+                // selected expert slot a, chunk w of its (gate, up) row pairs; the slot's
+                // matrices come from the expert table (rows interleaved as in GATEUP)
+                const uint32_t n = lds_ld(&ctl->moe_n), nx = (uint32_t)(P.n_shared + P.E);
+                const uint32_t rb = (uint32_t)P.d * 2u;
+                const uint32_t per = 2u * in.count * rb / kChunk;
                 const uint16_t* const* tab = P.eptr + (size_t)in.layer * 3u * nx;
                 auto slot_stream = [&](uint32_t a, Stream& X) {
                     const uint32_t x = __builtin_amdgcn_readfirstlane((uint32_t)ctl->moe_list[a]);
                     X.attn = X.sliced = false;
                     X.end0 = X.end1 = 0xFFFFFFFFu;
                     X.p1 = X.p2 = X.head = nullptr;
-                    if (egu) {
-                        X.p0 = (const char*)(ld_const(tab + x) + (size_t)in.begin * P.d);
-                        X.p1 = (const char*)(ld_const(tab + nx + x) + (size_t)in.begin * P.d);
-                        X.per_shift = (uint32_t)__builtin_ctz(rb / kChunk);
-                        X.inter = true;
-                    } else {
-                        X.p0 = (const char*)(ld_const(tab + 2u * nx + x) + (size_t)in.begin * P.Fe);
-                        X.inter = false;
-                    }
+                    X.p0 = (const char*)(ld_const(tab + x) + (size_t)in.begin * P.d);
+                    X.p1 = (const char*)(ld_const(tab + nx + x) + (size_t)in.begin * P.d);
+                    X.per_shift = (uint32_t)__builtin_ctz(rb / kChunk);
+                    X.inter = true;
                 };
-                if (egu && P.x_slices > 1) {
+                if (P.x_slices > 1) {
                     // sliced input: slice-major over every selected slot: slice s of
                     // slot a's (gate, up) row pairs, cps chunks per row slice
                     const uint32_t sb = rb / (uint32_t)P.x_slices, cps = sb / kChunk, pss = 2u * in.count * cps;
@@ -1586,26 +1613,126 @@ __device__ __forceinline__ bool moe_egu_sliced(const Params& P, const StepArgs& 
     return true;
 }
 
-// OP_EDOWN: route again (same logits, same result); for every selected slot in
-// order (shared, then ascending experts) stage its SwiGLU rows and add its down
-// rows [begin, begin + count), weighted by the sequence's probability (1 for the
-// shared expert, 0 where the sequence did not select it); then h += the sum.
+// OP_EPART: route again (same logits, same result; the loader waits for the slot
+// list, so the weight stream starts before the SwiGLU outputs are ready); then for
+// each selected slot a in the CU's share of the (slot, down row) pairs: stage the
+// slot's SwiGLU rows and store the unweighted down rows' outputs epart[a][b][row].
+// A CU stages the inputs of the few slots its share touches, not of every slot.
 template <int B>
-__device__ __forceinline__ bool moe_edown(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs,
+__device__ __forceinline__ bool moe_epart(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs,
                                           int wave, const Instr& in, uint32_t qi, uint32_t S, Spin& spin,
                                           CwBarrier& barrier, uint32_t& land_wait, uint32_t* tr, uint32_t& bytes) {
     const int lane = lane_id();
     const int layer = in.layer;
-    const uint32_t E = (uint32_t)P.E, Fe = (uint32_t)P.Fe, cnt = in.count;
+    const uint32_t E = (uint32_t)P.E, Fe = (uint32_t)P.Fe, d = (uint32_t)P.d;
     const uint32_t tag_o = phase_tag(A.tag0, layer, 2), tag_a = phase_tag(A.tag0, layer, 3);
-    float* hres = xs + B * Fe;    // [B][cnt] residual rows after O
-    float* acc = hres + B * cnt;  // [B][cnt] weighted expert sums
-    float* zeta = acc + B * cnt;  // [B][E] router logits
-    float* wtab = zeta + B * E;   // [slot][B] weights of the selected slots
+    float* zeta = xs + B * Fe;  // [B][E] router logits, after one slot's SwiGLU rows
+    {
+        float ss[1] = {0.f};
+        const StageSeg sg[1] = {{P.route, zeta, nullptr, E, (uint32_t)B, E, E, tag_o, 0u}};
+        if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kComputeWaves, spin, ss)) return false;
+    }
+    if (!barrier()) return false;
+    uint32_t n;
+    {
+        uint64_t sel[B];
+        float prob[B];
+        n = moe_route<B>(P, ctl, zeta, wave, qi, sel, prob);
+    }
+    if (!barrier()) return false;  // the slot list is visible
+    if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
+    uint32_t t0, t1;
+    moe_part_range(n, d, P.n_cu, (int)in.begin, &t0, &t1);
+    bytes = (t1 - t0) * Fe * 2u;
+    const uint32_t rb = Fe * 2u;
+    uint32_t off = S;
+    for (uint32_t t = t0; t < t1;) {
+        const uint32_t a = t / d, i0 = t - a * d, nr = min(d, t1 - a * d) - i0;
+        const uint32_t x = __builtin_amdgcn_readfirstlane((uint32_t)ctl->moe_list[a]);
+        if (t > t0 && !barrier()) return false;  // every wave is done with the previous slot's rows
+        float ss[1] = {0.f};
+        const StageSeg sa[1] = {{P.eact + (size_t)x * P.B * Fe, xs, nullptr, Fe, (uint32_t)B, Fe, Fe, tag_a, 0u}};
+        if (!stage_segs<kStagePassWordsWide, 1, 1>(sa, wave, kComputeWaves, spin, ss)) return false;
+        if (!barrier()) return false;
+        uint64_t* dst = P.epart + (size_t)a * B * d + i0;
+        auto epi = [&](uint32_t r0, uint32_t nrr, auto& res) {
+            #pragma unroll
+            for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i) {
+                if (i >= nrr) break;
+                if (lane < B) st_tagged(dst + (size_t)lane * d + r0 + i, pick<B>(res[i], lane), tag_a);
+            }
+        };
+        if (!gemv_ring_auto<B>(P, ctl, ring, off, rb, nr, XLds{xs, Fe}, wave, land_wait, epi, false)) return false;
+        off += nr * rb;
+        release_region(ctl, wave, off);
+        t += nr;
+    }
+    return true;
+}
+
+// Stages rows [0, nrows) x columns [0, cnt) (cnt <= 16) of the tagged words at
+// src (row stride `stride` words) into dst [nrows][cnt] once each carries `tag`.
+// Lane l of compute wave w takes column l % 16 of rows 4 w + l / 16 + 16 k: K
+// rows per lane per pass, any number of rows (the generic staging resolves at
+// most kMaxBatch rows per segment).
+static_assert(kMaxEredRows <= 16, "the combine stages at most 16 columns a row");
+template <int K>
+__device__ __forceinline__ bool stage_grid16(const uint64_t* src, uint32_t stride, uint32_t nrows, uint32_t cnt,
+                                             float* dst, uint32_t tag, int wave, Spin& spin) {
+    const uint32_t lane = (uint32_t)lane_id(), j = lane & 15u;
+    const uint32_t first = (uint32_t)wave * 4u + (lane >> 4);
+    for (uint32_t p0 = 0; p0 < nrows; p0 += 16u * (uint32_t)K) {
+        uint64_t v[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const uint32_t r = p0 + first + 16u * (uint32_t)k;
+            v[k] = (r < nrows && j < cnt) ? ld_tagged(src + (size_t)r * stride + j) : 0ull;
+        }
+        spin.start();
+        for (;;) {
+            bool ok = true;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const uint32_t r = p0 + first + 16u * (uint32_t)k;
+                ok &= !(r < nrows && j < cnt) || tv_tag(v[k]) == tag;
+            }
+            if (__all(ok)) break;
+            if (!spin.again(tag, p0)) return false;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const uint32_t r = p0 + first + 16u * (uint32_t)k;
+                if (r < nrows && j < cnt && tv_tag(v[k]) != tag) v[k] = ld_tagged(src + (size_t)r * stride + j);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const uint32_t r = p0 + first + 16u * (uint32_t)k;
+            if (r < nrows && j < cnt) dst[r * cnt + j] = tv_val(v[k]);
+        }
+    }
+    return true;
+}
+
+// OP_EDOWN: route again; for output rows [begin, begin + count) stage every
+// selected slot's outputs (epart) and add them in slot order (shared, then
+// ascending experts), weighted by the sequence's probability (1 for the shared
+// expert; slots the sequence did not select are skipped); then h += the sum.
+template <int B>
+__device__ __forceinline__ bool moe_ered(const Params& P, const StepArgs& A, Ctl* ctl, float* xs, int wave,
+                                         const Instr& in, uint32_t qi, Spin& spin, CwBarrier& barrier, uint32_t* tr) {
+    const int lane = lane_id();
+    const int layer = in.layer;
+    const uint32_t E = (uint32_t)P.E, d = (uint32_t)P.d, cnt = in.count;
+    const uint32_t tag_o = phase_tag(A.tag0, layer, 2), tag_a = phase_tag(A.tag0, layer, 3);
+    const uint32_t smax = (uint32_t)P.n_shared + min(E, (uint32_t)(B * P.top_k));
+    float* zeta = xs;                    // [B][E] router logits
+    float* wtab = zeta + B * E;          // [slot][B] weights of the selected slots
+    float* hres = wtab + (smax + 1u) * B;  // [B][cnt] residual rows after O
+    float* part = hres + B * cnt;        // [slot][B][cnt] the slots' outputs of the rows
     {
         float ss[1] = {0.f};
         const StageSeg sg[2] = {{P.route, zeta, nullptr, E, (uint32_t)B, E, E, tag_o, 0u},
-                                {P.h + in.begin, hres, nullptr, cnt, (uint32_t)B, (uint32_t)P.d, cnt, tag_o, 0u}};
+                                {P.h + in.begin, hres, nullptr, cnt, (uint32_t)B, d, cnt, tag_o, 0u}};
         if (!stage_segs<kStagePassWordsWide, 1, 2>(sg, wave, kComputeWaves, spin, ss)) return false;
     }
     if (!barrier()) return false;
@@ -1627,42 +1754,21 @@ __device__ __forceinline__ bool moe_edown(const Params& P, const StepArgs& A, Ct
                 if (mine) wtab[slot * B + b] = ((sel[b] >> lane) & 1ull) ? prob[b] : 0.f;
                 if (lane < P.n_shared) wtab[lane * B + b] = 1.0f;
             }
-            for (uint32_t i = (uint32_t)lane; i < B * cnt; i += 64u) acc[i] = 0.f;
         }
     }
-    if (!barrier()) return false;  // the slot list, the weights and the zeroed sums are visible
     if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
-    bytes = moe_bytes(P, in, n);
-    const uint32_t rb = Fe * 2u;
-    for (uint32_t a = 0; a < n; ++a) {
-        const uint32_t x = __builtin_amdgcn_readfirstlane((uint32_t)ctl->moe_list[a]);
-        float wgt[B];
-#pragma unroll
-        for (int b = 0; b < B; ++b) wgt[b] = wtab[a * B + b];
-        if (a > 0 && !barrier()) return false;  // every wave is done with the previous slot's rows
-        float ss[1] = {0.f};
-        const StageSeg sa[1] = {{P.eact + (size_t)x * P.B * Fe, xs, nullptr, Fe, (uint32_t)B, Fe, Fe, tag_a, 0u}};
-        if (!stage_segs<kStagePassWordsWide, 1, 1>(sa, wave, kComputeWaves, spin, ss)) return false;
-        if (!barrier()) return false;
-        auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
-            #pragma unroll
-            for (uint32_t i = 0; i < (uint32_t)(sizeof(res) / sizeof(res[0])); ++i) {
-                if (i >= nr) break;
-                if (lane < B) {
-                    const float wv = pick<B>(wgt, lane);
-                    if (wv != 0.f) acc[lane * cnt + r0 + i] += wv * pick<B>(res[i], lane);
-                }
-            }
-        };
-        if (!gemv_ring_auto<B>(P, ctl, ring, S + a * cnt * rb, rb, cnt, XLds{xs, Fe}, wave, land_wait, epi, false))
-            return false;
-        release_region(ctl, wave, S + (a + 1u) * cnt * rb);
-    }
-    if (!barrier()) return false;
+    // row a * B + b of the staged outputs is epart row a * B + b
+    if (!stage_grid16<8>(P.epart + in.begin, d, n * (uint32_t)B, cnt, part, tag_a, wave, spin)) return false;
+    if (!barrier()) return false;  // the weights and the staged outputs are visible
     const uint32_t tag_out = phase_tag(A.tag0, layer, 4);
     for (uint32_t i = (uint32_t)(wave * 64 + lane); i < B * cnt; i += 64u * kComputeWaves) {
         const uint32_t b = i / cnt, j = i - b * cnt;
-        st_tagged(P.h + (size_t)b * P.d + in.begin + j, hres[i] + acc[i], tag_out);
+        float acc = 0.f;
+        for (uint32_t a = 0; a < n; ++a) {
+            const float wv = wtab[a * B + b];
+            if (wv != 0.f) acc += wv * part[(a * B + b) * cnt + j];
+        }
+        st_tagged(P.h + (size_t)b * d + in.begin + j, hres[i] + acc, tag_out);
     }
     return true;
 }
@@ -1736,8 +1842,11 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
                 }
                 if constexpr (MOE) ok = moe_egu<B>(P, A, ctl, ring, xs, wave, in, qi, S, spin, barrier, land_wait, tr, bytes);
                 break;
+            case OP_EPART:
+                if constexpr (MOE) ok = moe_epart<B>(P, A, ctl, ring, xs, wave, in, qi, S, spin, barrier, land_wait, tr, bytes);
+                break;
             case OP_EDOWN:
-                if constexpr (MOE) ok = moe_edown<B>(P, A, ctl, ring, xs, wave, in, qi, S, spin, barrier, land_wait, tr, bytes);
+                if constexpr (MOE) ok = moe_ered<B>(P, A, ctl, xs, wave, in, qi, spin, barrier, tr);
                 break;
             case OP_QKV:
             case OP_GATEUP:

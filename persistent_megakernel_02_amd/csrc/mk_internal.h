@@ -142,8 +142,22 @@ enum Op : uint16_t {
     OP_HEAD = 6,    // final RMSNorm + LM-head rows + argmax partials
     OP_ROUTE = 7,   // MoE: RMSNorm + router rows -> router logits (fp32)
     OP_EGU = 8,     // MoE: RMSNorm + top-k routing + (gate, up) row pairs of the selected experts
-    OP_EDOWN = 9,   // MoE: top-k routing + down rows of the selected experts, weighted sum, residual add
+    OP_EDOWN = 9,   // MoE: per output row, the selected experts' outputs weighted in ascending order, residual add
+    OP_EPART = 10,  // MoE: down rows of the CU's share of (selected expert, row) pairs -> unweighted outputs
 };
+
+// MoE expert down projection: the (selected slot, output row) pairs of a layer,
+// n_slots x d of them in slot-major order, are dealt to the CUs in contiguous
+// ranges, so a CU stages the SwiGLU outputs of at most a few slots; the row
+// owners then combine the slots' outputs (OP_EDOWN instructions of at most
+// kMaxEredRows rows, whose staged outputs of every slot fit the LDS).
+constexpr uint32_t kMaxEredRows = 16;
+__host__ __device__ inline void moe_part_range(uint32_t n_slots, uint32_t d, int n_cu, int c, uint32_t* t0,
+                                               uint32_t* t1) {
+    const uint64_t T = (uint64_t)n_slots * d;
+    *t0 = (uint32_t)(T * (uint64_t)c / (uint64_t)n_cu);
+    *t1 = (uint32_t)(T * (uint64_t)(c + 1) / (uint64_t)n_cu);
+}
 
 // MoE limits: the selected-expert set of a layer is one 64-bit mask.
 constexpr int kMaxExperts = 64;
@@ -219,6 +233,7 @@ struct Params {
     uint64_t* head_part;  // [n_head_slots][B][2] argmax partials (value, index)
     uint64_t* route;      // MoE [B][E] router logits
     uint64_t* eact;       // MoE [n_shared + E][B][Fe] SwiGLU outputs of the experts
+    uint64_t* epart;      // MoE [selected slot][B][d] unweighted down outputs of the selected experts
     const uint16_t* const* eptr;  // MoE [L][3 (gate, up, down)][n_shared + E] expert matrices (shared first)
     uint32_t* attn_ticket;  // [L][B][Hkv] * kCtrStride, reset by the merger
     uint32_t* head_ticket;  // kCtrStride, reset by the reducer

@@ -215,8 +215,9 @@ def test_moe_schedule_verifies(cfg, batch, cus):
     st, info = mk.mk_plan_inspect(mk.model_config(cfg), rt(batch, 300), cus)
     assert st == mk.MK_OK
     assert info["verify"] == 0
-    # per layer: QKV, ATTN, O, ROUTE, EGU, EDOWN; then the LM head
-    assert info["phases"] == 6 * cfg.n_layers + 1
+    # per layer: QKV, ATTN, O, ROUTE, EGU, EPART (one expert-down share per CU),
+    # EDOWN (the weighted combine); then the LM head
+    assert info["phases"] == 7 * cfg.n_layers + 1
     assert info["weight_bytes"] == cfg.weight_bytes()
     assert info["ring_chunks"] >= MIN_RING
     assert info["gemv_kind"] == mk.MK_GEMV_VALU
