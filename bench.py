@@ -267,6 +267,8 @@ def main() -> int:
     ap.add_argument("--config", default="1b", choices=sorted(WORKLOADS))
     ap.add_argument("--gemv", default="auto", choices=["auto", "valu", "mfma"],
                     help="GEMV arithmetic of the persistent kernel (auto: matrix cores from batch 4)")
+    ap.add_argument("--down-split", default="auto", choices=["auto", "on", "off"],
+                    help="dense down projection split by columns (automatic: batch 4 and 8)")
     ap.add_argument("--no-graph", action="store_true", help="skip the one-kernel-per-op comparison")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-steps", type=int, default=24)
@@ -315,7 +317,8 @@ def main() -> int:
 
     def run_path(mode: int, label: str):
         dec = mk.Decoder(cfg, w, max_batch=B, max_seq=max_seq, mode=mode, device="cuda:0", device_weights=dw,
-                         gemv_kind=gemv if mode == mk.MK_MODE_MEGAKERNEL else mk.MK_GEMV_AUTO)
+                         gemv_kind=gemv if mode == mk.MK_MODE_MEGAKERNEL else mk.MK_GEMV_AUTO,
+                         down_split={"auto": 0, "on": 1, "off": -1}[args.down_split])
         st = dec.stream
         tok = torch.zeros(B, dtype=torch.int32, device=dev)
         logits = torch.empty((B, cfg.vocab), dtype=torch.float32, device=dev)

@@ -130,6 +130,11 @@ typedef struct {
     uint32_t spin_timeout_ms; /* watchdog of every device spin-wait; 0 = 2000 ms */
     int32_t trace;            /* 1: record a per-instruction timeline (mk_read_trace) */
     int32_t attn_splits;      /* KV splits per (sequence, KV head); 0 = automatic */
+    int32_t down_split;       /* dense down projection split by columns (per-part partial
+                                 outputs from a transposed copy of Wdown that the workspace
+                                 holds, then a per-row sum): 0 = automatic (batch 4 and 8,
+                                 VALU GEMV, hidden <= 2048), 1 = on where supported, -1 = off.
+                                 mk_create_static never splits. */
 } mk_runtime_config;
 
 typedef struct mk_handle mk_handle;

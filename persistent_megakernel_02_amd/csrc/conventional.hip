@@ -248,6 +248,91 @@ __global__ void __launch_bounds__(kConvThreads) k_proj(Params P, StepArgs A, int
     }
 }
 
+// Split down projection, one part per workgroup (the persistent kernel's OP_DPART
+// with the transposed Wdown rows read from HBM instead of the ring).
+struct DpartGlobalRows {
+    const uint16_t* w;  // the part's first transposed row
+    uint32_t d, o;      // row length, this lane's first output
+    bool on;
+    __device__ __forceinline__ bool get(uint32_t f, uint4 (&q)[kDpartRowsPerGet]) {
+#pragma unroll
+        for (int u = 0; u < kDpartRowsPerGet; ++u)
+            q[u] = on ? *(const uint4*)(w + (size_t)(f + (uint32_t)u) * d + o) : make_uint4(0u, 0u, 0u, 0u);
+        return true;
+    }
+};
+
+template <int B>
+__global__ void __launch_bounds__(kConvThreads) k_dpart(Params P, StepArgs A, int layer) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    float* xs = (float*)lds;
+    const int wave = threadIdx.x >> 6, lane = lane_id();
+    Spin spin(&P, nullptr);
+    const DevLayer Lw = P.layers[layer];
+    const uint32_t j = blockIdx.x, d = (uint32_t)P.d, f0 = j * kDownPart;
+    const uint32_t tag_a = phase_tag(A.tag0, layer, 3);
+    float ss[1] = {0.f};
+    const StageSeg sg[1] = {{P.act + f0, xs, nullptr, kDownPart, (uint32_t)B, (uint32_t)P.F, kDownPart, tag_a, 0u}};
+    if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kConvWaves, spin, ss)) return;
+    __syncthreads();
+    const uint32_t o = 8u * (uint32_t)(wave * 64 + lane);
+    DpartGlobalRows rows{Lw.w_down_t + (size_t)f0 * d, d, o, o < d};
+    float acc[B][8];
+    dpart_acc<B>(rows, xs, kDownPart, acc);
+    float* out = xs + B * kDownPart;  // [B][d], stored with consecutive lanes on consecutive words
+    if (rows.on) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            float* q = out + (size_t)b * d + o;
+            *(float4*)q = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+            *(float4*)(q + 4) = make_float4(acc[b][4], acc[b][5], acc[b][6], acc[b][7]);
+        }
+    }
+    __syncthreads();
+    dpart_store<B>(P, out, j, tag_a, wave, kConvWaves);
+}
+
+// Split down projection, the row sums: rows [blockIdx.x rpb, + rpb).
+template <int B>
+__global__ void __launch_bounds__(kConvThreads) k_dred(Params P, StepArgs A, int layer, uint32_t rpb) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    float* xs = (float*)lds;
+    const int wave = threadIdx.x >> 6;
+    Spin spin(&P, nullptr);
+    const uint32_t d = (uint32_t)P.d, begin = blockIdx.x * rpb, cnt = min(rpb, d - begin);
+    const uint32_t np = (uint32_t)P.F / kDownPart;
+    float* hres = xs;
+    float* part = hres + B * cnt;
+    if (!stage_grid<kStagePassWordsWide>(P.h + begin, (uint32_t)B, phase_tag(A.tag0, layer, 2), P.dpart + begin,
+                                         np * (uint32_t)B, phase_tag(A.tag0, layer, 3), d, cnt, xs, wave, kConvWaves,
+                                         spin))
+        return;
+    __syncthreads();
+    dred_out<B>(P, part, hres, begin, cnt, np, phase_tag(A.tag0, layer, 4), wave, kConvWaves);
+}
+
+// bf16 transpose through LDS: dst [cols][rows] = src [rows][cols]^T (the split
+// down projection's copy of Wdown, made once at create).
+__global__ void __launch_bounds__(256) k_transpose_bf16(uint16_t* dst, const uint16_t* src, int rows, int cols) {
+    __shared__ uint16_t t[64][65];
+    const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+    for (int i = threadIdx.y; i < 64; i += blockDim.y) {
+        const int r = r0 + i, c = c0 + (int)threadIdx.x;
+        if (r < rows && c < cols) t[i][threadIdx.x] = src[(size_t)r * cols + c];
+    }
+    __syncthreads();
+    for (int i = threadIdx.y; i < 64; i += blockDim.y) {
+        const int c = c0 + i, r = r0 + (int)threadIdx.x;
+        if (c < cols && r < rows) dst[(size_t)c * rows + r] = t[threadIdx.x][i];
+    }
+}
+
+hipError_t transpose_bf16(uint16_t* dst, const uint16_t* src, int rows, int cols, hipStream_t stream) {
+    const dim3 blk(64, 4), grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+    hipLaunchKernelGGL(k_transpose_bf16, grid, blk, 0, stream, dst, src, rows, cols);
+    return hipGetLastError();
+}
+
 template <int HD>
 __global__ void __launch_bounds__(kConvThreads) k_attn(Params P, StepArgs A, int layer) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -273,14 +358,15 @@ __global__ void __launch_bounds__(kConvThreads) k_attn(Params P, StepArgs A, int
 // ------------------------------------------------------------------------------------------------
 // host-side launch of one step (the host captures this sequence into a graph)
 // ------------------------------------------------------------------------------------------------
-int conventional_kernels_per_step(const Params& P) { return P.L * kPhasesPerLayer + 1; }
+int conventional_kernels_per_step(const Params& P) { return P.L * (kPhasesPerLayer + (P.down_split ? 1 : 0)) + 1; }
 
 int conventional_head_blocks(const Params& P) { return (int)((P.V + kHeadRowsPerBlock - 1) / kHeadRowsPerBlock); }
 
 template <int B, int HD>
 static hipError_t prepare_t(size_t lds) {
     const void* fns[] = {(const void*)k_norm_gemv<B, OP_QKV>, (const void*)k_norm_gemv<B, OP_GATEUP>,
-                         (const void*)k_norm_gemv<B, OP_HEAD>, (const void*)k_proj<B>, (const void*)k_attn<HD>};
+                         (const void*)k_norm_gemv<B, OP_HEAD>, (const void*)k_proj<B>, (const void*)k_attn<HD>,
+                         (const void*)k_dpart<B>, (const void*)k_dred<B>};
     for (const void* f : fns) {
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -303,7 +389,13 @@ static hipError_t launch_step_t(const Params& P, const StepArgs& A, hipStream_t 
         hipLaunchKernelGGL(k_attn<HD>, dim3(items), blk, lds, st, P, A, l);
         hipLaunchKernelGGL(k_proj<B>, dim3(d_blocks), blk, lds, st, P, A, l, 0, d_rpb);
         hipLaunchKernelGGL((k_norm_gemv<B, OP_GATEUP>), dim3(f_blocks), blk, lds, st, P, A, l, f_rpb);
-        hipLaunchKernelGGL(k_proj<B>, dim3(d_blocks), blk, lds, st, P, A, l, 1, d_rpb);
+        if (P.down_split) {
+            const uint32_t rr = dred_rows((uint32_t)P.d, (uint32_t)P.F);
+            hipLaunchKernelGGL(k_dpart<B>, dim3((unsigned)(P.F / (int)kDownPart)), blk, lds, st, P, A, l);
+            hipLaunchKernelGGL(k_dred<B>, dim3((unsigned)((P.d + rr - 1) / rr)), blk, lds, st, P, A, l, rr);
+        } else {
+            hipLaunchKernelGGL(k_proj<B>, dim3(d_blocks), blk, lds, st, P, A, l, 1, d_rpb);
+        }
     }
     hipLaunchKernelGGL((k_norm_gemv<B, OP_HEAD>), dim3(conventional_head_blocks(P)), blk, lds, st, P, A, P.L,
                        kHeadRowsPerBlock);

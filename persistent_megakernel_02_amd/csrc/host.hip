@@ -34,6 +34,7 @@ bool megakernel_supports(int B, int hd);
 size_t megakernel_lds_bytes(const Params& P);
 hipError_t launch_conventional(const Params& P, const StepArgs& A, hipStream_t stream);
 hipError_t prepare_conventional(const Params& P);
+hipError_t transpose_bf16(uint16_t* dst, const uint16_t* src, int rows, int cols, hipStream_t stream);
 int conventional_kernels_per_step(const Params& P);
 int conventional_head_blocks(const Params& P);
 }  // namespace mk
@@ -85,6 +86,19 @@ bool use_mfma(const mk_model_config* c, const mk_runtime_config* rt) {
     return ring_chunks_for((x_floats_kind(c, rt, 1, true) * 4 + 15) & ~(size_t)15) >= kMinRingChunks;
 }
 
+// The dense down projection split by columns (OP_DPART per part of kDownPart
+// SwiGLU outputs, then OP_DRED per output row): each CU stages only its parts'
+// inputs, not the whole B x F activation, at the cost of a transposed copy of
+// Wdown in the workspace and a second, smaller all-to-all (the parts' partials).
+// Automatic from batch 4, where staging B x F tagged words per CU dominates DOWN.
+bool down_split_on(const mk_model_config* c, const mk_runtime_config* rt) {
+    if (c->n_experts || rt->down_split < 0) return false;
+    if (c->hidden > kDownSplitMaxHidden || c->ffn % (int)kDownPart || use_mfma(c, rt)) return false;
+    return rt->down_split > 0 || rt->max_batch >= 4;
+}
+
+uint32_t dred_rows_for(const mk_model_config* c) { return dred_rows((uint32_t)c->hidden, (uint32_t)c->ffn); }
+
 // LDS floats of activations one instruction stages (x rows, residual rows of
 // O / DOWN, or an attention item's area).
 size_t x_floats_kind(const mk_model_config* c, const mk_runtime_config* rt, int nsplit, bool mfma, int nnew) {
@@ -117,6 +131,14 @@ size_t x_floats_kind(const mk_model_config* c, const mk_runtime_config* rt, int 
         n = std::max(n, B * (dw + E) + (xsl > 1 ? slots * 2 * kMaxEguSlicedRows * B : 0));
         n = std::max(n, B * ((size_t)c->expert_ffn + E));
         n = std::max(n, B * E + (slots + 1) * B + B * kMaxEredRows + slots * B * kMaxEredRows);
+        return std::max(n, attn_lds_floats((int)G, (int)hd, nsplit, nnew));
+    }
+    if (down_split_on(c, rt)) {
+        // DPART: the inputs of its parts and one part's outputs; DRED: the residual
+        // rows and every part's partials of its rows
+        const size_t np = (size_t)c->ffn / kDownPart, rows = dred_rows_for(c);
+        n = std::max(n, B * (kMaxDpartParts * kDownPart + (size_t)c->hidden));
+        n = std::max(n, B * rows * (np + 1));
         return std::max(n, attn_lds_floats((int)G, (int)hd, nsplit, nnew));
     }
     // DOWN: one column slice of the input, the residual rows and the partial sums
@@ -186,8 +208,13 @@ uint32_t max_wave_span(const mk_model_config* c, const mk_runtime_config* rt) {
         gemv((uint32_t)c->expert_ffn * 2u, false);                  // expert DOWN
     } else {
         gemv(d2, true);                                             // (gate, up) pairs
-        const int ns = std::max(1, down_slices_for(B, c->ffn));
-        gemv((uint32_t)(c->ffn / ns) * 2u, false);                  // DOWN column slice
+        if (down_split_on(c, rt)) {
+            // a DPART wave waits for kDpartRowsPerGet transposed rows at a time
+            span = std::max(span, ((uint32_t)kDpartRowsPerGet * (uint32_t)c->hidden * 2u + kChunk - 1u) / kChunk + 1u);
+        } else {
+            const int ns = std::max(1, down_slices_for(B, c->ffn));
+            gemv((uint32_t)(c->ffn / ns) * 2u, false);              // DOWN column slice
+        }
     }
     return span;
 }
@@ -309,6 +336,12 @@ Plan build_plan(const mk_model_config* c, const mk_runtime_config* rt, int n_cu)
             for (int cu = 0; cu < n_cu; ++cu) q[cu].push_back(mk_instr(OP_EPART, l, (uint32_t)cu, 1));
             ++pl.phases;
             gemv_phase(OP_EDOWN, l, (uint32_t)c->hidden, kMaxEredRows);
+        } else if (down_split_on(c, rt)) {
+            // the F / kDownPart parts dealt like rows (a CU's parts are its GATEUP
+            // f-range when F / n_cu is a multiple of kDownPart), then the row sums
+            gemv_phase(OP_GATEUP, l, (uint32_t)c->ffn, all);
+            gemv_phase(OP_DPART, l, (uint32_t)c->ffn / kDownPart, kMaxDpartParts);
+            gemv_phase(OP_DRED, l, (uint32_t)c->hidden, dred_rows_for(c));
         } else {
             gemv_phase(OP_GATEUP, l, (uint32_t)c->ffn, all);
             gemv_phase(OP_DOWN, l, (uint32_t)c->hidden, kMaxResidRows);
@@ -332,16 +365,18 @@ Plan build_plan(const mk_model_config* c, const mk_runtime_config* rt, int n_cu)
 int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Plan& pl) {
     const int L = c->n_layers, B = rt->max_batch;
     const uint32_t qkv_rows = (uint32_t)((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim);
-    // sub-phases per layer: QKV, ATTN, O, ROUTE (MoE), GATEUP / EGU, EPART (MoE), DOWN / EDOWN
+    // sub-phases per layer: QKV, ATTN, O, ROUTE (MoE), GATEUP / EGU, EPART (MoE) / DPART (split DOWN),
+    // DOWN / EDOWN / DRED
     constexpr int kSub = 7;
     const bool moe = c->n_experts != 0;
+    const bool split = down_split_on(c, rt);
     const bool sliced = x_slices_for(B, c->hidden, c->n_q_heads * c->head_dim, moe) > 1;
     const int nphase = L * kSub + 1;
     std::vector<std::vector<uint8_t>> seen(nphase);
     auto phase_of = [&](const Instr& in) -> int {
         if (in.op == OP_HEAD) return L * kSub;
         const int k = in.op == OP_QKV ? 0 : in.op == OP_ATTN ? 1 : in.op == OP_O ? 2 : in.op == OP_ROUTE ? 3
-                    : (in.op == OP_GATEUP || in.op == OP_EGU) ? 4 : in.op == OP_EPART ? 5 : 6;
+                    : (in.op == OP_GATEUP || in.op == OP_EGU) ? 4 : (in.op == OP_EPART || in.op == OP_DPART) ? 5 : 6;
         return in.layer * kSub + k;
     };
     auto extent = [&](int ph) -> uint32_t {
@@ -352,7 +387,7 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
             case 2: return (uint32_t)c->hidden;
             case 3: return moe ? (uint32_t)c->n_experts : 0u;
             case 4: return moe ? (uint32_t)c->expert_ffn : (uint32_t)c->ffn;
-            case 5: return moe ? (uint32_t)pl.n_cu : 0u;  // one expert-down share per CU
+            case 5: return moe ? (uint32_t)pl.n_cu : split ? (uint32_t)c->ffn / kDownPart : 0u;  // shares, parts
             default: return (uint32_t)c->hidden;
         }
     };
@@ -363,9 +398,12 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
         int last = -1;
         for (uint32_t i = pl.qoff[cu]; i < pl.qoff[cu + 1]; ++i) {
             const Instr& in = pl.instrs[i];
-            if (in.op < OP_QKV || in.op > OP_EPART) return 1;
+            if (in.op < OP_QKV || in.op > OP_DRED) return 1;
             const bool moe_op = in.op == OP_ROUTE || in.op == OP_EGU || in.op == OP_EDOWN || in.op == OP_EPART;
             if (moe_op != moe && in.op != OP_QKV && in.op != OP_ATTN && in.op != OP_O && in.op != OP_HEAD) return 1;
+            if ((in.op == OP_DPART || in.op == OP_DRED) != split && (in.op == OP_DPART || in.op == OP_DRED ||
+                                                                     in.op == OP_DOWN))
+                return 1;
             if (in.op != OP_HEAD && in.layer >= L) return 2;
             const int ph = phase_of(in);
             if (ph < last) return 3;  // queue not in phase order
@@ -374,6 +412,8 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
             if (in.count == 0 || in.begin + in.count > ext || in.begin + in.count < in.begin) return 5;
             if ((in.op == OP_O || in.op == OP_DOWN) && in.count > kMaxResidRows) return 4;
             if (in.op == OP_EDOWN && in.count > kMaxEredRows) return 4;
+            if (in.op == OP_DPART && in.count > kMaxDpartParts) return 4;
+            if (in.op == OP_DRED && in.count > dred_rows_for(c)) return 4;
             if (in.op == OP_EPART && (in.begin != (uint32_t)cu || in.count != 1)) return 4;
             if (sliced && (in.op == OP_QKV || in.op == OP_ROUTE) && in.count > kMaxResidRows) return 4;
             if (sliced && in.op == OP_EGU && in.count > kMaxEguSlicedRows) return 4;
@@ -395,7 +435,7 @@ int verify_plan(const mk_model_config* c, const mk_runtime_config* rt, const Pla
 
 struct Layout {
     size_t state, tickets, instrs, qoff, layers, rope, h, qkv, attn, act, attn_part, head_part, logits_scr, tok_scr,
-        trace, trace_bytes, route, eact, eptr, cuts, epart, total;
+        trace, trace_bytes, route, eact, eptr, cuts, epart, dpart, wdt, total;
     size_t head_slots;  // argmax partial slots (per sequence)
 };
 
@@ -414,13 +454,18 @@ void plan_counts(const mk_model_config* c, const mk_runtime_config* rt, int n, i
     const size_t qkv = sliced ? cut(qkv_rows, kMaxResidRows) : 1;  // sliced inputs: cut instructions
     const size_t route = !moe ? 0 : sliced ? cut((size_t)c->n_experts, kMaxResidRows) : 1;
     const size_t ffn = sliced ? cut((size_t)c->expert_ffn, kMaxEguSlicedRows) : 1;  // GATEUP / EGU
-    // MoE: one expert-down share per CU, and combine instructions of kMaxEredRows rows
-    const size_t epart = moe ? 1 : 0, down = moe ? cut((size_t)c->hidden, kMaxEredRows) : od;
+    // MoE: one expert-down share per CU, and combine instructions of kMaxEredRows rows;
+    // split DOWN: part instructions, then row-sum instructions
+    const bool split = down_split_on(c, rt);
+    const size_t epart = moe ? 1 : split ? cut((size_t)c->ffn / kDownPart, kMaxDpartParts) : 0;
+    const size_t down = moe ? cut((size_t)c->hidden, kMaxEredRows) : split ? cut((size_t)c->hidden, dred_rows_for(c)) : od;
     *per_cu = (size_t)c->n_layers * (qkv + route + ffn + epart + od + down + (items + n - 1) / n) + 1;
     *total = (size_t)c->n_layers * ((qkv + route + ffn + epart + od + down) * (size_t)n + items) + (size_t)n;
 }
 
-Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, int nsplit) {
+// with_wdt: also the transposed down matrices (the decode layout; a multi-position
+// plan uses those of its decode handle).
+Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, int nsplit, bool with_wdt = true) {
     Layout lo{};
     const size_t B = (size_t)rt->max_batch, d = c->hidden, hd = c->head_dim;
     const size_t qkv_rows = (size_t)(c->n_q_heads + 2 * c->n_kv_heads) * hd;
@@ -449,6 +494,9 @@ Layout layout(const mk_model_config* c, const mk_runtime_config* rt, int n_cu, i
     // selected slots of a layer at most: the shared experts and B x top_k routed ones
     const size_t slots = c->n_experts ? (size_t)c->n_shared_experts + std::min((size_t)c->n_experts, B * c->top_k) : 0;
     lo.epart = take(slots * B * d * 8);
+    const bool split = down_split_on(c, rt);
+    lo.dpart = take(split ? (size_t)c->ffn / kDownPart * B * d * 8 : 0);
+    lo.wdt = take(split && with_wdt ? (size_t)c->n_layers * c->ffn * d * 2 : 0);
     lo.eptr = take((size_t)c->n_layers * 3 * nx * 8);
     lo.attn_part = take(B * c->n_kv_heads * nsplit * G * (hd + 2) * 8);
     // argmax partial slots: one LM-head instruction per CU (persistent), or the
@@ -489,8 +537,9 @@ int resolve_cus(const mk_runtime_config* rt) { return rt->num_cus > 0 ? rt->num_
 // The multi-position plan of a persistent decode handle: kChunkRows rows of one
 // sequence per launch (prompt chunks, draft verification), VALU GEMVs, one
 // attention split per item.
-mk_runtime_config chunk_rt(const mk_runtime_config* rt) {
+mk_runtime_config chunk_rt(const mk_model_config* c, const mk_runtime_config* rt) {
     mk_runtime_config r = *rt;
+    r.down_split = down_split_on(c, rt) ? 1 : -1;  // the decode handle's transposed Wdown, if any
     r.max_batch = kChunkRows;
     r.mode = MK_MODE_MEGAKERNEL;
     r.gemv_kind = 1;
@@ -502,7 +551,7 @@ mk_runtime_config chunk_rt(const mk_runtime_config* rt) {
 // Whether a handle of this configuration carries the multi-position plan.
 bool chunk_supported(const mk_model_config* c, const mk_runtime_config* rt) {
     if (rt->mode != MK_MODE_MEGAKERNEL) return false;
-    const mk_runtime_config r = chunk_rt(rt);
+    const mk_runtime_config r = chunk_rt(c, rt);
     if (validate(c, &r, nullptr) != MK_OK) return false;
     const uint32_t ring = ring_chunks_for(x_bytes_for(c, &r, 1, kChunkRows));
     return ring >= kMinRingChunks && max_wave_span(c, &r) <= ring;
@@ -515,8 +564,8 @@ size_t handle_bytes(const mk_model_config* c, const mk_runtime_config* rt, int n
     size_t total = (m.total + 255) & ~(size_t)255;
     Layout k{};
     if (chunk_supported(c, rt)) {
-        const mk_runtime_config r = chunk_rt(rt);
-        k = layout(c, &r, n, 1);
+        const mk_runtime_config r = chunk_rt(c, rt);
+        k = layout(c, &r, n, 1, false);
         total += k.total;
     }
     if (main_lo) *main_lo = m;
@@ -639,11 +688,11 @@ mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* r
                               : 3 * (int64_t)cfg->ffn * d;
     const int64_t per_layer = (cfg->n_q_heads + 2 * cfg->n_kv_heads) * hd * d + d * cfg->n_q_heads * hd + ffn_w + 2 * d;
     const size_t xb = x_bytes_for(cfg, rt, pl.nsplit);
-    int64_t vals[13] = {num_cus, (int64_t)pl.instrs.size(), (int64_t)ring_chunks_for(xb), (int64_t)pl.max_per_cu,
+    int64_t vals[14] = {num_cus, (int64_t)pl.instrs.size(), (int64_t)ring_chunks_for(xb), (int64_t)pl.max_per_cu,
                         2 * (cfg->n_layers * per_layer + (int64_t)cfg->vocab * d + d), verify_plan(cfg, rt, pl),
                         pl.nsplit, pl.phases, (int64_t)xb, (int64_t)pl.n_head, use_mfma(cfg, rt) ? 2 : 1, pl.hsplit,
-                        (int64_t)max_wave_span(cfg, rt)};
-    for (int i = 0; i < cap && i < 13; ++i) out[i] = vals[i];
+                        (int64_t)max_wave_span(cfg, rt), down_split_on(cfg, rt) ? 1 : 0};
+    for (int i = 0; i < cap && i < 14; ++i) out[i] = vals[i];
     return MK_OK;
 }
 
@@ -735,6 +784,7 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
     P.top_k = cfg->top_k;
     P.n_shared = cfg->n_experts ? cfg->n_shared_experts : 0;
     P.Fe = cfg->expert_ffn;
+    P.down_split = down_split_on(cfg, rt) ? 1 : 0;
     P.V = cfg->vocab;
     P.B = rt->max_batch;
     P.S = rt->max_seq;
@@ -767,6 +817,7 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
     P.eact = (uint64_t*)(ws + lo.eact);
     P.eptr = (const uint16_t* const*)(ws + lo.eptr);
     P.epart = (uint64_t*)(ws + lo.epart);
+    P.dpart = (uint64_t*)(ws + lo.dpart);
     P.attn_ticket = (uint32_t*)(ws + lo.tickets);
     P.head_ticket = P.attn_ticket + (size_t)cfg->n_layers * rt->max_batch * cfg->n_kv_heads * kCtrStride;
     P.state = (DevState*)(ws + lo.state);
@@ -827,7 +878,7 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
     // ---- the multi-position plan: same weights, KV cache, context lengths and error
     // state as the decode plan; its own schedule, activations and tickets
     if (h->chunk_ok) {
-        const mk_runtime_config r8 = chunk_rt(rt);
+        const mk_runtime_config r8 = chunk_rt(cfg, rt);
         h->cplan = build_plan(cfg, &r8, n_cu);
         Params& C = h->cP;
         C = P;
@@ -850,6 +901,8 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
         C.route = (uint64_t*)(cb + cl.route);
         C.eact = (uint64_t*)(cb + cl.eact);
         C.epart = (uint64_t*)(cb + cl.epart);
+        C.dpart = (uint64_t*)(cb + cl.dpart);
+        C.down_split = down_split_on(cfg, &r8) ? 1 : 0;
         C.eptr = (const uint16_t* const*)(cb + cl.eptr);
         C.attn_ticket = (uint32_t*)(cb + cl.tickets);
         C.head_ticket = C.attn_ticket + (size_t)cfg->n_layers * kChunkRows * cfg->n_kv_heads * kCtrStride;
@@ -878,7 +931,9 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
         dl[l] = DevLayer{(const uint16_t*)Lw.attn_norm, (const uint16_t*)Lw.wq,     (const uint16_t*)Lw.wk,
                          (const uint16_t*)Lw.wv,        (const uint16_t*)Lw.wo,     (const uint16_t*)Lw.mlp_norm,
                          (const uint16_t*)Lw.w_gate,    (const uint16_t*)Lw.w_up,   (const uint16_t*)Lw.w_down,
-                         (const uint16_t*)Lw.router};
+                         (const uint16_t*)Lw.router,    nullptr};
+        if (P.down_split)
+            dl[l].w_down_t = (const uint16_t*)(ws + lo.wdt + (size_t)l * cfg->ffn * cfg->hidden * 2);
     }
     // MoE expert table [L][gate, up, down][shared (if any), experts 0..E-1]
     const int nx = cfg->n_experts ? cfg->n_shared_experts + cfg->n_experts : 0;
@@ -921,6 +976,9 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
         cp(h->coff + cl.rope, rope.data(), rope.size() * 4);
         cp(h->coff + cl.eptr, ep.data(), ep.size() * sizeof(void*));
     }
+    // the split down projection's transposed Wdown, [F][d] per layer
+    for (int l = 0; l < cfg->n_layers && P.down_split && e == hipSuccess; ++l)
+        e = transpose_bf16((uint16_t*)dl[l].w_down_t, (const uint16_t*)dl[l].w_down, cfg->hidden, cfg->ffn, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(d_kv, 0, need_kv, h->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
     if (e != hipSuccess) {
@@ -944,8 +1002,9 @@ mk_status mk_create_static(const mk_model_config* cfg, const mk_weights* w, cons
                            size_t kv_bytes, void* stream, mk_handle** out) {
     if (!out || !rt_in || !cfg) return MK_E_INVALID;
     *out = nullptr;
-    const mk_runtime_config rt = resolve_mode(rt_in);
+    mk_runtime_config rt = resolve_mode(rt_in);
     if (rt.mode != MK_MODE_MEGAKERNEL) return MK_E_UNSUPPORTED;
+    rt.down_split = -1;  // the transposed Wdown would not fit the array
     mk_status s = validate(cfg, &rt, nullptr);
     if (s != MK_OK) return s;
     // the workspace this handle lays out, against the array (host-only arithmetic)
@@ -1244,12 +1303,12 @@ mk_status mk_set_cuts(mk_handle* h, const int32_t* h_layers, int32_t n) {
         return MK_OK;
     }
     // launch j runs the instructions of phases [b_j, b_{j+1}): phase = layer * 7 +
-    // sub-phase (QKV, ATTN, O, ROUTE, GATEUP / EGU, EPART, DOWN / EDOWN), the LM head L * 7
+    // sub-phase (QKV, ATTN, O, ROUTE, GATEUP / EGU, EPART / DPART, DOWN / EDOWN / DRED), the LM head L * 7
     constexpr int kSub = 7;
     auto phase_of = [&](const Instr& in) -> int {
         if (in.op == OP_HEAD) return L * kSub;
         const int k = in.op == OP_QKV ? 0 : in.op == OP_ATTN ? 1 : in.op == OP_O ? 2 : in.op == OP_ROUTE ? 3
-                    : (in.op == OP_GATEUP || in.op == OP_EGU) ? 4 : in.op == OP_EPART ? 5 : 6;
+                    : (in.op == OP_GATEUP || in.op == OP_EGU) ? 4 : (in.op == OP_EPART || in.op == OP_DPART) ? 5 : 6;
         return in.layer * kSub + k;
     };
     std::vector<int> bnd(1, 0);

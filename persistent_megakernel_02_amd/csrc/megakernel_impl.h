@@ -101,6 +101,7 @@ __device__ __forceinline__ uint32_t instr_bytes(const Params& P, const Instr& in
         case OP_O: return align_chunk(in.count * (uint32_t)(P.Hq * HD) * 2u);
         case OP_GATEUP: return align_chunk(2u * in.count * (uint32_t)P.d * 2u);
         case OP_DOWN: return align_chunk(in.count * (uint32_t)P.F * 2u);
+        case OP_DPART: return in.count * kDownPart * (uint32_t)P.d * 2u;  // whole 16 KB multiples
         case OP_ATTN: {
             const AttnItem it = attn_item_of(P, in.begin);
             const SplitRange R = split_range<HD>(ctx_of(ctx, it.b), it.s, P.nsplit);
@@ -305,6 +306,9 @@ __device__ __forceinline__ bool setup_stream(const Params& P, const Instr& in, c
             S.p0 = (const char*)uniform_p(Lw.router) + (size_t)in.begin * rb;
             if (P.x_slices > 1) return slice_stream(S, in.count, rb, (uint32_t)P.x_slices);
             break;
+        case OP_DPART:  // the parts' transposed Wdown rows: one contiguous run of whole chunks
+            S.p0 = (const char*)uniform_p(Lw.w_down_t) + (size_t)in.begin * kDownPart * P.d * 2u;
+            return true;
         case OP_GATEUP: {
             rb = (uint32_t)P.d * 2u;
             const uint32_t cpr = rb / kChunk;
@@ -1675,44 +1679,6 @@ __device__ __forceinline__ bool moe_epart(const Params& P, const StepArgs& A, Ct
 // Lane l of compute wave w takes column l % 16 of rows 4 w + l / 16 + 16 k: K
 // rows per lane per pass, any number of rows (the generic staging resolves at
 // most kMaxBatch rows per segment).
-static_assert(kMaxEredRows <= 16, "the combine stages at most 16 columns a row");
-template <int K>
-__device__ __forceinline__ bool stage_grid16(const uint64_t* src, uint32_t stride, uint32_t nrows, uint32_t cnt,
-                                             float* dst, uint32_t tag, int wave, Spin& spin) {
-    const uint32_t lane = (uint32_t)lane_id(), j = lane & 15u;
-    const uint32_t first = (uint32_t)wave * 4u + (lane >> 4);
-    for (uint32_t p0 = 0; p0 < nrows; p0 += 16u * (uint32_t)K) {
-        uint64_t v[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const uint32_t r = p0 + first + 16u * (uint32_t)k;
-            v[k] = (r < nrows && j < cnt) ? ld_tagged(src + (size_t)r * stride + j) : 0ull;
-        }
-        spin.start();
-        for (;;) {
-            bool ok = true;
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const uint32_t r = p0 + first + 16u * (uint32_t)k;
-                ok &= !(r < nrows && j < cnt) || tv_tag(v[k]) == tag;
-            }
-            if (__all(ok)) break;
-            if (!spin.again(tag, p0)) return false;
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const uint32_t r = p0 + first + 16u * (uint32_t)k;
-                if (r < nrows && j < cnt && tv_tag(v[k]) != tag) v[k] = ld_tagged(src + (size_t)r * stride + j);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const uint32_t r = p0 + first + 16u * (uint32_t)k;
-            if (r < nrows && j < cnt) dst[r * cnt + j] = tv_val(v[k]);
-        }
-    }
-    return true;
-}
-
 // OP_EDOWN: route again; for output rows [begin, begin + count) stage every
 // selected slot's outputs (epart) and add them in slot order (shared, then
 // ascending experts), weighted by the sequence's probability (1 for the shared
@@ -1758,7 +1724,9 @@ __device__ __forceinline__ bool moe_ered(const Params& P, const StepArgs& A, Ctl
     }
     if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
     // row a * B + b of the staged outputs is epart row a * B + b
-    if (!stage_grid16<8>(P.epart + in.begin, d, n * (uint32_t)B, cnt, part, tag_a, wave, spin)) return false;
+    if (!stage_grid<kStagePassWordsWide>(nullptr, 0u, 0u, P.epart + in.begin, n * (uint32_t)B, tag_a, d, cnt, part,
+                                         wave, kComputeWaves, spin))
+        return false;
     if (!barrier()) return false;  // the weights and the staged outputs are visible
     const uint32_t tag_out = phase_tag(A.tag0, layer, 4);
     for (uint32_t i = (uint32_t)(wave * 64 + lane); i < B * cnt; i += 64u * kComputeWaves) {
@@ -1770,6 +1738,96 @@ __device__ __forceinline__ bool moe_ered(const Params& P, const StepArgs& A, Ctl
         }
         st_tagged(P.h + (size_t)b * d + in.begin + j, hres[i] + acc, tag_out);
     }
+    return true;
+}
+
+// Transposed Wdown rows of an OP_DPART instruction in the ring: get(f, q) gives
+// this lane's 16 bytes of rows f .. f + kDpartRowsPerGet - 1 of the current part
+// (rows taken in order from f = 0; `cur` is the ring byte of the lane's piece of
+// the next row), once they have landed; the wave's mark moves to row f first.
+struct DpartRingRows {
+    const Params* P;
+    Ctl* ctl;
+    const char* ring;
+    uint32_t base, rb, ring_bytes, cur;  // stream byte of the part's first row, row bytes, ring bytes
+    int wave;
+    bool on;  // the lane has outputs (its piece lies inside the row)
+    uint32_t* lw;
+    __device__ __forceinline__ bool get(uint32_t f, uint4 (&q)[kDpartRowsPerGet]) {
+        const uint32_t s0 = base + f * rb;
+        set_consumed(ctl, wave, s0 / kChunk);
+        if (!wait_landed(*P, ctl, (s0 + (uint32_t)kDpartRowsPerGet * rb + kChunk - 1u) / kChunk, *lw)) return false;
+#pragma unroll
+        for (int u = 0; u < kDpartRowsPerGet; ++u) {
+            q[u] = on ? *(const uint4*)(ring + cur) : make_uint4(0u, 0u, 0u, 0u);
+            cur += rb;
+            if (cur >= ring_bytes) cur -= ring_bytes;
+        }
+        return true;
+    }
+};
+
+// OP_DPART (split down projection): parts [begin, begin + count) of F.  The
+// compute waves stage the parts' SwiGLU inputs (a CU's parts are normally its own
+// GATEUP outputs: no wait on other CUs), then every wave reads every transposed
+// row of the parts from the ring, lane l of wave w the outputs 8 (64 w + l) ..
+// + 7; each part's partial outputs of all rows go through LDS to dpart[part][b][row],
+// tagged (dpart_store).
+template <int B>
+__device__ __forceinline__ bool dpart_instr(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs,
+                                            int wave, const Instr& in, uint32_t S, Spin& spin, CwBarrier& barrier,
+                                            uint32_t& land_wait, uint32_t* tr) {
+    const int lane = lane_id();
+    const uint32_t d = (uint32_t)P.d, np = in.count, nf = np * kDownPart, f0 = in.begin * kDownPart;
+    const uint32_t tag_a = phase_tag(A.tag0, in.layer, 3);
+    float* out = xs + B * nf;  // [B][d] one part's outputs, after the staged inputs [B][nf]
+    {
+        float ss[1] = {0.f};
+        const StageSeg sg[1] = {{P.act + f0, xs, nullptr, nf, (uint32_t)B, (uint32_t)P.F, nf, tag_a, 0u}};
+        if (!stage_segs<kStagePassWordsWide, 1, 1>(sg, wave, kComputeWaves, spin, ss)) return false;
+    }
+    if (!barrier()) return false;
+    if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
+    const uint32_t rb = d * 2u, lo = 16u * (uint32_t)(wave * 64 + lane);
+    DpartRingRows rows{&P, ctl, ring, S, rb, P.ring_chunks * kChunk, 0u, wave, lo < rb, &land_wait};
+    for (uint32_t j = 0; j < np; ++j) {
+        rows.base = S + j * kDownPart * rb;
+        rows.cur = ring_addr(rows.base + lo, P.ring_chunks);
+        float acc[B][8];
+        if (!dpart_acc<B>(rows, xs + j * kDownPart, nf, acc)) return false;
+        release_region(ctl, wave, rows.base + kDownPart * rb);
+        if (j > 0 && !barrier()) return false;  // every wave has stored the previous part's outputs
+        if (rows.on) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                float* o = out + (size_t)b * d + lo / 2u;
+                *(float4*)o = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+                *(float4*)(o + 4) = make_float4(acc[b][4], acc[b][5], acc[b][6], acc[b][7]);
+            }
+        }
+        if (!barrier()) return false;
+        dpart_store<B>(P, out, in.begin + j, tag_a, wave, kComputeWaves);
+    }
+    return true;
+}
+
+// OP_DRED (split down projection): output rows [begin, begin + count): stage the
+// residual rows after O and every part's partials of the rows, then h = hres +
+// the partials added in part order.
+template <int B>
+__device__ __forceinline__ bool dred_instr(const Params& P, const StepArgs& A, float* xs, int wave, const Instr& in,
+                                           Spin& spin, CwBarrier& barrier, uint32_t* tr) {
+    const uint32_t d = (uint32_t)P.d, cnt = in.count, np = (uint32_t)P.F / kDownPart;
+    float* hres = xs;             // [B][cnt]
+    float* part = hres + B * cnt;  // [part][B][cnt]
+    // the residual rows after O, then every part's partials of the rows (one round trip)
+    if (!stage_grid<kStagePassWordsWide>(P.h + in.begin, (uint32_t)B, phase_tag(A.tag0, in.layer, 2),
+                                         P.dpart + in.begin, np * (uint32_t)B, phase_tag(A.tag0, in.layer, 3), d, cnt,
+                                         xs, wave, kComputeWaves, spin))
+        return false;
+    if (!barrier()) return false;
+    if (tr && lane_id() == 0) tr[2] = (uint32_t)now_ticks();
+    dred_out<B>(P, part, hres, in.begin, cnt, np, phase_tag(A.tag0, in.layer, 4), wave, kComputeWaves);
     return true;
 }
 
@@ -1847,6 +1905,12 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
                 break;
             case OP_EDOWN:
                 if constexpr (MOE) ok = moe_ered<B>(P, A, ctl, xs, wave, in, qi, spin, barrier, tr);
+                break;
+            case OP_DPART:
+                if constexpr (!MOE) ok = dpart_instr<B>(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr);
+                break;
+            case OP_DRED:
+                if constexpr (!MOE) ok = dred_instr<B>(P, A, xs, wave, in, spin, barrier, tr);
                 break;
             case OP_QKV:
             case OP_GATEUP:

@@ -546,6 +546,156 @@ __device__ __forceinline__ bool stage_segs(const StageSeg (&sg)[NS], int w, int 
     return true;
 }
 
+// Stages a grid of tagged words into dst [n0 + n1][cnt]: rows [0, n0) from src0
+// carrying tag0, then rows [0, n1) from src1 carrying tag1 (row stride `stride`
+// words in both, columns [0, cnt)), once each word carries its tag.  Element
+// e = r cnt + c is lane e mod 64 of wave (e / 64) mod nw's passes, K per lane per
+// pass and two passes in flight, like stage_segs, but for any number of rows
+// (StageSeg resolves at most kMaxBatch rows per segment).  The row of e is
+// e * ceil(2^32 / cnt) >> 32, exact for e < 2^32 / cnt.
+template <int K>
+__device__ __forceinline__ bool stage_grid(const uint64_t* src0, uint32_t n0, uint32_t tag0, const uint64_t* src1,
+                                           uint32_t n1, uint32_t tag1, uint32_t stride, uint32_t cnt, float* dst,
+                                           int w, int nw, Spin& spin) {
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint32_t step = 64u * (uint32_t)nw, per_pass = step * (uint32_t)K, total = (n0 + n1) * cnt;
+    const uint64_t magic = ((1ull << 32) + cnt - 1u) / cnt;
+    const uint32_t e1 = n0 * cnt;  // first element of the second block
+    auto word = [&](uint32_t e) -> const uint64_t* {
+        const uint32_t r = (uint32_t)(((uint64_t)e * magic) >> 32), c = e - r * cnt;
+        return r < n0 ? src0 + (size_t)r * stride + c : src1 + (size_t)(r - n0) * stride + c;
+    };
+    auto tag_of = [&](uint32_t e) { return e < e1 ? tag0 : tag1; };
+    auto issue = [&](uint32_t p0, uint64_t (&v)[K]) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const uint32_t e = p0 + 64u * (uint32_t)w + lane + step * (uint32_t)k;
+            v[k] = ld_tagged(word(e < total ? e : 0u));
+        }
+    };
+    auto finish = [&](uint32_t p0, uint64_t (&v)[K]) -> bool {
+        spin.start();
+        for (;;) {
+            bool ok = true;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const uint32_t e = p0 + 64u * (uint32_t)w + lane + step * (uint32_t)k;
+                ok &= e >= total || tv_tag(v[k]) == tag_of(e);
+            }
+            if (__all(ok)) break;
+            if (!spin.again(tag1, p0)) return false;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const uint32_t e = p0 + 64u * (uint32_t)w + lane + step * (uint32_t)k;
+                if (e < total && tv_tag(v[k]) != tag_of(e)) v[k] = ld_tagged(word(e));
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const uint32_t e = p0 + 64u * (uint32_t)w + lane + step * (uint32_t)k;
+            if (e < total) dst[e] = tv_val(v[k]);
+        }
+        return true;
+    };
+    if (total == 0) return true;
+    uint64_t va[K], vb[K];
+    issue(0u, va);
+    for (uint32_t p0 = 0;; p0 += 2u * per_pass) {
+        const bool more = p0 + per_pass < total;
+        if (more) issue(p0 + per_pass, vb);
+        if (!finish(p0, va)) return false;
+        if (!more) break;
+        const bool more2 = p0 + 2u * per_pass < total;
+        if (more2) issue(p0 + 2u * per_pass, va);
+        if (!finish(p0 + per_pass, vb)) return false;
+        if (!more2) break;
+    }
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
+    return true;
+}
+
+// Split down projection, one part: acc[b][e] = sum over the part's kDownPart
+// SwiGLU outputs f, in ascending order, of x[b][f] * WT[f][o + e] (fp32 fma), where
+// o = 8 (64 w + l) is this lane's first output row and WT the transposed Wdown
+// rows of the part.  `rows.get(f, q)` supplies this lane's 16 bytes of rows f ..
+// f + kDpartRowsPerGet - 1 (after any wait); x is [B][xstride] in LDS from the
+// part's first column.
+// Both the persistent kernel (rows from the LDS ring) and the one-kernel-per-op
+// path (rows from HBM) call it, so their partials are the same bits.
+template <int B, class Rows>
+__device__ __forceinline__ bool dpart_acc(Rows& rows, const float* x, uint32_t xstride, float (&acc)[B][8]) {
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
+    for (uint32_t f = 0; f < kDownPart; f += kDpartRowsPerGet) {
+        uint4 q[kDpartRowsPerGet];
+        if (!rows.get(f, q)) return false;
+        static_assert(kDpartRowsPerGet == 4, "one float4 of inputs per batch row and get");
+        float4 xv[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) xv[b] = *(const float4*)(x + (size_t)b * xstride + f);
+#pragma unroll
+        for (int u = 0; u < kDpartRowsPerGet; ++u) {
+            const float wv[8] = {bf_lo(q[u].x), bf_hi(q[u].x), bf_lo(q[u].y), bf_hi(q[u].y),
+                                 bf_lo(q[u].z), bf_hi(q[u].z), bf_lo(q[u].w), bf_hi(q[u].w)};
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const float a = u == 0 ? xv[b].x : u == 1 ? xv[b].y : u == 2 ? xv[b].z : xv[b].w;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[b][e] = fmaf(a, wv[e], acc[b][e]);
+            }
+        }
+    }
+    return true;
+}
+
+// Split down projection, rows [begin, begin + cnt): h[b][row] = hres + the sum of
+// the parts' partials, from the staged partials part[(j B + b) cnt + i] and
+// residual rows hres[b cnt + i] in LDS.  Output k = b cnt + i goes to wave k mod
+// nw: lane l adds the partials of parts l, l + 64, ... in ascending order, then
+// wave_total adds the 64 lane sums in its fixed tree (four outputs at a time).
+template <int B>
+__device__ __forceinline__ void dred_out(const Params& P, const float* part, const float* hres, uint32_t begin,
+                                         uint32_t cnt, uint32_t np, uint32_t tag, int w, int nw) {
+    const uint32_t lane = (uint32_t)lane_id(), total = (uint32_t)B * cnt, step = (uint32_t)nw;
+    for (uint32_t k0 = (uint32_t)w; k0 < total; k0 += 4u * step) {
+        float s[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t k = k0 + (uint32_t)t * step;
+            s[t] = 0.f;
+            if (k < total) {
+                const uint32_t b = k / cnt, i = k - b * cnt;
+                for (uint32_t p = lane; p < np; p += 64u) s[t] += part[(p * B + b) * cnt + i];
+            }
+        }
+        wave_total_n<4>(s);
+        if (lane == 0) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t k = k0 + (uint32_t)t * step;
+                if (k < total) {
+                    const uint32_t b = k / cnt, i = k - b * cnt;
+                    st_tagged(P.h + (size_t)b * P.d + begin + i, hres[k] + s[t], tag);
+                }
+            }
+        }
+    }
+}
+
+// Split down projection: one part's partial outputs out[b][row] (LDS, written by
+// dpart_acc's lanes 8 rows each) stored to dpart with consecutive lanes on
+// consecutive words (a lane's own 8 rows are 64 bytes apart from its
+// neighbour's: stored directly, every store would touch 64 cache lines).
+template <int B>
+__device__ __forceinline__ void dpart_store(const Params& P, const float* out, uint32_t part, uint32_t tag, int w,
+                                            int nw) {
+    const uint32_t n = (uint32_t)B * (uint32_t)P.d;
+    uint64_t* dst = P.dpart + (size_t)part * n;
+    for (uint32_t i = (uint32_t)(w * 64 + lane_id()); i < n; i += 64u * (uint32_t)nw) st_tagged(dst + i, out[i], tag);
+}
+
 // Same from a bf16 row that needs no wait (the token embedding of layer 0);
 // g == nullptr copies without a gain.
 __device__ __forceinline__ void stage_bf16(const uint16_t* __restrict__ src, uint32_t n, float* __restrict__ dst,

@@ -144,7 +144,28 @@ enum Op : uint16_t {
     OP_EGU = 8,     // MoE: RMSNorm + top-k routing + (gate, up) row pairs of the selected experts
     OP_EDOWN = 9,   // MoE: per output row, the selected experts' outputs weighted in ascending order, residual add
     OP_EPART = 10,  // MoE: down rows of the CU's share of (selected expert, row) pairs -> unweighted outputs
+    OP_DPART = 11,  // dense DOWN by columns: parts [begin, begin + count) of F -> partial outputs of every row
+    OP_DRED = 12,   // dense DOWN by columns: per output row the parts' partials in order, residual add
 };
+
+// The dense down projection split by columns (batch 4 and 8; opt-in below): F is
+// cut into parts of kDownPart SwiGLU outputs.  Part j's partial output of every
+// row i is the sum over its f of act[f] * Wdown[i][f], accumulated in ascending f
+// from a transposed copy of Wdown (rows of d, so a part streams contiguously); the
+// owner of a row adds the parts' partials in part order.  The transposed rows are
+// read whole by all four compute waves: lane l of wave w takes outputs
+// 8 (64 w + l) .. + 7, so d <= kDownSplitMaxHidden.
+constexpr uint32_t kDownPart = 32;
+constexpr int kDownSplitMaxHidden = 8 * 64 * 4;
+constexpr uint32_t kMaxDpartParts = 8;  // parts per OP_DPART instruction (their inputs staged at once)
+constexpr int kDpartRowsPerGet = 4;     // transposed rows a wave waits for at a time
+// Output rows per OP_DRED instruction (and per row-sum workgroup of the
+// one-kernel-per-op path): the staged partials, parts x B x rows words, stay
+// within the B x hidden floats a QKV instruction stages.
+__host__ __device__ inline uint32_t dred_rows(uint32_t d, uint32_t F) {
+    const uint32_t np = F / kDownPart, r = np ? d / np : 1u;
+    return r < 1u ? 1u : r > kMaxResidRows ? kMaxResidRows : r;
+}
 
 // MoE expert down projection: the (selected slot, output row) pairs of a layer,
 // n_slots x d of them in slot-major order, are dealt to the CUs in contiguous
@@ -189,6 +210,7 @@ static_assert(sizeof(Instr) == 16, "instruction record is 16 bytes");
 struct DevLayer {
     const uint16_t *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *w_gate, *w_up, *w_down;
     const uint16_t* router;  // MoE [E, d], else nullptr
+    const uint16_t* w_down_t;  // Wdown transposed [F][d] (the split down projection), else nullptr
 };
 
 // Device-resident state (in the workspace).
@@ -217,6 +239,7 @@ struct Params {
     int32_t x_slices;                          // QKV, router, expert gate/up and O inputs: column slices (power of 2)
     int32_t gemv_mfma;                         // 1: GEMVs on the matrix cores (tile-major weight chunks)
     int32_t E, top_k, n_shared, Fe;            // MoE: experts, selected per token, shared experts, expert width
+    int32_t down_split;                        // 1: DOWN as OP_DPART + OP_DRED (F / kDownPart parts)
     float eps, attn_scale;
     // weights
     const DevLayer* layers;
@@ -234,6 +257,7 @@ struct Params {
     uint64_t* route;      // MoE [B][E] router logits
     uint64_t* eact;       // MoE [n_shared + E][B][Fe] SwiGLU outputs of the experts
     uint64_t* epart;      // MoE [selected slot][B][d] unweighted down outputs of the selected experts
+    uint64_t* dpart;      // split DOWN [F / kDownPart][B][d] partial outputs of the parts
     const uint16_t* const* eptr;  // MoE [L][3 (gate, up, down)][n_shared + E] expert matrices (shared first)
     uint32_t* attn_ticket;  // [L][B][Hkv] * kCtrStride, reset by the merger
     uint32_t* head_ticket;  // kCtrStride, reset by the reducer

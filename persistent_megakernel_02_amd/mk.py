@@ -68,7 +68,7 @@ class mk_cut_costs(ctypes.Structure):
 class mk_runtime_config(ctypes.Structure):
     _fields_ = [("max_batch", ctypes.c_int32), ("max_seq", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("num_cus", ctypes.c_int32), ("gemv_kind", ctypes.c_int32), ("spin_timeout_ms", ctypes.c_uint32),
-                ("trace", ctypes.c_int32), ("attn_splits", ctypes.c_int32)]
+                ("trace", ctypes.c_int32), ("attn_splits", ctypes.c_int32), ("down_split", ctypes.c_int32)]
 
 
 _lib = None
@@ -166,10 +166,11 @@ def model_config(cfg) -> mk_model_config:
 
 def runtime_config(max_batch: int, max_seq: int, mode: int = MK_MODE_MEGAKERNEL, num_cus: int = 0,
                    spin_timeout_ms: int = 0, attn_splits: int = 0, trace: int = 0,
-                   gemv_kind: int = MK_GEMV_AUTO) -> mk_runtime_config:
+                   gemv_kind: int = MK_GEMV_AUTO, down_split: int = 0) -> mk_runtime_config:
     r = mk_runtime_config()
     r.max_batch, r.max_seq, r.mode, r.num_cus = max_batch, max_seq, mode, num_cus
     r.gemv_kind, r.spin_timeout_ms, r.trace, r.attn_splits = gemv_kind, spin_timeout_ms, trace, attn_splits
+    r.down_split = down_split
     return r
 
 
@@ -181,7 +182,7 @@ def mk_query_sizes(cfg: mk_model_config, rt: mk_runtime_config):
 
 def mk_plan_inspect(cfg: mk_model_config, rt: mk_runtime_config, num_cus: int):
     keys = ["cus", "instructions", "ring_chunks", "max_per_cu", "weight_bytes", "verify", "attn_splits", "phases",
-            "x_bytes", "head_instructions", "gemv_kind", "attn_hsplit", "max_wave_span"]
+            "x_bytes", "head_instructions", "gemv_kind", "attn_hsplit", "max_wave_span", "down_split"]
     out = (ctypes.c_int64 * len(keys))()
     st = lib().mk_plan_inspect(ctypes.byref(cfg), ctypes.byref(rt), num_cus, out, len(keys))
     return st, dict(zip(keys, list(out)))
@@ -204,7 +205,7 @@ class Decoder:
     def __init__(self, cfg, weights, max_batch: int, max_seq: int, mode: int = MK_MODE_MEGAKERNEL,
                  device: str = "cuda:0", num_cus: int = 0, spin_timeout_ms: int = 0, attn_splits: int = 0,
                  device_weights: Optional[Dict[str, object]] = None, trace: int = 0,
-                 gemv_kind: int = 0, static_workspace: bool = False):
+                 gemv_kind: int = 0, static_workspace: bool = False, down_split: int = 0):
         import torch
 
         self.torch = torch
@@ -213,7 +214,8 @@ class Decoder:
         self.B = max_batch
         self.max_seq = max_seq
         self._c = model_config(cfg)
-        self._rt = runtime_config(max_batch, max_seq, mode, num_cus, spin_timeout_ms, attn_splits, trace, gemv_kind)
+        self._rt = runtime_config(max_batch, max_seq, mode, num_cus, spin_timeout_ms, attn_splits, trace, gemv_kind,
+                                  down_split)
         st, ws, kv = mk_query_sizes(self._c, self._rt)
         if st != MK_OK:
             raise MKError(st, "mk_query_sizes")

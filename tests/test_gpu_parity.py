@@ -519,25 +519,56 @@ def test_down_column_slices():
     rt_, rl = oracle_run(cfg, w, prompt, 6, 16)
     for mode, kind in ((0, 1), (0, 2), (1, 0)):
         print(f"case wide-ffn b8 mode={mode} gemv={kind}", flush=True)
-        d = _decoder(cfg, w, B, 16, mode, gemv_kind=kind)
+        d = _decoder(cfg, w, B, 16, mode, gemv_kind=kind, down_split=-1)
         gt, gl = gpu_run(d, prompt, rt_, 6)
         compare(rt_, rl, gt, gl, f"wide-ffn b8 mode={mode} gemv={kind}")
         d.close()
 
 
+@pytest.mark.parametrize("ffn,B,cus", [(768, 1, 0), (768, 2, 0), (768, 4, 0), (768, 8, 0), (768, 4, 7),
+                                       (4096, 8, 0), (4096, 4, 7), (4096, 2, 1)])
+def test_down_split(ffn, B, cus):
+    """The down projection split by columns (per-part partial outputs from the
+    transposed Wdown, then per-row sums in part order), forced on at every batch
+    size, on all CUs, on 7 (parts not aligned with the GATEUP f-ranges; several
+    part instructions per CU at ffn 4096) and on 1: against the oracle, and the
+    persistent kernel equal bit for bit to the one-kernel-per-op path."""
+    import persistent_megakernel_02_amd.mk as mk
+
+    cfg = I.replace(I.TINY, ffn=ffn)
+    w = I.make_weights(cfg, seed=14)
+    prompt = I.make_prompt(cfg, B, 5, seed=15)
+    rt_, rl = oracle_run(cfg, w, prompt, 6, 16)
+    st, info = mk.mk_plan_inspect(mk.model_config(cfg), mk.runtime_config(B, 16, down_split=1), cus or 256)
+    assert st == mk.MK_OK and info["down_split"] == 1 and info["verify"] == 0
+    outs = []
+    for mode in (0, 1):
+        print(f"case down-split ffn={ffn} b{B} cus={cus} mode={mode}", flush=True)
+        d = _decoder(cfg, w, B, 16, mode, num_cus=cus, down_split=1)
+        gt, gl = gpu_run(d, prompt, rt_, 6, per_token=True)
+        compare(rt_, rl, gt, gl, f"down-split ffn={ffn} b{B} cus={cus} mode={mode}")
+        outs.append((gt, gl))
+        d.close()
+    for x, y in zip(outs[0][1], outs[1][1]):
+        assert np.array_equal(x, y)
+    for x, y in zip(outs[0][0], outs[1][0]):
+        assert np.array_equal(x, y)
+
+
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("B,ctx,kind", [(4, 8192, 0), (8, 8192, 0), (8, 8192, 2)],
-                         ids=["b4-auto", "b8-auto", "b8-mfma"])
-def test_llama1b_batch_long_context(B, ctx, kind):
+@pytest.mark.parametrize("B,ctx,kind,split", [(4, 8192, 0, 0), (8, 8192, 0, 0), (8, 8192, 2, 0), (4, 8192, 0, -1)],
+                         ids=["b4-auto", "b8-auto", "b8-mfma", "b4-unsplit-down"])
+def test_llama1b_batch_long_context(B, ctx, kind, split):
     """The 1B shape at batch 4 and 8 over an 8192-position synthetic context:
-    split attention and sliced DOWN, 8 steps; at batch 8 also on the matrix cores."""
+    split attention, DOWN split by columns (automatic at these batches) or in
+    column slices, 8 steps; at batch 8 also on the matrix cores."""
     cfg = I.LLAMA_1B
     w = I.make_weights(cfg, seed=9)
     steps, S = 8, ctx + 16
     start = I.make_prompt(cfg, B, 1, seed=9)[:, 0]
     orc = O.Oracle(cfg, w, B, S)
-    print(f"case 1B b{B} ctx={ctx} megakernel gemv={kind}", flush=True)
-    d = _decoder(cfg, w, B, S, 0, gemv_kind=kind)
+    print(f"case 1B b{B} ctx={ctx} megakernel gemv={kind} down_split={split}", flush=True)
+    d = _decoder(cfg, w, B, S, 0, gemv_kind=kind, down_split=split)
     t0 = time.time()
     _fill_context(cfg, orc, d, ctx, seed=9)
     print(f"context filled in {time.time() - t0:.1f}s", flush=True)
@@ -556,7 +587,7 @@ def test_llama1b_batch_long_context(B, ctx, kind):
     d.close()
 
 
-@pytest.mark.parametrize("cfg_name,B,P", [("tiny", 2, 13), ("tiny", 1, 8), ("1b", 1, 19)])
+@pytest.mark.parametrize("cfg_name,B,P", [("tiny", 2, 13), ("tiny", 1, 8), ("tiny", 4, 11), ("1b", 1, 19)])
 def test_multi_position_prefill(cfg_name, B, P):
     """mk_prefill in the persistent mode runs each sequence's prompt in launches of
     up to 8 positions (causal attention inside a launch, every position's K/V
