@@ -785,6 +785,8 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
     P.n_shared = cfg->n_experts ? cfg->n_shared_experts : 0;
     P.Fe = cfg->expert_ffn;
     P.down_split = down_split_on(cfg, rt) ? 1 : 0;
+    P.gu_direct = (rt->max_batch == 1 && !cfg->n_experts && !P.gemv_mfma &&
+                   (uint32_t)cfg->hidden * 2u == kGuRowPieces * 16u) ? 1 : 0;
     P.V = cfg->vocab;
     P.B = rt->max_batch;
     P.S = rt->max_seq;
@@ -903,6 +905,7 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
         C.epart = (uint64_t*)(cb + cl.epart);
         C.dpart = (uint64_t*)(cb + cl.dpart);
         C.down_split = down_split_on(cfg, &r8) ? 1 : 0;
+        C.gu_direct = 0;  // (the multi-position kernels stream every GEMV through the ring)
         C.eptr = (const uint16_t* const*)(cb + cl.eptr);
         C.attn_ticket = (uint32_t*)(cb + cl.tickets);
         C.head_ticket = C.attn_ticket + (size_t)cfg->n_layers * kChunkRows * cfg->n_kv_heads * kCtrStride;

@@ -49,6 +49,10 @@ struct Ctl {
     // LM head: queue index + 1 once the final-norm input is staged and its statistics
     // are in ss (published by compute wave 0 for the loader waves, which join the head)
     uint32_t head_seq;
+    // (gate, up) rows streamed by the loader waves (batch 1, 4 KB rows): queue index +
+    // 1 once the input is staged and its statistics are in ss (compute wave 0), and
+    // the loaders' reads of that input (monotonic, one per loader and instruction)
+    uint32_t gu_seq, gu_done;
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -99,7 +103,7 @@ __device__ __forceinline__ uint32_t instr_bytes(const Params& P, const Instr& in
         case OP_QKV:
         case OP_ROUTE: return align_chunk(in.count * (uint32_t)P.d * 2u);
         case OP_O: return align_chunk(in.count * (uint32_t)(P.Hq * HD) * 2u);
-        case OP_GATEUP: return align_chunk(2u * in.count * (uint32_t)P.d * 2u);
+        case OP_GATEUP: return P.gu_direct ? 0u : align_chunk(2u * in.count * (uint32_t)P.d * 2u);
         case OP_DOWN: return align_chunk(in.count * (uint32_t)P.F * 2u);
         case OP_DPART: return in.count * kDownPart * (uint32_t)P.d * 2u;  // whole 16 KB multiples
         case OP_ATTN: {
@@ -398,9 +402,139 @@ __device__ __forceinline__ uint32_t landed_prefix(const Ctl* ctl) {
 
 // Returns the queue index of the LM-head instruction when this kernel kind has
 // the loader waves join it (head_direct), else q1.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// (gate, up) rows at batch 1 with rows of 4 KB (hidden 2048), from HBM straight
+// into the loader waves' registers.  Through the ring each pair cost a compute wave
+// about 0.7 us of LDS traffic (8 KB of weights and 8 KB of fp32 x read per pair,
+// next to the loaders' writes of the same bytes); the compute waves have no
+// registers to spare for rows in flight, the loader waves do.  A loader reaching
+// the instruction in its stream retires its chunks in flight, requests its first
+// kGuAhead rows (during attention and O, while the ring is full and it would only
+// wait), waits for the compute waves to publish the staged input, copies its four
+// pieces of x to registers, and computes pairs k, k + 4, ... (the gate row, then
+// the up row), refilling a row's registers as soon as its products have read them.
+// It stores its SwiGLU outputs after the last row (a store between the row loads
+// would make every later wait on a load also wait for the write-through store),
+// then streams the down projection into the ring.  Each lane accumulates its
+// pieces lane, lane + 64, ... in ascending order and wave_total reduces in its
+// fixed tree: the values are bit for bit those of the ring GEMV.
+typedef __attribute__((address_space(1))) const u32x4_t* gu32x4_ptr;  // global memory (no flat loads)
+
+struct GuRows {
+    gu32x4_ptr gate;  // uniform: the instruction's first gate row
+    gu32x4_ptr up;
+    uint32_t off;         // this lane's first piece of the wave's first row (16-byte units)
+    uint32_t nu;          // rows of this wave: two per pair
+    // row u of the wave (the callers' unrolled loops make is_up a constant) into dst
+    __device__ __forceinline__ void issue(uint32_t u, bool is_up, uint4 (&dst)[4]) const {
+        const gu32x4_ptr base = is_up ? up : gate;
+        const uint32_t o = off + (u >> 1) * (uint32_t)(kLoaderWaves * kGuRowPieces);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const u32x4_t v = __builtin_nontemporal_load(base + o + 64u * (uint32_t)g);
+            dst[g] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+    }
+};
+
+// Waits (with the watchdog) until the LDS word *p reaches `want`; false on abort.
+__device__ __forceinline__ bool wait_lds_at_least(const Params& P, Ctl* ctl, const uint32_t* p, uint32_t want,
+                                                  uint32_t code) {
+    const uint64_t t0 = now_ticks();
+    uint32_t polls = 0;
+    while ((int32_t)(lds_ld(p) - want) < 0) {
+        if (lds_ld(&ctl->abort)) return false;
+        if ((++polls & 255u) == 0 && now_ticks() - t0 > P.spin_ticks) {
+            raise_error_impl(P.state, P.host_err, &ctl->abort, DERR_TIMEOUT, code, want);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    return true;
+}
+
+// Loader wave k's part of (gate, up) instruction qi (its stream has no ring bytes).
+__device__ __forceinline__ bool gu_loader(const Params& P, Ctl* ctl, const float* xs, const Instr& in, int k,
+                                          uint32_t qi, uint32_t tag0) {
+    constexpr int D = kGuAhead;
+    static_assert(D % 2 == 0, "a row's parity must be its slot's parity");
+    const uint32_t lane = (uint32_t)lane_id(), nw = (uint32_t)kLoaderWaves;
+    const DevLayer Lw = ld_const(P.layers + (in.layer < P.L ? in.layer : 0));
+    const uint32_t npair = in.count > (uint32_t)k ? (in.count - (uint32_t)k + nw - 1u) / nw : 0u;
+    const size_t first = (size_t)in.begin * kGuRowPieces;
+    const GuRows gr{(gu32x4_ptr)uniform_p(Lw.w_gate) + first, (gu32x4_ptr)uniform_p(Lw.w_up) + first,
+                    (uint32_t)k * kGuRowPieces + lane, 2u * npair};
+    // Rows go in blocks of kGuBlock (one block per instruction when each loader has
+    // kGuBlock / 2 pairs): inside a block the loop is unrolled, so every row buffer
+    // is a fixed register and every wait on a row's loads counts exactly the loads
+    // issued after it (a buffer carried around a loop back edge gets a full vmcnt
+    // wait).  Blocks of other sizes (other CU counts) take one row at a time.
+    const bool blocked = gr.nu >= (uint32_t)kGuBlock;
+    uint4 w[D][4];
+    if (blocked) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) gr.issue((uint32_t)i, (i & 1) != 0, w[i]);
+    }
+    // the staged input (h * g in xs) and its RMSNorm statistics
+    if (!wait_lds_at_least(P, ctl, &ctl->gu_seq, qi + 1u, 0xFFFFFFF9u)) return false;
+    const float r = rms_scale(ctl->ss[0], kComputeWaves, P.d, P.eps);
+    const XLds x{xs, (uint32_t)P.d};
+    float4 xa[4], xb[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) x.piece(0, lane + 64u * (uint32_t)g, xa[g], xb[g]);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): x is in registers before xs may be reused
+    if (lane == 0) __hip_atomic_fetch_add(&ctl->gu_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t tag_out = phase_tag(tag0, in.layer, 3);
+    float g_val = 0.f, keep = 0.f;
+    // row u's products; after an up row, pair u / 2's output goes to lane (u / 2) mod
+    // 64, and 64 pairs (or the last) are stored
+    auto row = [&](uint32_t u, bool is_up, const uint4 (&v)[4]) {
+        float acc[1] = {0.f};
+#pragma unroll
+        for (int g = 0; g < 4; ++g) acc[0] = dot8(v[g], xa[g], xb[g], acc[0]);
+        wave_total_n<1>(acc);
+        if (!is_up) {
+            g_val = acc[0];
+            return;
+        }
+        const uint32_t t = u >> 1, tl = t & 63u;
+        const float o = silu_mul(g_val * r, acc[0] * r);
+        keep = lane == tl ? o : keep;
+        if (tl == 63u || t + 1u == npair) {
+            if (lane <= tl) st_tagged(P.act + in.begin + (uint32_t)k + nw * (t - tl + lane), keep, tag_out);
+        }
+    };
+    uint32_t u0 = 0;
+    if (blocked) {
+        for (;; u0 += (uint32_t)kGuBlock) {
+            const bool next = u0 + 2u * (uint32_t)kGuBlock <= gr.nu;  // another whole block follows
+#pragma unroll
+            for (int i = 0; i < kGuBlock; ++i) {
+                const uint32_t u = u0 + (uint32_t)i;
+                row(u, (i & 1) != 0, w[i % D]);
+                if (i + D < kGuBlock) gr.issue(u + D, (i & 1) != 0, w[i % D]);
+                else if (next) gr.issue(u + D, (i & 1) != 0, w[i % D]);
+            }
+            if (!next) break;
+        }
+        u0 += (uint32_t)kGuBlock;
+    }
+    for (uint32_t u = u0; u < gr.nu; ++u) {  // the rest, one row at a time
+        uint4 v[4];
+        gr.issue(u, (u & 1u) != 0, v);
+        row(u, (u & 1u) != 0, v);
+    }
+    // (the stores may still be in flight when the chunk stream resumes: they are
+    // older than every chunk, so a vmcnt bound that guarantees a chunk has landed
+    // still does, since loads land in order)
+    return true;
+}
+
 template <int B, int HD, bool MF, bool MOE>
 __device__ __forceinline__ uint32_t loader_wave(const Params& P, Ctl* ctl, char* ring, int k, uint32_t q0, uint32_t q1,
-                                                const int32_t* ctx) {
+                                                const int32_t* ctx, const float* xs, uint32_t tag0) {
     constexpr int LAG = loader_lag<B>();
     const uint32_t N = P.ring_chunks;
     const uint32_t NL = (uint32_t)kLoaderWaves;
@@ -494,6 +628,25 @@ __device__ __forceinline__ uint32_t loader_wave(const Params& P, Ctl* ctl, char*
         if (!MF && in.op == OP_HEAD) {  // the last instruction of every queue
             head_at = i;
             break;
+        }
+        if constexpr (B == 1 && !MF && !MOE) {
+            if (in.op == OP_GATEUP && P.gu_direct) {  // rows into registers, no ring bytes
+                if (k == 0 && P.trace && lane_id() == 0 && i > q0) {
+                    uint32_t* rec = P.trace + ((size_t)blockIdx.x * P.trace_stride + (i - 1 - q0)) * kTraceWords;
+                    rec[5] = (uint32_t)now_ticks();
+                    rec[7] = stall;
+                }
+                stall = 0;
+                if (issued != landed) {  // retire the chunks in flight: vmcnt counts the row loads next
+                    wait_vmcnt<0>();
+                    publish(issued);
+                }
+                if (!gu_loader(P, ctl, xs, in, k, i, tag0)) {
+                    stop = true;
+                    break;
+                }
+                continue;
+            }
         }
         uint32_t nch;
         if (MOE && is_moe_expert(in.op)) {
@@ -1870,6 +2023,7 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
     Spin spin(&P, &ctl->abort);
     CwBarrier barrier{ctl, &P, 0u};
     uint32_t head_qi = q1;
+    uint32_t gu_expect = 0;  // loader reads of staged (gate, up) inputs seen so far (gu_loader)
     for (uint32_t qi = q0; qi < q1; ++qi, ++k) {
         const Instr in = ld_const(P.instrs + qi);
         uint32_t bytes = instr_bytes<HD, MF>(P, in, ctx);  // MoE expert instructions set it once routed
@@ -1998,6 +2152,17 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
                     ok = gemv_ring_auto<B>(P, ctl, ring, S, rb, nrows, x, wave, land_wait, epi, false);
                 } else if (in.op == OP_GATEUP) {
                     const uint32_t tag_out = phase_tag(A.tag0, layer, 3);
+                    if (B == 1 && !MOE && P.gu_direct) {
+                        // the loader waves compute the rows (gu_loader): publish the input,
+                        // then wait until every loader holds its x before xs is reused
+                        if (wave == 0 && lane == 0) {
+                            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                            lds_st(&ctl->gu_seq, qi + 1u);
+                        }
+                        gu_expect += (uint32_t)kLoaderWaves;
+                        ok = wait_lds_at_least(P, ctl, &ctl->gu_done, gu_expect, 0xFFFFFFFAu);
+                        break;
+                    }
                     auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
                         #pragma unroll
                         for (uint32_t i = 0; i + 1 < (uint32_t)(sizeof(res) / sizeof(res[0])); i += 2) {
@@ -2155,6 +2320,8 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
         ctl.moe_seq = 0;
         ctl.moe_n = 0;
         ctl.head_seq = 0;
+        ctl.gu_seq = 0;
+        ctl.gu_done = 0;
     }
     // context lengths at launch (a multi-position step: every row sees the sequence's cached length)
     if (threadIdx.x < kMaxBatch)
@@ -2165,7 +2332,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
     const uint32_t q0 = ld_const(qr), q1 = ld_const(qr + 1);
     uint32_t hi;
     if (wave >= kComputeWaves) {
-        hi = loader_wave<B, HD, MF, MOE>(P, &ctl, ring, wave - kComputeWaves, q0, q1, ctl.ctx);
+        hi = loader_wave<B, HD, MF, MOE>(P, &ctl, ring, wave - kComputeWaves, q0, q1, ctl.ctx, xs, A.tag0);
     } else {
         hi = compute_wave<B, HD, MF, MOE, CH>(P, A, &ctl, ring, xs, wave, q0, q1, ctl.ctx);
     }

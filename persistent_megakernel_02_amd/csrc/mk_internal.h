@@ -148,6 +148,13 @@ enum Op : uint16_t {
     OP_DRED = 12,   // dense DOWN by columns: per output row the parts' partials in order, residual add
 };
 
+// Batch 1 with rows of 4 KB (hidden 2048): the compute waves load the (gate, up)
+// rows from HBM into registers, kGuAhead rows in flight per wave, instead of
+// reading them from the LDS ring (Params::gu_direct).
+constexpr int kGuAhead = 8;   // rows in flight per loader wave
+constexpr int kGuBlock = 16;  // rows per unrolled block (kGuBlock / 2 pairs)
+constexpr uint32_t kGuRowPieces = 256;  // 16-byte pieces of a 4 KB row (4 per lane)
+
 // The dense down projection split by columns (batch 4 and 8; opt-in below): F is
 // cut into parts of kDownPart SwiGLU outputs.  Part j's partial output of every
 // row i is the sum over its f of act[f] * Wdown[i][f], accumulated in ascending f
@@ -240,6 +247,7 @@ struct Params {
     int32_t gemv_mfma;                         // 1: GEMVs on the matrix cores (tile-major weight chunks)
     int32_t E, top_k, n_shared, Fe;            // MoE: experts, selected per token, shared experts, expert width
     int32_t down_split;                        // 1: DOWN as OP_DPART + OP_DRED (F / kDownPart parts)
+    int32_t gu_direct;                         // 1: (gate, up) rows HBM -> compute-wave registers, not the ring
     float eps, attn_scale;
     // weights
     const DevLayer* layers;
