@@ -51,8 +51,12 @@ struct Ctl {
     uint32_t head_seq;
     // (gate, up) rows streamed by the loader waves (batch 1, 4 KB rows): queue index +
     // 1 once the input is staged and its statistics are in ss (compute wave 0), and
-    // the loaders' reads of that input (monotonic, one per loader and instruction)
+    // the loaders that have finished such an instruction (monotonic, one per loader
+    // and instruction)
     uint32_t gu_seq, gu_done;
+    // compute wave 0's progress: 2 qi + 1 once instruction qi has started, 2 qi + 2
+    // once an O instruction's input is staged (monotonic)
+    uint32_t prog;
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -457,7 +461,7 @@ __device__ __forceinline__ bool wait_lds_at_least(const Params& P, Ctl* ctl, con
 
 // Loader wave k's part of (gate, up) instruction qi (its stream has no ring bytes).
 __device__ __forceinline__ bool gu_loader(const Params& P, Ctl* ctl, const float* xs, const Instr& in, int k,
-                                          uint32_t qi, uint32_t tag0) {
+                                          uint32_t qi, uint32_t tag0, uint32_t* tr) {
     constexpr int D = kGuAhead;
     static_assert(D % 2 == 0, "a row's parity must be its slot's parity");
     const uint32_t lane = (uint32_t)lane_id(), nw = (uint32_t)kLoaderWaves;
@@ -473,19 +477,24 @@ __device__ __forceinline__ bool gu_loader(const Params& P, Ctl* ctl, const float
     // wait).  Blocks of other sizes (other CU counts) take one row at a time.
     const bool blocked = gr.nu >= (uint32_t)kGuBlock;
     uint4 w[D][4];
+    // The first rows are requested once the compute waves have staged the O input
+    // before this instruction (or started this one): early enough to land before
+    // the (gate, up) input is staged, late enough to stay out of the QKV and
+    // attention edges, whose polls the burst would slow.
+    if (!wait_lds_at_least(P, ctl, &ctl->prog, 2u * qi, 0xFFFFFFF8u)) return false;
     if (blocked) {
 #pragma unroll
         for (int i = 0; i < D; ++i) gr.issue((uint32_t)i, (i & 1) != 0, w[i]);
     }
+    if (tr && lane == 0) tr[9] = (uint32_t)now_ticks();
     // the staged input (h * g in xs) and its RMSNorm statistics
     if (!wait_lds_at_least(P, ctl, &ctl->gu_seq, qi + 1u, 0xFFFFFFF9u)) return false;
+    if (tr && lane == 0) tr[10] = (uint32_t)now_ticks();
     const float r = rms_scale(ctl->ss[0], kComputeWaves, P.d, P.eps);
     const XLds x{xs, (uint32_t)P.d};
     float4 xa[4], xb[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) x.piece(0, lane + 64u * (uint32_t)g, xa[g], xb[g]);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): x is in registers before xs may be reused
-    if (lane == 0) __hip_atomic_fetch_add(&ctl->gu_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     const uint32_t tag_out = phase_tag(tag0, in.layer, 3);
     float g_val = 0.f, keep = 0.f;
     // row u's products; after an up row, pair u / 2's output goes to lane (u / 2) mod
@@ -526,6 +535,11 @@ __device__ __forceinline__ bool gu_loader(const Params& P, Ctl* ctl, const float
         gr.issue(u, (u & 1u) != 0, v);
         row(u, (u & 1u) != 0, v);
     }
+    if (tr && lane == 0) tr[11] = (uint32_t)now_ticks();
+    // done: the compute waves, waiting for every loader, go on to stage the down
+    // projection's input (polling it while this CU still streams its rows would only
+    // slow the stream), and may overwrite xs
+    if (lane == 0) __hip_atomic_fetch_add(&ctl->gu_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     // (the stores may still be in flight when the chunk stream resumes: they are
     // older than every chunk, so a vmcnt bound that guarantees a chunk has landed
     // still does, since loads land in order)
@@ -641,7 +655,9 @@ __device__ __forceinline__ uint32_t loader_wave(const Params& P, Ctl* ctl, char*
                     wait_vmcnt<0>();
                     publish(issued);
                 }
-                if (!gu_loader(P, ctl, xs, in, k, i, tag0)) {
+                uint32_t* tr = (k == 0 && P.trace) ? P.trace + ((size_t)blockIdx.x * P.trace_stride + (i - q0)) * kTraceWords
+                                                   : nullptr;
+                if (!gu_loader(P, ctl, xs, in, k, i, tag0, tr)) {
                     stop = true;
                     break;
                 }
@@ -2036,6 +2052,7 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
         // every wave has finished reading the previous instruction's staged inputs
         if (!barrier()) return q1;
         if (tr && lane == 0) tr[8] = (uint32_t)now_ticks();
+        if (wave == 0 && lane == 0) lds_st(&ctl->prog, 2u * qi + 1u);
         uint32_t land_wait = 0;
         const int layer = in.layer;
         const DevLayer Lw = ld_const(P.layers + (layer < P.L ? layer : 0));
@@ -2154,7 +2171,7 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
                     const uint32_t tag_out = phase_tag(A.tag0, layer, 3);
                     if (B == 1 && !MOE && P.gu_direct) {
                         // the loader waves compute the rows (gu_loader): publish the input,
-                        // then wait until every loader holds its x before xs is reused
+                        // then wait until every loader has stored its outputs
                         if (wave == 0 && lane == 0) {
                             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
                             lds_st(&ctl->gu_seq, qi + 1u);
@@ -2215,6 +2232,7 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
                     }
                     if (!barrier()) return q1;
                     if (tr && lane == 0 && ks == 0) tr[2] = (uint32_t)now_ticks();
+                    if (is_o && ks == 0 && wave == 0 && lane == 0) lds_st(&ctl->prog, 2u * qi + 2u);
                     const XLds x{xs, Ks};
                     const bool last = ks + 1 == ns;
                     auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {
@@ -2249,7 +2267,9 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
             tr[3] = (uint32_t)now_ticks();
             tr[6] = land_wait;
         }
-        if (P.trace && wave > 0 && in.op != OP_ATTN && lane == 0)  // the other waves' compute ends
+        // the other waves' compute ends (for (gate, up) rows computed by the loaders,
+        // loader 0 writes these words: rows requested, input seen, rows done)
+        if (P.trace && wave > 0 && in.op != OP_ATTN && !(in.op == OP_GATEUP && P.gu_direct) && lane == 0)
             P.trace[((size_t)blockIdx.x * P.trace_stride + k) * kTraceWords + 8 + wave] = (uint32_t)now_ticks();
         S += bytes;
         set_consumed(ctl, wave, S / kChunk);
@@ -2322,6 +2342,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
         ctl.head_seq = 0;
         ctl.gu_seq = 0;
         ctl.gu_done = 0;
+        ctl.prog = 0;
     }
     // context lengths at launch (a multi-position step: every row sees the sequence's cached length)
     if (threadIdx.x < kMaxBatch)
