@@ -202,6 +202,33 @@ __global__ void __launch_bounds__(kConvThreads) k_proj(Params P, StepArgs A, int
     const uint32_t tag_out = is_down ? phase_tag(A.tag0, layer, 4) : phase_tag(A.tag0, layer, 2);
     const uint32_t begin = blockIdx.x * rpb;
     const uint32_t count = min(rpb, (uint32_t)P.d - begin);
+    if (B == 1 && is_down && P.down_q) {
+        // by column quarters, as the persistent kernel's down_q_instr (weights from HBM)
+        float* hres1 = xs + K;
+        float* part4 = hres1 + kMaxResidRows;
+        float ss[1] = {0.f};
+        const StageSeg sg[2] = {{P.act, xs, nullptr, K, 1u, K, K, tag_x},
+                                {P.h + begin, hres1, nullptr, count, 1u, (uint32_t)P.d, count, tag_res}};
+        if (!stage_segs<kStagePassWordsWide, 1, 2>(sg, wave, kConvWaves, spin, ss)) return;
+        __syncthreads();
+        const XLds x{xs, K};
+        float4 xa[4], xb[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x.piece(0, (uint32_t)wave * kDownQPieces + (uint32_t)lane + 64u * (uint32_t)k, xa[k], xb[k]);
+        for (uint32_t j = 0; j < count; ++j) {
+            const uint4* rp = (const uint4*)(Lw.w_down + (size_t)(begin + j) * K) + (uint32_t)wave * kDownQPieces + lane;
+            uint4 w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[k] = rp[64 * k];
+            const float v = down_q_partial(w, xa, xb);
+            if (lane == 0) part4[j * 4u + (uint32_t)wave] = v;
+        }
+        __syncthreads();
+        if (wave == 0)
+            for (uint32_t j = (uint32_t)lane; j < count; j += 64u)
+                st_tagged(P.h + begin + j, hres1[j] + down_q_row(part4 + j * 4u), tag_out);
+        return;
+    }
     // DOWN runs over P.down_slices column slices of its input; partial sums wait in LDS
     const uint32_t ns = is_down ? (uint32_t)P.down_slices : 1u, Ks = K / ns;
     float* hres = xs + B * Ks;

@@ -97,6 +97,11 @@ bool down_split_on(const mk_model_config* c, const mk_runtime_config* rt) {
     return rt->down_split > 0 || rt->max_batch >= 4;
 }
 
+// DOWN by column quarters (batch 1, F = 8192, VALU, not split by columns).
+bool down_q_on(const mk_model_config* c, const mk_runtime_config* rt) {
+    return !c->n_experts && down_quarters_for(rt->max_batch, c->ffn) && !use_mfma(c, rt) && !down_split_on(c, rt);
+}
+
 uint32_t dred_rows_for(const mk_model_config* c) { return dred_rows((uint32_t)c->hidden, (uint32_t)c->ffn); }
 
 // LDS floats of activations one instruction stages (x rows, residual rows of
@@ -142,8 +147,9 @@ size_t x_floats_kind(const mk_model_config* c, const mk_runtime_config* rt, int 
         return std::max(n, attn_lds_floats((int)G, (int)hd, nsplit, nnew));
     }
     // DOWN: one column slice of the input, the residual rows and the partial sums
+    // (by column quarters: the input, the residual rows and four values per row)
     const int ns = std::max(1, down_slices_for((int)B, c->ffn));
-    n = std::max(n, B * ((size_t)(c->ffn / ns) + 2 * kMaxResidRows));
+    n = std::max(n, B * ((size_t)(c->ffn / ns) + (down_q_on(c, rt) ? 5 : 2) * kMaxResidRows));
     return std::max(n, attn_lds_floats((int)G, (int)hd, nsplit, nnew));
 }
 
@@ -785,6 +791,7 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
     P.n_shared = cfg->n_experts ? cfg->n_shared_experts : 0;
     P.Fe = cfg->expert_ffn;
     P.down_split = down_split_on(cfg, rt) ? 1 : 0;
+    P.down_q = down_q_on(cfg, rt) ? 1 : 0;
     P.gu_direct = (rt->max_batch == 1 && !cfg->n_experts && !P.gemv_mfma &&
                    (uint32_t)cfg->hidden * 2u == kGuRowPieces * 16u) ? 1 : 0;
     P.V = cfg->vocab;
@@ -906,6 +913,7 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
         C.dpart = (uint64_t*)(cb + cl.dpart);
         C.down_split = down_split_on(cfg, &r8) ? 1 : 0;
         C.gu_direct = 0;  // (the multi-position kernels stream every GEMV through the ring)
+        C.down_q = 0;
         C.eptr = (const uint16_t* const*)(cb + cl.eptr);
         C.attn_ticket = (uint32_t*)(cb + cl.tickets);
         C.head_ticket = C.attn_ticket + (size_t)cfg->n_layers * kChunkRows * cfg->n_kv_heads * kCtrStride;

@@ -2031,6 +2031,64 @@ __device__ __forceinline__ bool attn_instr(const Params& P, const StepArgs& A, C
 // Returns the queue index of the LM-head instruction once its input is staged
 // and published (the caller runs its rows: head_instr), or q1 (none in this kind,
 // or the workgroup stopped).
+// The down projection at batch 1 with F = 8192, by column quarters (down_q_partial):
+// the input and the residual rows are staged as for DOWN, then compute wave q keeps
+// its quarter of x in registers and, row by row, waits for that row's quarter in the
+// ring (4 KB), reduces it and leaves the value in LDS; after a barrier wave 0 adds
+// each row's quarters in order and the residual.
+__device__ __forceinline__ bool down_q_instr(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs,
+                                             int wave, const Instr& in, uint32_t S, Spin& spin, CwBarrier& barrier,
+                                             uint32_t& land_wait, uint32_t* tr) {
+    const uint32_t lane = (uint32_t)lane_id(), K = (uint32_t)P.F, layer = in.layer;
+    float* hres = xs + K;                 // [count] residual rows
+    float* part = hres + kMaxResidRows;   // [count][4] quarter values
+    float ss[1] = {0.f};
+    const StageSeg sg[2] = {{P.act, xs, nullptr, K, 1u, K, K, phase_tag(A.tag0, layer, 3)},
+                            {P.h + in.begin, hres, nullptr, in.count, 1u, (uint32_t)P.d, in.count,
+                             phase_tag(A.tag0, layer, 2)}};
+    if (!stage_segs<stage_words_wide<1>(), 1, 2>(sg, wave, kComputeWaves, spin, ss)) return false;
+    if (!barrier()) return false;
+    if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
+    const XLds x{xs, K};
+    float4 xa[4], xb[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x.piece(0, (uint32_t)wave * kDownQPieces + lane + 64u * (uint32_t)k, xa[k], xb[k]);
+    // two rows at a time: one wait, all eight pieces requested together, the two
+    // reductions interleaved (each row's value is the one down_q_partial gives)
+    const uint32_t rb = K * 2u, ring_bytes = P.ring_chunks * kChunk, qb = kDownQPieces * 16u;
+    for (uint32_t j = 0; j < in.count; j += 2u) {
+        const uint32_t nr = min(2u, in.count - j);
+        const uint32_t off = S + j * rb + (uint32_t)wave * qb;
+        set_consumed(ctl, wave, off / kChunk);
+        if (!wait_landed(P, ctl, (off + (nr - 1u) * rb + qb + kChunk - 1u) / kChunk, land_wait)) return false;
+        uint4 w[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            // (a lone last row reads its own quarter twice)
+            const RingBatch q{ring, ring_addr(off + (i < (int)nr ? (uint32_t)i : 0u) * rb, P.ring_chunks), rb, ring_bytes};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[i][k] = q.piece(0u, lane + 64u * (uint32_t)k);
+        }
+        float acc[2] = {0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) acc[i] = dot8(w[i][k], xa[k], xb[k], acc[i]);
+        wave_total_n<2>(acc);
+        if (lane == 0) {
+            part[j * 4u + (uint32_t)wave] = acc[0];
+            if (nr > 1u) part[(j + 1u) * 4u + (uint32_t)wave] = acc[1];
+        }
+    }
+    if (!barrier()) return false;
+    if (wave == 0) {
+        const uint32_t tag_out = phase_tag(A.tag0, layer, 4);
+        for (uint32_t j = lane; j < in.count; j += 64u)
+            st_tagged(P.h + in.begin + j, hres[j] + down_q_row(part + j * 4u), tag_out);
+    }
+    return true;
+}
+
 template <int B, int HD, bool MF, bool MOE, bool CH>
 __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring,
                                                  float* xs, int wave, uint32_t q0, uint32_t q1, const int32_t* ctx) {
@@ -2052,7 +2110,9 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
         // every wave has finished reading the previous instruction's staged inputs
         if (!barrier()) return q1;
         if (tr && lane == 0) tr[8] = (uint32_t)now_ticks();
-        if (wave == 0 && lane == 0) lds_st(&ctl->prog, 2u * qi + 1u);
+        if constexpr (B == 1 && !MOE) {  // (read only by gu_loader)
+            if (wave == 0 && lane == 0) lds_st(&ctl->prog, 2u * qi + 1u);
+        }
         uint32_t land_wait = 0;
         const int layer = in.layer;
         const DevLayer Lw = ld_const(P.layers + (layer < P.L ? layer : 0));
@@ -2169,7 +2229,7 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
                     ok = gemv_ring_auto<B>(P, ctl, ring, S, rb, nrows, x, wave, land_wait, epi, false);
                 } else if (in.op == OP_GATEUP) {
                     const uint32_t tag_out = phase_tag(A.tag0, layer, 3);
-                    if (B == 1 && !MOE && P.gu_direct) {
+                    if (B == 1 && !MOE && P.gu_direct) {  // (B is a template constant)
                         // the loader waves compute the rows (gu_loader): publish the input,
                         // then wait until every loader has stored its outputs
                         if (wave == 0 && lane == 0) {
@@ -2200,6 +2260,12 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
             case OP_O:
             case OP_DOWN: {
                 const bool is_o = in.op == OP_O;
+                if constexpr (B == 1 && !MOE) {
+                    if (!is_o && P.down_q) {
+                        ok = down_q_instr(P, A, ctl, ring, xs, wave, in, S, spin, barrier, land_wait, tr);
+                        break;
+                    }
+                }
                 const uint32_t K = is_o ? (uint32_t)(P.Hq * HD) : (uint32_t)P.F;
                 const uint32_t tag_x = is_o ? phase_tag(A.tag0, layer, 1) : phase_tag(A.tag0, layer, 3);
                 const uint32_t tag_res = is_o ? phase_tag(A.tag0, layer - 1, 4) : phase_tag(A.tag0, layer, 2);
@@ -2232,7 +2298,9 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
                     }
                     if (!barrier()) return q1;
                     if (tr && lane == 0 && ks == 0) tr[2] = (uint32_t)now_ticks();
-                    if (is_o && ks == 0 && wave == 0 && lane == 0) lds_st(&ctl->prog, 2u * qi + 2u);
+                    if constexpr (B == 1 && !MOE) {
+                        if (is_o && ks == 0 && wave == 0 && lane == 0) lds_st(&ctl->prog, 2u * qi + 2u);
+                    }
                     const XLds x{xs, Ks};
                     const bool last = ks + 1 == ns;
                     auto epi = [&](uint32_t r0, uint32_t nr, auto& res) {

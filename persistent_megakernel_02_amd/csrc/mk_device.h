@@ -793,6 +793,19 @@ __device__ __forceinline__ void rows_dot(const Rows& rows, int np, const X& x, f
         for (int b = 0; b < B; ++b) out[i][b] = t[i * B + b];
 }
 
+// Quarter q of a down-projection row (batch 1, F = 8192): this lane's 4 pieces
+// lane + 64 k of the quarter against the matching x pieces (in registers), in
+// ascending order, then the fixed wave_total tree.  The row is the four quarters'
+// values added in order (down_q_row).
+__device__ __forceinline__ float down_q_partial(const uint4 (&w)[4], const float4 (&xa)[4], const float4 (&xb)[4]) {
+    float acc[1] = {0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[0] = dot8(w[k], xa[k], xb[k], acc[0]);
+    wave_total_n<1>(acc);
+    return acc[0];
+}
+__device__ __forceinline__ float down_q_row(const float* q4) { return ((q4[0] + q4[1]) + q4[2]) + q4[3]; }
+
 // a[i] for a per-lane i < B.  The empty asm between the selects keeps the chain
 // of v_cndmask: folded into a table lookup it would index a private array.
 template <int B>

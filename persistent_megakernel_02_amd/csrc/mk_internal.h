@@ -148,6 +148,14 @@ enum Op : uint16_t {
     OP_DRED = 12,   // dense DOWN by columns: per output row the parts' partials in order, residual add
 };
 
+// Batch 1 with F = 8192: the down projection is reduced by column quarters.  Compute
+// wave q keeps x[2048 q, 2048 q + 2048) in registers (4 pieces per lane) and reduces
+// quarter q of every row of the instruction; a row is its quarters' sums added in
+// quarter order (Params::down_q).  Each wave reads only its quarter of the weights
+// from LDS, not the whole 32 KB input once per row.
+constexpr uint32_t kDownQPieces = 256;  // 16-byte pieces of one quarter row
+__host__ __device__ constexpr bool down_quarters_for(int B, int F) { return B == 1 && F == 4 * (int)kDownQPieces * 8; }
+
 // Batch 1 with rows of 4 KB (hidden 2048): the compute waves load the (gate, up)
 // rows from HBM into registers, kGuAhead rows in flight per wave, instead of
 // reading them from the LDS ring (Params::gu_direct).
@@ -247,7 +255,6 @@ struct Params {
     int32_t gemv_mfma;                         // 1: GEMVs on the matrix cores (tile-major weight chunks)
     int32_t E, top_k, n_shared, Fe;            // MoE: experts, selected per token, shared experts, expert width
     int32_t down_split;                        // 1: DOWN as OP_DPART + OP_DRED (F / kDownPart parts)
-    int32_t gu_direct;                         // 1: (gate, up) rows HBM -> compute-wave registers, not the ring
     float eps, attn_scale;
     // weights
     const DevLayer* layers;
@@ -291,6 +298,8 @@ struct Params {
     // A step cut into several persistent launches: this launch runs instructions
     // [cut_q[2 cu], cut_q[2 cu + 1]) of each CU's queue (nullptr: the whole queue).
     const uint32_t* cut_q;
+    int32_t gu_direct;  // 1: (gate, up) rows HBM -> loader-wave registers, not the ring (batch 1, hidden 2048)
+    int32_t down_q;     // 1: DOWN reduced by column quarters (down_quarters_for)
 };
 // Most persistent launches one decode step may be cut into.
 constexpr int kMaxCuts = 64;
@@ -302,7 +311,9 @@ constexpr int kChunkRows = kMaxBatch;
 //  ticks waiting for landed chunks, ticks the loaders waited for ring space,
 //  staging start (after the wave barrier), then three op-specific words: for
 //  attention the marks inputs staged, KV groups consumed, merged output
-//  written; for the other ops the compute ends of waves 1, 2, 3; 0 = unused}
+//  written; for (gate, up) rows streamed by the loader waves loader 0's rows
+//  requested, input seen, rows done; for the other ops the compute ends of
+//  waves 1, 2, 3; 0 = unused}
 constexpr int kTraceWords = 12;
 
 // Per-launch arguments.
