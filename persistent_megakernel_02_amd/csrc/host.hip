@@ -793,7 +793,8 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
     P.down_split = down_split_on(cfg, rt) ? 1 : 0;
     P.down_q = down_q_on(cfg, rt) ? 1 : 0;
     P.gu_direct = (rt->max_batch == 1 && !cfg->n_experts && !P.gemv_mfma &&
-                   (uint32_t)cfg->hidden * 2u == kGuRowPieces * 16u) ? 1 : 0;
+                   (cfg->head_dim == 64 || cfg->head_dim == 128) &&
+                   cfg->hidden == 512 * gu_npl(cfg->head_dim)) ? 1 : 0;
     P.V = cfg->vocab;
     P.B = rt->max_batch;
     P.S = rt->max_seq;

@@ -408,14 +408,14 @@ __device__ __forceinline__ uint32_t landed_prefix(const Ctl* ctl) {
 // the loader waves join it (head_direct), else q1.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// (gate, up) rows at batch 1 with rows of 4 KB (hidden 2048), from HBM straight
-// into the loader waves' registers.  Through the ring each pair cost a compute wave
+// (gate, up) rows at batch 1 (rows of 4 KB at hidden 2048, 8 KB at 4096), from HBM
+// straight into the loader waves' registers.  Through the ring each pair cost a compute wave
 // about 0.7 us of LDS traffic (8 KB of weights and 8 KB of fp32 x read per pair,
 // next to the loaders' writes of the same bytes); the compute waves have no
 // registers to spare for rows in flight, the loader waves do.  A loader reaching
 // the instruction in its stream retires its chunks in flight, requests its first
-// kGuAhead rows (during attention and O, while the ring is full and it would only
-// wait), waits for the compute waves to publish the staged input, copies its four
+// first rows (during attention and O, while the ring is full and it would only
+// wait), waits for the compute waves to publish the staged input, copies its
 // pieces of x to registers, and computes pairs k, k + 4, ... (the gate row, then
 // the up row), refilling a row's registers as soon as its products have read them.
 // It stores its SwiGLU outputs after the last row (a store between the row loads
@@ -425,17 +425,18 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // fixed tree: the values are bit for bit those of the ring GEMV.
 typedef __attribute__((address_space(1))) const u32x4_t* gu32x4_ptr;  // global memory (no flat loads)
 
+template <int NPL>
 struct GuRows {
     gu32x4_ptr gate;  // uniform: the instruction's first gate row
     gu32x4_ptr up;
-    uint32_t off;         // this lane's first piece of the wave's first row (16-byte units)
-    uint32_t nu;          // rows of this wave: two per pair
+    uint32_t off;     // this lane's first piece of the wave's first row (16-byte units)
+    uint32_t nu;      // rows of this wave: two per pair
     // row u of the wave (the callers' unrolled loops make is_up a constant) into dst
-    __device__ __forceinline__ void issue(uint32_t u, bool is_up, uint4 (&dst)[4]) const {
+    __device__ __forceinline__ void issue(uint32_t u, bool is_up, uint4 (&dst)[NPL]) const {
         const gu32x4_ptr base = is_up ? up : gate;
-        const uint32_t o = off + (u >> 1) * (uint32_t)(kLoaderWaves * kGuRowPieces);
+        const uint32_t o = off + (u >> 1) * (uint32_t)(kLoaderWaves * 64 * NPL);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int g = 0; g < NPL; ++g) {
             const u32x4_t v = __builtin_nontemporal_load(base + o + 64u * (uint32_t)g);
             dst[g] = make_uint4(v.x, v.y, v.z, v.w);
         }
@@ -459,24 +460,27 @@ __device__ __forceinline__ bool wait_lds_at_least(const Params& P, Ctl* ctl, con
     return true;
 }
 
-// Loader wave k's part of (gate, up) instruction qi (its stream has no ring bytes).
+// Loader wave k's part of (gate, up) instruction qi (its stream has no ring bytes);
+// rows of 64 NPL pieces.
+template <int NPL>
 __device__ __forceinline__ bool gu_loader(const Params& P, Ctl* ctl, const float* xs, const Instr& in, int k,
                                           uint32_t qi, uint32_t tag0, uint32_t* tr) {
-    constexpr int D = kGuAhead;
-    static_assert(D % 2 == 0, "a row's parity must be its slot's parity");
+    constexpr int D = gu_ahead(NPL), BLK = gu_block(NPL);
+    constexpr uint32_t RP = 64u * NPL;  // pieces of a row
+    static_assert(D % 2 == 0 && BLK % D == 0, "a row's parity must be its slot's parity");
     const uint32_t lane = (uint32_t)lane_id(), nw = (uint32_t)kLoaderWaves;
     const DevLayer Lw = ld_const(P.layers + (in.layer < P.L ? in.layer : 0));
     const uint32_t npair = in.count > (uint32_t)k ? (in.count - (uint32_t)k + nw - 1u) / nw : 0u;
-    const size_t first = (size_t)in.begin * kGuRowPieces;
-    const GuRows gr{(gu32x4_ptr)uniform_p(Lw.w_gate) + first, (gu32x4_ptr)uniform_p(Lw.w_up) + first,
-                    (uint32_t)k * kGuRowPieces + lane, 2u * npair};
-    // Rows go in blocks of kGuBlock (one block per instruction when each loader has
-    // kGuBlock / 2 pairs): inside a block the loop is unrolled, so every row buffer
-    // is a fixed register and every wait on a row's loads counts exactly the loads
-    // issued after it (a buffer carried around a loop back edge gets a full vmcnt
-    // wait).  Blocks of other sizes (other CU counts) take one row at a time.
-    const bool blocked = gr.nu >= (uint32_t)kGuBlock;
-    uint4 w[D][4];
+    const size_t first = (size_t)in.begin * RP;
+    const GuRows<NPL> gr{(gu32x4_ptr)uniform_p(Lw.w_gate) + first, (gu32x4_ptr)uniform_p(Lw.w_up) + first,
+                         (uint32_t)k * RP + lane, 2u * npair};
+    // Rows go in blocks of BLK (one block per instruction at 1B on 256 CUs): inside a
+    // block the loop is unrolled, so every row buffer is a fixed register and every
+    // wait on a row's loads counts exactly the loads issued after it (a buffer
+    // carried around a loop back edge gets a full vmcnt wait).  Rows after the last
+    // whole block go D at a time.
+    const bool blocked = gr.nu >= (uint32_t)BLK;
+    uint4 w[D][NPL];
     // The first rows are requested once the compute waves have staged the O input
     // before this instruction (or started this one): early enough to land before
     // the (gate, up) input is staged, late enough to stay out of the QKV and
@@ -492,17 +496,17 @@ __device__ __forceinline__ bool gu_loader(const Params& P, Ctl* ctl, const float
     if (tr && lane == 0) tr[10] = (uint32_t)now_ticks();
     const float r = rms_scale(ctl->ss[0], kComputeWaves, P.d, P.eps);
     const XLds x{xs, (uint32_t)P.d};
-    float4 xa[4], xb[4];
+    float4 xa[NPL], xb[NPL];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) x.piece(0, lane + 64u * (uint32_t)g, xa[g], xb[g]);
+    for (int g = 0; g < NPL; ++g) x.piece(0, lane + 64u * (uint32_t)g, xa[g], xb[g]);
     const uint32_t tag_out = phase_tag(tag0, in.layer, 3);
     float g_val = 0.f, keep = 0.f;
     // row u's products; after an up row, pair u / 2's output goes to lane (u / 2) mod
     // 64, and 64 pairs (or the last) are stored
-    auto row = [&](uint32_t u, bool is_up, const uint4 (&v)[4]) {
+    auto row = [&](uint32_t u, bool is_up, const uint4 (&v)[NPL]) {
         float acc[1] = {0.f};
 #pragma unroll
-        for (int g = 0; g < 4; ++g) acc[0] = dot8(v[g], xa[g], xb[g], acc[0]);
+        for (int g = 0; g < NPL; ++g) acc[0] = dot8(v[g], xa[g], xb[g], acc[0]);
         wave_total_n<1>(acc);
         if (!is_up) {
             g_val = acc[0];
@@ -517,23 +521,26 @@ __device__ __forceinline__ bool gu_loader(const Params& P, Ctl* ctl, const float
     };
     uint32_t u0 = 0;
     if (blocked) {
-        for (;; u0 += (uint32_t)kGuBlock) {
-            const bool next = u0 + 2u * (uint32_t)kGuBlock <= gr.nu;  // another whole block follows
+        for (;; u0 += (uint32_t)BLK) {
+            const bool next = u0 + 2u * (uint32_t)BLK <= gr.nu;  // another whole block follows
 #pragma unroll
-            for (int i = 0; i < kGuBlock; ++i) {
+            for (int i = 0; i < BLK; ++i) {
                 const uint32_t u = u0 + (uint32_t)i;
                 row(u, (i & 1) != 0, w[i % D]);
-                if (i + D < kGuBlock) gr.issue(u + D, (i & 1) != 0, w[i % D]);
+                if (i + D < BLK) gr.issue(u + D, (i & 1) != 0, w[i % D]);
                 else if (next) gr.issue(u + D, (i & 1) != 0, w[i % D]);
             }
             if (!next) break;
         }
-        u0 += (uint32_t)kGuBlock;
+        u0 += (uint32_t)BLK;
     }
-    for (uint32_t u = u0; u < gr.nu; ++u) {  // the rest, one row at a time
-        uint4 v[4];
-        gr.issue(u, (u & 1u) != 0, v);
-        row(u, (u & 1u) != 0, v);
+    for (; u0 < gr.nu; u0 += (uint32_t)D) {  // the rest (u0 even): D rows requested at once
+#pragma unroll
+        for (int i = 0; i < D; ++i)
+            if (u0 + (uint32_t)i < gr.nu) gr.issue(u0 + (uint32_t)i, (i & 1) != 0, w[i]);
+#pragma unroll
+        for (int i = 0; i < D; ++i)
+            if (u0 + (uint32_t)i < gr.nu) row(u0 + (uint32_t)i, (i & 1) != 0, w[i]);
     }
     if (tr && lane == 0) tr[11] = (uint32_t)now_ticks();
     // done: the compute waves, waiting for every loader, go on to stage the down
@@ -657,7 +664,7 @@ __device__ __forceinline__ uint32_t loader_wave(const Params& P, Ctl* ctl, char*
                 }
                 uint32_t* tr = (k == 0 && P.trace) ? P.trace + ((size_t)blockIdx.x * P.trace_stride + (i - q0)) * kTraceWords
                                                    : nullptr;
-                if (!gu_loader(P, ctl, xs, in, k, i, tag0, tr)) {
+                if (!gu_loader<gu_npl(HD)>(P, ctl, xs, in, k, i, tag0, tr)) {
                     stop = true;
                     break;
                 }

@@ -156,12 +156,14 @@ enum Op : uint16_t {
 constexpr uint32_t kDownQPieces = 256;  // 16-byte pieces of one quarter row
 __host__ __device__ constexpr bool down_quarters_for(int B, int F) { return B == 1 && F == 4 * (int)kDownQPieces * 8; }
 
-// Batch 1 with rows of 4 KB (hidden 2048): the compute waves load the (gate, up)
-// rows from HBM into registers, kGuAhead rows in flight per wave, instead of
-// reading them from the LDS ring (Params::gu_direct).
-constexpr int kGuAhead = 8;   // rows in flight per loader wave
-constexpr int kGuBlock = 16;  // rows per unrolled block (kGuBlock / 2 pairs)
-constexpr uint32_t kGuRowPieces = 256;  // 16-byte pieces of a 4 KB row (4 per lane)
+// Batch 1: the loader waves load the (gate, up) rows from HBM into registers
+// instead of reading them from the LDS ring (Params::gu_direct), for the Llama
+// shapes each head_dim instantiation serves: head_dim 64 kernels rows of hidden
+// 2048 (4 KB: 4 pieces per lane), head_dim 128 kernels hidden 4096 (8 KB: 8).
+// 128 registers of rows in flight per loader wave, unrolled blocks of 16 KB x 4.
+__host__ __device__ constexpr int gu_npl(int head_dim) { return head_dim == 64 ? 4 : 8; }
+__host__ __device__ constexpr int gu_ahead(int npl) { return 32 / npl; }  // rows in flight per loader wave
+__host__ __device__ constexpr int gu_block(int npl) { return 64 / npl; }  // rows per unrolled block
 
 // The dense down projection split by columns (batch 4 and 8; opt-in below): F is
 // cut into parts of kDownPart SwiGLU outputs.  Part j's partial output of every
