@@ -1109,9 +1109,10 @@ __device__ __forceinline__ bool gemv_ring_auto(const Params& P, Ctl* ctl, const 
 // coupling of loader and consumers capped the head near 4.5 TB/s.  Wave hw of 8
 // takes rows hw, hw + 8, ... of the instruction in 4 KB segments; lane l loads
 // pieces l, l + 64, l + 128, l + 192 of each segment with non-temporal loads,
-// four segments ahead at batch 1 (two at batch 2, one from batch 4, where the
-// registers hold the batch's accumulators and activations), so 128 KB (64, 32
-// KB) stream per CU at once.  Each lane accumulates
+// four segments ahead at batch 1, two at batch 2 and 8, one at batch 4 (where the
+// registers hold the batch's accumulators and activations; a second one measured
+// 10 us slower per step at batch 4 and 17 us faster at batch 8), so 128 KB (64,
+// 32 KB) stream per CU at once.  Each lane accumulates
 // its pieces in ascending order and wave_total reduces in its fixed tree: the
 // logits are bit for bit those of the ring GEMV (rows_dot).  The first segments
 // are issued before `ready()`, which waits for the staged final-norm input and
@@ -1130,7 +1131,7 @@ __device__ __forceinline__ bool head_direct(const Params& P, const StepArgs& A, 
                                             Spin& spin, Ready& ready) {
     constexpr int NW = kComputeWaves + kLoaderWaves;
     constexpr int G = 4;  // pieces per lane of one 4 KB segment of a row
-    constexpr int D = B == 1 ? 4 : B == 2 ? 2 : 1;  // segments in flight per wave (fewer next to B accumulators)
+    constexpr int D = B == 1 ? 4 : B == 4 ? 1 : 2;  // segments in flight per wave (measured per batch)
     const uint32_t d = (uint32_t)P.d, np = d >> 3, lane = (uint32_t)lane_id();
     const uint32_t nseg = (np + 64u * G - 1u) / (64u * G);  // segments per row
     const uint32_t nrow = in.count > (uint32_t)hw ? (in.count - (uint32_t)hw + NW - 1u) / NW : 0u;
