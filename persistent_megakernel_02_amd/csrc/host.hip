@@ -795,6 +795,7 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
     P.gu_direct = (rt->max_batch == 1 && !cfg->n_experts && !P.gemv_mfma &&
                    (cfg->head_dim == 64 || cfg->head_dim == 128) &&
                    cfg->hidden == 512 * gu_npl(cfg->head_dim)) ? 1 : 0;
+    P.o_direct = (P.gu_direct && cfg->head_dim == 128 && cfg->n_q_heads * cfg->head_dim == cfg->hidden) ? 1 : 0;
     P.V = cfg->vocab;
     P.B = rt->max_batch;
     P.S = rt->max_seq;
@@ -915,6 +916,7 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
         C.down_split = down_split_on(cfg, &r8) ? 1 : 0;
         C.gu_direct = 0;  // (the multi-position kernels stream every GEMV through the ring)
         C.down_q = 0;
+        C.o_direct = 0;
         C.eptr = (const uint16_t* const*)(cb + cl.eptr);
         C.attn_ticket = (uint32_t*)(cb + cl.tickets);
         C.head_ticket = C.attn_ticket + (size_t)cfg->n_layers * kChunkRows * cfg->n_kv_heads * kCtrStride;

@@ -57,6 +57,9 @@ struct Ctl {
     // compute wave 0's progress: 2 qi + 1 once instruction qi has started, 2 qi + 2
     // once an O instruction's input is staged (monotonic)
     uint32_t prog;
+    // O rows computed by the loader waves: loaders done (monotonic), and the layer + 1
+    // whose QKV input compute wave 0 has staged
+    uint32_t o_done, qkv_layer;
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -106,7 +109,7 @@ __device__ __forceinline__ uint32_t instr_bytes(const Params& P, const Instr& in
         case OP_HEAD: return 0;  // all eight waves stream the LM head into registers (head_direct)
         case OP_QKV:
         case OP_ROUTE: return align_chunk(in.count * (uint32_t)P.d * 2u);
-        case OP_O: return align_chunk(in.count * (uint32_t)(P.Hq * HD) * 2u);
+        case OP_O: return (HD == 128 && P.o_direct) ? 0u : align_chunk(in.count * (uint32_t)(P.Hq * HD) * 2u);
         case OP_GATEUP: return P.gu_direct ? 0u : align_chunk(2u * in.count * (uint32_t)P.d * 2u);
         case OP_DOWN: return align_chunk(in.count * (uint32_t)P.F * 2u);
         case OP_DPART: return in.count * kDownPart * (uint32_t)P.d * 2u;  // whole 16 KB multiples
@@ -553,6 +556,73 @@ __device__ __forceinline__ bool gu_loader(const Params& P, Ctl* ctl, const float
     return true;
 }
 
+// Loader wave k's part of O instruction qi at batch 1 with hidden 4096 (the 8B
+// shape; Params::o_direct; rows of 64 NPL pieces): rows k, k + 4, ... of the
+// instruction.  (At hidden 2048 the O rows are light and the loaders, busy with
+// them when the O input is staged, requested the (gate, up) rows later: 786 -> 816
+// us per 1B step; at 4096: 3778 -> 3691 us per 8B step.)
+// The rows are requested once this layer's QKV input is staged (not during the QKV
+// staging polls); the loader then waits for the O input (the attention output and
+// the residual rows, staged by the compute waves), keeps its pieces of x in
+// registers and stores h = residual + row.  Each lane accumulates its pieces in
+// ascending order and wave_total reduces in its fixed tree: the ring GEMV's bits.
+template <int NPL>
+__device__ __forceinline__ bool o_loader(const Params& P, Ctl* ctl, const float* xs, const Instr& in, int k,
+                                         uint32_t qi, uint32_t tag0) {
+    constexpr int D = 16 / NPL;  // rows in flight: 64 registers (more spilled with x at hidden 4096)
+    constexpr uint32_t RP = 64u * NPL;
+    const uint32_t lane = (uint32_t)lane_id(), nw = (uint32_t)kLoaderWaves;
+    const DevLayer Lw = ld_const(P.layers + (in.layer < P.L ? in.layer : 0));
+    const uint32_t nrw = in.count > (uint32_t)k ? (in.count - (uint32_t)k + nw - 1u) / nw : 0u;
+    const gu32x4_ptr base = (gu32x4_ptr)uniform_p(Lw.wo) + (size_t)in.begin * RP;
+    const uint32_t off = (uint32_t)k * RP + lane;
+    auto issue = [&](uint32_t j, uint4 (&dst)[NPL]) {
+        const uint32_t o = off + j * nw * RP;
+#pragma unroll
+        for (int g = 0; g < NPL; ++g) {
+            const u32x4_t v = __builtin_nontemporal_load(base + o + 64u * (uint32_t)g);
+            dst[g] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+    };
+    if (!wait_lds_at_least(P, ctl, &ctl->qkv_layer, (uint32_t)in.layer + 1u, 0xFFFFFFF7u)) return false;
+    uint4 w[D][NPL];
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        if ((uint32_t)i < nrw) issue((uint32_t)i, w[i]);
+    if (!wait_lds_at_least(P, ctl, &ctl->prog, 2u * qi + 2u, 0xFFFFFFF6u)) return false;
+    const uint32_t K = (uint32_t)(P.Hq * P.hd);
+    const XLds x{xs, K};
+    const float* hres = xs + K;
+    float4 xa[NPL], xb[NPL];
+#pragma unroll
+    for (int g = 0; g < NPL; ++g) x.piece(0, lane + 64u * (uint32_t)g, xa[g], xb[g]);
+    const uint32_t tag_out = phase_tag(tag0, in.layer, 2);
+    float keep = 0.f;
+    for (uint32_t j0 = 0; j0 < nrw; j0 += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {  // (no break: w must stay register-indexed)
+            const uint32_t j = j0 + (uint32_t)i;
+            if (j < nrw) {
+                float acc[1] = {0.f};
+#pragma unroll
+                for (int g = 0; g < NPL; ++g) acc[0] = dot8(w[i][g], xa[g], xb[g], acc[0]);
+                if (j + D < nrw) issue(j + D, w[i]);
+                wave_total_n<1>(acc);
+                // row j of this loader is row k + 4 j of the instruction; 64 rows (or the
+                // last) are stored at once
+                const uint32_t jl = j & 63u;
+                const float v = hres[(uint32_t)k + nw * j] + acc[0];
+                keep = lane == jl ? v : keep;
+                if (jl == 63u || j + 1u == nrw) {
+                    if (lane <= jl) st_tagged(P.h + in.begin + (uint32_t)k + nw * (j - jl + lane), keep, tag_out);
+                }
+            }
+        }
+    }
+    if (lane == 0) __hip_atomic_fetch_add(&ctl->o_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return true;
+}
+
 template <int B, int HD, bool MF, bool MOE>
 __device__ __forceinline__ uint32_t loader_wave(const Params& P, Ctl* ctl, char* ring, int k, uint32_t q0, uint32_t q1,
                                                 const int32_t* ctx, const float* xs, uint32_t tag0) {
@@ -651,6 +721,23 @@ __device__ __forceinline__ uint32_t loader_wave(const Params& P, Ctl* ctl, char*
             break;
         }
         if constexpr (B == 1 && !MF && !MOE) {
+            if (HD == 128 && in.op == OP_O && P.o_direct) {  // rows into registers, no ring bytes
+                if (k == 0 && P.trace && lane_id() == 0 && i > q0) {
+                    uint32_t* rec = P.trace + ((size_t)blockIdx.x * P.trace_stride + (i - 1 - q0)) * kTraceWords;
+                    rec[5] = (uint32_t)now_ticks();
+                    rec[7] = stall;
+                }
+                stall = 0;
+                if (issued != landed) {  // retire the chunks in flight: vmcnt counts the row loads next
+                    wait_vmcnt<0>();
+                    publish(issued);
+                }
+                if (!o_loader<gu_npl(128)>(P, ctl, xs, in, k, i, tag0)) {
+                    stop = true;
+                    break;
+                }
+                continue;
+            }
             if (in.op == OP_GATEUP && P.gu_direct) {  // rows into registers, no ring bytes
                 if (k == 0 && P.trace && lane_id() == 0 && i > q0) {
                     uint32_t* rec = P.trace + ((size_t)blockIdx.x * P.trace_stride + (i - 1 - q0)) * kTraceWords;
@@ -2106,6 +2193,7 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
     CwBarrier barrier{ctl, &P, 0u};
     uint32_t head_qi = q1;
     uint32_t gu_expect = 0;  // loader reads of staged (gate, up) inputs seen so far (gu_loader)
+    uint32_t o_expect = 0;   // loader completions of O instructions seen so far (o_loader)
     for (uint32_t qi = q0; qi < q1; ++qi, ++k) {
         const Instr in = ld_const(P.instrs + qi);
         uint32_t bytes = instr_bytes<HD, MF>(P, in, ctx);  // MoE expert instructions set it once routed
@@ -2201,6 +2289,9 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
 #pragma unroll
                 for (int b = 0; b < B; ++b) r[b] = rms_scale(ctl->ss[b], kComputeWaves, P.d, P.eps);
                 if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
+                if constexpr (B == 1 && !MOE && HD == 128) {  // (read only by o_loader)
+                    if (in.op == OP_QKV && wave == 0 && lane == 0) lds_st(&ctl->qkv_layer, (uint32_t)layer + 1u);
+                }
                 if (in.op == OP_HEAD) {
                     // the LM-head input is staged: publish it to the loader waves; all
                     // eight waves stream the rows after the loop (head_instr)
@@ -2308,6 +2399,13 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
                     if (tr && lane == 0 && ks == 0) tr[2] = (uint32_t)now_ticks();
                     if constexpr (B == 1 && !MOE) {
                         if (is_o && ks == 0 && wave == 0 && lane == 0) lds_st(&ctl->prog, 2u * qi + 2u);
+                        if (HD == 128 && is_o && P.o_direct) {
+                            // the loader waves compute the rows (o_loader); xs is reused
+                            // only once every loader is done
+                            o_expect += (uint32_t)kLoaderWaves;
+                            ok = wait_lds_at_least(P, ctl, &ctl->o_done, o_expect, 0xFFFFFFF5u);
+                            break;
+                        }
                     }
                     const XLds x{xs, Ks};
                     const bool last = ks + 1 == ns;
@@ -2419,6 +2517,10 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
         ctl.gu_seq = 0;
         ctl.gu_done = 0;
         ctl.prog = 0;
+        if constexpr (HD == 128) {  // (o_loader)
+            ctl.o_done = 0;
+            ctl.qkv_layer = 0;
+        }
     }
     // context lengths at launch (a multi-position step: every row sees the sequence's cached length)
     if (threadIdx.x < kMaxBatch)

@@ -302,6 +302,7 @@ struct Params {
     const uint32_t* cut_q;
     int32_t gu_direct;  // 1: (gate, up) rows HBM -> loader-wave registers, not the ring (batch 1, hidden 2048)
     int32_t down_q;     // 1: DOWN reduced by column quarters (down_quarters_for)
+    int32_t o_direct;   // 1: O rows HBM -> loader-wave registers, computed there (batch 1, hidden 4096)
 };
 // Most persistent launches one decode step may be cut into.
 constexpr int kMaxCuts = 64;
