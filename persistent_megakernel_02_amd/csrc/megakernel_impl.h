@@ -102,14 +102,14 @@ __device__ __forceinline__ uint32_t moe_bytes(const Params& P, const Instr& in, 
 
 // Bytes of the CU stream that instruction `in` consumes (whole chunks).  With the
 // matrix cores (MF) a GEMV streams whole 16-row tiles of 1 KB chunks.
-template <int HD, bool MF = false>
+template <int HD, bool MF = false, bool ODIR = false>
 __device__ __forceinline__ uint32_t instr_bytes(const Params& P, const Instr& in, const int32_t* ctx) {
     if (MF && is_gemv(in.op)) return mfma_geo<HD>(P, in).chunks() * kChunk;
     switch (in.op) {
         case OP_HEAD: return 0;  // all eight waves stream the LM head into registers (head_direct)
         case OP_QKV:
         case OP_ROUTE: return align_chunk(in.count * (uint32_t)P.d * 2u);
-        case OP_O: return (HD == 128 && P.o_direct) ? 0u : align_chunk(in.count * (uint32_t)(P.Hq * HD) * 2u);
+        case OP_O: return (ODIR && P.o_direct) ? 0u : align_chunk(in.count * (uint32_t)(P.Hq * HD) * 2u);
         case OP_GATEUP: return P.gu_direct ? 0u : align_chunk(2u * in.count * (uint32_t)P.d * 2u);
         case OP_DOWN: return align_chunk(in.count * (uint32_t)P.F * 2u);
         case OP_DPART: return in.count * kDownPart * (uint32_t)P.d * 2u;  // whole 16 KB multiples
@@ -766,7 +766,7 @@ __device__ __forceinline__ uint32_t loader_wave(const Params& P, Ctl* ctl, char*
             }
             nch = moe_bytes(P, in, lds_ld(&ctl->moe_n)) / kChunk;
         } else {
-            nch = instr_bytes<HD, MF>(P, in, ctx) / kChunk;
+            nch = instr_bytes<HD, MF, B == 1 && !MF && !MOE && HD == 128>(P, in, ctx) / kChunk;
         }
         if (k == 0 && P.trace && lane_id() == 0 && i > q0) {
             uint32_t* rec = P.trace + ((size_t)blockIdx.x * P.trace_stride + (i - 1 - q0)) * kTraceWords;
@@ -1196,10 +1196,10 @@ __device__ __forceinline__ bool gemv_ring_auto(const Params& P, Ctl* ctl, const 
 // coupling of loader and consumers capped the head near 4.5 TB/s.  Wave hw of 8
 // takes rows hw, hw + 8, ... of the instruction in 4 KB segments; lane l loads
 // pieces l, l + 64, l + 128, l + 192 of each segment with non-temporal loads,
-// four segments ahead at batch 1, two at batch 2 and 8, one at batch 4 (where the
-// registers hold the batch's accumulators and activations; a second one measured
-// 10 us slower per step at batch 4 and 17 us faster at batch 8), so 128 KB (64,
-// 32 KB) stream per CU at once.  Each lane accumulates
+// four segments ahead at batch 1, two at batch 2 and 8 (dense), one at batch 4 and
+// for the MoE kernels at 8 (where the registers hold the batch's accumulators and
+// activations; a second one measured 10 us slower per step at dense batch 4 and 17 us
+// faster at dense batch 8), so 128 KB (64, 32 KB) stream per CU at once.  Each lane accumulates
 // its pieces in ascending order and wave_total reduces in its fixed tree: the
 // logits are bit for bit those of the ring GEMV (rows_dot).  The first segments
 // are issued before `ready()`, which waits for the staged final-norm input and
@@ -1213,12 +1213,12 @@ __device__ __forceinline__ uint4 ld_nt16(const uint4* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int B, class Ready>
+template <int B, bool MOE, class Ready>
 __device__ __forceinline__ bool head_direct(const Params& P, const StepArgs& A, const float* xs, const Instr& in, int hw,
                                             Spin& spin, Ready& ready) {
     constexpr int NW = kComputeWaves + kLoaderWaves;
     constexpr int G = 4;  // pieces per lane of one 4 KB segment of a row
-    constexpr int D = B == 1 ? 4 : B == 4 ? 1 : 2;  // segments in flight per wave (measured per batch)
+    constexpr int D = B == 1 ? 4 : (B == 4 || (MOE && B == 8)) ? 1 : 2;  // segments in flight per wave (measured)
     const uint32_t d = (uint32_t)P.d, np = d >> 3, lane = (uint32_t)lane_id();
     const uint32_t nseg = (np + 64u * G - 1u) / (64u * G);  // segments per row
     const uint32_t nrow = in.count > (uint32_t)hw ? (in.count - (uint32_t)hw + NW - 1u) / NW : 0u;
@@ -2196,7 +2196,7 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
     uint32_t o_expect = 0;   // loader completions of O instructions seen so far (o_loader)
     for (uint32_t qi = q0; qi < q1; ++qi, ++k) {
         const Instr in = ld_const(P.instrs + qi);
-        uint32_t bytes = instr_bytes<HD, MF>(P, in, ctx);  // MoE expert instructions set it once routed
+        uint32_t bytes = instr_bytes<HD, MF, B == 1 && !MF && !MOE && HD == 128>(P, in, ctx);  // MoE expert instructions set it once routed
         uint32_t* tr =
             (P.trace && wave == 0) ? P.trace + ((size_t)blockIdx.x * P.trace_stride + k) * kTraceWords : nullptr;
         if (tr && lane == 0) {
@@ -2460,7 +2460,7 @@ __device__ __forceinline__ uint32_t compute_wave(const Params& P, const StepArgs
 // loads are issued ahead, and inside the loop the compiler would have to assume
 // some may still be in flight at the back edge, guarding every later write of
 // their registers (in the GEMV row loops) with a vmcnt wait.
-template <int B>
+template <int B, bool MOE>
 __device__ __forceinline__ void head_instr(const Params& P, const StepArgs& A, Ctl* ctl, float* xs, int wave,
                                            uint32_t q0, uint32_t qi) {
     const Instr in = ld_const(P.instrs + qi);
@@ -2492,7 +2492,7 @@ __device__ __forceinline__ void head_instr(const Params& P, const StepArgs& A, C
         for (int b = 0; b < B; ++b) r[b] = rms_scale(ctl->ss[b], kComputeWaves, P.d, P.eps);
         return true;
     };
-    const bool ok = head_direct<B>(P, A, xs, in, wave, spin, ready);
+    const bool ok = head_direct<B, MOE>(P, A, xs, in, wave, spin, ready);
     if (ok && P.trace && wave == 0 && lane_id() == 0) {  // compute end and end of the head's record
         uint32_t* tr = P.trace + ((size_t)blockIdx.x * P.trace_stride + (qi - q0)) * kTraceWords;
         tr[3] = tr[4] = (uint32_t)now_ticks();
@@ -2517,7 +2517,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
         ctl.gu_seq = 0;
         ctl.gu_done = 0;
         ctl.prog = 0;
-        if constexpr (HD == 128) {  // (o_loader)
+        if constexpr (B == 1 && !MF && !MOE && HD == 128) {  // (o_loader)
             ctl.o_done = 0;
             ctl.qkv_layer = 0;
         }
@@ -2538,7 +2538,7 @@ __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(Params P, StepArgs 
     if constexpr (!MF) {
         float* hx = xs;
         if constexpr (MOE && B == kMaxBatch) hx = P.x_slices > 1 ? (float*)ring : xs;  // staged over the ring
-        if (hi < q1) head_instr<B>(P, A, &ctl, hx, wave, q0, hi);
+        if (hi < q1) head_instr<B, MOE>(P, A, &ctl, hx, wave, q0, hi);
     }
 }
 
