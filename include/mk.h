@@ -274,7 +274,11 @@ const char* mk_last_error(const mk_handle* h);
  * (MK_GEMV_VALU or MK_GEMV_MFMA), [11] q-head groups per attention item (1, or
  * the q heads per KV head when one position split leaves compute units idle),
  * [12] the most ring chunks one compute wave holds while it waits for its data
- * (mk_create refuses a configuration where this exceeds [2]). */
+ * (mk_create refuses a configuration where this exceeds [2]), [13] 1 when the dense
+ * down projection is split by columns, then 1 when the batch-1 path applies: [14]
+ * the (gate, up) rows computed by the loader waves from registers, [15] the down
+ * projection reduced by column quarters, [16] the O rows computed by the loader
+ * waves. */
 mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* rt, int32_t num_cus, int64_t* out,
                           int32_t cap);
 

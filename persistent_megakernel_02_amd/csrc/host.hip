@@ -102,6 +102,18 @@ bool down_q_on(const mk_model_config* c, const mk_runtime_config* rt) {
     return !c->n_experts && down_quarters_for(rt->max_batch, c->ffn) && !use_mfma(c, rt) && !down_split_on(c, rt);
 }
 
+// (gate, up) rows computed by the loader waves from registers (batch 1, dense, VALU,
+// hidden 2048 with head_dim 64 or 4096 with head_dim 128).
+bool gu_direct_on(const mk_model_config* c, const mk_runtime_config* rt) {
+    return rt->max_batch == 1 && !c->n_experts && !use_mfma(c, rt) && (c->head_dim == 64 || c->head_dim == 128) &&
+           c->hidden == 512 * gu_npl(c->head_dim);
+}
+
+// O rows computed by the loader waves (as gu_direct_on, hidden 4096 only).
+bool o_direct_on(const mk_model_config* c, const mk_runtime_config* rt) {
+    return gu_direct_on(c, rt) && c->head_dim == 128 && c->n_q_heads * c->head_dim == c->hidden;
+}
+
 uint32_t dred_rows_for(const mk_model_config* c) { return dred_rows((uint32_t)c->hidden, (uint32_t)c->ffn); }
 
 // LDS floats of activations one instruction stages (x rows, residual rows of
@@ -694,11 +706,14 @@ mk_status mk_plan_inspect(const mk_model_config* cfg, const mk_runtime_config* r
                               : 3 * (int64_t)cfg->ffn * d;
     const int64_t per_layer = (cfg->n_q_heads + 2 * cfg->n_kv_heads) * hd * d + d * cfg->n_q_heads * hd + ffn_w + 2 * d;
     const size_t xb = x_bytes_for(cfg, rt, pl.nsplit);
-    int64_t vals[14] = {num_cus, (int64_t)pl.instrs.size(), (int64_t)ring_chunks_for(xb), (int64_t)pl.max_per_cu,
+    const bool pm = rt->mode == MK_MODE_MEGAKERNEL;  // (the three batch-1 paths are persistent-kernel paths)
+    int64_t vals[17] = {num_cus, (int64_t)pl.instrs.size(), (int64_t)ring_chunks_for(xb), (int64_t)pl.max_per_cu,
                         2 * (cfg->n_layers * per_layer + (int64_t)cfg->vocab * d + d), verify_plan(cfg, rt, pl),
                         pl.nsplit, pl.phases, (int64_t)xb, (int64_t)pl.n_head, use_mfma(cfg, rt) ? 2 : 1, pl.hsplit,
-                        (int64_t)max_wave_span(cfg, rt), down_split_on(cfg, rt) ? 1 : 0};
-    for (int i = 0; i < cap && i < 14; ++i) out[i] = vals[i];
+                        (int64_t)max_wave_span(cfg, rt), down_split_on(cfg, rt) ? 1 : 0,
+                        (pm && gu_direct_on(cfg, rt)) ? 1 : 0, down_q_on(cfg, rt) ? 1 : 0,
+                        (pm && o_direct_on(cfg, rt)) ? 1 : 0};
+    for (int i = 0; i < cap && i < 17; ++i) out[i] = vals[i];
     return MK_OK;
 }
 
@@ -792,10 +807,8 @@ static mk_status create_impl(const mk_model_config* cfg, const mk_weights* w, co
     P.Fe = cfg->expert_ffn;
     P.down_split = down_split_on(cfg, rt) ? 1 : 0;
     P.down_q = down_q_on(cfg, rt) ? 1 : 0;
-    P.gu_direct = (rt->max_batch == 1 && !cfg->n_experts && !P.gemv_mfma &&
-                   (cfg->head_dim == 64 || cfg->head_dim == 128) &&
-                   cfg->hidden == 512 * gu_npl(cfg->head_dim)) ? 1 : 0;
-    P.o_direct = (P.gu_direct && cfg->head_dim == 128 && cfg->n_q_heads * cfg->head_dim == cfg->hidden) ? 1 : 0;
+    P.gu_direct = gu_direct_on(cfg, rt) ? 1 : 0;
+    P.o_direct = o_direct_on(cfg, rt) ? 1 : 0;
     P.V = cfg->vocab;
     P.B = rt->max_batch;
     P.S = rt->max_seq;

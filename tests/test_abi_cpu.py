@@ -324,3 +324,28 @@ def test_static_create_refuses_on_the_host():
     assert L.mk_create_static(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(big), None, 0, None,
                               ctypes.byref(h)) == mk.MK_E_CAPACITY
     assert h.value is None
+
+
+def test_batch1_loader_paths_selection():
+    """The three batch-1 persistent-kernel paths: the (gate, up) rows by the loader
+    waves on both dense shapes (hidden 2048 / head_dim 64 and 4096 / 128), the down
+    projection by column quarters where F = 8192 (the 1B shape), the O rows by the
+    loader waves on the hidden-4096 shape only; none at batch 4, with MFMA, for the
+    mixture of experts or off those shapes, and only the quarters in the graph
+    mode."""
+    keys = ("gateup_by_loaders", "down_quarters", "o_by_loaders")
+
+    def sel(cfg, r):
+        st, info = mk.mk_plan_inspect(mk.model_config(cfg), r, 256)
+        assert st == mk.MK_OK
+        return tuple(info[k] for k in keys)
+
+    assert sel(I.LLAMA_1B, rt(1, 200)) == (1, 1, 0)
+    assert sel(I.LLAMA_8B, rt(1, 200)) == (1, 0, 1)
+    assert sel(I.LLAMA_1B, rt(4, 200)) == (0, 0, 0)
+    assert sel(I.LLAMA_8B, rt(1, 200, mode=mk.MK_MODE_GRAPH)) == (0, 0, 0)
+    assert sel(I.LLAMA_1B, mk.runtime_config(1, 200, gemv_kind=mk.MK_GEMV_MFMA)) == (0, 0, 0)
+    # the graph mode takes the same quarter order for its DOWN kernel, not the loader rows
+    assert sel(I.LLAMA_1B, rt(1, 200, mode=mk.MK_MODE_GRAPH)) == (0, 1, 0)
+    assert sel(I.MOE, rt(4, 4200)) == (0, 0, 0)
+    assert sel(I.TINY, rt(1, 200)) == (0, 0, 0)
