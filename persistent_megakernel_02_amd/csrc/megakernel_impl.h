@@ -2127,10 +2127,10 @@ __device__ __forceinline__ bool attn_instr(const Params& P, const StepArgs& A, C
 // and published (the caller runs its rows: head_instr), or q1 (none in this kind,
 // or the workgroup stopped).
 // The down projection at batch 1 with F = 8192, by column quarters (down_q_partial):
-// the input and the residual rows are staged as for DOWN, then compute wave q keeps
-// its quarter of x in registers and, row by row, waits for that row's quarter in the
-// ring (4 KB), reduces it and leaves the value in LDS; after a barrier wave 0 adds
-// each row's quarters in order and the residual.
+// compute wave q stages quarter q of the input (wave 0 also the residual rows), keeps
+// it in registers and, row by row, waits for that row's quarter in the ring (4 KB),
+// reduces it and leaves the value in LDS; after a barrier wave 0 adds each row's
+// quarters in order and the residual.
 __device__ __forceinline__ bool down_q_instr(const Params& P, const StepArgs& A, Ctl* ctl, const char* ring, float* xs,
                                              int wave, const Instr& in, uint32_t S, Spin& spin, CwBarrier& barrier,
                                              uint32_t& land_wait, uint32_t* tr) {
@@ -2138,12 +2138,15 @@ __device__ __forceinline__ bool down_q_instr(const Params& P, const StepArgs& A,
     float* hres = xs + K;                 // [count] residual rows
     float* part = hres + kMaxResidRows;   // [count][4] quarter values
     float ss[1] = {0.f};
-    const StageSeg sg[2] = {{P.act, xs, nullptr, K, 1u, K, K, phase_tag(A.tag0, layer, 3)},
-                            {P.h + in.begin, hres, nullptr, in.count, 1u, (uint32_t)P.d, in.count,
+    // each wave stages only its own quarter of the input (the one it reads), wave 0
+    // also the residual rows (read only by wave 0, after the closing barrier): no
+    // wave reads what another staged before that barrier
+    const uint32_t qw = K / 4u, qoff = (uint32_t)wave * qw;
+    const StageSeg sg[2] = {{P.act + qoff, xs + qoff, nullptr, qw, 1u, qw, qw, phase_tag(A.tag0, layer, 3)},
+                            {P.h + in.begin, hres, nullptr, wave == 0 ? in.count : 0u, 1u, (uint32_t)P.d, in.count,
                              phase_tag(A.tag0, layer, 2)}};
-    if (!stage_segs<stage_words_wide<1>(), 1, 2>(sg, wave, kComputeWaves, spin, ss)) return false;
-    if (!barrier()) return false;
-    if (tr && lane == 0) tr[2] = (uint32_t)now_ticks();
+    if (!stage_segs<stage_words_wide<1>(), 1, 2>(sg, 0, 1, spin, ss)) return false;
+    if (tr && lane == 0 && wave == 0) tr[2] = (uint32_t)now_ticks();
     const XLds x{xs, K};
     float4 xa[4], xb[4];
 #pragma unroll
